@@ -1,0 +1,219 @@
+"""Python binding of libdg, the MI355X canvas-denoise library (C ABI in include/dg.h).
+
+Argument marshalling only: every call checks the torch tensors it is handed (device,
+dtype, contiguity), passes their device pointers and the context's HIP stream to the
+C entry point of the same name, and raises DGError on a non-OK status. All of the
+step's arithmetic runs in the library's HIP kernels; there is no fallback path, and
+importing this package fails loudly when libdg.so has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["DGError", "Dims", "Context", "workspace_bytes", "temperature", "lib_path",
+           "STOP_GO", "STOP_STOP", "STOP_CAP"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+STOP_GO, STOP_STOP, STOP_CAP = 0, 1, 2
+
+_STATUS = {0: "DG_OK", 1: "DG_ERR_NULL", 2: "DG_ERR_SHAPE", 3: "DG_ERR_ALIGN", 4: "DG_ERR_RANGE",
+           5: "DG_ERR_CAPACITY", 6: "DG_ERR_STATE", 7: "DG_ERR_NONFINITE", 8: "DG_ERR_HIP",
+           9: "DG_ERR_UNSUPPORTED"}
+
+
+class DGError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.name = _STATUS.get(status, str(status))
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libdg.so")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("V", "d", "C", "Hq", "Hkv", "hd", "F")]
+
+    @classmethod
+    def of(cls, obj) -> "Dims":
+        if isinstance(obj, Dims):
+            return obj
+        g = (lambda k: obj[k]) if isinstance(obj, dict) else (lambda k: getattr(obj, k))
+        return cls(*(int(g(k)) for k in ("V", "d", "C", "Hq", "Hkv", "hd", "F")))
+
+
+_P = ctypes.c_void_p
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise ImportError(f"libdg.so is not built ({path}); run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    i32, i64, f32, u32, u64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_uint32, ctypes.c_uint64
+    D = ctypes.POINTER(Dims)
+    sig = {
+        "dg_create": (i32, [ctypes.POINTER(_P), ctypes.c_int, _P]),
+        "dg_destroy": (None, [_P]),
+        "dg_set_stream": (i32, [_P, _P]),
+        "dg_last_error": (ctypes.c_char_p, [_P]),
+        "dg_sync": (i32, [_P]),
+        "dg_clear_status": (i32, [_P]),
+        "dg_workspace_bytes": (ctypes.c_size_t, [D, i64]),
+        "dg_temperature": (f32, [i32, i32, f32, f32]),
+        "dg_canvas_attn": (i32, [_P, D, _P, _P, _P, _P, _P, _P, _P, _P, _P, i64, i64, _P, _P]),
+        "dg_logits_entropy": (i32, [_P, D, _P, _P, f32, _P, _P, _P]),
+        "dg_entropy_accept": (i32, [_P, i32, i32, _P, f32, _P, _P]),
+        "dg_renoise": (i32, [_P, i32, i32, i32, _P, _P, u64, u32, u32, _P]),
+        "dg_selfcond": (i32, [_P, D, _P, _P, _P, _P, _P]),
+        "dg_stop_test": (i32, [_P, i32, i32, _P, _P, _P, f32, i32, i32, _P]),
+        "dg_commit_kv": (i32, [_P, D, _P, _P, _P, _P, _P, _P, i64, i64, ctypes.POINTER(i64)]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def workspace_bytes(dims, Pcap: int) -> int:
+    d = Dims.of(dims)
+    n = _load().dg_workspace_bytes(ctypes.byref(d), int(Pcap))
+    if n == 0:
+        raise DGError(2, "dg_workspace_bytes: unsupported dims")
+    return int(n)
+
+
+def temperature(k: int, N: int, tau0: float = 0.8, tau1: float = 0.4) -> float:
+    return float(_load().dg_temperature(int(k), int(N), float(tau0), float(tau1)))
+
+
+def _ptr(t, dtype, name, optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+_BF16, _F32, _I32, _U8 = torch.bfloat16, torch.float32, torch.int32, torch.uint8
+
+
+class Context:
+    """One dg_ctx: a device, a HIP stream and the sticky device status word."""
+
+    def __init__(self, device: int = 0, stream=None):
+        self._lib = _load()
+        self.device = int(device)
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        self._stream = stream
+        h = _P()
+        st = self._lib.dg_create(ctypes.byref(h), self.device, self._raw_stream(stream))
+        if st != 0:
+            raise DGError(st, "dg_create failed")
+        self._h = h
+
+    @staticmethod
+    def _raw_stream(stream):
+        if stream is None:
+            return None
+        if isinstance(stream, int):
+            return stream
+        return stream.cuda_stream
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.dg_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _check(self, st: int):
+        if st != 0:
+            raise DGError(st, self._lib.dg_last_error(self._h).decode())
+
+    def set_stream(self, stream):
+        self._stream = stream
+        self._check(self._lib.dg_set_stream(self._h, self._raw_stream(stream)))
+
+    @property
+    def stream(self):
+        return self._stream
+
+    def sync(self):
+        self._check(self._lib.dg_sync(self._h))
+
+    def clear_status(self):
+        self._check(self._lib.dg_clear_status(self._h))
+
+    # ------------------------------------------------------------ the seven calls
+    def canvas_attn(self, dims, tokens, z, E, Wq, Wk, Wv, Wo, Kp, Vt, P, ws, A):
+        d = Dims.of(dims)
+        Pcap = Kp.shape[1] if Kp is not None else 0
+        self._check(self._lib.dg_canvas_attn(
+            self._h, ctypes.byref(d), _ptr(tokens, _I32, "tokens"), _ptr(z, _BF16, "z", True),
+            _ptr(E, _BF16, "E"), _ptr(Wq, _BF16, "Wq"), _ptr(Wk, _BF16, "Wk"), _ptr(Wv, _BF16, "Wv"),
+            _ptr(Wo, _BF16, "Wo"), _ptr(Kp, _BF16, "Kp", True), _ptr(Vt, _BF16, "Vt", True),
+            int(P), int(Pcap), _ptr(ws, _U8, "ws"), _ptr(A, _BF16, "A")))
+
+    def logits_entropy(self, dims, H, E, tau, ws, entropy, argmax):
+        d = Dims.of(dims)
+        self._check(self._lib.dg_logits_entropy(
+            self._h, ctypes.byref(d), _ptr(H, _BF16, "H"), _ptr(E, _BF16, "E"), float(tau),
+            _ptr(ws, _U8, "ws"), _ptr(entropy, _F32, "entropy"), _ptr(argmax, _I32, "argmax")))
+
+    def entropy_accept(self, entropy, b, accept, n_accept):
+        B, C = (1, entropy.shape[0]) if entropy.dim() == 1 else tuple(entropy.shape)
+        self._check(self._lib.dg_entropy_accept(
+            self._h, B, C, _ptr(entropy, _F32, "entropy"), float(b), _ptr(accept, _U8, "accept"),
+            _ptr(n_accept, _I32, "n_accept")))
+
+    def renoise(self, V, argmax, accept, seed, canvas_base, step, tokens):
+        B, C = (1, tokens.shape[0]) if tokens.dim() == 1 else tuple(tokens.shape)
+        self._check(self._lib.dg_renoise(
+            self._h, B, C, int(V), _ptr(argmax, _I32, "argmax", True), _ptr(accept, _U8, "accept", True),
+            int(seed), int(canvas_base), int(step), _ptr(tokens, _I32, "tokens")))
+
+    def selfcond(self, dims, ws, E, W1, W2, z):
+        d = Dims.of(dims)
+        self._check(self._lib.dg_selfcond(
+            self._h, ctypes.byref(d), _ptr(ws, _U8, "ws"), _ptr(E, _BF16, "E"), _ptr(W1, _BF16, "W1"),
+            _ptr(W2, _BF16, "W2"), _ptr(z, _BF16, "z")))
+
+    def stop_test(self, entropy, argmax, prev_argmax, thr, step, N, flag):
+        B, C = (1, entropy.shape[0]) if entropy.dim() == 1 else tuple(entropy.shape)
+        self._check(self._lib.dg_stop_test(
+            self._h, B, C, _ptr(entropy, _F32, "entropy"), _ptr(argmax, _I32, "argmax"),
+            _ptr(prev_argmax, _I32, "prev_argmax", True), float(thr), int(step), int(N),
+            _ptr(flag, _I32, "flag")))
+
+    def commit_kv(self, dims, tokens, E, Wk, Wv, Kp, Vt, P) -> int:
+        d = Dims.of(dims)
+        out = ctypes.c_int64(0)
+        self._check(self._lib.dg_commit_kv(
+            self._h, ctypes.byref(d), _ptr(tokens, _I32, "tokens"), _ptr(E, _BF16, "E"),
+            _ptr(Wk, _BF16, "Wk"), _ptr(Wv, _BF16, "Wv"), _ptr(Kp, _BF16, "Kp"), _ptr(Vt, _BF16, "Vt"),
+            int(P), int(Kp.shape[1]), ctypes.byref(out)))
+        return int(out.value)

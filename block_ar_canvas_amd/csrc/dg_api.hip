@@ -1,0 +1,390 @@
+// C ABI of the canvas-denoise library (declarations and contracts in include/dg.h).
+//
+// Host-side responsibilities: validate every argument before anything is enqueued,
+// carve the caller's workspace, and launch the kernels of each call in order on the
+// context's stream. No call allocates device memory (the context's 4-byte status word
+// is allocated once in dg_create) and no call waits for the device except dg_sync.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <climits>
+#include <new>
+
+#include "../../include/dg.h"
+#include "dg_common.h"
+
+struct dg_ctx_s {
+  int device = 0;
+  hipStream_t stream = nullptr;
+  int *d_status = nullptr;
+  char err[512] = {0};
+  // p0 hand-off between dg_logits_entropy and dg_selfcond.
+  const void *p0_ws = nullptr;
+  dg_dims p0_dims = {0, 0, 0, 0, 0, 0, 0};
+  bool p0_valid = false;
+};
+
+namespace {
+
+dg_status fail(dg_ctx ctx, dg_status st, const char *fmt, ...) {
+  if (ctx) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(ctx->err, sizeof ctx->err, fmt, ap);
+    va_end(ap);
+  }
+  return st;
+}
+
+dg_status hip_fail(dg_ctx ctx, hipError_t e, const char *where) {
+  return fail(ctx, DG_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define DG_REQUIRE_PTR(p)                                                         \
+  do {                                                                            \
+    if (!(p)) return fail(ctx, DG_ERR_NULL, "%s: %s is NULL", __func__, #p);      \
+    if (!aligned16(p)) return fail(ctx, DG_ERR_ALIGN, "%s: %s is not 16-byte aligned", __func__, #p); \
+  } while (0)
+
+dg_status check_dims(dg_ctx ctx, const dg_dims *m, const char *fn) {
+  if (!m) return fail(ctx, DG_ERR_NULL, "%s: dims is NULL", fn);
+  if (m->V < 1) return fail(ctx, DG_ERR_SHAPE, "%s: V=%d must be >= 1", fn, m->V);
+  if (m->d < 32 || m->d % 32 || m->d > 16384)
+    return fail(ctx, DG_ERR_SHAPE, "%s: d=%d must be a multiple of 32 in [32, 16384]", fn, m->d);
+  if (m->C < 1 || m->C > 1024) return fail(ctx, DG_ERR_SHAPE, "%s: C=%d must be in [1, 1024]", fn, m->C);
+  if (m->Hq < 1 || m->Hkv < 1 || m->Hq % m->Hkv)
+    return fail(ctx, DG_ERR_SHAPE, "%s: Hq=%d must be a positive multiple of Hkv=%d", fn, m->Hq, m->Hkv);
+  if (m->hd != 16 && m->hd != 32 && m->hd != 64 && m->hd != 128)
+    return fail(ctx, DG_ERR_SHAPE, "%s: hd=%d must be 16, 32, 64 or 128", fn, m->hd);
+  if ((m->Hq * m->hd) % 32 || (m->Hkv * m->hd) % 8)
+    return fail(ctx, DG_ERR_SHAPE, "%s: Hq*hd=%d must be a multiple of 32", fn, m->Hq * m->hd);
+  if (m->F < 32 || m->F % 32 || m->F > 16384)
+    return fail(ctx, DG_ERR_SHAPE, "%s: F=%d must be a multiple of 32 in [32, 16384]", fn, m->F);
+  return DG_OK;
+}
+
+dg_status check_cache(dg_ctx ctx, int64_t P, int64_t Pcap, const char *fn) {
+  if (P < 0 || Pcap < 0 || P > Pcap)
+    return fail(ctx, DG_ERR_RANGE, "%s: need 0 <= P=%lld <= Pcap=%lld", fn, (long long)P, (long long)Pcap);
+  if (Pcap % 8) return fail(ctx, DG_ERR_ALIGN, "%s: Pcap=%lld must be a multiple of 8", fn, (long long)Pcap);
+  if (Pcap > (int64_t)1 << 30) return fail(ctx, DG_ERR_SHAPE, "%s: Pcap=%lld too large", fn, (long long)Pcap);
+  return DG_OK;
+}
+
+template <typename T>
+T *ws_at(void *ws, size_t off) {
+  return (T *)((char *)ws + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+dg_status dg_create(dg_ctx *out, int device, void *hip_stream) {
+  if (!out) return DG_ERR_NULL;
+  *out = nullptr;
+  dg_ctx ctx = new (std::nothrow) dg_ctx_s;
+  if (!ctx) return DG_ERR_UNSUPPORTED;
+  ctx->device = device;
+  ctx->stream = (hipStream_t)hip_stream;
+  hipError_t e = hipSetDevice(device);
+  if (e == hipSuccess) e = hipMalloc((void **)&ctx->d_status, sizeof(int));
+  if (e == hipSuccess) e = hipMemset(ctx->d_status, 0, sizeof(int));
+  if (e != hipSuccess) {
+    delete ctx;
+    return DG_ERR_HIP;
+  }
+  *out = ctx;
+  return DG_OK;
+}
+
+void dg_destroy(dg_ctx ctx) {
+  if (!ctx) return;
+  if (ctx->d_status) {
+    (void)hipSetDevice(ctx->device);
+    (void)hipStreamSynchronize(ctx->stream);
+    (void)hipFree(ctx->d_status);
+  }
+  delete ctx;
+}
+
+dg_status dg_set_stream(dg_ctx ctx, void *hip_stream) {
+  if (!ctx) return DG_ERR_NULL;
+  ctx->stream = (hipStream_t)hip_stream;
+  return DG_OK;
+}
+
+const char *dg_last_error(dg_ctx ctx) { return ctx ? ctx->err : "NULL context"; }
+
+dg_status dg_sync(dg_ctx ctx) {
+  if (!ctx) return DG_ERR_NULL;
+  hipError_t e = hipStreamSynchronize(ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "dg_sync");
+  int st = 0;
+  e = hipMemcpy(&st, ctx->d_status, sizeof(int), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(ctx, e, "dg_sync");
+  if (st == DGS_NONFINITE) return fail(ctx, DG_ERR_NONFINITE, "device saw non-finite logits");
+  if (st == DGS_RANGE) return fail(ctx, DG_ERR_RANGE, "device saw a token id outside [0, V)");
+  if (st) return fail(ctx, DG_ERR_UNSUPPORTED, "device status %d", st);
+  return DG_OK;
+}
+
+dg_status dg_clear_status(dg_ctx ctx) {
+  if (!ctx) return DG_ERR_NULL;
+  hipError_t e = hipMemsetAsync(ctx->d_status, 0, sizeof(int), ctx->stream);
+  return e == hipSuccess ? DG_OK : hip_fail(ctx, e, "dg_clear_status");
+}
+
+size_t dg_workspace_bytes(const dg_dims *m, int64_t Pcap) {
+  if (!m || check_dims(nullptr, m, "dg_workspace_bytes") != DG_OK || Pcap < 0) return 0;
+  return dg_ws_layout(m->V, m->d, m->C, m->Hq, m->Hkv, m->hd, m->F, Pcap).total;
+}
+
+float dg_temperature(int32_t k, int32_t N, float tau0, float tau1) {
+  if (N <= 1) return tau0;
+  return (float)((double)tau0 + ((double)tau1 - (double)tau0) * (double)k / (double)(N - 1));
+}
+
+dg_status dg_canvas_attn(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens,
+                         const dg_bf16 *z, const dg_bf16 *E, const dg_bf16 *Wq,
+                         const dg_bf16 *Wk, const dg_bf16 *Wv, const dg_bf16 *Wo,
+                         const dg_bf16 *Kp, const dg_bf16 *Vt, int64_t P, int64_t Pcap,
+                         void *ws, dg_bf16 *A) {
+  if (!ctx) return DG_ERR_NULL;
+  dg_status st = check_dims(ctx, dims, __func__);
+  if (st) return st;
+  if ((st = check_cache(ctx, P, Pcap, __func__))) return st;
+  DG_REQUIRE_PTR(tokens);
+  DG_REQUIRE_PTR(E);
+  DG_REQUIRE_PTR(Wq);
+  DG_REQUIRE_PTR(Wk);
+  DG_REQUIRE_PTR(Wv);
+  DG_REQUIRE_PTR(Wo);
+  DG_REQUIRE_PTR(ws);
+  DG_REQUIRE_PTR(A);
+  if (z && !aligned16(z)) return fail(ctx, DG_ERR_ALIGN, "%s: z is not 16-byte aligned", __func__);
+  if (P > 0) {
+    DG_REQUIRE_PTR(Kp);
+    DG_REQUIRE_PTR(Vt);
+  }
+  const dg_dims &m = *dims;
+  const DgWs w = dg_ws_layout(m.V, m.d, m.C, m.Hq, m.Hkv, m.hd, m.F, Pcap);
+  const int qd = m.Hq * m.hd, kd = m.Hkv * m.hd;
+  u16 *q = ws_at<u16>(ws, w.q), *kc = ws_at<u16>(ws, w.kc), *vct = ws_at<u16>(ws, w.vct);
+  u16 *o = ws_at<u16>(ws, w.o);
+
+  // Q, K, V of the denoiser input X = bf16(E[tokens] + z).
+  GemmArgs g{};
+  g.M = m.C;
+  g.K = m.d;
+  g.tokens = tokens;
+  g.E = E;
+  g.z = z;
+  g.V = m.V;
+  g.status = ctx->d_status;
+  g.nseg = 3;
+  g.seg[0] = GemmSeg{Wq, qd, q, qd, 0, 1, INT_MAX, m.C, 0};
+  g.seg[1] = GemmSeg{Wk, kd, kc, kd, 0, 1, INT_MAX, w.Cpad, 0};
+  g.seg[2] = GemmSeg{Wv, kd, vct, 1, 0, w.Cpad, INT_MAX, w.Cpad, 0};
+  hipError_t e = dg_launch_gemm(g, ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "dg_canvas_attn(qkv)");
+
+  AttnArgs at{};
+  at.Q = q;
+  at.Kp = Kp;
+  at.Vt = Vt;
+  at.Kc = kc;
+  at.Vct = vct;
+  at.P = P;
+  at.Pcap = Pcap;
+  at.C = m.C;
+  at.Cpad = w.Cpad;
+  at.Hq = m.Hq;
+  at.Hkv = m.Hkv;
+  at.hd = m.hd;
+  at.nsplit = dg_attn_nsplit(m.Hkv, m.Hq, m.C, P);
+  at.scale_log2 = (float)(1.4426950408889634 / sqrt((double)m.hd));
+  at.po = ws_at<float>(ws, w.po);
+  at.pml = ws_at<float>(ws, w.pml);
+  at.O = o;
+  e = dg_launch_attention(at, ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "dg_canvas_attn(attention)");
+
+  GemmArgs go{};
+  go.M = m.C;
+  go.K = qd;
+  go.A = o;
+  go.nseg = 1;
+  go.seg[0] = GemmSeg{Wo, m.d, A, m.d, 0, 1, INT_MAX, m.C, 0};
+  e = dg_launch_gemm(go, ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "dg_canvas_attn(wo)");
+  return DG_OK;
+}
+
+dg_status dg_logits_entropy(dg_ctx ctx, const dg_dims *dims, const dg_bf16 *H,
+                            const dg_bf16 *E, float tau, void *ws, float *entropy,
+                            int32_t *argmax) {
+  if (!ctx) return DG_ERR_NULL;
+  dg_status st = check_dims(ctx, dims, __func__);
+  if (st) return st;
+  DG_REQUIRE_PTR(H);
+  DG_REQUIRE_PTR(E);
+  DG_REQUIRE_PTR(ws);
+  DG_REQUIRE_PTR(entropy);
+  DG_REQUIRE_PTR(argmax);
+  if (!(tau > 0.f) || !isfinite(tau)) return fail(ctx, DG_ERR_RANGE, "%s: tau=%g must be > 0", __func__, tau);
+  const dg_dims &m = *dims;
+  const DgWs w = dg_ws_layout(m.V, m.d, m.C, m.Hq, m.Hkv, m.hd, m.F, 0);
+  LogitsArgs a{};
+  a.H = H;
+  a.E = E;
+  a.V = m.V;
+  a.d = m.d;
+  a.C = m.C;
+  a.Cpad = w.Cpad;
+  a.T = w.T;
+  a.inv_tau = 1.0f / tau;
+  a.ptilde = ws_at<u16>(ws, w.ptilde);
+  a.tmax = ws_at<float>(ws, w.tmax);
+  a.tsum = ws_at<float>(ws, w.tsum);
+  a.tent = ws_at<float>(ws, w.tent);
+  a.targ = ws_at<int>(ws, w.targ);
+  a.fac = ws_at<float>(ws, w.fac);
+  a.entropy = entropy;
+  a.argmax = argmax;
+  a.status = ctx->d_status;
+  hipError_t e = dg_launch_logits(a, ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "dg_logits_entropy");
+  ctx->p0_ws = ws;
+  ctx->p0_dims = m;
+  ctx->p0_valid = true;
+  return DG_OK;
+}
+
+dg_status dg_entropy_accept(dg_ctx ctx, int32_t B, int32_t C, const float *entropy, float b,
+                            uint8_t *accept, int32_t *n_accept) {
+  if (!ctx) return DG_ERR_NULL;
+  if (B < 1 || C < 1 || C > 1024) return fail(ctx, DG_ERR_SHAPE, "%s: need B >= 1, 1 <= C <= 1024", __func__);
+  if (!entropy || !accept || !n_accept) return fail(ctx, DG_ERR_NULL, "%s: NULL buffer", __func__);
+  if (!(b >= 0.f && b < 65536.f)) return fail(ctx, DG_ERR_RANGE, "%s: b=%g must be in [0, 65536)", __func__, b);
+  const uint64_t budget = (uint64_t)floor((double)b * 4294967296.0);
+  hipError_t e = dg_launch_accept(B, C, entropy, budget, accept, n_accept, ctx->stream);
+  return e == hipSuccess ? DG_OK : hip_fail(ctx, e, "dg_entropy_accept");
+}
+
+dg_status dg_renoise(dg_ctx ctx, int32_t B, int32_t C, int32_t V, const int32_t *argmax,
+                     const uint8_t *accept, uint64_t seed, uint32_t canvas_base, uint32_t step,
+                     int32_t *tokens) {
+  if (!ctx) return DG_ERR_NULL;
+  if (B < 1 || C < 1 || V < 1) return fail(ctx, DG_ERR_SHAPE, "%s: need B, C, V >= 1", __func__);
+  if (!tokens) return fail(ctx, DG_ERR_NULL, "%s: tokens is NULL", __func__);
+  if (accept && !argmax) return fail(ctx, DG_ERR_NULL, "%s: argmax is NULL", __func__);
+  hipError_t e = dg_launch_renoise(B, C, V, argmax, accept, seed, canvas_base, step, tokens, ctx->stream);
+  return e == hipSuccess ? DG_OK : hip_fail(ctx, e, "dg_renoise");
+}
+
+dg_status dg_selfcond(dg_ctx ctx, const dg_dims *dims, void *ws, const dg_bf16 *E,
+                      const dg_bf16 *W1, const dg_bf16 *W2, dg_bf16 *z) {
+  if (!ctx) return DG_ERR_NULL;
+  dg_status st = check_dims(ctx, dims, __func__);
+  if (st) return st;
+  DG_REQUIRE_PTR(ws);
+  DG_REQUIRE_PTR(E);
+  DG_REQUIRE_PTR(W1);
+  DG_REQUIRE_PTR(W2);
+  DG_REQUIRE_PTR(z);
+  const dg_dims &m = *dims;
+  if (!ctx->p0_valid || ctx->p0_ws != ws || memcmp(&ctx->p0_dims, &m, sizeof m) != 0)
+    return fail(ctx, DG_ERR_STATE, "%s: ws does not hold p0 of a dg_logits_entropy with these dims", __func__);
+  const DgWs w = dg_ws_layout(m.V, m.d, m.C, m.Hq, m.Hkv, m.hd, m.F, 0);
+  SelfcondArgs a{};
+  a.ptilde = ws_at<u16>(ws, w.ptilde);
+  a.fac = ws_at<float>(ws, w.fac);
+  a.E = E;
+  a.V = m.V;
+  a.d = m.d;
+  a.C = m.C;
+  a.Cpad = w.Cpad;
+  a.T = w.T;
+  a.nsc = w.nsc;
+  a.ps = ws_at<float>(ws, w.ps);
+  a.s = ws_at<u16>(ws, w.s);
+  hipError_t e = dg_launch_selfcond(a, ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "dg_selfcond(p0 E)");
+
+  u16 *gbuf = ws_at<u16>(ws, w.g);
+  GemmArgs g1{};
+  g1.M = m.C;
+  g1.K = m.d;
+  g1.A = a.s;
+  g1.gelu = 1;
+  g1.nseg = 1;
+  g1.seg[0] = GemmSeg{W1, m.F, gbuf, m.F, 0, 1, INT_MAX, m.C, 0};
+  e = dg_launch_gemm(g1, ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "dg_selfcond(W1)");
+  GemmArgs g2{};
+  g2.M = m.C;
+  g2.K = m.F;
+  g2.A = gbuf;
+  g2.nseg = 1;
+  g2.seg[0] = GemmSeg{W2, m.d, z, m.d, 0, 1, INT_MAX, m.C, 0};
+  e = dg_launch_gemm(g2, ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "dg_selfcond(W2)");
+  return DG_OK;
+}
+
+dg_status dg_stop_test(dg_ctx ctx, int32_t B, int32_t C, const float *entropy,
+                       const int32_t *argmax, const int32_t *prev_argmax, float thr, int32_t step,
+                       int32_t N, int32_t *flag) {
+  if (!ctx) return DG_ERR_NULL;
+  if (B < 1 || C < 1 || C > 1024) return fail(ctx, DG_ERR_SHAPE, "%s: need B >= 1, 1 <= C <= 1024", __func__);
+  if (!entropy || !argmax || !flag) return fail(ctx, DG_ERR_NULL, "%s: NULL buffer", __func__);
+  if (!(thr >= 0.f && thr < 65536.f)) return fail(ctx, DG_ERR_RANGE, "%s: thr=%g must be in [0, 65536)", __func__, thr);
+  if (step < 0 || N < 1) return fail(ctx, DG_ERR_RANGE, "%s: need step >= 0, N >= 1", __func__);
+  const uint64_t limit = (uint64_t)floor((double)thr * (double)C * 4294967296.0);
+  hipError_t e = dg_launch_stop(B, C, entropy, argmax, prev_argmax, limit, step, N, flag, ctx->stream);
+  return e == hipSuccess ? DG_OK : hip_fail(ctx, e, "dg_stop_test");
+}
+
+dg_status dg_commit_kv(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens, const dg_bf16 *E,
+                       const dg_bf16 *Wk, const dg_bf16 *Wv, dg_bf16 *Kp, dg_bf16 *Vt, int64_t P,
+                       int64_t Pcap, int64_t *P_out) {
+  if (!ctx) return DG_ERR_NULL;
+  dg_status st = check_dims(ctx, dims, __func__);
+  if (st) return st;
+  if ((st = check_cache(ctx, P, Pcap, __func__))) return st;
+  DG_REQUIRE_PTR(tokens);
+  DG_REQUIRE_PTR(E);
+  DG_REQUIRE_PTR(Wk);
+  DG_REQUIRE_PTR(Wv);
+  DG_REQUIRE_PTR(Kp);
+  DG_REQUIRE_PTR(Vt);
+  if (!P_out) return fail(ctx, DG_ERR_NULL, "%s: P_out is NULL", __func__);
+  const dg_dims &m = *dims;
+  if (P + m.C > Pcap)
+    return fail(ctx, DG_ERR_CAPACITY, "%s: P=%lld + C=%d exceeds Pcap=%lld", __func__, (long long)P, m.C,
+                (long long)Pcap);
+  const int hd = m.hd, kd = m.Hkv * m.hd;
+  GemmArgs g{};
+  g.M = m.C;
+  g.K = m.d;
+  g.tokens = tokens;
+  g.E = E;
+  g.V = m.V;
+  g.status = ctx->d_status;
+  g.nseg = 2;
+  // K rows: Kp[g][P + m][e] = base + m*hd + g*Pcap*hd + e, n = g*hd + e
+  g.seg[0] = GemmSeg{Wk, kd, Kp + P * hd, hd, Pcap * hd, 1, hd, m.C, 0};
+  // V columns: Vt[g][e][P + m] = base + (g*hd + e)*Pcap + m = base + n*Pcap + m
+  g.seg[1] = GemmSeg{Wv, kd, Vt + P, 1, 0, Pcap, INT_MAX, m.C, 0};
+  hipError_t e = dg_launch_gemm(g, ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "dg_commit_kv");
+  *P_out = P + m.C;
+  return DG_OK;
+}
+
+}  // extern "C"

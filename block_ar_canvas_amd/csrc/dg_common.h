@@ -1,0 +1,229 @@
+// Shared device helpers and the workspace layout of the canvas-denoise library.
+//
+// Matrix-core convention used by every kernel (CDNA4 / gfx950, wave64):
+//   v_mfma_f32_32x32x16_bf16 computes D[32x32] += A[32x16] * B[16x32] where lane l
+//   holds A[l%32][8*(l/32) .. +8], B[8*(l/32) .. +8][l%32], and accumulator register r
+//   holds D[8*(r/4) + 4*(l/32) + r%4][l%32].
+// Kernels put the "long" operand (vocabulary rows, keys, weight rows) in A and the
+// canvas-side operand in B, so each lane's accumulator column is one canvas position
+// (or query row): row reductions over vocabulary / keys stay inside a lane pair.
+//
+// Row permutation trick: when an accumulator tile is fed back into a second MFMA as
+// its B operand (attention probabilities into P.V, softmax probabilities into p0.E),
+// A-row i of the first MFMA is loaded from physical row pi(i) = i with bits 2 and 3
+// swapped. Then accumulator registers [8s, 8s+8) of lane (c, h) hold physical rows
+// 16s + 8h + [0, 8): exactly the B fragment of k-step s of the second MFMA, in
+// natural order, with no data movement.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+typedef uint16_t u16;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+#define DG_DEV __device__ __forceinline__
+
+DG_DEV f32x16_t mfma_32x32x16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Physical row of MFMA A-row i (swap bits 2 and 3), see the header comment.
+DG_DEV int perm_row(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+
+// Row of accumulator register r for the lane half h (natural A-row order).
+DG_DEV int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+// Physical row of accumulator register r when A rows were loaded through perm_row.
+DG_DEV int acc_row_perm(int r, int h) { return 16 * (r >> 3) + 8 * h + (r & 7); }
+
+DG_DEV float bf16_to_f32(u16 b) { return __uint_as_float((uint32_t)b << 16); }
+DG_DEV float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+DG_DEV float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// float -> bf16, round to nearest even; NaN stays NaN.
+DG_DEV u16 f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u16)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (u16)(u >> 16);
+}
+DG_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+DG_DEV float wave_xor32(float v) { return __shfl_xor(v, 32, 64); }
+DG_DEV int wave_xor32(int v) { return __shfl_xor(v, 32, 64); }
+
+// Sticky device status codes (mirror dg_status).
+#define DGS_RANGE 4
+#define DGS_NONFINITE 7
+DG_DEV void set_status(int *status, int code) {
+  if (status) atomicMax(status, code);
+}
+
+// ------------------------------------------------------------------ tiling constants
+#define DG_CT 32        // canvas columns per MFMA tile
+#define DG_BV 128       // vocabulary rows per logits tile (one set of tile statistics)
+#define DG_KT 32        // keys per attention tile
+
+static inline int64_t dg_round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+static inline int64_t dg_cdiv(int64_t x, int64_t m) { return (x + m - 1) / m; }
+
+// ------------------------------------------------------------------ workspace layout
+// All regions are 256-byte aligned. Sizes depend on the dims and the cache capacity
+// only, so one workspace serves every step of a run.
+struct DgWs {
+  int Cpad;        // C rounded up to 32
+  int Vpad;        // V rounded up to DG_BV
+  int T;           // vocabulary tiles = Vpad / DG_BV
+  int nsc;         // self-conditioning split-K parts over the vocabulary
+  int nsplit_max;  // attention split-K parts at Pcap
+  size_t ptilde;   // bf16 p~ in MFMA fragment order: [Cpad/32][Vpad/16][64 lanes][8]
+  size_t tmax, tsum, tent, targ;  // per-(tile, column) statistics [T][Cpad]
+  size_t fac;      // per-(tile, column) p0 scale exp(m_t - m) / Z    [T][Cpad]
+  size_t q;        // Q   bf16 [Cpad][Hq*hd]
+  size_t kc;       // canvas keys   bf16 [Cpad][Hkv*hd]
+  size_t vct;      // canvas values bf16 [Hkv*hd][Cpad] (transposed)
+  size_t o;        // attention output before Wo, bf16 [Cpad][Hq*hd]
+  size_t po;       // attention partial O fp32 [nsplit][Hq][Cpad][hd]
+  size_t pml;      // attention partial (max, sum) fp32 [nsplit][Hq][Cpad][2]
+  size_t ps;       // self-cond partial s fp32 [nsc][Cpad][d]
+  size_t s;        // s = p0 E rounded to bf16 [Cpad][d]
+  size_t g;        // GELU(s W1^T) bf16 [Cpad][F]
+  size_t total;
+};
+
+// Attention split count for a given number of cached tokens (non-decreasing in P).
+static inline int dg_attn_nsplit(int Hkv, int Hq, int C, int64_t P) {
+  const int64_t rows = (int64_t)(Hq / Hkv) * C;
+  const int64_t nq = dg_cdiv(rows, 256);
+  const int64_t tiles = dg_cdiv(dg_round_up(C, DG_CT), DG_KT) + dg_cdiv(P, DG_KT);
+  int64_t ns = dg_cdiv(512, (int64_t)Hkv * nq);       // aim at >= 512 workgroups
+  const int64_t by_len = dg_cdiv(tiles, 8);              // >= 8 key tiles per part
+  if (ns > by_len) ns = by_len;
+  if (ns < 1) ns = 1;
+  if (ns > 256) ns = 256;
+  return (int)ns;
+}
+
+static inline int dg_selfcond_nsplit(int d, int Cpad, int T) {
+  const int64_t jt = dg_cdiv(d, 128) * dg_cdiv(Cpad, 256);
+  int64_t ns = dg_cdiv(512, jt);
+  const int64_t by_len = T / 16;                        // >= 16 tiles (2048 ids) per part
+  if (ns > by_len) ns = by_len;
+  if (ns < 1) ns = 1;
+  return (int)ns;
+}
+
+static inline DgWs dg_ws_layout(int V, int d, int C, int Hq, int Hkv, int hd, int F,
+                                int64_t Pcap) {
+  DgWs w;
+  w.Cpad = (int)dg_round_up(C, DG_CT);
+  w.Vpad = (int)dg_round_up(V, DG_BV);
+  w.T = w.Vpad / DG_BV;
+  w.nsc = dg_selfcond_nsplit(d, w.Cpad, w.T);
+  w.nsplit_max = dg_attn_nsplit(Hkv, Hq, C, Pcap);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = (size_t)dg_round_up((int64_t)(off + bytes), 256);
+    return at;
+  };
+  const size_t CT = (size_t)w.T * w.Cpad;
+  w.ptilde = take((size_t)w.Cpad * w.Vpad * 2);
+  w.tmax = take(CT * 4);
+  w.tsum = take(CT * 4);
+  w.tent = take(CT * 4);
+  w.targ = take(CT * 4);
+  w.fac = take(CT * 4);
+  w.q = take((size_t)w.Cpad * Hq * hd * 2);
+  w.kc = take((size_t)w.Cpad * Hkv * hd * 2);
+  w.vct = take((size_t)w.Cpad * Hkv * hd * 2);
+  w.o = take((size_t)w.Cpad * Hq * hd * 2);
+  w.ps = take((size_t)w.nsc * w.Cpad * d * 4);
+  w.s = take((size_t)w.Cpad * d * 2);
+  w.g = take((size_t)w.Cpad * F * 2);
+  // Regions sized by the cache capacity come last, so every other offset is the same
+  // whatever Pcap the layout is computed for.
+  w.po = take((size_t)w.nsplit_max * Hq * w.Cpad * hd * 4);
+  w.pml = take((size_t)w.nsplit_max * Hq * w.Cpad * 2 * 4);
+  w.total = off;
+  return w;
+}
+
+// ------------------------------------------------------------------ launcher API
+// Host-side launchers implemented by the kernel translation units.
+struct GemmSeg {
+  const u16 *W;        // [N][K] weight rows (output features x input features)
+  int N;               // output features of this segment
+  u16 *out;            // output: out + m*sm + (n/seg)*sg + (n%seg)*se
+  int64_t sm, sg, se;
+  int seg;
+  int m_store;         // rows m >= m_store are computed but not stored
+  int nblk0;           // first n-block of this segment in the grid
+};
+struct GemmArgs {
+  int M, K;
+  const u16 *A;        // plain activation [M][K], or NULL for the embedding gather
+  const int *tokens;   // gather: row m = E[tokens[m]] (+ z[m]), rounded to bf16
+  const u16 *E;
+  const u16 *z;        // NULL: no self-conditioning term
+  int V;
+  int *status;
+  int gelu;            // apply exact GELU before storing
+  int nseg;
+  GemmSeg seg[3];
+};
+hipError_t dg_launch_gemm(const GemmArgs &a, hipStream_t st);
+
+struct AttnArgs {
+  const u16 *Q;        // [Cpad][Hq*hd]
+  const u16 *Kp;       // [Hkv][Pcap][hd]
+  const u16 *Vt;       // [Hkv][hd][Pcap]
+  const u16 *Kc;       // [Cpad][Hkv*hd]
+  const u16 *Vct;      // [Hkv*hd][Cpad]
+  int64_t P, Pcap;
+  int C, Cpad, Hq, Hkv, hd;
+  int nsplit;
+  float scale_log2;    // log2(e) / sqrt(hd)
+  float *po;           // [nsplit][Hq][Cpad][hd]
+  float *pml;          // [nsplit][Hq][Cpad][2]
+  u16 *O;              // merged output [Cpad][Hq*hd]
+};
+hipError_t dg_launch_attention(const AttnArgs &a, hipStream_t st);
+
+struct LogitsArgs {
+  const u16 *H;        // [C][d]
+  const u16 *E;        // [V][d]
+  int V, d, C, Cpad, T;
+  float inv_tau;
+  u16 *ptilde;
+  float *tmax, *tsum, *tent;
+  int *targ;
+  float *fac;
+  float *entropy;      // [C]
+  int *argmax;         // [C]
+  int *status;
+};
+hipError_t dg_launch_logits(const LogitsArgs &a, hipStream_t st);
+
+struct SelfcondArgs {
+  const u16 *ptilde;
+  const float *fac;
+  const u16 *E;        // [V][d]
+  int V, d, C, Cpad, T, nsc;
+  float *ps;           // [nsc][Cpad][d]
+  u16 *s;              // [Cpad][d]
+};
+hipError_t dg_launch_selfcond(const SelfcondArgs &a, hipStream_t st);
+
+hipError_t dg_launch_accept(int B, int C, const float *ent, uint64_t budget, uint8_t *acc,
+                            int *nacc, hipStream_t st);
+hipError_t dg_launch_renoise(int B, int C, int V, const int *am, const uint8_t *acc,
+                             uint64_t seed, uint32_t canvas_base, uint32_t step, int *tok,
+                             hipStream_t st);
+hipError_t dg_launch_stop(int B, int C, const float *ent, const int *am, const int *prev,
+                          uint64_t limit, int step, int N, int *flag, hipStream_t st);

@@ -1,0 +1,177 @@
+// Integer part of the sampler: acceptance, renoise, stop test.
+//
+// Entropy-bounded acceptance (DiffusionGemma Technical Report page, "Method steps"
+// (3): sort by entropy ascending and accept within the cumulative entropy budget
+// b = 0.1; "Technical novelty": MaskGIT-like entropy-bounded acceptance). The budget
+// sum runs in 2^-32 fixed point, q = ceil(h * 2^32) and budget floor(b * 2^32), so a
+// parallel scan gives the same bits as a sequential loop and the accepted real-valued
+// entropy sum never exceeds b. One workgroup per canvas: a bitonic sort of the 64-bit
+// keys (entropy bits << 32 | position) in LDS, then an inclusive scan of q in sorted
+// order; the accepted set is the sorted prefix whose scan stays within the budget.
+//
+// Uniform renoise (Technical Report page, "Method steps" (2)-(3); Google
+// "DiffusionGemma explained", "Uniform State Diffusion"): rejected positions get a
+// token drawn uniformly from the whole vocabulary. The generator is Philox4x64-10
+// (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC'11),
+// counter-based, so every (seed, canvas, step, position) draw is independent of
+// launch shape and a resumed run needs no generator state.
+//
+// Stop test (Technical Report page, "Method steps" (4)): the canvas stops when its
+// mean entropy is <= the threshold and the argmax did not change since the previous
+// step; the step cap commits anyway.
+#include "dg_common.h"
+
+namespace {
+
+constexpr float H_LIMIT = 65536.0f;
+constexpr uint64_t Q_SENTINEL = 1ull << 48;
+
+// Fixed-point entropy; out-of-domain entropies (NaN, +Inf, >= 2^16) get the sentinel.
+DG_DEV uint64_t entropy_q(float h) {
+  if (!(h < H_LIMIT)) return Q_SENTINEL;
+  if (!(h > 0.f)) return 0;
+  return (uint64_t)ceil((double)h * 4294967296.0);
+}
+
+__global__ __launch_bounds__(1024) void accept_kernel(int C, const float *ent, uint64_t budget,
+                                                      uint8_t *acc, int *nacc) {
+  __shared__ uint64_t key[1024];
+  __shared__ uint64_t scan[2][1024];
+  __shared__ int cnt[1024];
+  const int b = blockIdx.x, tid = threadIdx.x, n = blockDim.x;
+  const float *e = ent + (int64_t)b * C;
+
+  uint64_t k = ~0ull;
+  if (tid < C) {
+    const float h = e[tid];
+    uint32_t bits;
+    if (!(h < H_LIMIT)) bits = 0xFFFFFFFFu;
+    else bits = h > 0.f ? __float_as_uint(h) : 0u;
+    k = ((uint64_t)bits << 32) | (uint32_t)tid;
+  }
+  key[tid] = k;
+  __syncthreads();
+  // Bitonic sort, ascending, n = power of two.
+  for (int size = 2; size <= n; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const int partner = tid ^ stride;
+      if (partner > tid) {
+        const uint64_t x = key[tid], y = key[partner];
+        const bool up = (tid & size) == 0;
+        if ((x > y) == up) { key[tid] = y; key[partner] = x; }
+      }
+      __syncthreads();
+    }
+  }
+  k = key[tid];
+  const bool real = k != ~0ull;
+  uint64_t q = 0;
+  if (real) {
+    const uint32_t bits = (uint32_t)(k >> 32);
+    q = bits == 0xFFFFFFFFu ? Q_SENTINEL : entropy_q(__uint_as_float(bits));
+  }
+  // Inclusive scan (Hillis-Steele, double-buffered).
+  int cur = 0;
+  scan[0][tid] = q;
+  __syncthreads();
+  for (int off = 1; off < n; off <<= 1) {
+    uint64_t v = scan[cur][tid];
+    if (tid >= off) v += scan[cur][tid - off];
+    scan[cur ^ 1][tid] = v;
+    cur ^= 1;
+    __syncthreads();
+  }
+  const bool take = real && scan[cur][tid] <= budget;
+  if (real) acc[(int64_t)b * C + (uint32_t)k] = take ? 1 : 0;
+  cnt[tid] = take ? 1 : 0;
+  __syncthreads();
+  for (int w = n >> 1; w > 0; w >>= 1) {
+    if (tid < w) cnt[tid] += cnt[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0 && nacc) nacc[b] = cnt[0];
+}
+
+// Philox4x64-10.
+DG_DEV void philox4x64_10(uint64_t c[4], uint64_t k0, uint64_t k1) {
+  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t hi0 = __umul64hi(M0, c[0]), lo0 = M0 * c[0];
+    const uint64_t hi1 = __umul64hi(M1, c[2]), lo1 = M1 * c[2];
+    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0; c[1] = lo1; c[2] = n2; c[3] = lo0;
+    k0 += W0;
+    k1 += W1;
+  }
+}
+
+__global__ __launch_bounds__(256) void renoise_kernel(int B, int C, int V, const int *am,
+                                                      const uint8_t *acc, uint64_t seed,
+                                                      uint32_t canvas_base, uint32_t step,
+                                                      int *tok) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)B * C) return;
+  const int b = (int)(i / C), pos = (int)(i % C);
+  if (acc && acc[i]) {
+    tok[i] = am[i];
+    return;
+  }
+  uint64_t c[4] = {(uint64_t)pos, (uint64_t)step, acc ? 0ull : 1ull, 0ull};
+  philox4x64_10(c, seed, (uint64_t)(canvas_base + (uint32_t)b));
+  tok[i] = (int)__umul64hi(c[0], (uint64_t)V);
+}
+
+__global__ __launch_bounds__(256) void stop_kernel(int C, const float *ent, const int *am,
+                                                   const int *prev, uint64_t limit, int step,
+                                                   int N, int *flag) {
+  __shared__ uint64_t ssum[256];
+  __shared__ int sok[256];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  uint64_t s = 0;
+  int ok = 1;
+  for (int i = tid; i < C; i += 256) {
+    const int64_t o = (int64_t)b * C + i;
+    const float h = ent[o];
+    if (!(h < H_LIMIT)) ok = 0;
+    else s += entropy_q(h);
+    if (prev && am[o] != prev[o]) ok = 0;
+  }
+  ssum[tid] = s;
+  sok[tid] = ok;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) { ssum[tid] += ssum[tid + w]; sok[tid] &= sok[tid + w]; }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const bool stop = step >= 1 && prev != nullptr && sok[0] && ssum[0] <= limit;
+    flag[b] = stop ? 1 : (step >= N - 1 ? 2 : 0);
+  }
+}
+
+}  // namespace
+
+hipError_t dg_launch_accept(int B, int C, const float *ent, uint64_t budget, uint8_t *acc,
+                            int *nacc, hipStream_t st) {
+  int n = 64;
+  while (n < C) n <<= 1;
+  hipLaunchKernelGGL(accept_kernel, dim3(B), dim3(n), 0, st, C, ent, budget, acc, nacc);
+  return hipGetLastError();
+}
+
+hipError_t dg_launch_renoise(int B, int C, int V, const int *am, const uint8_t *acc,
+                             uint64_t seed, uint32_t canvas_base, uint32_t step, int *tok,
+                             hipStream_t st) {
+  const int64_t n = (int64_t)B * C;
+  hipLaunchKernelGGL(renoise_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, B, C, V,
+                     am, acc, seed, canvas_base, step, tok);
+  return hipGetLastError();
+}
+
+hipError_t dg_launch_stop(int B, int C, const float *ent, const int *am, const int *prev,
+                          uint64_t limit, int step, int N, int *flag, hipStream_t st) {
+  hipLaunchKernelGGL(stop_kernel, dim3(B), dim3(256), 0, st, C, ent, am, prev, limit, step, N, flag);
+  return hipGetLastError();
+}

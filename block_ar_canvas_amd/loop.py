@@ -1,0 +1,90 @@
+"""Block-autoregressive canvas loop over the libdg calls.
+
+The loop follows the DiffusionGemma inference steps (Technical Report page, "Method
+steps" (2)-(5); tutorial chapter "DiffusionGemma", data-flow pseudocode): initialize
+a canvas with uniform tokens and z = 0, run at most N denoise steps (attention,
+sampler head, acceptance, renoise, self-conditioning, stop test), then commit the
+finalized block x0 = argmax to the KV cache and start the next canvas.
+
+This module only sequences calls and owns the device buffers of one canvas; every
+step of the arithmetic is a libdg kernel. The sampler head reads hidden states from
+a caller-supplied source (the synthetic driver standing in for the denoiser stack).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import STOP_GO, Context, Dims, temperature, workspace_bytes
+
+
+class CanvasLoop:
+    """Device state and buffers for denoising canvases of one model/cache shape.
+
+    weights: dict of bf16 device tensors E, Wq, Wk, Wv, Wo, W1, W2 ([out, in] layout).
+    Kp [Hkv, Pcap, hd] and Vt [Hkv, hd, Pcap] bf16 device tensors: the KV cache.
+    """
+
+    def __init__(self, ctx: Context, dims, weights, Kp, Vt, P: int, *, N: int, seed: int,
+                 b: float = 0.1, thr: float = 0.005, tau0: float = 0.8, tau1: float = 0.4):
+        self.ctx, self.dims = ctx, Dims.of(dims)
+        self.W, self.Kp, self.Vt, self.P = weights, Kp, Vt, int(P)
+        self.N, self.seed, self.b, self.thr, self.tau0, self.tau1 = N, seed, b, thr, tau0, tau1
+        dev = Kp.device
+        C, d = self.dims.C, self.dims.d
+        self.ws = torch.empty(workspace_bytes(self.dims, Kp.shape[1]), dtype=torch.uint8, device=dev)
+        self.tokens = torch.empty(C, dtype=torch.int32, device=dev)
+        self.z = torch.zeros(C, d, dtype=torch.bfloat16, device=dev)
+        self.A = torch.empty(C, d, dtype=torch.bfloat16, device=dev)
+        self.entropy = torch.empty(C, dtype=torch.float32, device=dev)
+        self.argmax = [torch.empty(C, dtype=torch.int32, device=dev) for _ in range(2)]
+        self.accept = torch.empty(C, dtype=torch.uint8, device=dev)
+        self.n_accept = torch.empty(1, dtype=torch.int32, device=dev)
+        self.flag = torch.empty(1, dtype=torch.int32, device=dev)
+        self.flag_host = torch.empty(1, dtype=torch.int32, pin_memory=True)
+
+    def init_canvas(self, canvas: int):
+        """Uniform random canvas (init stream) and z = 0."""
+        self.ctx.renoise(self.dims.V, None, None, self.seed, canvas, 0, self.tokens)
+        self.canvas = canvas
+
+    def step(self, k: int, H):
+        """One denoise step k on hidden states H [C, d]; leaves the flag on the device."""
+        W, dm = self.W, self.dims
+        am, prev = self.argmax[k & 1], (self.argmax[(k - 1) & 1] if k > 0 else None)
+        self.ctx.canvas_attn(dm, self.tokens, self.z if k > 0 else None, W["E"], W["Wq"], W["Wk"],
+                             W["Wv"], W["Wo"], self.Kp, self.Vt, self.P, self.ws, self.A)
+        tau = temperature(k, self.N, self.tau0, self.tau1)
+        self.ctx.logits_entropy(dm, H, W["E"], tau, self.ws, self.entropy, am)
+        self.ctx.entropy_accept(self.entropy, self.b, self.accept, self.n_accept)
+        self.ctx.renoise(dm.V, am, self.accept, self.seed, self.canvas, k, self.tokens)
+        self.ctx.selfcond(dm, self.ws, W["E"], W["W1"], W["W2"], self.z)
+        self.ctx.stop_test(self.entropy, am, prev, self.thr, k, self.N, self.flag)
+        return am
+
+    def read_flag(self) -> int:
+        self.flag_host.copy_(self.flag, non_blocking=True)
+        torch.cuda.current_stream().synchronize()
+        return int(self.flag_host[0])
+
+    def commit(self, x0):
+        self.P = self.ctx.commit_kv(self.dims, x0, self.W["E"], self.W["Wk"], self.W["Wv"],
+                                    self.Kp, self.Vt, self.P)
+        return self.P
+
+    def run_canvas(self, canvas: int, hidden, on_step=None):
+        """Init, denoise until the stop test or the cap, commit. Returns steps run.
+
+        hidden(k) -> H_k device tensor; on_step(k, loop) is called after each step
+        (before the flag is read), e.g. to record intermediate state.
+        """
+        self.init_canvas(canvas)
+        self.z.zero_()
+        am = None
+        for k in range(self.N):
+            am = self.step(k, hidden(k))
+            if on_step is not None:
+                on_step(k, self)
+            if self.read_flag() != STOP_GO:
+                break
+        self.commit(am)
+        return k + 1

@@ -1,0 +1,179 @@
+/*
+ * dg.h - C ABI of the MI355X (gfx950) canvas-denoise step of a block-autoregressive
+ * uniform-state text diffusion model (DiffusionGemma's sampler loop).
+ *
+ * One denoise step of the 256-token canvas is, in call order:
+ *   dg_canvas_attn     bidirectional canvas attention over the static prefix KV cache
+ *   dg_logits_entropy  lm_head logits fused with tempered softmax, entropy and argmax
+ *   dg_entropy_accept  entropy-bounded acceptance (segmented sort + fixed-point scan)
+ *   dg_renoise         accepted positions keep the argmax, the rest are redrawn
+ *   dg_selfcond        self-conditioning z = FFW(p0 . E)
+ *   dg_stop_test       adaptive stop (mean entropy and stable argmax) / step cap
+ * and, once per canvas, dg_commit_kv appends the finalized block to the KV cache.
+ * The method is the DiffusionGemma inference loop as summarized by the
+ * "DiffusionGemma Technical Report" page (paper.rainbus.top/paper/2608.00146),
+ * section "Method steps" (1)-(5), with the sampler hyper-parameters of its
+ * "Reproducibility" section (canvas 256, N = 48, b = 0.1, stop 0.005, tau 0.8 -> 0.4).
+ *
+ * Conventions for every call
+ *  - Tensor arguments are DEVICE pointers owned by the caller (contiguous, row-major,
+ *    16-byte aligned). bf16 values are raw IEEE bfloat16 bit patterns (dg_bf16).
+ *  - Weights use the [out_features, in_features] row-major layout.
+ *  - The KV cache of one layer is two arrays:
+ *        Kp [Hkv][Pcap][hd]   keys, one row per cached token
+ *        Vt [Hkv][hd][Pcap]   values stored transposed (token index fastest)
+ *    Rows / columns [0, P) hold the prefix; [P, Pcap) is free capacity.
+ *  - Calls validate their arguments on the host, enqueue work on the context's HIP
+ *    stream and return without waiting. No call allocates or frees device memory;
+ *    scratch space comes from the caller's workspace (dg_workspace_bytes).
+ *  - On a non-OK return nothing was enqueued; dg_last_error() describes the problem.
+ *  - Conditions only the device can see (a token id outside [0, V), non-finite
+ *    logits) set a sticky status word in the context, reported by dg_sync().
+ *  - A context is used by one host thread at a time. No C++ exception crosses the ABI.
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t dg_bf16;
+typedef struct dg_ctx_s *dg_ctx;
+
+typedef enum {
+  DG_OK = 0,
+  DG_ERR_NULL = 1,        /* a required pointer is NULL                                  */
+  DG_ERR_SHAPE = 2,       /* a dimension is out of the supported set                     */
+  DG_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned / Pcap not a multiple of 8 */
+  DG_ERR_RANGE = 4,       /* a scalar is out of range (tau <= 0, b < 0, token id, ...)   */
+  DG_ERR_CAPACITY = 5,    /* P + C > Pcap: the KV cache has no room                      */
+  DG_ERR_STATE = 6,       /* dg_selfcond without a matching dg_logits_entropy            */
+  DG_ERR_NONFINITE = 7,   /* device saw non-finite logits (sticky, via dg_sync)          */
+  DG_ERR_HIP = 8,         /* a HIP runtime call failed                                   */
+  DG_ERR_UNSUPPORTED = 9
+} dg_status;
+
+/* Model / canvas shape.
+ *  V   vocabulary size (rows of the tied embedding / lm_head table E)      1 <= V < 2^31
+ *  d   model width                                               multiple of 32, <= 16384
+ *  C   canvas length (positions denoised together)                              1..1024
+ *  Hq  query heads, Hkv key/value heads (Hq % Hkv == 0)
+ *  hd  head dimension                                                 16, 32, 64 or 128
+ *  F   self-conditioning FFW hidden width                        multiple of 32, <= 16384 */
+typedef struct {
+  int32_t V, d, C, Hq, Hkv, hd, F;
+} dg_dims;
+
+/* ---------------------------------------------------------------- context */
+/* Creates a context on HIP device `device` that enqueues on `hip_stream`
+ * (a hipStream_t; NULL = the device's null stream). Allocates the context's status
+ * word on the device. */
+dg_status dg_create(dg_ctx *out, int device, void *hip_stream);
+void dg_destroy(dg_ctx ctx);
+/* Switches the stream later calls enqueue on. */
+dg_status dg_set_stream(dg_ctx ctx, void *hip_stream);
+/* Human-readable description of the last non-OK status of this context. */
+const char *dg_last_error(dg_ctx ctx);
+/* Waits for the stream; returns the sticky device status (DG_ERR_RANGE for an
+ * out-of-range token id, DG_ERR_NONFINITE for non-finite logits) or DG_OK. */
+dg_status dg_sync(dg_ctx ctx);
+/* Clears the sticky device status (enqueued, stream-ordered). */
+dg_status dg_clear_status(dg_ctx ctx);
+
+/* Bytes of device workspace one step needs for these dims and cache capacity.
+ * The same workspace is passed to dg_canvas_attn, dg_logits_entropy and dg_selfcond;
+ * dg_selfcond consumes what the preceding dg_logits_entropy left in it. */
+size_t dg_workspace_bytes(const dg_dims *dims, int64_t Pcap);
+
+/* Annealed temperature of step k of a budget of N steps (host only, pure):
+ * tau_k = float(tau0 + (tau1 - tau0) * k / (N - 1)) evaluated in double; N <= 1 gives
+ * tau0. Linear decrease 0.8 -> 0.4: tutorial chapter "DiffusionGemma" (sampler
+ * configuration) and the Technical Report page, "Method steps" (3). */
+float dg_temperature(int32_t k, int32_t N, float tau0, float tau1);
+
+/* ---------------------------------------------------------------- the step */
+/* Bidirectional canvas attention (Google "DiffusionGemma explained", section
+ * "Architecture: incremental prefill and denoising": in denoise mode a query at any
+ * canvas position attends to every canvas token and to the KV cache, with no mask).
+ *   X  = bf16(E[tokens] + z)                   denoiser input [C, d] (z NULL: 0)
+ *   Q  = bf16(X Wq^T), Kc = bf16(X Wk^T), Vc = bf16(X Wv^T)
+ *   O_h = softmax(Q_h [Kp_g ; Kc_g]^T / sqrt(hd)) [Vp_g ; Vc_g],  g = floor(h*Hkv/Hq)
+ *   A  = bf16(O Wo^T)                           [C, d]
+ * tokens [C] int32 (ids outside [0, V) set DG_ERR_RANGE on the device and read as 0);
+ * z [C, d] or NULL; E [V, d]; Wq [Hq*hd, d]; Wk, Wv [Hkv*hd, d]; Wo [d, Hq*hd];
+ * Kp, Vt: the KV cache (layout above) holding P tokens (0 <= P <= Pcap, Pcap % 8 == 0);
+ * the cache is only read. ws: workspace; A [C, d] output. */
+dg_status dg_canvas_attn(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens,
+                         const dg_bf16 *z, const dg_bf16 *E, const dg_bf16 *Wq,
+                         const dg_bf16 *Wk, const dg_bf16 *Wv, const dg_bf16 *Wo,
+                         const dg_bf16 *Kp, const dg_bf16 *Vt, int64_t P, int64_t Pcap,
+                         void *ws, dg_bf16 *A);
+
+/* Sampler head (Technical Report page, "Method steps" (3)): logits H E^T, softmax at
+ * temperature tau giving p0, per-position Shannon entropy in nats (clamped at 0) and
+ * argmax (ties to the lowest id). H [C, d]; E [V, d]; tau > 0. Writes entropy [C]
+ * float32 and argmax [C] int32, and leaves p0 (as bf16 per-tile scaled probabilities
+ * plus fp32 tile statistics) in ws for dg_selfcond; the C x V probabilities are never
+ * materialized in fp32. Non-finite logits give a NaN entropy for that position and
+ * set DG_ERR_NONFINITE. */
+dg_status dg_logits_entropy(dg_ctx ctx, const dg_dims *dims, const dg_bf16 *H,
+                            const dg_bf16 *E, float tau, void *ws, float *entropy,
+                            int32_t *argmax);
+
+/* Entropy-bounded acceptance for B independent canvases of C positions (Technical
+ * Report page, "Method steps" (3) and "Technical novelty": sort by entropy ascending,
+ * accept within the cumulative entropy budget b). Sums use 2^-32 fixed point:
+ * q = ceil(h * 2^32), order = (h, position) ascending, accept the longest prefix with
+ * sum q <= floor(b * 2^32). Zero accepted positions is legal. Entropies that are NaN,
+ * infinite or >= 65536 are never accepted; negative ones count as 0.
+ * entropy [B, C] float32; 0 <= b < 65536; accept [B, C] uint8 (0/1); n_accept [B]. */
+dg_status dg_entropy_accept(dg_ctx ctx, int32_t B, int32_t C, const float *entropy,
+                            float b, uint8_t *accept, int32_t *n_accept);
+
+/* Uniform-state renoise (Technical Report page, "Method steps" (2)-(3); Google page,
+ * "Uniform State Diffusion"): accepted positions take argmax, every other position a
+ * token drawn uniformly over [0, V):
+ *   token = floor(r * V / 2^64),  r = word 0 of Philox4x64-10 with
+ *   key (seed, canvas_base + s) and counter (position, step, stream, 0)
+ * (Salmon et al., SC'11). stream = 0 for renoise; accept == NULL initializes a canvas:
+ * every position is drawn on stream 1 and argmax may be NULL.
+ * argmax, tokens [B, C] int32; accept [B, C] uint8 or NULL. */
+dg_status dg_renoise(dg_ctx ctx, int32_t B, int32_t C, int32_t V, const int32_t *argmax,
+                     const uint8_t *accept, uint64_t seed, uint32_t canvas_base,
+                     uint32_t step, int32_t *tokens);
+
+/* Self-conditioning (Technical Report page, "Method steps" (3): z = FFW(p0 E); Google
+ * page, "Self-conditioning"): s = p0 E with p0 from the immediately preceding
+ * dg_logits_entropy on the same workspace and dims, then z = bf16(GELU_erf(s W1^T) W2^T).
+ * E [V, d]; W1 [F, d]; W2 [d, F]; z [C, d] output. DG_ERR_STATE if ws does not hold
+ * the p0 of a matching dg_logits_entropy. */
+dg_status dg_selfcond(dg_ctx ctx, const dg_dims *dims, void *ws, const dg_bf16 *E,
+                      const dg_bf16 *W1, const dg_bf16 *W2, dg_bf16 *z);
+
+/* Adaptive stop (Technical Report page, "Method steps" (4)): flag 1 when step >= 1,
+ * the mean entropy is <= thr (sum ceil(h 2^32) <= floor(thr * C * 2^32), every entropy
+ * in the valid domain) and argmax equals prev_argmax at every position; else 2 when
+ * step >= N - 1 (step cap: commit anyway); else 0. prev_argmax may be NULL (no stop).
+ * entropy [B, C]; argmax, prev_argmax [B, C]; 0 <= thr < 65536; flag [B] int32. */
+dg_status dg_stop_test(dg_ctx ctx, int32_t B, int32_t C, const float *entropy,
+                       const int32_t *argmax, const int32_t *prev_argmax, float thr,
+                       int32_t step, int32_t N, int32_t *flag);
+
+/* Commit (Technical Report page, "Method steps" (5); tutorial chapter "DiffusionGemma",
+ * KV-cache write timing): appends the finalized block's keys and values at token
+ * positions [P, P + C) of every KV head: K = bf16(E[tokens] Wk^T), V = bf16(E[tokens]
+ * Wv^T) (a stand-in for the causal re-encode of the block). Rows [0, P) are not touched.
+ * tokens [C] int32 (x0 = argmax); Kp, Vt in/out; *P_out (host) = P + C.
+ * DG_ERR_CAPACITY (nothing written) when P + C > Pcap. */
+dg_status dg_commit_kv(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens,
+                       const dg_bf16 *E, const dg_bf16 *Wk, const dg_bf16 *Wv,
+                       dg_bf16 *Kp, dg_bf16 *Vt, int64_t P, int64_t Pcap, int64_t *P_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DG_H */

@@ -16,3 +16,16 @@ def pytest_configure(config):
 def pytest_collection_modifyitems(config, items):
     # Collect the GPU parity tests in file order; nothing else to reorder.
     pass
+
+
+@pytest.fixture(scope="session")
+def dg_ctx():
+    """One libdg context on cuda:0 for the GPU tests (fails loudly without a GPU)."""
+    import torch
+
+    import block_ar_canvas_amd as dg
+
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    ctx = dg.Context(0)
+    yield ctx
+    ctx.close()

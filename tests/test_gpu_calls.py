@@ -1,0 +1,235 @@
+"""Per-call parity of the HIP path against the CPU oracle (needs an MI355X).
+
+Sizes span several tiles of every kernel and ragged tails (V, C, P and d not multiples
+of the tile sizes). Tolerances:
+  * entropy within 1e-3 nats; argmax exact except where the oracle's top-2 gap of the
+    tempered logits is within 1e-3 max(1, |u_top|);
+  * attention output A, self-conditioning z and committed K/V: max|g - r| / max|r| <= 2e-2
+    (bf16 inputs, fp32 accumulation vs the float64 oracle);
+  * acceptance, renoise and the stop flag bit-exact when fed the oracle's vectors.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_ar_canvas_amd as dg
+import dg_inputs as di
+import oracle as O
+from gpu_util import (DEV, argmax_mismatch_unexcused, bf16_dev, bits_np, f32_dev, i32_dev,
+                      maxrel, u8_dev, upload_cache, upload_weights)
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = {
+    "tiny": di.config(0),
+    "small": di.config(1),
+    "ragged": di.Config("ragged", V=5000, d=96, C=100, Hq=6, Hkv=3, hd=32, F=64, P0=77, N=6,
+                        alpha_max=8.0, seed=21),
+    "hd64": di.Config("hd64", V=3000, d=128, C=40, Hq=4, Hkv=1, hd=64, F=96, P0=300, N=6,
+                      alpha_max=9.0, seed=22),
+    "c1000": di.Config("c1000", V=1000, d=64, C=1000, Hq=2, Hkv=2, hd=16, F=32, P0=5, N=4,
+                       alpha_max=6.0, seed=23),
+}
+
+_cache = {}
+
+
+def setup(name):
+    if name not in _cache:
+        cfg = SHAPES[name]
+        W = di.weights(cfg)
+        Pcap = -(-(cfg.P0 + cfg.C) // 8) * 8
+        Kp, Vp = di.prefix_kv(cfg, Pcap)
+        _cache[name] = (cfg, W, Kp, Vp, Pcap, upload_weights(W))
+    return _cache[name]
+
+
+def ws_for(cfg, Pcap):
+    return torch.empty(dg.workspace_bytes(cfg, Pcap), dtype=torch.uint8, device=DEV)
+
+
+def run_head(ctx, cfg, Wd, H, tau, ws):
+    ent = torch.empty(cfg.C, dtype=torch.float32, device=DEV)
+    am = torch.empty(cfg.C, dtype=torch.int32, device=DEV)
+    ctx.logits_entropy(cfg, bf16_dev(H), Wd["E"], tau, ws, ent, am)
+    return ent, am
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_logits_entropy_and_selfcond(dg_ctx, name):
+    cfg, W, Kp, Vp, Pcap, Wd = setup(name)
+    ws = ws_for(cfg, Pcap)
+    tgt = di.targets(cfg, 0)
+    for k in sorted({0, cfg.N // 2, cfg.N - 1}):
+        H = di.hidden(cfg, W["E"], 0, k, tgt)
+        tau = O.temperature(k, cfg.N)
+        assert np.float32(dg.temperature(k, cfg.N)) == tau
+        ent, am = run_head(dg_ctx, cfg, Wd, H, tau, ws)
+        z = torch.empty(cfg.C, cfg.d, dtype=torch.bfloat16, device=DEV)
+        dg_ctx.selfcond(cfg, ws, Wd["E"], Wd["W1"], Wd["W2"], z)
+        dg_ctx.sync()
+        ent_r, am_r, p_r, u_r = O.logits_entropy(H, W["E"], tau)
+        e = ent.cpu().numpy()
+        assert np.all(np.isfinite(e))
+        assert np.max(np.abs(e - ent_r)) <= 1e-3, (k, np.max(np.abs(e - ent_r)))
+        assert argmax_mismatch_unexcused(am.cpu().numpy(), am_r, u_r) == 0
+        z_r, _ = O.selfcond(p_r, W["E"], W["W1"], W["W2"])
+        assert maxrel(O.from_bf16(bits_np(z)), O.from_bf16(z_r)) <= 2e-2
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+@pytest.mark.parametrize("prefix", ["full", "empty"])
+def test_canvas_attention(dg_ctx, name, prefix):
+    cfg, W, Kp, Vp, Pcap, Wd = setup(name)
+    P = cfg.P0 if prefix == "full" else 0
+    rng = np.random.default_rng(cfg.seed + 100)
+    tok = rng.integers(0, cfg.V, cfg.C).astype(np.int32)
+    z = di.f32_to_bf16_bits(rng.standard_normal((cfg.C, cfg.d)).astype(np.float32) * 0.3)
+    Kd, Vtd = upload_cache(Kp, Vp)
+    ws = ws_for(cfg, Pcap)
+    A = torch.empty(cfg.C, cfg.d, dtype=torch.bfloat16, device=DEV)
+    dg_ctx.canvas_attn(cfg, i32_dev(tok), bf16_dev(z), Wd["E"], Wd["Wq"], Wd["Wk"], Wd["Wv"],
+                       Wd["Wo"], Kd, Vtd, P, ws, A)
+    dg_ctx.sync()
+    A_r, _ = O.canvas_attn(tok, z, W["E"], W["Wq"], W["Wk"], W["Wv"], W["Wo"], Kp, Vp, P,
+                           cfg.Hq, cfg.Hkv, cfg.hd)
+    assert maxrel(O.from_bf16(bits_np(A)), O.from_bf16(A_r)) <= 2e-2
+    # the cache is only read
+    Kb, Vb = upload_cache(Kp, Vp)
+    assert torch.equal(Kd.view(torch.int16), Kb.view(torch.int16))
+    assert torch.equal(Vtd.view(torch.int16), Vb.view(torch.int16))
+
+
+def test_canvas_attention_without_selfcond_term(dg_ctx):
+    cfg, W, Kp, Vp, Pcap, Wd = setup("ragged")
+    tok = np.random.default_rng(5).integers(0, cfg.V, cfg.C).astype(np.int32)
+    Kd, Vtd = upload_cache(Kp, Vp)
+    A = torch.empty(cfg.C, cfg.d, dtype=torch.bfloat16, device=DEV)
+    dg_ctx.canvas_attn(cfg, i32_dev(tok), None, Wd["E"], Wd["Wq"], Wd["Wk"], Wd["Wv"], Wd["Wo"],
+                       Kd, Vtd, cfg.P0, ws_for(cfg, Pcap), A)
+    dg_ctx.sync()
+    A_r, _ = O.canvas_attn(tok, None, W["E"], W["Wq"], W["Wk"], W["Wv"], W["Wo"], Kp, Vp,
+                           cfg.P0, cfg.Hq, cfg.Hkv, cfg.hd)
+    assert maxrel(O.from_bf16(bits_np(A)), O.from_bf16(A_r)) <= 2e-2
+
+
+def _accept_cases():
+    rng = np.random.default_rng(31)
+    cases = []
+    for C in (1, 7, 16, 100, 256, 1000, 1024):
+        h = rng.exponential(10 ** rng.uniform(-3, -1), (3, C)).astype(np.float32)
+        h[1, ::3] = h[1, 0]                               # ties
+        h[2, : C // 2] = np.float32(0.0)
+        cases.append(h)
+    edge = np.array([[np.nan, 0.0, np.inf, 70000.0, 0.01, -0.0, -1.0, -np.inf,
+                      0.05, 0.05, 0.05, 65535.0]], np.float32)
+    cases.append(edge)
+    cases.append(np.full((2, 3), 0.05, np.float32))
+    # the oracle's own entropies along a small-config trajectory
+    cfg, W, *_ = setup("small")
+    tgt = di.targets(cfg, 0)
+    rows = [O.logits_entropy(di.hidden(cfg, W["E"], 0, k, tgt), W["E"], O.temperature(k, cfg.N))[0]
+            for k in (30, 38, 42, 47)]
+    cases.append(np.stack(rows))
+    return cases
+
+
+@pytest.mark.parametrize("b", [0.1, 0.0, 0.37, 65000.0])
+def test_entropy_accept_bit_exact(dg_ctx, b):
+    for h in _accept_cases():
+        B, C = h.shape
+        acc = torch.full((B, C), 7, dtype=torch.uint8, device=DEV)
+        n = torch.empty(B, dtype=torch.int32, device=DEV)
+        dg_ctx.entropy_accept(f32_dev(h), b, acc, n)
+        acc_r, n_r = O.entropy_accept(h, b)
+        np.testing.assert_array_equal(acc.cpu().numpy(), acc_r)
+        np.testing.assert_array_equal(n.cpu().numpy(), n_r)
+
+
+@pytest.mark.parametrize("V", [2, 3, 512, 5000, 262144, 2 ** 31 - 1])
+def test_renoise_bit_exact(dg_ctx, V):
+    rng = np.random.default_rng(V % 1000)
+    B, C = 3, 257
+    am = rng.integers(0, V, (B, C)).astype(np.int32)
+    acc = (rng.random((B, C)) < 0.4).astype(np.uint8)
+    for seed, base, step in ((0, 0, 0), (2 ** 63 + 5, 7, 47), (12345, 2 ** 31, 3)):
+        tok = torch.empty(B, C, dtype=torch.int32, device=DEV)
+        dg_ctx.renoise(V, i32_dev(am), u8_dev(acc), seed, base, step, tok)
+        np.testing.assert_array_equal(tok.cpu().numpy(), O.renoise(am, acc, seed, base, step, V))
+        dg_ctx.renoise(V, None, None, seed, base, 0, tok)
+        np.testing.assert_array_equal(tok.cpu().numpy(), O.renoise(am, None, seed, base, 0, V))
+
+
+def test_stop_test_bit_exact(dg_ctx):
+    C, N = 256, 48
+    am = np.arange(C, dtype=np.int32)
+    h = np.full(C, 0.005, np.float32)
+    h_up = h.copy()
+    h_up[7] = np.nextafter(np.float32(0.005), np.float32(1))
+    am2 = am.copy()
+    am2[100] += 1
+    h_nan = np.zeros(C, np.float32)
+    h_nan[0] = np.nan
+    cases = [(h, am, am, 3), (h_up, am, am, 3), (h, am2, am, 3), (h, am, None, 0), (h, am, am, 0),
+             (h_up, am, am, N - 1), (h, am, am, N - 1), (h_nan, am, am, 3), (h_up, am, None, N - 1)]
+    rng = np.random.default_rng(41)
+    for _ in range(10):
+        hh = rng.exponential(0.004, C).astype(np.float32)
+        cases.append((hh, am, am, int(rng.integers(1, N))))
+    for hh, a, p, step in cases:
+        flag = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+        dg_ctx.stop_test(f32_dev(hh), i32_dev(a), None if p is None else i32_dev(p), 0.005, step, N, flag)
+        assert int(flag.item()) == int(O.stop_test(hh, a, p, 0.005, step, N)[0])
+    # segments
+    hb = np.zeros((3, 16), np.float32)
+    hb[1, 3] = 1.0
+    ab = np.zeros((3, 16), np.int32)
+    pb = ab.copy()
+    pb[2, 5] = 1
+    flag = torch.empty(3, dtype=torch.int32, device=DEV)
+    dg_ctx.stop_test(f32_dev(hb), i32_dev(ab), i32_dev(pb), 0.005, 2, 8, flag)
+    np.testing.assert_array_equal(flag.cpu().numpy(), O.stop_test(hb, ab, pb, 0.005, 2, 8))
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged", "hd64"])
+def test_commit_kv(dg_ctx, name):
+    cfg, W, Kp, Vp, Pcap, Wd = setup(name)
+    rng = np.random.default_rng(51)
+    tok = rng.integers(0, cfg.V, cfg.C).astype(np.int32)
+    Kd, Vtd = upload_cache(Kp, Vp, Pcap)
+    K0, V0 = bits_np(Kd), bits_np(Vtd)
+    P2 = dg_ctx.commit_kv(cfg, i32_dev(tok), Wd["E"], Wd["Wk"], Wd["Wv"], Kd, Vtd, cfg.P0)
+    dg_ctx.sync()
+    assert P2 == cfg.P0 + cfg.C
+    Ko, Vo = Kp.copy(), Vp.copy()
+    O.commit_kv(tok, W["E"], W["Wk"], W["Wv"], Ko, Vo, cfg.P0, cfg.Hkv, cfg.hd)
+    Kg, Vtg = bits_np(Kd), bits_np(Vtd)
+    P0 = cfg.P0
+    np.testing.assert_array_equal(Kg[:, :P0], K0[:, :P0])           # prefix untouched
+    np.testing.assert_array_equal(Vtg[:, :, :P0], V0[:, :, :P0])
+    np.testing.assert_array_equal(Kg[:, P2:], K0[:, P2:])           # beyond the block
+    np.testing.assert_array_equal(Vtg[:, :, P2:], V0[:, :, P2:])
+    for got, ref in ((O.from_bf16(Kg[:, P0:P2]), O.from_bf16(Ko[:, P0:P2])),
+                     (O.from_bf16(Vtg[:, :, P0:P2].transpose(0, 2, 1)), O.from_bf16(Vo[:, P0:P2]))):
+        assert maxrel(got, ref) <= 2e-2
+        assert np.all(np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-30)   # <= 1 bf16 ulp
+
+
+def test_determinism(dg_ctx):
+    cfg, W, Kp, Vp, Pcap, Wd = setup("ragged")
+    H = di.hidden(cfg, W["E"], 0, cfg.N - 1)
+    outs = []
+    for _ in range(2):
+        ws = ws_for(cfg, Pcap)
+        ent, am = run_head(dg_ctx, cfg, Wd, H, 0.4, ws)
+        z = torch.empty(cfg.C, cfg.d, dtype=torch.bfloat16, device=DEV)
+        dg_ctx.selfcond(cfg, ws, Wd["E"], Wd["W1"], Wd["W2"], z)
+        Kd, Vtd = upload_cache(Kp, Vp, Pcap)
+        A = torch.empty(cfg.C, cfg.d, dtype=torch.bfloat16, device=DEV)
+        dg_ctx.canvas_attn(cfg, am, z, Wd["E"], Wd["Wq"], Wd["Wk"], Wd["Wv"], Wd["Wo"], Kd, Vtd,
+                           cfg.P0, ws, A)
+        dg_ctx.sync()
+        outs.append([x.cpu().numpy().tobytes() for x in (ent, am, z.view(torch.int16), A.view(torch.int16))])
+    assert outs[0] == outs[1]
