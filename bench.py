@@ -1,0 +1,264 @@
+"""Benchmark of the MI355X canvas-denoise step (one GPU).
+
+A "step" is one pass of the whole hot path over one 256-token canvas: canvas attention
+over the prefix KV cache, the fused logits/entropy/argmax sampler head over the
+262144-token vocabulary, entropy-bounded acceptance, renoise, self-conditioning and the
+stop test; whenever a canvas reaches its stop or its 48-step cap the commit of its K/V
+and the next canvas's initialization fall inside the timed region too.
+
+Workload (default "gemma_head"): V=262144, d=2048, C=256, 16 query / 8 KV heads of
+128, FFW 1024, prefix 8192 tokens, N=48, synthetic seeded weights and driver hidden
+states (dg_inputs), all resident in HBM before timing starts.
+
+Prints one JSON line: denoise steps/s (value), canvas tokens/s, the roofline of the
+dominant kernel (the sampler-head logits GEMM, timed live with HIP events) and the CPU
+oracle's rate on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "denoise steps/s & canvas tokens/s (256-canvas, 262K vocab); % MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=240)
+    ap.add_argument("--warmup", type=int, default=48)
+    ap.add_argument("--config", default="gemma_head")
+    ap.add_argument("--roofline-reps", type=int, default=20)
+    ap.add_argument("--cpu-steps", type=int, default=1, help="oracle steps timed for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one 1 GiB device copy (for HBM counter calibration)")
+    return ap.parse_args()
+
+
+def traffic_from_profiles(kernel_src: str, name: str):
+    """HBM bytes per launch from the committed counter summary, if it matches the source."""
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        parts = line.split()
+        if len(parts) == 2 and not line.startswith("#"):
+            vals[parts[0]] = parts[1]
+    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
+    if vals.get("source_sha256_16") != sha or "hbm_bytes_per_launch" not in vals:
+        return None
+    return float(vals["hbm_bytes_per_launch"])
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU sharding of the path is described in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_ar_canvas_amd as dg
+    import dg_inputs as di
+    from block_ar_canvas_amd.loop import CanvasLoop
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    cfg = di.config(args.config)
+    total = args.warmup + args.steps
+    n_canvas = total // cfg.N + 2
+    Pcap = -(-(cfg.P0 + cfg.C * n_canvas) // 8) * 8
+
+    t_gen = time.time()
+    W = di.weights(cfg)
+    Kp, Vp = di.prefix_kv(cfg, Pcap)
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    Wd = {k: bf(v) for k, v in W.items()}
+    Kd = bf(Kp)
+    Vtd = bf(np.ascontiguousarray(Vp.transpose(0, 2, 1)))
+    del Vp
+    Hd = [bf(di.hidden_all(cfg, W["E"], c)) for c in range(n_canvas)]
+    torch.cuda.synchronize()
+    t_gen = time.time() - t_gen
+
+    ctx = dg.Context(0)
+    loop = CanvasLoop(ctx, cfg, Wd, Kd, Vtd, cfg.P0, N=cfg.N, seed=cfg.seed)
+
+    # Drive the block-AR loop step by step so that exactly `steps` steps are timed.
+    state = {"canvas": -1, "k": 0, "done": True, "commits": 0}
+
+    def one_step():
+        s = state
+        if s["done"]:
+            s["canvas"] += 1
+            s["k"] = 0
+            s["done"] = False
+            loop.init_canvas(s["canvas"])
+            loop.z.zero_()
+            loop.step(0, Hd[s["canvas"]][0])
+            s["pending"] = 0
+            return
+        k = s["k"]
+        if k + 1 < cfg.N:
+            loop.step(k + 1, Hd[s["canvas"]][k + 1])
+        flag = loop.wait_flag(k)
+        if flag != dg.STOP_GO:
+            loop.commit(loop.argmax[k & 1])
+            s["commits"] += 1
+            s["done"] = True
+            return
+        s["k"] = k + 1
+
+    # Each call of one_step enqueues one denoise step (or, at a canvas end, the commit
+    # whose step was the speculative one); count enqueued denoise steps.
+    def run(n):
+        steps = 0
+        while steps < n:
+            before = (state["canvas"], state["k"], state["done"])
+            one_step()
+            after = (state["canvas"], state["k"], state["done"])
+            if not after[2]:
+                steps += 1
+        return steps
+
+    run(args.warmup)
+    torch.cuda.synchronize()
+    c0 = state["commits"]
+    t0 = time.perf_counter()
+    run(args.steps)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    commits = state["commits"] - c0
+    sec = t1 - t0
+    steps_per_s = args.steps / sec
+    ctx.sync()
+
+    # Roofline of the dominant kernel: the sampler-head logits GEMM (dg_logits_entropy),
+    # timed live with HIP events on the stream the library launches on.
+    H = Hd[0][cfg.N - 1]
+    ent = torch.empty(cfg.C, dtype=torch.float32, device=dev)
+    am = torch.empty(cfg.C, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        ctx.logits_entropy(cfg, H, Wd["E"], 0.4, loop.ws, ent, am)
+    e0.record(stream)
+    for _ in range(args.roofline_reps):
+        ctx.logits_entropy(cfg, H, Wd["E"], 0.4, loop.ws, ent, am)
+    e1.record(stream)
+    e1.synchronize()
+    logits_ms = e0.elapsed_time(e1) / args.roofline_reps
+    alg_bytes = cfg.V * cfg.d * 2 + cfg.C * cfg.d * 2 + cfg.C * 8
+    alg_flops = 2.0 * cfg.C * cfg.V * cfg.d
+    achieved = alg_bytes / (logits_ms * 1e-3) / 1e9
+    src = os.path.join(ROOT, "block_ar_canvas_amd", "csrc", "k_logits.hip")
+    traffic = traffic_from_profiles(src, "logits_tile_kernel_gemma_head")
+
+    # Self-conditioning product, timed the same way (reported beside the roofline).
+    ctx.logits_entropy(cfg, H, Wd["E"], 0.4, loop.ws, ent, am)
+    z = torch.empty(cfg.C, cfg.d, dtype=torch.bfloat16, device=dev)
+    e0.record(stream)
+    for _ in range(args.roofline_reps):
+        ctx.selfcond(cfg, loop.ws, Wd["E"], Wd["W1"], Wd["W2"], z)
+    e1.record(stream)
+    e1.synchronize()
+    selfcond_ms = e0.elapsed_time(e1) / args.roofline_reps
+    ctx.sync()
+
+    if args.calibrate_copy:
+        src_t = torch.empty(1 << 29, dtype=torch.int16, device=dev)
+        dst_t = torch.empty_like(src_t)
+        dst_t.copy_(src_t)
+        torch.cuda.synchronize()
+
+    result = {
+        "metric": METRIC,
+        "value": round(steps_per_s, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * sec / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: V={cfg.V} d={cfg.d} C={cfg.C} Hq={cfg.Hq} Hkv={cfg.Hkv} "
+                               f"hd={cfg.hd} F={cfg.F} prefix={cfg.P0} N={cfg.N}",
+                   "canvas": cfg.C, "vocab": cfg.V, "prefix_tokens": cfg.P0, "max_steps": cfg.N,
+                   "parallelism": "single-gpu"},
+        "canvas_tokens_per_s": round(commits * cfg.C / sec, 1),
+        "canvas_tokens_per_s_at_12_steps": round(steps_per_s * cfg.C / 12, 1),
+        "commits_timed": commits,
+        "roofline": {"kernel": "logits_tile_kernel+row_finalize (dg_logits_entropy)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "ms_per_launch": round(logits_ms, 4),
+                     "mfma_frac": round(alg_flops / (logits_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        "selfcond_ms_per_call": round(selfcond_ms, 4),
+        "input_gen_s": round(t_gen, 1),
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, W, Kp, args.cpu_steps)
+    print(json.dumps(result))
+
+
+def cpu_baseline(cfg, W, Kp, n_steps):
+    """The CPU oracle, as it stands, on a bounded sample: n full steps of the same canvas."""
+    import oracle as O
+    import dg_inputs as di
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(i.get("num_threads", 1) for i in threadpool_info()) or 1
+    except Exception:
+        cores = os.cpu_count() or 1
+    Kp_o = Kp[:, :cfg.P0 + cfg.C].copy()
+    _, Vp_o = di.prefix_kv(cfg, cfg.P0 + cfg.C)
+    tgt = di.targets(cfg, 0)
+    tok = np.random.default_rng(0).integers(0, cfg.V, cfg.C).astype(np.int32)
+    z = np.zeros((cfg.C, cfg.d), np.uint16)
+    k0 = cfg.N // 2
+    H = [di.hidden(cfg, W["E"], 0, k0 + i, tgt) for i in range(n_steps)]
+    prev = None
+    t0 = time.perf_counter()
+    for i in range(n_steps):
+        k = k0 + i
+        tau = O.temperature(k, cfg.N)
+        O.canvas_attn(tok, z, W["E"], W["Wq"], W["Wk"], W["Wv"], W["Wo"], Kp_o, Vp_o, cfg.P0,
+                      cfg.Hq, cfg.Hkv, cfg.hd)
+        ent, am, p, _ = O.logits_entropy(H[i], W["E"], tau)
+        acc, _ = O.entropy_accept(ent[None], 0.1)
+        tok = O.renoise(am[None], acc, cfg.seed, 0, k, cfg.V)[0]
+        z, _ = O.selfcond(p, W["E"], W["W1"], W["W2"])
+        O.stop_test(ent, am, prev, 0.005, k, cfg.N)
+        prev = am
+    sec = time.perf_counter() - t0
+    return {"value": round(n_steps / sec, 5), "unit": "steps/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{n_steps} full denoise step(s) of {cfg.name} (k={k0}..), numpy float64, "
+                      f"{sec:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -39,8 +39,11 @@ class CanvasLoop:
         self.argmax = [torch.empty(C, dtype=torch.int32, device=dev) for _ in range(2)]
         self.accept = torch.empty(C, dtype=torch.uint8, device=dev)
         self.n_accept = torch.empty(1, dtype=torch.int32, device=dev)
-        self.flag = torch.empty(1, dtype=torch.int32, device=dev)
-        self.flag_host = torch.empty(1, dtype=torch.int32, pin_memory=True)
+        # Stop flags are double-buffered so step k+1 can be enqueued before the host
+        # reads the flag of step k.
+        self.flags = [torch.empty(1, dtype=torch.int32, device=dev) for _ in range(2)]
+        self.flags_host = [torch.empty(1, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+        self.flag_events = [torch.cuda.Event() for _ in range(2)]
 
     def init_canvas(self, canvas: int):
         """Uniform random canvas (init stream) and z = 0."""
@@ -58,13 +61,15 @@ class CanvasLoop:
         self.ctx.entropy_accept(self.entropy, self.b, self.accept, self.n_accept)
         self.ctx.renoise(dm.V, am, self.accept, self.seed, self.canvas, k, self.tokens)
         self.ctx.selfcond(dm, self.ws, W["E"], W["W1"], W["W2"], self.z)
-        self.ctx.stop_test(self.entropy, am, prev, self.thr, k, self.N, self.flag)
+        self.ctx.stop_test(self.entropy, am, prev, self.thr, k, self.N, self.flags[k & 1])
+        self.flags_host[k & 1].copy_(self.flags[k & 1], non_blocking=True)
+        self.flag_events[k & 1].record()
         return am
 
-    def read_flag(self) -> int:
-        self.flag_host.copy_(self.flag, non_blocking=True)
-        torch.cuda.current_stream().synchronize()
-        return int(self.flag_host[0])
+    def wait_flag(self, k: int) -> int:
+        """Blocks until step k's stop flag has reached the host and returns it."""
+        self.flag_events[k & 1].synchronize()
+        return int(self.flags_host[k & 1][0])
 
     def commit(self, x0):
         self.P = self.ctx.commit_kv(self.dims, x0, self.W["E"], self.W["Wk"], self.W["Wv"],
@@ -74,17 +79,25 @@ class CanvasLoop:
     def run_canvas(self, canvas: int, hidden, on_step=None):
         """Init, denoise until the stop test or the cap, commit. Returns steps run.
 
-        hidden(k) -> H_k device tensor; on_step(k, loop) is called after each step
-        (before the flag is read), e.g. to record intermediate state.
+        hidden(k) -> H_k device tensor; on_step(k, loop) is called with the state right
+        after step k (before step k + 1 is enqueued). Step k + 1 is enqueued before the
+        host waits for step k's flag, so the device never idles on the flag read; when
+        step k stops the canvas, the speculative step k + 1 is discarded (the commit
+        uses step k's own argmax buffer, which step k + 1 does not write).
         """
         self.init_canvas(canvas)
         self.z.zero_()
-        am = None
-        for k in range(self.N):
-            am = self.step(k, hidden(k))
+        k = 0
+        self.step(0, hidden(0))
+        if on_step is not None:
+            on_step(0, self)
+        while True:
+            if k + 1 < self.N:
+                self.step(k + 1, hidden(k + 1))
+            if self.wait_flag(k) != STOP_GO:
+                break
+            k += 1
             if on_step is not None:
                 on_step(k, self)
-            if self.read_flag() != STOP_GO:
-                break
-        self.commit(am)
+        self.commit(self.argmax[k & 1])
         return k + 1
