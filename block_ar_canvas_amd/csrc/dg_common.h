@@ -57,6 +57,25 @@ DG_DEV uint32_t pack_bf16x2(float lo, float hi) {
 DG_DEV float wave_xor32(float v) { return __shfl_xor(v, 32, 64); }
 DG_DEV int wave_xor32(int v) { return __shfl_xor(v, 32, 64); }
 
+// Direct global -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4):
+// lane l's 16 bytes land at LDS byte address lds_base + 16*l, lds_base wave-uniform.
+// Issued through inline asm so that only the explicit dma_wait<N>() (s_waitcnt
+// vmcnt(N): at most N of this wave's vector-memory loads still outstanding) orders
+// the copies against LDS reads; callers follow it with a workgroup barrier.
+DG_DEV void dma16(const void *gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+template <int N>
+DG_DEV void dma_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+DG_DEV uint32_t lds_addr(const void *p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+
 // Sticky device status codes (mirror dg_status).
 #define DGS_RANGE 4
 #define DGS_NONFINITE 7
@@ -66,7 +85,7 @@ DG_DEV void set_status(int *status, int code) {
 
 // ------------------------------------------------------------------ tiling constants
 #define DG_CT 32        // canvas columns per MFMA tile
-#define DG_BV 128       // vocabulary rows per logits tile (one set of tile statistics)
+#define DG_BV 256       // vocabulary rows per logits tile (one set of tile statistics)
 #define DG_KT 32        // keys per attention tile
 
 static inline int64_t dg_round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -82,7 +101,7 @@ struct DgWs {
   int nsc;         // self-conditioning split-K parts over the vocabulary
   int nsplit_max;  // attention split-K parts at Pcap
   size_t ptilde;   // bf16 p~ in MFMA fragment order: [Cpad/32][Vpad/16][64 lanes][8]
-  size_t tmax, tsum, tent, targ;  // per-(tile, column) statistics [T][Cpad]
+  size_t tmax, tsum, tent, targ;  // per-(column, tile) statistics [Cpad][T]
   size_t fac;      // per-(tile, column) p0 scale exp(m_t - m) / Z    [T][Cpad]
   size_t q;        // Q   bf16 [Cpad][Hq*hd]
   size_t kc;       // canvas keys   bf16 [Cpad][Hkv*hd]

@@ -7,10 +7,11 @@
 // vocabulary projection over every canvas position is a bandwidth and temporary-tensor
 // hog; here the C x V logits never reach memory in fp32.
 //
-// logits_tile_kernel: one workgroup = 128 vocabulary rows x up to 256 canvas columns,
-// K (model width) in steps of 64 through LDS with a register prefetch. E rows are the
-// MFMA A operand (loaded through perm_row), H rows the B operand, so each lane owns a
-// canvas column and its share of the tile's 128 logits. The epilogue, per column:
+// logits_tile_kernel: one workgroup = 256 vocabulary rows x up to 256 canvas columns,
+// the model width streamed through LDS rings of direct global -> LDS copies. E
+// rows are the MFMA A operand (loaded through perm_row), H rows the B operand, so each
+// lane owns a canvas column and its share of the tile's 256 logits. The epilogue, per
+// column:
 //   u = logit / tau, m_t = max u, a_t = argmax (lowest id), Z_t = sum exp(u - m_t),
 //   S_t = sum exp(u - m_t) (u - m_t),
 // and stores p~ = bf16(exp(u - m_t)) in the exact MFMA-fragment order dg_selfcond
@@ -27,28 +28,89 @@
 
 namespace {
 
-constexpr int BV = DG_BV, BC = 256, BK = 64, PITCH = BK + 8;
+// Workgroup tile 256 vocabulary rows x 256 canvas columns, 8 waves (4 along the
+// vocabulary x 2 along the canvas), each wave 64 x 128 = 2 x 4 MFMA tiles.
+// The model width is consumed in steps of BK = 64 through LDS rings filled by direct
+// global -> LDS copies: E (streamed from HBM) has 3 stages, so two are in flight while
+// one is consumed; H (L2-resident, re-read by every workgroup) has 2. Each copy
+// instruction moves 8 rows x 128 contiguous bytes (8 lanes per row segment: one full
+// cache line per 8 lanes). LDS rows are 128 bytes with XOR-swizzled 16-byte chunks
+// (see swz) so fragment reads are free of bank conflicts. E rows are stored in
+// perm_row order within each 32-row tile, so fragment reads are plain row reads.
+constexpr int BV = DG_BV, BC = 256, BK = 64, NSE = 3, NSH = 2;
+constexpr int TILE = 256 * 128;                  // bytes of one 256-row x 64-k stage
+constexpr int SMEM = (NSE + NSH) * TILE;         // 160 KiB
 constexpr float LOG2E = 1.4426950408889634f;
 
 DG_DEV bool better(float u, int v, float best, int bi) {
   return u > best || (u == best && v < bi);
 }
 
-__global__ __launch_bounds__(256) void logits_tile_kernel(LogitsArgs a) {
-  __shared__ __attribute__((aligned(16))) u16 Es[BV * PITCH];
-  __shared__ __attribute__((aligned(16))) u16 Hs[BC * PITCH];
-  __shared__ float red_m[2][BC];
-  __shared__ int red_i[2][BC];
-  __shared__ float red_z[2][BC];
-  __shared__ float red_s[2][BC];
-  __shared__ int red_bad[2][BC];
+// Byte offset of logical 16-byte chunk c (0..7) of LDS row R. A 128-byte row covers
+// half of the 64 LDS banks, so rows alternate bank halves; XOR-ing the chunk with
+// (R >> 1) & 7 gives the 16 rows read by a 16-lane group 16 distinct 16-byte slots.
+DG_DEV int swz(int R, int c) { return R * 128 + ((c ^ ((R >> 1) & 7)) << 4); }
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wv = wave & 1, wc = wave >> 1;
+__global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  // epilogue scratch aliases the stage rings once the main loop is done
+  float(*red_m)[BC] = (float(*)[BC])(smem);
+  int(*red_i)[BC] = (int(*)[BC])(smem + 4 * BC * 4);
+  int(*red_bad)[BC] = (int(*)[BC])(smem + 8 * BC * 4);
+  float(*red_z)[BC] = (float(*)[BC])(smem + 12 * BC * 4);
+  float(*red_s)[BC] = (float(*)[BC])(smem + 16 * BC * 4);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = wave & 3, wc = wave >> 2;
   const int hh = lane >> 5, l32 = lane & 31;
   const int vt = blockIdx.x;
   const int v0 = vt * BV;
   const int cb = blockIdx.y * BC;
+
+  // Copy duties per stage: rows [32*wave, 32*wave + 32) of E and of H, as 4 copy
+  // instructions of 8 rows each. Lane l of instruction j fills LDS row
+  // R = 32*wave + 8*j + l/8 at chunk position l%8, i.e. logical chunk (l%8) ^ (R&7).
+  const u16 *ge[4], *gh[4];
+  int lch[4];                                            // logical chunk per instruction
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int R = 32 * wave + 8 * j + (lane >> 3);
+    const int c = (lane & 7) ^ ((R >> 1) & 7);
+    lch[j] = c;
+    int er = v0 + (R & ~31) + perm_row(R & 31);
+    er = er < a.V ? er : a.V - 1;                    // clamp: masked in the epilogue
+    int hr = cb + R;
+    hr = hr < a.C ? hr : a.C - 1;                    // clamp: columns never stored
+    ge[j] = a.E + (int64_t)er * a.d + c * 8;
+    gh[j] = a.H + (int64_t)hr * a.d + c * 8;
+  }
+  const uint32_t sbase = lds_addr(smem);
+  const uint32_t wrow = (uint32_t)(32 * wave) * 128u;
+  // When d is an odd multiple of 32, the last stage holds only 32 valid k values: its
+  // upper four chunks are copied from the lower four of the same row (never past the
+  // row end) and the k-steps that would read them are skipped.
+  const int KI = (a.d + BK - 1) / BK;
+  // Workgroups start at different K chunks (rotation by the tile index) so that the
+  // GPU's concurrent copies spread over the address space instead of all reading the
+  // same column band of E and H at once. The partial tail chunk always comes last.
+  const int KF = a.d / BK;                                 // full chunks
+  const int rot = KF > 0 ? vt % KF : 0;
+  auto kchunk = [&](int it) { return it < KF ? (it + rot) % KF : it; };
+  const bool half_tail = (a.d % BK) != 0;
+  auto koff = [&](int it, int j) {
+    return kchunk(it) * BK + ((it == KI - 1 && half_tail && lch[j] >= 4) ? -32 : 0);
+  };
+  auto issue_e = [&](int it) {
+    const uint32_t st = sbase + (uint32_t)(it % NSE) * TILE + wrow;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma16(ge[j] + koff(it, j), st + j * 1024);
+  };
+  auto issue_h = [&](int it) {
+    const uint32_t st = sbase + (uint32_t)(NSE + it % NSH) * TILE + wrow;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma16(gh[j] + koff(it, j), st + j * 1024);
+  };
 
   f32x16_t acc[2][4];
 #pragma unroll
@@ -56,60 +118,42 @@ __global__ __launch_bounds__(256) void logits_tile_kernel(LogitsArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
 
-  uint4 pe[4], ph[8];
-  auto load = [&](int k0) {
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int q = tid + 256 * it;
-      const int row = q >> 3, col = (q & 7) * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (v0 + row < a.V && k0 + col < a.d) v = *(const uint4 *)(a.E + (int64_t)(v0 + row) * a.d + k0 + col);
-      pe[it] = v;
-    }
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int q = tid + 256 * it;
-      const int row = q >> 3, col = (q & 7) * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (cb + row < a.C && k0 + col < a.d) v = *(const uint4 *)(a.H + (int64_t)(cb + row) * a.d + k0 + col);
-      ph[it] = v;
-    }
-  };
-  auto store = [&]() {
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int q = tid + 256 * it;
-      *(uint4 *)(Es + (q >> 3) * PITCH + (q & 7) * 8) = pe[it];
-    }
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int q = tid + 256 * it;
-      *(uint4 *)(Hs + (q >> 3) * PITCH + (q & 7) * 8) = ph[it];
-    }
-  };
-
-  const int wcol0 = cb + wc * 128;   // first canvas column of this wave
-  load(0);
-  for (int k0 = 0; k0 < a.d; k0 += BK) {
-    __syncthreads();
-    store();
-    __syncthreads();
-    if (k0 + BK < a.d) load(k0 + BK);
+  // Issue order keeps the in-order vmcnt simple: stage it's H copies go out one
+  // iteration ahead, its E copies two iterations ahead; at the top of iteration it
+  // only E(it+1) (the last 4 copies of this wave) may still be in flight.
+  auto compute = [&](int it, int nks) {
+    const char *se = smem + (it % NSE) * TILE;
+    const char *sh = smem + (NSE + it % NSH) * TILE;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      u32x4_t af[2];
+      if (ks >= nks) break;
+      u32x4_t af[2], bf[4];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
-        af[mt] = *(const u32x4_t *)(Es + (wv * 64 + mt * 32 + perm_row(l32)) * PITCH + ks * 16 + 8 * hh);
+        af[mt] = *(const u32x4_t *)(se + swz(wv * 64 + mt * 32 + l32, 2 * ks + hh));
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        if (wcol0 + nt * 32 >= a.C) continue;   // wave-uniform: columns past the canvas
-        const u32x4_t bf = *(const u32x4_t *)(Hs + (wc * 128 + nt * 32 + l32) * PITCH + ks * 16 + 8 * hh);
+      for (int nt = 0; nt < 4; ++nt)
+        bf[nt] = *(const u32x4_t *)(sh + swz(wc * 128 + nt * 32 + l32, 2 * ks + hh));
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) acc[mt][nt] = mfma_32x32x16(af[mt], bf, acc[mt][nt]);
-      }
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) acc[mt][nt] = mfma_32x32x16(af[mt], bf[nt], acc[mt][nt]);
     }
+  };
+  issue_e(0);
+  issue_h(0);
+  if (KI > 1) issue_e(1);
+  for (int it = 0; it < KI - 1; ++it) {
+    dma_wait<4>();           // everything but E(it+1) has landed
+    __syncthreads();
+    issue_h(it + 1);
+    if (it + 2 < KI) issue_e(it + 2);
+    compute(it, BK / 16);
   }
+  dma_wait<0>();
+  __syncthreads();
+  compute(KI - 1, (a.d - (KI - 1) * BK) / 16);
+  __syncthreads();   // the rings become epilogue scratch
 
   // ---------------- epilogue, phase 1: tile max / argmax per column
 #pragma unroll
@@ -150,7 +194,8 @@ __global__ __launch_bounds__(256) void logits_tile_kernel(LogitsArgs a) {
   for (int nt = 0; nt < 4; ++nt) {
     const int lc = wc * 128 + nt * 32 + l32;
     float m = red_m[0][lc];
-    if (red_m[1][lc] > m) m = red_m[1][lc];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) m = fmaxf(m, red_m[w][lc]);
     float Z = 0.f, S = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
@@ -187,37 +232,46 @@ __global__ __launch_bounds__(256) void logits_tile_kernel(LogitsArgs a) {
   __syncthreads();
 
   // ---------------- phase 3: tile statistics (one writer per column)
-  if (wv == 0 && hh == 0) {
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int lc = wc * 128 + nt * 32 + l32;
-      const int c = cb + lc;
-      if (c >= a.Cpad) continue;
+  if (tid < BC) {
+    const int lc = tid;
+    const int c = cb + lc;
+    if (c < a.Cpad) {
       float m = red_m[0][lc];
       int ai = red_i[0][lc];
-      if (better(red_m[1][lc], red_i[1][lc], m, ai)) { m = red_m[1][lc]; ai = red_i[1][lc]; }
-      const bool bad = red_bad[0][lc] | red_bad[1][lc];
-      const int64_t o = (int64_t)vt * a.Cpad + c;
+      int bad = red_bad[0][lc];
+      float Z = red_z[0][lc], S = red_s[0][lc];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) {
+        if (better(red_m[w][lc], red_i[w][lc], m, ai)) { m = red_m[w][lc]; ai = red_i[w][lc]; }
+        bad |= red_bad[w][lc];
+        Z += red_z[w][lc];
+        S += red_s[w][lc];
+      }
+      const int64_t o = (int64_t)c * a.T + vt;       // statistics are [column][tile]
       a.tmax[o] = bad ? __builtin_nanf("") : m;
-      a.tsum[o] = red_z[0][lc] + red_z[1][lc];
-      a.tent[o] = red_s[0][lc] + red_s[1][lc];
+      a.tsum[o] = Z;
+      a.tent[o] = S;
       a.targ[o] = ai;
     }
   }
 }
 
-// One workgroup per canvas column; tile order is fixed, so the result is deterministic.
+// One workgroup per canvas column merges that column's tile statistics ([column][tile]
+// layout: contiguous reads) in a fixed order, so the result is deterministic. It also
+// writes the per-tile scale exp(m_t - m) / Z in [tile][column] order for dg_selfcond.
 __global__ __launch_bounds__(256) void row_finalize_kernel(LogitsArgs a) {
   __shared__ float sm[256];
-  __shared__ int si[256];
+  __shared__ int si[256], sbad[256];
   __shared__ float sz[256], ss[256];
-  __shared__ int sbad[256];
   const int c = blockIdx.x, tid = threadIdx.x;
+  const float *tmax = a.tmax + (int64_t)c * a.T;
+  const float *tsum = a.tsum + (int64_t)c * a.T;
+  const float *tent = a.tent + (int64_t)c * a.T;
 
   float m = -INFINITY;
   int tb = 0x7FFFFFFF, bad = 0;
   for (int t = tid; t < a.T; t += 256) {
-    const float mt = a.tmax[(int64_t)t * a.Cpad + c];
+    const float mt = tmax[t];
     if (mt != mt) bad = 1;
     else if (mt > m) { m = mt; tb = t; }
   }
@@ -235,15 +289,13 @@ __global__ __launch_bounds__(256) void row_finalize_kernel(LogitsArgs a) {
   m = sm[0];
   tb = si[0];
   bad = sbad[0];
-  __syncthreads();
 
   float Z = 0.f, S = 0.f;
   for (int t = tid; t < a.T; t += 256) {
-    const int64_t o = (int64_t)t * a.Cpad + c;
-    const float dm = a.tmax[o] - m;
+    const float dm = tmax[t] - m;
     const float w = expf(dm);
-    Z += a.tsum[o] * w;
-    S += (a.tent[o] + a.tsum[o] * dm) * w;
+    Z += tsum[t] * w;
+    S += (tent[t] + tsum[t] * dm) * w;
   }
   sz[tid] = Z; ss[tid] = S;
   __syncthreads();
@@ -254,10 +306,8 @@ __global__ __launch_bounds__(256) void row_finalize_kernel(LogitsArgs a) {
   Z = sz[0];
   S = ss[0];
   const float invZ = 1.0f / Z;
-  for (int t = tid; t < a.T; t += 256) {
-    const int64_t o = (int64_t)t * a.Cpad + c;
-    a.fac[o] = bad ? 0.f : expf(a.tmax[o] - m) * invZ;
-  }
+  for (int t = tid; t < a.T; t += 256)
+    a.fac[(int64_t)t * a.Cpad + c] = bad ? 0.f : expf(tmax[t] - m) * invZ;
   if (tid == 0) {
     float ent = logf(Z) - S / Z;
     ent = ent > 0.f ? ent : 0.f;
@@ -266,14 +316,21 @@ __global__ __launch_bounds__(256) void row_finalize_kernel(LogitsArgs a) {
       set_status(a.status, DGS_NONFINITE);
     }
     a.entropy[c] = ent;
-    a.argmax[c] = bad ? 0 : a.targ[(int64_t)tb * a.Cpad + c];
+    a.argmax[c] = bad ? 0 : a.targ[(int64_t)c * a.T + tb];
   }
 }
 
 }  // namespace
 
 hipError_t dg_launch_logits(const LogitsArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL(logits_tile_kernel, dim3(a.T, (a.Cpad + BC - 1) / BC), dim3(256), 0, st, a);
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void *)logits_tile_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, SMEM);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL(logits_tile_kernel, dim3(a.T, (a.Cpad + BC - 1) / BC), dim3(512), SMEM, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(row_finalize_kernel, dim3(a.C), dim3(256), 0, st, a);
