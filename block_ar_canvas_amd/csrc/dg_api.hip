@@ -62,6 +62,8 @@ dg_status check_dims(dg_ctx ctx, const dg_dims *m, const char *fn) {
     return fail(ctx, DG_ERR_SHAPE, "%s: hd=%d must be 16, 32, 64 or 128", fn, m->hd);
   if ((m->Hq * m->hd) % 32 || (m->Hkv * m->hd) % 8)
     return fail(ctx, DG_ERR_SHAPE, "%s: Hq*hd=%d must be a multiple of 32", fn, m->Hq * m->hd);
+  if ((int64_t)m->V * m->d >= ((int64_t)1 << 31))
+    return fail(ctx, DG_ERR_SHAPE, "%s: V*d=%lld must be < 2^31", fn, (long long)m->V * m->d);
   if (m->F < 32 || m->F % 32 || m->F > 16384)
     return fail(ctx, DG_ERR_SHAPE, "%s: F=%d must be a multiple of 32 in [32, 16384]", fn, m->F);
   return DG_OK;

@@ -50,8 +50,11 @@ DG_DEV u16 f32_to_bf16(float f) {
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (u16)(u >> 16);
 }
+// Two floats -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32 on gfx950).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 DG_DEV uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 DG_DEV float wave_xor32(float v) { return __shfl_xor(v, 32, 64); }

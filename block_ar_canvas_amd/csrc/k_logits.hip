@@ -29,18 +29,20 @@
 namespace {
 
 // Workgroup tile 256 vocabulary rows x 256 canvas columns, 8 waves (4 along the
-// vocabulary x 2 along the canvas), each wave 64 x 128 = 2 x 4 MFMA tiles.
-// The model width is consumed in steps of BK = 64 through LDS rings filled by direct
-// global -> LDS copies: E (streamed from HBM) has 3 stages, so two are in flight while
-// one is consumed; H (L2-resident, re-read by every workgroup) has 2. Each copy
-// instruction moves 8 rows x 128 contiguous bytes (8 lanes per row segment: one full
-// cache line per 8 lanes). LDS rows are 128 bytes with XOR-swizzled 16-byte chunks
-// (see swz) so fragment reads are free of bank conflicts. E rows are stored in
-// perm_row order within each 32-row tile, so fragment reads are plain row reads.
+// vocabulary x 2 along the canvas), each wave 64 x 128 = 2 x 4 MFMA tiles (128
+// accumulators, two waves per SIMD so one wave's LDS-read latency hides behind the
+// other's MFMAs). The model width is consumed in steps of BK = 64 through LDS rings
+// filled by direct global -> LDS copies: E (streamed from HBM) has 3 stages, so two are
+// in flight while one is consumed; H (L2-resident, re-read by every workgroup) has 2.
+// Each copy instruction moves 8 rows x 128 contiguous bytes (one full cache line per 8
+// lanes). LDS rows are 128 bytes with XOR-swizzled 16-byte chunks (see swz), so
+// fragment reads are free of bank conflicts. E rows are stored in perm_row order within
+// each 32-row tile, so fragment reads are plain row reads.
 constexpr int BV = DG_BV, BC = 256, BK = 64, NSE = 3, NSH = 2;
 constexpr int TILE = 256 * 128;                  // bytes of one 256-row x 64-k stage
 constexpr int SMEM = (NSE + NSH) * TILE;         // 160 KiB
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
 
 DG_DEV bool better(float u, int v, float best, int bi) {
   return u > best || (u == best && v < bi);
@@ -51,14 +53,15 @@ DG_DEV bool better(float u, int v, float best, int bi) {
 // (R >> 1) & 7 gives the 16 rows read by a 16-lane group 16 distinct 16-byte slots.
 DG_DEV int swz(int R, int c) { return R * 128 + ((c ^ ((R >> 1) & 7)) << 4); }
 
+// HALF_TAIL: d is an odd multiple of 32, so the last K chunk holds 32 valid columns.
+template <bool HALF_TAIL>
 __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   // epilogue scratch aliases the stage rings once the main loop is done
   float(*red_m)[BC] = (float(*)[BC])(smem);
   int(*red_i)[BC] = (int(*)[BC])(smem + 4 * BC * 4);
-  int(*red_bad)[BC] = (int(*)[BC])(smem + 8 * BC * 4);
-  float(*red_z)[BC] = (float(*)[BC])(smem + 12 * BC * 4);
-  float(*red_s)[BC] = (float(*)[BC])(smem + 16 * BC * 4);
+  float(*red_z)[BC] = (float(*)[BC])(smem + 8 * BC * 4);
+  float(*red_s)[BC] = (float(*)[BC])(smem + 12 * BC * 4);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -70,14 +73,12 @@ __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a) {
 
   // Copy duties per stage: rows [32*wave, 32*wave + 32) of E and of H, as 4 copy
   // instructions of 8 rows each. Lane l of instruction j fills LDS row
-  // R = 32*wave + 8*j + l/8 at chunk position l%8, i.e. logical chunk (l%8) ^ (R&7).
+  // R = 32*wave + 8*j + l/8 at chunk slot l%8, i.e. logical chunk (l%8) ^ ((R>>1)&7).
   const u16 *ge[4], *gh[4];
-  int lch[4];                                            // logical chunk per instruction
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int R = 32 * wave + 8 * j + (lane >> 3);
     const int c = (lane & 7) ^ ((R >> 1) & 7);
-    lch[j] = c;
     int er = v0 + (R & ~31) + perm_row(R & 31);
     er = er < a.V ? er : a.V - 1;                    // clamp: masked in the epilogue
     int hr = cb + R;
@@ -87,30 +88,30 @@ __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a) {
   }
   const uint32_t sbase = lds_addr(smem);
   const uint32_t wrow = (uint32_t)(32 * wave) * 128u;
-  // When d is an odd multiple of 32, the last stage holds only 32 valid k values: its
-  // upper four chunks are copied from the lower four of the same row (never past the
-  // row end) and the k-steps that would read them are skipped.
+
+  // K order: workgroups start at different chunks (rotation by the tile index) so the
+  // GPU's concurrent copies spread over the address space. With HALF_TAIL the partial
+  // chunk comes last; its upper four 16-byte chunks are copied from the lower four of
+  // the same row (never past the row end) and the k-steps reading them are skipped.
   const int KI = (a.d + BK - 1) / BK;
-  // Workgroups start at different K chunks (rotation by the tile index) so that the
-  // GPU's concurrent copies spread over the address space instead of all reading the
-  // same column band of E and H at once. The partial tail chunk always comes last.
-  const int KF = a.d / BK;                                 // full chunks
+  const int KF = a.d / BK;
   const int rot = KF > 0 ? vt % KF : 0;
-  auto kchunk = [&](int it) { return it < KF ? (it + rot) % KF : it; };
-  const bool half_tail = (a.d % BK) != 0;
-  auto koff = [&](int it, int j) {
-    return kchunk(it) * BK + ((it == KI - 1 && half_tail && lch[j] >= 4) ? -32 : 0);
-  };
-  auto issue_e = [&](int it) {
-    const uint32_t st = sbase + (uint32_t)(it % NSE) * TILE + wrow;
+  auto kcol = [&](int it) { return (it < KF ? (it + rot) % KF : it) * BK; };
+  auto issue = [&](int it, const u16 *const *g, uint32_t st) {
+    const int k = kcol(it);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(ge[j] + koff(it, j), st + j * 1024);
+    for (int j = 0; j < 4; ++j) {
+      int kk = k;
+      if (HALF_TAIL && it == KI - 1) {
+        const int R = 32 * wave + 8 * j + (lane >> 3);
+        const int c = (lane & 7) ^ ((R >> 1) & 7);   // logical chunk of this copy lane
+        kk = k - (c >= 4 ? 32 : 0);
+      }
+      dma16(g[j] + kk, st + j * 1024);
+    }
   };
-  auto issue_h = [&](int it) {
-    const uint32_t st = sbase + (uint32_t)(NSE + it % NSH) * TILE + wrow;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(gh[j] + koff(it, j), st + j * 1024);
-  };
+  auto issue_e = [&](int it) { issue(it, ge, sbase + (uint32_t)(it % NSE) * TILE + wrow); };
+  auto issue_h = [&](int it) { issue(it, gh, sbase + (uint32_t)(NSE + it % NSH) * TILE + wrow); };
 
   f32x16_t acc[2][4];
 #pragma unroll
@@ -118,9 +119,6 @@ __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
 
-  // Issue order keeps the in-order vmcnt simple: stage it's H copies go out one
-  // iteration ahead, its E copies two iterations ahead; at the top of iteration it
-  // only E(it+1) (the last 4 copies of this wave) may still be in flight.
   auto compute = [&](int it, int nks) {
     const char *se = smem + (it % NSE) * TILE;
     const char *sh = smem + (NSE + it % NSH) * TILE;
@@ -140,11 +138,15 @@ __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a) {
         for (int mt = 0; mt < 2; ++mt) acc[mt][nt] = mfma_32x32x16(af[mt], bf[nt], acc[mt][nt]);
     }
   };
+
+  // Issue order keeps the in-order vmcnt simple: stage it's H copies go out one
+  // iteration ahead, its E copies two iterations ahead; at the top of iteration it
+  // only E(it+1) (the last 4 copies of this wave) may still be in flight.
   issue_e(0);
   issue_h(0);
   if (KI > 1) issue_e(1);
   for (int it = 0; it < KI - 1; ++it) {
-    dma_wait<4>();           // everything but E(it+1) has landed
+    dma_wait<4>();
     __syncthreads();
     issue_h(it + 1);
     if (it + 2 < KI) issue_e(it + 2);
@@ -152,59 +154,54 @@ __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a) {
   }
   dma_wait<0>();
   __syncthreads();
-  compute(KI - 1, (a.d - (KI - 1) * BK) / 16);
+  compute(KI - 1, HALF_TAIL ? 2 : BK / 16);
   __syncthreads();   // the rings become epilogue scratch
 
-  // ---------------- epilogue, phase 1: tile max / argmax per column
+  // ---------------- epilogue, phase 1: tile max / argmax per column, in the log2
+  // domain x = logit * log2(e) / tau. Within a lane the registers are visited in
+  // ascending vocabulary order, so a strict '>' keeps the lowest id among ties.
+  const float k2 = a.inv_tau * LOG2E;
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     const int lc = wc * 128 + nt * 32 + l32;
     float best = -INFINITY;
-    int bi = 0x7FFFFFFF, bad = 0;
+    int bi = 0x7FFFFFFF;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
+      const int vb = v0 + wv * 64 + mt * 32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int v = v0 + wv * 64 + mt * 32 + acc_row_perm(r, hh);
-        float u = acc[mt][nt][r] * a.inv_tau;
-        if (v < a.V) {
-          bad |= !(fabsf(u) <= FLT_MAX);
-          if (better(u, v, best, bi)) { best = u; bi = v; }
-        } else {
-          u = -INFINITY;
-        }
-        acc[mt][nt][r] = u;
+        const int v = vb + acc_row_perm(r, hh);
+        const float x = v < a.V ? acc[mt][nt][r] * k2 : -INFINITY;
+        acc[mt][nt][r] = x;
+        if (x > best) { best = x; bi = v; }
       }
     }
     const float ob = wave_xor32(best);
     const int oi = wave_xor32(bi);
     if (better(ob, oi, best, bi)) { best = ob; bi = oi; }
-    bad |= wave_xor32(bad);
     if (hh == 0) {
       red_m[wv][lc] = best;
       red_i[wv][lc] = bi;
-      red_bad[wv][lc] = bad;
     }
   }
   __syncthreads();
 
-  // ---------------- phase 2: exp, Z_t, S_t, and p~ fragments
+  // ---------------- phase 2: exp2, Z_t, S_t (log2 units), and p~ fragments
   const int VS = a.T * (BV / 16);            // 16-row vocabulary steps in p~
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     const int lc = wc * 128 + nt * 32 + l32;
-    float m = red_m[0][lc];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) m = fmaxf(m, red_m[w][lc]);
+    const float m = fmaxf(fmaxf(red_m[0][lc], red_m[1][lc]), fmaxf(red_m[2][lc], red_m[3][lc]));
     float Z = 0.f, S = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float du = acc[mt][nt][r] - m;
-        const float e = exp2f(du * LOG2E);
+        const float dx = fmaxf(acc[mt][nt][r] - m, -1e30f);   // masked rows: e = 0, e*dx = 0
+        const float e = exp2f(dx);
         Z += e;
-        S += (e > 0.f) ? e * du : 0.f;
+        S = fmaf(e, dx, S);
         acc[mt][nt][r] = e;
       }
     }
@@ -218,39 +215,39 @@ __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a) {
     if (ctile * 32 < a.Cpad) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
+        const int vs0 = (v0 + wv * 64 + mt * 32) / 16;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          const int vstep = (v0 + wv * 64 + mt * 32) / 16 + s;
           const f32x16_t &e = acc[mt][nt];
           const uint4 w = make_uint4(pack_bf16x2(e[8 * s + 0], e[8 * s + 1]), pack_bf16x2(e[8 * s + 2], e[8 * s + 3]),
                                      pack_bf16x2(e[8 * s + 4], e[8 * s + 5]), pack_bf16x2(e[8 * s + 6], e[8 * s + 7]));
-          *(uint4 *)(a.ptilde + (((int64_t)ctile * VS + vstep) * 64 + lane) * 8) = w;
+          *(uint4 *)(a.ptilde + (((int64_t)ctile * VS + vs0 + s) * 64 + lane) * 8) = w;
         }
       }
     }
   }
   __syncthreads();
 
-  // ---------------- phase 3: tile statistics (one writer per column)
+  // ---------------- phase 3: tile statistics in natural units (one writer per column).
+  // A non-finite logit makes m, Z or S non-finite; the tile max is then stored as NaN.
   if (tid < BC) {
     const int lc = tid;
     const int c = cb + lc;
     if (c < a.Cpad) {
       float m = red_m[0][lc];
       int ai = red_i[0][lc];
-      int bad = red_bad[0][lc];
       float Z = red_z[0][lc], S = red_s[0][lc];
 #pragma unroll
       for (int w = 1; w < 4; ++w) {
         if (better(red_m[w][lc], red_i[w][lc], m, ai)) { m = red_m[w][lc]; ai = red_i[w][lc]; }
-        bad |= red_bad[w][lc];
         Z += red_z[w][lc];
         S += red_s[w][lc];
       }
+      const bool bad = !(fabsf(m) <= FLT_MAX) || !(Z <= FLT_MAX) || !(fabsf(S) <= FLT_MAX);
       const int64_t o = (int64_t)c * a.T + vt;       // statistics are [column][tile]
-      a.tmax[o] = bad ? __builtin_nanf("") : m;
+      a.tmax[o] = bad ? __builtin_nanf("") : m * LN2;
       a.tsum[o] = Z;
-      a.tent[o] = S;
+      a.tent[o] = S * LN2;
       a.targ[o] = ai;
     }
   }
@@ -325,12 +322,19 @@ __global__ __launch_bounds__(256) void row_finalize_kernel(LogitsArgs a) {
 hipError_t dg_launch_logits(const LogitsArgs &a, hipStream_t st) {
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void *)logits_tile_kernel,
+    hipError_t e = hipFuncSetAttribute((const void *)logits_tile_kernel<false>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, SMEM);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void *)logits_tile_kernel<true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, SMEM);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  hipLaunchKernelGGL(logits_tile_kernel, dim3(a.T, (a.Cpad + BC - 1) / BC), dim3(512), SMEM, st, a);
+  const dim3 grid(a.T, (a.Cpad + BC - 1) / BC);
+  if (a.d % BK)
+    hipLaunchKernelGGL(logits_tile_kernel<true>, grid, dim3(512), SMEM, st, a);
+  else
+    hipLaunchKernelGGL(logits_tile_kernel<false>, grid, dim3(512), SMEM, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(row_finalize_kernel, dim3(a.C), dim3(256), 0, st, a);
