@@ -252,10 +252,13 @@ dg_status dg_logits_entropy(dg_ctx ctx, const dg_dims *dims, const dg_bf16 *H,
   a.inv_tau = 1.0f / tau;
   a.ptilde = ws_at<u16>(ws, w.ptilde);
   a.tmax = ws_at<float>(ws, w.tmax);
+  a.trho = ws_at<float>(ws, w.trho);
   a.tsum = ws_at<float>(ws, w.tsum);
   a.tent = ws_at<float>(ws, w.tent);
   a.targ = ws_at<int>(ws, w.targ);
-  a.fac = ws_at<float>(ws, w.fac);
+  a.nsh = ws_at<int>(ws, w.nsh);
+  a.gsc = ws_at<float>(ws, w.gsc);
+  a.nsc = w.nsc;
   a.entropy = entropy;
   a.argmax = argmax;
   a.status = ctx->d_status;
@@ -305,7 +308,8 @@ dg_status dg_selfcond(dg_ctx ctx, const dg_dims *dims, void *ws, const dg_bf16 *
   const DgWs w = dg_ws_layout(m.V, m.d, m.C, m.Hq, m.Hkv, m.hd, m.F, 0);
   SelfcondArgs a{};
   a.ptilde = ws_at<u16>(ws, w.ptilde);
-  a.fac = ws_at<float>(ws, w.fac);
+  a.nsh = ws_at<int>(ws, w.nsh);
+  a.gsc = ws_at<float>(ws, w.gsc);
   a.E = E;
   a.V = m.V;
   a.d = m.d;

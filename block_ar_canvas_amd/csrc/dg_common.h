@@ -104,8 +104,9 @@ struct DgWs {
   int nsc;         // self-conditioning split-K parts over the vocabulary
   int nsplit_max;  // attention split-K parts at Pcap
   size_t ptilde;   // bf16 p~ in MFMA fragment order: [Cpad/32][Vpad/16][64 lanes][8]
-  size_t tmax, tsum, tent, targ;  // per-(column, tile) statistics [Cpad][T]
-  size_t fac;      // per-(tile, column) p0 scale exp(m_t - m) / Z    [T][Cpad]
+  size_t tmax, trho, tsum, tent, targ;  // per-(column, tile) statistics [Cpad][T]
+  size_t nsh;      // per-(tile, column) exponent shift of p~ within its split [T][Cpad]
+  size_t gsc;      // per-(split, column) scale 2^(rho_S - R) / Z           [nsc][Cpad]
   size_t q;        // Q   bf16 [Cpad][Hq*hd]
   size_t kc;       // canvas keys   bf16 [Cpad][Hkv*hd]
   size_t vct;      // canvas values bf16 [Hkv*hd][Cpad] (transposed)
@@ -131,11 +132,16 @@ static inline int dg_attn_nsplit(int Hkv, int Hq, int C, int64_t P) {
   return (int)ns;
 }
 
+// Self-conditioning split count over the T vocabulary tiles: aim at >= 256 workgroups
+// (256-wide j slices x 256-canvas blocks x splits), >= 16 tiles per split, and at most
+// 128 tiles per split (the split's shift table is staged in 32 KiB of LDS).
 static inline int dg_selfcond_nsplit(int d, int Cpad, int T) {
-  const int64_t jt = dg_cdiv(d, 128) * dg_cdiv(Cpad, 256);
-  int64_t ns = dg_cdiv(512, jt);
-  const int64_t by_len = T / 16;                        // >= 16 tiles (2048 ids) per part
+  const int64_t jt = dg_cdiv(d, 256) * dg_cdiv(Cpad, 256);
+  int64_t ns = dg_cdiv(256, jt);
+  const int64_t by_len = T / 16;
   if (ns > by_len) ns = by_len;
+  const int64_t min_ns = dg_cdiv(T, 128);
+  if (ns < min_ns) ns = min_ns;
   if (ns < 1) ns = 1;
   return (int)ns;
 }
@@ -157,10 +163,12 @@ static inline DgWs dg_ws_layout(int V, int d, int C, int Hq, int Hkv, int hd, in
   const size_t CT = (size_t)w.T * w.Cpad;
   w.ptilde = take((size_t)w.Cpad * w.Vpad * 2);
   w.tmax = take(CT * 4);
+  w.trho = take(CT * 4);
   w.tsum = take(CT * 4);
   w.tent = take(CT * 4);
   w.targ = take(CT * 4);
-  w.fac = take(CT * 4);
+  w.nsh = take(CT * 4);
+  w.gsc = take((size_t)w.nsc * w.Cpad * 4);
   w.q = take((size_t)w.Cpad * Hq * hd * 2);
   w.kc = take((size_t)w.Cpad * Hkv * hd * 2);
   w.vct = take((size_t)w.Cpad * Hkv * hd * 2);
@@ -223,9 +231,11 @@ struct LogitsArgs {
   int V, d, C, Cpad, T;
   float inv_tau;
   u16 *ptilde;
-  float *tmax, *tsum, *tent;
+  float *tmax, *trho, *tsum, *tent;
   int *targ;
-  float *fac;
+  int *nsh;            // exponent shift of p~ per (tile, column)
+  float *gsc;          // scale per (self-cond split, column)
+  int nsc;             // self-cond splits (tile ranges [S*T/nsc, (S+1)*T/nsc))
   float *entropy;      // [C]
   int *argmax;         // [C]
   int *status;
@@ -234,7 +244,8 @@ hipError_t dg_launch_logits(const LogitsArgs &a, hipStream_t st);
 
 struct SelfcondArgs {
   const u16 *ptilde;
-  const float *fac;
+  const int *nsh;
+  const float *gsc;
   const u16 *E;        // [V][d]
   int V, d, C, Cpad, T, nsc;
   float *ps;           // [nsc][Cpad][d]

@@ -8,20 +8,24 @@
 // hog; here the C x V logits never reach memory in fp32.
 //
 // logits_tile_kernel: one workgroup = 256 vocabulary rows x up to 256 canvas columns,
-// the model width streamed through LDS rings of direct global -> LDS copies. E
-// rows are the MFMA A operand (loaded through perm_row), H rows the B operand, so each
-// lane owns a canvas column and its share of the tile's 256 logits. The epilogue, per
-// column:
-//   u = logit / tau, m_t = max u, a_t = argmax (lowest id), Z_t = sum exp(u - m_t),
-//   S_t = sum exp(u - m_t) (u - m_t),
-// and stores p~ = bf16(exp(u - m_t)) in the exact MFMA-fragment order dg_selfcond
-// consumes (no re-layout), plus (m_t, Z_t, S_t, a_t) per (tile, column).
+// the model width streamed through LDS rings of direct global -> LDS copies. E rows
+// are the MFMA A operand (loaded through perm_row), H rows the B operand, so each lane
+// owns a canvas column and its share of the tile's 256 logits. The epilogue works in
+// log2 units x = logit * log2(e) / tau; per column it finds the tile max m_t and argmax
+// a_t (lowest id), the reference rho_t = ceil(m_t) (an integer), and
+//   Z_t = sum 2^(x - rho_t),   S_t = ln2 * sum 2^(x - rho_t) (x - rho_t)   (nats),
+// and stores p~ = bf16(2^(x - rho_t)) in the exact MFMA-fragment order dg_selfcond
+// consumes. Because every reference is an integer in log2 units, moving p~ from one
+// tile's reference to another's is an exact power-of-two scale.
 //
-// row_finalize_kernel: per canvas column, merges the tile statistics in tile order:
-//   m = max m_t, Z = sum Z_t e^(m_t - m), S = sum (S_t + Z_t (m_t - m)) e^(m_t - m),
+// row_finalize_kernel: per canvas column, merges the tile statistics in tile order with
+// the column reference R = max rho_t:
+//   Z = sum Z_t 2^(rho_t - R),  S = sum 2^(rho_t - R) (S_t + Z_t (rho_t - R) ln2),
 //   entropy = ln Z - S / Z  (= -sum p ln p, both terms >= 0: no cancellation),
-// argmax from the first tile reaching m, and the per-tile scale e^(m_t - m) / Z that
-// turns p~ into p0 for the self-conditioning product.
+// argmax from the first tile reaching the largest m_t, and, for each self-conditioning
+// split S (a contiguous tile range) with rho_S = max of its rho_t, the integer shift
+// rho_S - rho_t of each tile and the split scale 2^(rho_S - R) / Z, so that
+// p0 = p~ * 2^-(rho_S - rho_t) * 2^(rho_S - R) / Z.
 #include <float.h>
 
 #include "dg_common.h"
@@ -192,7 +196,7 @@ __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a) {
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     const int lc = wc * 128 + nt * 32 + l32;
-    const float m = fmaxf(fmaxf(red_m[0][lc], red_m[1][lc]), fmaxf(red_m[2][lc], red_m[3][lc]));
+    const float m = ceilf(fmaxf(fmaxf(red_m[0][lc], red_m[1][lc]), fmaxf(red_m[2][lc], red_m[3][lc])));
     float Z = 0.f, S = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
@@ -243,9 +247,11 @@ __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a) {
         Z += red_z[w][lc];
         S += red_s[w][lc];
       }
+      const float rho = ceilf(m);
       const bool bad = !(fabsf(m) <= FLT_MAX) || !(Z <= FLT_MAX) || !(fabsf(S) <= FLT_MAX);
       const int64_t o = (int64_t)c * a.T + vt;       // statistics are [column][tile]
-      a.tmax[o] = bad ? __builtin_nanf("") : m * LN2;
+      a.tmax[o] = bad ? __builtin_nanf("") : m;
+      a.trho[o] = rho;
       a.tsum[o] = Z;
       a.tent[o] = S * LN2;
       a.targ[o] = ai;
@@ -254,25 +260,26 @@ __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a) {
 }
 
 // One workgroup per canvas column merges that column's tile statistics ([column][tile]
-// layout: contiguous reads) in a fixed order, so the result is deterministic. It also
-// writes the per-tile scale exp(m_t - m) / Z in [tile][column] order for dg_selfcond.
+// layout: contiguous reads) in a fixed order, so the result is deterministic.
 __global__ __launch_bounds__(256) void row_finalize_kernel(LogitsArgs a) {
-  __shared__ float sm[256];
+  __shared__ float sm[256], sr[256];
   __shared__ int si[256], sbad[256];
   __shared__ float sz[256], ss[256];
   const int c = blockIdx.x, tid = threadIdx.x;
   const float *tmax = a.tmax + (int64_t)c * a.T;
+  const float *trho = a.trho + (int64_t)c * a.T;
   const float *tsum = a.tsum + (int64_t)c * a.T;
   const float *tent = a.tent + (int64_t)c * a.T;
 
-  float m = -INFINITY;
+  float m = -INFINITY, R = -INFINITY;
   int tb = 0x7FFFFFFF, bad = 0;
   for (int t = tid; t < a.T; t += 256) {
     const float mt = tmax[t];
     if (mt != mt) bad = 1;
     else if (mt > m) { m = mt; tb = t; }
+    R = fmaxf(R, trho[t]);
   }
-  sm[tid] = m; si[tid] = tb; sbad[tid] = bad;
+  sm[tid] = m; si[tid] = tb; sbad[tid] = bad; sr[tid] = R;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
     if (tid < w) {
@@ -280,19 +287,20 @@ __global__ __launch_bounds__(256) void row_finalize_kernel(LogitsArgs a) {
       const int t2 = si[tid + w];
       if (m2 > sm[tid] || (m2 == sm[tid] && t2 < si[tid])) { sm[tid] = m2; si[tid] = t2; }
       sbad[tid] |= sbad[tid + w];
+      sr[tid] = fmaxf(sr[tid], sr[tid + w]);
     }
     __syncthreads();
   }
-  m = sm[0];
   tb = si[0];
   bad = sbad[0];
+  R = sr[0];
 
   float Z = 0.f, S = 0.f;
   for (int t = tid; t < a.T; t += 256) {
-    const float dm = tmax[t] - m;
-    const float w = expf(dm);
+    const float dr = trho[t] - R;                    // integer <= 0
+    const float w = exp2f(dr);
     Z += tsum[t] * w;
-    S += (tent[t] + tsum[t] * dm) * w;
+    S += (tent[t] + tsum[t] * dr * LN2) * w;
   }
   sz[tid] = Z; ss[tid] = S;
   __syncthreads();
@@ -302,9 +310,18 @@ __global__ __launch_bounds__(256) void row_finalize_kernel(LogitsArgs a) {
   }
   Z = sz[0];
   S = ss[0];
-  const float invZ = 1.0f / Z;
-  for (int t = tid; t < a.T; t += 256)
-    a.fac[(int64_t)t * a.Cpad + c] = bad ? 0.f : expf(tmax[t] - m) * invZ;
+
+  // Per self-conditioning split: exponent shift of each tile and the split scale.
+  for (int sp = tid; sp < a.nsc; sp += 256) {
+    const int t0 = (int)((int64_t)sp * a.T / a.nsc), t1 = (int)((int64_t)(sp + 1) * a.T / a.nsc);
+    float rs = -INFINITY;
+    for (int t = t0; t < t1; ++t) rs = fmaxf(rs, trho[t]);
+    for (int t = t0; t < t1; ++t) {
+      const float n = rs - trho[t];
+      a.nsh[(int64_t)t * a.Cpad + c] = bad ? 0 : (int)fminf(n, 255.f);
+    }
+    a.gsc[(int64_t)sp * a.Cpad + c] = bad ? 0.f : exp2f(rs - R) / Z;
+  }
   if (tid == 0) {
     float ent = logf(Z) - S / Z;
     ent = ent > 0.f ? ent : 0.f;

@@ -6,38 +6,64 @@
 // passed to the next step). The report's limitations single out this 262K-wide
 // product as slow in plain framework code; here it is one split-K MFMA pass over E.
 //
-// selfcond_split_kernel computes s^T[j][c] = sum_v E[v][j] p0[c][v] for a 128-wide
-// slice of the model width j, up to 256 canvas columns c and one contiguous range of
-// vocabulary tiles. Operands:
-//   B = p0^T: the bf16 p~ fragments written by the logits epilogue, already in MFMA
-//       B-fragment order. Each 16-byte fragment holds 8 probabilities of one column c
-//       and one 128-row tile t; it is scaled by exp(m_t - m_c) / Z_c (the finalize
-//       factor) and rounded back to bf16 while it is copied into LDS.
-//   A = E^T: E rows (vocabulary-major, j contiguous) are staged in LDS as loaded; each
-//       lane gathers its 8 vocabulary values of one j column (the transpose happens in
-//       the LDS read, E is never copied).
-// Partial sums (one per vocabulary range) are reduced in range order by
-// selfcond_reduce_kernel, which also rounds s to bf16 for the FFW.
+// selfcond_split_kernel computes s^T[j][c] = sum_v E[v][j] p~[c][v] 2^-n(t,c) for a
+// 256-wide slice of the model width j, up to 256 canvas columns c and one split S (a
+// contiguous range of 256-row vocabulary tiles t). p~ holds bf16 2^(x - rho_t) from the
+// logits epilogue; n(t, c) = rho_S - rho_t is an integer, so the rescale to the split's
+// common reference is an exact exponent shift, applied to the bf16 fragments with packed
+// 16-bit integer arithmetic. The remaining per-(split, column) factor 2^(rho_S - R) / Z
+// is applied by selfcond_reduce_kernel, which sums the split partials in split order
+// (deterministic) and rounds s to bf16 for the FFW.
+//
+// Data movement: a ring of 4 LDS stages, 32 vocabulary rows each, filled by direct
+// global -> LDS copies (three stages in flight while one is consumed):
+//   E tile [32 v][256 j] bf16, copied as 512-byte row segments (32 lanes per row) with
+//     16-byte chunks XOR-swizzled by 4*(v & 3);
+//   p~ fragments, copied as the 1 KiB blocks the logits epilogue wrote.
+// MFMA operands: A = E^T (j rows, vocabulary k) via two ds_read_b64_tr_b16 transposing
+// reads per fragment; B = p~ (canvas columns) via linear 16-byte reads. Each wave owns
+// 128 j x 64 canvas (4 x 2 MFMA tiles, 128 accumulators, two waves per SIMD).
 #include "dg_common.h"
 
 namespace {
 
-constexpr int BJ = 128, BC = 256, BKV = 64, EPITCH = BJ + 8;
+constexpr int BJ = 256, BC = 256, BKV = 32, NS = 4;
+constexpr int ESTAGE = BKV * BJ * 2;           // 16 KiB
+constexpr int PSTAGE = 8 * 2 * 1024;           // 16 KiB: 8 canvas tiles x 2 k-steps
+constexpr int STAGE = ESTAGE + PSTAGE;
+constexpr int NTAB_MAX = 32 * 1024;            // LDS bytes for the split's shift table
+constexpr int SMEM = NS * STAGE + NTAB_MAX;    // 160 KiB
 
-__global__ __launch_bounds__(256) void selfcond_split_kernel(SelfcondArgs a, int nj) {
-  __shared__ __attribute__((aligned(16))) u16 Es[BKV * EPITCH];
-  __shared__ __attribute__((aligned(16))) u16 Ps[8 * (BKV / 16) * 64 * 8];
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef short v2i16_t __attribute__((ext_vector_type(2)));
+#define LDS3 __attribute__((address_space(3)))
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Byte offset of element (row v, column j) in the E stage.
+DG_DEV int eoff(int v, int j) { return v * 512 + ((((j >> 3) ^ (4 * (v & 3))) & 31) << 4) + ((j & 7) << 1); }
+
+// bf16 pair scaled by 2^-n (n >= 0) through the exponent field, flushing to zero below
+// the smallest normal (values are non-negative probabilities).
+DG_DEV uint32_t shift2(uint32_t w, v2i16_t dn) {
+  v2i16_t x = __builtin_bit_cast(v2i16_t, w) - dn;
+  const v2i16_t z = {0, 0};
+  x = x > z ? x : z;
+  return __builtin_bit_cast(uint32_t, x);
+}
+
+__global__ __launch_bounds__(512) void selfcond_split_kernel(SelfcondArgs a, int nj) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  unsigned char *ntab = (unsigned char *)(smem + NS * STAGE);   // [tile in split][256 columns]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wj = wave & 1, wc = wave >> 1;
   const int hh = lane >> 5, l32 = lane & 31;
 
-  // blockIdx.x -> (split, j-slice); the j-slices of one split share the p~ range and
+  // blockIdx.x -> (split, j-slice); the j-slices of one split share its p~ range and
   // are kept on one XCD when the split count allows it.
   const int b = blockIdx.x;
-  const int units = a.nsc;
   int split, jb;
-  if ((units & 7) == 0) {
+  if ((a.nsc & 7) == 0) {
     const int xcd = b & 7, r = b >> 3;
     split = xcd + 8 * (r / nj);
     jb = r % nj;
@@ -52,99 +78,120 @@ __global__ __launch_bounds__(256) void selfcond_split_kernel(SelfcondArgs a, int
   const int VS = a.T * (DG_BV / 16);
   const int tile0 = (int)((int64_t)split * a.T / a.nsc);
   const int tile1 = (int)((int64_t)(split + 1) * a.T / a.nsc);
-  const int vbeg = tile0 * DG_BV, vend = tile1 * DG_BV;
+  const int vbeg = tile0 * DG_BV;
+  const int NIT = (tile1 - tile0) * (DG_BV / BKV);
 
-  f32x16_t acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+  // Shift table of this split and canvas block, staged once before the copy pipeline.
+  for (int i = tid; i < (tile1 - tile0) * BC; i += 512) {
+    const int tl = i / BC, cl = i % BC, c = cb + cl;
+    ntab[i] = (unsigned char)((c < a.C) ? a.nsh[(int64_t)(tile0 + tl) * a.Cpad + c] : 255);
+  }
 
-  uint4 pe[4], pp[8];
-  float pf[8];
-  auto load = [&](int v0) {
+  // Copy duties per stage (2 E and 2 p~ instructions per wave). E instruction `ins`
+  // fills stage rows 2*ins and 2*ins + 1 (32 lanes per 512-byte row segment).
+  int erow[2], ecol[2];
+  const u16 *gp[2];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int q = tid + 256 * it;
-      const int row = q >> 4, col = (q & 15) * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (v0 + row < a.V && j0 + col < a.d) v = *(const uint4 *)(a.E + (int64_t)(v0 + row) * a.d + j0 + col);
-      pe[it] = v;
-    }
+  for (int q = 0; q < 2; ++q) {
+    const int ins = wave * 2 + q;                   // 0..15
+    const int v = 2 * ins + (lane >> 5);             // E row in the stage
+    const int lchunk = (lane & 31) ^ (4 * (v & 3));
+    int jc = j0 + 8 * lchunk;
+    jc = jc < a.d ? jc : a.d - 8;                    // clamp: columns past d never stored
+    erow[q] = v;
+    ecol[q] = jc;
+    int ctile = ct0 + (ins >> 1);
+    ctile = ctile < nct ? ctile : nct - 1;           // clamp: columns never stored
+    gp[q] = a.ptilde + (((int64_t)ctile * VS + vbeg / 16 + (ins & 1)) * 64 + lane) * 8;
+  }
+  const uint32_t sbase = lds_addr(smem);
+  auto issue = [&](int it) {
+    const uint32_t st = sbase + (uint32_t)(it % NS) * STAGE;
+    const int vo = it * BKV;
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int q = tid + 256 * it;             // chunk = (canvas tile, vocab step, lane)
-      const int ctl = q >> 8, vs = (q >> 6) & 3, ln = q & 63;
-      const int ctile = ct0 + ctl;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      float f = 0.f;
-      if (ctile < nct) {
-        const int vstep = v0 / 16 + vs;
-        v = *(const uint4 *)(a.ptilde + (((int64_t)ctile * VS + vstep) * 64 + ln) * 8);
-        const int c = ctile * 32 + (ln & 31);
-        if (c < a.C) f = a.fac[(int64_t)(vstep / (DG_BV / 16)) * a.Cpad + c];
-      }
-      pp[it] = v;
-      pf[it] = f;
-    }
-  };
-  auto store = [&]() {
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int q = tid + 256 * it;
-      *(uint4 *)(Es + (q >> 4) * EPITCH + (q & 15) * 8) = pe[it];
-    }
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int q = tid + 256 * it;
-      const uint32_t *w = (const uint32_t *)&pp[it];
-      const float f = pf[it];
-      const uint4 o = make_uint4(pack_bf16x2(bf16lo(w[0]) * f, bf16hi(w[0]) * f),
-                                 pack_bf16x2(bf16lo(w[1]) * f, bf16hi(w[1]) * f),
-                                 pack_bf16x2(bf16lo(w[2]) * f, bf16hi(w[2]) * f),
-                                 pack_bf16x2(bf16lo(w[3]) * f, bf16hi(w[3]) * f));
-      *(uint4 *)(Ps + q * 8) = o;
+    for (int q = 0; q < 2; ++q) {
+      const int ins = wave * 2 + q;
+      int vr = vbeg + vo + erow[q];
+      vr = vr < a.V ? vr : a.V - 1;                  // rows past V meet p~ = 0
+      dma16(a.E + (int64_t)vr * a.d + ecol[q], st + ins * 1024);
+      dma16(gp[q] + (int64_t)(vo / 16) * 64 * 8, st + ESTAGE + ins * 1024);
     }
   };
 
-  if (vbeg < vend) load(vbeg);
-  for (int v0 = vbeg; v0 < vend; v0 += BKV) {
-    __syncthreads();
-    store();
-    __syncthreads();
-    if (v0 + BKV < vend) load(v0 + BKV);
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+
+  // Transposing-read source addresses: lane i of 16-lane group g reads 4 consecutive
+  // j of row 4r + i/4 (+ 16ks + 8h); the group returns E^T rows j = 16(g&1) + i.
+  const int g = lane >> 4, gi = lane & 15;
+  const int trow = 8 * (g >> 1) + (gi >> 2);
+  const int tcol = wj * 128 + 16 * (g & 1) + 4 * (gi & 3);
+
+  auto compute = [&](int it) {
+    const char *se = smem + (it % NS) * STAGE;
+    const char *sp = se + ESTAGE;
+    const int tl = (it * BKV) / DG_BV;               // tile of this stage within the split
+    v2i16_t dn[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const short n = (short)ntab[tl * BC + (wc * 2 + ct) * 32 + l32];
+      dn[ct] = v2i16_t{(short)(n << 7), (short)(n << 7)};
+    }
 #pragma unroll
     for (int ks = 0; ks < BKV / 16; ++ks) {
-      u32x4_t af[2];
+      u32x4_t af[4], bf[2];
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        const u16 *src = Es + (ks * 16 + 8 * hh) * EPITCH + wj * 64 + jt * 32 + l32;
+      for (int jt = 0; jt < 4; ++jt) {
         uint32_t w[4];
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
-          w[p] = (uint32_t)src[(2 * p) * EPITCH] | ((uint32_t)src[(2 * p + 1) * EPITCH] << 16);
+        for (int r = 0; r < 2; ++r) {
+          const int off = eoff(16 * ks + 4 * r + trow, tcol + 32 * jt);
+          const v4i16_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 v4i16_t *)(se + off));
+          const uint2 u = __builtin_bit_cast(uint2, t);
+          w[2 * r] = u.x;
+          w[2 * r + 1] = u.y;
+        }
         af[jt] = u32x4_t{w[0], w[1], w[2], w[3]};
       }
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        if (ct0 + wc * 4 + ct >= nct) continue;   // wave-uniform
-        const u32x4_t bf = *(const u32x4_t *)(Ps + (((wc * 4 + ct) * 4 + ks) * 64 + lane) * 8);
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt) acc[jt][ct] = mfma_32x32x16(af[jt], bf, acc[jt][ct]);
+      for (int ct = 0; ct < 2; ++ct) {
+        u32x4_t v = *(const u32x4_t *)(sp + ((wc * 2 + ct) * 2 + ks) * 1024 + lane * 16);
+        bf[ct] = u32x4_t{shift2(v[0], dn[ct]), shift2(v[1], dn[ct]), shift2(v[2], dn[ct]), shift2(v[3], dn[ct])};
       }
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) acc[jt][ct] = mfma_32x32x16(af[jt], bf[ct], acc[jt][ct]);
     }
+  };
+
+  __syncthreads();                                   // shift table visible
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < NIT) issue(s);
+  for (int it = 0; it < NIT; ++it) {
+    const int ahead = NIT - 1 - it;                  // stages issued beyond this one
+    if (ahead >= 2) dma_wait<8>();
+    else if (ahead == 1) dma_wait<4>();
+    else dma_wait<0>();
+    __syncthreads();
+    if (it + NS - 1 < NIT) issue(it + NS - 1);
+    compute(it);
   }
 
-  // Partial s for this vocabulary range: ps[split][c][j], 4 consecutive j per store.
+  // Partial s^T for this split: ps[split][c][j], 4 consecutive j per store.
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    const int c = cb + wc * 128 + ct * 32 + l32;
+  for (int ct = 0; ct < 2; ++ct) {
+    const int c = cb + (wc * 2 + ct) * 32 + l32;
     if (c >= a.Cpad) continue;
 #pragma unroll
-    for (int jt = 0; jt < 2; ++jt) {
+    for (int jt = 0; jt < 4; ++jt) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int j = j0 + wj * 64 + jt * 32 + 8 * q + 4 * hh;
+        const int j = j0 + wj * 128 + jt * 32 + 8 * q + 4 * hh;
         if (j >= a.d) continue;
         const float4 v = make_float4(acc[jt][ct][4 * q], acc[jt][ct][4 * q + 1],
                                      acc[jt][ct][4 * q + 2], acc[jt][ct][4 * q + 3]);
@@ -154,17 +201,20 @@ __global__ __launch_bounds__(256) void selfcond_split_kernel(SelfcondArgs a, int
   }
 }
 
+// s[c][j] = sum over splits (in split order) of gsc[split][c] * ps[split][c][j].
 __global__ __launch_bounds__(256) void selfcond_reduce_kernel(SelfcondArgs a) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;   // element of [Cpad][d]
   const int64_t n = (int64_t)a.Cpad * a.d;
   if (i >= n) return;
   const int c = (int)(i / a.d);
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int p = 0; p < a.nsc; ++p) {
-    const float4 v = *(const float4 *)(a.ps + (int64_t)p * n + i);
-    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  if (c < a.C) {
+    for (int p = 0; p < a.nsc; ++p) {
+      const float gs = a.gsc[(int64_t)p * a.Cpad + c];
+      const float4 v = *(const float4 *)(a.ps + (int64_t)p * n + i);
+      s.x += gs * v.x; s.y += gs * v.y; s.z += gs * v.z; s.w += gs * v.w;
+    }
   }
-  if (c >= a.C) s = make_float4(0.f, 0.f, 0.f, 0.f);
   const uint2 o = make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
   *(uint2 *)(a.s + i) = o;
 }
@@ -172,8 +222,15 @@ __global__ __launch_bounds__(256) void selfcond_reduce_kernel(SelfcondArgs a) {
 }  // namespace
 
 hipError_t dg_launch_selfcond(const SelfcondArgs &a, hipStream_t st) {
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void *)selfcond_split_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, SMEM);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
   const int nj = (a.d + BJ - 1) / BJ;
-  hipLaunchKernelGGL(selfcond_split_kernel, dim3(nj * a.nsc, (a.Cpad + BC - 1) / BC), dim3(256), 0,
+  hipLaunchKernelGGL(selfcond_split_kernel, dim3(nj * a.nsc, (a.Cpad + BC - 1) / BC), dim3(512), SMEM,
                      st, a, nj);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
