@@ -183,11 +183,17 @@ dg_status dg_canvas_attn(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens,
   GemmArgs g{};
   g.M = m.C;
   g.K = m.d;
-  g.tokens = tokens;
-  g.E = E;
-  g.z = z;
   g.V = m.V;
   g.status = ctx->d_status;
+  if (z) {
+    u16 *x = ws_at<u16>(ws, w.x);
+    hipError_t e = dg_launch_xgather(tokens, E, z, m.V, m.C, m.d, x, ctx->d_status, ctx->stream);
+    if (e != hipSuccess) return hip_fail(ctx, e, "dg_canvas_attn(gather)");
+    g.A = x;
+  } else {
+    g.tokens = tokens;
+    g.E = E;
+  }
   g.nseg = 3;
   g.seg[0] = GemmSeg{Wq, qd, q, qd, 0, 1, INT_MAX, m.C, 0};
   g.seg[1] = GemmSeg{Wk, kd, kc, kd, 0, 1, INT_MAX, w.Cpad, 0};

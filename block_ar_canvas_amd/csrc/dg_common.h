@@ -116,6 +116,7 @@ struct DgWs {
   size_t ps;       // self-cond partial s fp32 [nsc][Cpad][d]
   size_t s;        // s = p0 E rounded to bf16 [Cpad][d]
   size_t g;        // GELU(s W1^T) bf16 [Cpad][F]
+  size_t x;        // denoiser input E[x] + z, bf16 [Cpad][d]
   size_t total;
 };
 
@@ -176,6 +177,7 @@ static inline DgWs dg_ws_layout(int V, int d, int C, int Hq, int Hkv, int hd, in
   w.ps = take((size_t)w.nsc * w.Cpad * d * 4);
   w.s = take((size_t)w.Cpad * d * 2);
   w.g = take((size_t)w.Cpad * F * 2);
+  w.x = take((size_t)w.Cpad * d * 2);
   // Regions sized by the cache capacity come last, so every other offset is the same
   // whatever Pcap the layout is computed for.
   w.po = take((size_t)w.nsplit_max * Hq * w.Cpad * hd * 4);
@@ -198,16 +200,18 @@ struct GemmSeg {
 struct GemmArgs {
   int M, K;
   const u16 *A;        // plain activation [M][K], or NULL for the embedding gather
-  const int *tokens;   // gather: row m = E[tokens[m]] (+ z[m]), rounded to bf16
+  const int *tokens;   // gather: row m = E[tokens[m]]
   const u16 *E;
-  const u16 *z;        // NULL: no self-conditioning term
   int V;
   int *status;
   int gelu;            // apply exact GELU before storing
   int nseg;
   GemmSeg seg[3];
+  int store_mode[3];   // set by the launcher
 };
 hipError_t dg_launch_gemm(const GemmArgs &a, hipStream_t st);
+hipError_t dg_launch_xgather(const int *tokens, const u16 *E, const u16 *z, int V, int M, int K,
+                             u16 *X, int *status, hipStream_t st);
 
 struct AttnArgs {
   const u16 *Q;        // [Cpad][Hq*hd]

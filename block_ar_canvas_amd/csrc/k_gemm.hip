@@ -1,127 +1,239 @@
 // Small-M bf16 GEMM with fp32 accumulation: D[m][n] = sum_k X[m][k] W[n][k].
 //
 // Used for every dense projection of the step whose M is the canvas (C <= 1024):
-// the Q/K/V projections of the denoiser input X = E[x] + z (the gather and the bf16
-// rounding of the sum happen in the operand loader, so X never exists in memory),
-// the attention output projection Wo, the two self-conditioning FFW layers (exact-erf
-// GELU fused into the epilogue of the first) and the K/V projection of a committed
-// block. Up to three weight segments share one launch; each segment has its own output
-// address map out + m*sm + (n/seg)*sg + (n%seg)*se, which covers row-major outputs,
-// the transposed canvas V, and the [Hkv][Pcap][hd] / [Hkv][hd][Pcap] cache layouts.
+// the Q/K/V projections of the denoiser input X = E[x] + z, the attention output
+// projection Wo, the two self-conditioning FFW layers (exact-erf GELU fused into the
+// epilogue of the first) and the K/V projection of a committed block. Up to three
+// weight segments share one launch; each segment has its own output address map
+// out + m*sm + (n/seg)*sg + (n%seg)*se, which covers row-major outputs, the transposed
+// canvas V, and the [Hkv][Pcap][hd] / [Hkv][hd][Pcap] cache layouts.
 //
-// Tiling: 256 threads = 4 waves in a 2 (n) x 2 (m) grid, block tile 64 n x 64 m,
-// K in steps of 64 staged through LDS with a register prefetch of the next step.
-// Weight rows are MFMA A operands, activation rows B operands (see dg_common.h).
+// With M this small every workgroup streams a long K range for a small output tile, so
+// the kernel is bound by how fast operand bytes reach the CUs, not by the MFMAs:
+//   * Workgroup tile 64 n x 64 m, K in stages of 128 (256-byte row pieces), fed by
+//     direct global -> LDS copies (global_load_lds_dwordx4) into an NS-stage ring with
+//     one barrier per stage; 256-byte LDS rows are XOR-swizzled by (row & 15) so the
+//     fragment reads are conflict-free on 64 banks.
+//   * 8 waves; wave w computes the whole 64 x 64 tile (four independent 32 x 32
+//     accumulators) for k16-step w of every stage, so each wave issues four
+//     independent MFMAs per stage instead of a dependent chain. The eight partial
+//     tiles are summed through LDS in a fixed wave order (deterministic).
+//   * The epilogue (GELU, bf16 rounding) writes the tile to LDS and stores it with
+//     16-byte stores along whichever output direction is contiguous.
+//   * Workgroups that share a weight tile (same n tile, other m tiles) are placed on
+//     the same XCD, so each weight tile is fetched from HBM once per L2.
+// The embedding gather X = E[tokens] (rows read through per-lane addresses) is done by
+// the copies themselves; the self-conditioned input E[tokens] + z is formed once by
+// xgather_kernel (a bf16 add needs ALU work that a direct copy cannot do).
 #include "dg_common.h"
 
 namespace {
 
-constexpr int BN = 64, BM = 64, BK = 64, PITCH = BK + 8;
+constexpr int BN = 64, BM = 64, BK = 128, NW = 8, NS = 4;
+constexpr int RB = BK * 2;                  // bytes of one row piece per stage
+constexpr int TILE = 64 * RB;               // bytes of one operand tile per stage
+constexpr int STAGE = 2 * TILE;
+constexpr int RED = NW * 4 * 16 * 64 * 4;   // fp32 partial tiles of all waves
+constexpr int SMEM = NS * STAGE > RED ? NS * STAGE : RED;
+constexpr int OPITCH = BN + 8;              // bf16 output tile pitch (elements)
 
-struct Prefetch {
-  uint4 w[2];
-  uint4 x[2];
-  uint4 zx[2];
-};
+DG_DEV int swz(int row, int chunk) { return row * RB + ((chunk ^ (row & 15)) << 4); }
 
-__device__ __forceinline__ void load_tile(const GemmArgs &a, const GemmSeg &sg, int nb0, int m0,
-                                          int k0, int tid, Prefetch &pf) {
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int q = tid + 256 * it;
-    const int row = q >> 3, col = (q & 7) * 8;
-    const int n = nb0 + row, k = k0 + col;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (n < sg.N && k < a.K) v = *(const uint4 *)(sg.W + (int64_t)n * a.K + k);
-    pf.w[it] = v;
-    const int m = m0 + row;
-    uint4 x = make_uint4(0, 0, 0, 0), zx = make_uint4(0, 0, 0, 0);
-    if (m < a.M && k < a.K) {
-      if (a.A) {
-        x = *(const uint4 *)(a.A + (int64_t)m * a.K + k);
-      } else {
-        int t = a.tokens[m];
-        if (t < 0 || t >= a.V) {
-          if (k0 == 0 && col == 0) set_status(a.status, DGS_RANGE);
-          t = -1;
-        }
-        if (t >= 0) x = *(const uint4 *)(a.E + (int64_t)t * a.K + k);
-        if (a.z) zx = *(const uint4 *)(a.z + (int64_t)m * a.K + k);
-      }
-    }
-    pf.x[it] = x;
-    pf.zx[it] = zx;
+// s_waitcnt for "at most 4*rem of this wave's copies still in flight".
+DG_DEV void wait_stages(int rem) {
+  switch (rem) {
+    case 0: dma_wait<0>(); break;
+    case 1: dma_wait<4>(); break;
+    default: dma_wait<8>(); break;
   }
 }
 
-__device__ __forceinline__ void store_tile(const GemmArgs &a, u16 *Ws, u16 *Xs, int tid,
-                                           const Prefetch &pf) {
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int q = tid + 256 * it;
-    const int row = q >> 3, col = (q & 7) * 8;
-    *(uint4 *)(Ws + row * PITCH + col) = pf.w[it];
-    uint4 x = pf.x[it];
-    if (!a.A && a.z) {
-      // X = bf16(E[x] + z): the sum of two bf16 values in fp32, rounded once to bf16.
-      const uint32_t *e = (const uint32_t *)&pf.x[it];
-      const uint32_t *z = (const uint32_t *)&pf.zx[it];
-      uint32_t o[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        o[j] = pack_bf16x2(bf16lo(e[j]) + bf16lo(z[j]), bf16hi(e[j]) + bf16hi(z[j]));
-      x = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-    *(uint4 *)(Xs + row * PITCH + col) = x;
-  }
-}
+// Output store modes of a segment (chosen on the host).
+enum { ST_SCALAR = 0, ST_NVEC = 1, ST_MVEC = 2 };
 
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) u16 Ws[BN * PITCH];
-  __shared__ __attribute__((aligned(16))) u16 Xs[BM * PITCH];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wn = wave & 1, wm = wave >> 1;
+template <bool GATHER>
+__global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
 
+  // Tile of this workgroup; consecutive m tiles of one n tile share an XCD.
+  const int total = gridDim.x;
+  int idx = blockIdx.x;
+  if ((total & 7) == 0 && ((total >> 3) % MB) == 0) idx = (idx & 7) * (total >> 3) + (idx >> 3);
+  const int mb = idx % MB, nbg = idx / MB;
   int si = 0;
   for (int s = 1; s < a.nseg; ++s)
-    if ((int)blockIdx.x >= a.seg[s].nblk0) si = s;
+    if (nbg >= a.seg[s].nblk0) si = s;
   const GemmSeg &sg = a.seg[si];
-  const int nb0 = ((int)blockIdx.x - sg.nblk0) * BN;
-  const int m0 = blockIdx.y * BM;
+  const int nb0 = (nbg - sg.nblk0) * BN, m0 = mb * BM;
+  const int K = a.K;
+  const int nst = (K + BK - 1) / BK;
 
-  f32x16_t acc = {};
-  Prefetch pf;
-  load_tile(a, sg, nb0, m0, 0, tid, pf);
-  for (int k0 = 0; k0 < a.K; k0 += BK) {
-    __syncthreads();
-    store_tile(a, Ws, Xs, tid, pf);
-    __syncthreads();
-    if (k0 + BK < a.K) load_tile(a, sg, nb0, m0, k0 + BK, tid, pf);
+  // Copy assignment: wave w fills rows [8w, 8w + 8) of both tiles, 4 rows (1 KiB) per
+  // instruction; lane l covers row 8w + 4j + l/16, physical 16-byte chunk l % 16.
+  const u16 *wrow[2], *xrow[2];
+  int lchunk[2];
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const u32x4_t af = *(const u32x4_t *)(Ws + (wn * 32 + l32) * PITCH + ks * 16 + 8 * h);
-      const u32x4_t bf = *(const u32x4_t *)(Xs + (wm * 32 + l32) * PITCH + ks * 16 + 8 * h);
-      acc = mfma_32x32x16(af, bf, acc);
+  for (int j = 0; j < 2; ++j) {
+    const int R = 8 * wave + 4 * j + (lane >> 4);
+    lchunk[j] = (lane & 15) ^ (R & 15);
+    const int n = min(nb0 + R, sg.N - 1);
+    wrow[j] = sg.W + (int64_t)n * K;
+    const int m = min(m0 + R, a.M - 1);
+    if (GATHER) {
+      int tok = a.tokens[m];
+      if (tok < 0 || tok >= a.V) {
+        set_status(a.status, DGS_RANGE);
+        tok = 0;
+      }
+      xrow[j] = a.E + (int64_t)tok * K;
+    } else {
+      xrow[j] = a.A + (int64_t)m * K;
+    }
+  }
+  const uint32_t lbase = lds_addr(smem);
+  auto issue = [&](int i) {
+    const int k0 = i * BK;
+    const uint32_t wb = lbase + (uint32_t)((i % NS) * STAGE);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int k = min(k0 + 8 * lchunk[j], K - 8);   // chunks past K: any valid data
+      const uint32_t off = (uint32_t)((8 * wave + 4 * j) * RB);
+      dma16(wrow[j] + k, wb + off);
+      dma16(xrow[j] + k, wb + TILE + off);
+    }
+  };
+
+  f32x16_t acc[4] = {};
+  for (int i = 0; i < NS - 1 && i < nst; ++i) issue(i);
+  for (int i = 0; i < nst; ++i) {
+    wait_stages(min(nst - 1 - i, NS - 2));
+    __syncthreads();
+    if (i + NS - 1 < nst) issue(i + NS - 1);
+    if (i * BK + 16 * wave < K) {
+      const uint8_t *Ws = smem + (i % NS) * STAGE, *Xs = Ws + TILE;
+      const int c = 2 * wave + h;
+      const u32x4_t a0 = *(const u32x4_t *)(Ws + swz(l32, c));
+      const u32x4_t a1 = *(const u32x4_t *)(Ws + swz(32 + l32, c));
+      const u32x4_t b0 = *(const u32x4_t *)(Xs + swz(l32, c));
+      const u32x4_t b1 = *(const u32x4_t *)(Xs + swz(32 + l32, c));
+      acc[0] = mfma_32x32x16(a0, b0, acc[0]);
+      acc[1] = mfma_32x32x16(a1, b0, acc[1]);
+      acc[2] = mfma_32x32x16(a0, b1, acc[2]);
+      acc[3] = mfma_32x32x16(a1, b1, acc[3]);
     }
   }
 
-  const int m = m0 + wm * 32 + l32;
-  if (m >= sg.m_store) return;
+  // Sum of the eight waves' tiles. Tile q covers n [32(q&1), +32) x m [32(q>>1), +32).
+  __syncthreads();
+  float *red = (float *)smem;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int n = nb0 + wn * 32 + acc_row(r, h);
-    if (n >= sg.N) continue;
-    float v = acc[r];
-    if (a.gelu) v = 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
-    sg.out[(int64_t)m * sg.sm + (int64_t)(n / sg.seg) * sg.sg + (int64_t)(n % sg.seg) * sg.se] =
-        f32_to_bf16(v);
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[((wave * 4 + q) * 16 + r) * 64 + lane] = acc[q][r];
+  __syncthreads();
+  const int q = wave >> 1, rb = 8 * (wave & 1);
+  float v[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) s += red[((w * 4 + q) * 16 + rb + r) * 64 + lane];
+    if (a.gelu) s = 0.5f * s * (1.0f + erff(s * 0.70710678118654752f));
+    v[r] = s;
   }
+  __syncthreads();
+  u16 *ot = (u16 *)smem;   // [64 m][OPITCH] bf16
+  const int ml = (q >> 1) * 32 + l32;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) ot[ml * OPITCH + (q & 1) * 32 + acc_row(rb + r, h)] = f32_to_bf16(v[r]);
+  __syncthreads();
+
+  const int mode = a.store_mode[si];
+  if (mode == ST_NVEC) {
+    const int row = tid >> 3, c8 = (tid & 7) * 8;
+    const int m = m0 + row, n = nb0 + c8;
+    if (m < sg.m_store && n < sg.N)
+      *(uint4 *)(sg.out + (int64_t)m * sg.sm + (int64_t)(n / sg.seg) * sg.sg +
+                 (int64_t)(n % sg.seg) * sg.se) = *(const uint4 *)(ot + row * OPITCH + c8);
+  } else if (mode == ST_MVEC) {
+    const int col = tid >> 3, r8 = (tid & 7) * 8;
+    const int m = m0 + r8, n = nb0 + col;
+    if (n < sg.N && m + 8 > sg.m_store) {
+      for (int i = 0; i < 8 && m + i < sg.m_store; ++i)
+        sg.out[(int64_t)(m + i) + (int64_t)(n / sg.seg) * sg.sg + (int64_t)(n % sg.seg) * sg.se] =
+            ot[(r8 + i) * OPITCH + col];
+    } else if (n < sg.N) {
+      uint32_t w4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w4[i] = (uint32_t)ot[(r8 + 2 * i) * OPITCH + col] |
+                ((uint32_t)ot[(r8 + 2 * i + 1) * OPITCH + col] << 16);
+      *(uint4 *)(sg.out + (int64_t)m + (int64_t)(n / sg.seg) * sg.sg + (int64_t)(n % sg.seg) * sg.se) =
+          make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    }
+  } else {
+    const int row = tid >> 3, c8 = (tid & 7) * 8;
+    const int m = m0 + row;
+    if (m < sg.m_store) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int n = nb0 + c8 + i;
+        if (n < sg.N)
+          sg.out[(int64_t)m * sg.sm + (int64_t)(n / sg.seg) * sg.sg + (int64_t)(n % sg.seg) * sg.se] =
+              ot[row * OPITCH + c8 + i];
+      }
+    }
+  }
+}
+
+// X[m][k] = bf16(E[tokens[m]][k] + z[m][k]) for m < M; an out-of-range token sets the
+// range status and contributes a zero embedding row.
+__global__ __launch_bounds__(256) void xgather_kernel(const int *tokens, const u16 *E,
+                                                      const u16 *z, int V, int K, u16 *X,
+                                                      int *status) {
+  const int m = blockIdx.x;
+  const int tok = tokens[m];
+  const bool ok = tok >= 0 && tok < V;
+  if (!ok && threadIdx.x == 0) set_status(status, DGS_RANGE);
+  for (int k = threadIdx.x * 8; k < K; k += 256 * 8) {
+    const uint4 zz = *(const uint4 *)(z + (int64_t)m * K + k);
+    const uint4 ee = ok ? *(const uint4 *)(E + (int64_t)tok * K + k) : make_uint4(0, 0, 0, 0);
+    const uint32_t *e = (const uint32_t *)&ee, *zw = (const uint32_t *)&zz;
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o[j] = pack_bf16x2(bf16lo(e[j]) + bf16lo(zw[j]), bf16hi(e[j]) + bf16hi(zw[j]));
+    *(uint4 *)(X + (int64_t)m * K + k) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+// 16-byte stores are used when eight consecutive n (or m) map to one aligned run.
+int store_mode(const GemmSeg &s) {
+  if (!aligned16(s.out)) return ST_SCALAR;
+  const bool seg8 = s.seg % 8 == 0 || s.seg >= (1 << 30);   // INT_MAX: one segment
+  if (s.se == 1 && seg8 && s.sm % 8 == 0 && s.sg % 8 == 0) return ST_NVEC;
+  if (s.sm == 1 && seg8 && s.se % 8 == 0 && s.sg % 8 == 0) return ST_MVEC;
+  return ST_SCALAR;
 }
 
 }  // namespace
 
 hipError_t dg_launch_gemm(const GemmArgs &a0, hipStream_t st) {
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<false>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, SMEM);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void *)gemm_kernel<true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, SMEM);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
   GemmArgs a = a0;
   int nblk = 0;
   int mmax = a.M;
@@ -129,8 +241,19 @@ hipError_t dg_launch_gemm(const GemmArgs &a0, hipStream_t st) {
     a.seg[s].nblk0 = nblk;
     nblk += (a.seg[s].N + BN - 1) / BN;
     if (a.seg[s].m_store > mmax) mmax = a.seg[s].m_store;
+    a.store_mode[s] = store_mode(a.seg[s]);
   }
-  dim3 grid(nblk, (mmax + BM - 1) / BM);
-  hipLaunchKernelGGL(gemm_kernel, grid, dim3(256), 0, st, a);
+  const int MB = (mmax + BM - 1) / BM;
+  const dim3 grid(nblk * MB);
+  if (a.A)
+    hipLaunchKernelGGL(gemm_kernel<false>, grid, dim3(512), SMEM, st, a, MB);
+  else
+    hipLaunchKernelGGL(gemm_kernel<true>, grid, dim3(512), SMEM, st, a, MB);
+  return hipGetLastError();
+}
+
+hipError_t dg_launch_xgather(const int *tokens, const u16 *E, const u16 *z, int V, int M, int K,
+                             u16 *X, int *status, hipStream_t st) {
+  hipLaunchKernelGGL(xgather_kernel, dim3(M), dim3(256), 0, st, tokens, E, z, V, K, X, status);
   return hipGetLastError();
 }
