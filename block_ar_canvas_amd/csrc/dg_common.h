@@ -89,7 +89,7 @@ DG_DEV void set_status(int *status, int code) {
 // ------------------------------------------------------------------ tiling constants
 #define DG_CT 32        // canvas columns per MFMA tile
 #define DG_BV 256       // vocabulary rows per logits tile (one set of tile statistics)
-#define DG_KT 32        // keys per attention tile
+#define DG_KT 64        // keys per attention tile
 
 static inline int64_t dg_round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 static inline int64_t dg_cdiv(int64_t x, int64_t m) { return (x + m - 1) / m; }
@@ -120,13 +120,14 @@ struct DgWs {
   size_t total;
 };
 
-// Attention split count for a given number of cached tokens (non-decreasing in P).
+// Attention split count for a given number of cached tokens (non-decreasing in P):
+// about one workgroup (one KV head, 128 query rows, one key range) per CU, with at
+// least 4 key tiles of 64 per range.
 static inline int dg_attn_nsplit(int Hkv, int Hq, int C, int64_t P) {
-  const int64_t rows = (int64_t)(Hq / Hkv) * C;
-  const int64_t nq = dg_cdiv(rows, 256);
-  const int64_t tiles = dg_cdiv(dg_round_up(C, DG_CT), DG_KT) + dg_cdiv(P, DG_KT);
-  int64_t ns = dg_cdiv(512, (int64_t)Hkv * nq);       // aim at >= 512 workgroups
-  const int64_t by_len = dg_cdiv(tiles, 8);              // >= 8 key tiles per part
+  const int64_t nq = dg_cdiv((int64_t)(Hq / Hkv) * C, 128);
+  const int64_t tiles = dg_cdiv(C, DG_KT) + dg_cdiv(P, DG_KT);
+  int64_t ns = dg_cdiv(256, (int64_t)Hkv * nq);
+  const int64_t by_len = dg_cdiv(tiles, 4);
   if (ns > by_len) ns = by_len;
   if (ns < 1) ns = 1;
   if (ns > 256) ns = 256;

@@ -6,44 +6,78 @@
 // chapter "DiffusionGemma", the per-phase attention masks: the current canvas uses
 // full bidirectional attention and reads the cache). Attention is a softmax over a
 // set of keys, so the key order is free: the kernel walks the canvas keys first, then
-// the prefix, in tiles of 32 that never straddle the two segments.
+// the prefix, in tiles of 64 that never straddle the two segments.
 //
 // Work split (split-K / "flash decoding" over keys): a workgroup owns one KV head g,
-// 256 query rows of that head's group (row = (head in group, canvas position)) and
-// a contiguous range of key tiles. It streams K and V^T tiles HBM -> registers -> LDS
-// (the next tile is prefetched into registers while the current one is consumed) and
-// keeps an online softmax per query row in the log2 domain. Partial (O, max, sum) go
-// to the workspace; attn_merge_kernel combines the parts in a fixed order.
+// 128 query rows of that head's group (row = (head in group, canvas position)) and a
+// contiguous range of key tiles. Eight waves: wave (qg, kh) holds 32 query rows
+// (qg = 0..3) and takes key half kh of every 64-key tile, with its own online softmax;
+// the two halves are merged through LDS at the end. K and V^T tiles stream HBM -> LDS
+// through direct copies (global_load_lds_dwordx4) in a 3-stage ring, one barrier per
+// tile. The split's partial (O, max, sum) go to the workspace as row-major fp32
+// (coalesced), and attn_merge_kernel combines the splits in a fixed order.
 //
 // Orientation: S^T = K Q^T (keys are MFMA rows, loaded through perm_row so that the
 // probabilities come out as ready B fragments), O^T = V^T P^T (V is stored transposed
 // in the cache, so its A fragments are contiguous 16-byte LDS reads). Each lane owns
 // one query row: its softmax statistics need only one cross-lane exchange (lane ^ 32).
+//
+// Softmax reference: a lane keeps the reference m_ref its probabilities are scaled
+// against and moves it (rescaling O and the sum) only when the running maximum
+// exceeds it by more than 8 in log2 units, so probabilities stay below 2^8 and the
+// O rescale (64 accumulator registers per lane) is rare after the first tiles.
 #include "dg_common.h"
 
 namespace {
 
-constexpr int KT = DG_KT;
+constexpr int KT = 64;      // keys per tile
+constexpr int NS = 3;       // copy ring stages
+constexpr int QB = 128;     // query rows per workgroup
+constexpr float RESCALE_LOG2 = 8.f;
 
 template <int HD>
-struct AttnCfg {
-  static constexpr int EROWS = HD < 32 ? 32 : HD;   // V^T rows padded to an MFMA tile
-  static constexpr int ET = EROWS / 32;             // e-tiles of O^T
-  static constexpr int KS = HD / 16;                // k-steps of S = K Q^T
-  static constexpr int KPITCH = HD + 8;
-  static constexpr int VPITCH = KT + 8;
-  static constexpr int KCHUNKS = KT * HD / 8;       // 16-byte chunks per K tile
-  static constexpr int VCHUNKS = HD * KT / 8;
+struct Cfg {
+  static constexpr int ER = HD < 32 ? 32 : HD;       // V^T rows padded to an MFMA tile
+  static constexpr int ET = ER / 32;                 // e-tiles of O^T
+  static constexpr int KS = HD / 16;                 // k-steps of S = K Q^T
+  static constexpr int KRB = HD * 2;                 // bytes per K row
+  static constexpr int KTILE = KT * KRB;             // K tile bytes
+  static constexpr int VTILE = ER * KT * 2;          // V^T tile bytes (128-byte rows)
+  static constexpr int STAGE = KTILE + VTILE;
+  static constexpr int KI = KTILE / 1024;            // copy instructions for K
+  static constexpr int VI = HD * KT * 2 / 1024;      // copy instructions for V^T
+  static constexpr int TI = KI + VI;
+  static constexpr int PER_WAVE = TI >= 8 ? TI / 8 : 1;   // copies per issuing wave
+  static constexpr int KSH = HD == 128 ? 0 : HD == 64 ? 1 : HD == 32 ? 2 : 3;
+  static constexpr int OSLOT_ACC = ET * 16 * 64 * 4;      // one wave's O^T registers
+  static constexpr int OSLOT_T = 32 * (HD + 4) * 4;       // 32 rows x HD fp32 (padded)
+  static constexpr int OSLOT = OSLOT_ACC > OSLOT_T ? OSLOT_ACC : OSLOT_T;
+  static constexpr int SMEM_RING = NS * STAGE;
+  static constexpr int SMEM_END = 4 * OSLOT + 4 * 64 * 2 * 4;
+  static constexpr int SMEM = SMEM_RING > SMEM_END ? SMEM_RING : SMEM_END;
 };
 
+// K rows: physical 16-byte chunk = logical ^ fk(row) (conflict-free A-fragment reads).
 template <int HD>
-__global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a, int nq, int ntc,
-                                                         int ntiles, int units) {
-  using Cfg = AttnCfg<HD>;
-  __shared__ __attribute__((aligned(16))) u16 Ks[KT * Cfg::KPITCH];
-  __shared__ __attribute__((aligned(16))) u16 Vs[Cfg::EROWS * Cfg::VPITCH];
+DG_DEV int kswz(int row, int chunk) {
+  return row * Cfg<HD>::KRB + ((chunk ^ ((row >> Cfg<HD>::KSH) & (HD / 8 - 1))) << 4);
+}
+DG_DEV int vswz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+template <int N>
+DG_DEV void wait_ring(int rem) {
+  if (rem <= 0) dma_wait<0>();
+  else dma_wait<N>();
+}
+
+template <int HD>
+__global__ __launch_bounds__(512) void attn_split_kernel(AttnArgs a, int nq, int ntc,
+                                                         int ntiles, int units) {
+  using F = Cfg<HD>;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qg = wave & 3, kh = wave >> 2;
   const int hh = lane >> 5, l32 = lane & 31;
 
   // Workgroups that read the same key range (same unit) land on the same XCD.
@@ -62,211 +96,241 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a, int nq, int
   const int t0 = (int)((int64_t)split * ntiles / a.nsplit);
   const int t1 = (int)((int64_t)(split + 1) * ntiles / a.nsplit);
 
-  // Zero the padded V^T rows once (head dims below one MFMA tile).
-  if (Cfg::EROWS > HD) {
-    for (int i = tid; i < (Cfg::EROWS - HD) * Cfg::VPITCH; i += 256) Vs[HD * Cfg::VPITCH + i] = 0;
-  }
-
-  // Query rows of this wave: two 32-row column tiles.
-  int qrow_c[2], qrow_h[2];
-  bool qrow_ok[2];
-  u32x4_t qf[2][Cfg::KS];
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    const int r = qb * 256 + wave * 64 + ct * 32 + l32;
-    qrow_ok[ct] = r < G * a.C;
-    const int hi = qrow_ok[ct] ? r / a.C : 0;
-    qrow_c[ct] = qrow_ok[ct] ? r % a.C : 0;
-    qrow_h[ct] = g * G + hi;
-#pragma unroll
-    for (int ks = 0; ks < Cfg::KS; ++ks) {
-      u32x4_t v = {0, 0, 0, 0};
-      if (qrow_ok[ct])
-        v = *(const u32x4_t *)(a.Q + (int64_t)qrow_c[ct] * a.Hq * HD + qrow_h[ct] * HD +
-                               ks * 16 + 8 * hh);
-      qf[ct][ks] = v;
+  // Padded V^T rows (head dims below one MFMA tile) are zero in every ring slot.
+  if (F::ER > HD) {
+    for (int i = tid; i < NS * (F::ER - HD) * 32; i += 512) {
+      const int s = i / ((F::ER - HD) * 32), o = i % ((F::ER - HD) * 32);
+      *(uint32_t *)(smem + s * F::STAGE + F::KTILE + HD * 128 + 4 * o) = 0;
     }
   }
 
-  f32x16_t O[2][Cfg::ET];
+  // Query rows of this wave: r = qb*128 + qg*32 + l32 -> (head, canvas position).
+  const int r = qb * QB + qg * 32 + l32;
+  const bool qok = r < G * a.C;
+  const int qh = g * G + (qok ? r / a.C : 0), qc = qok ? r % a.C : 0;
+  u32x4_t qf[F::KS];
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-    for (int et = 0; et < Cfg::ET; ++et) O[ct][et] = f32x16_t{};
-  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+  for (int ks = 0; ks < F::KS; ++ks) {
+    u32x4_t v = {0, 0, 0, 0};
+    if (qok) v = *(const u32x4_t *)(a.Q + (int64_t)qc * a.Hq * HD + qh * HD + ks * 16 + 8 * hh);
+    qf[ks] = v;
+  }
 
-  // Register prefetch of one K tile and one V^T tile (at most 2 chunks each per thread).
-  uint4 pk[2], pv[2];
-  auto load = [&](int t) {
+  // Copies of tile t into ring slot `slot`. Instruction i (of TI) covers 1 KiB of the
+  // stage: K tile bytes for i < KI, V^T tile bytes after that.
+  const uint32_t lbase = lds_addr(smem);
+  auto issue = [&](int t, int slot) {
     const bool canvas = t < ntc;
-    const int kbase = canvas ? t * KT : (t - ntc) * KT;
-    const int64_t nvalid = canvas ? a.C : a.P;
+    const int k0 = (canvas ? t : t - ntc) * KT;
+    const int seglen = canvas ? a.C : (int)a.P;
+    const uint32_t sb = lbase + (uint32_t)(slot * F::STAGE);
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int q = tid + 256 * it;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (q < Cfg::KCHUNKS) {
-        const int kr = q / (HD / 8), col = (q % (HD / 8)) * 8;
-        const int key = kbase + kr;
-        if (key < nvalid) {
-          const u16 *src = canvas ? a.Kc + (int64_t)key * a.Hkv * HD + g * HD + col
-                                  : a.Kp + ((int64_t)g * a.Pcap + key) * HD + col;
-          v = *(const uint4 *)src;
-        }
-      }
-      pk[it] = v;
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (q < Cfg::VCHUNKS) {
-        const int e = q / (KT / 8), col = (q % (KT / 8)) * 8;
-        const int start = kbase + col;
-        if (canvas) {
-          w = *(const uint4 *)(a.Vct + ((int64_t)g * HD + e) * a.Cpad + start);
-        } else if (start < a.P) {
-          w = *(const uint4 *)(a.Vt + ((int64_t)g * HD + e) * a.Pcap + start);
-          const int64_t nv = a.P - start;   // zero the tail beyond the cached length
-          if (nv < 8) {
-            uint32_t *ww = (uint32_t *)&w;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              if (2 * j >= nv) ww[j] = 0;
-              else if (2 * j + 1 >= nv) ww[j] &= 0xFFFFu;
-            }
-          }
-        }
-      }
-      pv[it] = w;
-    }
-  };
-  auto store = [&]() {
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int q = tid + 256 * it;
-      if (q < Cfg::KCHUNKS) {
-        const int kr = q / (HD / 8), col = (q % (HD / 8)) * 8;
-        *(uint4 *)(Ks + kr * Cfg::KPITCH + col) = pk[it];
-      }
-      if (q < Cfg::VCHUNKS) {
-        const int e = q / (KT / 8), col = (q % (KT / 8)) * 8;
-        *(uint4 *)(Vs + e * Cfg::VPITCH + col) = pv[it];
+    for (int j = 0; j < F::PER_WAVE; ++j) {
+      const int i = wave + 8 * j;
+      if (i >= F::TI) break;
+      const int off = (i < F::KI ? i : i - F::KI) * 1024 + 16 * lane;
+      const u16 *src;
+      if (i < F::KI) {
+        const int row = off / F::KRB, pc = (off % F::KRB) >> 4;
+        const int lc = pc ^ ((row >> F::KSH) & (HD / 8 - 1));
+        const int key = min(k0 + row, seglen - 1);
+        src = canvas ? a.Kc + (int64_t)key * a.Hkv * HD + g * HD + 8 * lc
+                     : a.Kp + ((int64_t)g * a.Pcap + key) * HD + 8 * lc;
+        dma16(src, sb + i * 1024);
+      } else {
+        const int e = off >> 7, pc = (off & 127) >> 4;
+        const int lc = pc ^ ((e >> 1) & 7);
+        int ks = k0 + 8 * lc;
+        if (ks >= seglen) ks = (seglen - 1) & ~7;
+        src = canvas ? a.Vct + ((int64_t)g * HD + e) * a.Cpad + ks
+                     : a.Vt + ((int64_t)g * HD + e) * a.Pcap + ks;
+        dma16(src, sb + F::KTILE + (i - F::KI) * 1024);
       }
     }
   };
 
-  if (t0 < t1) load(t0);
-  for (int t = t0; t < t1; ++t) {
-    __syncthreads();
-    store();
-    __syncthreads();
-    if (t + 1 < t1) load(t + 1);
+  f32x16_t O[F::ET];
+#pragma unroll
+  for (int et = 0; et < F::ET; ++et) O[et] = f32x16_t{};
+  float mref = -INFINITY, lsum = 0.f;
 
+  const int nt = t1 - t0;
+  for (int i = 0; i < NS - 1 && i < nt; ++i) issue(t0 + i, i);
+  for (int i = 0; i < nt; ++i) {
+    const int t = t0 + i;
+    wait_ring<F::PER_WAVE>(min(nt - 1 - i, NS - 2));
+    __syncthreads();
+    if (i + NS - 1 < nt) issue(t + NS - 1, (i + NS - 1) % NS);
     const bool canvas = t < ntc;
-    const int kbase = canvas ? t * KT : (t - ntc) * KT;
-    const int64_t nvalid = canvas ? a.C : a.P;
-
-    // S^T tile: 32 keys x 32 query rows per column tile.
-    f32x16_t S[2] = {f32x16_t{}, f32x16_t{}};
-#pragma unroll
-    for (int ks = 0; ks < Cfg::KS; ++ks) {
-      const u32x4_t af = *(const u32x4_t *)(Ks + perm_row(l32) * Cfg::KPITCH + ks * 16 + 8 * hh);
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) S[ct] = mfma_32x32x16(af, qf[ct][ks], S[ct]);
-    }
-
-    // Online softmax (log2 domain) per query row; probabilities become B fragments.
-    u32x4_t pf[2][2];
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      float x[16];
-      float mt = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kbase + acc_row_perm(r, hh);
-        x[r] = key < nvalid ? S[ct][r] * a.scale_log2 : -INFINITY;
-        mt = fmaxf(mt, x[r]);
+    const int k0 = (canvas ? t : t - ntc) * KT;
+    const int nvalid = min(KT, (canvas ? a.C : (int)a.P) - k0);
+    uint8_t *Ks = smem + (i % NS) * F::STAGE;
+    uint8_t *Vs = Ks + F::KTILE;
+    if (nvalid < KT) {
+      // Tail tile: zero V^T at keys >= nvalid (cache slots past the valid length may
+      // hold any bit pattern, and 0 * NaN would poison O).
+      for (int x = tid; x < HD * (KT - nvalid); x += 512) {
+        const int e = x / (KT - nvalid), key = nvalid + x % (KT - nvalid);
+        *(u16 *)(Vs + vswz(e, key >> 3) + 2 * (key & 7)) = 0;
       }
-      mt = fmaxf(mt, wave_xor32(mt));
-      const float mnew = fmaxf(mrun[ct], mt);
-      const float alpha = exp2f(mrun[ct] - mnew);
-      float ls = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        x[r] = exp2f(x[r] - mnew);
-        ls += x[r];
-      }
-      ls += wave_xor32(ls);
-      lrun[ct] = lrun[ct] * alpha + ls;
-      mrun[ct] = mnew;
-#pragma unroll
-      for (int et = 0; et < Cfg::ET; ++et) O[ct][et] *= alpha;
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-        pf[ct][s] = u32x4_t{pack_bf16x2(x[8 * s + 0], x[8 * s + 1]), pack_bf16x2(x[8 * s + 2], x[8 * s + 3]),
-                            pack_bf16x2(x[8 * s + 4], x[8 * s + 5]), pack_bf16x2(x[8 * s + 6], x[8 * s + 7])};
+      __syncthreads();
     }
+    if (32 * kh >= nvalid) continue;   // this key half is empty
 
-    // O^T += V^T P^T
+    // S^T tile: 32 keys (half kh) x 32 query rows.
+    f32x16_t S = {};
 #pragma unroll
-    for (int et = 0; et < Cfg::ET; ++et) {
+    for (int ks = 0; ks < F::KS; ++ks) {
+      const u32x4_t af = *(const u32x4_t *)(Ks + kswz<HD>(32 * kh + perm_row(l32), 2 * ks + hh));
+      S = mfma_32x32x16(af, qf[ks], S);
+    }
+    float y[16];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int key = 32 * kh + acc_row_perm(rr, hh);
+      y[rr] = key < nvalid ? S[rr] * a.scale_log2 : -INFINITY;
+      mt = fmaxf(mt, y[rr]);
+    }
+    mt = fmaxf(mt, wave_xor32(mt));
+    if (__builtin_amdgcn_ballot_w64(mt > mref + RESCALE_LOG2)) {
+      const float mnew = fmaxf(mref, mt);
+      const float alpha = exp2f(mref - mnew);
+      lsum *= alpha;
+#pragma unroll
+      for (int et = 0; et < F::ET; ++et) O[et] *= alpha;
+      mref = mnew;
+    }
+    float ls = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      y[rr] = exp2f(y[rr] - mref);
+      ls += y[rr];
+    }
+    lsum += ls + wave_xor32(ls);
+    u32x4_t pf[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      pf[s] = u32x4_t{pack_bf16x2(y[8 * s + 0], y[8 * s + 1]), pack_bf16x2(y[8 * s + 2], y[8 * s + 3]),
+                      pack_bf16x2(y[8 * s + 4], y[8 * s + 5]), pack_bf16x2(y[8 * s + 6], y[8 * s + 7])};
+    // O^T += V^T P^T over the 32 keys of this half.
+#pragma unroll
+    for (int et = 0; et < F::ET; ++et) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const u32x4_t af = *(const u32x4_t *)(Vs + (et * 32 + l32) * Cfg::VPITCH + 16 * s + 8 * hh);
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) O[ct][et] = mfma_32x32x16(af, pf[ct][s], O[ct][et]);
+        const u32x4_t af = *(const u32x4_t *)(Vs + vswz(et * 32 + l32, 4 * kh + 2 * s + hh));
+        O[et] = mfma_32x32x16(af, pf[s], O[et]);
       }
     }
   }
 
-  // Partial results of this key range.
+  // Merge the two key halves of each query group through LDS, then store the split's
+  // partial O row-major (coalesced) and its (max, sum).
+  dma_wait<0>();
+  __syncthreads();
+  float *ml = (float *)(smem + 4 * F::OSLOT);   // [qg][lane][2]
+  uint8_t *slot = smem + qg * F::OSLOT;
+  if (kh == 1) {
+    float *d = (float *)slot;
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    if (!qrow_ok[ct]) continue;
-    const int64_t row = ((int64_t)split * a.Hq + qrow_h[ct]) * a.Cpad + qrow_c[ct];
-    if (hh == 0) {
-      a.pml[2 * row] = mrun[ct];
-      a.pml[2 * row + 1] = lrun[ct];
-    }
+    for (int et = 0; et < F::ET; ++et)
 #pragma unroll
-    for (int et = 0; et < Cfg::ET; ++et) {
+      for (int rr = 0; rr < 16; ++rr) d[(et * 16 + rr) * 64 + lane] = O[et][rr];
+    ml[(qg * 64 + lane) * 2] = mref;
+    ml[(qg * 64 + lane) * 2 + 1] = lsum;
+  }
+  __syncthreads();
+  if (kh == 0) {
+    const float m1 = ml[(qg * 64 + lane) * 2], l1 = ml[(qg * 64 + lane) * 2 + 1];
+    const float M = fmaxf(mref, m1);
+    const float a0 = M == -INFINITY ? 0.f : exp2f(mref - M);
+    const float a1 = M == -INFINITY ? 0.f : exp2f(m1 - M);
+    const float *d = (const float *)slot;
+    float o[F::ET * 16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int e = et * 32 + acc_row(r, hh);
-        if (e < HD) a.po[row * HD + e] = O[ct][et][r];
+    for (int et = 0; et < F::ET; ++et)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr)
+        o[et * 16 + rr] = O[et][rr] * a0 + d[(et * 16 + rr) * 64 + lane] * a1;
+    // transposed tile [query l32][e], pitch HD + 4 floats (same slot, read above)
+    float *ot = (float *)slot;
+#pragma unroll
+    for (int et = 0; et < F::ET; ++et)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int e = et * 32 + acc_row(rr, hh);
+        if (e < HD) ot[l32 * (HD + 4) + e] = o[et * 16 + rr];
       }
+    if (hh == 0 && qok) {
+      const int64_t row = ((int64_t)split * a.Hq + qh) * a.Cpad + qc;
+      a.pml[2 * row] = M;
+      a.pml[2 * row + 1] = lsum * a0 + l1 * a1;
     }
+  }
+  __syncthreads();
+  constexpr int F4 = HD / 4;   // float4 per row
+  for (int f = tid; f < QB * F4; f += 512) {
+    const int row = f / F4, c4 = f % F4;
+    const int rq = qb * QB + row;
+    if (rq >= G * a.C) continue;
+    const int h = g * G + rq / a.C, c = rq % a.C;
+    const float *src = (const float *)(smem + (row >> 5) * F::OSLOT) + (row & 31) * (HD + 4) + 4 * c4;
+    *(float4 *)(a.po + (((int64_t)split * a.Hq + h) * a.Cpad + c) * HD + 4 * c4) =
+        make_float4(src[0], src[1], src[2], src[3]);
   }
 }
 
-// Log-sum-exp merge of the key-range partials, in split order.
+// Log-sum-exp merge of the key-range partials, in split order. HD/8 threads per
+// output row, eight head dims each.
 template <int HD>
-__global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a) {
-  const int h = blockIdx.x / a.C, c = blockIdx.x % a.C, e = threadIdx.x;
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+  constexpr int TPR = HD / 8, RPB = 256 / TPR;
+  const int row = blockIdx.x * RPB + threadIdx.x / TPR;
+  if (row >= a.Hq * a.C) return;
+  const int h = row / a.C, c = row % a.C, e0 = (threadIdx.x % TPR) * 8;
   float M = -INFINITY;
+  for (int s = 0; s < a.nsplit; ++s)
+    M = fmaxf(M, a.pml[2 * (((int64_t)s * a.Hq + h) * a.Cpad + c)]);
+  float L = 0.f, o[8] = {};
   for (int s = 0; s < a.nsplit; ++s) {
-    const int64_t row = ((int64_t)s * a.Hq + h) * a.Cpad + c;
-    M = fmaxf(M, a.pml[2 * row]);
+    const int64_t pr = ((int64_t)s * a.Hq + h) * a.Cpad + c;
+    const float ms = a.pml[2 * pr];
+    const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
+    L += a.pml[2 * pr + 1] * w;
+    const float4 *p = (const float4 *)(a.po + pr * HD + e0);
+    const float4 x0 = p[0], x1 = p[1];
+    o[0] += x0.x * w; o[1] += x0.y * w; o[2] += x0.z * w; o[3] += x0.w * w;
+    o[4] += x1.x * w; o[5] += x1.y * w; o[6] += x1.z * w; o[7] += x1.w * w;
   }
-  float L = 0.f, o = 0.f;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const int64_t row = ((int64_t)s * a.Hq + h) * a.Cpad + c;
-    const float w = exp2f(a.pml[2 * row] - M);
-    L += a.pml[2 * row + 1] * w;
-    if (e < HD) o += a.po[row * HD + e] * w;
-  }
-  if (e < HD) a.O[(int64_t)c * a.Hq * HD + h * HD + e] = f32_to_bf16(o / L);
+  const float inv = 1.f / L;
+  uint4 out;
+  out.x = pack_bf16x2(o[0] * inv, o[1] * inv);
+  out.y = pack_bf16x2(o[2] * inv, o[3] * inv);
+  out.z = pack_bf16x2(o[4] * inv, o[5] * inv);
+  out.w = pack_bf16x2(o[6] * inv, o[7] * inv);
+  *(uint4 *)(a.O + (int64_t)c * a.Hq * HD + h * HD + e0) = out;
 }
 
 template <int HD>
 hipError_t launch(const AttnArgs &a, hipStream_t st) {
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void *)attn_split_kernel<HD>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, Cfg<HD>::SMEM);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
   const int G = a.Hq / a.Hkv;
-  const int nq = (G * a.C + 255) / 256;
-  const int ntc = a.Cpad / KT;
+  const int nq = (G * a.C + QB - 1) / QB;
+  const int ntc = (a.C + KT - 1) / KT;
   const int ntiles = ntc + (int)((a.P + KT - 1) / KT);
   const int units = a.Hkv * a.nsplit;
-  hipLaunchKernelGGL(attn_split_kernel<HD>, dim3(units * nq), dim3(256), 0, st, a, nq, ntc,
-                     ntiles, units);
+  hipLaunchKernelGGL(attn_split_kernel<HD>, dim3(units * nq), dim3(512), Cfg<HD>::SMEM, st, a, nq,
+                     ntc, ntiles, units);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_merge_kernel<HD>, dim3(a.Hq * a.C), dim3(128), 0, st, a);
+  constexpr int RPB = 256 / (HD / 8);
+  hipLaunchKernelGGL(attn_merge_kernel<HD>, dim3((a.Hq * a.C + RPB - 1) / RPB), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
