@@ -59,6 +59,20 @@ DG_DEV uint32_t pack_bf16x2(float lo, float hi) {
 
 DG_DEV float wave_xor32(float v) { return __shfl_xor(v, 32, 64); }
 DG_DEV int wave_xor32(int v) { return __shfl_xor(v, 32, 64); }
+// Max / sum over the lane pair (l, l ^ 32) without an LDS round trip: one
+// v_permlane32_swap leaves {v[l], v[l ^ 32]} in the two registers of every lane (in an
+// order that depends on the half, which neither symmetric operation sees).
+DG_DEV float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+DG_DEV float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// 2^x by the hardware instruction (no denormal-range fix-up: results below 2^-126 may
+// flush to zero, which no softmax weight here can notice).
+DG_DEV float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Direct global -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4):
 // lane l's 16 bytes land at LDS byte address lds_base + 16*l, lds_base wave-uniform.

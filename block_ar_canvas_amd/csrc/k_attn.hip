@@ -177,37 +177,46 @@ __global__ __launch_bounds__(512) void attn_split_kernel(AttnArgs a, int nq, int
     }
     if (32 * kh >= nvalid) continue;   // this key half is empty
 
-    // S^T tile: 32 keys (half kh) x 32 query rows.
-    f32x16_t S = {};
+    // S^T tile: 32 keys (half kh) x 32 query rows; even and odd k-steps accumulate
+    // separately to halve the dependent MFMA chain.
+    f32x16_t S0 = {}, S1 = {};
 #pragma unroll
-    for (int ks = 0; ks < F::KS; ++ks) {
-      const u32x4_t af = *(const u32x4_t *)(Ks + kswz<HD>(32 * kh + perm_row(l32), 2 * ks + hh));
-      S = mfma_32x32x16(af, qf[ks], S);
+    for (int ks = 0; ks < F::KS; ks += 2) {
+      const u32x4_t a0 = *(const u32x4_t *)(Ks + kswz<HD>(32 * kh + perm_row(l32), 2 * ks + hh));
+      S0 = mfma_32x32x16(a0, qf[ks], S0);
+      if (ks + 1 < F::KS) {
+        const u32x4_t a1 = *(const u32x4_t *)(Ks + kswz<HD>(32 * kh + perm_row(l32), 2 * ks + 2 + hh));
+        S1 = mfma_32x32x16(a1, qf[ks + 1], S1);
+      }
     }
     float y[16];
-    float mt = -INFINITY;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int key = 32 * kh + acc_row_perm(rr, hh);
-      y[rr] = key < nvalid ? S[rr] * a.scale_log2 : -INFINITY;
-      mt = fmaxf(mt, y[rr]);
+    for (int rr = 0; rr < 16; ++rr) y[rr] = F::KS > 1 ? S0[rr] + S1[rr] : S0[rr];
+    if (nvalid < KT) {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr)
+        if (32 * kh + acc_row_perm(rr, hh) >= nvalid) y[rr] = -INFINITY;
     }
-    mt = fmaxf(mt, wave_xor32(mt));
+    float mt = y[0];
+#pragma unroll
+    for (int rr = 1; rr < 16; ++rr) mt = fmaxf(mt, y[rr]);
+    mt = pair_max(mt) * a.scale_log2;   // the scale is positive: max commutes with it
     if (__builtin_amdgcn_ballot_w64(mt > mref + RESCALE_LOG2)) {
       const float mnew = fmaxf(mref, mt);
-      const float alpha = exp2f(mref - mnew);
+      const float alpha = exp2_fast(mref - mnew);
       lsum *= alpha;
 #pragma unroll
       for (int et = 0; et < F::ET; ++et) O[et] *= alpha;
       mref = mnew;
     }
+    const float nm = -mref;
     float ls = 0.f;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-      y[rr] = exp2f(y[rr] - mref);
+      y[rr] = exp2_fast(fmaf(y[rr], a.scale_log2, nm));
       ls += y[rr];
     }
-    lsum += ls + wave_xor32(ls);
+    lsum += pair_sum(ls);
     u32x4_t pf[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
@@ -243,8 +252,8 @@ __global__ __launch_bounds__(512) void attn_split_kernel(AttnArgs a, int nq, int
   if (kh == 0) {
     const float m1 = ml[(qg * 64 + lane) * 2], l1 = ml[(qg * 64 + lane) * 2 + 1];
     const float M = fmaxf(mref, m1);
-    const float a0 = M == -INFINITY ? 0.f : exp2f(mref - M);
-    const float a1 = M == -INFINITY ? 0.f : exp2f(m1 - M);
+    const float a0 = M == -INFINITY ? 0.f : exp2_fast(mref - M);
+    const float a1 = M == -INFINITY ? 0.f : exp2_fast(m1 - M);
     const float *d = (const float *)slot;
     float o[F::ET * 16];
 #pragma unroll
@@ -295,7 +304,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   for (int s = 0; s < a.nsplit; ++s) {
     const int64_t pr = ((int64_t)s * a.Hq + h) * a.Cpad + c;
     const float ms = a.pml[2 * pr];
-    const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
+    const float w = ms == -INFINITY ? 0.f : exp2_fast(ms - M);
     L += a.pml[2 * pr + 1] * w;
     const float4 *p = (const float4 *)(a.po + pr * HD + e0);
     const float4 x0 = p[0], x1 = p[1];
