@@ -262,9 +262,8 @@ dg_status dg_logits_entropy(dg_ctx ctx, const dg_dims *dims, const dg_bf16 *H,
   a.tsum = ws_at<float>(ws, w.tsum);
   a.tent = ws_at<float>(ws, w.tent);
   a.targ = ws_at<int>(ws, w.targ);
-  a.nsh = ws_at<int>(ws, w.nsh);
-  a.gsc = ws_at<float>(ws, w.gsc);
-  a.nsc = w.nsc;
+  a.colR = ws_at<float>(ws, w.colR);
+  a.colZ = ws_at<float>(ws, w.colZ);
   a.entropy = entropy;
   a.argmax = argmax;
   a.status = ctx->d_status;
@@ -314,8 +313,10 @@ dg_status dg_selfcond(dg_ctx ctx, const dg_dims *dims, void *ws, const dg_bf16 *
   const DgWs w = dg_ws_layout(m.V, m.d, m.C, m.Hq, m.Hkv, m.hd, m.F, 0);
   SelfcondArgs a{};
   a.ptilde = ws_at<u16>(ws, w.ptilde);
-  a.nsh = ws_at<int>(ws, w.nsh);
-  a.gsc = ws_at<float>(ws, w.gsc);
+  a.trho = ws_at<float>(ws, w.trho);
+  a.colR = ws_at<float>(ws, w.colR);
+  a.colZ = ws_at<float>(ws, w.colZ);
+  a.rhoS = ws_at<float>(ws, w.rhoS);
   a.E = E;
   a.V = m.V;
   a.d = m.d;

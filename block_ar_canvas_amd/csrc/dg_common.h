@@ -119,15 +119,16 @@ struct DgWs {
   int nsplit_max;  // attention split-K parts at Pcap
   size_t ptilde;   // bf16 p~ in MFMA fragment order: [Cpad/32][Vpad/16][64 lanes][8]
   size_t tmax, trho, tsum, tent, targ;  // per-(column, tile) statistics [Cpad][T]
-  size_t nsh;      // per-(tile, column) exponent shift of p~ within its split [T][Cpad]
-  size_t gsc;      // per-(split, column) scale 2^(rho_S - R) / Z           [nsc][Cpad]
+  size_t colR;     // per-column reference R = max_t rho_t                  [Cpad]
+  size_t colZ;     // per-column softmax sum relative to 2^R                 [Cpad]
+  size_t rhoS;     // per-(split, column) reference rho_S = max over the split [nsc][Cpad]
   size_t q;        // Q   bf16 [Cpad][Hq*hd]
   size_t kc;       // canvas keys   bf16 [Cpad][Hkv*hd]
   size_t vct;      // canvas values bf16 [Hkv*hd][Cpad] (transposed)
   size_t o;        // attention output before Wo, bf16 [Cpad][Hq*hd]
   size_t po;       // attention partial O fp32 [nsplit][Hq][Cpad][hd]
   size_t pml;      // attention partial (max, sum) fp32 [nsplit][Hq][Cpad][2]
-  size_t ps;       // self-cond partial s fp32 [nsc][Cpad][d]
+  size_t ps;       // self-cond partial s^T fp32 [nsc][d][Cpad]
   size_t s;        // s = p0 E rounded to bf16 [Cpad][d]
   size_t g;        // GELU(s W1^T) bf16 [Cpad][F]
   size_t x;        // denoiser input E[x] + z, bf16 [Cpad][d]
@@ -183,8 +184,9 @@ static inline DgWs dg_ws_layout(int V, int d, int C, int Hq, int Hkv, int hd, in
   w.tsum = take(CT * 4);
   w.tent = take(CT * 4);
   w.targ = take(CT * 4);
-  w.nsh = take(CT * 4);
-  w.gsc = take((size_t)w.nsc * w.Cpad * 4);
+  w.colR = take((size_t)w.Cpad * 4);
+  w.colZ = take((size_t)w.Cpad * 4);
+  w.rhoS = take((size_t)w.nsc * w.Cpad * 4);
   w.q = take((size_t)w.Cpad * Hq * hd * 2);
   w.kc = take((size_t)w.Cpad * Hkv * hd * 2);
   w.vct = take((size_t)w.Cpad * Hkv * hd * 2);
@@ -252,9 +254,7 @@ struct LogitsArgs {
   u16 *ptilde;
   float *tmax, *trho, *tsum, *tent;
   int *targ;
-  int *nsh;            // exponent shift of p~ per (tile, column)
-  float *gsc;          // scale per (self-cond split, column)
-  int nsc;             // self-cond splits (tile ranges [S*T/nsc, (S+1)*T/nsc))
+  float *colR, *colZ;  // per-column reference and softmax sum
   float *entropy;      // [C]
   int *argmax;         // [C]
   int *status;
@@ -263,11 +263,12 @@ hipError_t dg_launch_logits(const LogitsArgs &a, hipStream_t st);
 
 struct SelfcondArgs {
   const u16 *ptilde;
-  const int *nsh;
-  const float *gsc;
+  const float *trho;   // [Cpad][T] tile references
+  const float *colR, *colZ;
+  float *rhoS;         // [nsc][Cpad] split references (written here)
   const u16 *E;        // [V][d]
   int V, d, C, Cpad, T, nsc;
-  float *ps;           // [nsc][Cpad][d]
+  float *ps;           // [nsc][d][Cpad]
   u16 *s;              // [Cpad][d]
 };
 hipError_t dg_launch_selfcond(const SelfcondArgs &a, hipStream_t st);

@@ -22,10 +22,9 @@
 // the column reference R = max rho_t:
 //   Z = sum Z_t 2^(rho_t - R),  S = sum 2^(rho_t - R) (S_t + Z_t (rho_t - R) ln2),
 //   entropy = ln Z - S / Z  (= -sum p ln p, both terms >= 0: no cancellation),
-// argmax from the first tile reaching the largest m_t, and, for each self-conditioning
-// split S (a contiguous tile range) with rho_S = max of its rho_t, the integer shift
-// rho_S - rho_t of each tile and the split scale 2^(rho_S - R) / Z, so that
-// p0 = p~ * 2^-(rho_S - rho_t) * 2^(rho_S - R) / Z.
+// and the argmax from the first tile reaching the largest m_t. It keeps R and Z per
+// column: p0 = p~ * 2^(rho_t - R) / Z, which the self-conditioning product applies
+// as exact power-of-two shifts plus one scale per column.
 #include <float.h>
 
 #include "dg_common.h"
@@ -161,10 +160,22 @@ __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a) {
   compute(KI - 1, HALF_TAIL ? 2 : BK / 16);
   __syncthreads();   // the rings become epilogue scratch
 
-  // ---------------- epilogue, phase 1: tile max / argmax per column, in the log2
-  // domain x = logit * log2(e) / tau. Within a lane the registers are visited in
-  // ascending vocabulary order, so a strict '>' keeps the lowest id among ties.
+  // ---------------- epilogue, phase 1: tile max / argmax per column on the raw
+  // logits (the scale k2 = log2(e) / tau is positive, so the order is the same as in
+  // the log2 domain x = logit * k2). Within a lane the registers are visited in
+  // ascending vocabulary order, so a strict '>' keeps the lowest id among ties. Rows
+  // past V (last tile only) become -inf.
   const float k2 = a.inv_tau * LOG2E;
+  const bool full = v0 + BV <= a.V;
+  if (!full) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (v0 + wv * 64 + mt * 32 + acc_row_perm(r, hh) >= a.V)
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) acc[mt][nt][r] = -INFINITY;
+  }
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     const int lc = wc * 128 + nt * 32 + l32;
@@ -175,17 +186,21 @@ __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a) {
       const int vb = v0 + wv * 64 + mt * 32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int v = vb + acc_row_perm(r, hh);
-        const float x = v < a.V ? acc[mt][nt][r] * k2 : -INFINITY;
-        acc[mt][nt][r] = x;
-        if (x > best) { best = x; bi = v; }
+        const float x = acc[mt][nt][r];
+        if (x > best) { best = x; bi = vb + acc_row_perm(r, hh); }
       }
     }
-    const float ob = wave_xor32(best);
-    const int oi = wave_xor32(bi);
-    if (better(ob, oi, best, bi)) { best = ob; bi = oi; }
+    // lane pair (l, l ^ 32): the swap leaves both candidates in every lane, and the
+    // choice between them is symmetric.
+    const auto pb = __builtin_amdgcn_permlane32_swap(__float_as_uint(best), __float_as_uint(best), false, false);
+    const auto pi = __builtin_amdgcn_permlane32_swap((uint32_t)bi, (uint32_t)bi, false, false);
+    const float b0 = __uint_as_float(pb[0]), b1 = __uint_as_float(pb[1]);
+    const int i0 = (int)pi[0], i1 = (int)pi[1];
+    const bool take1 = better(b1, i1, b0, i0);
+    best = take1 ? b1 : b0;
+    bi = take1 ? i1 : i0;
     if (hh == 0) {
-      red_m[wv][lc] = best;
+      red_m[wv][lc] = best * k2;
       red_i[wv][lc] = bi;
     }
   }
@@ -197,20 +212,22 @@ __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a) {
   for (int nt = 0; nt < 4; ++nt) {
     const int lc = wc * 128 + nt * 32 + l32;
     const float m = ceilf(fmaxf(fmaxf(red_m[0][lc], red_m[1][lc]), fmaxf(red_m[2][lc], red_m[3][lc])));
+    const float nm = -m;
     float Z = 0.f, S = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float dx = fmaxf(acc[mt][nt][r] - m, -1e30f);   // masked rows: e = 0, e*dx = 0
-        const float e = exp2f(dx);
+        float dx = fmaf(acc[mt][nt][r], k2, nm);
+        if (!full) dx = fmaxf(dx, -1e30f);                 // masked rows: e = 0, e*dx = 0
+        const float e = exp2_fast(dx);
         Z += e;
         S = fmaf(e, dx, S);
         acc[mt][nt][r] = e;
       }
     }
-    Z += wave_xor32(Z);
-    S += wave_xor32(S);
+    Z = pair_sum(Z);
+    S = pair_sum(S);
     if (hh == 0) {
       red_z[wv][lc] = Z;
       red_s[wv][lc] = S;
@@ -260,17 +277,19 @@ __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a) {
 }
 
 // One workgroup per canvas column merges that column's tile statistics ([column][tile]
-// layout: contiguous reads) in a fixed order, so the result is deterministic.
+// layout: contiguous reads) in a fixed order, so the result is deterministic. Besides
+// entropy and argmax it leaves the column reference R and the sum Z (relative to R)
+// for the self-conditioning product.
 __global__ __launch_bounds__(256) void row_finalize_kernel(LogitsArgs a) {
-  __shared__ float sm[256], sr[256];
-  __shared__ int si[256], sbad[256];
-  __shared__ float sz[256], ss[256];
-  const int c = blockIdx.x, tid = threadIdx.x;
+  __shared__ float sm[4], sr[4], sz[4], ss[4];
+  __shared__ int si[4], sbad[4];
+  const int c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float *tmax = a.tmax + (int64_t)c * a.T;
   const float *trho = a.trho + (int64_t)c * a.T;
   const float *tsum = a.tsum + (int64_t)c * a.T;
   const float *tent = a.tent + (int64_t)c * a.T;
 
+  // (tile max, first tile reaching it), NaN flag and R, in ascending tile order.
   float m = -INFINITY, R = -INFINITY;
   int tb = 0x7FFFFFFF, bad = 0;
   for (int t = tid; t < a.T; t += 256) {
@@ -279,50 +298,41 @@ __global__ __launch_bounds__(256) void row_finalize_kernel(LogitsArgs a) {
     else if (mt > m) { m = mt; tb = t; }
     R = fmaxf(R, trho[t]);
   }
-  sm[tid] = m; si[tid] = tb; sbad[tid] = bad; sr[tid] = R;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) {
-      const float m2 = sm[tid + w];
-      const int t2 = si[tid + w];
-      if (m2 > sm[tid] || (m2 == sm[tid] && t2 < si[tid])) { sm[tid] = m2; si[tid] = t2; }
-      sbad[tid] |= sbad[tid + w];
-      sr[tid] = fmaxf(sr[tid], sr[tid + w]);
-    }
-    __syncthreads();
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, 64);
+    const int t2 = __shfl_xor(tb, o, 64);
+    if (m2 > m || (m2 == m && t2 < tb)) { m = m2; tb = t2; }
+    bad |= __shfl_xor(bad, o, 64);
+    R = fmaxf(R, __shfl_xor(R, o, 64));
   }
-  tb = si[0];
-  bad = sbad[0];
-  R = sr[0];
+  if (lane == 0) { sm[wave] = m; si[wave] = tb; sbad[wave] = bad; sr[wave] = R; }
+  __syncthreads();
+  m = sm[0]; tb = si[0]; bad = sbad[0]; R = sr[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) {
+    if (sm[w] > m || (sm[w] == m && si[w] < tb)) { m = sm[w]; tb = si[w]; }
+    bad |= sbad[w];
+    R = fmaxf(R, sr[w]);
+  }
 
   float Z = 0.f, S = 0.f;
   for (int t = tid; t < a.T; t += 256) {
     const float dr = trho[t] - R;                    // integer <= 0
-    const float w = exp2f(dr);
+    const float w = exp2_fast(dr);
     Z += tsum[t] * w;
     S += (tent[t] + tsum[t] * dr * LN2) * w;
   }
-  sz[tid] = Z; ss[tid] = S;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    Z += __shfl_xor(Z, o, 64);
+    S += __shfl_xor(S, o, 64);
+  }
+  if (lane == 0) { sz[wave] = Z; ss[wave] = S; }
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) { sz[tid] += sz[tid + w]; ss[tid] += ss[tid + w]; }
-    __syncthreads();
-  }
-  Z = sz[0];
-  S = ss[0];
-
-  // Per self-conditioning split: exponent shift of each tile and the split scale.
-  for (int sp = tid; sp < a.nsc; sp += 256) {
-    const int t0 = (int)((int64_t)sp * a.T / a.nsc), t1 = (int)((int64_t)(sp + 1) * a.T / a.nsc);
-    float rs = -INFINITY;
-    for (int t = t0; t < t1; ++t) rs = fmaxf(rs, trho[t]);
-    for (int t = t0; t < t1; ++t) {
-      const float n = rs - trho[t];
-      a.nsh[(int64_t)t * a.Cpad + c] = bad ? 0 : (int)fminf(n, 255.f);
-    }
-    a.gsc[(int64_t)sp * a.Cpad + c] = bad ? 0.f : exp2f(rs - R) / Z;
-  }
   if (tid == 0) {
+    Z = (sz[0] + sz[1]) + (sz[2] + sz[3]);
+    S = (ss[0] + ss[1]) + (ss[2] + ss[3]);
     float ent = logf(Z) - S / Z;
     ent = ent > 0.f ? ent : 0.f;
     if (bad || !(ent == ent)) {
@@ -331,6 +341,8 @@ __global__ __launch_bounds__(256) void row_finalize_kernel(LogitsArgs a) {
     }
     a.entropy[c] = ent;
     a.argmax[c] = bad ? 0 : a.targ[(int64_t)c * a.T + tb];
+    a.colR[c] = bad ? __builtin_nanf("") : R;
+    a.colZ[c] = bad ? __builtin_nanf("") : Z;
   }
 }
 

@@ -12,8 +12,9 @@
 // logits epilogue; n(t, c) = rho_S - rho_t is an integer, so the rescale to the split's
 // common reference is an exact exponent shift, applied to the bf16 fragments with packed
 // 16-bit integer arithmetic. The remaining per-(split, column) factor 2^(rho_S - R) / Z
-// is applied by selfcond_reduce_kernel, which sums the split partials in split order
-// (deterministic) and rounds s to bf16 for the FFW.
+// (R = the column reference, Z = the softmax sum relative to 2^R, both from the logits
+// finalize) is applied by selfcond_reduce_kernel, which sums the split partials in
+// split order (deterministic) and rounds s to bf16 for the FFW.
 //
 // Data movement: a ring of 4 LDS stages, 32 vocabulary rows each, filled by direct
 // global -> LDS copies (three stages in flight while one is consumed):
@@ -81,11 +82,30 @@ __global__ __launch_bounds__(512) void selfcond_split_kernel(SelfcondArgs a, int
   const int vbeg = tile0 * DG_BV;
   const int NIT = (tile1 - tile0) * (DG_BV / BKV);
 
-  // Shift table of this split and canvas block, staged once before the copy pipeline.
+  // Split reference rho_S = max of the split's tile references per column, and the
+  // shift table n(t, c) = rho_S - rho_t (uint8; 255 flushes a tile, a column past C or
+  // a column whose statistics are not finite), staged once before the copy pipeline.
+  float *rs_lds = (float *)(smem);                 // [2][256], reused by the ring below
+  {
+    const int cl = tid & 255, half = tid >> 8, c = cb + cl;
+    float rs = -INFINITY;
+    if (c < a.C) {
+      const float *tr = a.trho + (int64_t)c * a.T;
+      for (int t = tile0 + half; t < tile1; t += 2) rs = fmaxf(rs, tr[t]);
+    }
+    rs_lds[half * 256 + cl] = rs;
+  }
+  __syncthreads();
   for (int i = tid; i < (tile1 - tile0) * BC; i += 512) {
     const int tl = i / BC, cl = i % BC, c = cb + cl;
-    ntab[i] = (unsigned char)((c < a.C) ? a.nsh[(int64_t)(tile0 + tl) * a.Cpad + c] : 255);
+    const float rs = fmaxf(rs_lds[cl], rs_lds[256 + cl]);
+    float n = 255.f;
+    if (c < a.C && rs - rs == 0.f) n = fminf(rs - a.trho[(int64_t)c * a.T + tile0 + tl], 255.f);
+    ntab[i] = (unsigned char)(n == n ? n : 255.f);
   }
+  if (jb == 0 && tid < BC && cb + tid < a.Cpad)
+    a.rhoS[(int64_t)split * a.Cpad + cb + tid] = fmaxf(rs_lds[tid], rs_lds[256 + tid]);
+  __syncthreads();                                   // rs_lds is ring space from here on
 
   // Copy duties per stage (2 E and 2 p~ instructions per wave). E instruction `ins`
   // fills stage rows 2*ins and 2*ins + 1 (32 lanes per 512-byte row segment).
@@ -168,7 +188,6 @@ __global__ __launch_bounds__(512) void selfcond_split_kernel(SelfcondArgs a, int
     }
   };
 
-  __syncthreads();                                   // shift table visible
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (s < NIT) issue(s);
@@ -182,7 +201,8 @@ __global__ __launch_bounds__(512) void selfcond_split_kernel(SelfcondArgs a, int
     compute(it);
   }
 
-  // Partial s^T for this split: ps[split][c][j], 4 consecutive j per store.
+  // Partial s^T for this split, stored as ps[split][j][c]: for each accumulator
+  // register the 32 lanes of a half-wave write 32 consecutive columns (128 bytes).
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
     const int c = cb + (wc * 2 + ct) * 32 + l32;
@@ -190,33 +210,62 @@ __global__ __launch_bounds__(512) void selfcond_split_kernel(SelfcondArgs a, int
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int j = j0 + wj * 128 + jt * 32 + 8 * q + 4 * hh;
-        if (j >= a.d) continue;
-        const float4 v = make_float4(acc[jt][ct][4 * q], acc[jt][ct][4 * q + 1],
-                                     acc[jt][ct][4 * q + 2], acc[jt][ct][4 * q + 3]);
-        *(float4 *)(a.ps + ((int64_t)split * a.Cpad + c) * a.d + j) = v;
+      for (int r = 0; r < 16; ++r) {
+        const int j = j0 + wj * 128 + jt * 32 + acc_row(r, hh);
+        if (j < a.d) a.ps[((int64_t)split * a.d + j) * a.Cpad + c] = acc[jt][ct][r];
       }
     }
   }
 }
 
-// s[c][j] = sum over splits (in split order) of gsc[split][c] * ps[split][c][j].
+// s[c][j] = bf16( sum over splits S, in split order, of
+//                 2^(rho_S - R_c) / Z_c * ps[S][j][c] ).
+// A workgroup owns 16 j x 64 c (one float4 of columns per thread): reads run along c,
+// the bf16 result is transposed through LDS and written along j.
 __global__ __launch_bounds__(256) void selfcond_reduce_kernel(SelfcondArgs a) {
-  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;   // element of [Cpad][d]
-  const int64_t n = (int64_t)a.Cpad * a.d;
-  if (i >= n) return;
-  const int c = (int)(i / a.d);
-  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (c < a.C) {
-    for (int p = 0; p < a.nsc; ++p) {
-      const float gs = a.gsc[(int64_t)p * a.Cpad + c];
-      const float4 v = *(const float4 *)(a.ps + (int64_t)p * n + i);
-      s.x += gs * v.x; s.y += gs * v.y; s.z += gs * v.z; s.w += gs * v.w;
+  __shared__ float scale[64 * 33];                   // [c][split], 32 splits per pass
+  __shared__ u16 out[64][24];
+  const int tid = threadIdx.x;
+  const int j0 = blockIdx.x * 16, c0 = blockIdx.y * 64;
+  const int jj = tid >> 4, c4 = (tid & 15) * 4;
+  const int j = j0 + jj;
+  const bool live = j < a.d && c0 + c4 < a.Cpad;
+  const float *src = a.ps + (int64_t)j * a.Cpad + c0 + c4;
+  const int64_t pstride = (int64_t)a.d * a.Cpad;
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int p0 = 0; p0 < a.nsc; p0 += 32) {
+    const int np = min(32, a.nsc - p0);
+    __syncthreads();
+    for (int i = tid; i < 64 * np; i += 256) {
+      const int cl = i / np, p = i % np, c = c0 + cl;
+      float sc = 0.f;
+      if (c < a.C) {
+        const float R = a.colR[c], Z = a.colZ[c];
+        const float rs = a.rhoS[(int64_t)(p0 + p) * a.Cpad + c];
+        if (Z > 0.f && Z <= 3.0e38f && rs - rs == 0.f) sc = exp2_fast(rs - R) / Z;
+      }
+      scale[cl * 33 + p] = sc;
+    }
+    __syncthreads();
+    if (live) {
+#pragma unroll 8
+      for (int p = 0; p < np; ++p) {
+        const float4 x = *(const float4 *)(src + (int64_t)(p0 + p) * pstride);
+        v[0] += scale[(c4 + 0) * 33 + p] * x.x;
+        v[1] += scale[(c4 + 1) * 33 + p] * x.y;
+        v[2] += scale[(c4 + 2) * 33 + p] * x.z;
+        v[3] += scale[(c4 + 3) * 33 + p] * x.w;
+      }
     }
   }
-  const uint2 o = make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
-  *(uint2 *)(a.s + i) = o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) out[c4 + q][jj] = f32_to_bf16(v[q]);
+  __syncthreads();
+  if (tid < 128) {
+    const int cl = tid >> 1, j8 = (tid & 1) * 8;
+    const int c = c0 + cl, jo = j0 + j8;
+    if (c < a.Cpad && jo < a.d) *(uint4 *)(a.s + (int64_t)c * a.d + jo) = *(const uint4 *)(&out[cl][j8]);
+  }
 }
 
 }  // namespace
@@ -234,7 +283,6 @@ hipError_t dg_launch_selfcond(const SelfcondArgs &a, hipStream_t st) {
                      st, a, nj);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t n4 = (int64_t)a.Cpad * a.d / 4;
-  hipLaunchKernelGGL(selfcond_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(selfcond_reduce_kernel, dim3((a.d + 15) / 16, (a.Cpad + 63) / 64), dim3(256), 0, st, a);
   return hipGetLastError();
 }
