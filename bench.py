@@ -42,6 +42,10 @@ def parse():
     ap.add_argument("--roofline-reps", type=int, default=20)
     ap.add_argument("--cpu-steps", type=int, default=1, help="oracle steps timed for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-long-prefix", action="store_true",
+                    help="skip the isolated attention call over a 262144-token prefix")
+    ap.add_argument("--no-chain", action="store_true",
+                    help="skip the 8-canvas block-AR chain with commits")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB device copy (for HBM counter calibration)")
     return ap.parse_args()
@@ -218,9 +222,98 @@ def main():
         "input_gen_s": round(t_gen, 1),
     }
 
+    if not args.no_long_prefix:
+        result["long_prefix_attention"] = long_prefix_attention(ctx, cfg, Wd, Hd[0], args.roofline_reps)
+    del Hd, Kd, Vtd, loop
+    if not args.no_chain:
+        result["chain8"] = chain(ctx)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, W, Kp, args.cpu_steps)
     print(json.dumps(result))
+
+
+def _bf(a, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def long_prefix_attention(ctx, cfg, Wd, H, reps):
+    """One dg_canvas_attn call over a 262144-token prefix (the long-prefix workload's
+    cache, seed 3, with the sampler-head workload's weights), timed with HIP events.
+    The rates are per whole call (embedding gather, Q/K/V projection, split attention,
+    merge and Wo), so they understate the attention kernel itself."""
+    import torch
+    import dg_inputs as di
+
+    lp = di.config("long_prefix")
+    dev = torch.device("cuda:0")
+    P = lp.P0
+    Pcap = -(-(P + cfg.C) // 8) * 8
+    Kp, Vp = di.prefix_kv(lp, Pcap)
+    Kd = _bf(Kp, dev)
+    del Kp
+    Vtd = _bf(np.ascontiguousarray(Vp.transpose(0, 2, 1)), dev)
+    del Vp
+    ws = torch.empty(__import__("block_ar_canvas_amd").workspace_bytes(cfg, Pcap), dtype=torch.uint8,
+                     device=dev)
+    tok = torch.from_numpy(di.targets(lp, 0)).to(dev)
+    z = H[cfg.N - 1]
+    A = torch.empty(cfg.C, cfg.d, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        ctx.canvas_attn(cfg, tok, z, Wd["E"], Wd["Wq"], Wd["Wk"], Wd["Wv"], Wd["Wo"], Kd, Vtd, P, ws, A)
+    e0.record(stream)
+    for _ in range(reps):
+        ctx.canvas_attn(cfg, tok, z, Wd["E"], Wd["Wq"], Wd["Wk"], Wd["Wv"], Wd["Wo"], Kd, Vtd, P, ws, A)
+    e1.record(stream)
+    e1.synchronize()
+    ctx.sync()
+    ms = e0.elapsed_time(e1) / reps
+    keys = P + cfg.C
+    kv_bytes = 2 * cfg.Hkv * keys * cfg.hd * 2
+    flops = 4.0 * cfg.Hq * cfg.C * keys * cfg.hd
+    gbs = kv_bytes / (ms * 1e-3) / 1e9
+    tfs = flops / (ms * 1e-3) / 1e12
+    return {"prefix_tokens": P, "ms_per_call": round(ms, 4), "kv_bytes": kv_bytes,
+            "achieved_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "attention_tflops": round(tfs, 1), "mfma_frac": round(tfs / BF16_PEAK_TFLOPS, 4)}
+
+
+def chain(ctx):
+    """The 8-canvas block-AR chain (chain8 workload: prefix 32768, seed 4): every canvas
+    runs its step loop to the stop test or the 48-step cap and commits its K/V before
+    the next canvas starts. Returns canvas tokens/s including commits."""
+    import torch
+    import dg_inputs as di
+    from block_ar_canvas_amd.loop import CanvasLoop
+
+    cc = di.config("chain8")
+    dev = torch.device("cuda:0")
+    W = di.weights(cc)
+    Wd = {k: _bf(v, dev) for k, v in W.items()}
+    Kp, Vp = di.prefix_kv(cc)
+    Kd = _bf(Kp, dev)
+    Vtd = _bf(np.ascontiguousarray(Vp.transpose(0, 2, 1)), dev)
+    del Kp, Vp
+    Hd = [_bf(di.hidden_all(cc, W["E"], c), dev) for c in range(cc.n_canvas)]
+    del W
+    loop = CanvasLoop(ctx, cc, Wd, Kd, Vtd, cc.P0, N=cc.N, seed=cc.seed)
+    # warm-up: one canvas on a copy of the cache start, then reset the length
+    loop.run_canvas(0, lambda k: Hd[0][k])
+    loop.P = cc.P0
+    torch.cuda.synchronize()
+    steps = 0
+    t0 = time.perf_counter()
+    for c in range(cc.n_canvas):
+        steps += loop.run_canvas(c, lambda k, c=c: Hd[c][k])
+    torch.cuda.synchronize()
+    sec = time.perf_counter() - t0
+    ctx.sync()
+    assert loop.P == cc.P0 + cc.n_canvas * cc.C
+    return {"workload": f"chain8: {cc.n_canvas} canvases of {cc.C} from prefix {cc.P0}, V={cc.V} d={cc.d}",
+            "canvas_tokens_per_s": round(cc.n_canvas * cc.C / sec, 1),
+            "steps": steps, "steps_per_s": round(steps / sec, 2), "seconds": round(sec, 4)}
 
 
 def cpu_baseline(cfg, W, Kp, n_steps):

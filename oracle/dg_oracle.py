@@ -92,7 +92,7 @@ def temperature(k: int, N: int, tau0: float = 0.8, tau1: float = 0.4) -> np.floa
 
 
 # ------------------------------------------------------------------ (a2-a4) attention
-def canvas_attn(tokens, z_bits, E_bits, Wq, Wk, Wv, Wo, Kp, Vp, P, Hq, Hkv, hd):
+def canvas_attn(tokens, z_bits, E_bits, Wq, Wk, Wv, Wo, Kp, Vp, P, Hq, Hkv, hd, rows=None):
     """Bidirectional canvas attention over the static prefix KV cache, then Wo.
 
     [GGL] "Architecture": in denoise mode a query at any canvas position attends to all
@@ -102,17 +102,21 @@ def canvas_attn(tokens, z_bits, E_bits, Wq, Wk, Wv, Wo, Kp, Vp, P, Hq, Hkv, hd):
 
     tokens [C] int; z_bits [C, d] bf16 or None (z = 0); E_bits [V, d]; Wq [Hq*hd, d];
     Wk, Wv [Hkv*hd, d]; Wo [d, Hq*hd]; Kp, Vp [Hkv, >=P, hd] bf16 (logical layout).
-    Returns (A bits [C, d], dict of intermediates as float64).
+    ``rows`` restricts the queries (and the returned A) to those canvas positions; the
+    keys and values still come from every canvas token.
+    Returns (A bits [C or len(rows), d], dict of intermediates as float64).
     """
     tokens = np.asarray(tokens)
     C = tokens.shape[0]
     Ex = from_bf16(E_bits[tokens])
     z = 0.0 if z_bits is None else from_bf16(z_bits)
     X = from_bf16(to_bf16(Ex + z))
-    Q = from_bf16(to_bf16(X @ from_bf16(Wq).T)).reshape(C, Hq, hd)
+    Xq = X if rows is None else X[np.asarray(rows)]
+    nq = Xq.shape[0]
+    Q = from_bf16(to_bf16(Xq @ from_bf16(Wq).T)).reshape(nq, Hq, hd)
     Kc = from_bf16(to_bf16(X @ from_bf16(Wk).T)).reshape(C, Hkv, hd)
     Vc = from_bf16(to_bf16(X @ from_bf16(Wv).T)).reshape(C, Hkv, hd)
-    O = np.zeros((C, Hq, hd))
+    O = np.zeros((nq, Hq, hd))
     scale = 1.0 / math.sqrt(hd)
     for h in range(Hq):
         g = (h * Hkv) // Hq
@@ -123,7 +127,7 @@ def canvas_attn(tokens, z_bits, E_bits, Wq, Wk, Wv, Wo, Kp, Vp, P, Hq, Hkv, hd):
         W = np.exp(S)
         W /= W.sum(axis=1, keepdims=True)
         O[:, h] = W @ V
-    A = to_bf16(O.reshape(C, Hq * hd) @ from_bf16(Wo).T)
+    A = to_bf16(O.reshape(nq, Hq * hd) @ from_bf16(Wo).T)
     return A, {"X": X, "Q": Q, "Kc": Kc, "Vc": Vc, "O": O}
 
 

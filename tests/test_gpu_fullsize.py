@@ -1,0 +1,119 @@
+"""Parity at the full workload sizes, on sampled outputs the oracle computes one by one.
+
+These tests make the same library calls, with the same workspace layout and launch
+configuration, that the benchmark times: the 262144-token vocabulary (d 2048, C 256),
+an 8192-token and a 262144-token prefix cache, and a commit at the end of an 8-canvas
+chain. The float64 oracle evaluates a handful of canvas positions in full; properties
+that hold at any size are checked over every position. Tolerances are those of the
+per-call parity tests (entropy 1e-3 nats; argmax exact unless the oracle's top-2 gap is
+a near-tie; A and z max-relative error 2e-2; committed K/V within one bf16 ulp).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_ar_canvas_amd as dg
+import dg_inputs as di
+import oracle as O
+from gpu_util import (DEV, argmax_mismatch_unexcused, bf16_dev, bits_np, cache_logical, i32_dev,
+                      maxrel, upload_cache, upload_weights)
+
+pytestmark = pytest.mark.gpu
+
+ROWS = [0, 1, 77, 128, 200, 255]
+
+_cache = {}
+
+
+def full(name):
+    if name not in _cache:
+        cfg = di.config(name)
+        W = di.weights(cfg)
+        _cache[name] = (cfg, W, upload_weights(W))
+    return _cache[name]
+
+
+def ws_for(cfg, Pcap):
+    return torch.empty(dg.workspace_bytes(cfg, Pcap), dtype=torch.uint8, device=DEV)
+
+
+@pytest.mark.parametrize("k", [24, 47])
+def test_sampler_head_and_selfcond_full_vocab(dg_ctx, k):
+    cfg, W, Wd = full("gemma_head")
+    ws = ws_for(cfg, cfg.Pcap)
+    H = di.hidden(cfg, W["E"], 0, k)
+    tau = O.temperature(k, cfg.N)
+    ent = torch.empty(cfg.C, dtype=torch.float32, device=DEV)
+    am = torch.empty(cfg.C, dtype=torch.int32, device=DEV)
+    dg_ctx.logits_entropy(cfg, bf16_dev(H), Wd["E"], tau, ws, ent, am)
+    z = torch.empty(cfg.C, cfg.d, dtype=torch.bfloat16, device=DEV)
+    dg_ctx.selfcond(cfg, ws, Wd["E"], Wd["W1"], Wd["W2"], z)
+    dg_ctx.sync()
+    e = ent.cpu().numpy()
+    a = am.cpu().numpy()
+    # every position: finite entropy in [0, ln V], argmax a vocabulary id
+    assert np.all(np.isfinite(e))
+    assert e.min() >= 0.0 and e.max() <= math.log(cfg.V) + 1e-3
+    assert a.min() >= 0 and a.max() < cfg.V
+    # sampled positions against the oracle
+    ent_r, am_r, p_r, u_r = O.logits_entropy(H, W["E"], tau, rows=ROWS)
+    assert np.max(np.abs(e[ROWS] - ent_r)) <= 1e-3, np.max(np.abs(e[ROWS] - ent_r))
+    assert argmax_mismatch_unexcused(a[ROWS], am_r, u_r) == 0
+    z_r, _ = O.selfcond(p_r, W["E"], W["W1"], W["W2"])
+    zg = bits_np(z)
+    assert np.all(np.isfinite(O.from_bf16(zg)))
+    assert maxrel(O.from_bf16(zg[ROWS]), O.from_bf16(z_r)) <= 2e-2
+
+
+@pytest.mark.parametrize("name", ["gemma_head", "long_prefix"])
+def test_canvas_attention_full_prefix(dg_ctx, name):
+    cfg, W, Wd = full(name)
+    P = cfg.P0
+    Pcap = -(-(P + cfg.C) // 8) * 8
+    Kp, Vp = di.prefix_kv(cfg, Pcap)
+    rng = np.random.default_rng(cfg.seed + 300)
+    tok = di.targets(cfg, 0)
+    z = di.f32_to_bf16_bits(rng.standard_normal((cfg.C, cfg.d)).astype(np.float32) * 0.3)
+    Kd, Vtd = upload_cache(Kp, Vp, Pcap)
+    ws = ws_for(cfg, Pcap)
+    A = torch.empty(cfg.C, cfg.d, dtype=torch.bfloat16, device=DEV)
+    dg_ctx.canvas_attn(cfg, i32_dev(tok), bf16_dev(z), Wd["E"], Wd["Wq"], Wd["Wk"], Wd["Wv"],
+                       Wd["Wo"], Kd, Vtd, P, ws, A)
+    dg_ctx.sync()
+    Ag = O.from_bf16(bits_np(A))
+    assert np.all(np.isfinite(Ag))
+    A_r, _ = O.canvas_attn(tok, z, W["E"], W["Wq"], W["Wk"], W["Wv"], W["Wo"], Kp, Vp, P,
+                           cfg.Hq, cfg.Hkv, cfg.hd, rows=ROWS)
+    assert maxrel(Ag[ROWS], O.from_bf16(A_r)) <= 2e-2
+
+
+def test_commit_at_end_of_chain(dg_ctx):
+    cfg, W, Wd = full("chain8")
+    Pcap = cfg.Pcap
+    P = cfg.P0 + (cfg.n_canvas - 1) * cfg.C          # the last canvas of the chain
+    Kp, Vp = di.prefix_kv(cfg, Pcap)
+    rng = np.random.default_rng(cfg.seed + 400)
+    Kp[:, cfg.P0:P] = di.f32_to_bf16_bits(rng.standard_normal((cfg.Hkv, P - cfg.P0, cfg.hd)).astype(np.float32))
+    Vp[:, cfg.P0:P] = di.f32_to_bf16_bits(rng.standard_normal((cfg.Hkv, P - cfg.P0, cfg.hd)).astype(np.float32))
+    tok = rng.integers(0, cfg.V, cfg.C).astype(np.int32)
+    Kd, Vtd = upload_cache(Kp, Vp, Pcap)
+    P_new = dg_ctx.commit_kv(cfg, i32_dev(tok), Wd["E"], Wd["Wk"], Wd["Wv"], Kd, Vtd, P)
+    dg_ctx.sync()
+    assert P_new == P + cfg.C == Pcap
+    Kg, Vg = cache_logical(Kd, Vtd)
+    K_r, V_r = Kp.copy(), Vp.copy()
+    assert O.commit_kv(tok, W["E"], W["Wk"], W["Wv"], K_r, V_r, P, cfg.Hkv, cfg.hd) == Pcap
+    np.testing.assert_array_equal(Kg[:, :P], Kp[:, :P])
+    np.testing.assert_array_equal(Vg[:, :P], Vp[:, :P])
+    for got, ref in ((Kg[:, P:], K_r[:, P:]), (Vg[:, P:], V_r[:, P:])):
+        g = O.from_bf16(got)
+        r = O.from_bf16(ref)
+        assert maxrel(g, r) <= 2e-2
+        # one bf16 ulp, plus the fp32 accumulation error of a 2048-term dot product for
+        # results that cancel to far below the tensor's scale
+        err = np.abs(g - r)
+        bound = np.abs(r) * 2.0 ** -7 + 2.0 ** -16 * np.max(np.abs(r))
+        worst = np.unravel_index(np.argmax(err - bound), err.shape)
+        assert np.all(err <= bound), (int(np.sum(err > bound)), worst, g[worst], r[worst])

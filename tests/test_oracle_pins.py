@@ -18,6 +18,7 @@ import torch
 
 import oracle as O
 from dg_inputs import f32_to_bf16_bits, bf16_bits_to_f32
+import dg_inputs as di
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -515,3 +516,19 @@ def test_commit_rows_and_capacity():
     np.testing.assert_array_equal(Kp[:, P:P + C], kref.transpose(1, 0, 2))
     with pytest.raises(ValueError):
         O.commit_kv(tok, E, Wk, Wv, Kp, Vp, P + 1, Hkv, hd)
+
+
+def test_attention_row_restriction_matches_full():
+    """canvas_attn(rows=r) returns exactly the rows r of the full computation."""
+    cfg = di.config(0)
+    W = di.weights(cfg)
+    Kp, Vp = di.prefix_kv(cfg)
+    rng = np.random.default_rng(7)
+    tok = rng.integers(0, cfg.V, cfg.C).astype(np.int32)
+    z = di.f32_to_bf16_bits(rng.standard_normal((cfg.C, cfg.d)).astype(np.float32) * 0.3)
+    A, _ = O.canvas_attn(tok, z, W["E"], W["Wq"], W["Wk"], W["Wv"], W["Wo"], Kp, Vp, cfg.P0,
+                         cfg.Hq, cfg.Hkv, cfg.hd)
+    rows = [0, 5, 15]
+    Ar, _ = O.canvas_attn(tok, z, W["E"], W["Wq"], W["Wk"], W["Wv"], W["Wo"], Kp, Vp, cfg.P0,
+                          cfg.Hq, cfg.Hkv, cfg.hd, rows=rows)
+    np.testing.assert_array_equal(Ar, A[rows])
