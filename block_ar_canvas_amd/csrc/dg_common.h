@@ -136,10 +136,10 @@ struct DgWs {
 };
 
 // Attention split count for a given number of cached tokens (non-decreasing in P):
-// about one workgroup (one KV head, 128 query rows, one key range) per CU, with at
+// about one workgroup (one KV head, 256 query rows, one key range) per CU, with at
 // least 4 key tiles of 64 per range.
 static inline int dg_attn_nsplit(int Hkv, int Hq, int C, int64_t P) {
-  const int64_t nq = dg_cdiv((int64_t)(Hq / Hkv) * C, 128);
+  const int64_t nq = dg_cdiv((int64_t)(Hq / Hkv) * C, 256);
   const int64_t tiles = dg_cdiv(C, DG_KT) + dg_cdiv(P, DG_KT);
   int64_t ns = dg_cdiv(256, (int64_t)Hkv * nq);
   const int64_t by_len = dg_cdiv(tiles, 4);

@@ -13,8 +13,8 @@
 // contiguous range of key tiles. Eight waves: wave (qg, kh) holds 32 query rows
 // (qg = 0..3) and takes key half kh of every 64-key tile, with its own online softmax;
 // the two halves are merged through LDS at the end. K and V^T tiles stream HBM -> LDS
-// through direct copies (global_load_lds_dwordx4) in a 3-stage ring, one barrier per
-// tile. The split's partial (O, max, sum) go to the workspace as row-major fp32
+// through direct copies (global_load_lds_dwordx4) in a 4-stage ring, one barrier per
+// tile; within a wave the S MFMAs of tile i+1 overlap the softmax of tile i. The split's partial (O, max, sum) go to the workspace as row-major fp32
 // (coalesced), and attn_merge_kernel combines the splits in a fixed order.
 //
 // Orientation: S^T = K Q^T (keys are MFMA rows, loaded through perm_row so that the
@@ -31,8 +31,9 @@
 namespace {
 
 constexpr int KT = 64;      // keys per tile
-constexpr int NS = 3;       // copy ring stages
-constexpr int QB = 128;     // query rows per workgroup
+constexpr int NS = 4;       // copy ring stages
+constexpr int NW = 8;       // waves per workgroup (two per SIMD)
+constexpr int QB = NW * 32; // query rows per workgroup
 constexpr float RESCALE_LOG2 = 8.f;
 
 template <int HD>
@@ -47,14 +48,14 @@ struct Cfg {
   static constexpr int KI = KTILE / 1024;            // copy instructions for K
   static constexpr int VI = HD * KT * 2 / 1024;      // copy instructions for V^T
   static constexpr int TI = KI + VI;
-  static constexpr int PER_WAVE = TI >= 8 ? TI / 8 : 1;   // copies per issuing wave
+  static constexpr int PER_WAVE = TI >= NW ? TI / NW : 1;   // copies per issuing wave
   static constexpr int KSH = HD == 128 ? 0 : HD == 64 ? 1 : HD == 32 ? 2 : 3;
-  static constexpr int OSLOT_ACC = ET * 16 * 64 * 4;      // one wave's O^T registers
-  static constexpr int OSLOT_T = 32 * (HD + 4) * 4;       // 32 rows x HD fp32 (padded)
-  static constexpr int OSLOT = OSLOT_ACC > OSLOT_T ? OSLOT_ACC : OSLOT_T;
+  static constexpr int OPITCH = HD + 4;              // floats per row of the O transpose
+  static constexpr int OSLOT = 32 * OPITCH * 4;      // one wave's 32 x HD fp32 tile
   static constexpr int SMEM_RING = NS * STAGE;
-  static constexpr int SMEM_END = 4 * OSLOT + 4 * 64 * 2 * 4;
+  static constexpr int SMEM_END = NW * OSLOT;
   static constexpr int SMEM = SMEM_RING > SMEM_END ? SMEM_RING : SMEM_END;
+  static_assert(TI < NW || TI % NW == 0, "copy split");
 };
 
 // K rows: physical 16-byte chunk = logical ^ fk(row) (conflict-free A-fragment reads).
@@ -64,20 +65,21 @@ DG_DEV int kswz(int row, int chunk) {
 }
 DG_DEV int vswz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
+// s_waitcnt for "at most rem tiles of this wave's copies still in flight" (rem <= 2).
 template <int N>
 DG_DEV void wait_ring(int rem) {
   if (rem <= 0) dma_wait<0>();
-  else dma_wait<N>();
+  else if (rem == 1) dma_wait<N>();
+  else dma_wait<2 * N>();
 }
 
 template <int HD>
-__global__ __launch_bounds__(512) void attn_split_kernel(AttnArgs a, int nq, int ntc,
-                                                         int ntiles, int units) {
+__global__ __launch_bounds__(NW * 64) void attn_split_kernel(AttnArgs a, int nq, int ntc,
+                                                             int ntiles, int units) {
   using F = Cfg<HD>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qg = wave & 3, kh = wave >> 2;
   const int hh = lane >> 5, l32 = lane & 31;
 
   // Workgroups that read the same key range (same unit) land on the same XCD.
@@ -98,14 +100,14 @@ __global__ __launch_bounds__(512) void attn_split_kernel(AttnArgs a, int nq, int
 
   // Padded V^T rows (head dims below one MFMA tile) are zero in every ring slot.
   if (F::ER > HD) {
-    for (int i = tid; i < NS * (F::ER - HD) * 32; i += 512) {
+    for (int i = tid; i < NS * (F::ER - HD) * 32; i += NW * 64) {
       const int s = i / ((F::ER - HD) * 32), o = i % ((F::ER - HD) * 32);
       *(uint32_t *)(smem + s * F::STAGE + F::KTILE + HD * 128 + 4 * o) = 0;
     }
   }
 
-  // Query rows of this wave: r = qb*128 + qg*32 + l32 -> (head, canvas position).
-  const int r = qb * QB + qg * 32 + l32;
+  // Query rows of this wave: r = qb*256 + wave*32 + l32 -> (head, canvas position).
+  const int r = qb * QB + wave * 32 + l32;
   const bool qok = r < G * a.C;
   const int qh = g * G + (qok ? r / a.C : 0), qc = qok ? r % a.C : 0;
   u32x4_t qf[F::KS];
@@ -126,7 +128,7 @@ __global__ __launch_bounds__(512) void attn_split_kernel(AttnArgs a, int nq, int
     const uint32_t sb = lbase + (uint32_t)(slot * F::STAGE);
 #pragma unroll
     for (int j = 0; j < F::PER_WAVE; ++j) {
-      const int i = wave + 8 * j;
+      const int i = wave + NW * j;
       if (i >= F::TI) break;
       const int off = (i < F::KI ? i : i - F::KI) * 1024 + 16 * lane;
       const u16 *src;
@@ -164,126 +166,99 @@ __global__ __launch_bounds__(512) void attn_split_kernel(AttnArgs a, int nq, int
     const bool canvas = t < ntc;
     const int k0 = (canvas ? t : t - ntc) * KT;
     const int nvalid = min(KT, (canvas ? a.C : (int)a.P) - k0);
-    uint8_t *Ks = smem + (i % NS) * F::STAGE;
-    uint8_t *Vs = Ks + F::KTILE;
+    const uint8_t *Ks = smem + (i % NS) * F::STAGE;
+    uint8_t *Vs = smem + (i % NS) * F::STAGE + F::KTILE;
     if (nvalid < KT) {
       // Tail tile: zero V^T at keys >= nvalid (cache slots past the valid length may
-      // hold any bit pattern, and 0 * NaN would poison O).
-      for (int x = tid; x < HD * (KT - nvalid); x += 512) {
+      // hold any bit pattern, and 0 * NaN would poison O). The K rows there are copies
+      // of the last valid key (finite) and their scores are masked.
+      for (int x = tid; x < HD * (KT - nvalid); x += NW * 64) {
         const int e = x / (KT - nvalid), key = nvalid + x % (KT - nvalid);
         *(u16 *)(Vs + vswz(e, key >> 3) + 2 * (key & 7)) = 0;
       }
       __syncthreads();
     }
-    if (32 * kh >= nvalid) continue;   // this key half is empty
 
-    // S^T tile: 32 keys (half kh) x 32 query rows; even and odd k-steps accumulate
-    // separately to halve the dependent MFMA chain.
-    f32x16_t S0 = {}, S1 = {};
+    // S^T for both 32-key halves of the tile (two independent MFMA chains), then one
+    // online-softmax update and O^T += V^T P^T per half.
+    const int nkt = nvalid > 32 ? 2 : 1;
+    f32x16_t S[2] = {f32x16_t{}, f32x16_t{}};
 #pragma unroll
-    for (int ks = 0; ks < F::KS; ks += 2) {
-      const u32x4_t a0 = *(const u32x4_t *)(Ks + kswz<HD>(32 * kh + perm_row(l32), 2 * ks + hh));
-      S0 = mfma_32x32x16(a0, qf[ks], S0);
-      if (ks + 1 < F::KS) {
-        const u32x4_t a1 = *(const u32x4_t *)(Ks + kswz<HD>(32 * kh + perm_row(l32), 2 * ks + 2 + hh));
-        S1 = mfma_32x32x16(a1, qf[ks + 1], S1);
+    for (int ks = 0; ks < F::KS; ++ks) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        if (kt >= nkt) break;
+        const u32x4_t af = *(const u32x4_t *)(Ks + kswz<HD>(32 * kt + perm_row(l32), 2 * ks + hh));
+        S[kt] = mfma_32x32x16(af, qf[ks], S[kt]);
       }
     }
-    float y[16];
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) y[rr] = F::KS > 1 ? S0[rr] + S1[rr] : S0[rr];
-    if (nvalid < KT) {
+    for (int kt = 0; kt < 2; ++kt) {
+      if (kt >= nkt) break;
+      if (nvalid < KT) {
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr)
-        if (32 * kh + acc_row_perm(rr, hh) >= nvalid) y[rr] = -INFINITY;
-    }
-    float mt = y[0];
-#pragma unroll
-    for (int rr = 1; rr < 16; ++rr) mt = fmaxf(mt, y[rr]);
-    mt = pair_max(mt) * a.scale_log2;   // the scale is positive: max commutes with it
-    if (__builtin_amdgcn_ballot_w64(mt > mref + RESCALE_LOG2)) {
-      const float mnew = fmaxf(mref, mt);
-      const float alpha = exp2_fast(mref - mnew);
-      lsum *= alpha;
-#pragma unroll
-      for (int et = 0; et < F::ET; ++et) O[et] *= alpha;
-      mref = mnew;
-    }
-    const float nm = -mref;
-    float ls = 0.f;
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      y[rr] = exp2_fast(fmaf(y[rr], a.scale_log2, nm));
-      ls += y[rr];
-    }
-    lsum += pair_sum(ls);
-    u32x4_t pf[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-      pf[s] = u32x4_t{pack_bf16x2(y[8 * s + 0], y[8 * s + 1]), pack_bf16x2(y[8 * s + 2], y[8 * s + 3]),
-                      pack_bf16x2(y[8 * s + 4], y[8 * s + 5]), pack_bf16x2(y[8 * s + 6], y[8 * s + 7])};
-    // O^T += V^T P^T over the 32 keys of this half.
-#pragma unroll
-    for (int et = 0; et < F::ET; ++et) {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const u32x4_t af = *(const u32x4_t *)(Vs + vswz(et * 32 + l32, 4 * kh + 2 * s + hh));
-        O[et] = mfma_32x32x16(af, pf[s], O[et]);
+        for (int rr = 0; rr < 16; ++rr)
+          if (32 * kt + acc_row_perm(rr, hh) >= nvalid) S[kt][rr] = -INFINITY;
       }
-    }
-  }
-
-  // Merge the two key halves of each query group through LDS, then store the split's
-  // partial O row-major (coalesced) and its (max, sum).
-  dma_wait<0>();
-  __syncthreads();
-  float *ml = (float *)(smem + 4 * F::OSLOT);   // [qg][lane][2]
-  uint8_t *slot = smem + qg * F::OSLOT;
-  if (kh == 1) {
-    float *d = (float *)slot;
+      float mt = S[kt][0];
 #pragma unroll
-    for (int et = 0; et < F::ET; ++et)
+      for (int rr = 1; rr < 16; ++rr) mt = fmaxf(mt, S[kt][rr]);
+      mt = pair_max(mt) * a.scale_log2;   // the scale is positive: max commutes with it
+      if (__builtin_amdgcn_ballot_w64(mt > mref + RESCALE_LOG2)) {
+        const float mnew = fmaxf(mref, mt);
+        const float alpha = exp2_fast(mref - mnew);
+        lsum *= alpha;
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) d[(et * 16 + rr) * 64 + lane] = O[et][rr];
-    ml[(qg * 64 + lane) * 2] = mref;
-    ml[(qg * 64 + lane) * 2 + 1] = lsum;
-  }
-  __syncthreads();
-  if (kh == 0) {
-    const float m1 = ml[(qg * 64 + lane) * 2], l1 = ml[(qg * 64 + lane) * 2 + 1];
-    const float M = fmaxf(mref, m1);
-    const float a0 = M == -INFINITY ? 0.f : exp2_fast(mref - M);
-    const float a1 = M == -INFINITY ? 0.f : exp2_fast(m1 - M);
-    const float *d = (const float *)slot;
-    float o[F::ET * 16];
-#pragma unroll
-    for (int et = 0; et < F::ET; ++et)
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr)
-        o[et * 16 + rr] = O[et][rr] * a0 + d[(et * 16 + rr) * 64 + lane] * a1;
-    // transposed tile [query l32][e], pitch HD + 4 floats (same slot, read above)
-    float *ot = (float *)slot;
-#pragma unroll
-    for (int et = 0; et < F::ET; ++et)
+        for (int et = 0; et < F::ET; ++et) O[et] *= alpha;
+        mref = mnew;
+      }
+      const float nm = -mref;
+      float y[16], ls = 0.f;
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
-        const int e = et * 32 + acc_row(rr, hh);
-        if (e < HD) ot[l32 * (HD + 4) + e] = o[et * 16 + rr];
+        y[rr] = exp2_fast(fmaf(S[kt][rr], a.scale_log2, nm));
+        ls += y[rr];
       }
-    if (hh == 0 && qok) {
-      const int64_t row = ((int64_t)split * a.Hq + qh) * a.Cpad + qc;
-      a.pml[2 * row] = M;
-      a.pml[2 * row + 1] = lsum * a0 + l1 * a1;
+      lsum += pair_sum(ls);
+      u32x4_t pf[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        pf[s] = u32x4_t{pack_bf16x2(y[8 * s + 0], y[8 * s + 1]), pack_bf16x2(y[8 * s + 2], y[8 * s + 3]),
+                        pack_bf16x2(y[8 * s + 4], y[8 * s + 5]), pack_bf16x2(y[8 * s + 6], y[8 * s + 7])};
+#pragma unroll
+      for (int et = 0; et < F::ET; ++et) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const u32x4_t af = *(const u32x4_t *)(Vs + vswz(et * 32 + l32, 4 * kt + 2 * s + hh));
+          O[et] = mfma_32x32x16(af, pf[s], O[et]);
+        }
+      }
     }
   }
+
+  // The split's partial O, row-major through a per-wave LDS transpose, and (max, sum).
+  dma_wait<0>();
   __syncthreads();
+  float *ot = (float *)(smem + wave * F::OSLOT);   // [32 query rows][OPITCH]
+#pragma unroll
+  for (int et = 0; et < F::ET; ++et)
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int e = et * 32 + acc_row(rr, hh);
+      if (e < HD) ot[l32 * F::OPITCH + e] = O[et][rr];
+    }
+  if (hh == 0 && qok) {
+    const int64_t row = ((int64_t)split * a.Hq + qh) * a.Cpad + qc;
+    a.pml[2 * row] = mref;
+    a.pml[2 * row + 1] = lsum;
+  }
   constexpr int F4 = HD / 4;   // float4 per row
-  for (int f = tid; f < QB * F4; f += 512) {
-    const int row = f / F4, c4 = f % F4;
-    const int rq = qb * QB + row;
+  for (int f = lane; f < 32 * F4; f += 64) {
+    const int rl = f / F4, c4 = f % F4;
+    const int rq = qb * QB + wave * 32 + rl;
     if (rq >= G * a.C) continue;
     const int h = g * G + rq / a.C, c = rq % a.C;
-    const float *src = (const float *)(smem + (row >> 5) * F::OSLOT) + (row & 31) * (HD + 4) + 4 * c4;
+    const float *src = ot + rl * F::OPITCH + 4 * c4;
     *(float4 *)(a.po + (((int64_t)split * a.Hq + h) * a.Cpad + c) * HD + 4 * c4) =
         make_float4(src[0], src[1], src[2], src[3]);
   }
@@ -334,8 +309,8 @@ hipError_t launch(const AttnArgs &a, hipStream_t st) {
   const int ntc = (a.C + KT - 1) / KT;
   const int ntiles = ntc + (int)((a.P + KT - 1) / KT);
   const int units = a.Hkv * a.nsplit;
-  hipLaunchKernelGGL(attn_split_kernel<HD>, dim3(units * nq), dim3(512), Cfg<HD>::SMEM, st, a, nq,
-                     ntc, ntiles, units);
+  hipLaunchKernelGGL(attn_split_kernel<HD>, dim3(units * nq), dim3(NW * 64), Cfg<HD>::SMEM, st, a,
+                     nq, ntc, ntiles, units);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int RPB = 256 / (HD / 8);
