@@ -89,6 +89,9 @@ template <int N>
 DG_DEV void dma_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
+// All of this wave's LDS reads complete (their values are in registers), so a
+// following barrier may hand their LDS space to new copies.
+DG_DEV void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
 DG_DEV uint32_t lds_addr(const void *p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
 }

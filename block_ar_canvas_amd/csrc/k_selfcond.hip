@@ -82,31 +82,6 @@ __global__ __launch_bounds__(512) void selfcond_split_kernel(SelfcondArgs a, int
   const int vbeg = tile0 * DG_BV;
   const int NIT = (tile1 - tile0) * (DG_BV / BKV);
 
-  // Split reference rho_S = max of the split's tile references per column, and the
-  // shift table n(t, c) = rho_S - rho_t (uint8; 255 flushes a tile, a column past C or
-  // a column whose statistics are not finite), staged once before the copy pipeline.
-  float *rs_lds = (float *)(smem);                 // [2][256], reused by the ring below
-  {
-    const int cl = tid & 255, half = tid >> 8, c = cb + cl;
-    float rs = -INFINITY;
-    if (c < a.C) {
-      const float *tr = a.trho + (int64_t)c * a.T;
-      for (int t = tile0 + half; t < tile1; t += 2) rs = fmaxf(rs, tr[t]);
-    }
-    rs_lds[half * 256 + cl] = rs;
-  }
-  __syncthreads();
-  for (int i = tid; i < (tile1 - tile0) * BC; i += 512) {
-    const int tl = i / BC, cl = i % BC, c = cb + cl;
-    const float rs = fmaxf(rs_lds[cl], rs_lds[256 + cl]);
-    float n = 255.f;
-    if (c < a.C && rs - rs == 0.f) n = fminf(rs - a.trho[(int64_t)c * a.T + tile0 + tl], 255.f);
-    ntab[i] = (unsigned char)(n == n ? n : 255.f);
-  }
-  if (jb == 0 && tid < BC && cb + tid < a.Cpad)
-    a.rhoS[(int64_t)split * a.Cpad + cb + tid] = fmaxf(rs_lds[tid], rs_lds[256 + tid]);
-  __syncthreads();                                   // rs_lds is ring space from here on
-
   // Copy duties per stage (2 E and 2 p~ instructions per wave). E instruction `ins`
   // fills stage rows 2*ins and 2*ins + 1 (32 lanes per 512-byte row segment).
   int erow[2], ecol[2];
@@ -150,47 +125,95 @@ __global__ __launch_bounds__(512) void selfcond_split_kernel(SelfcondArgs a, int
   const int trow = 8 * (g >> 1) + (gi >> 2);
   const int tcol = wj * 128 + 16 * (g & 1) + 4 * (gi & 3);
 
-  auto compute = [&](int it) {
+  // Operands of one 16-deep k-step: 4 E^T fragments, 2 raw p~ fragments and their
+  // shift counts (the shift is applied just before the MFMAs).
+  struct Frag {
+    u32x4_t af[4], bf[2];
+    short n[2];
+  };
+  auto load = [&](int it, int ks, Frag &f) {
     const char *se = smem + (it % NS) * STAGE;
     const char *sp = se + ESTAGE;
     const int tl = (it * BKV) / DG_BV;               // tile of this stage within the split
-    v2i16_t dn[2];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      uint32_t w[4];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int off = eoff(16 * ks + 4 * r + trow, tcol + 32 * jt);
+        const v4i16_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 v4i16_t *)(se + off));
+        const uint2 u = __builtin_bit_cast(uint2, t);
+        w[2 * r] = u.x;
+        w[2 * r + 1] = u.y;
+      }
+      f.af[jt] = u32x4_t{w[0], w[1], w[2], w[3]};
+    }
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-      const short n = (short)ntab[tl * BC + (wc * 2 + ct) * 32 + l32];
-      dn[ct] = v2i16_t{(short)(n << 7), (short)(n << 7)};
-    }
-#pragma unroll
-    for (int ks = 0; ks < BKV / 16; ++ks) {
-      u32x4_t af[4], bf[2];
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        uint32_t w[4];
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const int off = eoff(16 * ks + 4 * r + trow, tcol + 32 * jt);
-          const v4i16_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 v4i16_t *)(se + off));
-          const uint2 u = __builtin_bit_cast(uint2, t);
-          w[2 * r] = u.x;
-          w[2 * r + 1] = u.y;
-        }
-        af[jt] = u32x4_t{w[0], w[1], w[2], w[3]};
-      }
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        u32x4_t v = *(const u32x4_t *)(sp + ((wc * 2 + ct) * 2 + ks) * 1024 + lane * 16);
-        bf[ct] = u32x4_t{shift2(v[0], dn[ct]), shift2(v[1], dn[ct]), shift2(v[2], dn[ct]), shift2(v[3], dn[ct])};
-      }
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) acc[jt][ct] = mfma_32x32x16(af[jt], bf[ct], acc[jt][ct]);
+      f.n[ct] = (short)ntab[tl * BC + (wc * 2 + ct) * 32 + l32];
+      f.bf[ct] = *(const u32x4_t *)(sp + ((wc * 2 + ct) * 2 + ks) * 1024 + lane * 16);
     }
   };
+  auto mma = [&](const Frag &f) {
+    u32x4_t bf[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const v2i16_t dn = v2i16_t{(short)(f.n[ct] << 7), (short)(f.n[ct] << 7)};
+      const u32x4_t v = f.bf[ct];
+      bf[ct] = u32x4_t{shift2(v[0], dn), shift2(v[1], dn), shift2(v[2], dn), shift2(v[3], dn)};
+    }
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) acc[jt][ct] = mfma_32x32x16(f.af[jt], bf[ct], acc[jt][ct]);
+  };
 
+  // Three stages' copies fly while one is consumed; each iteration waits for its own
+  // stage, passes one barrier (which also frees the slot read in the previous
+  // iteration) and refills that slot before computing.
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (s < NIT) issue(s);
+  // Split reference rho_S = max of the split's tile references per column, and the
+  // shift table n(t, c) = rho_S - rho_t (uint8; 255 flushes a tile, a column past C or
+  // a column whose statistics are not finite). Staged while the first stages' copies
+  // are in flight: 8 lanes share a column (consecutive tiles, so a wave's load touches
+  // 8 columns' contiguous references), 64 columns per pass, and the lane group's
+  // maximum comes from three xor shuffles.
+  {
+    constexpr int TPL = NTAB_MAX / BC / 8;         // tiles per lane (ntl <= 8 * TPL)
+    const int ntl = tile1 - tile0;
+    const int sub = tid & 7, cg = tid >> 3;
+#pragma unroll
+    for (int pass = 0; pass < BC / 64; ++pass) {
+      const int cl = pass * 64 + cg, c = cb + cl;
+      const bool live = c < a.C;
+      const float *tr = a.trho + (int64_t)(live ? c : 0) * a.T + tile0;
+      float v[TPL];
+      float rs = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < TPL; ++k) {
+        const int t = sub + 8 * k;
+        v[k] = (live && t < ntl) ? tr[t] : -INFINITY;
+        rs = fmaxf(rs, v[k]);
+      }
+      rs = fmaxf(rs, __shfl_xor(rs, 1));
+      rs = fmaxf(rs, __shfl_xor(rs, 2));
+      rs = fmaxf(rs, __shfl_xor(rs, 4));
+      const bool ok = live && rs - rs == 0.f;
+#pragma unroll
+      for (int k = 0; k < TPL; ++k) {
+        const int t = sub + 8 * k;
+        if (t < ntl) {
+          const float n = ok ? fminf(rs - v[k], 255.f) : 255.f;
+          ntab[t * BC + cl] = (unsigned char)(n == n ? n : 255.f);
+        }
+      }
+      if (jb == 0 && sub == 0 && c < a.Cpad) a.rhoS[(int64_t)split * a.Cpad + c] = rs;
+    }
+  }
+
+  Frag f0, f1;
   for (int it = 0; it < NIT; ++it) {
     const int ahead = NIT - 1 - it;                  // stages issued beyond this one
     if (ahead >= 2) dma_wait<8>();
@@ -198,7 +221,10 @@ __global__ __launch_bounds__(512) void selfcond_split_kernel(SelfcondArgs a, int
     else dma_wait<0>();
     __syncthreads();
     if (it + NS - 1 < NIT) issue(it + NS - 1);
-    compute(it);
+    load(it, 0, f0);
+    load(it, 1, f1);
+    mma(f0);
+    mma(f1);
   }
 
   // Partial s^T for this split, stored as ps[split][j][c]: for each accumulator
@@ -221,40 +247,55 @@ __global__ __launch_bounds__(512) void selfcond_split_kernel(SelfcondArgs a, int
 // s[c][j] = bf16( sum over splits S, in split order, of
 //                 2^(rho_S - R_c) / Z_c * ps[S][j][c] ).
 // A workgroup owns 16 j x 64 c (one float4 of columns per thread): reads run along c,
-// the bf16 result is transposed through LDS and written along j.
+// the bf16 result is transposed through LDS and written along j. Splits are taken 32
+// at a time; a chunk's 32 partial loads are issued together, ahead of the scale
+// computation, so each chunk costs one memory round trip.
 __global__ __launch_bounds__(256) void selfcond_reduce_kernel(SelfcondArgs a) {
-  __shared__ float scale[64 * 33];                   // [c][split], 32 splits per pass
+  constexpr int PC = 32;                             // splits per chunk
+  __shared__ float scale[64 * (PC + 1)];             // [c][split in chunk]
   __shared__ u16 out[64][24];
   const int tid = threadIdx.x;
   const int j0 = blockIdx.x * 16, c0 = blockIdx.y * 64;
   const int jj = tid >> 4, c4 = (tid & 15) * 4;
   const int j = j0 + jj;
   const bool live = j < a.d && c0 + c4 < a.Cpad;
-  const float *src = a.ps + (int64_t)j * a.Cpad + c0 + c4;
+  const float *src = a.ps + (int64_t)(live ? j : 0) * a.Cpad + (live ? c0 + c4 : 0);
   const int64_t pstride = (int64_t)a.d * a.Cpad;
   float v[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int p0 = 0; p0 < a.nsc; p0 += 32) {
-    const int np = min(32, a.nsc - p0);
-    __syncthreads();
-    for (int i = tid; i < 64 * np; i += 256) {
-      const int cl = i / np, p = i % np, c = c0 + cl;
-      float sc = 0.f;
-      if (c < a.C) {
-        const float R = a.colR[c], Z = a.colZ[c];
-        const float rs = a.rhoS[(int64_t)(p0 + p) * a.Cpad + c];
-        if (Z > 0.f && Z <= 3.0e38f && rs - rs == 0.f) sc = exp2_fast(rs - R) / Z;
-      }
-      scale[cl * 33 + p] = sc;
+  for (int p0 = 0; p0 < a.nsc; p0 += PC) {
+    const int np = min(PC, a.nsc - p0);
+    float4 x[PC];
+#pragma unroll
+    for (int p = 0; p < PC; ++p)                     // clamped split: always a valid address
+      x[p] = *(const float4 *)(src + (int64_t)(p0 + min(p, np - 1)) * pstride);
+    __syncthreads();                                 // previous chunk's scales consumed
+    // clamped (always valid) addresses, loads first: they all go out together
+    constexpr int SK = 64 * PC / 256;
+    float R[SK], Z[SK], rs[SK];
+#pragma unroll
+    for (int k = 0; k < SK; ++k) {
+      const int i = min(tid + 256 * k, 64 * np - 1);
+      const int cc = min(c0 + i / np, a.C - 1);
+      R[k] = a.colR[cc];
+      Z[k] = a.colZ[cc];
+      rs[k] = a.rhoS[(int64_t)(p0 + i % np) * a.Cpad + cc];
+    }
+#pragma unroll
+    for (int k = 0; k < SK; ++k) {                  // branch-free, so no load is sunk
+      const int i = tid + 256 * k;
+      const int cl = i / np, p = i % np;
+      const float e = exp2_fast(rs[k] - R[k]) / Z[k];
+      const bool ok = c0 + cl < a.C && Z[k] > 0.f && Z[k] <= 3.0e38f && rs[k] - rs[k] == 0.f;
+      if (i < 64 * np) scale[cl * (PC + 1) + p] = ok ? e : 0.f;
     }
     __syncthreads();
-    if (live) {
-#pragma unroll 8
-      for (int p = 0; p < np; ++p) {
-        const float4 x = *(const float4 *)(src + (int64_t)(p0 + p) * pstride);
-        v[0] += scale[(c4 + 0) * 33 + p] * x.x;
-        v[1] += scale[(c4 + 1) * 33 + p] * x.y;
-        v[2] += scale[(c4 + 2) * 33 + p] * x.z;
-        v[3] += scale[(c4 + 3) * 33 + p] * x.w;
+#pragma unroll
+    for (int p = 0; p < PC; ++p) {
+      if (p < np) {
+        v[0] += scale[(c4 + 0) * (PC + 1) + p] * x[p].x;
+        v[1] += scale[(c4 + 1) * (PC + 1) + p] * x[p].y;
+        v[2] += scale[(c4 + 2) * (PC + 1) + p] * x[p].z;
+        v[3] += scale[(c4 + 3) * (PC + 1) + p] * x[p].w;
       }
     }
   }
