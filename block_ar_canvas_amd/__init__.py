@@ -97,15 +97,15 @@ def temperature(k: int, N: int, tau0: float = 0.8, tau1: float = 0.4) -> float:
     return float(_load().dg_temperature(int(k), int(N), float(tau0), float(tau1)))
 
 
-def _ptr(t, dtype, name, optional=False):
+def _ptr(t, dtype, name, optional=False, pinned_ok=False):
     if t is None:
         if optional:
             return None
         raise ValueError(f"{name} is required")
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch tensor")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_cuda and not (pinned_ok and t.is_pinned()):
+        raise ValueError(f"{name} must live on the GPU" + (" or in pinned host memory" if pinned_ok else ""))
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
@@ -207,7 +207,7 @@ class Context:
         self._check(self._lib.dg_stop_test(
             self._h, B, C, _ptr(entropy, _F32, "entropy"), _ptr(argmax, _I32, "argmax"),
             _ptr(prev_argmax, _I32, "prev_argmax", True), float(thr), int(step), int(N),
-            _ptr(flag, _I32, "flag")))
+            _ptr(flag, _I32, "flag", pinned_ok=True)))
 
     def commit_kv(self, dims, tokens, E, Wk, Wv, Kp, Vt, P) -> int:
         d = Dims.of(dims)

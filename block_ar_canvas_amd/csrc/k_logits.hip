@@ -290,13 +290,29 @@ __global__ __launch_bounds__(256) void row_finalize_kernel(LogitsArgs a) {
   const float *tent = a.tent + (int64_t)c * a.T;
 
   // (tile max, first tile reaching it), NaN flag and R, in ascending tile order.
+  // Chunks of 1024 tiles, four per thread, loads issued before use (clamped indices,
+  // so every load is valid): one memory round trip per chunk and pass.
+  constexpr int U = 4;
   float m = -INFINITY, R = -INFINITY;
   int tb = 0x7FFFFFFF, bad = 0;
-  for (int t = tid; t < a.T; t += 256) {
-    const float mt = tmax[t];
-    if (mt != mt) bad = 1;
-    else if (mt > m) { m = mt; tb = t; }
-    R = fmaxf(R, trho[t]);
+  for (int t0 = 0; t0 < a.T; t0 += 256 * U) {
+    float vm[U], vr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = min(t0 + tid + 256 * u, a.T - 1);
+      vm[u] = tmax[t];
+      vr[u] = trho[t];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + tid + 256 * u;
+      if (t < a.T) {
+        const float mt = vm[u];
+        if (mt != mt) bad = 1;
+        else if (mt > m) { m = mt; tb = t; }
+        R = fmaxf(R, vr[u]);
+      }
+    }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -317,11 +333,24 @@ __global__ __launch_bounds__(256) void row_finalize_kernel(LogitsArgs a) {
   }
 
   float Z = 0.f, S = 0.f;
-  for (int t = tid; t < a.T; t += 256) {
-    const float dr = trho[t] - R;                    // integer <= 0
-    const float w = exp2_fast(dr);
-    Z += tsum[t] * w;
-    S += (tent[t] + tsum[t] * dr * LN2) * w;
+  for (int t0 = 0; t0 < a.T; t0 += 256 * U) {
+    float vr[U], vz[U], ve[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = min(t0 + tid + 256 * u, a.T - 1);
+      vr[u] = trho[t];
+      vz[u] = tsum[t];
+      ve[u] = tent[t];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (t0 + tid + 256 * u < a.T) {
+        const float dr = vr[u] - R;                  // integer <= 0
+        const float w = exp2_fast(dr);
+        Z += vz[u] * w;
+        S += (ve[u] + vz[u] * dr * LN2) * w;
+      }
+    }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {

@@ -5,9 +5,12 @@
 // b = 0.1; "Technical novelty": MaskGIT-like entropy-bounded acceptance). The budget
 // sum runs in 2^-32 fixed point, q = ceil(h * 2^32) and budget floor(b * 2^32), so a
 // parallel scan gives the same bits as a sequential loop and the accepted real-valued
-// entropy sum never exceeds b. One workgroup per canvas: a bitonic sort of the 64-bit
-// keys (entropy bits << 32 | position) in LDS, then an inclusive scan of q in sorted
-// order; the accepted set is the sorted prefix whose scan stays within the budget.
+// entropy sum never exceeds b. One workgroup per canvas. The 64-bit sort keys
+// (entropy bits << 32 | position) are distinct, so the inclusive scan of q in
+// ascending key order, taken at a position's own place, is the sum of q over all keys
+// not above its key: each thread evaluates that sum directly over the canvas (no sort
+// is materialised). Since q >= 0 the scan is monotone, and the accepted set is the
+// sorted prefix whose scan stays within the budget.
 //
 // Uniform renoise (Technical Report page, "Method steps" (2)-(3); Google
 // "DiffusionGemma explained", "Uniform State Diffusion"): rejected positions get a
@@ -35,61 +38,37 @@ DG_DEV uint64_t entropy_q(float h) {
 
 __global__ __launch_bounds__(1024) void accept_kernel(int C, const float *ent, uint64_t budget,
                                                       uint8_t *acc, int *nacc) {
-  __shared__ uint64_t key[1024];
-  __shared__ uint64_t scan[2][1024];
-  __shared__ int cnt[1024];
-  const int b = blockIdx.x, tid = threadIdx.x, n = blockDim.x;
+  __shared__ ulonglong2 kq[1024];                    // (sort key, fixed-point entropy)
+  const int b = blockIdx.x, tid = threadIdx.x;
   const float *e = ent + (int64_t)b * C;
 
-  uint64_t k = ~0ull;
+  uint64_t key = ~0ull, q = 0;
   if (tid < C) {
     const float h = e[tid];
     uint32_t bits;
     if (!(h < H_LIMIT)) bits = 0xFFFFFFFFu;
     else bits = h > 0.f ? __float_as_uint(h) : 0u;
-    k = ((uint64_t)bits << 32) | (uint32_t)tid;
-  }
-  key[tid] = k;
-  __syncthreads();
-  // Bitonic sort, ascending, n = power of two.
-  for (int size = 2; size <= n; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const int partner = tid ^ stride;
-      if (partner > tid) {
-        const uint64_t x = key[tid], y = key[partner];
-        const bool up = (tid & size) == 0;
-        if ((x > y) == up) { key[tid] = y; key[partner] = x; }
-      }
-      __syncthreads();
-    }
-  }
-  k = key[tid];
-  const bool real = k != ~0ull;
-  uint64_t q = 0;
-  if (real) {
-    const uint32_t bits = (uint32_t)(k >> 32);
+    key = ((uint64_t)bits << 32) | (uint32_t)tid;
     q = bits == 0xFFFFFFFFu ? Q_SENTINEL : entropy_q(__uint_as_float(bits));
+    kq[tid] = make_ulonglong2(key, q);
   }
-  // Inclusive scan (Hillis-Steele, double-buffered).
-  int cur = 0;
-  scan[0][tid] = q;
   __syncthreads();
-  for (int off = 1; off < n; off <<= 1) {
-    uint64_t v = scan[cur][tid];
-    if (tid >= off) v += scan[cur][tid - off];
-    scan[cur ^ 1][tid] = v;
-    cur ^= 1;
-    __syncthreads();
+  // The inclusive scan of q in ascending key order, evaluated at this position's own
+  // place in that order: the sum of q over all keys <= this key (keys are distinct).
+  uint64_t sum = 0, sum2 = 0;
+  int j = 0;
+#pragma unroll 8
+  for (; j + 1 < C; j += 2) {
+    const ulonglong2 v = kq[j], w = kq[j + 1];
+    sum += v.x <= key ? v.y : 0ull;
+    sum2 += w.x <= key ? w.y : 0ull;
   }
-  const bool take = real && scan[cur][tid] <= budget;
-  if (real) acc[(int64_t)b * C + (uint32_t)k] = take ? 1 : 0;
-  cnt[tid] = take ? 1 : 0;
-  __syncthreads();
-  for (int w = n >> 1; w > 0; w >>= 1) {
-    if (tid < w) cnt[tid] += cnt[tid + w];
-    __syncthreads();
-  }
-  if (tid == 0 && nacc) nacc[b] = cnt[0];
+  if (j < C) sum += kq[j].x <= key ? kq[j].y : 0ull;
+  sum += sum2;
+  const bool take = tid < C && sum <= budget;
+  if (tid < C) acc[(int64_t)b * C + tid] = take ? 1 : 0;
+  const int n = __syncthreads_count(take);
+  if (tid == 0 && nacc) nacc[b] = n;
 }
 
 // Philox4x64-10.
@@ -147,7 +126,9 @@ __global__ __launch_bounds__(256) void stop_kernel(int C, const float *ent, cons
   }
   if (tid == 0) {
     const bool stop = step >= 1 && prev != nullptr && sok[0] && ssum[0] <= limit;
-    flag[b] = stop ? 1 : (step >= N - 1 ? 2 : 0);
+    // system-scope store: flag may live in host memory that the host polls
+    __hip_atomic_store(flag + b, stop ? 1 : (step >= N - 1 ? 2 : 0), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_SYSTEM);
   }
 }
 
@@ -155,8 +136,7 @@ __global__ __launch_bounds__(256) void stop_kernel(int C, const float *ent, cons
 
 hipError_t dg_launch_accept(int B, int C, const float *ent, uint64_t budget, uint8_t *acc,
                             int *nacc, hipStream_t st) {
-  int n = 64;
-  while (n < C) n <<= 1;
+  const int n = C > 64 ? (C + 63) / 64 * 64 : 64;   // C <= 1024 (checked by the caller)
   hipLaunchKernelGGL(accept_kernel, dim3(B), dim3(n), 0, st, C, ent, budget, acc, nacc);
   return hipGetLastError();
 }

@@ -12,6 +12,8 @@ a caller-supplied source (the synthetic driver standing in for the denoiser stac
 """
 from __future__ import annotations
 
+import time
+
 import torch
 
 from . import STOP_GO, Context, Dims, temperature, workspace_bytes
@@ -39,19 +41,25 @@ class CanvasLoop:
         self.argmax = [torch.empty(C, dtype=torch.int32, device=dev) for _ in range(2)]
         self.accept = torch.empty(C, dtype=torch.uint8, device=dev)
         self.n_accept = torch.empty(1, dtype=torch.int32, device=dev)
-        # Stop flags are double-buffered so step k+1 can be enqueued before the host
-        # reads the flag of step k.
-        self.flags = [torch.empty(1, dtype=torch.int32, device=dev) for _ in range(2)]
-        self.flags_host = [torch.empty(1, dtype=torch.int32, pin_memory=True) for _ in range(2)]
-        self.flag_events = [torch.cuda.Event() for _ in range(2)]
+        # Stop flags live in pinned host memory; the stop kernel writes them with
+        # system-scope stores, the host pre-fills -1 when it enqueues the step and polls,
+        # so no copy or event sits between two steps' kernels on the stream. Steps take
+        # the four buffers in enqueue order: when a step is enqueued, at most the two
+        # steps before it may still be pending (the driving loop enqueues step k + 1 before
+        # waiting for step k, and a canvas switch adds one speculative step), so a buffer
+        # is never refilled while an older step's stop kernel may still write it.
+        self.flags = [torch.full((1,), -1, dtype=torch.int32, pin_memory=True) for _ in range(4)]
+        self._seq = 0
+        self._slot = {}
 
     def init_canvas(self, canvas: int):
         """Uniform random canvas (init stream) and z = 0."""
         self.ctx.renoise(self.dims.V, None, None, self.seed, canvas, 0, self.tokens)
         self.canvas = canvas
+        self._slot = {}
 
     def step(self, k: int, H):
-        """One denoise step k on hidden states H [C, d]; leaves the flag on the device."""
+        """Enqueues denoise step k on hidden states H [C, d]; wait_flag(k) returns its flag."""
         W, dm = self.W, self.dims
         am, prev = self.argmax[k & 1], (self.argmax[(k - 1) & 1] if k > 0 else None)
         self.ctx.canvas_attn(dm, self.tokens, self.z if k > 0 else None, W["E"], W["Wq"], W["Wk"],
@@ -61,15 +69,28 @@ class CanvasLoop:
         self.ctx.entropy_accept(self.entropy, self.b, self.accept, self.n_accept)
         self.ctx.renoise(dm.V, am, self.accept, self.seed, self.canvas, k, self.tokens)
         self.ctx.selfcond(dm, self.ws, W["E"], W["W1"], W["W2"], self.z)
-        self.ctx.stop_test(self.entropy, am, prev, self.thr, k, self.N, self.flags[k & 1])
-        self.flags_host[k & 1].copy_(self.flags[k & 1], non_blocking=True)
-        self.flag_events[k & 1].record()
+        slot = self._seq % len(self.flags)
+        self._seq += 1
+        self._slot[k] = slot
+        self.flags[slot].fill_(-1)
+        self.ctx.stop_test(self.entropy, am, prev, self.thr, k, self.N, self.flags[slot])
         return am
 
-    def wait_flag(self, k: int) -> int:
-        """Blocks until step k's stop flag has reached the host and returns it."""
-        self.flag_events[k & 1].synchronize()
-        return int(self.flags_host[k & 1][0])
+    def wait_flag(self, k: int, timeout_s: float = 60.0) -> int:
+        """Returns step k's stop flag once the device has written it (polls the pinned
+        flag; after timeout_s a full device synchronization settles it or raises)."""
+        f = self.flags[self._slot[k]]
+        deadline = time.monotonic() + timeout_s
+        while True:
+            v = int(f[0])
+            if v >= 0:
+                return v
+            if time.monotonic() > deadline:
+                torch.cuda.synchronize(self.Kp.device)
+                v = int(f[0])
+                if v >= 0:
+                    return v
+                raise RuntimeError(f"stop flag of step {k} was never written")
 
     def commit(self, x0):
         self.P = self.ctx.commit_kv(self.dims, x0, self.W["E"], self.W["Wk"], self.W["Wv"],

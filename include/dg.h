@@ -158,7 +158,10 @@ dg_status dg_selfcond(dg_ctx ctx, const dg_dims *dims, void *ws, const dg_bf16 *
  * the mean entropy is <= thr (sum ceil(h 2^32) <= floor(thr * C * 2^32), every entropy
  * in the valid domain) and argmax equals prev_argmax at every position; else 2 when
  * step >= N - 1 (step cap: commit anyway); else 0. prev_argmax may be NULL (no stop).
- * entropy [B, C]; argmax, prev_argmax [B, C]; 0 <= thr < 65536; flag [B] int32. */
+ * entropy [B, C]; argmax, prev_argmax [B, C]; 0 <= thr < 65536; flag [B] int32.
+ * flag may be device memory or pinned host memory (hipHostMalloc): it is written with
+ * system-scope stores, so a host that pre-fills it with a value outside {0, 1, 2} can
+ * poll it for the result without a stream synchronization. */
 dg_status dg_stop_test(dg_ctx ctx, int32_t B, int32_t C, const float *entropy,
                        const int32_t *argmax, const int32_t *prev_argmax, float thr,
                        int32_t step, int32_t N, int32_t *flag);

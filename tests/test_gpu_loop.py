@@ -55,7 +55,7 @@ def run_both(dg_ctx, cfg, n_canvas=1):
                         "accept": lp.accept.cpu().numpy().copy(),
                         "tokens": lp.tokens.cpu().numpy().copy(),
                         "z": bits_np(lp.z), "A": bits_np(lp.A),
-                        "flag": int(lp.flags[k & 1].item())})
+                        "flag": lp.wait_flag(k)})
 
         loop.run_canvas(c, lambda k: Hd[k], on_step=on_step)
         P_o, recs = O.run_canvas(W, Kp, Vp, P_o, lambda k: Hs[k], V=cfg.V, C=cfg.C, Hq=cfg.Hq,
