@@ -9,13 +9,13 @@
 // the prefix, in tiles of 64 that never straddle the two segments.
 //
 // Work split (split-K / "flash decoding" over keys): a workgroup owns one KV head g,
-// 128 query rows of that head's group (row = (head in group, canvas position)) and a
-// contiguous range of key tiles. Eight waves: wave (qg, kh) holds 32 query rows
-// (qg = 0..3) and takes key half kh of every 64-key tile, with its own online softmax;
-// the two halves are merged through LDS at the end. K and V^T tiles stream HBM -> LDS
-// through direct copies (global_load_lds_dwordx4) in a 4-stage ring, one barrier per
-// tile; within a wave the S MFMAs of tile i+1 overlap the softmax of tile i. The split's partial (O, max, sum) go to the workspace as row-major fp32
-// (coalesced), and attn_merge_kernel combines the splits in a fixed order.
+// 256 query rows of that head's group (row = (head in group, canvas position)) and a
+// contiguous range of 64-key tiles. Eight waves of 32 query rows each, two per SIMD,
+// every wave on whole tiles with its own online softmax. K and V^T tiles stream
+// HBM -> LDS through direct copies (global_load_lds_dwordx4) in a 4-stage ring, one
+// barrier per tile. The split's partial (O, max, sum) go to the workspace as
+// row-major fp32 (coalesced), and attn_merge_kernel combines the splits in a fixed
+// order.
 //
 // Orientation: S^T = K Q^T (keys are MFMA rows, loaded through perm_row so that the
 // probabilities come out as ready B fragments), O^T = V^T P^T (V is stored transposed
@@ -180,21 +180,22 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(AttnArgs a, int nq,
     }
 
     // S^T for both 32-key halves of the tile (two independent MFMA chains), then one
-    // online-softmax update and O^T += V^T P^T per half.
-    const int nkt = nvalid > 32 ? 2 : 1;
+    // online-softmax update and O^T += V^T P^T per half. Both halves always run, with
+    // no branch between the MFMAs: in a tail tile the keys past nvalid have finite
+    // (clamped) K rows, masked scores and zeroed V^T, so they add exactly nothing, and
+    // the first half always holds a valid key, so the reference is finite before an
+    // all-masked second half is seen.
     f32x16_t S[2] = {f32x16_t{}, f32x16_t{}};
 #pragma unroll
     for (int ks = 0; ks < F::KS; ++ks) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        if (kt >= nkt) break;
         const u32x4_t af = *(const u32x4_t *)(Ks + kswz<HD>(32 * kt + perm_row(l32), 2 * ks + hh));
         S[kt] = mfma_32x32x16(af, qf[ks], S[kt]);
       }
     }
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      if (kt >= nkt) break;
       if (nvalid < KT) {
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr)
