@@ -160,6 +160,10 @@ dg_status dg_canvas_attn(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens,
   dg_status st = check_dims(ctx, dims, __func__);
   if (st) return st;
   if ((st = check_cache(ctx, P, Pcap, __func__))) return st;
+  // the attention copies address one head's cache array with 32-bit byte offsets
+  if ((int64_t)dims->Hkv * dims->hd * Pcap * 2 > (int64_t)UINT32_MAX)
+    return fail(ctx, DG_ERR_SHAPE, "%s: Hkv*hd*Pcap*2 = %lld bytes exceeds 4 GiB", __func__,
+                (long long)dims->Hkv * dims->hd * Pcap * 2);
   DG_REQUIRE_PTR(tokens);
   DG_REQUIRE_PTR(E);
   DG_REQUIRE_PTR(Wq);

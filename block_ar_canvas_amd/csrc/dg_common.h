@@ -85,13 +85,18 @@ DG_DEV void dma16(const void *gptr, uint32_t lds_base) {
                : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory");
 }
+// Same copy with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit byte offset
+// (the "saddr" form): no 64-bit address arithmetic per lane.
+DG_DEV void dma16s(const void *sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
 template <int N>
 DG_DEV void dma_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
-// All of this wave's LDS reads complete (their values are in registers), so a
-// following barrier may hand their LDS space to new copies.
-DG_DEV void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
 DG_DEV uint32_t lds_addr(const void *p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
 }

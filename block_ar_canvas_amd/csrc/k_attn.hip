@@ -26,6 +26,8 @@
 // against and moves it (rescaling O and the sum) only when the running maximum
 // exceeds it by more than 8 in log2 units, so probabilities stay below 2^8 and the
 // O rescale (64 accumulator registers per lane) is rare after the first tiles.
+#include <type_traits>
+
 #include "dg_common.h"
 
 namespace {
@@ -119,13 +121,46 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(AttnArgs a, int nq,
   }
 
   // Copies of tile t into ring slot `slot`. Instruction i (of TI) covers 1 KiB of the
-  // stage: K tile bytes for i < KI, V^T tile bytes after that.
+  // stage: K tile bytes for i < KI, V^T tile bytes after that. A lane's source offset
+  // splits into a tile-invariant part (precomputed below, per segment) plus the tile's
+  // first key times the key stride; whole tiles then cost one add per copy. The last
+  // tile of a segment clamps keys to the segment and takes the general path.
   const uint32_t lbase = lds_addr(smem);
+  uint32_t ofc[F::PER_WAVE], ofp[F::PER_WAVE];       // element offsets at key 0
+#pragma unroll
+  for (int j = 0; j < F::PER_WAVE; ++j) {
+    const int i = wave + NW * j;
+    const int off = (i < F::KI ? i : i - F::KI) * 1024 + 16 * lane;
+    if (i < F::KI) {
+      const int row = off / F::KRB, pc = (off % F::KRB) >> 4;
+      const int lc = pc ^ ((row >> F::KSH) & (HD / 8 - 1));
+      ofc[j] = (uint32_t)(row * a.Hkv * HD + g * HD + 8 * lc);
+      ofp[j] = (uint32_t)(((int64_t)g * a.Pcap + row) * HD + 8 * lc);
+    } else {
+      const int e = off >> 7, pc = (off & 127) >> 4;
+      const int lc = pc ^ ((e >> 1) & 7);
+      ofc[j] = (uint32_t)((g * HD + e) * a.Cpad + 8 * lc);
+      ofp[j] = (uint32_t)(((int64_t)g * HD + e) * a.Pcap + 8 * lc);
+    }
+  }
   auto issue = [&](int t, int slot) {
     const bool canvas = t < ntc;
     const int k0 = (canvas ? t : t - ntc) * KT;
     const int seglen = canvas ? a.C : (int)a.P;
     const uint32_t sb = lbase + (uint32_t)(slot * F::STAGE);
+    if (k0 + KT <= seglen) {
+#pragma unroll
+      for (int j = 0; j < F::PER_WAVE; ++j) {
+        const int i = wave + NW * j;
+        if (i >= F::TI) break;
+        const bool isk = i < F::KI;
+        const u16 *base = canvas ? (isk ? a.Kc : a.Vct) : (isk ? a.Kp : a.Vt);
+        const uint32_t kst = isk ? (canvas ? (uint32_t)(a.Hkv * HD) : (uint32_t)HD) : 1u;
+        const uint32_t eo = (canvas ? ofc[j] : ofp[j]) + (uint32_t)k0 * kst;
+        dma16s(base, 2u * eo, sb + (isk ? i * 1024 : F::KTILE + (i - F::KI) * 1024));
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < F::PER_WAVE; ++j) {
       const int i = wave + NW * j;
@@ -156,86 +191,109 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(AttnArgs a, int nq,
   for (int et = 0; et < F::ET; ++et) O[et] = f32x16_t{};
   float mref = -INFINITY, lsum = 0.f;
 
-  const int nt = t1 - t0;
-  for (int i = 0; i < NS - 1 && i < nt; ++i) issue(t0 + i, i);
-  for (int i = 0; i < nt; ++i) {
-    const int t = t0 + i;
-    wait_ring<F::PER_WAVE>(min(nt - 1 - i, NS - 2));
-    __syncthreads();
-    if (i + NS - 1 < nt) issue(t + NS - 1, (i + NS - 1) % NS);
-    const bool canvas = t < ntc;
-    const int k0 = (canvas ? t : t - ntc) * KT;
-    const int nvalid = min(KT, (canvas ? a.C : (int)a.P) - k0);
-    const uint8_t *Ks = smem + (i % NS) * F::STAGE;
-    uint8_t *Vs = smem + (i % NS) * F::STAGE + F::KTILE;
-    if (nvalid < KT) {
-      // Tail tile: zero V^T at keys >= nvalid (cache slots past the valid length may
-      // hold any bit pattern, and 0 * NaN would poison O). The K rows there are copies
-      // of the last valid key (finite) and their scores are masked.
-      for (int x = tid; x < HD * (KT - nvalid); x += NW * 64) {
-        const int e = x / (KT - nvalid), key = nvalid + x % (KT - nvalid);
-        *(u16 *)(Vs + vswz(e, key >> 3) + 2 * (key & 7)) = 0;
-      }
+  // The two waves of a SIMD (w and w + 4) run the same loop with opposite issue
+  // priorities: the first is favoured in the MFMA phases (scores, P.V), the second in
+  // the softmax phases. Both meet at every tile barrier; without the asymmetry they
+  // stay in lockstep and contend for the matrix core and the vector ALU in turn.
+  auto run = [&](auto PM, auto PL) {
+    const int nt = t1 - t0;
+    for (int i = 0; i < NS - 1 && i < nt; ++i) issue(t0 + i, i);
+    for (int i = 0; i < nt; ++i) {
+      const int t = t0 + i;
+      wait_ring<F::PER_WAVE>(min(nt - 1 - i, NS - 2));
       __syncthreads();
-    }
-
-    // S^T for both 32-key halves of the tile (two independent MFMA chains), then one
-    // online-softmax update and O^T += V^T P^T per half. Both halves always run, with
-    // no branch between the MFMAs: in a tail tile the keys past nvalid have finite
-    // (clamped) K rows, masked scores and zeroed V^T, so they add exactly nothing, and
-    // the first half always holds a valid key, so the reference is finite before an
-    // all-masked second half is seen.
-    f32x16_t S[2] = {f32x16_t{}, f32x16_t{}};
-#pragma unroll
-    for (int ks = 0; ks < F::KS; ++ks) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const u32x4_t af = *(const u32x4_t *)(Ks + kswz<HD>(32 * kt + perm_row(l32), 2 * ks + hh));
-        S[kt] = mfma_32x32x16(af, qf[ks], S[kt]);
-      }
-    }
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+      if (i + NS - 1 < nt) issue(t + NS - 1, (i + NS - 1) % NS);
+      const bool canvas = t < ntc;
+      const int k0 = (canvas ? t : t - ntc) * KT;
+      const int nvalid = min(KT, (canvas ? a.C : (int)a.P) - k0);
+      const uint8_t *Ks = smem + (i % NS) * F::STAGE;
+      uint8_t *Vs = smem + (i % NS) * F::STAGE + F::KTILE;
       if (nvalid < KT) {
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr)
-          if (32 * kt + acc_row_perm(rr, hh) >= nvalid) S[kt][rr] = -INFINITY;
+        // Tail tile: zero V^T at keys >= nvalid (cache slots past the valid length may
+        // hold any bit pattern, and 0 * NaN would poison O). The K rows there are copies
+        // of the last valid key (finite) and their scores are masked.
+        for (int x = tid; x < HD * (KT - nvalid); x += NW * 64) {
+          const int e = x / (KT - nvalid), key = nvalid + x % (KT - nvalid);
+          *(u16 *)(Vs + vswz(e, key >> 3) + 2 * (key & 7)) = 0;
+        }
+        __syncthreads();
       }
-      float mt = S[kt][0];
-#pragma unroll
-      for (int rr = 1; rr < 16; ++rr) mt = fmaxf(mt, S[kt][rr]);
-      mt = pair_max(mt) * a.scale_log2;   // the scale is positive: max commutes with it
-      if (__builtin_amdgcn_ballot_w64(mt > mref + RESCALE_LOG2)) {
-        const float mnew = fmaxf(mref, mt);
-        const float alpha = exp2_fast(mref - mnew);
-        lsum *= alpha;
-#pragma unroll
-        for (int et = 0; et < F::ET; ++et) O[et] *= alpha;
-        mref = mnew;
+
+      // S^T for both 32-key halves of the tile (two independent MFMA chains), then one
+      // online-softmax update and O^T += V^T P^T per half. Both halves always run, with
+      // no branch between the MFMAs: in a tail tile the keys past nvalid have finite
+      // (clamped) K rows, masked scores and zeroed V^T, so they add exactly nothing, and
+      // the first half always holds a valid key, so the reference is finite before an
+      // all-masked second half is seen.
+      // The K fragments of k-step ks + 1 are read while k-step ks's two MFMAs run
+      // (scheduling groups: 2 LDS reads, then 2 MFMAs).
+      __builtin_amdgcn_s_setprio(decltype(PM)::value);
+      f32x16_t S[2] = {f32x16_t{}, f32x16_t{}};
+      u32x4_t ka[2][2];
+  #pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        ka[0][kt] = *(const u32x4_t *)(Ks + kswz<HD>(32 * kt + perm_row(l32), hh));
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  #pragma unroll
+      for (int ks = 0; ks < F::KS; ++ks) {
+        if (ks + 1 < F::KS) {
+  #pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+            ka[(ks + 1) & 1][kt] = *(const u32x4_t *)(Ks + kswz<HD>(32 * kt + perm_row(l32), 2 * (ks + 1) + hh));
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+  #pragma unroll
+        for (int kt = 0; kt < 2; ++kt) S[kt] = mfma_32x32x16(ka[ks & 1][kt], qf[ks], S[kt]);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
-      const float nm = -mref;
-      float y[16], ls = 0.f;
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        y[rr] = exp2_fast(fmaf(S[kt][rr], a.scale_log2, nm));
-        ls += y[rr];
-      }
-      lsum += pair_sum(ls);
-      u32x4_t pf[2];
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-        pf[s] = u32x4_t{pack_bf16x2(y[8 * s + 0], y[8 * s + 1]), pack_bf16x2(y[8 * s + 2], y[8 * s + 3]),
-                        pack_bf16x2(y[8 * s + 4], y[8 * s + 5]), pack_bf16x2(y[8 * s + 6], y[8 * s + 7])};
-#pragma unroll
-      for (int et = 0; et < F::ET; ++et) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const u32x4_t af = *(const u32x4_t *)(Vs + vswz(et * 32 + l32, 4 * kt + 2 * s + hh));
-          O[et] = mfma_32x32x16(af, pf[s], O[et]);
+  #pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        __builtin_amdgcn_s_setprio(decltype(PL)::value);
+        if (nvalid < KT) {
+  #pragma unroll
+          for (int rr = 0; rr < 16; ++rr)
+            if (32 * kt + acc_row_perm(rr, hh) >= nvalid) S[kt][rr] = -INFINITY;
+        }
+        float mt = S[kt][0];
+  #pragma unroll
+        for (int rr = 1; rr < 16; ++rr) mt = fmaxf(mt, S[kt][rr]);
+        mt = pair_max(mt) * a.scale_log2;   // the scale is positive: max commutes with it
+        if (__builtin_amdgcn_ballot_w64(mt > mref + RESCALE_LOG2)) {
+          const float mnew = fmaxf(mref, mt);
+          const float alpha = exp2_fast(mref - mnew);
+          lsum *= alpha;
+  #pragma unroll
+          for (int et = 0; et < F::ET; ++et) O[et] *= alpha;
+          mref = mnew;
+        }
+        const float nm = -mref;
+        float y[16], ls = 0.f;
+  #pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          y[rr] = exp2_fast(fmaf(S[kt][rr], a.scale_log2, nm));
+          ls += y[rr];
+        }
+        lsum += pair_sum(ls);
+        u32x4_t pf[2];
+  #pragma unroll
+        for (int s = 0; s < 2; ++s)
+          pf[s] = u32x4_t{pack_bf16x2(y[8 * s + 0], y[8 * s + 1]), pack_bf16x2(y[8 * s + 2], y[8 * s + 3]),
+                          pack_bf16x2(y[8 * s + 4], y[8 * s + 5]), pack_bf16x2(y[8 * s + 6], y[8 * s + 7])};
+        __builtin_amdgcn_s_setprio(decltype(PM)::value);
+  #pragma unroll
+        for (int et = 0; et < F::ET; ++et) {
+  #pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            const u32x4_t af = *(const u32x4_t *)(Vs + vswz(et * 32 + l32, 4 * kt + 2 * s + hh));
+            O[et] = mfma_32x32x16(af, pf[s], O[et]);
+          }
         }
       }
     }
-  }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  if (wave < NW / 2) run(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+  else run(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
 
   // The split's partial O, row-major through a per-wave LDS transpose, and (max, sum).
   dma_wait<0>();
@@ -266,26 +324,46 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(AttnArgs a, int nq,
 }
 
 // Log-sum-exp merge of the key-range partials, in split order. HD/8 threads per
-// output row, eight head dims each.
+// output row, eight head dims each. Splits are taken eight at a time with clamped
+// (always valid) indices, so a chunk's loads go out together: one memory round trip
+// per eight splits instead of one per split.
 template <int HD>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  constexpr int TPR = HD / 8, RPB = 256 / TPR;
+  constexpr int TPR = HD / 8, RPB = 256 / TPR, U = 8;
   const int row = blockIdx.x * RPB + threadIdx.x / TPR;
   if (row >= a.Hq * a.C) return;
   const int h = row / a.C, c = row % a.C, e0 = (threadIdx.x % TPR) * 8;
+  const int ns = a.nsplit;
+  auto prow = [&](int s) { return ((int64_t)s * a.Hq + h) * a.Cpad + c; };
   float M = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s)
-    M = fmaxf(M, a.pml[2 * (((int64_t)s * a.Hq + h) * a.Cpad + c)]);
+  for (int s0 = 0; s0 < ns; s0 += U) {
+    float m[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) m[u] = a.pml[2 * prow(min(s0 + u, ns - 1))];
+#pragma unroll
+    for (int u = 0; u < U; ++u) M = fmaxf(M, m[u]);   // clamped repeats do not change a max
+  }
   float L = 0.f, o[8] = {};
-  for (int s = 0; s < a.nsplit; ++s) {
-    const int64_t pr = ((int64_t)s * a.Hq + h) * a.Cpad + c;
-    const float ms = a.pml[2 * pr];
-    const float w = ms == -INFINITY ? 0.f : exp2_fast(ms - M);
-    L += a.pml[2 * pr + 1] * w;
-    const float4 *p = (const float4 *)(a.po + pr * HD + e0);
-    const float4 x0 = p[0], x1 = p[1];
-    o[0] += x0.x * w; o[1] += x0.y * w; o[2] += x0.z * w; o[3] += x0.w * w;
-    o[4] += x1.x * w; o[5] += x1.y * w; o[6] += x1.z * w; o[7] += x1.w * w;
+  for (int s0 = 0; s0 < ns; s0 += U) {
+    float ms[U], ls[U];
+    float4 x0[U], x1[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t pr = prow(min(s0 + u, ns - 1));
+      ms[u] = a.pml[2 * pr];
+      ls[u] = a.pml[2 * pr + 1];
+      const float4 *p = (const float4 *)(a.po + pr * HD + e0);
+      x0[u] = p[0];
+      x1[u] = p[1];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {                  // branch-free: clamped repeats weigh 0
+      const float e = exp2_fast(ms[u] - M);
+      const float w = (s0 + u < ns && ms[u] != -INFINITY) ? e : 0.f;
+      L += ls[u] * w;
+      o[0] += x0[u].x * w; o[1] += x0[u].y * w; o[2] += x0[u].z * w; o[3] += x0[u].w * w;
+      o[4] += x1[u].x * w; o[5] += x1[u].y * w; o[6] += x1[u].z * w; o[7] += x1[u].w * w;
+    }
   }
   const float inv = 1.f / L;
   uint4 out;
