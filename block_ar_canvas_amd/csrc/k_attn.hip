@@ -12,8 +12,7 @@
 // 256 query rows of that head's group (row = (head in group, canvas position)) and a
 // contiguous range of 64-key tiles. Eight waves of 32 query rows each, two per SIMD,
 // every wave on whole tiles with its own online softmax. K and V^T tiles stream
-// HBM -> LDS through direct copies (global_load_lds_dwordx4) in a 4-stage ring, one
-// barrier per tile. The split's partial (O, max, sum) go to the workspace as
+// HBM -> registers -> LDS into a 4-slot ring (two tiles ahead), one barrier per tile. The split's partial (O, max, sum) go to the workspace as
 // row-major fp32 (coalesced), and attn_merge_kernel combines the splits in a fixed
 // order.
 //
@@ -67,14 +66,6 @@ DG_DEV int kswz(int row, int chunk) {
 }
 DG_DEV int vswz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
-// s_waitcnt for "at most rem tiles of this wave's copies still in flight" (rem <= 2).
-template <int N>
-DG_DEV void wait_ring(int rem) {
-  if (rem <= 0) dma_wait<0>();
-  else if (rem == 1) dma_wait<N>();
-  else dma_wait<2 * N>();
-}
-
 template <int HD>
 __global__ __launch_bounds__(NW * 64) void attn_split_kernel(AttnArgs a, int nq, int ntc,
                                                              int ntiles, int units) {
@@ -119,14 +110,26 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(AttnArgs a, int nq,
     if (qok) v = *(const u32x4_t *)(a.Q + (int64_t)qc * a.Hq * HD + qh * HD + ks * 16 + 8 * hh);
     qf[ks] = v;
   }
+  // Settle the Q loads once, here. Passing the fragments through an empty asm makes
+  // them plain register values for the compiler; otherwise its wait-count tracking
+  // carries "maybe pending" across the tile loop's back edge and puts a full
+  // vector-memory wait (which also waits for the tile prefetch) before every score
+  // MFMA.
+#pragma unroll
+  for (int ks = 0; ks < F::KS; ++ks) asm volatile("" : "+v"(qf[ks]));
 
-  // Copies of tile t into ring slot `slot`. Instruction i (of TI) covers 1 KiB of the
-  // stage: K tile bytes for i < KI, V^T tile bytes after that. A lane's source offset
-  // splits into a tile-invariant part (precomputed below, per segment) plus the tile's
-  // first key times the key stride; whole tiles then cost one add per copy. The last
-  // tile of a segment clamps keys to the segment and takes the general path.
-  const uint32_t lbase = lds_addr(smem);
-  uint32_t ofc[F::PER_WAVE], ofp[F::PER_WAVE];       // element offsets at key 0
+  // Tile t is fetched into registers (one 16-byte load per lane per KiB of the stage:
+  // K tile bytes for copy index i < KI, V^T tile bytes after that) and written to its
+  // ring slot one iteration later. Ordinary loads plus LDS writes keep the matrix core
+  // fed: with direct global -> LDS copies (global_load_lds) of the same bytes the MFMA
+  // work of this loop took about 45% more cycles on gfx950.
+  // Source of lane `lane` in copy index i: K row / V^T row and logical 16-byte chunk
+  // follow from the lane (the LDS layout is swizzled by chunk). The element offset at
+  // key 0 of each segment is precomputed per lane; a tile adds its first key times the
+  // key stride, plus (only ever nonzero in a segment's last tile) the clamp of the key
+  // to the segment, so every load stays inside the valid rows. Loads use a wave-uniform
+  // base and a 32-bit byte offset (the API caps each cache array below 4 GiB).
+  uint32_t ofc[F::PER_WAVE], ofp[F::PER_WAVE];
 #pragma unroll
   for (int j = 0; j < F::PER_WAVE; ++j) {
     const int i = wave + NW * j;
@@ -135,54 +138,46 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(AttnArgs a, int nq,
       const int row = off / F::KRB, pc = (off % F::KRB) >> 4;
       const int lc = pc ^ ((row >> F::KSH) & (HD / 8 - 1));
       ofc[j] = (uint32_t)(row * a.Hkv * HD + g * HD + 8 * lc);
-      ofp[j] = (uint32_t)(((int64_t)g * a.Pcap + row) * HD + 8 * lc);
+      ofp[j] = (uint32_t)((g * (uint32_t)a.Pcap + row) * HD + 8 * lc);
     } else {
       const int e = off >> 7, pc = (off & 127) >> 4;
       const int lc = pc ^ ((e >> 1) & 7);
       ofc[j] = (uint32_t)((g * HD + e) * a.Cpad + 8 * lc);
-      ofp[j] = (uint32_t)(((int64_t)g * HD + e) * a.Pcap + 8 * lc);
+      ofp[j] = (uint32_t)((g * HD + e) * (uint32_t)a.Pcap + 8 * lc);
     }
   }
-  auto issue = [&](int t, int slot) {
+  u32x4_t rbuf[F::PER_WAVE];
+  auto fetch = [&](int t) {
     const bool canvas = t < ntc;
     const int k0 = (canvas ? t : t - ntc) * KT;
     const int seglen = canvas ? a.C : (int)a.P;
-    const uint32_t sb = lbase + (uint32_t)(slot * F::STAGE);
-    if (k0 + KT <= seglen) {
-#pragma unroll
-      for (int j = 0; j < F::PER_WAVE; ++j) {
-        const int i = wave + NW * j;
-        if (i >= F::TI) break;
-        const bool isk = i < F::KI;
-        const u16 *base = canvas ? (isk ? a.Kc : a.Vct) : (isk ? a.Kp : a.Vt);
-        const uint32_t kst = isk ? (canvas ? (uint32_t)(a.Hkv * HD) : (uint32_t)HD) : 1u;
-        const uint32_t eo = (canvas ? ofc[j] : ofp[j]) + (uint32_t)k0 * kst;
-        dma16s(base, 2u * eo, sb + (isk ? i * 1024 : F::KTILE + (i - F::KI) * 1024));
-      }
-      return;
-    }
 #pragma unroll
     for (int j = 0; j < F::PER_WAVE; ++j) {
       const int i = wave + NW * j;
-      if (i >= F::TI) break;
+      if (F::TI < NW && i >= F::TI) break;   // only when fewer copies than waves
       const int off = (i < F::KI ? i : i - F::KI) * 1024 + 16 * lane;
-      const u16 *src;
+      const u16 *base;
+      uint32_t eo;
       if (i < F::KI) {
-        const int row = off / F::KRB, pc = (off % F::KRB) >> 4;
-        const int lc = pc ^ ((row >> F::KSH) & (HD / 8 - 1));
-        const int key = min(k0 + row, seglen - 1);
-        src = canvas ? a.Kc + (int64_t)key * a.Hkv * HD + g * HD + 8 * lc
-                     : a.Kp + ((int64_t)g * a.Pcap + key) * HD + 8 * lc;
-        dma16(src, sb + i * 1024);
+        const int key = k0 + off / F::KRB;                    // unclamped key of this row
+        const int kst = canvas ? a.Hkv * HD : HD;
+        base = canvas ? a.Kc : a.Kp;
+        eo = (canvas ? ofc[j] : ofp[j]) + (uint32_t)((k0 + min(0, seglen - 1 - key)) * kst);
       } else {
         const int e = off >> 7, pc = (off & 127) >> 4;
-        const int lc = pc ^ ((e >> 1) & 7);
-        int ks = k0 + 8 * lc;
-        if (ks >= seglen) ks = (seglen - 1) & ~7;
-        src = canvas ? a.Vct + ((int64_t)g * HD + e) * a.Cpad + ks
-                     : a.Vt + ((int64_t)g * HD + e) * a.Pcap + ks;
-        dma16(src, sb + F::KTILE + (i - F::KI) * 1024);
+        const int ks = k0 + 8 * (pc ^ ((e >> 1) & 7));        // unclamped first key
+        base = canvas ? a.Vct : a.Vt;
+        eo = (canvas ? ofc[j] : ofp[j]) + (uint32_t)(k0 + min(0, ((seglen - 1) & ~7) - ks));
       }
+      rbuf[j] = *(const u32x4_t *)((const char *)base + 2u * eo);
+    }
+  };
+  auto put = [&](int slot) {
+#pragma unroll
+    for (int j = 0; j < F::PER_WAVE; ++j) {
+      const int i = wave + NW * j;
+      if (F::TI < NW && i >= F::TI) break;   // only when fewer copies than waves
+      *(u32x4_t *)(smem + slot * F::STAGE + (i < F::KI ? i * 1024 : F::KTILE + (i - F::KI) * 1024) + 16 * lane) = rbuf[j];
     }
   };
 
@@ -196,13 +191,21 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(AttnArgs a, int nq,
   // the softmax phases. Both meet at every tile barrier; without the asymmetry they
   // stay in lockstep and contend for the matrix core and the vector ALU in turn.
   auto run = [&](auto PM, auto PL) {
+    // Tiles 0 and 1 go to their slots up front and tile 2 into registers; iteration i
+    // writes tile i + 2 (slot of tile i - 2, free after the barrier) and fetches i + 3.
     const int nt = t1 - t0;
-    for (int i = 0; i < NS - 1 && i < nt; ++i) issue(t0 + i, i);
+    for (int i = 0; i < 2 && i < nt; ++i) {
+      fetch(t0 + i);
+      put(i);
+    }
+    if (nt > 2) fetch(t0 + 2);
     for (int i = 0; i < nt; ++i) {
       const int t = t0 + i;
-      wait_ring<F::PER_WAVE>(min(nt - 1 - i, NS - 2));
       __syncthreads();
-      if (i + NS - 1 < nt) issue(t + NS - 1, (i + NS - 1) % NS);
+      if (i + 2 < nt) {
+        put((i + 2) % NS);
+        if (i + 3 < nt) fetch(t + 3);
+      }
       const bool canvas = t < ntc;
       const int k0 = (canvas ? t : t - ntc) * KT;
       const int nvalid = min(KT, (canvas ? a.C : (int)a.P) - k0);
@@ -296,7 +299,6 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(AttnArgs a, int nq,
   else run(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
 
   // The split's partial O, row-major through a per-wave LDS transpose, and (max, sum).
-  dma_wait<0>();
   __syncthreads();
   float *ot = (float *)(smem + wave * F::OSLOT);   // [32 query rows][OPITCH]
 #pragma unroll
