@@ -78,3 +78,15 @@ def test_binding_rejects_host_tensors(lib):
 
     with pytest.raises((ValueError, TypeError)):
         dg._ptr(torch.zeros(4), torch.float32, "x")
+
+
+def test_binding_flag_may_be_pinned_host_only(lib):
+    """Only the stop flag may live in host memory, and only if it is pinned."""
+    import torch
+
+    import block_ar_canvas_amd as dg
+
+    with pytest.raises(ValueError):
+        dg._ptr(torch.zeros(1, dtype=torch.int32), torch.int32, "flag", pinned_ok=True)
+    with pytest.raises(ValueError):
+        dg._ptr(torch.zeros(4), torch.float32, "x", pinned_ok=False)

@@ -193,6 +193,31 @@ def test_stop_test_bit_exact(dg_ctx):
     np.testing.assert_array_equal(flag.cpu().numpy(), O.stop_test(hb, ab, pb, 0.005, 2, 8))
 
 
+def test_stop_flag_in_pinned_host_memory(dg_ctx):
+    """The stop kernel's system-scope store reaches a pinned host flag without any copy:
+    pre-filled with -1, the flag is polled until it changes, and it must equal both the
+    oracle's flag and the device-memory result."""
+    import time
+    C, N = 256, 48
+    rng = np.random.default_rng(43)
+    for step in (0, 3, N - 1):
+        hh = rng.exponential(0.002, C).astype(np.float32)
+        am = rng.integers(0, 1000, C).astype(np.int32)
+        prev = am.copy()
+        if step == 3:
+            prev[5] += 1
+        host = torch.full((1,), -1, dtype=torch.int32, pin_memory=True)
+        dev = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+        dg_ctx.stop_test(f32_dev(hh), i32_dev(am), i32_dev(prev), 0.005, step, N, host)
+        dg_ctx.stop_test(f32_dev(hh), i32_dev(am), i32_dev(prev), 0.005, step, N, dev)
+        deadline = time.monotonic() + 30.0
+        while int(host[0]) < 0 and time.monotonic() < deadline:
+            pass
+        dg_ctx.sync()
+        want = int(O.stop_test(hh, am, prev, 0.005, step, N)[0])
+        assert int(host[0]) == int(dev.item()) == want
+
+
 @pytest.mark.parametrize("name", ["tiny", "ragged", "hd64"])
 def test_commit_kv(dg_ctx, name):
     cfg, W, Kp, Vp, Pcap, Wd = setup(name)
