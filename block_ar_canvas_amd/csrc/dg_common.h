@@ -39,7 +39,6 @@ DG_DEV int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 // Physical row of accumulator register r when A rows were loaded through perm_row.
 DG_DEV int acc_row_perm(int r, int h) { return 16 * (r >> 3) + 8 * h + (r & 7); }
 
-DG_DEV float bf16_to_f32(u16 b) { return __uint_as_float((uint32_t)b << 16); }
 DG_DEV float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 DG_DEV float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -57,8 +56,6 @@ DG_DEV uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-DG_DEV float wave_xor32(float v) { return __shfl_xor(v, 32, 64); }
-DG_DEV int wave_xor32(int v) { return __shfl_xor(v, 32, 64); }
 // Max / sum over the lane pair (l, l ^ 32) without an LDS round trip: one
 // v_permlane32_swap leaves {v[l], v[l ^ 32]} in the two registers of every lane (in an
 // order that depends on the half, which neither symmetric operation sees).
@@ -83,14 +80,6 @@ DG_DEV void dma16(const void *gptr, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-               : "memory");
-}
-// Same copy with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit byte offset
-// (the "saddr" form): no 64-bit address arithmetic per lane.
-DG_DEV void dma16s(const void *sbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory");
 }
 template <int N>

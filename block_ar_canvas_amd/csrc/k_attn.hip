@@ -12,9 +12,9 @@
 // 256 query rows of that head's group (row = (head in group, canvas position)) and a
 // contiguous range of 64-key tiles. Eight waves of 32 query rows each, two per SIMD,
 // every wave on whole tiles with its own online softmax. K and V^T tiles stream
-// HBM -> registers -> LDS into a 4-slot ring (two tiles ahead), one barrier per tile. The split's partial (O, max, sum) go to the workspace as
-// row-major fp32 (coalesced), and attn_merge_kernel combines the splits in a fixed
-// order.
+// HBM -> registers -> LDS into a 4-slot ring (two tiles ahead), one barrier per tile.
+// The split's partial (O, max, sum) go to the workspace as row-major fp32
+// (coalesced), and attn_merge_kernel combines the splits in a fixed order.
 //
 // Orientation: S^T = K Q^T (keys are MFMA rows, loaded through perm_row so that the
 // probabilities come out as ready B fragments), O^T = V^T P^T (V is stored transposed
@@ -32,7 +32,7 @@
 namespace {
 
 constexpr int KT = 64;      // keys per tile
-constexpr int NS = 4;       // copy ring stages
+constexpr int NS = 4;       // LDS ring slots
 constexpr int NW = 8;       // waves per workgroup (two per SIMD)
 constexpr int QB = NW * 32; // query rows per workgroup
 constexpr float RESCALE_LOG2 = 8.f;
