@@ -233,59 +233,66 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(AttnArgs a, int nq,
       __builtin_amdgcn_s_setprio(decltype(PM)::value);
       f32x16_t S[2] = {f32x16_t{}, f32x16_t{}};
       u32x4_t ka[2][2];
-  #pragma unroll
+#pragma unroll
       for (int kt = 0; kt < 2; ++kt)
         ka[0][kt] = *(const u32x4_t *)(Ks + kswz<HD>(32 * kt + perm_row(l32), hh));
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-  #pragma unroll
+#pragma unroll
       for (int ks = 0; ks < F::KS; ++ks) {
         if (ks + 1 < F::KS) {
-  #pragma unroll
+#pragma unroll
           for (int kt = 0; kt < 2; ++kt)
             ka[(ks + 1) & 1][kt] = *(const u32x4_t *)(Ks + kswz<HD>(32 * kt + perm_row(l32), 2 * (ks + 1) + hh));
           __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
-  #pragma unroll
+#pragma unroll
         for (int kt = 0; kt < 2; ++kt) S[kt] = mfma_32x32x16(ka[ks & 1][kt], qf[ks], S[kt]);
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
-  #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        __builtin_amdgcn_s_setprio(decltype(PL)::value);
-        if (nvalid < KT) {
-  #pragma unroll
+      // One reference update per tile, from the maximum over both halves (so the
+      // softmax and P.V code below is branch-free and the compiler can overlap half
+      // 1's softmax with half 0's MFMAs).
+      __builtin_amdgcn_s_setprio(decltype(PL)::value);
+      if (nvalid < KT) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
           for (int rr = 0; rr < 16; ++rr)
             if (32 * kt + acc_row_perm(rr, hh) >= nvalid) S[kt][rr] = -INFINITY;
-        }
-        float mt = S[kt][0];
-  #pragma unroll
-        for (int rr = 1; rr < 16; ++rr) mt = fmaxf(mt, S[kt][rr]);
-        mt = pair_max(mt) * a.scale_log2;   // the scale is positive: max commutes with it
-        if (__builtin_amdgcn_ballot_w64(mt > mref + RESCALE_LOG2)) {
-          const float mnew = fmaxf(mref, mt);
-          const float alpha = exp2_fast(mref - mnew);
-          lsum *= alpha;
-  #pragma unroll
-          for (int et = 0; et < F::ET; ++et) O[et] *= alpha;
-          mref = mnew;
-        }
-        const float nm = -mref;
+      }
+      float mt = fmaxf(S[0][0], S[1][0]);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) mt = fmaxf(mt, S[kt][rr]);
+      mt = pair_max(mt) * a.scale_log2;     // the scale is positive: max commutes with it
+      if (__builtin_amdgcn_ballot_w64(mt > mref + RESCALE_LOG2)) {
+        const float mnew = fmaxf(mref, mt);
+        const float alpha = exp2_fast(mref - mnew);
+        lsum *= alpha;
+#pragma unroll
+        for (int et = 0; et < F::ET; ++et) O[et] *= alpha;
+        mref = mnew;
+      }
+      const float nm = -mref;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
         float y[16], ls = 0.f;
-  #pragma unroll
+#pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
           y[rr] = exp2_fast(fmaf(S[kt][rr], a.scale_log2, nm));
           ls += y[rr];
         }
         lsum += pair_sum(ls);
         u32x4_t pf[2];
-  #pragma unroll
+#pragma unroll
         for (int s = 0; s < 2; ++s)
           pf[s] = u32x4_t{pack_bf16x2(y[8 * s + 0], y[8 * s + 1]), pack_bf16x2(y[8 * s + 2], y[8 * s + 3]),
                           pack_bf16x2(y[8 * s + 4], y[8 * s + 5]), pack_bf16x2(y[8 * s + 6], y[8 * s + 7])};
-        __builtin_amdgcn_s_setprio(decltype(PM)::value);
-  #pragma unroll
+        if (kt == 0) __builtin_amdgcn_s_setprio(decltype(PM)::value);
+#pragma unroll
         for (int et = 0; et < F::ET; ++et) {
-  #pragma unroll
+#pragma unroll
           for (int s = 0; s < 2; ++s) {
             const u32x4_t af = *(const u32x4_t *)(Vs + vswz(et * 32 + l32, 4 * kt + 2 * s + hh));
             O[et] = mfma_32x32x16(af, pf[s], O[et]);
