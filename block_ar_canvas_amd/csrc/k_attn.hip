@@ -147,7 +147,7 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(AttnArgs a, int nq,
     }
   }
   u32x4_t rbuf[F::PER_WAVE];
-  auto fetch = [&](int t) {
+  auto fetch = [&](int t, u32x4_t (&rb)[F::PER_WAVE]) {
     const bool canvas = t < ntc;
     const int k0 = (canvas ? t : t - ntc) * KT;
     const int seglen = canvas ? a.C : (int)a.P;
@@ -169,15 +169,15 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(AttnArgs a, int nq,
         base = canvas ? a.Vct : a.Vt;
         eo = (canvas ? ofc[j] : ofp[j]) + (uint32_t)(k0 + min(0, ((seglen - 1) & ~7) - ks));
       }
-      rbuf[j] = *(const u32x4_t *)((const char *)base + 2u * eo);
+      rb[j] = *(const u32x4_t *)((const char *)base + 2u * eo);
     }
   };
-  auto put = [&](int slot) {
+  auto put = [&](int slot, const u32x4_t (&rb)[F::PER_WAVE]) {
 #pragma unroll
     for (int j = 0; j < F::PER_WAVE; ++j) {
       const int i = wave + NW * j;
       if (F::TI < NW && i >= F::TI) break;   // only when fewer copies than waves
-      *(u32x4_t *)(smem + slot * F::STAGE + (i < F::KI ? i * 1024 : F::KTILE + (i - F::KI) * 1024) + 16 * lane) = rbuf[j];
+      *(u32x4_t *)(smem + slot * F::STAGE + (i < F::KI ? i * 1024 : F::KTILE + (i - F::KI) * 1024) + 16 * lane) = rb[j];
     }
   };
 
@@ -191,20 +191,24 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(AttnArgs a, int nq,
   // the softmax phases. Both meet at every tile barrier; without the asymmetry they
   // stay in lockstep and contend for the matrix core and the vector ALU in turn.
   auto run = [&](auto PM, auto PL) {
-    // Tiles 0 and 1 go to their slots up front and tile 2 into registers; iteration i
-    // writes tile i + 2 (slot of tile i - 2, free after the barrier) and fetches i + 3.
+    // Tiles 0 and 1 go to their slots up front (both loads in flight together) and tile
+    // 2 into registers; iteration i writes tile i + 2 (slot of tile i - 2, free after
+    // the barrier) and fetches i + 3.
     const int nt = t1 - t0;
-    for (int i = 0; i < 2 && i < nt; ++i) {
-      fetch(t0 + i);
-      put(i);
+    {
+      u32x4_t rb1[F::PER_WAVE];
+      if (nt > 0) fetch(t0, rbuf);
+      if (nt > 1) fetch(t0 + 1, rb1);
+      if (nt > 0) put(0, rbuf);
+      if (nt > 1) put(1, rb1);
     }
-    if (nt > 2) fetch(t0 + 2);
+    if (nt > 2) fetch(t0 + 2, rbuf);
     for (int i = 0; i < nt; ++i) {
       const int t = t0 + i;
       __syncthreads();
       if (i + 2 < nt) {
-        put((i + 2) % NS);
-        if (i + 3 < nt) fetch(t + 3);
+        put((i + 2) % NS, rbuf);
+        if (i + 3 < nt) fetch(t + 3, rbuf);
       }
       const bool canvas = t < ntc;
       const int k0 = (canvas ? t : t - ntc) * KT;
