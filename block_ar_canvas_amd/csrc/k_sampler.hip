@@ -36,38 +36,43 @@ DG_DEV uint64_t entropy_q(float h) {
   return (uint64_t)ceil((double)h * 4294967296.0);
 }
 
-__global__ __launch_bounds__(1024) void accept_kernel(int C, const float *ent, uint64_t budget,
-                                                      uint8_t *acc, int *nacc) {
+// tpp threads per canvas position (1, 2 or 4; tpp * C <= 1024) share that position's sum.
+__global__ __launch_bounds__(1024) void accept_kernel(int C, int tpp, const float *ent,
+                                                      uint64_t budget, uint8_t *acc, int *nacc) {
   __shared__ ulonglong2 kq[1024];                    // (sort key, fixed-point entropy)
   const int b = blockIdx.x, tid = threadIdx.x;
+  const int pos = tid / tpp, sub = tid % tpp;
   const float *e = ent + (int64_t)b * C;
 
   uint64_t key = ~0ull, q = 0;
-  if (tid < C) {
-    const float h = e[tid];
+  if (pos < C) {
+    const float h = e[pos];
     uint32_t bits;
     if (!(h < H_LIMIT)) bits = 0xFFFFFFFFu;
     else bits = h > 0.f ? __float_as_uint(h) : 0u;
-    key = ((uint64_t)bits << 32) | (uint32_t)tid;
+    key = ((uint64_t)bits << 32) | (uint32_t)pos;
     q = bits == 0xFFFFFFFFu ? Q_SENTINEL : entropy_q(__uint_as_float(bits));
-    kq[tid] = make_ulonglong2(key, q);
+    if (sub == 0) kq[pos] = make_ulonglong2(key, q);
   }
   __syncthreads();
   // The inclusive scan of q in ascending key order, evaluated at this position's own
   // place in that order: the sum of q over all keys <= this key (keys are distinct).
+  // The tpp threads of a position take every tpp-th key; integer sums, so the split
+  // and its order do not change the result.
   uint64_t sum = 0, sum2 = 0;
-  int j = 0;
-#pragma unroll 8
-  for (; j + 1 < C; j += 2) {
-    const ulonglong2 v = kq[j], w = kq[j + 1];
+  int j = sub;
+#pragma unroll 4
+  for (; j + tpp < C; j += 2 * tpp) {
+    const ulonglong2 v = kq[j], w = kq[j + tpp];
     sum += v.x <= key ? v.y : 0ull;
     sum2 += w.x <= key ? w.y : 0ull;
   }
   if (j < C) sum += kq[j].x <= key ? kq[j].y : 0ull;
   sum += sum2;
-  const bool take = tid < C && sum <= budget;
-  if (tid < C) acc[(int64_t)b * C + tid] = take ? 1 : 0;
-  const int n = __syncthreads_count(take);
+  for (int o = 1; o < tpp; o <<= 1) sum += __shfl_xor(sum, o);
+  const bool take = pos < C && sum <= budget;
+  if (pos < C && sub == 0) acc[(int64_t)b * C + pos] = take ? 1 : 0;
+  const int n = __syncthreads_count(take && sub == 0);
   if (tid == 0 && nacc) nacc[b] = n;
 }
 
@@ -105,9 +110,9 @@ __global__ __launch_bounds__(256) void renoise_kernel(int B, int C, int V, const
 __global__ __launch_bounds__(256) void stop_kernel(int C, const float *ent, const int *am,
                                                    const int *prev, uint64_t limit, int step,
                                                    int N, int *flag) {
-  __shared__ uint64_t ssum[256];
-  __shared__ int sok[256];
-  const int b = blockIdx.x, tid = threadIdx.x;
+  __shared__ uint64_t ssum[4];
+  __shared__ int sok[4];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint64_t s = 0;
   int ok = 1;
   for (int i = tid; i < C; i += 256) {
@@ -117,15 +122,20 @@ __global__ __launch_bounds__(256) void stop_kernel(int C, const float *ent, cons
     else s += entropy_q(h);
     if (prev && am[o] != prev[o]) ok = 0;
   }
-  ssum[tid] = s;
-  sok[tid] = ok;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) { ssum[tid] += ssum[tid + w]; sok[tid] &= sok[tid + w]; }
-    __syncthreads();
+  // integer sums: any reduction order gives the same bits
+  for (int o = 32; o > 0; o >>= 1) {
+    s += __shfl_xor(s, o);
+    ok &= __shfl_xor(ok, o);
   }
+  if (lane == 0) {
+    ssum[wave] = s;
+    sok[wave] = ok;
+  }
+  __syncthreads();
   if (tid == 0) {
-    const bool stop = step >= 1 && prev != nullptr && sok[0] && ssum[0] <= limit;
+    const uint64_t tot = ssum[0] + ssum[1] + ssum[2] + ssum[3];
+    const int all = sok[0] & sok[1] & sok[2] & sok[3];
+    const bool stop = step >= 1 && prev != nullptr && all && tot <= limit;
     // system-scope store: flag may live in host memory that the host polls
     __hip_atomic_store(flag + b, stop ? 1 : (step >= N - 1 ? 2 : 0), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_SYSTEM);
@@ -136,8 +146,10 @@ __global__ __launch_bounds__(256) void stop_kernel(int C, const float *ent, cons
 
 hipError_t dg_launch_accept(int B, int C, const float *ent, uint64_t budget, uint8_t *acc,
                             int *nacc, hipStream_t st) {
-  const int n = C > 64 ? (C + 63) / 64 * 64 : 64;   // C <= 1024 (checked by the caller)
-  hipLaunchKernelGGL(accept_kernel, dim3(B), dim3(n), 0, st, C, ent, budget, acc, nacc);
+  // C <= 1024 (checked by the caller); up to 4 threads per position
+  const int tpp = C <= 256 ? 4 : C <= 512 ? 2 : 1;
+  const int n = (C * tpp + 63) / 64 * 64;
+  hipLaunchKernelGGL(accept_kernel, dim3(B), dim3(n), 0, st, C, tpp, ent, budget, acc, nacc);
   return hipGetLastError();
 }
 
