@@ -259,6 +259,7 @@ dg_status dg_logits_entropy(dg_ctx ctx, const dg_dims *dims, const dg_bf16 *H,
   a.C = m.C;
   a.Cpad = w.Cpad;
   a.T = w.T;
+  a.nsc = w.nsc;
   a.inv_tau = 1.0f / tau;
   a.ptilde = ws_at<u16>(ws, w.ptilde);
   a.tmax = ws_at<float>(ws, w.tmax);

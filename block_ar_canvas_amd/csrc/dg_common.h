@@ -247,6 +247,7 @@ struct LogitsArgs {
   const u16 *H;        // [C][d]
   const u16 *E;        // [V][d]
   int V, d, C, Cpad, T;
+  int nsc;             // self-conditioning splits (sets the tile dispatch order)
   float inv_tau;
   u16 *ptilde;
   float *tmax, *trho, *tsum, *tent;

@@ -70,7 +70,16 @@ __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wv = wave & 3, wc = wave >> 2;
   const int hh = lane >> 5, l32 = lane & 31;
-  const int vt = blockIdx.x;
+  // Dispatch order: when the vocabulary tiles split evenly into the self-conditioning
+  // splits, workgroup b takes tile L-1-b/nsc of split b%nsc (L tiles per split). The
+  // self-conditioning pass walks every split from its first tile to its last, so the
+  // first workgroups here read the E rows it read last, which may still be in the
+  // memory-side cache (measured: about 3% off this kernel at V = 262144).
+  int vt = blockIdx.x;
+  if (a.nsc > 0 && a.T % a.nsc == 0) {
+    const int L = a.T / a.nsc;
+    vt = (vt % a.nsc) * L + (L - 1 - vt / a.nsc);
+  }
   const int v0 = vt * BV;
   const int cb = blockIdx.y * BC;
 
