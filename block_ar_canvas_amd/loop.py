@@ -51,6 +51,9 @@ class CanvasLoop:
         self.flags = [torch.full((1,), -1, dtype=torch.int32, pin_memory=True) for _ in range(4)]
         self._seq = 0
         self._slot = {}
+        # When a list, every step appends a (start, end) pair of timing events recorded
+        # on the context's stream around its dg_logits_entropy call.
+        self.logits_events = None
 
     def init_canvas(self, canvas: int):
         """Uniform random canvas (init stream) and z = 0."""
@@ -65,7 +68,15 @@ class CanvasLoop:
         self.ctx.canvas_attn(dm, self.tokens, self.z if k > 0 else None, W["E"], W["Wq"], W["Wk"],
                              W["Wv"], W["Wo"], self.Kp, self.Vt, self.P, self.ws, self.A)
         tau = temperature(k, self.N, self.tau0, self.tau1)
+        ev = self.logits_events
+        if ev is not None:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e0.record(self.ctx._stream)
         self.ctx.logits_entropy(dm, H, W["E"], tau, self.ws, self.entropy, am)
+        if ev is not None:
+            e1 = torch.cuda.Event(enable_timing=True)
+            e1.record(self.ctx._stream)
+            ev.append((e0, e1))
         self.ctx.entropy_accept(self.entropy, self.b, self.accept, self.n_accept)
         self.ctx.renoise(dm.V, am, self.accept, self.seed, self.canvas, k, self.tokens)
         self.ctx.selfcond(dm, self.ws, W["E"], W["W1"], W["W2"], self.z)
