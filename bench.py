@@ -70,8 +70,8 @@ def traffic_from_profiles(kernel_src: str, name: str):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU sharding of the path is described in DESIGN.md", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); the path has "
+              "no multi-GPU sharding, so N > 1 is not supported", file=sys.stderr)
         sys.exit(2)
 
     import torch
