@@ -70,18 +70,31 @@ __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wv = wave & 3, wc = wave >> 2;
   const int hh = lane >> 5, l32 = lane & 31;
+  // Workgroup -> (vocabulary tile, canvas block). With more than one canvas block (a
+  // batch of canvases), the blocks of one tile run back to back on one XCD (workgroups
+  // b, b + 8, ... share an XCD), so all but the first read the tile's E rows from that
+  // XCD's L2 while the first streams them from HBM.
+  const int ncb = (a.Cpad + BC - 1) / BC;
+  int vt, cbk;
+  if (ncb > 1 && (a.T & 7) == 0) {
+    const int q = blockIdx.x >> 3;
+    cbk = q % ncb;
+    vt = (q / ncb) * 8 + (blockIdx.x & 7);
+  } else {
+    vt = blockIdx.x / ncb;
+    cbk = blockIdx.x % ncb;
+  }
   // Dispatch order: when the vocabulary tiles split evenly into the self-conditioning
-  // splits, workgroup b takes tile L-1-b/nsc of split b%nsc (L tiles per split). The
-  // self-conditioning pass walks every split from its first tile to its last, so the
-  // first workgroups here read the E rows it read last, which may still be in the
-  // memory-side cache (measured: about 3% off this kernel at V = 262144).
-  int vt = blockIdx.x;
+  // splits, the t-th tile in dispatch order is tile L-1-t/nsc of split t%nsc (L tiles
+  // per split). The self-conditioning pass walks every split from its first tile to its
+  // last, so the first workgroups here read the E rows it read last, which may still be
+  // in the memory-side cache (measured: about 3% off this kernel at V = 262144).
   if (a.nsc > 0 && a.T % a.nsc == 0) {
     const int L = a.T / a.nsc;
     vt = (vt % a.nsc) * L + (L - 1 - vt / a.nsc);
   }
   const int v0 = vt * BV;
-  const int cb = blockIdx.y * BC;
+  const int cb = cbk * BC;
 
   // Copy duties per stage: rows [32*wave, 32*wave + 32) of E and of H, as 4 copy
   // instructions of 8 rows each. Lane l of instruction j fills LDS row
@@ -397,7 +410,7 @@ hipError_t dg_launch_logits(const LogitsArgs &a, hipStream_t st) {
     if (e != hipSuccess) return e;
     attr = true;
   }
-  const dim3 grid(a.T, (a.Cpad + BC - 1) / BC);
+  const dim3 grid(a.T * ((a.Cpad + BC - 1) / BC));
   if (a.d % BK)
     hipLaunchKernelGGL(logits_tile_kernel<true>, grid, dim3(512), SMEM, st, a);
   else

@@ -60,20 +60,24 @@ __global__ __launch_bounds__(512) void selfcond_split_kernel(SelfcondArgs a, int
   const int wj = wave & 1, wc = wave >> 1;
   const int hh = lane >> 5, l32 = lane & 31;
 
-  // blockIdx.x -> (split, j-slice); the j-slices of one split share its p~ range and
-  // are kept on one XCD when the split count allows it.
+  // blockIdx.x -> (split, j-slice, canvas block). The j-slices of one split share its
+  // p~ range and its canvas blocks share its E rows; all of a split's workgroups are
+  // dispatched together and kept on one XCD when the split count allows it.
   const int b = blockIdx.x;
-  int split, jb;
+  const int ncb = (a.Cpad + BC - 1) / BC;
+  const int per = nj * ncb;                       // workgroups of one split
+  int split, rem;
   if ((a.nsc & 7) == 0) {
     const int xcd = b & 7, r = b >> 3;
-    split = xcd + 8 * (r / nj);
-    jb = r % nj;
+    split = xcd + 8 * (r / per);
+    rem = r % per;
   } else {
-    split = b / nj;
-    jb = b % nj;
+    split = b / per;
+    rem = b % per;
   }
+  const int jb = rem % nj;
   const int j0 = jb * BJ;
-  const int cb = blockIdx.y * BC;
+  const int cb = (rem / nj) * BC;
   const int ct0 = cb / 32;                        // first canvas tile of this block
   const int nct = a.Cpad / 32;
   const int VS = a.T * (DG_BV / 16);
@@ -320,8 +324,8 @@ hipError_t dg_launch_selfcond(const SelfcondArgs &a, hipStream_t st) {
     attr = true;
   }
   const int nj = (a.d + BJ - 1) / BJ;
-  hipLaunchKernelGGL(selfcond_split_kernel, dim3(nj * a.nsc, (a.Cpad + BC - 1) / BC), dim3(512), SMEM,
-                     st, a, nj);
+  hipLaunchKernelGGL(selfcond_split_kernel, dim3(nj * a.nsc * ((a.Cpad + BC - 1) / BC)), dim3(512),
+                     SMEM, st, a, nj);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(selfcond_reduce_kernel, dim3((a.d + 15) / 16, (a.Cpad + 63) / 64), dim3(256), 0, st, a);

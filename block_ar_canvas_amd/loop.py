@@ -133,3 +133,126 @@ class CanvasLoop:
                 on_step(k, self)
         self.commit(self.argmax[k & 1])
         return k + 1
+
+
+class BatchLoop:
+    """B canvases denoised in lockstep, one per request, each request with its own
+    prefix KV cache (the pages' multi-request serving: several users' canvases share one
+    pass of the vocabulary-wide kernels).
+
+    Per step, canvas attention runs once per canvas against that canvas's cache; the
+    sampler head and self-conditioning run once over all B*C positions (every position
+    is its own column of the logits and of p0 E), and acceptance, renoise and the stop
+    test run once with B segments of C positions. Canvas b of batch j has canvas id
+    j*B + b (the renoise key). A batch ends when every canvas has stopped or reached
+    the cap; a canvas that stops earlier keeps the argmax of its stop step, which is what
+    its commit writes, while the others go on (its later steps are computed and ignored).
+
+    caches: list of B (Kp [Hkv, Pcap, hd], Vt [Hkv, hd, Pcap], P) per request.
+    """
+
+    def __init__(self, ctx: Context, dims, weights, caches, *, N: int, seed: int,
+                 b: float = 0.1, thr: float = 0.005, tau0: float = 0.8, tau1: float = 0.4):
+        self.ctx, self.W = ctx, weights
+        self.B = len(caches)
+        self.dims = Dims.of(dims)                       # one canvas
+        C, d = self.dims.C, self.dims.d
+        self.dims_all = Dims(self.dims.V, d, self.B * C, self.dims.Hq, self.dims.Hkv,
+                             self.dims.hd, self.dims.F)  # all B canvases as columns
+        self.Kp = [c[0] for c in caches]
+        self.Vt = [c[1] for c in caches]
+        self.P = [int(c[2]) for c in caches]
+        self.N, self.seed, self.b, self.thr, self.tau0, self.tau1 = N, seed, b, thr, tau0, tau1
+        dev = self.Kp[0].device
+        B = self.B
+        self.ws_attn = torch.empty(workspace_bytes(self.dims, max(k.shape[1] for k in self.Kp)),
+                                   dtype=torch.uint8, device=dev)
+        self.ws = torch.empty(workspace_bytes(self.dims_all, 0), dtype=torch.uint8, device=dev)
+        self.tokens = torch.empty(B, C, dtype=torch.int32, device=dev)
+        self.z = torch.zeros(B, C, d, dtype=torch.bfloat16, device=dev)
+        self.A = torch.empty(B, C, d, dtype=torch.bfloat16, device=dev)
+        self.entropy = torch.empty(B, C, dtype=torch.float32, device=dev)
+        self.argmax = [torch.empty(B, C, dtype=torch.int32, device=dev) for _ in range(2)]
+        self.accept = torch.empty(B, C, dtype=torch.uint8, device=dev)
+        self.n_accept = torch.empty(B, dtype=torch.int32, device=dev)
+        # Same protocol as CanvasLoop: pinned flags written by the stop kernel, four
+        # buffers taken in enqueue order.
+        self.flags = [torch.full((B,), -1, dtype=torch.int32, pin_memory=True) for _ in range(4)]
+        self._seq = 0
+        self._slot = {}
+
+    def init_batch(self, batch: int):
+        """Uniform random canvases (init stream) for canvas ids batch*B .. batch*B+B-1, z = 0."""
+        self.batch = batch
+        self.ctx.renoise(self.dims.V, None, None, self.seed, batch * self.B, 0, self.tokens)
+        self.z.zero_()
+        self._slot = {}
+
+    def step(self, k: int, H):
+        """Enqueues denoise step k of every canvas; H [B*C, d] holds the canvases' hidden
+        states in canvas order."""
+        W, dm = self.W, self.dims
+        am, prev = self.argmax[k & 1], (self.argmax[(k - 1) & 1] if k > 0 else None)
+        for i in range(self.B):
+            self.ctx.canvas_attn(dm, self.tokens[i], self.z[i] if k > 0 else None, W["E"], W["Wq"],
+                                 W["Wk"], W["Wv"], W["Wo"], self.Kp[i], self.Vt[i], self.P[i],
+                                 self.ws_attn, self.A[i])
+        tau = temperature(k, self.N, self.tau0, self.tau1)
+        self.ctx.logits_entropy(self.dims_all, H, W["E"], tau, self.ws, self.entropy.view(-1),
+                                am.view(-1))
+        self.ctx.entropy_accept(self.entropy, self.b, self.accept, self.n_accept)
+        self.ctx.renoise(dm.V, am, self.accept, self.seed, self.batch * self.B, k, self.tokens)
+        self.ctx.selfcond(self.dims_all, self.ws, W["E"], W["W1"], W["W2"], self.z.view(-1, dm.d))
+        slot = self._seq % len(self.flags)
+        self._seq += 1
+        self._slot[k] = slot
+        self.flags[slot].fill_(-1)
+        self.ctx.stop_test(self.entropy, am, prev, self.thr, k, self.N, self.flags[slot])
+        return am
+
+    def wait_flags(self, k: int, timeout_s: float = 60.0):
+        """Step k's stop flags (one per canvas) once the device has written them all."""
+        f = self.flags[self._slot[k]]
+        deadline = time.monotonic() + timeout_s
+        while True:
+            v = f.tolist()
+            if min(v) >= 0:
+                return v
+            if time.monotonic() > deadline:
+                torch.cuda.synchronize(self.Kp[0].device)
+                v = f.tolist()
+                if min(v) >= 0:
+                    return v
+                raise RuntimeError(f"stop flags of step {k} were never written")
+
+    def run_batch(self, batch: int, hidden, on_step=None):
+        """Init, denoise until every canvas has stopped or capped, commit every canvas.
+        Returns each canvas's step count. hidden(k) -> [B*C, d] device tensor; on_step as
+        in CanvasLoop.run_canvas. Step k + 1 is enqueued before the host reads step k's
+        flags; x0 of a canvas that stops at step k is copied from step k's argmax buffer
+        before step k + 2, the next writer of that buffer, is enqueued."""
+        self.init_batch(batch)
+        B, C = self.B, self.dims.C
+        x0 = [None] * B
+        steps = [0] * B
+        k = 0
+        self.step(0, hidden(0))
+        if on_step is not None:
+            on_step(0, self)
+        while True:
+            if k + 1 < self.N:
+                self.step(k + 1, hidden(k + 1))
+            flags = self.wait_flags(k)
+            for i in range(B):
+                if x0[i] is None and flags[i] != STOP_GO:
+                    x0[i] = self.argmax[k & 1][i].clone()
+                    steps[i] = k + 1
+            if all(x is not None for x in x0):
+                break
+            k += 1
+            if on_step is not None:
+                on_step(k, self)
+        for i in range(B):
+            self.P[i] = self.ctx.commit_kv(self.dims, x0[i], self.W["E"], self.W["Wk"],
+                                           self.W["Wv"], self.Kp[i], self.Vt[i], self.P[i])
+        return steps

@@ -145,17 +145,19 @@ def weights(cfg: Config) -> dict:
     }
 
 
-def prefix_kv(cfg: Config, Pcap: int | None = None):
+def prefix_kv(cfg: Config, Pcap: int | None = None, request: int = 0):
     """Prefix K and V caches, logical layout [Hkv, Pcap, hd], rows [0, P0) ~ N(0, 1).
 
-    Rows [P0, Pcap) are zero (free capacity for committed canvases).
+    Rows [P0, Pcap) are zero (free capacity for committed canvases). ``request`` r > 0
+    draws an independent prefix (tags offset by 32 r) for the r-th request of a batch.
     """
     Pcap = cfg.Pcap if Pcap is None else Pcap
     K = np.zeros((cfg.Hkv, Pcap, cfg.hd), dtype=np.uint16)
     V = np.zeros((cfg.Hkv, Pcap, cfg.hd), dtype=np.uint16)
     if cfg.P0:
-        K[:, :cfg.P0] = gaussian_bf16(cfg.seed, TAG_KP, (cfg.Hkv, cfg.P0, cfg.hd), 1.0)
-        V[:, :cfg.P0] = gaussian_bf16(cfg.seed, TAG_VP, (cfg.Hkv, cfg.P0, cfg.hd), 1.0)
+        off = 32 * int(request)
+        K[:, :cfg.P0] = gaussian_bf16(cfg.seed, TAG_KP + off, (cfg.Hkv, cfg.P0, cfg.hd), 1.0)
+        V[:, :cfg.P0] = gaussian_bf16(cfg.seed, TAG_VP + off, (cfg.Hkv, cfg.P0, cfg.hd), 1.0)
     return K, V
 
 

@@ -31,6 +31,10 @@ SHAPES = {
                       alpha_max=9.0, seed=22),
     "c1000": di.Config("c1000", V=1000, d=64, C=1000, Hq=2, Hkv=2, hd=16, F=32, P0=5, N=4,
                        alpha_max=6.0, seed=23),
+    # two canvas blocks over a tile count divisible by 8 and 8 self-conditioning splits:
+    # the workgroup mappings that keep a tile's (a split's) canvas blocks on one XCD
+    "wide": di.Config("wide", V=32768, d=256, C=300, Hq=4, Hkv=2, hd=64, F=128, P0=100, N=4,
+                      alpha_max=8.0, seed=24),
 }
 
 _cache = {}
