@@ -42,6 +42,7 @@ def parse():
     ap.add_argument("--roofline-reps", type=int, default=20)
     ap.add_argument("--cpu-steps", type=int, default=1, help="oracle steps timed for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-batched", action="store_true", help="skip the batched-canvas lines")
     ap.add_argument("--no-long-prefix", action="store_true",
                     help="skip the isolated attention call over a 262144-token prefix")
     ap.add_argument("--no-chain", action="store_true",
@@ -224,7 +225,10 @@ def main():
 
     if not args.no_long_prefix:
         result["long_prefix_attention"] = long_prefix_attention(ctx, cfg, Wd, Hd[0], args.roofline_reps)
-    del Hd, Kd, Vtd, loop
+    del Kd, Vtd, loop
+    if not args.no_batched:
+        result["batched"] = [batched_canvases(ctx, cfg, Wd, Hd, B) for B in (2, 4)]
+    del Hd
     if not args.no_chain:
         result["chain8"] = chain(ctx)
     if not args.no_cpu_baseline:
@@ -281,6 +285,50 @@ def long_prefix_attention(ctx, cfg, Wd, H, reps):
     return {"prefix_tokens": P, "ms_per_call": round(ms, 4), "kv_bytes": kv_bytes,
             "achieved_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
             "attention_tflops": round(tfs, 1), "mfma_frac": round(tfs / BF16_PEAK_TFLOPS, 4)}
+
+
+def batched_canvases(ctx, cfg, Wd, Hd, B):
+    """B canvases in lockstep, one per request, each request with its own prefix of
+    cfg.P0 tokens (seeded per request): one warm-up batch, then one timed batch from
+    init to the last commit. The logits kernel runs on B*C columns here; its in-step time
+    (HIP events around each dg_logits_entropy) gives the MFMA fraction at that width."""
+    import torch
+
+    import dg_inputs as di
+    from block_ar_canvas_amd.loop import BatchLoop
+    dev = Hd[0].device
+    Pcap = -(-(cfg.P0 + 2 * cfg.C) // 8) * 8
+    caches = []
+    for r in range(B):
+        Kp, Vp = di.prefix_kv(cfg, Pcap, request=r)
+        caches.append((_bf(Kp, dev), _bf(np.ascontiguousarray(Vp.transpose(0, 2, 1)), dev), cfg.P0))
+        del Kp, Vp
+    loop = BatchLoop(ctx, cfg, Wd, caches, N=cfg.N, seed=cfg.seed)
+    stream = torch.cuda.current_stream()
+
+    def hidden_of(j):
+        hs = [torch.cat([Hd[(j * B + i) % len(Hd)][k] for i in range(B)], dim=0) for k in range(cfg.N)]
+        return lambda k: hs[k]
+
+    loop.run_batch(0, hidden_of(0))
+    h1 = hidden_of(1)
+    torch.cuda.synchronize()
+    loop.logits_events = []
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    steps = loop.run_batch(1, h1)
+    e1.record(stream)
+    e1.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3
+    evs = loop.logits_events
+    logits_ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    flops = 2.0 * B * cfg.C * cfg.V * cfg.d
+    return {"B": B, "canvas_tokens_per_s": round(B * cfg.C / sec, 1),
+            "batched_steps_per_s": round(max(steps) / sec, 2),
+            "ms_per_batched_step": round(1e3 * sec / max(steps), 4),
+            "logits_ms_per_launch": round(logits_ms, 4),
+            "logits_mfma_frac": round(flops / (logits_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "prefix_tokens_per_request": cfg.P0}
 
 
 def chain(ctx):

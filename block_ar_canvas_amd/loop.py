@@ -180,6 +180,7 @@ class BatchLoop:
         self.flags = [torch.full((B,), -1, dtype=torch.int32, pin_memory=True) for _ in range(4)]
         self._seq = 0
         self._slot = {}
+        self.logits_events = None          # as in CanvasLoop
 
     def init_batch(self, batch: int):
         """Uniform random canvases (init stream) for canvas ids batch*B .. batch*B+B-1, z = 0."""
@@ -198,8 +199,16 @@ class BatchLoop:
                                  W["Wk"], W["Wv"], W["Wo"], self.Kp[i], self.Vt[i], self.P[i],
                                  self.ws_attn, self.A[i])
         tau = temperature(k, self.N, self.tau0, self.tau1)
+        ev = self.logits_events
+        if ev is not None:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e0.record(self.ctx._stream)
         self.ctx.logits_entropy(self.dims_all, H, W["E"], tau, self.ws, self.entropy.view(-1),
                                 am.view(-1))
+        if ev is not None:
+            e1 = torch.cuda.Event(enable_timing=True)
+            e1.record(self.ctx._stream)
+            ev.append((e0, e1))
         self.ctx.entropy_accept(self.entropy, self.b, self.accept, self.n_accept)
         self.ctx.renoise(dm.V, am, self.accept, self.seed, self.batch * self.B, k, self.tokens)
         self.ctx.selfcond(self.dims_all, self.ws, W["E"], W["W1"], W["W2"], self.z.view(-1, dm.d))
