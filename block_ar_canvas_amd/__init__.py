@@ -13,7 +13,7 @@ import os
 
 import torch
 
-__all__ = ["DGError", "Dims", "Context", "workspace_bytes", "temperature", "lib_path",
+__all__ = ["DGError", "Dims", "Context", "workspace_bytes", "temperature", "reveal_count", "lib_path",
            "STOP_GO", "STOP_STOP", "STOP_CAP"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -72,6 +72,9 @@ def _load():
         "dg_canvas_attn": (i32, [_P, D, _P, _P, _P, _P, _P, _P, _P, _P, _P, i64, i64, _P, _P]),
         "dg_logits_entropy": (i32, [_P, D, _P, _P, f32, _P, _P, _P]),
         "dg_entropy_accept": (i32, [_P, i32, i32, _P, f32, _P, _P]),
+        "dg_confidence": (i32, [_P, D, _P, _P]),
+        "dg_topk_accept": (i32, [_P, i32, i32, _P, i32, _P, _P]),
+        "dg_reveal_count": (i32, [i32, i32, i32]),
         "dg_renoise": (i32, [_P, i32, i32, i32, _P, _P, u64, u32, u32, _P]),
         "dg_selfcond": (i32, [_P, D, _P, _P, _P, _P, _P]),
         "dg_stop_test": (i32, [_P, i32, i32, _P, _P, _P, f32, i32, i32, _P]),
@@ -95,6 +98,14 @@ def workspace_bytes(dims, Pcap: int) -> int:
 
 def temperature(k: int, N: int, tau0: float = 0.8, tau1: float = 0.4) -> float:
     return float(_load().dg_temperature(int(k), int(N), float(tau0), float(tau1)))
+
+
+def reveal_count(C: int, N: int, step: int) -> int:
+    """Positions accepted at `step` under the confidence rule's reveal schedule."""
+    n = int(_load().dg_reveal_count(int(C), int(N), int(step)))
+    if n < 0:
+        raise ValueError(f"reveal_count: bad arguments C={C} N={N} step={step}")
+    return n
 
 
 def _ptr(t, dtype, name, optional=False, pinned_ok=False):
@@ -188,6 +199,17 @@ class Context:
         B, C = (1, entropy.shape[0]) if entropy.dim() == 1 else tuple(entropy.shape)
         self._check(self._lib.dg_entropy_accept(
             self._h, B, C, _ptr(entropy, _F32, "entropy"), float(b), _ptr(accept, _U8, "accept"),
+            _ptr(n_accept, _I32, "n_accept")))
+
+    def confidence(self, dims, ws, conf):
+        d = Dims.of(dims)
+        self._check(self._lib.dg_confidence(self._h, ctypes.byref(d), _ptr(ws, _U8, "ws"),
+                                            _ptr(conf, _F32, "confidence")))
+
+    def topk_accept(self, score, k, accept, n_accept):
+        B, C = (1, score.shape[0]) if score.dim() == 1 else tuple(score.shape)
+        self._check(self._lib.dg_topk_accept(
+            self._h, B, C, _ptr(score, _F32, "score"), int(k), _ptr(accept, _U8, "accept"),
             _ptr(n_accept, _I32, "n_accept")))
 
     def renoise(self, V, argmax, accept, seed, canvas_base, step, tokens):

@@ -269,6 +269,7 @@ dg_status dg_logits_entropy(dg_ctx ctx, const dg_dims *dims, const dg_bf16 *H,
   a.targ = ws_at<int>(ws, w.targ);
   a.colR = ws_at<float>(ws, w.colR);
   a.colZ = ws_at<float>(ws, w.colZ);
+  a.colP = ws_at<float>(ws, w.colP);
   a.entropy = entropy;
   a.argmax = argmax;
   a.status = ctx->d_status;
@@ -289,6 +290,39 @@ dg_status dg_entropy_accept(dg_ctx ctx, int32_t B, int32_t C, const float *entro
   const uint64_t budget = (uint64_t)floor((double)b * 4294967296.0);
   hipError_t e = dg_launch_accept(B, C, entropy, budget, accept, n_accept, ctx->stream);
   return e == hipSuccess ? DG_OK : hip_fail(ctx, e, "dg_entropy_accept");
+}
+
+dg_status dg_confidence(dg_ctx ctx, const dg_dims *dims, const void *ws, float *confidence) {
+  if (!ctx) return DG_ERR_NULL;
+  dg_status st = check_dims(ctx, dims, __func__);
+  if (st) return st;
+  DG_REQUIRE_PTR(ws);
+  DG_REQUIRE_PTR(confidence);
+  const dg_dims &m = *dims;
+  if (!ctx->p0_valid || ctx->p0_ws != ws || memcmp(&ctx->p0_dims, &m, sizeof m) != 0)
+    return fail(ctx, DG_ERR_STATE, "%s: ws does not hold p0 of a dg_logits_entropy with these dims", __func__);
+  const DgWs w = dg_ws_layout(m.V, m.d, m.C, m.Hq, m.Hkv, m.hd, m.F, 0);
+  hipError_t e = dg_launch_confidence(m.C, ws_at<float>(const_cast<void *>(ws), w.colP), confidence,
+                                      ctx->stream);
+  return e == hipSuccess ? DG_OK : hip_fail(ctx, e, "dg_confidence");
+}
+
+dg_status dg_topk_accept(dg_ctx ctx, int32_t B, int32_t C, const float *score, int32_t k,
+                         uint8_t *accept, int32_t *n_accept) {
+  if (!ctx) return DG_ERR_NULL;
+  if (B < 1 || C < 1 || C > 1024) return fail(ctx, DG_ERR_SHAPE, "%s: need B >= 1, 1 <= C <= 1024", __func__);
+  if (!score || !accept || !n_accept) return fail(ctx, DG_ERR_NULL, "%s: NULL buffer", __func__);
+  if (k < 0) return fail(ctx, DG_ERR_RANGE, "%s: k=%d must be >= 0", __func__, (int)k);
+  hipError_t e = dg_launch_topk(B, C, score, k > C ? C : k, accept, n_accept, ctx->stream);
+  return e == hipSuccess ? DG_OK : hip_fail(ctx, e, "dg_topk_accept");
+}
+
+int32_t dg_reveal_count(int32_t C, int32_t N, int32_t step) {
+  if (C < 0 || N < 1 || step < 0) return -1;
+  if (step >= N) step = N - 1;
+  int64_t n = 0;
+  for (int32_t t = 0; t <= step; ++t) n += (C - n + (N - t) - 1) / (N - t);
+  return (int32_t)n;
 }
 
 dg_status dg_renoise(dg_ctx ctx, int32_t B, int32_t C, int32_t V, const int32_t *argmax,

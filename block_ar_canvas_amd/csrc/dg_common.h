@@ -118,6 +118,7 @@ struct DgWs {
   size_t tmax, trho, tsum, tent, targ;  // per-(column, tile) statistics [Cpad][T]
   size_t colR;     // per-column reference R = max_t rho_t                  [Cpad]
   size_t colZ;     // per-column softmax sum relative to 2^R                 [Cpad]
+  size_t colP;     // per-column confidence: the largest probability of p0   [Cpad]
   size_t rhoS;     // per-(split, column) reference rho_S = max over the split [nsc][Cpad]
   size_t q;        // Q   bf16 [Cpad][Hq*hd]
   size_t kc;       // canvas keys   bf16 [Cpad][Hkv*hd]
@@ -183,6 +184,7 @@ static inline DgWs dg_ws_layout(int V, int d, int C, int Hq, int Hkv, int hd, in
   w.targ = take(CT * 4);
   w.colR = take((size_t)w.Cpad * 4);
   w.colZ = take((size_t)w.Cpad * 4);
+  w.colP = take((size_t)w.Cpad * 4);
   w.rhoS = take((size_t)w.nsc * w.Cpad * 4);
   w.q = take((size_t)w.Cpad * Hq * hd * 2);
   w.kc = take((size_t)w.Cpad * Hkv * hd * 2);
@@ -253,6 +255,7 @@ struct LogitsArgs {
   float *tmax, *trho, *tsum, *tent;
   int *targ;
   float *colR, *colZ;  // per-column reference and softmax sum
+  float *colP;         // per-column largest probability
   float *entropy;      // [C]
   int *argmax;         // [C]
   int *status;
@@ -273,6 +276,9 @@ hipError_t dg_launch_selfcond(const SelfcondArgs &a, hipStream_t st);
 
 hipError_t dg_launch_accept(int B, int C, const float *ent, uint64_t budget, uint8_t *acc,
                             int *nacc, hipStream_t st);
+hipError_t dg_launch_topk(int B, int C, const float *score, int k, uint8_t *acc, int *nacc,
+                          hipStream_t st);
+hipError_t dg_launch_confidence(int C, const float *colP, float *conf, hipStream_t st);
 hipError_t dg_launch_renoise(int B, int C, int V, const int *am, const uint8_t *acc,
                              uint64_t seed, uint32_t canvas_base, uint32_t step, int *tok,
                              hipStream_t st);

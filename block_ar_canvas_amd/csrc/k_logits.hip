@@ -301,7 +301,8 @@ __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a) {
 // One workgroup per canvas column merges that column's tile statistics ([column][tile]
 // layout: contiguous reads) in a fixed order, so the result is deterministic. Besides
 // entropy and argmax it leaves the column reference R and the sum Z (relative to R)
-// for the self-conditioning product.
+// for the self-conditioning product, and the column's largest probability (the
+// confidence that confidence-ranked acceptance orders positions by).
 __global__ __launch_bounds__(256) void row_finalize_kernel(LogitsArgs a) {
   __shared__ float sm[4], sr[4], sz[4], ss[4];
   __shared__ int si[4], sbad[4];
@@ -394,10 +395,23 @@ __global__ __launch_bounds__(256) void row_finalize_kernel(LogitsArgs a) {
     a.argmax[c] = bad ? 0 : a.targ[(int64_t)c * a.T + tb];
     a.colR[c] = bad ? __builtin_nanf("") : R;
     a.colZ[c] = bad ? __builtin_nanf("") : Z;
+    // confidence = the largest probability = 2^(m - R) / Z (m: the column's largest x)
+    a.colP[c] = bad ? __builtin_nanf("") : exp2_fast(m - R) / Z;
   }
 }
 
+// Copies the finalize kernel's per-column confidence out of the workspace.
+__global__ __launch_bounds__(256) void confidence_kernel(int C, const float *colP, float *conf) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < C) conf[i] = colP[i];
+}
+
 }  // namespace
+
+hipError_t dg_launch_confidence(int C, const float *colP, float *conf, hipStream_t st) {
+  hipLaunchKernelGGL(confidence_kernel, dim3((C + 255) / 256), dim3(256), 0, st, C, colP, conf);
+  return hipGetLastError();
+}
 
 hipError_t dg_launch_logits(const LogitsArgs &a, hipStream_t st) {
   static bool attr = false;

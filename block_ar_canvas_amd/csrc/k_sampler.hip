@@ -22,6 +22,12 @@
 // Stop test (Technical Report page, "Method steps" (4)): the canvas stops when its
 // mean entropy is <= the threshold and the argmax did not change since the previous
 // step; the step cap commits anyway.
+//
+// Confidence-ranked acceptance (the openai-hub page "从零拆开DiffusionGemma", step 4,
+// confidence decoding; the "Text diffusion models" survey, section 5): each step keeps
+// the k positions the model is most confident about. Same rank construction as the
+// entropy rule: distinct 64-bit keys (score order, position), rank = keys below one's
+// own, accepted iff rank < k.
 #include "dg_common.h"
 
 namespace {
@@ -71,6 +77,46 @@ __global__ __launch_bounds__(1024) void accept_kernel(int C, int tpp, const floa
   sum += sum2;
   for (int o = 1; o < tpp; o <<= 1) sum += __shfl_xor(sum, o);
   const bool take = pos < C && sum <= budget;
+  if (pos < C && sub == 0) acc[(int64_t)b * C + pos] = take ? 1 : 0;
+  const int n = __syncthreads_count(take && sub == 0);
+  if (tid == 0 && nacc) nacc[b] = n;
+}
+
+// Order-preserving code of a float score (ascending score = ascending code).
+DG_DEV uint32_t score_code(float s) {
+  const uint32_t b = __float_as_uint(s);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// tpp threads per position as in accept_kernel. Keys: (~code(score) << 32 | position),
+// so ascending keys = descending score, ties to the lower position; NaN scores get the
+// largest keys and are never accepted.
+__global__ __launch_bounds__(1024) void topk_kernel(int C, int tpp, const float *score, int k,
+                                                    uint8_t *acc, int *nacc) {
+  __shared__ uint64_t keys[1024];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int pos = tid / tpp, sub = tid % tpp;
+  uint64_t key = ~0ull;
+  bool valid = false;
+  if (pos < C) {
+    const float s = score[(int64_t)b * C + pos];
+    valid = s == s;
+    const uint32_t hi = valid ? ~score_code(s) : 0xFFFFFFFFu;
+    key = ((uint64_t)hi << 32) | (uint32_t)pos;
+    if (sub == 0) keys[pos] = key;
+  }
+  __syncthreads();
+  int rank = 0, rank2 = 0;
+  int j = sub;
+#pragma unroll 4
+  for (; j + tpp < C; j += 2 * tpp) {
+    rank += keys[j] < key ? 1 : 0;
+    rank2 += keys[j + tpp] < key ? 1 : 0;
+  }
+  if (j < C) rank += keys[j] < key ? 1 : 0;
+  rank += rank2;
+  for (int o = 1; o < tpp; o <<= 1) rank += __shfl_xor(rank, o);
+  const bool take = pos < C && valid && rank < k;
   if (pos < C && sub == 0) acc[(int64_t)b * C + pos] = take ? 1 : 0;
   const int n = __syncthreads_count(take && sub == 0);
   if (tid == 0 && nacc) nacc[b] = n;
@@ -150,6 +196,15 @@ hipError_t dg_launch_accept(int B, int C, const float *ent, uint64_t budget, uin
   const int tpp = C <= 256 ? 4 : C <= 512 ? 2 : 1;
   const int n = (C * tpp + 63) / 64 * 64;
   hipLaunchKernelGGL(accept_kernel, dim3(B), dim3(n), 0, st, C, tpp, ent, budget, acc, nacc);
+  return hipGetLastError();
+}
+
+hipError_t dg_launch_topk(int B, int C, const float *score, int k, uint8_t *acc, int *nacc,
+                          hipStream_t st) {
+  // C <= 1024 (checked by the caller); up to 4 threads per position
+  const int tpp = C <= 256 ? 4 : C <= 512 ? 2 : 1;
+  const int n = (C * tpp + 63) / 64 * 64;
+  hipLaunchKernelGGL(topk_kernel, dim3(B), dim3(n), 0, st, C, tpp, score, k, acc, nacc);
   return hipGetLastError();
 }
 

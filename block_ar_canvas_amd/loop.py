@@ -16,7 +16,9 @@ import time
 
 import torch
 
-from . import STOP_GO, Context, Dims, temperature, workspace_bytes
+from . import STOP_GO, Context, Dims, reveal_count, temperature, workspace_bytes
+
+RULES = ("entropy", "confidence")
 
 
 class CanvasLoop:
@@ -24,10 +26,16 @@ class CanvasLoop:
 
     weights: dict of bf16 device tensors E, Wq, Wk, Wv, Wo, W1, W2 ([out, in] layout).
     Kp [Hkv, Pcap, hd] and Vt [Hkv, hd, Pcap] bf16 device tensors: the KV cache.
+    rule: "entropy" (entropy-bounded acceptance with budget b) or "confidence" (the
+    reveal_count(C, N, k) most confident positions of step k are accepted).
     """
 
     def __init__(self, ctx: Context, dims, weights, Kp, Vt, P: int, *, N: int, seed: int,
-                 b: float = 0.1, thr: float = 0.005, tau0: float = 0.8, tau1: float = 0.4):
+                 b: float = 0.1, thr: float = 0.005, tau0: float = 0.8, tau1: float = 0.4,
+                 rule: str = "entropy"):
+        if rule not in RULES:
+            raise ValueError(f"rule must be one of {RULES}")
+        self.rule = rule
         self.ctx, self.dims = ctx, Dims.of(dims)
         self.W, self.Kp, self.Vt, self.P = weights, Kp, Vt, int(P)
         self.N, self.seed, self.b, self.thr, self.tau0, self.tau1 = N, seed, b, thr, tau0, tau1
@@ -38,6 +46,7 @@ class CanvasLoop:
         self.z = torch.zeros(C, d, dtype=torch.bfloat16, device=dev)
         self.A = torch.empty(C, d, dtype=torch.bfloat16, device=dev)
         self.entropy = torch.empty(C, dtype=torch.float32, device=dev)
+        self.conf = torch.empty(C, dtype=torch.float32, device=dev)
         self.argmax = [torch.empty(C, dtype=torch.int32, device=dev) for _ in range(2)]
         self.accept = torch.empty(C, dtype=torch.uint8, device=dev)
         self.n_accept = torch.empty(1, dtype=torch.int32, device=dev)
@@ -77,7 +86,11 @@ class CanvasLoop:
             e1 = torch.cuda.Event(enable_timing=True)
             e1.record(self.ctx._stream)
             ev.append((e0, e1))
-        self.ctx.entropy_accept(self.entropy, self.b, self.accept, self.n_accept)
+        if self.rule == "confidence":
+            self.ctx.confidence(dm, self.ws, self.conf)
+            self.ctx.topk_accept(self.conf, reveal_count(dm.C, self.N, k), self.accept, self.n_accept)
+        else:
+            self.ctx.entropy_accept(self.entropy, self.b, self.accept, self.n_accept)
         self.ctx.renoise(dm.V, am, self.accept, self.seed, self.canvas, k, self.tokens)
         self.ctx.selfcond(dm, self.ws, W["E"], W["W1"], W["W2"], self.z)
         slot = self._seq % len(self.flags)
@@ -152,7 +165,11 @@ class BatchLoop:
     """
 
     def __init__(self, ctx: Context, dims, weights, caches, *, N: int, seed: int,
-                 b: float = 0.1, thr: float = 0.005, tau0: float = 0.8, tau1: float = 0.4):
+                 b: float = 0.1, thr: float = 0.005, tau0: float = 0.8, tau1: float = 0.4,
+                 rule: str = "entropy"):
+        if rule not in RULES:
+            raise ValueError(f"rule must be one of {RULES}")
+        self.rule = rule
         self.ctx, self.W = ctx, weights
         self.B = len(caches)
         self.dims = Dims.of(dims)                       # one canvas
@@ -172,6 +189,7 @@ class BatchLoop:
         self.z = torch.zeros(B, C, d, dtype=torch.bfloat16, device=dev)
         self.A = torch.empty(B, C, d, dtype=torch.bfloat16, device=dev)
         self.entropy = torch.empty(B, C, dtype=torch.float32, device=dev)
+        self.conf = torch.empty(B, C, dtype=torch.float32, device=dev)
         self.argmax = [torch.empty(B, C, dtype=torch.int32, device=dev) for _ in range(2)]
         self.accept = torch.empty(B, C, dtype=torch.uint8, device=dev)
         self.n_accept = torch.empty(B, dtype=torch.int32, device=dev)
@@ -209,7 +227,11 @@ class BatchLoop:
             e1 = torch.cuda.Event(enable_timing=True)
             e1.record(self.ctx._stream)
             ev.append((e0, e1))
-        self.ctx.entropy_accept(self.entropy, self.b, self.accept, self.n_accept)
+        if self.rule == "confidence":
+            self.ctx.confidence(self.dims_all, self.ws, self.conf.view(-1))
+            self.ctx.topk_accept(self.conf, reveal_count(dm.C, self.N, k), self.accept, self.n_accept)
+        else:
+            self.ctx.entropy_accept(self.entropy, self.b, self.accept, self.n_accept)
         self.ctx.renoise(dm.V, am, self.accept, self.seed, self.batch * self.B, k, self.tokens)
         self.ctx.selfcond(self.dims_all, self.ws, W["E"], W["W1"], W["W2"], self.z.view(-1, dm.d))
         slot = self._seq % len(self.flags)

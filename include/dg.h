@@ -134,6 +134,31 @@ dg_status dg_logits_entropy(dg_ctx ctx, const dg_dims *dims, const dg_bf16 *H,
 dg_status dg_entropy_accept(dg_ctx ctx, int32_t B, int32_t C, const float *entropy,
                             float b, uint8_t *accept, int32_t *n_accept);
 
+/* Confidence of every canvas position: the largest probability of its tempered p0,
+ * max_v p0[c][v] = 2^(m - R) / Z in the log2-unit statistics the logits pass keeps (m the
+ * column's largest tempered logit, R its reference, Z the sum relative to 2^R); NaN for
+ * a column whose logits were not finite. It is the score confidence decoding ranks
+ * positions by (openai-hub page "从零拆开DiffusionGemma", step 4; "Text diffusion
+ * models" survey, section 5). ws must hold the p0 of the immediately preceding
+ * dg_logits_entropy with these dims (DG_ERR_STATE otherwise).
+ * confidence [C] float32 output. */
+dg_status dg_confidence(dg_ctx ctx, const dg_dims *dims, const void *ws, float *confidence);
+
+/* Confidence-ranked acceptance (same pages): in each of B segments of C positions,
+ * accept the k positions with the highest score; equal scores are taken in position
+ * order (compared by value bits, so -0 ranks below +0), and NaN scores are never
+ * accepted. k > C accepts every non-NaN position; k < 0 is DG_ERR_RANGE.
+ * score [B, C] float32; accept [B, C] uint8 (0/1); n_accept [B] int32. */
+dg_status dg_topk_accept(dg_ctx ctx, int32_t B, int32_t C, const float *score, int32_t k,
+                         uint8_t *accept, int32_t *n_accept);
+
+/* Host-side reveal schedule of confidence decoding (openai-hub page, step 4: each step
+ * reveals ceil(unresolved / remaining steps) positions): the number of positions
+ * revealed after steps 0..step of an N-step run over C positions,
+ *   n_{-1} = 0,  n_t = n_{t-1} + ceil((C - n_{t-1}) / (N - t)),
+ * so n_{N-1} = C; steps past N - 1 give C. Pure; -1 for C < 0, N < 1 or step < 0. */
+int32_t dg_reveal_count(int32_t C, int32_t N, int32_t step);
+
 /* Uniform-state renoise (Technical Report page, "Method steps" (2)-(3); Google page,
  * "Uniform State Diffusion"): accepted positions take argmax, every other position a
  * token drawn uniformly over [0, V):

@@ -21,7 +21,11 @@ Sources (web pages on DiffusionGemma):
         Diffusion", "Architecture: incremental prefill and denoising", "Self-conditioning",
         "Multi-canvas sampling".
   [SRV] "Text diffusion models" survey (papers.franksyz.com), section 11 (DiffusionGemma
-        defaults: 48 steps, entropy bound 0.1, temperature 0.8 -> 0.4).
+        defaults: 48 steps, entropy bound 0.1, temperature 0.8 -> 0.4), section 5 (reverse
+        generation: predict, select, accept, remask).
+  [HUB] openai-hub page "从零拆开DiffusionGemma" (news 2086), step 4 (confidence decoding:
+        predict every position, keep the most confident ones, the simplified decoder's
+        reveal count ceil(unresolved / remaining steps)).
 
 Readings taken where the pages leave a step open (each restated where it is used):
   * temperature: tau_k = tau0 + (tau1 - tau0) * k / (N - 1) over the step budget N,
@@ -38,6 +42,11 @@ Readings taken where the pages leave a step open (each restated where it is used
     previous step; otherwise the step cap N - 1 commits anyway;
   * commit: the finalized block is x^0 = argmax at the stopping step; its K/V rows are
     E[x^0] Wk^T and E[x^0] Wv^T (stand-in for the causal re-encode), appended at [P, P+C).
+  * the confidence rule (an alternative to the entropy budget): a position's confidence
+    is its largest tempered probability; step k accepts the n_k most confident positions
+    (ties to the lower position, NaN never), n_k the number the [HUB] decoder has revealed
+    after step k; accepted positions keep x^0, the rest are renoised as above, and every
+    position is ranked afresh each step.
 """
 from __future__ import annotations
 
@@ -216,6 +225,58 @@ def entropy_accept(entropy, b):
     return accept, n_acc
 
 
+# ------------------------------------------------------------------ confidence rule
+def confidence(H_bits, E_bits, tau, rows=None):
+    """Confidence of every position: its largest tempered probability max_v p^0[c][v].
+
+    [HUB] step 4: the decoder computes probs = softmax(logits / temperature) and takes
+    (confidence, candidates) = probs.max(-1). Stored as float32.
+    """
+    _, _, p, _ = logits_entropy(H_bits, E_bits, tau, rows)
+    return p.max(axis=1).astype(np.float32)
+
+
+def reveal_schedule(C: int, N: int):
+    """Number of positions revealed after each step of the [HUB] decoder.
+
+    The page's simplified decoder starts with C masked positions and at step s reveals
+    ceil(unresolved / remaining) of them, remaining = N - s, with the same C positions
+    never revealed twice. Counted here by running that bookkeeping: a list of the
+    cumulative revealed counts after steps 0 .. N-1 (the last one is C).
+    """
+    unresolved = C
+    out = []
+    for s in range(N):
+        remaining = N - s
+        reveal = min(-(-unresolved // remaining), unresolved)
+        unresolved -= reveal
+        out.append(C - unresolved)
+    return out
+
+
+def topk_accept(score, k):
+    """Accept the k highest-scoring positions of each of B segments.
+
+    Order: score descending, then position ascending (equal scores go to the lower
+    position; -0.0 counts as below +0.0, the order of their bit patterns); NaN scores
+    are never accepted. score float32 [B, C] -> (accept uint8 [B, C], n_accept int32 [B]).
+    """
+    sc = np.asarray(score, dtype=np.float32)
+    if sc.ndim == 1:
+        sc = sc[None]
+    B, C = sc.shape
+    accept = np.zeros((B, C), dtype=np.uint8)
+    n_acc = np.zeros(B, dtype=np.int32)
+    for s in range(B):
+        valid = [i for i in range(C) if not math.isnan(float(sc[s, i]))]
+        # value descending; for equal values +0.0 before -0.0; then position ascending
+        order = sorted(valid, key=lambda i: (-float(sc[s, i]), math.copysign(1.0, float(sc[s, i])) < 0, i))
+        for i in order[:max(0, int(k))]:
+            accept[s, i] = 1
+            n_acc[s] += 1
+    return accept, n_acc
+
+
 # ------------------------------------------------------------------ (a7, a11) renoise
 _M0, _M1 = 0xD2E7470EE14C6C93, 0xCA5A826395121157      # Philox4x64 multipliers
 _W0, _W1 = 0x9E3779B97F4A7C15, 0xBB67AE8584CAA73B      # Weyl key increments
@@ -357,16 +418,19 @@ def commit_kv(tokens, E_bits, Wk, Wv, Kp, Vp, P, Hkv, hd):
 
 # ------------------------------------------------------------------ the step loop
 def run_canvas(W, Kp, Vp, P, hidden_of_step, *, V, C, Hq, Hkv, hd, N, seed, canvas,
-               b=0.1, thr=0.005, tau0=0.8, tau1=0.4, record=True, with_attn=True):
+               b=0.1, thr=0.005, tau0=0.8, tau1=0.4, record=True, with_attn=True,
+               rule="entropy"):
     """One canvas of the block-AR loop: init, up to N denoise steps, commit.
 
     [TR] "Method steps" (2)-(5) in order; [TUT] data-flow pseudocode. The sampler head's
     hidden states come from ``hidden_of_step(k)`` (the synthetic driver standing in for
     the denoiser stack); the attention output A_k is computed on the true denoiser input
     X_k = E[x_k] + z_k every step and recorded, but does not feed H_k.
+    rule "confidence" replaces the entropy budget by the confidence rule (module header).
     Returns (new P, list of per-step records).
     """
     d = W["E"].shape[1]
+    schedule = reveal_schedule(C, N)
     x = renoise(np.zeros(C, np.int32), None, seed, canvas, 0, V)[0]
     z = np.zeros((C, d), dtype=np.uint16)            # z_1 = 0 (bf16 zero bits)
     prev = None
@@ -381,7 +445,12 @@ def run_canvas(W, Kp, Vp, P, hidden_of_step, *, V, C, Hq, Hkv, hd, N, seed, canv
                                Kp, Vp, P, Hq, Hkv, hd)
             rec["A"] = A
         ent, am, p, _ = logits_entropy(hidden_of_step(k), W["E"], tau)
-        acc, nacc = entropy_accept(ent[None], b)
+        if rule == "confidence":
+            conf = p.max(axis=1).astype(np.float32)
+            acc, nacc = topk_accept(conf[None], schedule[k])
+            rec["conf"] = conf
+        else:
+            acc, nacc = entropy_accept(ent[None], b)
         x = renoise(am[None], acc, seed, canvas, k, V)[0]
         z, _ = selfcond(p, W["E"], W["W1"], W["W2"])
         flag = int(stop_test(ent[None], am[None], None if prev is None else prev[None],

@@ -57,6 +57,17 @@ def test_temperature_matches_oracle(lib):
     assert dg.temperature(0, 48) == np.float32(0.8)
 
 
+def test_reveal_count_matches_oracle(lib):
+    import block_ar_canvas_amd as dg
+
+    for C, N in ((256, 48), (16, 8), (100, 7), (1000, 48), (0, 3), (5, 9)):
+        sched = O.reveal_schedule(C, N)
+        assert [dg.reveal_count(C, N, t) for t in range(N)] == sched
+        assert dg.reveal_count(C, N, N + 3) == C
+    assert lib.dg_reveal_count(4, 0, 0) == -1
+    assert lib.dg_reveal_count(-1, 4, 0) == -1
+
+
 def test_workspace_bytes(lib):
     import block_ar_canvas_amd as dg
 

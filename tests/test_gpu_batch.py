@@ -18,7 +18,7 @@ import dg_inputs as di
 import oracle as O
 from block_ar_canvas_amd.loop import BatchLoop
 from gpu_util import bf16_dev, bits_np, cache_logical, maxrel, near_tie, upload_cache, upload_weights
-from test_gpu_loop import cutoff_entropy
+from test_gpu_loop import cutoff_confidence, cutoff_entropy
 
 pytestmark = pytest.mark.gpu
 
@@ -30,7 +30,7 @@ RAGGED = di.Config("batch_ragged", V=5000, d=96, C=100, Hq=6, Hkv=3, hd=32, F=64
                    alpha_max=9.0, seed=32)
 
 
-def run_batch_both(dg_ctx, cfg, B, batch=1):
+def run_batch_both(dg_ctx, cfg, B, batch=1, rule="entropy"):
     W = di.weights(cfg)
     Pcap = -(-(cfg.P0 + cfg.C) // 8) * 8
     Wd = upload_weights(W)
@@ -40,7 +40,7 @@ def run_batch_both(dg_ctx, cfg, B, batch=1):
         Kd, Vtd = upload_cache(Kp, Vp, Pcap)
         host.append([Kp, Vp])
         caches.append((Kd, Vtd, cfg.P0))
-    loop = BatchLoop(dg_ctx, cfg, Wd, caches, N=cfg.N, seed=cfg.seed)
+    loop = BatchLoop(dg_ctx, cfg, Wd, caches, N=cfg.N, seed=cfg.seed, rule=rule)
     ids = [batch * B + i for i in range(B)]
     Hs = [[di.hidden(cfg, W["E"], c, k, di.targets(cfg, c)) for k in range(cfg.N)] for c in ids]
     Hd = [bf16_dev(np.concatenate([Hs[i][k] for i in range(B)], axis=0)) for k in range(cfg.N)]
@@ -61,7 +61,7 @@ def run_batch_both(dg_ctx, cfg, B, batch=1):
         Kp, Vp = host[i]
         P_o, recs = O.run_canvas(W, Kp, Vp, cfg.P0, lambda k: Hs[i][k], V=cfg.V, C=cfg.C,
                                  Hq=cfg.Hq, Hkv=cfg.Hkv, hd=cfg.hd, N=cfg.N, seed=cfg.seed,
-                                 canvas=c)
+                                 canvas=c, rule=rule)
         assert steps[i] == len(recs)
         for k, r in enumerate(recs):
             g = rec[k]
@@ -70,13 +70,20 @@ def run_batch_both(dg_ctx, cfg, B, batch=1):
             assert maxrel(O.from_bf16(g["A"][i]), O.from_bf16(r["A"])) <= 2e-2
             assert maxrel(O.from_bf16(g["z"][i]), O.from_bf16(r["z"])) <= 2e-2
             _, _, _, u = O.logits_entropy(Hs[i][r["k"]], W["E"], r["tau"])
-            cut = cutoff_entropy(r["entropy"], r["accept"])
+            if rule == "confidence":
+                assert int(g["accept"][i].sum()) == int(r["accept"].sum())
+                cut = cutoff_confidence(r["conf"], r["accept"])
+            else:
+                cut = cutoff_entropy(r["entropy"], r["accept"])
             gt, ga, gm = g["tokens"][i], g["accept"][i], g["argmax"][i]
             mism = np.nonzero(gt != r["tokens"])[0]
             stats["positions"] += cfg.C
             stats["mismatch"] += len(mism)
             for j in mism:
-                near_cut = ga[j] != r["accept"][j] and any(abs(float(r["entropy"][j]) - x) <= 1e-4 for x in cut)
+                if rule == "confidence":
+                    near_cut = ga[j] != r["accept"][j] and any(abs(float(r["conf"][j]) - x) <= 2e-5 * x for x in cut)
+                else:
+                    near_cut = ga[j] != r["accept"][j] and any(abs(float(r["entropy"][j]) - x) <= 1e-4 for x in cut)
                 tie = gm[j] != r["argmax"][j] and near_tie(u[j])
                 if not (near_cut or tie):
                     stats["unexcused"] += 1
@@ -93,6 +100,12 @@ def run_batch_both(dg_ctx, cfg, B, batch=1):
 @pytest.mark.parametrize("cfg,B", [(WIDE, 2), (RAGGED, 3)], ids=["wide_b2", "ragged_b3"])
 def test_batch_loop_parity(dg_ctx, cfg, B):
     s = run_batch_both(dg_ctx, cfg, B)
+    assert s["unexcused"] == 0, s
+    assert s["mismatch"] <= 0.001 * s["positions"], s
+
+
+def test_batch_loop_parity_confidence_rule(dg_ctx):
+    s = run_batch_both(dg_ctx, RAGGED, 2, rule="confidence")
     assert s["unexcused"] == 0, s
     assert s["mismatch"] <= 0.001 * s["positions"], s
 

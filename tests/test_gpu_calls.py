@@ -71,10 +71,15 @@ def test_logits_entropy_and_selfcond(dg_ctx, name):
         tau = O.temperature(k, cfg.N)
         assert np.float32(dg.temperature(k, cfg.N)) == tau
         ent, am = run_head(dg_ctx, cfg, Wd, H, tau, ws)
+        conf = torch.empty(cfg.C, dtype=torch.float32, device=DEV)
+        dg_ctx.confidence(cfg, ws, conf)
         z = torch.empty(cfg.C, cfg.d, dtype=torch.bfloat16, device=DEV)
         dg_ctx.selfcond(cfg, ws, Wd["E"], Wd["W1"], Wd["W2"], z)
         dg_ctx.sync()
         ent_r, am_r, p_r, u_r = O.logits_entropy(H, W["E"], tau)
+        # confidence = largest probability; fp32 statistics vs float64: 2e-5 relative
+        conf_r = p_r.max(axis=1)
+        np.testing.assert_allclose(conf.cpu().numpy(), conf_r, rtol=2e-5, atol=0)
         e = ent.cpu().numpy()
         assert np.all(np.isfinite(e))
         assert np.max(np.abs(e - ent_r)) <= 1e-3, (k, np.max(np.abs(e - ent_r)))
@@ -150,6 +155,40 @@ def test_entropy_accept_bit_exact(dg_ctx, b):
         acc_r, n_r = O.entropy_accept(h, b)
         np.testing.assert_array_equal(acc.cpu().numpy(), acc_r)
         np.testing.assert_array_equal(n.cpu().numpy(), n_r)
+
+
+def _topk_cases():
+    rng = np.random.default_rng(77)
+    cases = []
+    for B, C in ((1, 16), (3, 100), (2, 256), (1, 257), (2, 1000), (1, 1024)):
+        # few distinct values (many ties), NaNs and signed zeros
+        s = rng.choice(np.array([0.05, 0.2, 0.2, 0.5, 0.9], np.float32), size=(B, C))
+        s[rng.random((B, C)) < 0.05] = np.nan
+        s[rng.random((B, C)) < 0.03] = -0.0
+        s[rng.random((B, C)) < 0.03] = 0.0
+        cases.append(s.astype(np.float32))
+        cases.append(rng.random((B, C)).astype(np.float32))
+    return cases
+
+
+def test_topk_accept_bit_exact(dg_ctx):
+    for s in _topk_cases():
+        B, C = s.shape
+        for k in sorted({0, 1, C // 3, C - 1, C, C + 5}):
+            acc = torch.full((B, C), 7, dtype=torch.uint8, device=DEV)
+            n = torch.empty(B, dtype=torch.int32, device=DEV)
+            dg_ctx.topk_accept(f32_dev(s), k, acc, n)
+            acc_r, n_r = O.topk_accept(s, k)
+            np.testing.assert_array_equal(acc.cpu().numpy(), acc_r)
+            np.testing.assert_array_equal(n.cpu().numpy(), n_r)
+
+
+def test_topk_accept_rejects_negative_k(dg_ctx):
+    s = f32_dev(np.zeros((1, 8), np.float32))
+    acc = torch.empty(1, 8, dtype=torch.uint8, device=DEV)
+    n = torch.empty(1, dtype=torch.int32, device=DEV)
+    with pytest.raises(dg.DGError):
+        dg_ctx.topk_accept(s, -1, acc, n)
 
 
 @pytest.mark.parametrize("V", [2, 3, 512, 5000, 262144, 2 ** 31 - 1])

@@ -6,7 +6,8 @@ excused only where the two sides' acceptance differs at a position whose oracle 
 lies within 1e-4 of the cutoff (the entropy of the last accepted or first rejected
 position), or where the argmax differs at a near-tie of the oracle's logits. Entropies
 stay within 1e-3 nats, A and z within 2e-2 max relative error at every step, and the
-stop flags are identical.
+stop flags are identical. Under the confidence rule the accepted counts are equal and
+the cutoff excuse is a confidence within 2e-5 (relative) of the cutoff confidence.
 """
 import numpy as np
 import pytest
@@ -34,13 +35,24 @@ def cutoff_entropy(ent, acc):
     return cands
 
 
-def run_both(dg_ctx, cfg, n_canvas=1):
+def cutoff_confidence(conf, acc):
+    order = sorted(range(len(conf)), key=lambda i: (-float(conf[i]), i))
+    n = int(acc.sum())
+    cands = []
+    if n > 0:
+        cands.append(float(conf[order[n - 1]]))
+    if n < len(conf):
+        cands.append(float(conf[order[n]]))
+    return cands
+
+
+def run_both(dg_ctx, cfg, n_canvas=1, rule="entropy"):
     W = di.weights(cfg)
     Pcap = -(-(cfg.P0 + cfg.C * n_canvas) // 8) * 8
     Kp, Vp = di.prefix_kv(cfg, Pcap)
     Wd = upload_weights(W)
     Kd, Vtd = upload_cache(Kp, Vp, Pcap)
-    loop = CanvasLoop(dg_ctx, cfg, Wd, Kd, Vtd, cfg.P0, N=cfg.N, seed=cfg.seed)
+    loop = CanvasLoop(dg_ctx, cfg, Wd, Kd, Vtd, cfg.P0, N=cfg.N, seed=cfg.seed, rule=rule)
     P_o = cfg.P0
     stats = {"positions": 0, "mismatch": 0, "unexcused": 0}
     for c in range(n_canvas):
@@ -59,19 +71,30 @@ def run_both(dg_ctx, cfg, n_canvas=1):
 
         loop.run_canvas(c, lambda k: Hd[k], on_step=on_step)
         P_o, recs = O.run_canvas(W, Kp, Vp, P_o, lambda k: Hs[k], V=cfg.V, C=cfg.C, Hq=cfg.Hq,
-                                 Hkv=cfg.Hkv, hd=cfg.hd, N=cfg.N, seed=cfg.seed, canvas=c)
+                                 Hkv=cfg.Hkv, hd=cfg.hd, N=cfg.N, seed=cfg.seed, canvas=c,
+                                 rule=rule)
         assert [r["flag"] for r in rec] == [r["flag"] for r in recs]
         for g, r in zip(rec, recs):
             assert np.max(np.abs(g["entropy"] - r["entropy"])) <= 1e-3
             assert maxrel(O.from_bf16(g["A"]), O.from_bf16(r["A"])) <= 2e-2
             assert maxrel(O.from_bf16(g["z"]), O.from_bf16(r["z"])) <= 2e-2
             _, _, _, u = O.logits_entropy(Hs[r["k"]], W["E"], r["tau"])
-            cut = cutoff_entropy(r["entropy"], r["accept"])
+            if rule == "confidence":
+                # the accepted count is the schedule's on both sides (no NaN here)
+                assert int(g["accept"].sum()) == int(r["accept"].sum())
+                cut = cutoff_confidence(r["conf"], r["accept"])
+            else:
+                cut = cutoff_entropy(r["entropy"], r["accept"])
             mism = np.nonzero(g["tokens"] != r["tokens"])[0]
             stats["positions"] += cfg.C
             stats["mismatch"] += len(mism)
             for i in mism:
-                near_cut = g["accept"][i] != r["accept"][i] and any(abs(float(r["entropy"][i]) - x) <= 1e-4 for x in cut)
+                if rule == "confidence":   # fp32 statistics: 2e-5 relative
+                    near_cut = g["accept"][i] != r["accept"][i] and any(
+                        abs(float(r["conf"][i]) - x) <= 2e-5 * x for x in cut)
+                else:
+                    near_cut = g["accept"][i] != r["accept"][i] and any(
+                        abs(float(r["entropy"][i]) - x) <= 1e-4 for x in cut)
                 tie = g["argmax"][i] != r["argmax"][i] and near_tie(u[i])
                 if not (near_cut or tie):
                     stats["unexcused"] += 1
@@ -88,5 +111,12 @@ def run_both(dg_ctx, cfg, n_canvas=1):
                          ids=["tiny", "ragged", "small"])
 def test_loop_parity(dg_ctx, cfg, n_canvas):
     s = run_both(dg_ctx, cfg, n_canvas)
+    assert s["unexcused"] == 0, s
+    assert s["mismatch"] <= 0.001 * s["positions"], s
+
+
+@pytest.mark.parametrize("cfg,n_canvas", [(di.config(0), 2), (RAGGED, 1)], ids=["tiny", "ragged"])
+def test_loop_parity_confidence_rule(dg_ctx, cfg, n_canvas):
+    s = run_both(dg_ctx, cfg, n_canvas, rule="confidence")
     assert s["unexcused"] == 0, s
     assert s["mismatch"] <= 0.001 * s["positions"], s
