@@ -228,6 +228,7 @@ def main():
     del Kd, Vtd, loop
     if not args.no_batched:
         result["batched"] = [batched_canvases(ctx, cfg, Wd, Hd, B) for B in (2, 4)]
+        result["confidence_rule"] = confidence_rule(ctx, cfg, Wd, Hd)
     del Hd
     if not args.no_chain:
         result["chain8"] = chain(ctx)
@@ -329,6 +330,32 @@ def batched_canvases(ctx, cfg, Wd, Hd, B):
             "logits_ms_per_launch": round(logits_ms, 4),
             "logits_mfma_frac": round(flops / (logits_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "prefix_tokens_per_request": cfg.P0}
+
+
+def confidence_rule(ctx, cfg, Wd, Hd):
+    """The step loop with confidence-ranked acceptance instead of the entropy budget:
+    one warm-up canvas, then one timed canvas (init to commit) at the same workload."""
+    import torch
+
+    import dg_inputs as di
+    from block_ar_canvas_amd.loop import CanvasLoop
+    dev = Hd[0].device
+    Pcap = -(-(cfg.P0 + 2 * cfg.C) // 8) * 8
+    Kp, Vp = di.prefix_kv(cfg, Pcap)
+    loop = CanvasLoop(ctx, cfg, Wd, _bf(Kp, dev), _bf(np.ascontiguousarray(Vp.transpose(0, 2, 1)), dev),
+                      cfg.P0, N=cfg.N, seed=cfg.seed, rule="confidence")
+    del Kp, Vp
+    loop.run_canvas(0, lambda k: Hd[0][k])
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    steps = loop.run_canvas(1, lambda k: Hd[1 % len(Hd)][k])
+    e1.record(stream)
+    e1.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3
+    return {"rule": "confidence", "steps": steps, "ms_per_step": round(1e3 * sec / steps, 4),
+            "canvas_tokens_per_s": round(cfg.C / sec, 1)}
 
 
 def chain(ctx):
