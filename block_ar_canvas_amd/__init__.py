@@ -75,6 +75,7 @@ def _load():
         "dg_confidence": (i32, [_P, D, _P, _P]),
         "dg_topk_accept": (i32, [_P, i32, i32, _P, i32, _P, _P]),
         "dg_reveal_count": (i32, [i32, i32, i32]),
+        "dg_sample": (i32, [_P, D, _P, i32, u64, u32, u32, _P]),
         "dg_renoise": (i32, [_P, i32, i32, i32, _P, _P, u64, u32, u32, _P]),
         "dg_selfcond": (i32, [_P, D, _P, _P, _P, _P, _P]),
         "dg_stop_test": (i32, [_P, i32, i32, _P, _P, _P, f32, i32, i32, _P]),
@@ -211,6 +212,12 @@ class Context:
         self._check(self._lib.dg_topk_accept(
             self._h, B, C, _ptr(score, _F32, "score"), int(k), _ptr(accept, _U8, "accept"),
             _ptr(n_accept, _I32, "n_accept")))
+
+    def sample(self, dims, ws, B, seed, canvas_base, step, tokens):
+        d = Dims.of(dims)
+        self._check(self._lib.dg_sample(self._h, ctypes.byref(d), _ptr(ws, _U8, "ws"), int(B),
+                                        int(seed), int(canvas_base), int(step),
+                                        _ptr(tokens, _I32, "tokens")))
 
     def renoise(self, V, argmax, accept, seed, canvas_base, step, tokens):
         B, C = (1, tokens.shape[0]) if tokens.dim() == 1 else tuple(tokens.shape)

@@ -317,6 +317,38 @@ dg_status dg_topk_accept(dg_ctx ctx, int32_t B, int32_t C, const float *score, i
   return e == hipSuccess ? DG_OK : hip_fail(ctx, e, "dg_topk_accept");
 }
 
+dg_status dg_sample(dg_ctx ctx, const dg_dims *dims, const void *ws, int32_t B, uint64_t seed,
+                    uint32_t canvas_base, uint32_t step, int32_t *tokens) {
+  if (!ctx) return DG_ERR_NULL;
+  dg_status st = check_dims(ctx, dims, __func__);
+  if (st) return st;
+  DG_REQUIRE_PTR(ws);
+  DG_REQUIRE_PTR(tokens);
+  const dg_dims &m = *dims;
+  if (B < 1 || m.C % B != 0)
+    return fail(ctx, DG_ERR_SHAPE, "%s: B=%d must divide C=%d", __func__, (int)B, (int)m.C);
+  if (!ctx->p0_valid || ctx->p0_ws != ws || memcmp(&ctx->p0_dims, &m, sizeof m) != 0)
+    return fail(ctx, DG_ERR_STATE, "%s: ws does not hold p0 of a dg_logits_entropy with these dims", __func__);
+  const DgWs w = dg_ws_layout(m.V, m.d, m.C, m.Hq, m.Hkv, m.hd, m.F, 0);
+  void *wsm = const_cast<void *>(ws);
+  SampleArgs a{};
+  a.ptilde = ws_at<u16>(wsm, w.ptilde);
+  a.tsum = ws_at<float>(wsm, w.tsum);
+  a.trho = ws_at<float>(wsm, w.trho);
+  a.colR = ws_at<float>(wsm, w.colR);
+  a.T = w.T;
+  a.VS = w.Vpad / 16;
+  a.V = m.V;
+  a.B = B;
+  a.Cs = m.C / B;
+  a.seed = seed;
+  a.canvas_base = canvas_base;
+  a.step = step;
+  a.tokens = tokens;
+  hipError_t e = dg_launch_sample(a, ctx->stream);
+  return e == hipSuccess ? DG_OK : hip_fail(ctx, e, "dg_sample");
+}
+
 int32_t dg_reveal_count(int32_t C, int32_t N, int32_t step) {
   if (C < 0 || N < 1 || step < 0) return -1;
   if (step >= N) step = N - 1;

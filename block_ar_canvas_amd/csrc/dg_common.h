@@ -278,6 +278,16 @@ hipError_t dg_launch_accept(int B, int C, const float *ent, uint64_t budget, uin
                             int *nacc, hipStream_t st);
 hipError_t dg_launch_topk(int B, int C, const float *score, int k, uint8_t *acc, int *nacc,
                           hipStream_t st);
+struct SampleArgs {
+  const u16 *ptilde;   // p~ in MFMA fragment order (see DgWs)
+  const float *tsum, *trho, *colR;
+  int T, VS, V;        // tiles, Vpad / 16, vocabulary
+  int B, Cs;           // canvases and positions per canvas (columns = B * Cs)
+  uint64_t seed;
+  uint32_t canvas_base, step;
+  int *tokens;         // [B * Cs]
+};
+hipError_t dg_launch_sample(const SampleArgs &a, hipStream_t st);
 hipError_t dg_launch_confidence(int C, const float *colP, float *conf, hipStream_t st);
 hipError_t dg_launch_renoise(int B, int C, int V, const int *am, const uint8_t *acc,
                              uint64_t seed, uint32_t canvas_base, uint32_t step, int *tok,

@@ -28,6 +28,19 @@
 // the k positions the model is most confident about. Same rank construction as the
 // entropy rule: distinct 64-bit keys (score order, position), rank = keys below one's
 // own, accepted iff rank < k.
+//
+// Sampled tokens (same openai-hub step: real samplers draw with temperature and Gumbel
+// noise instead of taking the argmax): x~ ~ p0 in two stages that together are an exact
+// draw from p0. (1) Pick the 256-id vocabulary chunk t (a logits tile) with probability
+// proportional to its mass M_t = Z_t 2^(rho_t - R), from the tile statistics (float32
+// sums, prefix in float64), by inverse CDF: the first t whose running mass exceeds u1
+// times the total, u1 = (word 0 of counter (position, step, 2, 0)) / 2^64 on 53 bits.
+// (2) Inside the chunk, Gumbel-max over ln p~_v + G_v, G_v = -ln(-ln U_v), U_v = (h +
+// 1/2) / 2^32 with h the 32-bit half v mod 2 of word (v mod 8) / 2 of counter
+// (position, step, 3, v / 8); p~ is the stored bf16 2^(x - rho_t), whose common scale in
+// the chunk does not move the argmax.
+#include <float.h>
+
 #include "dg_common.h"
 
 namespace {
@@ -153,6 +166,95 @@ __global__ __launch_bounds__(256) void renoise_kernel(int B, int C, int V, const
   tok[i] = (int)__umul64hi(c[0], (uint64_t)V);
 }
 
+// One workgroup per canvas column (canvas b = column / Cs, position = column % Cs).
+__global__ __launch_bounds__(256) void sample_kernel(SampleArgs a) {
+  __shared__ double sloc[256];
+  __shared__ double sbest[4];
+  __shared__ int sidx[4];
+  __shared__ int st_star;
+  const int c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = c / a.Cs, pos = c % a.Cs;
+  const uint64_t key1 = (uint64_t)(a.canvas_base + (uint32_t)b);
+  const float R = a.colR[c];
+  if (!(fabsf(R) <= FLT_MAX)) {                       // non-finite logits (status already set)
+    if (tid == 0) a.tokens[c] = 0;
+    return;
+  }
+  const float *tz = a.tsum + (int64_t)c * a.T;
+  const float *tr = a.trho + (int64_t)c * a.T;
+  auto mass = [&](int t) { return (double)tz[t] * ldexp(1.0, (int)(tr[t] - R)); };
+
+  // (1) the chunk: thread tid owns tiles [t0, t1); masses summed in tile order
+  const int per = (a.T + 255) / 256;
+  const int t0 = min(tid * per, a.T), t1 = min(t0 + per, a.T);
+  double loc = 0.0;
+  for (int t = t0; t < t1; ++t) loc += mass(t);
+  sloc[tid] = loc;
+  if (tid == 0) st_star = -1;
+  __syncthreads();
+  if (tid == 0) {                                    // exclusive prefix, fixed order
+    double run = 0.0;
+    for (int i = 0; i < 256; ++i) {
+      const double x = sloc[i];
+      sloc[i] = run;
+      run += x;
+    }
+    sbest[0] = run;
+  }
+  __syncthreads();
+  uint64_t w[4] = {(uint64_t)pos, (uint64_t)a.step, 2ull, 0ull};
+  philox4x64_10(w, a.seed, key1);
+  const double u1 = (double)(w[0] >> 11) * 0x1.0p-53;
+  const double target = u1 * sbest[0];
+  const double excl = sloc[tid];
+  if (t0 < t1 && excl <= target && excl + loc > target) {
+    double run = excl;
+    int t = t0;
+    for (; t < t1 - 1; ++t) {
+      run += mass(t);
+      if (run > target) break;
+    }
+    st_star = t;                                     // exactly one thread crosses
+  }
+  __syncthreads();
+  int ts = st_star;
+  if (ts < 0) {                                      // rounding left target >= total:
+    ts = a.T - 1;                                    // the last tile with mass
+    while (ts > 0 && !(mass(ts) > 0.0)) --ts;
+  }
+
+  // (2) Gumbel-max over the chunk's ids
+  const int v = ts * 256 + tid;
+  double score = -INFINITY;
+  if (v < a.V) {
+    const int64_t off = (((int64_t)(c >> 5) * a.VS + (v >> 4)) * 64 + ((v & 15) >> 3) * 32 + (c & 31)) * 8 + (v & 7);
+    const float pv = __uint_as_float((uint32_t)a.ptilde[off] << 16);
+    if (pv > 0.f) {
+      uint64_t g[4] = {(uint64_t)pos, (uint64_t)a.step, 3ull, (uint64_t)(v >> 3)};
+      philox4x64_10(g, a.seed, key1);
+      const uint64_t word = g[(v & 7) >> 1];
+      const uint32_t h = (v & 1) ? (uint32_t)(word >> 32) : (uint32_t)word;
+      const double U = ((double)h + 0.5) * 0x1.0p-32;
+      score = log((double)pv) - log(-log(U));
+    }
+  }
+  int bi = v;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const double s2 = __shfl_xor(score, o);
+    const int i2 = __shfl_xor(bi, o);
+    if (s2 > score || (s2 == score && i2 < bi)) { score = s2; bi = i2; }
+  }
+  __syncthreads();
+  if (lane == 0) { sbest[wave] = score; sidx[wave] = bi; }
+  __syncthreads();
+  if (tid == 0) {
+    for (int i = 1; i < 4; ++i)
+      if (sbest[i] > score || (sbest[i] == score && sidx[i] < bi)) { score = sbest[i]; bi = sidx[i]; }
+    a.tokens[c] = bi;
+  }
+}
+
 __global__ __launch_bounds__(256) void stop_kernel(int C, const float *ent, const int *am,
                                                    const int *prev, uint64_t limit, int step,
                                                    int N, int *flag) {
@@ -205,6 +307,11 @@ hipError_t dg_launch_topk(int B, int C, const float *score, int k, uint8_t *acc,
   const int tpp = C <= 256 ? 4 : C <= 512 ? 2 : 1;
   const int n = (C * tpp + 63) / 64 * 64;
   hipLaunchKernelGGL(topk_kernel, dim3(B), dim3(n), 0, st, C, tpp, score, k, acc, nacc);
+  return hipGetLastError();
+}
+
+hipError_t dg_launch_sample(const SampleArgs &a, hipStream_t st) {
+  hipLaunchKernelGGL(sample_kernel, dim3(a.B * a.Cs), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -19,6 +19,7 @@ import torch
 from . import STOP_GO, Context, Dims, reveal_count, temperature, workspace_bytes
 
 RULES = ("entropy", "confidence")
+DRAWS = ("argmax", "sample")
 
 
 class CanvasLoop:
@@ -28,14 +29,16 @@ class CanvasLoop:
     Kp [Hkv, Pcap, hd] and Vt [Hkv, hd, Pcap] bf16 device tensors: the KV cache.
     rule: "entropy" (entropy-bounded acceptance with budget b) or "confidence" (the
     reveal_count(C, N, k) most confident positions of step k are accepted).
+    draw: "argmax" (accepted positions and the commit take x0 = argmax) or "sample"
+    (they take x~ ~ p0 drawn by dg_sample); the stop test compares argmaxes either way.
     """
 
     def __init__(self, ctx: Context, dims, weights, Kp, Vt, P: int, *, N: int, seed: int,
                  b: float = 0.1, thr: float = 0.005, tau0: float = 0.8, tau1: float = 0.4,
-                 rule: str = "entropy"):
-        if rule not in RULES:
-            raise ValueError(f"rule must be one of {RULES}")
-        self.rule = rule
+                 rule: str = "entropy", draw: str = "argmax"):
+        if rule not in RULES or draw not in DRAWS:
+            raise ValueError(f"rule must be one of {RULES}, draw one of {DRAWS}")
+        self.rule, self.draw = rule, draw
         self.ctx, self.dims = ctx, Dims.of(dims)
         self.W, self.Kp, self.Vt, self.P = weights, Kp, Vt, int(P)
         self.N, self.seed, self.b, self.thr, self.tau0, self.tau1 = N, seed, b, thr, tau0, tau1
@@ -48,6 +51,7 @@ class CanvasLoop:
         self.entropy = torch.empty(C, dtype=torch.float32, device=dev)
         self.conf = torch.empty(C, dtype=torch.float32, device=dev)
         self.argmax = [torch.empty(C, dtype=torch.int32, device=dev) for _ in range(2)]
+        self.sampled = [torch.empty(C, dtype=torch.int32, device=dev) for _ in range(2)]
         self.accept = torch.empty(C, dtype=torch.uint8, device=dev)
         self.n_accept = torch.empty(1, dtype=torch.int32, device=dev)
         # Stop flags live in pinned host memory; the stop kernel writes them with
@@ -86,12 +90,16 @@ class CanvasLoop:
             e1 = torch.cuda.Event(enable_timing=True)
             e1.record(self.ctx._stream)
             ev.append((e0, e1))
+        x0 = am
+        if self.draw == "sample":
+            x0 = self.sampled[k & 1]
+            self.ctx.sample(dm, self.ws, 1, self.seed, self.canvas, k, x0)
         if self.rule == "confidence":
             self.ctx.confidence(dm, self.ws, self.conf)
             self.ctx.topk_accept(self.conf, reveal_count(dm.C, self.N, k), self.accept, self.n_accept)
         else:
             self.ctx.entropy_accept(self.entropy, self.b, self.accept, self.n_accept)
-        self.ctx.renoise(dm.V, am, self.accept, self.seed, self.canvas, k, self.tokens)
+        self.ctx.renoise(dm.V, x0, self.accept, self.seed, self.canvas, k, self.tokens)
         self.ctx.selfcond(dm, self.ws, W["E"], W["W1"], W["W2"], self.z)
         slot = self._seq % len(self.flags)
         self._seq += 1
@@ -144,8 +152,12 @@ class CanvasLoop:
             k += 1
             if on_step is not None:
                 on_step(k, self)
-        self.commit(self.argmax[k & 1])
+        self.commit(self.final_tokens(k))
         return k + 1
+
+    def final_tokens(self, k: int):
+        """The block step k commits: its argmax, or its sampled tokens under draw="sample"."""
+        return (self.sampled if self.draw == "sample" else self.argmax)[k & 1]
 
 
 class BatchLoop:
@@ -166,10 +178,10 @@ class BatchLoop:
 
     def __init__(self, ctx: Context, dims, weights, caches, *, N: int, seed: int,
                  b: float = 0.1, thr: float = 0.005, tau0: float = 0.8, tau1: float = 0.4,
-                 rule: str = "entropy"):
-        if rule not in RULES:
-            raise ValueError(f"rule must be one of {RULES}")
-        self.rule = rule
+                 rule: str = "entropy", draw: str = "argmax"):
+        if rule not in RULES or draw not in DRAWS:
+            raise ValueError(f"rule must be one of {RULES}, draw one of {DRAWS}")
+        self.rule, self.draw = rule, draw
         self.ctx, self.W = ctx, weights
         self.B = len(caches)
         self.dims = Dims.of(dims)                       # one canvas
@@ -191,6 +203,7 @@ class BatchLoop:
         self.entropy = torch.empty(B, C, dtype=torch.float32, device=dev)
         self.conf = torch.empty(B, C, dtype=torch.float32, device=dev)
         self.argmax = [torch.empty(B, C, dtype=torch.int32, device=dev) for _ in range(2)]
+        self.sampled = [torch.empty(B, C, dtype=torch.int32, device=dev) for _ in range(2)]
         self.accept = torch.empty(B, C, dtype=torch.uint8, device=dev)
         self.n_accept = torch.empty(B, dtype=torch.int32, device=dev)
         # Same protocol as CanvasLoop: pinned flags written by the stop kernel, four
@@ -227,12 +240,16 @@ class BatchLoop:
             e1 = torch.cuda.Event(enable_timing=True)
             e1.record(self.ctx._stream)
             ev.append((e0, e1))
+        x0 = am
+        if self.draw == "sample":
+            x0 = self.sampled[k & 1]
+            self.ctx.sample(self.dims_all, self.ws, self.B, self.seed, self.batch * self.B, k, x0.view(-1))
         if self.rule == "confidence":
             self.ctx.confidence(self.dims_all, self.ws, self.conf.view(-1))
             self.ctx.topk_accept(self.conf, reveal_count(dm.C, self.N, k), self.accept, self.n_accept)
         else:
             self.ctx.entropy_accept(self.entropy, self.b, self.accept, self.n_accept)
-        self.ctx.renoise(dm.V, am, self.accept, self.seed, self.batch * self.B, k, self.tokens)
+        self.ctx.renoise(dm.V, x0, self.accept, self.seed, self.batch * self.B, k, self.tokens)
         self.ctx.selfcond(self.dims_all, self.ws, W["E"], W["W1"], W["W2"], self.z.view(-1, dm.d))
         slot = self._seq % len(self.flags)
         self._seq += 1
@@ -276,7 +293,7 @@ class BatchLoop:
             flags = self.wait_flags(k)
             for i in range(B):
                 if x0[i] is None and flags[i] != STOP_GO:
-                    x0[i] = self.argmax[k & 1][i].clone()
+                    x0[i] = (self.sampled if self.draw == "sample" else self.argmax)[k & 1][i].clone()
                     steps[i] = k + 1
             if all(x is not None for x in x0):
                 break

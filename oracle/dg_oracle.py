@@ -42,6 +42,10 @@ Readings taken where the pages leave a step open (each restated where it is used
     previous step; otherwise the step cap N - 1 commits anyway;
   * commit: the finalized block is x^0 = argmax at the stopping step; its K/V rows are
     E[x^0] Wk^T and E[x^0] Wv^T (stand-in for the causal re-encode), appended at [P, P+C).
+  * sampled tokens (an alternative to x^0 = argmax): x~ ~ p^0 drawn in two stages, a
+    256-id vocabulary chunk by inverse CDF over chunk masses with one Philox uniform,
+    then Gumbel-max inside the chunk with Philox-driven Gumbel noise; accepted positions
+    and the commit take x~, the stop test still compares argmaxes;
   * the confidence rule (an alternative to the entropy budget): a position's confidence
     is its largest tempered probability; step k accepts the n_k most confident positions
     (ties to the lower position, NaN never), n_k the number the [HUB] decoder has revealed
@@ -301,6 +305,8 @@ def philox4x64_10(counter, key):
 
 
 STREAM_RENOISE, STREAM_INIT = 0, 1
+STREAM_CHUNK, STREAM_GUMBEL = 2, 3
+SAMPLE_CHUNK = 256          # vocabulary ids per chunk of the two-stage draw
 
 
 def uniform_token(seed, canvas, step, stream, pos, V) -> int:
@@ -334,6 +340,65 @@ def renoise(argmax, accept, seed, canvas_base, step, V):
                 out[s, i] = am[s, i]
             else:
                 out[s, i] = uniform_token(seed, canvas_base + s, step, stream, i, V)
+    return out
+
+
+# ------------------------------------------------------------------ sampled tokens
+def gumbel_noise(seed, canvas, step, pos, v) -> float:
+    """G_v = -ln(-ln U), U = (h + 1/2) / 2^32, h the 32-bit half v mod 2 (0 = low) of word
+    (v mod 8) / 2 of Philox4x64-10 with counter (pos, step, 3, v / 8), key (seed, canvas)."""
+    w = philox4x64_10((pos, step, STREAM_GUMBEL, v // 8), (seed, canvas))[(v % 8) // 2]
+    h = (w >> 32) if (v % 2) else (w & 0xFFFFFFFF)
+    return -math.log(-math.log((h + 0.5) / 4294967296.0))
+
+
+def sample_tokens(p, seed, canvas_base, step, B=1, with_margins=False, positions=None):
+    """Sampled tokens x~ ~ p^0, the sampled-token alternative to x^0 = argmax.
+
+    [HUB] step 4 notes that real samplers draw with temperature and Gumbel noise instead
+    of always taking the most likely token. The draw (an exact sample from p):
+      1. split the vocabulary into chunks of 256 consecutive ids and pick the first chunk
+         whose running probability mass exceeds u1 = (Philox word 0 of counter
+         (pos, step, 2, 0) >> 11) / 2^53 (inverse CDF over the chunk masses);
+      2. inside the chunk take argmax_v ln p_v + G_v (Gumbel-max, ties to the lower id).
+    p float64 [B * Cs, V] (rows = canvas b position i at b * Cs + i); canvas id =
+    canvas_base + b. Returns int32 tokens; with_margins also returns, per row, the
+    distance of u1 to the nearest chunk boundary of the cumulative mass and the gap
+    between the best and second-best Gumbel score inside the chosen chunk. ``positions``
+    (B = 1 only) gives the canvas position of each row when p holds a subset of rows.
+    """
+    p = np.asarray(p, dtype=np.float64)
+    rows, V = p.shape
+    Cs = rows // B
+    nch = -(-V // SAMPLE_CHUNK)
+    out = np.zeros(rows, dtype=np.int32)
+    m_chunk = np.zeros(rows)
+    m_gap = np.zeros(rows)
+    for r in range(rows):
+        b, i = divmod(r, Cs)
+        if positions is not None:
+            b, i = 0, int(positions[r])
+        canvas = canvas_base + b
+        w = philox4x64_10((i, step, STREAM_CHUNK, 0), (seed, canvas))[0]
+        u1 = (w >> 11) * 2.0 ** -53
+        masses = np.array([p[r, t * SAMPLE_CHUNK:(t + 1) * SAMPLE_CHUNK].sum() for t in range(nch)])
+        cum = np.cumsum(masses)
+        t = int(np.searchsorted(cum, u1 * cum[-1], side="right"))
+        t = min(t, nch - 1)
+        lo = cum[t - 1] if t > 0 else 0.0
+        m_chunk[r] = min(abs(u1 * cum[-1] - lo), abs(cum[t] - u1 * cum[-1])) / cum[-1]
+        ids = range(t * SAMPLE_CHUNK, min(V, (t + 1) * SAMPLE_CHUNK))
+        scores = []
+        for v in ids:
+            pv = p[r, v]
+            scores.append(-math.inf if pv <= 0.0 else math.log(pv) + gumbel_noise(seed, canvas, step, i, v))
+        sc = np.array(scores)
+        j = int(np.argmax(sc))                     # first maximum = lower id
+        out[r] = t * SAMPLE_CHUNK + j
+        srt = np.sort(sc)
+        m_gap[r] = srt[-1] - srt[-2] if len(srt) > 1 else math.inf
+    if with_margins:
+        return out, m_chunk, m_gap
     return out
 
 
@@ -419,14 +484,15 @@ def commit_kv(tokens, E_bits, Wk, Wv, Kp, Vp, P, Hkv, hd):
 # ------------------------------------------------------------------ the step loop
 def run_canvas(W, Kp, Vp, P, hidden_of_step, *, V, C, Hq, Hkv, hd, N, seed, canvas,
                b=0.1, thr=0.005, tau0=0.8, tau1=0.4, record=True, with_attn=True,
-               rule="entropy"):
+               rule="entropy", draw="argmax"):
     """One canvas of the block-AR loop: init, up to N denoise steps, commit.
 
     [TR] "Method steps" (2)-(5) in order; [TUT] data-flow pseudocode. The sampler head's
     hidden states come from ``hidden_of_step(k)`` (the synthetic driver standing in for
     the denoiser stack); the attention output A_k is computed on the true denoiser input
     X_k = E[x_k] + z_k every step and recorded, but does not feed H_k.
-    rule "confidence" replaces the entropy budget by the confidence rule (module header).
+    rule "confidence" replaces the entropy budget by the confidence rule; draw "sample"
+    gives accepted positions, and the commit, x~ ~ p^0 instead of x^0 (module header).
     Returns (new P, list of per-step records).
     """
     d = W["E"].shape[1]
@@ -445,13 +511,17 @@ def run_canvas(W, Kp, Vp, P, hidden_of_step, *, V, C, Hq, Hkv, hd, N, seed, canv
                                Kp, Vp, P, Hq, Hkv, hd)
             rec["A"] = A
         ent, am, p, _ = logits_entropy(hidden_of_step(k), W["E"], tau)
+        x0 = am
+        if draw == "sample":
+            x0, m_chunk, m_gap = sample_tokens(p, seed, canvas, k, with_margins=True)
+            rec.update(sampled=x0, sample_margin_chunk=m_chunk, sample_margin_gap=m_gap)
         if rule == "confidence":
             conf = p.max(axis=1).astype(np.float32)
             acc, nacc = topk_accept(conf[None], schedule[k])
             rec["conf"] = conf
         else:
             acc, nacc = entropy_accept(ent[None], b)
-        x = renoise(am[None], acc, seed, canvas, k, V)[0]
+        x = renoise(x0[None], acc, seed, canvas, k, V)[0]
         z, _ = selfcond(p, W["E"], W["W1"], W["W2"])
         flag = int(stop_test(ent[None], am[None], None if prev is None else prev[None],
                              thr, k, N)[0])
@@ -462,5 +532,5 @@ def run_canvas(W, Kp, Vp, P, hidden_of_step, *, V, C, Hq, Hkv, hd, N, seed, canv
         prev = am
         if flag != STOP_GO:
             break
-    P = commit_kv(am, W["E"], W["Wk"], W["Wv"], Kp, Vp, P, Hkv, hd)
+    P = commit_kv(x0, W["E"], W["Wk"], W["Wv"], Kp, Vp, P, Hkv, hd)
     return P, recs

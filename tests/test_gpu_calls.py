@@ -88,6 +88,48 @@ def test_logits_entropy_and_selfcond(dg_ctx, name):
         assert maxrel(O.from_bf16(bits_np(z)), O.from_bf16(z_r)) <= 2e-2
 
 
+@pytest.mark.parametrize("name", ["tiny", "small", "ragged", "wide"])
+def test_sample_tokens(dg_ctx, name):
+    """dg_sample against the oracle's two-stage draw. A token may differ only where the
+    oracle's u1 lies within 1e-5 of a chunk boundary of the cumulative mass (float32 tile
+    sums) or where its best two Gumbel scores in the chunk are within 0.02 (the device
+    uses the bf16-stored probabilities)."""
+    cfg, W, Kp, Vp, Pcap, Wd = setup(name)
+    ws = ws_for(cfg, Pcap)
+    tgt = di.targets(cfg, 0)
+    B = 2 if cfg.C % 2 == 0 else 1
+    total = bad = same = 0
+    for k in sorted({0, cfg.N // 2, cfg.N - 1}):
+        H = di.hidden(cfg, W["E"], 0, k, tgt)
+        tau = O.temperature(k, cfg.N)
+        run_head(dg_ctx, cfg, Wd, H, tau, ws)
+        tok = torch.full((cfg.C,), -1, dtype=torch.int32, device=DEV)
+        dg_ctx.sample(cfg, ws, B, 1234 + k, 7, k, tok)
+        dg_ctx.sync()
+        _, _, p_r, _ = O.logits_entropy(H, W["E"], tau)
+        ref, mc, mg = O.sample_tokens(p_r, 1234 + k, 7, k, B=B, with_margins=True)
+        g = tok.cpu().numpy()
+        assert np.all((g >= 0) & (g < cfg.V))
+        for i in np.nonzero(g != ref)[0]:
+            if not (mc[i] <= 1e-5 or mg[i] <= 2e-2):
+                bad += 1
+        total += cfg.C
+        same += int((g == ref).sum())
+    assert bad == 0, (bad, total)
+    assert same >= 0.95 * total, (same, total)     # excuses stay rare
+
+
+def test_sample_rejects_bad_segments_and_stale_ws(dg_ctx):
+    cfg, W, Kp, Vp, Pcap, Wd = setup("ragged")
+    ws = ws_for(cfg, Pcap)
+    tok = torch.empty(cfg.C, dtype=torch.int32, device=DEV)
+    with pytest.raises(dg.DGError):                 # no dg_logits_entropy on this ws yet
+        dg_ctx.sample(cfg, ws, 1, 0, 0, 0, tok)
+    run_head(dg_ctx, cfg, Wd, di.hidden(cfg, W["E"], 0, 0, di.targets(cfg, 0)), 0.8, ws)
+    with pytest.raises(dg.DGError):                 # 3 does not divide C = 100
+        dg_ctx.sample(cfg, ws, 3, 0, 0, 0, tok)
+
+
 @pytest.mark.parametrize("name", list(SHAPES))
 @pytest.mark.parametrize("prefix", ["full", "empty"])
 def test_canvas_attention(dg_ctx, name, prefix):

@@ -50,6 +50,10 @@ def test_sampler_head_and_selfcond_full_vocab(dg_ctx, k):
     dg_ctx.logits_entropy(cfg, bf16_dev(H), Wd["E"], tau, ws, ent, am)
     z = torch.empty(cfg.C, cfg.d, dtype=torch.bfloat16, device=DEV)
     dg_ctx.selfcond(cfg, ws, Wd["E"], Wd["W1"], Wd["W2"], z)
+    conf = torch.empty(cfg.C, dtype=torch.float32, device=DEV)
+    dg_ctx.confidence(cfg, ws, conf)
+    tok = torch.empty(cfg.C, dtype=torch.int32, device=DEV)
+    dg_ctx.sample(cfg, ws, 1, 99, 3, k, tok)
     dg_ctx.sync()
     e = ent.cpu().numpy()
     a = am.cpu().numpy()
@@ -65,6 +69,13 @@ def test_sampler_head_and_selfcond_full_vocab(dg_ctx, k):
     zg = bits_np(z)
     assert np.all(np.isfinite(O.from_bf16(zg)))
     assert maxrel(O.from_bf16(zg[ROWS]), O.from_bf16(z_r)) <= 2e-2
+    # confidence and sampled tokens (same tolerances as the per-call tests)
+    np.testing.assert_allclose(conf.cpu().numpy()[ROWS], p_r.max(axis=1), rtol=2e-5, atol=0)
+    g = tok.cpu().numpy()
+    assert g.min() >= 0 and g.max() < cfg.V
+    ref, mc, mg = O.sample_tokens(p_r, 99, 3, k, with_margins=True, positions=ROWS)
+    for j, i in enumerate(ROWS):
+        assert g[i] == ref[j] or mc[j] <= 1e-5 or mg[j] <= 2e-2, (i, g[i], ref[j], mc[j], mg[j])
 
 
 @pytest.mark.parametrize("name", ["gemma_head", "long_prefix"])
