@@ -228,7 +228,8 @@ def main():
     del Kd, Vtd, loop
     if not args.no_batched:
         result["batched"] = [batched_canvases(ctx, cfg, Wd, Hd, B) for B in (2, 4)]
-        result["confidence_rule"] = confidence_rule(ctx, cfg, Wd, Hd)
+        result["confidence_rule"] = variant_canvas(ctx, cfg, Wd, Hd, rule="confidence")
+        result["sampled_tokens"] = variant_canvas(ctx, cfg, Wd, Hd, draw="sample")
     del Hd
     if not args.no_chain:
         result["chain8"] = chain(ctx)
@@ -332,9 +333,10 @@ def batched_canvases(ctx, cfg, Wd, Hd, B):
             "prefix_tokens_per_request": cfg.P0}
 
 
-def confidence_rule(ctx, cfg, Wd, Hd):
-    """The step loop with confidence-ranked acceptance instead of the entropy budget:
-    one warm-up canvas, then one timed canvas (init to commit) at the same workload."""
+def variant_canvas(ctx, cfg, Wd, Hd, rule="entropy", draw="argmax"):
+    """The step loop with another acceptance rule (confidence-ranked) or sampled tokens
+    instead of the argmax: one warm-up canvas, then one timed canvas (init to commit) at
+    the same workload."""
     import torch
 
     import dg_inputs as di
@@ -343,7 +345,7 @@ def confidence_rule(ctx, cfg, Wd, Hd):
     Pcap = -(-(cfg.P0 + 2 * cfg.C) // 8) * 8
     Kp, Vp = di.prefix_kv(cfg, Pcap)
     loop = CanvasLoop(ctx, cfg, Wd, _bf(Kp, dev), _bf(np.ascontiguousarray(Vp.transpose(0, 2, 1)), dev),
-                      cfg.P0, N=cfg.N, seed=cfg.seed, rule="confidence")
+                      cfg.P0, N=cfg.N, seed=cfg.seed, rule=rule, draw=draw)
     del Kp, Vp
     loop.run_canvas(0, lambda k: Hd[0][k])
     stream = torch.cuda.current_stream()
@@ -354,7 +356,7 @@ def confidence_rule(ctx, cfg, Wd, Hd):
     e1.record(stream)
     e1.synchronize()
     sec = e0.elapsed_time(e1) * 1e-3
-    return {"rule": "confidence", "steps": steps, "ms_per_step": round(1e3 * sec / steps, 4),
+    return {"rule": rule, "draw": draw, "steps": steps, "ms_per_step": round(1e3 * sec / steps, 4),
             "canvas_tokens_per_s": round(cfg.C / sec, 1)}
 
 

@@ -168,7 +168,6 @@ __global__ __launch_bounds__(256) void renoise_kernel(int B, int C, int V, const
 
 // One workgroup per canvas column (canvas b = column / Cs, position = column % Cs).
 __global__ __launch_bounds__(256) void sample_kernel(SampleArgs a) {
-  __shared__ double sloc[256];
   __shared__ double sbest[4];
   __shared__ int sidx[4];
   __shared__ int st_star;
@@ -189,24 +188,27 @@ __global__ __launch_bounds__(256) void sample_kernel(SampleArgs a) {
   const int t0 = min(tid * per, a.T), t1 = min(t0 + per, a.T);
   double loc = 0.0;
   for (int t = t0; t < t1; ++t) loc += mass(t);
-  sloc[tid] = loc;
+  // exclusive prefix of the per-thread sums: a wave scan, then the wave totals in order
+  // (a fixed association, so every run gives the same bits)
+  double incl = loc;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  double ex = __shfl_up(incl, 1);
+  if (lane == 0) ex = 0.0;
+  if (lane == 63) sbest[wave] = incl;
   if (tid == 0) st_star = -1;
   __syncthreads();
-  if (tid == 0) {                                    // exclusive prefix, fixed order
-    double run = 0.0;
-    for (int i = 0; i < 256; ++i) {
-      const double x = sloc[i];
-      sloc[i] = run;
-      run += x;
-    }
-    sbest[0] = run;
-  }
-  __syncthreads();
+  double woff = 0.0;
+  for (int i = 0; i < wave; ++i) woff += sbest[i];
+  const double total = ((sbest[0] + sbest[1]) + sbest[2]) + sbest[3];
   uint64_t w[4] = {(uint64_t)pos, (uint64_t)a.step, 2ull, 0ull};
   philox4x64_10(w, a.seed, key1);
   const double u1 = (double)(w[0] >> 11) * 0x1.0p-53;
-  const double target = u1 * sbest[0];
-  const double excl = sloc[tid];
+  const double target = u1 * total;
+  const double excl = woff + ex;
   if (t0 < t1 && excl <= target && excl + loc > target) {
     double run = excl;
     int t = t0;
