@@ -25,7 +25,9 @@ Sources (web pages on DiffusionGemma):
         generation: predict, select, accept, remask).
   [HUB] openai-hub page "从零拆开DiffusionGemma" (news 2086), step 4 (confidence decoding:
         predict every position, keep the most confident ones, the simplified decoder's
-        reveal count ceil(unresolved / remaining steps)).
+        reveal count ceil(unresolved / remaining steps)); the closing remarks of step 3
+        (the full model adds MoE layers, rotary position encoding, prompt prefill and a KV
+        cache to the teaching model).
 
 Readings taken where the pages leave a step open (each restated where it is used):
   * temperature: tau_k = tau0 + (tau1 - tau0) * k / (N - 1) over the step budget N,
@@ -105,7 +107,24 @@ def temperature(k: int, N: int, tau0: float = 0.8, tau1: float = 0.4) -> np.floa
 
 
 # ------------------------------------------------------------------ (a2-a4) attention
-def canvas_attn(tokens, z_bits, E_bits, Wq, Wk, Wv, Wo, Kp, Vp, P, Hq, Hkv, hd, rows=None):
+def rope(x, positions, base):
+    """Rotary position embedding, half-split pairing: for d < hd/2 the pair
+    (x_d, x_{d+hd/2}) is rotated by the angle pos * base^(-2d/hd). base 0 is the identity.
+    [HUB] names rotary position encoding as part of the full model; the pairing and the
+    base are readings (the Gemma family's convention). x float64 [n, H, hd]."""
+    if not base:
+        return x
+    n, H, hd = x.shape
+    h = hd // 2
+    theta = float(base) ** (-2.0 * np.arange(h) / hd)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * theta[None, :]
+    c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    x1, x2 = x[..., :h], x[..., h:]
+    return np.concatenate([x1 * c - x2 * s, x1 * s + x2 * c], axis=-1)
+
+
+def canvas_attn(tokens, z_bits, E_bits, Wq, Wk, Wv, Wo, Kp, Vp, P, Hq, Hkv, hd, rows=None,
+                rope_base=0.0):
     """Bidirectional canvas attention over the static prefix KV cache, then Wo.
 
     [GGL] "Architecture": in denoise mode a query at any canvas position attends to all
@@ -116,7 +135,8 @@ def canvas_attn(tokens, z_bits, E_bits, Wq, Wk, Wv, Wo, Kp, Vp, P, Hq, Hkv, hd, 
     tokens [C] int; z_bits [C, d] bf16 or None (z = 0); E_bits [V, d]; Wq [Hq*hd, d];
     Wk, Wv [Hkv*hd, d]; Wo [d, Hq*hd]; Kp, Vp [Hkv, >=P, hd] bf16 (logical layout).
     ``rows`` restricts the queries (and the returned A) to those canvas positions; the
-    keys and values still come from every canvas token.
+    keys and values still come from every canvas token. rope_base > 0 rotates the canvas
+    queries and keys at their token positions P + i (the prefix keys are stored rotated).
     Returns (A bits [C or len(rows), d], dict of intermediates as float64).
     """
     tokens = np.asarray(tokens)
@@ -129,6 +149,10 @@ def canvas_attn(tokens, z_bits, E_bits, Wq, Wk, Wv, Wo, Kp, Vp, P, Hq, Hkv, hd, 
     Q = from_bf16(to_bf16(Xq @ from_bf16(Wq).T)).reshape(nq, Hq, hd)
     Kc = from_bf16(to_bf16(X @ from_bf16(Wk).T)).reshape(C, Hkv, hd)
     Vc = from_bf16(to_bf16(X @ from_bf16(Wv).T)).reshape(C, Hkv, hd)
+    if rope_base:
+        qpos = P + (np.arange(C) if rows is None else np.asarray(rows))
+        Q = from_bf16(to_bf16(rope(Q, qpos, rope_base)))
+        Kc = from_bf16(to_bf16(rope(Kc, P + np.arange(C), rope_base)))
     O = np.zeros((nq, Hq, hd))
     scale = 1.0 / math.sqrt(hd)
     for h in range(Hq):
@@ -479,6 +503,49 @@ def commit_kv(tokens, E_bits, Wk, Wv, Kp, Vp, P, Hkv, hd):
     Kp[:, P:P + C] = Kn.transpose(1, 0, 2)
     Vp[:, P:P + C] = Vn.transpose(1, 0, 2)
     return P + C
+
+
+def prefill_block(tokens, E_bits, Wq, Wk, Wv, Wo, Kp, Vp, P, Hq, Hkv, hd, rope_base=0.0):
+    """Causal re-encode of a finalized block, appending its K/V to the cache.
+
+    [TUT] data-flow pseudocode (incremental_prefill of the finalized block into the KV
+    cache) and KV-cache write timing: the output KV comes from the backbone re-encoding
+    the finalized block in causal (prefill) mode, not from the denoiser's states. One
+    attention layer stands in for the backbone: X = E[x], Q/K/V = bf16(X W^T), Q and K
+    rotated at positions P + i (rope_base > 0) and rounded to bf16; block token i attends
+    to the prefix [0, P) and to block tokens j <= i; A = bf16(O Wo^T). The rotated K and V
+    rows are written at [P, P + C) of Kp/Vp (in place).
+    Returns (A bits [C, d], new P = P + C).
+    """
+    tokens = np.asarray(tokens)
+    C = tokens.shape[0]
+    if P + C > Kp.shape[1]:
+        raise ValueError("KV capacity exceeded")
+    X = from_bf16(E_bits[tokens])
+    pos = P + np.arange(C)
+    Q = from_bf16(to_bf16(X @ from_bf16(Wq).T)).reshape(C, Hq, hd)
+    Kb = from_bf16(to_bf16(X @ from_bf16(Wk).T)).reshape(C, Hkv, hd)
+    Vb = from_bf16(to_bf16(X @ from_bf16(Wv).T)).reshape(C, Hkv, hd)
+    if rope_base:
+        Q = from_bf16(to_bf16(rope(Q, pos, rope_base)))
+        Kb = from_bf16(to_bf16(rope(Kb, pos, rope_base)))
+    Kp[:, P:P + C] = to_bf16(Kb).transpose(1, 0, 2)
+    Vp[:, P:P + C] = to_bf16(Vb).transpose(1, 0, 2)
+    O = np.zeros((C, Hq, hd))
+    scale = 1.0 / math.sqrt(hd)
+    causal = np.tril(np.ones((C, C), dtype=bool))
+    for h in range(Hq):
+        g = (h * Hkv) // Hq
+        K = np.concatenate([from_bf16(Kp[g, :P]), Kb[:, g]], axis=0)
+        V = np.concatenate([from_bf16(Vp[g, :P]), Vb[:, g]], axis=0)
+        S = (Q[:, h] @ K.T) * scale
+        S[:, P:][~causal] = -np.inf
+        S = S - S.max(axis=1, keepdims=True)
+        W = np.exp(S)
+        W /= W.sum(axis=1, keepdims=True)
+        O[:, h] = W @ V
+    A = to_bf16(O.reshape(C, Hq * hd) @ from_bf16(Wo).T)
+    return A, P + C
 
 
 # ------------------------------------------------------------------ the step loop
