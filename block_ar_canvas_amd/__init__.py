@@ -76,6 +76,9 @@ def _load():
         "dg_topk_accept": (i32, [_P, i32, i32, _P, i32, _P, _P]),
         "dg_reveal_count": (i32, [i32, i32, i32]),
         "dg_sample": (i32, [_P, D, _P, i32, u64, u32, u32, _P]),
+        "dg_set_rope": (i32, [_P, f32]),
+        "dg_prefill_block": (i32, [_P, D, _P, _P, _P, _P, _P, _P, _P, _P, i64, i64, _P, _P,
+                                   ctypes.POINTER(i64)]),
         "dg_renoise": (i32, [_P, i32, i32, i32, _P, _P, u64, u32, u32, _P]),
         "dg_selfcond": (i32, [_P, D, _P, _P, _P, _P, _P]),
         "dg_stop_test": (i32, [_P, i32, i32, _P, _P, _P, f32, i32, i32, _P]),
@@ -237,6 +240,19 @@ class Context:
             self._h, B, C, _ptr(entropy, _F32, "entropy"), _ptr(argmax, _I32, "argmax"),
             _ptr(prev_argmax, _I32, "prev_argmax", True), float(thr), int(step), int(N),
             _ptr(flag, _I32, "flag", pinned_ok=True)))
+
+    def set_rope(self, base: float):
+        self._check(self._lib.dg_set_rope(self._h, float(base)))
+
+    def prefill_block(self, dims, tokens, E, Wq, Wk, Wv, Wo, Kp, Vt, P, ws, A) -> int:
+        d = Dims.of(dims)
+        out = ctypes.c_int64(0)
+        self._check(self._lib.dg_prefill_block(
+            self._h, ctypes.byref(d), _ptr(tokens, _I32, "tokens"), _ptr(E, _BF16, "E"),
+            _ptr(Wq, _BF16, "Wq"), _ptr(Wk, _BF16, "Wk"), _ptr(Wv, _BF16, "Wv"), _ptr(Wo, _BF16, "Wo"),
+            _ptr(Kp, _BF16, "Kp"), _ptr(Vt, _BF16, "Vt"), int(P), int(Kp.shape[1]),
+            _ptr(ws, _U8, "ws"), _ptr(A, _BF16, "A"), ctypes.byref(out)))
+        return int(out.value)
 
     def commit_kv(self, dims, tokens, E, Wk, Wv, Kp, Vt, P) -> int:
         d = Dims.of(dims)

@@ -20,6 +20,8 @@ struct dg_ctx_s {
   hipStream_t stream = nullptr;
   int *d_status = nullptr;
   char err[512] = {0};
+  // Rotary base for dg_canvas_attn and dg_prefill_block (0: no rotary positions).
+  double rope_base = 0.0;
   // p0 hand-off between dg_logits_entropy and dg_selfcond.
   const void *p0_ws = nullptr;
   dg_dims p0_dims = {0, 0, 0, 0, 0, 0, 0};
@@ -204,6 +206,11 @@ dg_status dg_canvas_attn(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens,
   g.seg[2] = GemmSeg{Wv, kd, vct, 1, 0, w.Cpad, INT_MAX, w.Cpad, 0};
   hipError_t e = dg_launch_gemm(g, ctx->stream);
   if (e != hipSuccess) return hip_fail(ctx, e, "dg_canvas_attn(qkv)");
+  if (ctx->rope_base > 0.0) {                        // canvas token i sits at position P + i
+    e = dg_launch_rope(q, m.C, m.Hq, m.hd, qd, P, ctx->rope_base, ctx->stream);
+    if (e == hipSuccess) e = dg_launch_rope(kc, m.C, m.Hkv, m.hd, kd, P, ctx->rope_base, ctx->stream);
+    if (e != hipSuccess) return hip_fail(ctx, e, "dg_canvas_attn(rope)");
+  }
 
   AttnArgs at{};
   at.Q = q;
@@ -234,6 +241,103 @@ dg_status dg_canvas_attn(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens,
   go.seg[0] = GemmSeg{Wo, m.d, A, m.d, 0, 1, INT_MAX, m.C, 0};
   e = dg_launch_gemm(go, ctx->stream);
   if (e != hipSuccess) return hip_fail(ctx, e, "dg_canvas_attn(wo)");
+  return DG_OK;
+}
+
+dg_status dg_set_rope(dg_ctx ctx, float base) {
+  if (!ctx) return DG_ERR_NULL;
+  if (!(base >= 0.f) || !isfinite(base)) return fail(ctx, DG_ERR_RANGE, "%s: base=%g must be >= 0", __func__, base);
+  ctx->rope_base = (double)base;
+  return DG_OK;
+}
+
+dg_status dg_prefill_block(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens,
+                           const dg_bf16 *E, const dg_bf16 *Wq, const dg_bf16 *Wk,
+                           const dg_bf16 *Wv, const dg_bf16 *Wo, dg_bf16 *Kp, dg_bf16 *Vt,
+                           int64_t P, int64_t Pcap, void *ws, dg_bf16 *A, int64_t *P_out) {
+  if (!ctx) return DG_ERR_NULL;
+  dg_status st = check_dims(ctx, dims, __func__);
+  if (st) return st;
+  if ((st = check_cache(ctx, P, Pcap, __func__))) return st;
+  if ((int64_t)dims->Hkv * dims->hd * Pcap * 2 > (int64_t)UINT32_MAX)
+    return fail(ctx, DG_ERR_SHAPE, "%s: Hkv*hd*Pcap*2 = %lld bytes exceeds 4 GiB", __func__,
+                (long long)dims->Hkv * dims->hd * Pcap * 2);
+  DG_REQUIRE_PTR(tokens);
+  DG_REQUIRE_PTR(E);
+  DG_REQUIRE_PTR(Wq);
+  DG_REQUIRE_PTR(Wk);
+  DG_REQUIRE_PTR(Wv);
+  DG_REQUIRE_PTR(Wo);
+  DG_REQUIRE_PTR(Kp);
+  DG_REQUIRE_PTR(Vt);
+  DG_REQUIRE_PTR(ws);
+  DG_REQUIRE_PTR(A);
+  DG_REQUIRE_PTR(P_out);
+  const dg_dims &m = *dims;
+  if (P + m.C > Pcap)
+    return fail(ctx, DG_ERR_CAPACITY, "%s: P + C = %lld exceeds Pcap = %lld", __func__,
+                (long long)(P + m.C), (long long)Pcap);
+  const DgWs w = dg_ws_layout(m.V, m.d, m.C, m.Hq, m.Hkv, m.hd, m.F, Pcap);
+  const int qd = m.Hq * m.hd, kd = m.Hkv * m.hd;
+  u16 *q = ws_at<u16>(ws, w.q), *kc = ws_at<u16>(ws, w.kc), *vct = ws_at<u16>(ws, w.vct);
+  u16 *o = ws_at<u16>(ws, w.o);
+
+  // Q, K, V of the block X = E[tokens], rotated to positions P + i.
+  GemmArgs g{};
+  g.M = m.C;
+  g.K = m.d;
+  g.V = m.V;
+  g.status = ctx->d_status;
+  g.tokens = tokens;
+  g.E = E;
+  g.nseg = 3;
+  g.seg[0] = GemmSeg{Wq, qd, q, qd, 0, 1, INT_MAX, m.C, 0};
+  g.seg[1] = GemmSeg{Wk, kd, kc, kd, 0, 1, INT_MAX, w.Cpad, 0};
+  g.seg[2] = GemmSeg{Wv, kd, vct, 1, 0, w.Cpad, INT_MAX, w.Cpad, 0};
+  hipError_t e = dg_launch_gemm(g, ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "dg_prefill_block(qkv)");
+  if (ctx->rope_base > 0.0) {
+    e = dg_launch_rope(q, m.C, m.Hq, m.hd, qd, P, ctx->rope_base, ctx->stream);
+    if (e == hipSuccess) e = dg_launch_rope(kc, m.C, m.Hkv, m.hd, kd, P, ctx->rope_base, ctx->stream);
+    if (e != hipSuccess) return hip_fail(ctx, e, "dg_prefill_block(rope)");
+  }
+
+  // Causal attention: the prefix [0, P) and block keys j <= i.
+  AttnArgs at{};
+  at.Q = q;
+  at.Kp = Kp;
+  at.Vt = Vt;
+  at.Kc = kc;
+  at.Vct = vct;
+  at.P = P;
+  at.Pcap = Pcap;
+  at.C = m.C;
+  at.Cpad = w.Cpad;
+  at.Hq = m.Hq;
+  at.Hkv = m.Hkv;
+  at.hd = m.hd;
+  at.nsplit = dg_attn_nsplit(m.Hkv, m.Hq, m.C, P);
+  at.causal = 1;
+  at.scale_log2 = (float)(1.4426950408889634 / sqrt((double)m.hd));
+  at.po = ws_at<float>(ws, w.po);
+  at.pml = ws_at<float>(ws, w.pml);
+  at.O = o;
+  e = dg_launch_attention(at, ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "dg_prefill_block(attention)");
+
+  GemmArgs go{};
+  go.M = m.C;
+  go.K = qd;
+  go.A = o;
+  go.nseg = 1;
+  go.seg[0] = GemmSeg{Wo, m.d, A, m.d, 0, 1, INT_MAX, m.C, 0};
+  e = dg_launch_gemm(go, ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "dg_prefill_block(wo)");
+
+  // The block's rotated keys and its values join the cache.
+  e = dg_launch_block_store(kc, vct, m.C, w.Cpad, m.Hkv, m.hd, Kp, Vt, P, Pcap, ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "dg_prefill_block(store)");
+  *P_out = P + m.C;
   return DG_OK;
 }
 

@@ -238,12 +238,17 @@ struct AttnArgs {
   int64_t P, Pcap;
   int C, Cpad, Hq, Hkv, hd;
   int nsplit;
+  int causal;          // 1: canvas-segment key j visible to query i only for j <= i
   float scale_log2;    // log2(e) / sqrt(hd)
   float *po;           // [nsplit][Hq][Cpad][hd]
   float *pml;          // [nsplit][Hq][Cpad][2]
   u16 *O;              // merged output [Cpad][Hq*hd]
 };
 hipError_t dg_launch_attention(const AttnArgs &a, hipStream_t st);
+hipError_t dg_launch_rope(u16 *x, int rows, int heads, int hd, int ld, int64_t pos0, double base,
+                          hipStream_t st);
+hipError_t dg_launch_block_store(const u16 *kc, const u16 *vct, int C, int Cpad, int Hkv, int hd,
+                                 u16 *Kp, u16 *Vt, int64_t P, int64_t Pcap, hipStream_t st);
 
 struct LogitsArgs {
   const u16 *H;        // [C][d]

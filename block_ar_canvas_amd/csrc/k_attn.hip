@@ -66,7 +66,9 @@ DG_DEV int kswz(int row, int chunk) {
 }
 DG_DEV int vswz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
-template <int HD>
+// CAUSAL (the block prefill): key j of the canvas segment (the block) is visible to
+// query i only for j <= i; prefix keys are always visible.
+template <int HD, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void attn_split_kernel(AttnArgs a, int nq, int ntc,
                                                              int ntiles, int units) {
   using F = Cfg<HD>;
@@ -264,6 +266,13 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(AttnArgs a, int nq,
           for (int rr = 0; rr < 16; ++rr)
             if (32 * kt + acc_row_perm(rr, hh) >= nvalid) S[kt][rr] = -INFINITY;
       }
+      if (CAUSAL && canvas && k0 + KT - 1 > qc) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr)
+            if (k0 + 32 * kt + acc_row_perm(rr, hh) > qc) S[kt][rr] = -INFINITY;
+      }
       float mt = fmaxf(S[0][0], S[1][0]);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -278,7 +287,9 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(AttnArgs a, int nq,
         for (int et = 0; et < F::ET; ++et) O[et] *= alpha;
         mref = mnew;
       }
-      const float nm = -mref;
+      // Under the causal mask a split may start with tiles that hide every key from a
+      // query: its reference stays -inf, and those tiles must contribute 0, not NaN.
+      const float nm = CAUSAL && mref == -INFINITY ? 0.f : -mref;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         float y[16], ls = 0.f;
@@ -387,11 +398,11 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   *(uint4 *)(a.O + (int64_t)c * a.Hq * HD + h * HD + e0) = out;
 }
 
-template <int HD>
+template <int HD, bool CAUSAL>
 hipError_t launch(const AttnArgs &a, hipStream_t st) {
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void *)attn_split_kernel<HD>,
+    hipError_t e = hipFuncSetAttribute((const void *)attn_split_kernel<HD, CAUSAL>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, Cfg<HD>::SMEM);
     if (e != hipSuccess) return e;
     attr = true;
@@ -401,8 +412,8 @@ hipError_t launch(const AttnArgs &a, hipStream_t st) {
   const int ntc = (a.C + KT - 1) / KT;
   const int ntiles = ntc + (int)((a.P + KT - 1) / KT);
   const int units = a.Hkv * a.nsplit;
-  hipLaunchKernelGGL(attn_split_kernel<HD>, dim3(units * nq), dim3(NW * 64), Cfg<HD>::SMEM, st, a,
-                     nq, ntc, ntiles, units);
+  hipLaunchKernelGGL((attn_split_kernel<HD, CAUSAL>), dim3(units * nq), dim3(NW * 64), Cfg<HD>::SMEM,
+                     st, a, nq, ntc, ntiles, units);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int RPB = 256 / (HD / 8);
@@ -413,11 +424,20 @@ hipError_t launch(const AttnArgs &a, hipStream_t st) {
 }  // namespace
 
 hipError_t dg_launch_attention(const AttnArgs &a, hipStream_t st) {
+  if (a.causal) {
+    switch (a.hd) {
+      case 16: return launch<16, true>(a, st);
+      case 32: return launch<32, true>(a, st);
+      case 64: return launch<64, true>(a, st);
+      case 128: return launch<128, true>(a, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (a.hd) {
-    case 16: return launch<16>(a, st);
-    case 32: return launch<32>(a, st);
-    case 64: return launch<64>(a, st);
-    case 128: return launch<128>(a, st);
+    case 16: return launch<16, false>(a, st);
+    case 32: return launch<32, false>(a, st);
+    case 64: return launch<64, false>(a, st);
+    case 128: return launch<128, false>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

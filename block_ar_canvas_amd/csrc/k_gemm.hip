@@ -252,6 +252,69 @@ hipError_t dg_launch_gemm(const GemmArgs &a0, hipStream_t st) {
   return hipGetLastError();
 }
 
+namespace {
+
+// Rotary position embedding in place on bf16 rows, half-split pairing: the pair
+// (x_d, x_{d+hd/2}) of row r turns by (pos0 + r) * base^(-2d/hd). The openai-hub page
+// "从零拆开DiffusionGemma" (closing remarks of step 3) names rotary positions as part of
+// the full model. Angle, sine, cosine and rotation in float64: token positions reach 2^18
+// and more, where a float32 angle is already off by about 1e-2 rad.
+__global__ __launch_bounds__(256) void rope_kernel(u16 *x, int rows, int heads, int hd, int ld,
+                                                   int64_t pos0, double base) {
+  const int half = hd / 2;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)rows * heads * half) return;
+  const int d = (int)(i % half);
+  const int64_t rh = i / half;
+  const int h = (int)(rh % heads), r = (int)(rh / heads);
+  u16 *p = x + (int64_t)r * ld + h * hd;
+  const double ang = (double)(pos0 + r) * pow(base, -2.0 * d / hd);
+  double sn, cs;
+  sincos(ang, &sn, &cs);
+  const double x1 = __uint_as_float((uint32_t)p[d] << 16);
+  const double x2 = __uint_as_float((uint32_t)p[d + half] << 16);
+  p[d] = f32_to_bf16((float)(x1 * cs - x2 * sn));
+  p[d + half] = f32_to_bf16((float)(x1 * sn + x2 * cs));
+}
+
+// Appends a block's keys (rows of kc [Cpad][Hkv*hd]) and values (vct [Hkv*hd][Cpad]) to
+// the cache at token positions [P, P + C): Kp[g][P + r][e] and Vt[g][e][P + r].
+__global__ __launch_bounds__(256) void block_store_kernel(const u16 *kc, const u16 *vct, int C, int Cpad,
+                                                          int Hkv, int hd, u16 *Kp, u16 *Vt, int64_t P,
+                                                          int64_t Pcap) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)C * Hkv * hd) return;
+  {
+    const int e = (int)(i % hd);
+    const int64_t t = i / hd;
+    const int g = (int)(t % Hkv), r = (int)(t / Hkv);
+    Kp[((int64_t)g * Pcap + P + r) * hd + e] = kc[(int64_t)r * Hkv * hd + g * hd + e];
+  }
+  {
+    const int r = (int)(i % C);
+    const int64_t ge = i / C;                      // g * hd + e
+    Vt[ge * Pcap + P + r] = vct[ge * Cpad + r];
+  }
+}
+
+}  // namespace
+
+hipError_t dg_launch_rope(u16 *x, int rows, int heads, int hd, int ld, int64_t pos0, double base,
+                          hipStream_t st) {
+  const int64_t n = (int64_t)rows * heads * (hd / 2);
+  hipLaunchKernelGGL(rope_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, x, rows, heads,
+                     hd, ld, pos0, base);
+  return hipGetLastError();
+}
+
+hipError_t dg_launch_block_store(const u16 *kc, const u16 *vct, int C, int Cpad, int Hkv, int hd,
+                                 u16 *Kp, u16 *Vt, int64_t P, int64_t Pcap, hipStream_t st) {
+  const int64_t n = (int64_t)C * Hkv * hd;
+  hipLaunchKernelGGL(block_store_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, kc, vct,
+                     C, Cpad, Hkv, hd, Kp, Vt, P, Pcap);
+  return hipGetLastError();
+}
+
 hipError_t dg_launch_xgather(const int *tokens, const u16 *E, const u16 *z, int V, int M, int K,
                              u16 *X, int *status, hipStream_t st) {
   hipLaunchKernelGGL(xgather_kernel, dim3(M), dim3(256), 0, st, tokens, E, z, V, K, X, status);

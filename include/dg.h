@@ -208,6 +208,29 @@ dg_status dg_stop_test(dg_ctx ctx, int32_t B, int32_t C, const float *entropy,
                        const int32_t *argmax, const int32_t *prev_argmax, float thr,
                        int32_t step, int32_t N, int32_t *flag);
 
+/* Rotary positions (openai-hub page "从零拆开DiffusionGemma", closing remarks of step 3:
+ * the full model has rotary position encoding) for dg_canvas_attn and dg_prefill_block
+ * of this context: base 0 (the default) turns them off; base > 0 rotates, in every head,
+ * the pair (q_d, q_{d+hd/2}) of a token at position p by p * base^(-2d/hd) (half-split
+ * pairing), in queries and keys, after the bf16 projection, re-rounded to bf16. Canvas
+ * and block token i sits at position P + i; cached prefix keys are taken as rotated.
+ * DG_ERR_RANGE for a negative or non-finite base. */
+dg_status dg_set_rope(dg_ctx ctx, float base);
+
+/* Causal re-encode of a finalized block (tutorial chapter "DiffusionGemma": the data-flow
+ * pseudocode's incremental prefill of the finalized block, and the KV-cache write
+ * timing: the next context comes from the backbone re-encoding the block causally, not
+ * from the denoiser's states). One attention layer stands in for the backbone:
+ * X = E[tokens]; Q, K, V = bf16(X W^T), Q and K rotated to positions P + i when the
+ * context has a rotary base; block token i attends to the prefix [0, P) and to block
+ * tokens j <= i; A = bf16(O Wo^T). The block's (rotated) K and V rows are appended at
+ * [P, P + C), and *P_out (host) = P + C. Same layouts as dg_canvas_attn; A [C, d] output.
+ * DG_ERR_CAPACITY (nothing enqueued) when P + C > Pcap. */
+dg_status dg_prefill_block(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens,
+                           const dg_bf16 *E, const dg_bf16 *Wq, const dg_bf16 *Wk,
+                           const dg_bf16 *Wv, const dg_bf16 *Wo, dg_bf16 *Kp, dg_bf16 *Vt,
+                           int64_t P, int64_t Pcap, void *ws, dg_bf16 *A, int64_t *P_out);
+
 /* Commit (Technical Report page, "Method steps" (5); tutorial chapter "DiffusionGemma",
  * KV-cache write timing): appends the finalized block's keys and values at token
  * positions [P, P + C) of every KV head: K = bf16(E[tokens] Wk^T), V = bf16(E[tokens]
