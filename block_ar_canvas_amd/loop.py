@@ -20,6 +20,7 @@ from . import STOP_GO, Context, Dims, reveal_count, temperature, workspace_bytes
 
 RULES = ("entropy", "confidence")
 DRAWS = ("argmax", "sample")
+COMMITS = ("projection", "prefill")
 
 
 class CanvasLoop:
@@ -31,15 +32,20 @@ class CanvasLoop:
     reveal_count(C, N, k) most confident positions of step k are accepted).
     draw: "argmax" (accepted positions and the commit take x0 = argmax) or "sample"
     (they take x~ ~ p0 drawn by dg_sample); the stop test compares argmaxes either way.
+    commit: "projection" (dg_commit_kv: K/V = E[x0] W^T) or "prefill" (dg_prefill_block:
+    the causal re-encode); rope_base > 0 sets the context's rotary positions (used by
+    canvas attention and the prefill).
     """
 
     def __init__(self, ctx: Context, dims, weights, Kp, Vt, P: int, *, N: int, seed: int,
                  b: float = 0.1, thr: float = 0.005, tau0: float = 0.8, tau1: float = 0.4,
-                 rule: str = "entropy", draw: str = "argmax"):
-        if rule not in RULES or draw not in DRAWS:
-            raise ValueError(f"rule must be one of {RULES}, draw one of {DRAWS}")
-        self.rule, self.draw = rule, draw
+                 rule: str = "entropy", draw: str = "argmax", commit: str = "projection",
+                 rope_base: float = 0.0):
+        if rule not in RULES or draw not in DRAWS or commit not in COMMITS:
+            raise ValueError(f"rule must be one of {RULES}, draw one of {DRAWS}, commit one of {COMMITS}")
+        self.rule, self.draw, self.commit_mode = rule, draw, commit
         self.ctx, self.dims = ctx, Dims.of(dims)
+        ctx.set_rope(rope_base)
         self.W, self.Kp, self.Vt, self.P = weights, Kp, Vt, int(P)
         self.N, self.seed, self.b, self.thr, self.tau0, self.tau1 = N, seed, b, thr, tau0, tau1
         dev = Kp.device
@@ -125,8 +131,12 @@ class CanvasLoop:
                 raise RuntimeError(f"stop flag of step {k} was never written")
 
     def commit(self, x0):
-        self.P = self.ctx.commit_kv(self.dims, x0, self.W["E"], self.W["Wk"], self.W["Wv"],
-                                    self.Kp, self.Vt, self.P)
+        W = self.W
+        if self.commit_mode == "prefill":
+            self.P = self.ctx.prefill_block(self.dims, x0, W["E"], W["Wq"], W["Wk"], W["Wv"], W["Wo"],
+                                            self.Kp, self.Vt, self.P, self.ws, self.A)
+        else:
+            self.P = self.ctx.commit_kv(self.dims, x0, W["E"], W["Wk"], W["Wv"], self.Kp, self.Vt, self.P)
         return self.P
 
     def run_canvas(self, canvas: int, hidden, on_step=None):
@@ -174,15 +184,18 @@ class BatchLoop:
     its commit writes, while the others go on (its later steps are computed and ignored).
 
     caches: list of B (Kp [Hkv, Pcap, hd], Vt [Hkv, hd, Pcap], P) per request.
+    rule, draw, commit and rope_base as in CanvasLoop.
     """
 
     def __init__(self, ctx: Context, dims, weights, caches, *, N: int, seed: int,
                  b: float = 0.1, thr: float = 0.005, tau0: float = 0.8, tau1: float = 0.4,
-                 rule: str = "entropy", draw: str = "argmax"):
-        if rule not in RULES or draw not in DRAWS:
-            raise ValueError(f"rule must be one of {RULES}, draw one of {DRAWS}")
-        self.rule, self.draw = rule, draw
+                 rule: str = "entropy", draw: str = "argmax", commit: str = "projection",
+                 rope_base: float = 0.0):
+        if rule not in RULES or draw not in DRAWS or commit not in COMMITS:
+            raise ValueError(f"rule must be one of {RULES}, draw one of {DRAWS}, commit one of {COMMITS}")
+        self.rule, self.draw, self.commit_mode = rule, draw, commit
         self.ctx, self.W = ctx, weights
+        ctx.set_rope(rope_base)
         self.B = len(caches)
         self.dims = Dims.of(dims)                       # one canvas
         C, d = self.dims.C, self.dims.d
@@ -300,7 +313,13 @@ class BatchLoop:
             k += 1
             if on_step is not None:
                 on_step(k, self)
+        W = self.W
         for i in range(B):
-            self.P[i] = self.ctx.commit_kv(self.dims, x0[i], self.W["E"], self.W["Wk"],
-                                           self.W["Wv"], self.Kp[i], self.Vt[i], self.P[i])
+            if self.commit_mode == "prefill":
+                self.P[i] = self.ctx.prefill_block(self.dims, x0[i], W["E"], W["Wq"], W["Wk"], W["Wv"],
+                                                   W["Wo"], self.Kp[i], self.Vt[i], self.P[i],
+                                                   self.ws_attn, self.A[i])
+            else:
+                self.P[i] = self.ctx.commit_kv(self.dims, x0[i], W["E"], W["Wk"], W["Wv"], self.Kp[i],
+                                               self.Vt[i], self.P[i])
         return steps

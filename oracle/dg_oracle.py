@@ -48,6 +48,9 @@ Readings taken where the pages leave a step open (each restated where it is used
     256-id vocabulary chunk by inverse CDF over chunk masses with one Philox uniform,
     then Gumbel-max inside the chunk with Philox-driven Gumbel noise; accepted positions
     and the commit take x~, the stop test still compares argmaxes;
+  * the commit as a causal re-encode (an alternative to the projection stand-in): one
+    attention layer over the prefix and the block's earlier tokens, with rotary positions
+    when a base is given, appends the block's rotated K and its V;
   * the confidence rule (an alternative to the entropy budget): a position's confidence
     is its largest tempered probability; step k accepts the n_k most confident positions
     (ties to the lower position, NaN never), n_k the number the [HUB] decoder has revealed
@@ -551,7 +554,7 @@ def prefill_block(tokens, E_bits, Wq, Wk, Wv, Wo, Kp, Vp, P, Hq, Hkv, hd, rope_b
 # ------------------------------------------------------------------ the step loop
 def run_canvas(W, Kp, Vp, P, hidden_of_step, *, V, C, Hq, Hkv, hd, N, seed, canvas,
                b=0.1, thr=0.005, tau0=0.8, tau1=0.4, record=True, with_attn=True,
-               rule="entropy", draw="argmax"):
+               rule="entropy", draw="argmax", commit="projection", rope_base=0.0):
     """One canvas of the block-AR loop: init, up to N denoise steps, commit.
 
     [TR] "Method steps" (2)-(5) in order; [TUT] data-flow pseudocode. The sampler head's
@@ -559,7 +562,9 @@ def run_canvas(W, Kp, Vp, P, hidden_of_step, *, V, C, Hq, Hkv, hd, N, seed, canv
     the denoiser stack); the attention output A_k is computed on the true denoiser input
     X_k = E[x_k] + z_k every step and recorded, but does not feed H_k.
     rule "confidence" replaces the entropy budget by the confidence rule; draw "sample"
-    gives accepted positions, and the commit, x~ ~ p^0 instead of x^0 (module header).
+    gives accepted positions, and the commit, x~ ~ p^0 instead of x^0; commit "prefill"
+    re-encodes the block causally (prefill_block) instead of projecting it; rope_base > 0
+    rotates canvas (and block) queries and keys to their positions (module header).
     Returns (new P, list of per-step records).
     """
     d = W["E"].shape[1]
@@ -575,7 +580,7 @@ def run_canvas(W, Kp, Vp, P, hidden_of_step, *, V, C, Hq, Hkv, hd, N, seed, canv
         rec = {"k": k, "tau": tau, "tokens_in": x.copy(), "z_in": z.copy()}
         if with_attn:
             A, _ = canvas_attn(x, z, W["E"], W["Wq"], W["Wk"], W["Wv"], W["Wo"],
-                               Kp, Vp, P, Hq, Hkv, hd)
+                               Kp, Vp, P, Hq, Hkv, hd, rope_base=rope_base)
             rec["A"] = A
         ent, am, p, _ = logits_entropy(hidden_of_step(k), W["E"], tau)
         x0 = am
@@ -599,5 +604,11 @@ def run_canvas(W, Kp, Vp, P, hidden_of_step, *, V, C, Hq, Hkv, hd, N, seed, canv
         prev = am
         if flag != STOP_GO:
             break
-    P = commit_kv(x0, W["E"], W["Wk"], W["Wv"], Kp, Vp, P, Hkv, hd)
+    if commit == "prefill":
+        A_block, P = prefill_block(x0, W["E"], W["Wq"], W["Wk"], W["Wv"], W["Wo"], Kp, Vp, P,
+                                   Hq, Hkv, hd, rope_base)
+        if record and recs:
+            recs[-1]["A_commit"] = A_block
+    else:
+        P = commit_kv(x0, W["E"], W["Wk"], W["Wv"], Kp, Vp, P, Hkv, hd)
     return P, recs

@@ -46,14 +46,15 @@ def cutoff_confidence(conf, acc):
     return cands
 
 
-def run_both(dg_ctx, cfg, n_canvas=1, rule="entropy", draw="argmax"):
+def run_both(dg_ctx, cfg, n_canvas=1, rule="entropy", draw="argmax", commit="projection",
+             rope_base=0.0):
     W = di.weights(cfg)
     Pcap = -(-(cfg.P0 + cfg.C * n_canvas) // 8) * 8
     Kp, Vp = di.prefix_kv(cfg, Pcap)
     Wd = upload_weights(W)
     Kd, Vtd = upload_cache(Kp, Vp, Pcap)
     loop = CanvasLoop(dg_ctx, cfg, Wd, Kd, Vtd, cfg.P0, N=cfg.N, seed=cfg.seed, rule=rule,
-                      draw=draw)
+                      draw=draw, commit=commit, rope_base=rope_base)
     P_o = cfg.P0
     stats = {"positions": 0, "mismatch": 0, "unexcused": 0}
     for c in range(n_canvas):
@@ -74,7 +75,7 @@ def run_both(dg_ctx, cfg, n_canvas=1, rule="entropy", draw="argmax"):
         loop.run_canvas(c, lambda k: Hd[k], on_step=on_step)
         P_o, recs = O.run_canvas(W, Kp, Vp, P_o, lambda k: Hs[k], V=cfg.V, C=cfg.C, Hq=cfg.Hq,
                                  Hkv=cfg.Hkv, hd=cfg.hd, N=cfg.N, seed=cfg.seed, canvas=c,
-                                 rule=rule, draw=draw)
+                                 rule=rule, draw=draw, commit=commit, rope_base=rope_base)
         assert [r["flag"] for r in rec] == [r["flag"] for r in recs]
         for g, r in zip(rec, recs):
             assert np.max(np.abs(g["entropy"] - r["entropy"])) <= 1e-3
@@ -133,6 +134,16 @@ def test_loop_parity_sampled_tokens(dg_ctx, cfg, rule):
     s = run_both(dg_ctx, cfg, 1, rule=rule, draw="sample")
     assert s["unexcused"] == 0, s
     assert s["mismatch"] <= 0.01 * s["positions"], s
+
+
+@pytest.mark.parametrize("cfg", [di.config(0), RAGGED], ids=["tiny", "ragged"])
+def test_loop_parity_prefill_commit_rotary(dg_ctx, cfg):
+    try:
+        s = run_both(dg_ctx, cfg, 2, commit="prefill", rope_base=10000.0)
+    finally:
+        dg_ctx.set_rope(0.0)
+    assert s["unexcused"] == 0, s
+    assert s["mismatch"] <= 0.001 * s["positions"], s
 
 
 @pytest.mark.parametrize("cfg,n_canvas", [(di.config(0), 2), (RAGGED, 1)], ids=["tiny", "ragged"])
