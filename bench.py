@@ -233,6 +233,7 @@ def main():
     del Hd
     if not args.no_chain:
         result["chain8"] = chain(ctx)
+        result["chain8_prefill"] = chain(ctx, commit="prefill", rope_base=10000.0)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, W, Kp, args.cpu_steps)
     print(json.dumps(result))
@@ -360,10 +361,12 @@ def variant_canvas(ctx, cfg, Wd, Hd, rule="entropy", draw="argmax"):
             "canvas_tokens_per_s": round(cfg.C / sec, 1)}
 
 
-def chain(ctx):
+def chain(ctx, commit="projection", rope_base=0.0):
     """The 8-canvas block-AR chain (chain8 workload: prefix 32768, seed 4): every canvas
     runs its step loop to the stop test or the 48-step cap and commits its K/V before
-    the next canvas starts. Returns canvas tokens/s including commits."""
+    the next canvas starts. Returns canvas tokens/s including commits. commit="prefill"
+    (with rope_base) commits by the causal re-encode, with rotary positions throughout,
+    and also reports the prefill call's own time."""
     import torch
     import dg_inputs as di
     from block_ar_canvas_amd.loop import CanvasLoop
@@ -378,7 +381,8 @@ def chain(ctx):
     del Kp, Vp
     Hd = [_bf(di.hidden_all(cc, W["E"], c), dev) for c in range(cc.n_canvas)]
     del W
-    loop = CanvasLoop(ctx, cc, Wd, Kd, Vtd, cc.P0, N=cc.N, seed=cc.seed)
+    loop = CanvasLoop(ctx, cc, Wd, Kd, Vtd, cc.P0, N=cc.N, seed=cc.seed, commit=commit,
+                      rope_base=rope_base)
     # warm-up: one canvas on a copy of the cache start, then reset the length
     loop.run_canvas(0, lambda k: Hd[0][k])
     loop.P = cc.P0
@@ -391,9 +395,29 @@ def chain(ctx):
     sec = time.perf_counter() - t0
     ctx.sync()
     assert loop.P == cc.P0 + cc.n_canvas * cc.C
-    return {"workload": f"chain8: {cc.n_canvas} canvases of {cc.C} from prefix {cc.P0}, V={cc.V} d={cc.d}",
-            "canvas_tokens_per_s": round(cc.n_canvas * cc.C / sec, 1),
-            "steps": steps, "steps_per_s": round(steps / sec, 2), "seconds": round(sec, 4)}
+    out = {"workload": f"chain8: {cc.n_canvas} canvases of {cc.C} from prefix {cc.P0}, V={cc.V} d={cc.d}",
+           "commit": commit, "rope_base": rope_base,
+           "canvas_tokens_per_s": round(cc.n_canvas * cc.C / sec, 1),
+           "steps": steps, "steps_per_s": round(steps / sec, 2), "seconds": round(sec, 4)}
+    if commit == "prefill":
+        # the commit call alone, at the chain's final length (reset after each call)
+        P_end = loop.P - cc.C
+        x0 = torch.zeros(cc.C, dtype=torch.int32, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        stream = torch.cuda.current_stream()
+        for _ in range(3):
+            loop.P = P_end
+            loop.commit(x0)
+        e0.record(stream)
+        for _ in range(10):
+            loop.P = P_end
+            loop.commit(x0)
+        e1.record(stream)
+        e1.synchronize()
+        out["prefill_ms_per_call"] = round(e0.elapsed_time(e1) / 10, 4)
+        out["prefill_prefix_tokens"] = P_end
+    ctx.set_rope(0.0)
+    return out
 
 
 def cpu_baseline(cfg, W, Kp, n_steps):
