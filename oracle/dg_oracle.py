@@ -23,6 +23,11 @@ Sources (web pages on DiffusionGemma):
   [SRV] "Text diffusion models" survey (papers.franksyz.com), section 11 (DiffusionGemma
         defaults: 48 steps, entropy bound 0.1, temperature 0.8 -> 0.4), section 5 (reverse
         generation: predict, select, accept, remask).
+  [MOE] the DiffusionGemma Technical Report page, section "Prerequisites" (mixture of
+        experts: 8 of 128 experts plus one shared expert per token; about 84 distinct
+        experts active per canvas against 8 per token), and the survey's section 11
+        (128 experts per layer, 8 routed, 1 shared) and section 13 (router top-k, expert
+        GEMM, token permutation).
   [HUB] openai-hub page "从零拆开DiffusionGemma" (news 2086), step 4 (confidence decoding:
         predict every position, keep the most confident ones, the simplified decoder's
         reveal count ceil(unresolved / remaining steps)); the closing remarks of step 3
@@ -549,6 +554,48 @@ def prefill_block(tokens, E_bits, Wq, Wk, Wv, Wo, Kp, Vp, P, Hq, Hkv, hd, rope_b
         O[:, h] = W @ V
     A = to_bf16(O.reshape(C, Hq * hd) @ from_bf16(Wo).T)
     return A, P + C
+
+
+# ------------------------------------------------------------------ canvas MoE FFN
+def moe_route(X_bits, Wr, K):
+    """Router of the canvas MoE FFN ([MOE]): logits r = X Wr^T; each token takes the K
+    experts with the largest logits (ties to the lower expert id) and gates them with a
+    softmax over those K logits. The selection is decided on the logits rounded to float32
+    (the device's precision for this discrete decision); gates in float64.
+    Returns (experts int32 [C, K] in rank order, gates float64 [C, K], logits float32 [C, E])."""
+    X = from_bf16(X_bits)
+    r = (X @ from_bf16(Wr).T).astype(np.float32)
+    C, E = r.shape
+    sel = np.zeros((C, K), dtype=np.int32)
+    gates = np.zeros((C, K))
+    for t in range(C):
+        order = sorted(range(E), key=lambda e: (-float(r[t, e]), e))[:K]
+        sel[t] = order
+        v = r[t, order].astype(np.float64)
+        w = np.exp(v - v.max())
+        gates[t] = w / w.sum()
+    return sel, gates, r
+
+
+def moe_ffn(X_bits, Wr, W1, W2, W1s, W2s, K):
+    """Canvas MoE FFN ([MOE]): y = sum over the token's K routed experts of gate * E_e(x)
+    + S(x), every expert and the shared one of the FFW form W2 GELU_erf(W1 x) (the form of
+    the self-conditioning FFW; the pages name no gating). Expert and shared outputs are
+    stored as bf16, combined in float64, and y is rounded to bf16.
+    X [C, d]; Wr [E, d]; W1 [E, Fe, d]; W2 [E, d, Fe]; W1s [Fs, d]; W2s [d, Fs] (bf16 bits).
+    Returns (Y bits [C, d], experts [C, K], gates [C, K], number of distinct experts used)."""
+    X = from_bf16(X_bits)
+    sel, gates, _ = moe_route(X_bits, Wr, K)
+    C, d = X.shape
+    acc = np.zeros((C, d))
+    for e in np.unique(sel):
+        rows, ranks = np.nonzero(sel == e)
+        h = from_bf16(to_bf16(gelu_erf(X[rows] @ from_bf16(W1[e]).T)))
+        y = from_bf16(to_bf16(h @ from_bf16(W2[e]).T))
+        acc[rows] += gates[rows, ranks][:, None] * y
+    hs = from_bf16(to_bf16(gelu_erf(X @ from_bf16(W1s).T)))
+    ys = from_bf16(to_bf16(hs @ from_bf16(W2s).T))
+    return to_bf16(acc + ys), sel, gates, int(len(np.unique(sel)))
 
 
 # ------------------------------------------------------------------ the step loop
