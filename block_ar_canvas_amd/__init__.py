@@ -13,7 +13,7 @@ import os
 
 import torch
 
-__all__ = ["DGError", "Dims", "Context", "workspace_bytes", "temperature", "reveal_count", "lib_path",
+__all__ = ["DGError", "Dims", "MoeDims", "Context", "moe_workspace_bytes", "workspace_bytes", "temperature", "reveal_count", "lib_path",
            "STOP_GO", "STOP_STOP", "STOP_CAP"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,6 +33,10 @@ class DGError(RuntimeError):
 
 def lib_path() -> str:
     return os.path.join(_HERE, "libdg.so")
+
+
+class MoeDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("d", "E", "K", "Fe", "Fs")]
 
 
 class Dims(ctypes.Structure):
@@ -77,6 +81,8 @@ def _load():
         "dg_reveal_count": (i32, [i32, i32, i32]),
         "dg_sample": (i32, [_P, D, _P, i32, u64, u32, u32, _P]),
         "dg_set_rope": (i32, [_P, f32]),
+        "dg_moe_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(MoeDims), i32]),
+        "dg_moe_ffn": (i32, [_P, ctypes.POINTER(MoeDims), i32, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
         "dg_prefill_block": (i32, [_P, D, _P, _P, _P, _P, _P, _P, _P, _P, i64, i64, _P, _P,
                                    ctypes.POINTER(i64)]),
         "dg_renoise": (i32, [_P, i32, i32, i32, _P, _P, u64, u32, u32, _P]),
@@ -102,6 +108,13 @@ def workspace_bytes(dims, Pcap: int) -> int:
 
 def temperature(k: int, N: int, tau0: float = 0.8, tau1: float = 0.4) -> float:
     return float(_load().dg_temperature(int(k), int(N), float(tau0), float(tau1)))
+
+
+def moe_workspace_bytes(md, C: int) -> int:
+    n = _load().dg_moe_workspace_bytes(ctypes.byref(md), int(C))
+    if n == 0:
+        raise DGError(2, "dg_moe_workspace_bytes: bad dims")
+    return int(n)
 
 
 def reveal_count(C: int, N: int, step: int) -> int:
@@ -240,6 +253,14 @@ class Context:
             self._h, B, C, _ptr(entropy, _F32, "entropy"), _ptr(argmax, _I32, "argmax"),
             _ptr(prev_argmax, _I32, "prev_argmax", True), float(thr), int(step), int(N),
             _ptr(flag, _I32, "flag", pinned_ok=True)))
+
+    def moe_ffn(self, md, X, Wr, W1, W2, W1s, W2s, ws, Y, n_active=None):
+        C = X.shape[0]
+        self._check(self._lib.dg_moe_ffn(
+            self._h, ctypes.byref(md), int(C), _ptr(X, _BF16, "X"), _ptr(Wr, _BF16, "Wr"),
+            _ptr(W1, _BF16, "W1"), _ptr(W2, _BF16, "W2"), _ptr(W1s, _BF16, "W1s"),
+            _ptr(W2s, _BF16, "W2s"), _ptr(ws, _U8, "ws"), _ptr(Y, _BF16, "Y"),
+            _ptr(n_active, _I32, "n_active", True)))
 
     def set_rope(self, base: float):
         self._check(self._lib.dg_set_rope(self._h, float(base)))

@@ -244,6 +244,101 @@ dg_status dg_canvas_attn(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens,
   return DG_OK;
 }
 
+static dg_status check_moe(dg_ctx ctx, const dg_moe_dims *m, int32_t C, const char *fn) {
+  if (!m) return fail(ctx, DG_ERR_NULL, "%s: moe dims is NULL", fn);
+  if (C < 1 || C > 1024) return fail(ctx, DG_ERR_SHAPE, "%s: need 1 <= C <= 1024", fn);
+  // the GEMMs take K in whole 16-deep MFMA steps, and every width is also an N or a K
+  if (m->d < 32 || m->d % 32 || m->Fe < 32 || m->Fe % 32 || m->Fs < 32 || m->Fs % 32)
+    return fail(ctx, DG_ERR_SHAPE, "%s: d, Fe, Fs must be positive multiples of 32", fn);
+  if (m->E < 1 || m->E > 256 || m->K < 1 || m->K > m->E || m->K > 32 || (int64_t)C * m->K > 8192)
+    return fail(ctx, DG_ERR_SHAPE, "%s: need 1 <= K <= min(E, 32), E <= 256, C * K <= 8192", fn);
+  return DG_OK;
+}
+
+size_t dg_moe_workspace_bytes(const dg_moe_dims *m, int32_t C) {
+  if (!m || check_moe(nullptr, m, C, "dg_moe_workspace_bytes") != DG_OK) return 0;
+  return dg_moe_ws_layout(C, m->d, m->E, m->K, m->Fe, m->Fs).total;
+}
+
+dg_status dg_moe_ffn(dg_ctx ctx, const dg_moe_dims *m, int32_t C, const dg_bf16 *X,
+                     const dg_bf16 *Wr, const dg_bf16 *W1, const dg_bf16 *W2, const dg_bf16 *W1s,
+                     const dg_bf16 *W2s, void *ws, dg_bf16 *Y, int32_t *n_active) {
+  if (!ctx) return DG_ERR_NULL;
+  dg_status st = check_moe(ctx, m, C, __func__);
+  if (st) return st;
+  DG_REQUIRE_PTR(X);
+  DG_REQUIRE_PTR(Wr);
+  DG_REQUIRE_PTR(W1);
+  DG_REQUIRE_PTR(W2);
+  DG_REQUIRE_PTR(W1s);
+  DG_REQUIRE_PTR(W2s);
+  DG_REQUIRE_PTR(ws);
+  DG_REQUIRE_PTR(Y);
+  const DgMoeWs w = dg_moe_ws_layout(C, m->d, m->E, m->K, m->Fe, m->Fs);
+  float *logits = ws_at<float>(ws, w.logits), *gate = ws_at<float>(ws, w.gate);
+  int *sel = ws_at<int>(ws, w.sel), *off = ws_at<int>(ws, w.off);
+  int *perm = ws_at<int>(ws, w.perm), *pos = ws_at<int>(ws, w.pos);
+  u16 *h = ws_at<u16>(ws, w.h), *yg = ws_at<u16>(ws, w.yg), *hs = ws_at<u16>(ws, w.hs);
+  u16 *ys = ws_at<u16>(ws, w.ys);
+
+  // router logits in float32 (the routing decision is taken on them)
+  GemmArgs gr{};
+  gr.M = C;
+  gr.K = m->d;
+  gr.A = X;
+  gr.nseg = 1;
+  gr.seg[0] = GemmSeg{Wr, m->E, nullptr, m->E, 0, 1, INT_MAX, C, 0};
+  gr.out32 = logits;
+  gr.ld32 = m->E;
+  hipError_t e = dg_launch_gemm(gr, ctx->stream);
+  if (e == hipSuccess) e = dg_launch_moe_route(logits, C, m->E, m->K, sel, gate, ctx->stream);
+  if (e == hipSuccess) e = dg_launch_moe_group(sel, C, m->K, m->E, off, perm, pos, n_active, ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "dg_moe_ffn(route)");
+
+  // routed experts: grouped GEMMs, hidden = GELU(X W1_e^T), out = hidden W2_e^T
+  GemmArgs g1{};
+  g1.M = C;
+  g1.K = m->d;
+  g1.A = X;
+  g1.gelu = 1;
+  g1.nseg = 1;
+  g1.seg[0] = GemmSeg{W1, m->Fe, h, m->Fe, 0, 1, INT_MAX, C, 0};
+  g1.g_E = m->E;
+  g1.g_off = off;
+  g1.g_perm = perm;
+  e = dg_launch_gemm(g1, ctx->stream);
+  GemmArgs g2{};
+  g2.M = C;
+  g2.K = m->Fe;
+  g2.A = h;
+  g2.nseg = 1;
+  g2.seg[0] = GemmSeg{W2, m->d, yg, m->d, 0, 1, INT_MAX, C, 0};
+  g2.g_E = m->E;
+  g2.g_off = off;
+  if (e == hipSuccess) e = dg_launch_gemm(g2, ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "dg_moe_ffn(experts)");
+
+  // shared expert
+  GemmArgs s1{};
+  s1.M = C;
+  s1.K = m->d;
+  s1.A = X;
+  s1.gelu = 1;
+  s1.nseg = 1;
+  s1.seg[0] = GemmSeg{W1s, m->Fs, hs, m->Fs, 0, 1, INT_MAX, C, 0};
+  e = dg_launch_gemm(s1, ctx->stream);
+  GemmArgs s2{};
+  s2.M = C;
+  s2.K = m->Fs;
+  s2.A = hs;
+  s2.nseg = 1;
+  s2.seg[0] = GemmSeg{W2s, m->d, ys, m->d, 0, 1, INT_MAX, C, 0};
+  if (e == hipSuccess) e = dg_launch_gemm(s2, ctx->stream);
+  if (e == hipSuccess) e = dg_launch_moe_combine(yg, ys, gate, pos, C, m->K, m->d, Y, ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "dg_moe_ffn(shared, combine)");
+  return DG_OK;
+}
+
 dg_status dg_set_rope(dg_ctx ctx, float base) {
   if (!ctx) return DG_ERR_NULL;
   if (!(base >= 0.f) || !isfinite(base)) return fail(ctx, DG_ERR_RANGE, "%s: base=%g must be >= 0", __func__, base);

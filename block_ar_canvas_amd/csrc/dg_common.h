@@ -224,8 +224,60 @@ struct GemmArgs {
   int nseg;
   GemmSeg seg[3];
   int store_mode[3];   // set by the launcher
+  // fp32 output (segment 0 only): out32[m * ld32 + n] = D[m][n] instead of bf16 stores
+  float *out32;
+  int ld32;
+  // Grouped by expert (segment 0 only): g_E groups; group e has rows
+  // [g_off[e], g_off[e+1]) of the output and its own weights seg[0].W + e * N * K. Its
+  // activation rows are A[g_perm[g_off[e] + m]] (g_perm non-NULL) or A[g_off[e] + m].
+  // M is the largest possible group size; blocks past a group's size do nothing.
+  int g_E;
+  const int *g_off, *g_perm;
 };
 hipError_t dg_launch_gemm(const GemmArgs &a, hipStream_t st);
+
+// Canvas MoE FFN workspace (256-byte aligned regions).
+struct DgMoeWs {
+  size_t logits;   // router logits fp32 [C][E]
+  size_t sel;      // selected experts int32 [C][K] (rank order)
+  size_t gate;     // gates fp32 [C][K]
+  size_t off;      // group offsets int32 [E + 1]
+  size_t perm;     // tokens in grouped order int32 [C * K]
+  size_t pos;      // grouped row of (token, rank) int32 [C * K]
+  size_t h;        // expert hidden bf16 [C * K][Fe] (grouped order)
+  size_t yg;       // expert outputs bf16 [C * K][d] (grouped order)
+  size_t hs;       // shared hidden bf16 [C][Fs]
+  size_t ys;       // shared output bf16 [C][d]
+  size_t total;
+};
+static inline DgMoeWs dg_moe_ws_layout(int C, int d, int E, int K, int Fe, int Fs) {
+  DgMoeWs w;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = (size_t)dg_round_up((int64_t)(off + bytes), 256);
+    return at;
+  };
+  const size_t CK = (size_t)C * K;
+  w.logits = take((size_t)C * E * 4);
+  w.sel = take(CK * 4);
+  w.gate = take(CK * 4);
+  w.off = take((size_t)(E + 1) * 4);
+  w.perm = take(CK * 4);
+  w.pos = take(CK * 4);
+  w.h = take(CK * Fe * 2);
+  w.yg = take(CK * d * 2);
+  w.hs = take((size_t)C * Fs * 2);
+  w.ys = take((size_t)C * d * 2);
+  w.total = off;
+  return w;
+}
+hipError_t dg_launch_moe_route(const float *logits, int C, int E, int K, int *sel, float *gate,
+                               hipStream_t st);
+hipError_t dg_launch_moe_group(const int *sel, int C, int K, int E, int *off, int *perm, int *pos,
+                               int *nact, hipStream_t st);
+hipError_t dg_launch_moe_combine(const u16 *Yg, const u16 *Ys, const float *gate, const int *pos,
+                                 int C, int K, int d, u16 *Y, hipStream_t st);
 hipError_t dg_launch_xgather(const int *tokens, const u16 *E, const u16 *z, int V, int M, int K,
                              u16 *X, int *status, hipStream_t st);
 

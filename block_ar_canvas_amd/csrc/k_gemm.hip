@@ -51,8 +51,10 @@ DG_DEV void wait_stages(int rem) {
 // Output store modes of a segment (chosen on the host).
 enum { ST_SCALAR = 0, ST_NVEC = 1, ST_MVEC = 2 };
 
-template <bool GATHER>
+// MODE: 0 plain rows of A, 1 embedding gather E[tokens[m]], 2 grouped by expert.
+template <int MODE>
 __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
+  constexpr bool GATHER = MODE == 1;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -62,11 +64,33 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
   const int total = gridDim.x;
   int idx = blockIdx.x;
   if ((total & 7) == 0 && ((total >> 3) % MB) == 0) idx = (idx & 7) * (total >> 3) + (idx >> 3);
-  const int mb = idx % MB, nbg = idx / MB;
+  int mb = idx % MB, nbg = idx / MB;
+  const u16 *Wsg = nullptr;
+  int mstore = 0;
+  int64_t orow = 0;                                  // output row of local row 0
+  const int *grows = nullptr;
+  int glen = 0;
+  if (MODE == 2) {
+    const int NB = (a.seg[0].N + BN - 1) / BN;
+    const int e = idx / (MB * NB), r = idx % (MB * NB);
+    mb = r % MB;
+    nbg = r / MB;
+    const int o0 = a.g_off[e];
+    glen = a.g_off[e + 1] - o0;
+    if (mb * BM >= glen) return;                     // whole workgroup: nothing to do
+    Wsg = a.seg[0].W + (int64_t)e * a.seg[0].N * a.K;
+    mstore = glen;
+    orow = o0;
+    grows = a.g_perm ? a.g_perm + o0 : nullptr;
+  }
   int si = 0;
   for (int s = 1; s < a.nseg; ++s)
     if (nbg >= a.seg[s].nblk0) si = s;
   const GemmSeg &sg = a.seg[si];
+  if (MODE != 2) {
+    Wsg = sg.W;
+    mstore = sg.m_store;
+  }
   const int nb0 = (nbg - sg.nblk0) * BN, m0 = mb * BM;
   const int K = a.K;
   const int nst = (K + BK - 1) / BK;
@@ -80,7 +104,13 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
     const int R = 8 * wave + 4 * j + (lane >> 4);
     lchunk[j] = (lane & 15) ^ (R & 15);
     const int n = min(nb0 + R, sg.N - 1);
-    wrow[j] = sg.W + (int64_t)n * K;
+    wrow[j] = Wsg + (int64_t)n * K;
+    if (MODE == 2) {
+      const int m = min(m0 + R, glen - 1);
+      const int row = grows ? grows[m] : (int)orow + m;
+      xrow[j] = a.A + (int64_t)row * K;
+      continue;
+    }
     const int m = min(m0 + R, a.M - 1);
     if (GATHER) {
       int tok = a.tokens[m];
@@ -144,6 +174,17 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
     if (a.gelu) s = 0.5f * s * (1.0f + erff(s * 0.70710678118654752f));
     v[r] = s;
   }
+  if (a.out32) {                                     // fp32 output, row-major
+    const int m = m0 + (q >> 1) * 32 + l32;
+    if (m < mstore) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int n = nb0 + (q & 1) * 32 + acc_row(rb + r, h);
+        if (n < sg.N) a.out32[(int64_t)(orow + m) * a.ld32 + n] = v[r];
+      }
+    }
+    return;
+  }
   __syncthreads();
   u16 *ot = (u16 *)smem;   // [64 m][OPITCH] bf16
   const int ml = (q >> 1) * 32 + l32;
@@ -152,18 +193,19 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
   __syncthreads();
 
   const int mode = a.store_mode[si];
+  u16 *const outp = sg.out + orow * sg.sm;
   if (mode == ST_NVEC) {
     const int row = tid >> 3, c8 = (tid & 7) * 8;
     const int m = m0 + row, n = nb0 + c8;
-    if (m < sg.m_store && n < sg.N)
-      *(uint4 *)(sg.out + (int64_t)m * sg.sm + (int64_t)(n / sg.seg) * sg.sg +
+    if (m < mstore && n < sg.N)
+      *(uint4 *)(outp + (int64_t)m * sg.sm + (int64_t)(n / sg.seg) * sg.sg +
                  (int64_t)(n % sg.seg) * sg.se) = *(const uint4 *)(ot + row * OPITCH + c8);
   } else if (mode == ST_MVEC) {
     const int col = tid >> 3, r8 = (tid & 7) * 8;
     const int m = m0 + r8, n = nb0 + col;
-    if (n < sg.N && m + 8 > sg.m_store) {
-      for (int i = 0; i < 8 && m + i < sg.m_store; ++i)
-        sg.out[(int64_t)(m + i) + (int64_t)(n / sg.seg) * sg.sg + (int64_t)(n % sg.seg) * sg.se] =
+    if (n < sg.N && m + 8 > mstore) {
+      for (int i = 0; i < 8 && m + i < mstore; ++i)
+        outp[(int64_t)(m + i) + (int64_t)(n / sg.seg) * sg.sg + (int64_t)(n % sg.seg) * sg.se] =
             ot[(r8 + i) * OPITCH + col];
     } else if (n < sg.N) {
       uint32_t w4[4];
@@ -171,18 +213,18 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
       for (int i = 0; i < 4; ++i)
         w4[i] = (uint32_t)ot[(r8 + 2 * i) * OPITCH + col] |
                 ((uint32_t)ot[(r8 + 2 * i + 1) * OPITCH + col] << 16);
-      *(uint4 *)(sg.out + (int64_t)m + (int64_t)(n / sg.seg) * sg.sg + (int64_t)(n % sg.seg) * sg.se) =
+      *(uint4 *)(outp + (int64_t)m + (int64_t)(n / sg.seg) * sg.sg + (int64_t)(n % sg.seg) * sg.se) =
           make_uint4(w4[0], w4[1], w4[2], w4[3]);
     }
   } else {
     const int row = tid >> 3, c8 = (tid & 7) * 8;
     const int m = m0 + row;
-    if (m < sg.m_store) {
+    if (m < mstore) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int n = nb0 + c8 + i;
         if (n < sg.N)
-          sg.out[(int64_t)m * sg.sm + (int64_t)(n / sg.seg) * sg.sg + (int64_t)(n % sg.seg) * sg.se] =
+          outp[(int64_t)m * sg.sm + (int64_t)(n / sg.seg) * sg.sg + (int64_t)(n % sg.seg) * sg.se] =
               ot[row * OPITCH + c8 + i];
       }
     }
@@ -226,10 +268,13 @@ int store_mode(const GemmSeg &s) {
 hipError_t dg_launch_gemm(const GemmArgs &a0, hipStream_t st) {
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<false>,
+    hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<0>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, SMEM);
     if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void *)gemm_kernel<true>,
+      e = hipFuncSetAttribute((const void *)gemm_kernel<1>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, SMEM);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void *)gemm_kernel<2>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, SMEM);
     if (e != hipSuccess) return e;
     attr = true;
@@ -244,11 +289,14 @@ hipError_t dg_launch_gemm(const GemmArgs &a0, hipStream_t st) {
     a.store_mode[s] = store_mode(a.seg[s]);
   }
   const int MB = (mmax + BM - 1) / BM;
-  const dim3 grid(nblk * MB);
-  if (a.A)
-    hipLaunchKernelGGL(gemm_kernel<false>, grid, dim3(512), SMEM, st, a, MB);
-  else
-    hipLaunchKernelGGL(gemm_kernel<true>, grid, dim3(512), SMEM, st, a, MB);
+  if (a.g_off) {                                     // grouped: one segment, g_E groups
+    const dim3 grid(a.g_E * nblk * MB);
+    hipLaunchKernelGGL(gemm_kernel<2>, grid, dim3(512), SMEM, st, a, MB);
+  } else if (a.A) {
+    hipLaunchKernelGGL(gemm_kernel<0>, dim3(nblk * MB), dim3(512), SMEM, st, a, MB);
+  } else {
+    hipLaunchKernelGGL(gemm_kernel<1>, dim3(nblk * MB), dim3(512), SMEM, st, a, MB);
+  }
   return hipGetLastError();
 }
 

@@ -38,6 +38,7 @@ __all__ = [
 TAG_E, TAG_WQ, TAG_WK, TAG_WV, TAG_WO, TAG_W1, TAG_W2 = 1, 2, 3, 4, 5, 6, 7
 TAG_KP, TAG_VP = 8, 9
 TAG_TARGET, TAG_NOISE = 10, 11
+TAG_MOE_X, TAG_MOE_WR, TAG_MOE_W1, TAG_MOE_W2, TAG_MOE_W1S, TAG_MOE_W2S = 12, 13, 14, 15, 16, 17
 
 # Large tensors are drawn in independent row blocks of this many elements so that
 # generation can be chunked; the block index is part of the stream key.
@@ -159,6 +160,20 @@ def prefix_kv(cfg: Config, Pcap: int | None = None, request: int = 0):
         K[:, :cfg.P0] = gaussian_bf16(cfg.seed, TAG_KP + off, (cfg.Hkv, cfg.P0, cfg.hd), 1.0)
         V[:, :cfg.P0] = gaussian_bf16(cfg.seed, TAG_VP + off, (cfg.Hkv, cfg.P0, cfg.hd), 1.0)
     return K, V
+
+
+def moe_inputs(C: int, d: int, E: int, K: int, Fe: int, Fs: int, seed: int) -> dict:
+    """Canvas MoE FFN stand-in weights and activations (bf16 bits): X ~ N(0, 1) rows, every
+    weight N(0, 1/fan_in). Layouts: Wr [E, d], W1 [E, Fe, d], W2 [E, d, Fe], W1s [Fs, d],
+    W2s [d, Fs]. K (experts per token) is not used for drawing."""
+    return {
+        "X": gaussian_bf16(seed, TAG_MOE_X, (C, d), 1.0),
+        "Wr": gaussian_bf16(seed, TAG_MOE_WR, (E, d), d ** -0.5),
+        "W1": gaussian_bf16(seed, TAG_MOE_W1, (E, Fe, d), d ** -0.5),
+        "W2": gaussian_bf16(seed, TAG_MOE_W2, (E, d, Fe), Fe ** -0.5),
+        "W1s": gaussian_bf16(seed, TAG_MOE_W1S, (Fs, d), d ** -0.5),
+        "W2s": gaussian_bf16(seed, TAG_MOE_W2S, (d, Fs), Fs ** -0.5),
+    }
 
 
 def targets(cfg: Config, canvas: int) -> np.ndarray:

@@ -231,6 +231,24 @@ dg_status dg_prefill_block(dg_ctx ctx, const dg_dims *dims, const int32_t *token
                            const dg_bf16 *Wv, const dg_bf16 *Wo, dg_bf16 *Kp, dg_bf16 *Vt,
                            int64_t P, int64_t Pcap, void *ws, dg_bf16 *A, int64_t *P_out);
 
+/* Canvas MoE FFN (Technical Report page, "Prerequisites", mixture of experts: 8 of 128
+ * experts plus one shared expert per token, about 84 distinct experts per 256-token
+ * canvas; "Text diffusion models" survey, sections 11 and 13: router top-k, expert GEMM,
+ * token permutation). For every row x of X:
+ *   router logits r = x Wr^T (float32); the K experts with the largest logits (ties to the
+ *   lower expert id) with gates g = softmax of those K logits;
+ *   y = bf16( sum_k g_k * bf16(W2_e GELU_erf(W1_e x)) + bf16(W2s GELU_erf(W1s x)) ),
+ *   each expert's hidden layer rounded to bf16 as well (the self-conditioning FFW's form).
+ * X [C, d]; Wr [E, d]; W1 [E][Fe][d]; W2 [E][d][Fe]; W1s [Fs, d]; W2s [d, Fs]; Y [C, d]
+ * output; n_active (device, optional) = the number of distinct experts used. The
+ * workspace holds dg_moe_workspace_bytes(m, C) bytes. DG_ERR_SHAPE unless d, Fe, Fs are
+ * positive multiples of 32, 1 <= K <= min(E, 32), E <= 256, C <= 1024 and C * K <= 8192. */
+typedef struct { int32_t d, E, K, Fe, Fs; } dg_moe_dims;
+size_t dg_moe_workspace_bytes(const dg_moe_dims *m, int32_t C);
+dg_status dg_moe_ffn(dg_ctx ctx, const dg_moe_dims *m, int32_t C, const dg_bf16 *X,
+                     const dg_bf16 *Wr, const dg_bf16 *W1, const dg_bf16 *W2, const dg_bf16 *W1s,
+                     const dg_bf16 *W2s, void *ws, dg_bf16 *Y, int32_t *n_active);
+
 /* Commit (Technical Report page, "Method steps" (5); tutorial chapter "DiffusionGemma",
  * KV-cache write timing): appends the finalized block's keys and values at token
  * positions [P, P + C) of every KV head: K = bf16(E[tokens] Wk^T), V = bf16(E[tokens]
