@@ -43,6 +43,7 @@ def parse():
     ap.add_argument("--cpu-steps", type=int, default=1, help="oracle steps timed for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batched", action="store_true", help="skip the batched-canvas lines")
+    ap.add_argument("--no-moe", action="store_true", help="skip the canvas MoE FFN line")
     ap.add_argument("--no-long-prefix", action="store_true",
                     help="skip the isolated attention call over a 262144-token prefix")
     ap.add_argument("--no-chain", action="store_true",
@@ -234,6 +235,8 @@ def main():
     if not args.no_chain:
         result["chain8"] = chain(ctx)
         result["chain8_prefill"] = chain(ctx, commit="prefill", rope_base=10000.0)
+    if not args.no_moe:
+        result["moe_ffn"] = moe_ffn(ctx, cfg, args.roofline_reps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, W, Kp, args.cpu_steps)
     print(json.dumps(result))
@@ -359,6 +362,45 @@ def variant_canvas(ctx, cfg, Wd, Hd, rule="entropy", draw="argmax"):
     sec = e0.elapsed_time(e1) * 1e-3
     return {"rule": rule, "draw": draw, "steps": steps, "ms_per_step": round(1e3 * sec / steps, 4),
             "canvas_tokens_per_s": round(cfg.C / sec, 1)}
+
+
+def moe_ffn(ctx, cfg, reps):
+    """The canvas MoE FFN on one canvas at the workload's width: 128 experts, 8 routed per
+    token plus a shared expert, expert width 512, shared width 1024 (stand-in sizes;
+    random routing, so about every expert is used, where the pages report about 84 on
+    real text). Reports the call time and the weight bytes it streams (router, the
+    experts used, the shared expert) as achieved GB/s."""
+    import torch
+
+    import block_ar_canvas_amd as dg
+    import dg_inputs as di
+    C, d, E, K, Fe, Fs = cfg.C, cfg.d, 128, 8, 512, 1024
+    dev = torch.device("cuda:0")
+    inp = di.moe_inputs(C, d, E, K, Fe, Fs, seed=61)
+    dv = {k: _bf(v, dev) for k, v in inp.items()}
+    del inp
+    md = dg.MoeDims(d, E, K, Fe, Fs)
+    ws = torch.empty(dg.moe_workspace_bytes(md, C), dtype=torch.uint8, device=dev)
+    Y = torch.empty(C, d, dtype=torch.bfloat16, device=dev)
+    nact = torch.zeros(1, dtype=torch.int32, device=dev)
+    args = (md, dv["X"], dv["Wr"], dv["W1"], dv["W2"], dv["W1s"], dv["W2s"], ws, Y, nact)
+    for _ in range(5):
+        ctx.moe_ffn(*args)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = max(reps, 10)
+    e0.record(stream)
+    for _ in range(n):
+        ctx.moe_ffn(*args)
+    e1.record(stream)
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    na = int(nact.item())
+    wbytes = 2 * (E * d + na * 2 * Fe * d + 2 * Fs * d)
+    return {"workload": f"canvas MoE FFN: C={C} d={d} experts={E} top-{K} Fe={Fe} shared Fs={Fs}",
+            "ms_per_call": round(ms, 4), "experts_used": na,
+            "weight_bytes": wbytes, "achieved_GBs": round(wbytes / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(wbytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4)}
 
 
 def chain(ctx, commit="projection", rope_base=0.0):

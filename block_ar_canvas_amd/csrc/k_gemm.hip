@@ -47,6 +47,17 @@ DG_DEV void wait_stages(int rem) {
     default: dma_wait<8>(); break;
   }
 }
+// The same for a wave that issues ops (2, 3 or 4) copies per stage (rem <= 2).
+DG_DEV void wait_stages_ops(int ops, int rem) {
+  switch (ops * rem) {
+    case 0: dma_wait<0>(); break;
+    case 2: dma_wait<2>(); break;
+    case 3: dma_wait<3>(); break;
+    case 4: dma_wait<4>(); break;
+    case 6: dma_wait<6>(); break;
+    default: dma_wait<8>(); break;
+  }
+}
 
 // Output store modes of a segment (chosen on the host).
 enum { ST_SCALAR = 0, ST_NVEC = 1, ST_MVEC = 2 };
@@ -124,6 +135,15 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
     }
   }
   const uint32_t lbase = lds_addr(smem);
+  // Grouped mode: activation rows at or past the group's size are never stored, so a
+  // copy instruction whose four rows all lie there is skipped (wave-uniform), and the
+  // upper 32-row half of the MFMAs is skipped for groups of at most 32 rows.
+  const int mrows = MODE == 2 ? glen - m0 : BM;
+  bool xcopy[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) xcopy[j] = 8 * wave + 4 * j < mrows;
+  const int ops = 2 + (xcopy[0] ? 1 : 0) + (xcopy[1] ? 1 : 0);
+  const bool upper = mrows > 32;
   auto issue = [&](int i) {
     const int k0 = i * BK;
     const uint32_t wb = lbase + (uint32_t)((i % NS) * STAGE);
@@ -132,14 +152,15 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
       const int k = min(k0 + 8 * lchunk[j], K - 8);   // chunks past K: any valid data
       const uint32_t off = (uint32_t)((8 * wave + 4 * j) * RB);
       dma16(wrow[j] + k, wb + off);
-      dma16(xrow[j] + k, wb + TILE + off);
+      if (MODE != 2 || xcopy[j]) dma16(xrow[j] + k, wb + TILE + off);
     }
   };
 
   f32x16_t acc[4] = {};
   for (int i = 0; i < NS - 1 && i < nst; ++i) issue(i);
   for (int i = 0; i < nst; ++i) {
-    wait_stages(min(nst - 1 - i, NS - 2));
+    if (MODE == 2) wait_stages_ops(ops, min(nst - 1 - i, NS - 2));
+    else wait_stages(min(nst - 1 - i, NS - 2));
     __syncthreads();
     if (i + NS - 1 < nst) issue(i + NS - 1);
     if (i * BK + 16 * wave < K) {
@@ -148,11 +169,13 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
       const u32x4_t a0 = *(const u32x4_t *)(Ws + swz(l32, c));
       const u32x4_t a1 = *(const u32x4_t *)(Ws + swz(32 + l32, c));
       const u32x4_t b0 = *(const u32x4_t *)(Xs + swz(l32, c));
-      const u32x4_t b1 = *(const u32x4_t *)(Xs + swz(32 + l32, c));
       acc[0] = mfma_32x32x16(a0, b0, acc[0]);
       acc[1] = mfma_32x32x16(a1, b0, acc[1]);
-      acc[2] = mfma_32x32x16(a0, b1, acc[2]);
-      acc[3] = mfma_32x32x16(a1, b1, acc[3]);
+      if (MODE != 2 || upper) {
+        const u32x4_t b1 = *(const u32x4_t *)(Xs + swz(32 + l32, c));
+        acc[2] = mfma_32x32x16(a0, b1, acc[2]);
+        acc[3] = mfma_32x32x16(a1, b1, acc[3]);
+      }
     }
   }
 

@@ -11,8 +11,9 @@
 //   from the router GEMM) and counts the experts that beat it (larger logit, or equal
 //   with a lower id); rank < K selects it. Gates: softmax over the K selected logits.
 // moe_group_kernel: one workgroup; per expert, the number of tokens routed to it, the
-//   exclusive offsets, the token list in token order (a counting sort: deterministic),
-//   and for every (token, rank) the row of its expert output in grouped order.
+//   exclusive offsets, the token list in token order (from per-expert token bitmasks:
+//   deterministic), and for every (token, rank) the row of its expert output in grouped
+//   order.
 // moe_combine_kernel: y[t] = bf16(sum over ranks k of gate[t][k] * Yg[pos[t][k]] + Ys[t]),
 //   float32, ranks in order.
 #include <float.h>
@@ -53,19 +54,28 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float *logits, int
   }
 }
 
+// Token sets as bitmasks: mask[e] holds bit t when token t routes to expert e (LDS
+// atomic OR, so the result does not depend on the order of the updates). A token's row in
+// its expert's group is the expert's offset plus the number of set bits below t: the
+// grouped order is token order within each expert, the same on every run.
 __global__ __launch_bounds__(256) void moe_group_kernel(const int *sel, int C, int K, int E, int *off,
                                                         int *perm, int *pos, int *nact) {
-  extern __shared__ int lsel[];                      // [C * K]
+  extern __shared__ uint32_t mask[];                 // [E][W], W = C / 32 rounded up
   __shared__ int loff[257];
-  const int tid = threadIdx.x, n = C * K;
-  for (int i = tid; i < n; i += 256) lsel[i] = sel[i];
+  const int tid = threadIdx.x, n = C * K, W = (C + 31) / 32;
+  for (int i = tid; i < E * W; i += 256) mask[i] = 0u;
+  __syncthreads();
+  for (int i = tid; i < n; i += 256) {
+    const int t = i / K, e = sel[i];
+    atomicOr(&mask[e * W + (t >> 5)], 1u << (t & 31));
+  }
   __syncthreads();
   int c = 0;
   if (tid < E)
-    for (int i = 0; i < n; ++i) c += lsel[i] == tid ? 1 : 0;
+    for (int w = 0; w < W; ++w) c += __popc(mask[tid * W + w]);
   loff[tid] = c;
   __syncthreads();
-  if (tid == 0) {
+  if (tid == 0) {                                    // at most 256 experts: a short walk
     int run = 0, na = 0;
     for (int e = 0; e < E; ++e) {
       const int ce = loff[e];
@@ -78,14 +88,14 @@ __global__ __launch_bounds__(256) void moe_group_kernel(const int *sel, int C, i
     if (nact) nact[0] = na;
   }
   __syncthreads();
-  if (tid < E) {
-    int p = loff[tid];
-    for (int i = 0; i < n; ++i)
-      if (lsel[i] == tid) {
-        perm[p] = i / K;
-        pos[i] = p;
-        ++p;
-      }
+  for (int i = tid; i < n; i += 256) {
+    const int t = i / K, e = sel[i];
+    const uint32_t *m = mask + e * W;
+    int p = loff[e];
+    for (int w = 0; w < (t >> 5); ++w) p += __popc(m[w]);
+    p += __popc(m[t >> 5] & ((1u << (t & 31)) - 1u));
+    perm[p] = t;
+    pos[i] = p;
   }
 }
 
@@ -123,8 +133,8 @@ hipError_t dg_launch_moe_route(const float *logits, int C, int E, int K, int *se
 
 hipError_t dg_launch_moe_group(const int *sel, int C, int K, int E, int *off, int *perm, int *pos,
                                int *nact, hipStream_t st) {
-  hipLaunchKernelGGL(moe_group_kernel, dim3(1), dim3(256), (size_t)C * K * 4, st, sel, C, K, E, off,
-                     perm, pos, nact);
+  hipLaunchKernelGGL(moe_group_kernel, dim3(1), dim3(256), (size_t)E * ((C + 31) / 32) * 4, st, sel, C,
+                     K, E, off, perm, pos, nact);
   return hipGetLastError();
 }
 
