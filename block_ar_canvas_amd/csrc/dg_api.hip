@@ -277,7 +277,7 @@ dg_status dg_moe_ffn(dg_ctx ctx, const dg_moe_dims *m, int32_t C, const dg_bf16 
   const DgMoeWs w = dg_moe_ws_layout(C, m->d, m->E, m->K, m->Fe, m->Fs);
   float *logits = ws_at<float>(ws, w.logits), *gate = ws_at<float>(ws, w.gate);
   int *sel = ws_at<int>(ws, w.sel), *off = ws_at<int>(ws, w.off);
-  int *perm = ws_at<int>(ws, w.perm), *pos = ws_at<int>(ws, w.pos);
+  int *perm = ws_at<int>(ws, w.perm), *pos = ws_at<int>(ws, w.pos), *tiles = ws_at<int>(ws, w.tiles);
   u16 *h = ws_at<u16>(ws, w.h), *yg = ws_at<u16>(ws, w.yg), *hs = ws_at<u16>(ws, w.hs);
   u16 *ys = ws_at<u16>(ws, w.ys);
 
@@ -292,30 +292,15 @@ dg_status dg_moe_ffn(dg_ctx ctx, const dg_moe_dims *m, int32_t C, const dg_bf16 
   gr.ld32 = m->E;
   hipError_t e = dg_launch_gemm(gr, ctx->stream);
   if (e == hipSuccess) e = dg_launch_moe_route(logits, C, m->E, m->K, sel, gate, ctx->stream);
-  if (e == hipSuccess) e = dg_launch_moe_group(sel, C, m->K, m->E, off, perm, pos, n_active, ctx->stream);
+  if (e == hipSuccess) e = dg_launch_moe_group(sel, C, m->K, m->E, off, perm, pos, n_active, tiles, ctx->stream);
   if (e != hipSuccess) return hip_fail(ctx, e, "dg_moe_ffn(route)");
 
   // routed experts: grouped GEMMs, hidden = GELU(X W1_e^T), out = hidden W2_e^T
-  GemmArgs g1{};
-  g1.M = C;
-  g1.K = m->d;
-  g1.A = X;
-  g1.gelu = 1;
-  g1.nseg = 1;
-  g1.seg[0] = GemmSeg{W1, m->Fe, h, m->Fe, 0, 1, INT_MAX, C, 0};
-  g1.g_E = m->E;
-  g1.g_off = off;
-  g1.g_perm = perm;
-  e = dg_launch_gemm(g1, ctx->stream);
-  GemmArgs g2{};
-  g2.M = C;
-  g2.K = m->Fe;
-  g2.A = h;
-  g2.nseg = 1;
-  g2.seg[0] = GemmSeg{W2, m->d, yg, m->d, 0, 1, INT_MAX, C, 0};
-  g2.g_E = m->E;
-  g2.g_off = off;
-  if (e == hipSuccess) e = dg_launch_gemm(g2, ctx->stream);
+  const int max_tiles = dg_moe_max_tiles(C, m->E, m->K);
+  const MoeGemmArgs g1{X, W1, off, perm, tiles, h, m->Fe, m->d, m->Fe, 1, max_tiles};
+  e = dg_launch_moe_expert(g1, ctx->stream);
+  const MoeGemmArgs g2{h, W2, off, nullptr, tiles, yg, m->d, m->Fe, m->d, 0, max_tiles};
+  if (e == hipSuccess) e = dg_launch_moe_expert(g2, ctx->stream);
   if (e != hipSuccess) return hip_fail(ctx, e, "dg_moe_ffn(experts)");
 
   // shared expert

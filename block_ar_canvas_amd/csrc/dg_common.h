@@ -244,12 +244,21 @@ struct DgMoeWs {
   size_t off;      // group offsets int32 [E + 1]
   size_t perm;     // tokens in grouped order int32 [C * K]
   size_t pos;      // grouped row of (token, rank) int32 [C * K]
+  size_t tiles;    // expert GEMM work list int32: count, then (expert | row block << 16)
   size_t h;        // expert hidden bf16 [C * K][Fe] (grouped order)
   size_t yg;       // expert outputs bf16 [C * K][d] (grouped order)
   size_t hs;       // shared hidden bf16 [C][Fs]
   size_t ys;       // shared output bf16 [C][d]
   size_t total;
 };
+// Rows per expert GEMM tile, and the most tiles a routing can produce: every non-empty
+// group has ceil(rows / MOE_TM) <= rows / MOE_TM + 1 tiles, and at most min(E, C * K)
+// groups are non-empty.
+constexpr int MOE_TM = 64;
+static inline int dg_moe_max_tiles(int C, int E, int K) {
+  const int ck = C * K;
+  return (E < ck ? E : ck) + ck / MOE_TM;
+}
 static inline DgMoeWs dg_moe_ws_layout(int C, int d, int E, int K, int Fe, int Fs) {
   DgMoeWs w;
   size_t off = 0;
@@ -265,6 +274,7 @@ static inline DgMoeWs dg_moe_ws_layout(int C, int d, int E, int K, int Fe, int F
   w.off = take((size_t)(E + 1) * 4);
   w.perm = take(CK * 4);
   w.pos = take(CK * 4);
+  w.tiles = take((size_t)(1 + dg_moe_max_tiles(C, E, K)) * 4);
   w.h = take(CK * Fe * 2);
   w.yg = take(CK * d * 2);
   w.hs = take((size_t)C * Fs * 2);
@@ -275,7 +285,17 @@ static inline DgMoeWs dg_moe_ws_layout(int C, int d, int E, int K, int Fe, int F
 hipError_t dg_launch_moe_route(const float *logits, int C, int E, int K, int *sel, float *gate,
                                hipStream_t st);
 hipError_t dg_launch_moe_group(const int *sel, int C, int K, int E, int *off, int *perm, int *pos,
-                               int *nact, hipStream_t st);
+                               int *nact, int *tiles, hipStream_t st);
+// Grouped expert GEMM: for each listed tile (expert e, rows [m0, m0 + 64) of its group),
+// Y[off[e] + m][n] = act(sum_k X[row][k] W[e][n][k]), row = perm[off[e] + m] (perm
+// non-NULL) or off[e] + m. N, K multiples of 32; Y row stride ldY.
+struct MoeGemmArgs {
+  const u16 *X, *W;
+  const int *off, *perm, *tiles;
+  u16 *Y;
+  int N, K, ldY, gelu, max_tiles;
+};
+hipError_t dg_launch_moe_expert(const MoeGemmArgs &a, hipStream_t st);
 hipError_t dg_launch_moe_combine(const u16 *Yg, const u16 *Ys, const float *gate, const int *pos,
                                  int C, int K, int d, u16 *Y, hipStream_t st);
 hipError_t dg_launch_xgather(const int *tokens, const u16 *E, const u16 *z, int V, int M, int K,

@@ -23,6 +23,9 @@ CASES = {
     "top1": dict(C=64, d=128, E=8, K=1, Fe=64, Fs=64),
     "canvas": dict(C=256, d=256, E=128, K=8, Fe=64, Fs=128),
     "gemma_width": dict(C=256, d=2048, E=128, K=8, Fe=512, Fs=1024),
+    # few experts: groups of ~150 rows span three 64-row tiles; d and Fe leave k tails
+    # past the last 128-deep chunk and output widths with idle waves
+    "skewed": dict(C=300, d=160, E=4, K=2, Fe=96, Fs=64),
 }
 
 
