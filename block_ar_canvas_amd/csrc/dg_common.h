@@ -22,6 +22,7 @@
 typedef uint16_t u16;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 #define DG_DEV __device__ __forceinline__
@@ -227,12 +228,6 @@ struct GemmArgs {
   // fp32 output (segment 0 only): out32[m * ld32 + n] = D[m][n] instead of bf16 stores
   float *out32;
   int ld32;
-  // Grouped by expert (segment 0 only): g_E groups; group e has rows
-  // [g_off[e], g_off[e+1]) of the output and its own weights seg[0].W + e * N * K. Its
-  // activation rows are A[g_perm[g_off[e] + m]] (g_perm non-NULL) or A[g_off[e] + m].
-  // M is the largest possible group size; blocks past a group's size do nothing.
-  int g_E;
-  const int *g_off, *g_perm;
 };
 hipError_t dg_launch_gemm(const GemmArgs &a, hipStream_t st);
 

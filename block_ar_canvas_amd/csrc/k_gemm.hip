@@ -47,25 +47,12 @@ DG_DEV void wait_stages(int rem) {
     default: dma_wait<8>(); break;
   }
 }
-// The same for a wave that issues ops (2, 3 or 4) copies per stage (rem <= 2).
-DG_DEV void wait_stages_ops(int ops, int rem) {
-  switch (ops * rem) {
-    case 0: dma_wait<0>(); break;
-    case 2: dma_wait<2>(); break;
-    case 3: dma_wait<3>(); break;
-    case 4: dma_wait<4>(); break;
-    case 6: dma_wait<6>(); break;
-    default: dma_wait<8>(); break;
-  }
-}
 
 // Output store modes of a segment (chosen on the host).
 enum { ST_SCALAR = 0, ST_NVEC = 1, ST_MVEC = 2 };
 
-// MODE: 0 plain rows of A, 1 embedding gather E[tokens[m]], 2 grouped by expert.
-template <int MODE>
+template <bool GATHER>
 __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
-  constexpr bool GATHER = MODE == 1;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -75,33 +62,11 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
   const int total = gridDim.x;
   int idx = blockIdx.x;
   if ((total & 7) == 0 && ((total >> 3) % MB) == 0) idx = (idx & 7) * (total >> 3) + (idx >> 3);
-  int mb = idx % MB, nbg = idx / MB;
-  const u16 *Wsg = nullptr;
-  int mstore = 0;
-  int64_t orow = 0;                                  // output row of local row 0
-  const int *grows = nullptr;
-  int glen = 0;
-  if (MODE == 2) {
-    const int NB = (a.seg[0].N + BN - 1) / BN;
-    const int e = idx / (MB * NB), r = idx % (MB * NB);
-    mb = r % MB;
-    nbg = r / MB;
-    const int o0 = a.g_off[e];
-    glen = a.g_off[e + 1] - o0;
-    if (mb * BM >= glen) return;                     // whole workgroup: nothing to do
-    Wsg = a.seg[0].W + (int64_t)e * a.seg[0].N * a.K;
-    mstore = glen;
-    orow = o0;
-    grows = a.g_perm ? a.g_perm + o0 : nullptr;
-  }
+  const int mb = idx % MB, nbg = idx / MB;
   int si = 0;
   for (int s = 1; s < a.nseg; ++s)
     if (nbg >= a.seg[s].nblk0) si = s;
   const GemmSeg &sg = a.seg[si];
-  if (MODE != 2) {
-    Wsg = sg.W;
-    mstore = sg.m_store;
-  }
   const int nb0 = (nbg - sg.nblk0) * BN, m0 = mb * BM;
   const int K = a.K;
   const int nst = (K + BK - 1) / BK;
@@ -115,13 +80,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
     const int R = 8 * wave + 4 * j + (lane >> 4);
     lchunk[j] = (lane & 15) ^ (R & 15);
     const int n = min(nb0 + R, sg.N - 1);
-    wrow[j] = Wsg + (int64_t)n * K;
-    if (MODE == 2) {
-      const int m = min(m0 + R, glen - 1);
-      const int row = grows ? grows[m] : (int)orow + m;
-      xrow[j] = a.A + (int64_t)row * K;
-      continue;
-    }
+    wrow[j] = sg.W + (int64_t)n * K;
     const int m = min(m0 + R, a.M - 1);
     if (GATHER) {
       int tok = a.tokens[m];
@@ -135,15 +94,6 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
     }
   }
   const uint32_t lbase = lds_addr(smem);
-  // Grouped mode: activation rows at or past the group's size are never stored, so a
-  // copy instruction whose four rows all lie there is skipped (wave-uniform), and the
-  // upper 32-row half of the MFMAs is skipped for groups of at most 32 rows.
-  const int mrows = MODE == 2 ? glen - m0 : BM;
-  bool xcopy[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) xcopy[j] = 8 * wave + 4 * j < mrows;
-  const int ops = 2 + (xcopy[0] ? 1 : 0) + (xcopy[1] ? 1 : 0);
-  const bool upper = mrows > 32;
   auto issue = [&](int i) {
     const int k0 = i * BK;
     const uint32_t wb = lbase + (uint32_t)((i % NS) * STAGE);
@@ -152,15 +102,14 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
       const int k = min(k0 + 8 * lchunk[j], K - 8);   // chunks past K: any valid data
       const uint32_t off = (uint32_t)((8 * wave + 4 * j) * RB);
       dma16(wrow[j] + k, wb + off);
-      if (MODE != 2 || xcopy[j]) dma16(xrow[j] + k, wb + TILE + off);
+      dma16(xrow[j] + k, wb + TILE + off);
     }
   };
 
   f32x16_t acc[4] = {};
   for (int i = 0; i < NS - 1 && i < nst; ++i) issue(i);
   for (int i = 0; i < nst; ++i) {
-    if (MODE == 2) wait_stages_ops(ops, min(nst - 1 - i, NS - 2));
-    else wait_stages(min(nst - 1 - i, NS - 2));
+    wait_stages(min(nst - 1 - i, NS - 2));
     __syncthreads();
     if (i + NS - 1 < nst) issue(i + NS - 1);
     if (i * BK + 16 * wave < K) {
@@ -169,13 +118,11 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
       const u32x4_t a0 = *(const u32x4_t *)(Ws + swz(l32, c));
       const u32x4_t a1 = *(const u32x4_t *)(Ws + swz(32 + l32, c));
       const u32x4_t b0 = *(const u32x4_t *)(Xs + swz(l32, c));
+      const u32x4_t b1 = *(const u32x4_t *)(Xs + swz(32 + l32, c));
       acc[0] = mfma_32x32x16(a0, b0, acc[0]);
       acc[1] = mfma_32x32x16(a1, b0, acc[1]);
-      if (MODE != 2 || upper) {
-        const u32x4_t b1 = *(const u32x4_t *)(Xs + swz(32 + l32, c));
-        acc[2] = mfma_32x32x16(a0, b1, acc[2]);
-        acc[3] = mfma_32x32x16(a1, b1, acc[3]);
-      }
+      acc[2] = mfma_32x32x16(a0, b1, acc[2]);
+      acc[3] = mfma_32x32x16(a1, b1, acc[3]);
     }
   }
 
@@ -199,11 +146,11 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
   }
   if (a.out32) {                                     // fp32 output, row-major
     const int m = m0 + (q >> 1) * 32 + l32;
-    if (m < mstore) {
+    if (m < sg.m_store) {
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         const int n = nb0 + (q & 1) * 32 + acc_row(rb + r, h);
-        if (n < sg.N) a.out32[(int64_t)(orow + m) * a.ld32 + n] = v[r];
+        if (n < sg.N) a.out32[(int64_t)m * a.ld32 + n] = v[r];
       }
     }
     return;
@@ -216,19 +163,18 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
   __syncthreads();
 
   const int mode = a.store_mode[si];
-  u16 *const outp = sg.out + orow * sg.sm;
   if (mode == ST_NVEC) {
     const int row = tid >> 3, c8 = (tid & 7) * 8;
     const int m = m0 + row, n = nb0 + c8;
-    if (m < mstore && n < sg.N)
-      *(uint4 *)(outp + (int64_t)m * sg.sm + (int64_t)(n / sg.seg) * sg.sg +
+    if (m < sg.m_store && n < sg.N)
+      *(uint4 *)(sg.out + (int64_t)m * sg.sm + (int64_t)(n / sg.seg) * sg.sg +
                  (int64_t)(n % sg.seg) * sg.se) = *(const uint4 *)(ot + row * OPITCH + c8);
   } else if (mode == ST_MVEC) {
     const int col = tid >> 3, r8 = (tid & 7) * 8;
     const int m = m0 + r8, n = nb0 + col;
-    if (n < sg.N && m + 8 > mstore) {
-      for (int i = 0; i < 8 && m + i < mstore; ++i)
-        outp[(int64_t)(m + i) + (int64_t)(n / sg.seg) * sg.sg + (int64_t)(n % sg.seg) * sg.se] =
+    if (n < sg.N && m + 8 > sg.m_store) {
+      for (int i = 0; i < 8 && m + i < sg.m_store; ++i)
+        sg.out[(int64_t)(m + i) + (int64_t)(n / sg.seg) * sg.sg + (int64_t)(n % sg.seg) * sg.se] =
             ot[(r8 + i) * OPITCH + col];
     } else if (n < sg.N) {
       uint32_t w4[4];
@@ -236,18 +182,18 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
       for (int i = 0; i < 4; ++i)
         w4[i] = (uint32_t)ot[(r8 + 2 * i) * OPITCH + col] |
                 ((uint32_t)ot[(r8 + 2 * i + 1) * OPITCH + col] << 16);
-      *(uint4 *)(outp + (int64_t)m + (int64_t)(n / sg.seg) * sg.sg + (int64_t)(n % sg.seg) * sg.se) =
+      *(uint4 *)(sg.out + (int64_t)m + (int64_t)(n / sg.seg) * sg.sg + (int64_t)(n % sg.seg) * sg.se) =
           make_uint4(w4[0], w4[1], w4[2], w4[3]);
     }
   } else {
     const int row = tid >> 3, c8 = (tid & 7) * 8;
     const int m = m0 + row;
-    if (m < mstore) {
+    if (m < sg.m_store) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int n = nb0 + c8 + i;
         if (n < sg.N)
-          outp[(int64_t)m * sg.sm + (int64_t)(n / sg.seg) * sg.sg + (int64_t)(n % sg.seg) * sg.se] =
+          sg.out[(int64_t)m * sg.sm + (int64_t)(n / sg.seg) * sg.sg + (int64_t)(n % sg.seg) * sg.se] =
               ot[row * OPITCH + c8 + i];
       }
     }
@@ -291,13 +237,10 @@ int store_mode(const GemmSeg &s) {
 hipError_t dg_launch_gemm(const GemmArgs &a0, hipStream_t st) {
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<0>,
+    hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<false>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, SMEM);
     if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void *)gemm_kernel<1>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, SMEM);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void *)gemm_kernel<2>,
+      e = hipFuncSetAttribute((const void *)gemm_kernel<true>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, SMEM);
     if (e != hipSuccess) return e;
     attr = true;
@@ -312,14 +255,11 @@ hipError_t dg_launch_gemm(const GemmArgs &a0, hipStream_t st) {
     a.store_mode[s] = store_mode(a.seg[s]);
   }
   const int MB = (mmax + BM - 1) / BM;
-  if (a.g_off) {                                     // grouped: one segment, g_E groups
-    const dim3 grid(a.g_E * nblk * MB);
-    hipLaunchKernelGGL(gemm_kernel<2>, grid, dim3(512), SMEM, st, a, MB);
-  } else if (a.A) {
-    hipLaunchKernelGGL(gemm_kernel<0>, dim3(nblk * MB), dim3(512), SMEM, st, a, MB);
-  } else {
-    hipLaunchKernelGGL(gemm_kernel<1>, dim3(nblk * MB), dim3(512), SMEM, st, a, MB);
-  }
+  const dim3 grid(nblk * MB);
+  if (a.A)
+    hipLaunchKernelGGL(gemm_kernel<false>, grid, dim3(512), SMEM, st, a, MB);
+  else
+    hipLaunchKernelGGL(gemm_kernel<true>, grid, dim3(512), SMEM, st, a, MB);
   return hipGetLastError();
 }
 

@@ -3,9 +3,9 @@
 // Method (DiffusionGemma Technical Report page, "Prerequisites", mixture of experts: each
 // token uses 8 of 128 experts plus one shared expert, and a 256-token canvas touches
 // about 84 distinct experts where one token touches 8; "Text diffusion models" survey,
-// section 13: router top-k, expert GEMM, token permutation). The expert GEMMs are the
-// grouped mode of gemm_kernel (one workgroup per expert x row block x column block,
-// weights streamed once per expert); the kernels here route, group and combine.
+// section 13: router top-k, expert GEMM, token permutation). The router logits and the
+// shared expert use the plain GEMM; the kernels here route, group, run the routed
+// experts and combine.
 //
 // moe_route_kernel: one workgroup per token; each thread holds one expert's logit (float32,
 //   from the router GEMM) and counts the experts that beat it (larger logit, or equal
@@ -16,9 +16,9 @@
 //   order.
 //   It also lists the work tiles of the expert GEMMs: one entry (expert, 64-row block) per
 //   non-empty row block of every group.
-// moe_expert_kernel: Y[g_off[e] + m] = act(X_e[m] . W[e]^T) for the grouped rows of
+// moe_expert_kernel: Y[off[e] + m] = act(X_e[m] . W[e]^T) for the grouped rows of
 //   expert e. The weights are read once per tile, straight from memory into the MFMA A
-//   operand (each wave owns 32 weight rows); the tile's activation rows (at most 64) are
+//   operands (each wave owns 32 weight rows); the tile's activation rows (at most 64) are
 //   staged per 128-deep k chunk in LDS and shared by the four waves.
 // moe_combine_kernel: y[t] = bf16(sum over ranks k of gate[t][k] * Yg[pos[t][k]] + Ys[t]),
 //   float32, ranks in order.
@@ -122,14 +122,25 @@ __global__ __launch_bounds__(256) void moe_group_kernel(const int *sel, int C, i
 // 32 rows read by one MFMA operand load fall in distinct banks.
 DG_DEV int xslot(int m, int q) { return m * 256 + ((q ^ (m & 15)) << 4); }
 
+DG_DEV f32x4_t mfma_16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
 // One workgroup = 4 waves = 128 weight rows of one tile (expert e, rows [m0, m0 + 64) of
-// its group). Lane (c, h) of a wave: A rows n0 + c, B rows m0 + c (and m0 + 32 + c).
-// MFMA j of a 128-deep chunk covers k [16j, 16j + 16) of it; lane half h holds 8 of them.
+// its group); each wave owns 32 weight rows as two 16-row A operands.
+// v_mfma_f32_16x16x32_bf16: lane l supplies row l % 16 of A (and column l % 16 of B) with
+// 8 k values; the four lane groups g = l / 16 cover the 32 k of a step. Lane group g takes
+// k [32j + 8g, +8) of the chunk in step j for both operands, so one weight load
+// instruction reads 16 rows x 64 contiguous bytes (16 cache lines per KiB; the memory
+// pipeline, not HBM, is what a weight stream with 32 lines per KiB saturates).
+// Accumulator register i of lane l holds D[4(l / 16) + i][l % 16]: four consecutive
+// weight rows of one activation row.
 // Every memory load is unconditional, with row and k addresses clamped into the operands
-// (rows past the group repeat its last row, k past K repeats the last 16 k): the
-// compiler then counts the loads in flight exactly and keeps the next chunk's loads
-// outstanding during the MFMAs. Clamped rows are never stored, and the MFMAs of k steps
-// past K are skipped (a wave-uniform test), so the repeats never reach a result.
+// (rows past the group repeat its last row, k past K repeats the last 32 k), and loads of
+// the chunk after the last read one fixed line: the compiler then counts the loads in
+// flight exactly and keeps the next chunk's loads outstanding during the MFMAs. Clamped
+// rows are never stored, and k steps past K are skipped (a wave-uniform test).
 __global__ __launch_bounds__(256) void moe_expert_kernel(MoeGemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[2][MOE_TM * 256];
   const int NB = (a.N + 127) / 128;
@@ -139,11 +150,14 @@ __global__ __launch_bounds__(256) void moe_expert_kernel(MoeGemmArgs a) {
   const int o0 = a.off[e], mrows = min(MOE_TM, a.off[e + 1] - o0 - m0);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c = lane & 31, h = lane >> 5;
+  const int r16 = lane & 15, g = lane >> 4;
   const int K = a.K, nch = (K + 127) / 128;
   const int n0 = nb * 128 + 32 * wave;
-  const bool upper = mrows > 32;
-  const u16 *wp = a.W + ((int64_t)e * a.N + min(n0 + c, a.N - 1)) * K + 8 * h;
+  const int nbop = (mrows + 15) >> 4;                // B operands (16 rows each) in use
+  const u16 *wp[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+    wp[s] = a.W + ((int64_t)e * a.N + min(n0 + 16 * s + r16, a.N - 1)) * K + 8 * g;
 
   // activation staging: thread t moves 16-byte chunk (t & 15) of rows t/16 + 16q
   const u16 *xr[4];
@@ -155,84 +169,88 @@ __global__ __launch_bounds__(256) void moe_expert_kernel(MoeGemmArgs a) {
   }
   auto xload = [&](int ch, u32x4_t *v) {
     const int k = min(ch * 128 + 8 * (tid & 15), K - 8);
+    const bool real = ch < nch;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = *(const u32x4_t *)(xr[q] + k);
+    for (int q = 0; q < 4; ++q) v[q] = *(const u32x4_t *)(real ? xr[q] + k : a.X);
   };
   auto xstore = [&](int ch, const u32x4_t *v) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) *(u32x4_t *)(xs[ch & 1] + xslot((tid >> 4) + 16 * q, tid & 15)) = v[q];
   };
+  // w[2j + s]: k step j, row half s
   auto wload = [&](int ch, u32x4_t *w) {
+    const bool real = ch < nch;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) w[j] = *(const u32x4_t *)(wp + min(ch * 128 + 16 * j, K - 16));
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        w[2 * j + s] = *(const u32x4_t *)(real ? wp[s] + min(ch * 128 + 32 * j, K - 32) : a.W);
   };
 
-  f32x16_t acc0 = {}, acc1 = {};
+  f32x4_t acc[2][4] = {};
   auto compute = [&](int ch, const u32x4_t *w) {
-    const int nj = min(8, (K - ch * 128) >> 4);
+    if (ch >= nch) return;
+    const int nj = min(4, (K - ch * 128) >> 5);
     const uint8_t *xb = xs[ch & 1];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 4; ++j) {
       if (j < nj) {
-        const u32x4_t b0 = *(const u32x4_t *)(xb + xslot(c, 2 * j + h));
-        acc0 = mfma_32x32x16(w[j], b0, acc0);
-        if (upper) {
-          const u32x4_t b1 = *(const u32x4_t *)(xb + xslot(32 + c, 2 * j + h));
-          acc1 = mfma_32x32x16(w[j], b1, acc1);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          if (b < nbop) {
+            const u32x4_t bv = *(const u32x4_t *)(xb + xslot(16 * b + r16, 4 * j + g));
+            acc[0][b] = mfma_16x16x32(w[2 * j], bv, acc[0][b]);
+            acc[1][b] = mfma_16x16x32(w[2 * j + 1], bv, acc[1][b]);
+          }
         }
       }
     }
   };
 
-  u32x4_t wa[8], wb[8], xv[4];
-  xload(0, xv);
-  wload(0, wa);
-  xstore(0, xv);
+  // Chunk ch is computed from weight registers W[ch & 1] and LDS buffer ch & 1; step ch
+  // first loads chunk ch + 1 (activations before weights, so waiting for the activations
+  // leaves the weight loads in flight), then computes chunk ch, then stores the
+  // activations of chunk ch + 1 into the other LDS buffer.
+  u32x4_t W[2][8], X[4];
+  xload(0, X);
+  wload(0, W[0]);
+  xstore(0, X);
   __syncthreads();
-  // chunk ch (not the last): its weights are in registers and its activations in LDS
-  // buffer ch & 1. The next chunk's activations are loaded before its weights, so
-  // waiting for them leaves the weight loads in flight.
-  auto step = [&](int ch, const u32x4_t *cur, u32x4_t *nxt) {
-    xload(ch + 1, xv);
-    wload(ch + 1, nxt);
-    compute(ch, cur);
-    xstore(ch + 1, xv);
-    __syncthreads();
-  };
-  int ch = 0;
-  for (; ch + 2 < nch; ch += 2) {
-    step(ch, wa, wb);
-    step(ch + 1, wb, wa);
-  }
-  if (ch + 2 == nch) {
-    step(ch, wa, wb);
-    compute(ch + 1, wb);
-  } else {
-    compute(ch, wa);
+  for (int ch = 0; ch < nch; ch += 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      xload(ch + u + 1, X);
+      __builtin_amdgcn_sched_barrier(0);             // keep the issue order: activations first
+      wload(ch + u + 1, W[u ^ 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(ch + u, W[u]);
+      xstore(ch + u + 1, X);
+      __syncthreads();
+    }
   }
   if (n0 >= a.N) return;                             // wave past the output width
 
-  // lane (c, h), register r: D[n0 + acc_row(r, h)][m0 + c]; four consecutive n per store
-  auto store = [&](const f32x16_t &acc, int mc) {
-    if (mc >= mrows) return;
-    u16 *yp = a.Y + (int64_t)(o0 + m0 + mc) * a.ldY + n0;
+  // lane l, register i of acc[s][b]: D[n0 + 16s + 4g + i][m0 + 16b + r16]
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+  for (int b = 0; b < 4; ++b) {
+    const int mc = 16 * b + r16;
+    if (b >= nbop || mc >= mrows) continue;
+    u16 *yp = a.Y + (int64_t)(o0 + m0 + mc) * a.ldY + n0 + 4 * g;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
       float v[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float s = acc[4 * g + i];
-        if (a.gelu) s = 0.5f * s * (1.0f + erff(s * 0.70710678118654752f));
-        v[i] = s;
+        float t = acc[s][b][i];
+        if (a.gelu) t = 0.5f * t * (1.0f + erff(t * 0.70710678118654752f));
+        v[i] = t;
       }
       uint2 o;
       o.x = pack_bf16x2(v[0], v[1]);
       o.y = pack_bf16x2(v[2], v[3]);
-      *(uint2 *)(yp + 8 * g + 4 * h) = o;
+      *(uint2 *)(yp + 16 * s) = o;
     }
-  };
-  store(acc0, c);
-  if (upper) store(acc1, 32 + c);
+  }
 }
 
 __global__ __launch_bounds__(256) void moe_combine_kernel(const u16 *Yg, const u16 *Ys, const float *gate,
