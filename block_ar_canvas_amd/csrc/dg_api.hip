@@ -26,6 +26,10 @@ struct dg_ctx_s {
   const void *p0_ws = nullptr;
   dg_dims p0_dims = {0, 0, 0, 0, 0, 0, 0};
   bool p0_valid = false;
+  // Second stream (default priority) and fork/join events of dg_moe_ffn, made on its
+  // first call: the shared expert runs beside the routed experts.
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
 };
 
 namespace {
@@ -113,6 +117,12 @@ void dg_destroy(dg_ctx ctx) {
     (void)hipStreamSynchronize(ctx->stream);
     (void)hipFree(ctx->d_status);
   }
+  if (ctx->side) {
+    (void)hipStreamSynchronize(ctx->side);
+    (void)hipStreamDestroy(ctx->side);
+  }
+  if (ctx->ev_fork) (void)hipEventDestroy(ctx->ev_fork);
+  if (ctx->ev_join) (void)hipEventDestroy(ctx->ev_join);
   delete ctx;
 }
 
@@ -281,6 +291,36 @@ dg_status dg_moe_ffn(dg_ctx ctx, const dg_moe_dims *m, int32_t C, const dg_bf16 
   u16 *h = ws_at<u16>(ws, w.h), *yg = ws_at<u16>(ws, w.yg), *hs = ws_at<u16>(ws, w.hs);
   u16 *ys = ws_at<u16>(ws, w.ys);
 
+  hipError_t e = hipSuccess;
+  if (!ctx->side) {
+    e = hipStreamCreateWithFlags(&ctx->side, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->ev_fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->ev_join, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(ctx, e, "dg_moe_ffn(side stream)");
+  }
+
+  // shared expert on the side stream: it needs only X, and overlaps the routing and the
+  // routed experts; the combine waits for it
+  GemmArgs s1{};
+  s1.M = C;
+  s1.K = m->d;
+  s1.A = X;
+  s1.gelu = 1;
+  s1.nseg = 1;
+  s1.seg[0] = GemmSeg{W1s, m->Fs, hs, m->Fs, 0, 1, INT_MAX, C, 0};
+  GemmArgs s2{};
+  s2.M = C;
+  s2.K = m->Fs;
+  s2.A = hs;
+  s2.nseg = 1;
+  s2.seg[0] = GemmSeg{W2s, m->d, ys, m->d, 0, 1, INT_MAX, C, 0};
+  e = hipEventRecord(ctx->ev_fork, ctx->stream);
+  if (e == hipSuccess) e = hipStreamWaitEvent(ctx->side, ctx->ev_fork, 0);
+  if (e == hipSuccess) e = dg_launch_gemm(s1, ctx->side);
+  if (e == hipSuccess) e = dg_launch_gemm(s2, ctx->side);
+  if (e == hipSuccess) e = hipEventRecord(ctx->ev_join, ctx->side);
+  if (e != hipSuccess) return hip_fail(ctx, e, "dg_moe_ffn(shared)");
+
   // router logits in float32 (the routing decision is taken on them)
   GemmArgs gr{};
   gr.M = C;
@@ -290,12 +330,12 @@ dg_status dg_moe_ffn(dg_ctx ctx, const dg_moe_dims *m, int32_t C, const dg_bf16 
   gr.seg[0] = GemmSeg{Wr, m->E, nullptr, m->E, 0, 1, INT_MAX, C, 0};
   gr.out32 = logits;
   gr.ld32 = m->E;
-  hipError_t e = dg_launch_gemm(gr, ctx->stream);
+  e = dg_launch_gemm(gr, ctx->stream);
   if (e == hipSuccess) e = dg_launch_moe_route(logits, C, m->E, m->K, sel, gate, ctx->stream);
   if (e == hipSuccess) e = dg_launch_moe_group(sel, C, m->K, m->E, off, perm, pos, n_active, tiles, ctx->stream);
   if (e != hipSuccess) return hip_fail(ctx, e, "dg_moe_ffn(route)");
 
-  // routed experts: grouped GEMMs, hidden = GELU(X W1_e^T), out = hidden W2_e^T
+  // routed experts over the tile list: hidden = GELU(X W1_e^T), out = hidden W2_e^T
   const int max_tiles = dg_moe_max_tiles(C, m->E, m->K);
   const MoeGemmArgs g1{X, W1, off, perm, tiles, h, m->Fe, m->d, m->Fe, 1, max_tiles};
   e = dg_launch_moe_expert(g1, ctx->stream);
@@ -303,22 +343,7 @@ dg_status dg_moe_ffn(dg_ctx ctx, const dg_moe_dims *m, int32_t C, const dg_bf16 
   if (e == hipSuccess) e = dg_launch_moe_expert(g2, ctx->stream);
   if (e != hipSuccess) return hip_fail(ctx, e, "dg_moe_ffn(experts)");
 
-  // shared expert
-  GemmArgs s1{};
-  s1.M = C;
-  s1.K = m->d;
-  s1.A = X;
-  s1.gelu = 1;
-  s1.nseg = 1;
-  s1.seg[0] = GemmSeg{W1s, m->Fs, hs, m->Fs, 0, 1, INT_MAX, C, 0};
-  e = dg_launch_gemm(s1, ctx->stream);
-  GemmArgs s2{};
-  s2.M = C;
-  s2.K = m->Fs;
-  s2.A = hs;
-  s2.nseg = 1;
-  s2.seg[0] = GemmSeg{W2s, m->d, ys, m->d, 0, 1, INT_MAX, C, 0};
-  if (e == hipSuccess) e = dg_launch_gemm(s2, ctx->stream);
+  e = hipStreamWaitEvent(ctx->stream, ctx->ev_join, 0);
   if (e == hipSuccess) e = dg_launch_moe_combine(yg, ys, gate, pos, C, m->K, m->d, Y, ctx->stream);
   if (e != hipSuccess) return hip_fail(ctx, e, "dg_moe_ffn(shared, combine)");
   return DG_OK;

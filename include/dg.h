@@ -242,7 +242,10 @@ dg_status dg_prefill_block(dg_ctx ctx, const dg_dims *dims, const int32_t *token
  * X [C, d]; Wr [E, d]; W1 [E][Fe][d]; W2 [E][d][Fe]; W1s [Fs, d]; W2s [d, Fs]; Y [C, d]
  * output; n_active (device, optional) = the number of distinct experts used. The
  * workspace holds dg_moe_workspace_bytes(m, C) bytes. DG_ERR_SHAPE unless d, Fe, Fs are
- * positive multiples of 32, 1 <= K <= min(E, 32), E <= 256, C <= 1024 and C * K <= 8192. */
+ * positive multiples of 32, 1 <= K <= min(E, 32), E <= 256, C <= 1024 and C * K <= 8192.
+ * The shared expert runs on a second stream of the context (made on the first call,
+ * default priority), forked from and joined back into the context's stream with events:
+ * the call stays ordered on the context's stream like every other call. */
 typedef struct { int32_t d, E, K, Fe, Fs; } dg_moe_dims;
 size_t dg_moe_workspace_bytes(const dg_moe_dims *m, int32_t C);
 dg_status dg_moe_ffn(dg_ctx ctx, const dg_moe_dims *m, int32_t C, const dg_bf16 *X,
