@@ -40,10 +40,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=48)
     ap.add_argument("--config", default="gemma_head")
     ap.add_argument("--roofline-reps", type=int, default=20)
-    ap.add_argument("--cpu-steps", type=int, default=1, help="oracle steps timed for cpu_baseline")
+    ap.add_argument("--cpu-steps", type=int, default=6, help="oracle steps timed for cpu_baseline (about 10 s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batched", action="store_true", help="skip the batched-canvas lines")
     ap.add_argument("--no-moe", action="store_true", help="skip the canvas MoE FFN line")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured HBM and MFMA ceilings")
     ap.add_argument("--no-long-prefix", action="store_true",
                     help="skip the isolated attention call over a 262144-token prefix")
     ap.add_argument("--no-chain", action="store_true",
@@ -237,9 +238,64 @@ def main():
         result["chain8_prefill"] = chain(ctx, commit="prefill", rope_base=10000.0)
     if not args.no_moe:
         result["moe_ffn"] = moe_ffn(ctx, cfg, args.roofline_reps)
+    if not args.no_peaks:
+        pk = measured_peaks(ctx)
+        result["measured_peaks"] = pk
+        rf = result["roofline"]
+        rf["frac_of_measured"] = round(rf["achieved"] / pk["hbm_read_GBs"], 4)
+        rf["mfma_frac_of_measured"] = round(rf["mfma_frac"] * BF16_PEAK_TFLOPS / pk["mfma_bf16_TFLOPs"], 4)
+        if "long_prefix_attention" in result:
+            lp = result["long_prefix_attention"]
+            lp["hbm_frac_of_measured"] = round(lp["achieved_GBs"] / pk["hbm_read_GBs"], 4)
+            lp["mfma_frac_of_measured"] = round(lp["attention_tflops"] / pk["mfma_bf16_TFLOPs"], 4)
+        if "moe_ffn" in result:
+            mo = result["moe_ffn"]
+            mo["hbm_frac_of_measured"] = round(mo["achieved_GBs"] / pk["hbm_read_GBs"], 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, W, Kp, args.cpu_steps)
     print(json.dumps(result))
+
+
+def measured_peaks(ctx):
+    """What this GPU reaches in practice: a streaming read of a 4 GiB buffer (16 times the
+    256 MB last-level cache, so it measures HBM) and back-to-back bf16 MFMAs with register
+    operands. Both through the library (dg_peak_stream_read, dg_peak_mfma_bf16), timed
+    with HIP events on the library's stream; best of several launches."""
+    import torch
+
+    import block_ar_canvas_amd as dg
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.empty(dg.PEAK_STREAM_BLOCKS, dtype=torch.int32, device=dev)
+    fsink = torch.empty(dg.PEAK_MFMA_BLOCKS * 4, dtype=torch.float32, device=dev)
+
+    def best_ms(fn, n):
+        fn()
+        best = float("inf")
+        for _ in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        return best
+
+    ms_r = best_ms(lambda: ctx.peak_stream_read(buf, sink), 5)
+    flop = [0]
+
+    def mf():
+        flop[0] = ctx.peak_mfma(4096, fsink)
+    ms_m = best_ms(mf, 5)
+    ctx.sync()
+    del buf
+    return {"hbm_read_GBs": round(nbytes / (ms_r * 1e-3) / 1e9, 1),
+            "hbm_read_frac_of_published": round(nbytes / (ms_r * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_bf16_TFLOPs": round(flop[0] / (ms_m * 1e-3) / 1e12, 1),
+            "mfma_frac_of_published": round(flop[0] / (ms_m * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "read_bytes": nbytes, "mfma_flop": flop[0]}
 
 
 def _bf(a, dev):

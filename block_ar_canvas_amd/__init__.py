@@ -14,10 +14,11 @@ import os
 import torch
 
 __all__ = ["DGError", "Dims", "MoeDims", "Context", "moe_workspace_bytes", "workspace_bytes", "temperature", "reveal_count", "lib_path",
-           "STOP_GO", "STOP_STOP", "STOP_CAP"]
+           "STOP_GO", "STOP_STOP", "STOP_CAP", "PEAK_STREAM_BLOCKS", "PEAK_MFMA_BLOCKS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 STOP_GO, STOP_STOP, STOP_CAP = 0, 1, 2
+PEAK_STREAM_BLOCKS, PEAK_MFMA_BLOCKS = 2048, 1024     # DG_PEAK_STREAM_BLOCKS, DG_PEAK_MFMA_BLOCKS
 
 _STATUS = {0: "DG_OK", 1: "DG_ERR_NULL", 2: "DG_ERR_SHAPE", 3: "DG_ERR_ALIGN", 4: "DG_ERR_RANGE",
            5: "DG_ERR_CAPACITY", 6: "DG_ERR_STATE", 7: "DG_ERR_NONFINITE", 8: "DG_ERR_HIP",
@@ -89,6 +90,8 @@ def _load():
         "dg_selfcond": (i32, [_P, D, _P, _P, _P, _P, _P]),
         "dg_stop_test": (i32, [_P, i32, i32, _P, _P, _P, f32, i32, i32, _P]),
         "dg_commit_kv": (i32, [_P, D, _P, _P, _P, _P, _P, _P, i64, i64, ctypes.POINTER(i64)]),
+        "dg_peak_stream_read": (i32, [_P, _P, ctypes.c_size_t, _P]),
+        "dg_peak_mfma_bf16": (i32, [_P, i32, _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -261,6 +264,19 @@ class Context:
             _ptr(W1, _BF16, "W1"), _ptr(W2, _BF16, "W2"), _ptr(W1s, _BF16, "W1s"),
             _ptr(W2s, _BF16, "W2s"), _ptr(ws, _U8, "ws"), _ptr(Y, _BF16, "Y"),
             _ptr(n_active, _I32, "n_active", True)))
+
+    def peak_stream_read(self, buf, sink):
+        """Streaming read of the whole of buf (measured HBM ceiling); sink: int32
+        [PEAK_STREAM_BLOCKS] receives per-workgroup XORs of the 16-byte words read."""
+        self._check(self._lib.dg_peak_stream_read(self._h, _ptr(buf, buf.dtype, "buf"),
+                                                  buf.numel() * buf.element_size(),
+                                                  _ptr(sink, _I32, "sink")))
+
+    def peak_mfma(self, iters: int, sink):
+        """Back-to-back bf16 MFMAs (measured MFMA ceiling); sink: float32
+        [PEAK_MFMA_BLOCKS * 4], each entry 1024 * iters. Returns the FLOP enqueued."""
+        self._check(self._lib.dg_peak_mfma_bf16(self._h, int(iters), _ptr(sink, _F32, "sink")))
+        return PEAK_MFMA_BLOCKS * 4 * int(iters) * 4 * 32768
 
     def set_rope(self, base: float):
         self._check(self._lib.dg_set_rope(self._h, float(base)))

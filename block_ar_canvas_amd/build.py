@@ -8,7 +8,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCES = ["dg_api.hip", "k_gemm.hip", "k_attn.hip", "k_logits.hip", "k_selfcond.hip",
-           "k_sampler.hip", "k_moe.hip"]
+           "k_sampler.hip", "k_moe.hip", "k_peak.hip"]
 # Packed fp32 VALU forms are disabled for all device code.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -680,4 +680,22 @@ dg_status dg_commit_kv(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens, c
   return DG_OK;
 }
 
+dg_status dg_peak_stream_read(dg_ctx ctx, const void *buf, size_t bytes, uint32_t *sink) {
+  if (!ctx) return DG_ERR_NULL;
+  DG_REQUIRE_PTR(buf);
+  DG_REQUIRE_PTR(sink);
+  if (bytes == 0 || bytes % 16 || ((uintptr_t)buf & 15))
+    return fail(ctx, DG_ERR_SHAPE, "%s: bytes must be a positive multiple of 16, buf 16-byte aligned", __func__);
+  const hipError_t e = dg_launch_stream_read(buf, (int64_t)bytes, sink, DG_PEAK_STREAM_BLOCKS, ctx->stream);
+  return e == hipSuccess ? DG_OK : hip_fail(ctx, e, __func__);
+}
+
+dg_status dg_peak_mfma_bf16(dg_ctx ctx, int32_t iters, float *sink) {
+  if (!ctx) return DG_ERR_NULL;
+  DG_REQUIRE_PTR(sink);
+  if (iters < 1 || iters > 16384) return fail(ctx, DG_ERR_RANGE, "%s: iters=%d outside [1, 16384]", __func__, iters);
+  const hipError_t e = dg_launch_mfma_peak(iters, sink, DG_PEAK_MFMA_BLOCKS, ctx->stream);
+  return e == hipSuccess ? DG_OK : hip_fail(ctx, e, __func__);
+}
+
 }  // extern "C"

@@ -291,6 +291,10 @@ struct MoeGemmArgs {
   int N, K, ldY, gelu, max_tiles;
 };
 hipError_t dg_launch_moe_expert(const MoeGemmArgs &a, hipStream_t st);
+
+// Measured ceilings (streaming read, back-to-back bf16 MFMAs).
+hipError_t dg_launch_stream_read(const void *buf, int64_t bytes, uint32_t *sink, int blocks, hipStream_t st);
+hipError_t dg_launch_mfma_peak(int iters, float *sink, int blocks, hipStream_t st);
 hipError_t dg_launch_moe_combine(const u16 *Yg, const u16 *Ys, const float *gate, const int *pos,
                                  int C, int K, int d, u16 *Y, hipStream_t st);
 hipError_t dg_launch_xgather(const int *tokens, const u16 *E, const u16 *z, int V, int M, int K,

@@ -262,6 +262,23 @@ dg_status dg_commit_kv(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens,
                        const dg_bf16 *E, const dg_bf16 *Wk, const dg_bf16 *Wv,
                        dg_bf16 *Kp, dg_bf16 *Vt, int64_t P, int64_t Pcap, int64_t *P_out);
 
+/* Measured ceilings for the rooflines (measurement utilities, not steps of the method).
+ * dg_peak_stream_read reads bytes (a positive multiple of 16) of the device buffer buf
+ * (16-byte aligned) once with 16-byte streaming loads over DG_PEAK_STREAM_BLOCKS
+ * workgroups, each writing the XOR of the words it read to sink[block] (device uint32,
+ * DG_PEAK_STREAM_BLOCKS entries): the achievable HBM read rate when buf is larger than
+ * the last-level cache.
+ * dg_peak_mfma_bf16 runs DG_PEAK_MFMA_BLOCKS x 4 waves, each issuing iters rounds of four
+ * independent v_mfma_f32_32x32x16_bf16 on register operands (bf16 1.0 everywhere), i.e.
+ * DG_PEAK_MFMA_BLOCKS * 4 * iters * 4 * 32768 FLOP; lane 0 of wave w writes its
+ * accumulator sum, exactly 1024 * iters, to sink[w] (device float, DG_PEAK_MFMA_BLOCKS * 4
+ * entries). 1 <= iters <= 16384 (DG_ERR_RANGE otherwise). Both are enqueued on the
+ * context's stream; the caller times them. */
+#define DG_PEAK_STREAM_BLOCKS 2048
+#define DG_PEAK_MFMA_BLOCKS 1024
+dg_status dg_peak_stream_read(dg_ctx ctx, const void *buf, size_t bytes, uint32_t *sink);
+dg_status dg_peak_mfma_bf16(dg_ctx ctx, int32_t iters, float *sink);
+
 #ifdef __cplusplus
 }
 #endif

@@ -54,6 +54,30 @@ def test_moe_ffn(dg_ctx, name):
         assert int(nact.item()) == n
 
 
+def test_moe_ffn_back_to_back_calls_share_the_workspace(dg_ctx):
+    # two calls with different tokens and one workspace, enqueued without a sync between
+    # them: the shared expert runs on the context's second stream, so the second call's
+    # shared expert must wait for the first call's combine before it overwrites its rows
+    c = CASES["canvas"]
+    md = dg.MoeDims(c["d"], c["E"], c["K"], c["Fe"], c["Fs"])
+    ws = torch.empty(dg.moe_workspace_bytes(md, c["C"]), dtype=torch.uint8, device=DEV)
+    inp = di.moe_inputs(c["C"], c["d"], c["E"], c["K"], c["Fe"], c["Fs"], seed=52)
+    X2 = di.moe_inputs(c["C"], c["d"], c["E"], c["K"], c["Fe"], c["Fs"], seed=53)["X"]
+    dv = {k: bf16_dev(v) for k, v in inp.items()}
+    Ys = [torch.empty(c["C"], c["d"], dtype=torch.bfloat16, device=DEV) for _ in range(2)]
+    X2d = bf16_dev(X2)
+    for X, Y in ((dv["X"], Ys[0]), (X2d, Ys[1])):
+        dg_ctx.moe_ffn(md, X, dv["Wr"], dv["W1"], dv["W2"], dv["W1s"], dv["W2s"], ws, Y, None)
+    dg_ctx.sync()
+    for Xb, Y in ((inp["X"], Ys[0]), (X2, Ys[1])):
+        Yo, _, _, _ = O.moe_ffn(Xb, inp["Wr"], inp["W1"], inp["W2"], inp["W1s"], inp["W2s"], c["K"])
+        _, _, r = O.moe_route(Xb, inp["Wr"], c["K"])
+        srt = -np.sort(-r.astype(np.float64), axis=1)
+        keep = srt[:, c["K"] - 1] - srt[:, c["K"]] > 1e-5 * np.abs(srt).max(axis=1)
+        assert keep.mean() >= 0.99
+        assert maxrel(O.from_bf16(bits_np(Y))[keep], O.from_bf16(Yo)[keep]) <= 2e-2
+
+
 def test_moe_ffn_rejects_bad_dims(dg_ctx):
     X = torch.zeros(8, 64, dtype=torch.bfloat16, device=DEV)
     Y = torch.empty_like(X)
