@@ -249,7 +249,7 @@ struct DgMoeWs {
 // Rows per expert GEMM tile, and the most tiles a routing can produce: every non-empty
 // group has ceil(rows / MOE_TM) <= rows / MOE_TM + 1 tiles, and at most min(E, C * K)
 // groups are non-empty.
-constexpr int MOE_TM = 64;
+constexpr int MOE_TM = 32;
 static inline int dg_moe_max_tiles(int C, int E, int K) {
   const int ck = C * K;
   return (E < ck ? E : ck) + ck / MOE_TM;
@@ -281,7 +281,7 @@ hipError_t dg_launch_moe_route(const float *logits, int C, int E, int K, int *se
                                hipStream_t st);
 hipError_t dg_launch_moe_group(const int *sel, int C, int K, int E, int *off, int *perm, int *pos,
                                int *nact, int *tiles, hipStream_t st);
-// Grouped expert GEMM: for each listed tile (expert e, rows [m0, m0 + 64) of its group),
+// Grouped expert GEMM: for each listed tile (expert e, rows [m0, m0 + MOE_TM) of its group),
 // Y[off[e] + m][n] = act(sum_k X[row][k] W[e][n][k]), row = perm[off[e] + m] (perm
 // non-NULL) or off[e] + m. N, K multiples of 32; Y row stride ldY.
 struct MoeGemmArgs {

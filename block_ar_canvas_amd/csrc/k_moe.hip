@@ -14,12 +14,11 @@
 //   exclusive offsets, the token list in token order (from per-expert token bitmasks:
 //   deterministic), and for every (token, rank) the row of its expert output in grouped
 //   order.
-//   It also lists the work tiles of the expert GEMMs: one entry (expert, 64-row block) per
+//   It also lists the work tiles of the expert GEMMs: one entry (expert, 32-row block) per
 //   non-empty row block of every group.
 // moe_expert_kernel: Y[off[e] + m] = act(X_e[m] . W[e]^T) for the grouped rows of
 //   expert e. The weights are read once per tile, straight from memory into the MFMA A
-//   operands (each wave owns 32 weight rows); the tile's activation rows (at most 64) are
-//   staged per 128-deep k chunk in LDS and shared by the four waves.
+//   tile: 128 weight rows and at most 32 grouped rows, both copied straight into LDS.
 // moe_combine_kernel: y[t] = bf16(sum over ranks k of gate[t][k] * Yg[pos[t][k]] + Ys[t]),
 //   float32, ranks in order.
 #include <float.h>
@@ -76,7 +75,7 @@ __global__ __launch_bounds__(256) void moe_group_kernel(const int *sel, int C, i
     atomicOr(&mask[e * W + (t >> 5)], 1u << (t & 31));
   }
   __syncthreads();
-  // per expert: rows, 64-row tiles and a non-empty flag, packed as 14 + 9 + 9 bits (the
+  // per expert: rows, 32-row tiles and a non-empty flag, packed as 14 + 9 + 9 bits (the
   // totals stay below 8192 rows, 384 tiles and 256 experts); one inclusive scan
   // (Hillis-Steele over the 256 threads) gives every offset at once
   __shared__ uint32_t scan[256];
@@ -127,22 +126,26 @@ DG_DEV f32x4_t mfma_16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// One workgroup = 4 waves = 128 weight rows of one tile (expert e, rows [m0, m0 + 64) of
-// its group); each wave owns 32 weight rows as two 16-row A operands.
+// One workgroup = 4 waves = 128 weight rows of one tile (expert e, rows [m0, m0 + 32) of
+// its group); wave w computes weight rows [32w, 32w + 32) as two 16-row A operands.
 // v_mfma_f32_16x16x32_bf16: lane l supplies row l % 16 of A (and column l % 16 of B) with
-// 8 k values; the four lane groups g = l / 16 cover the 32 k of a step. Lane group g takes
-// k [32j + 8g, +8) of the chunk in step j for both operands, so one weight load
-// instruction reads 16 rows x 64 contiguous bytes (16 cache lines per KiB; the memory
-// pipeline, not HBM, is what a weight stream with 32 lines per KiB saturates).
-// Accumulator register i of lane l holds D[4(l / 16) + i][l % 16]: four consecutive
-// weight rows of one activation row.
-// Every memory load is unconditional, with row and k addresses clamped into the operands
-// (rows past the group repeat its last row, k past K repeats the last 32 k), and loads of
-// the chunk after the last read one fixed line: the compiler then counts the loads in
-// flight exactly and keeps the next chunk's loads outstanding during the MFMAs. Clamped
-// rows are never stored, and k steps past K are skipped (a wave-uniform test).
+// 8 k values; lane group g = l / 16 takes k [32j + 8g, +8) of the chunk in step j for
+// both operands. Accumulator register i of lane l holds D[4(l / 16) + i][l % 16].
+//
+// Both operands come through LDS by direct global -> LDS copies (the weights once, the
+// activations once per workgroup): a stage holds a 128-deep chunk of the 128 weight rows
+// (32 KiB) and of the 32 activation rows (8 KiB), 256 bytes per row with its 16-byte
+// chunks XOR-swizzled by the row's low 4 bits. Two stages: the next chunk's copies are in
+// flight while the MFMAs read the current one. Every wave issues exactly 10 copies per
+// stage (8 of weight rows, 2 of activation rows; rows past the group repeat its last row,
+// k past K repeats the last 16 bytes), so one s_waitcnt vmcnt(10) waits for the current
+// stage. 80 KiB of LDS per workgroup: two workgroups per CU.
+constexpr int XW = 128 * 256, XX = MOE_TM * 256, XSTAGE = XW + XX, XSMEM = 2 * XSTAGE;
+
+DG_DEV int xswz(int row, int q) { return row * 256 + ((q ^ (row & 15)) << 4); }
+
 __global__ __launch_bounds__(256) void moe_expert_kernel(MoeGemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t xs[2][MOE_TM * 256];
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int NB = (a.N + 127) / 128;
   const int ti = blockIdx.x / NB, nb = blockIdx.x % NB;
   if (ti >= a.tiles[0]) return;
@@ -152,87 +155,74 @@ __global__ __launch_bounds__(256) void moe_expert_kernel(MoeGemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;
   const int K = a.K, nch = (K + 127) / 128;
-  const int n0 = nb * 128 + 32 * wave;
+  const int nw0 = nb * 128, n0 = nw0 + 32 * wave;
   const int nbop = (mrows + 15) >> 4;                // B operands (16 rows each) in use
-  const u16 *wp[2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s)
-    wp[s] = a.W + ((int64_t)e * a.N + min(n0 + 16 * s + r16, a.N - 1)) * K + 8 * g;
 
-  // activation staging: thread t moves 16-byte chunk (t & 15) of rows t/16 + 16q
-  const u16 *xr[4];
+  // copy sources: instruction i of this wave fills 4 rows x 256 bytes; lane l covers row
+  // base + l / 16 and loads global chunk (l & 15) ^ (row & 15) into LDS slot l & 15
+  const u16 *wsrc[8], *xsrc[2];
+  int wch[8], xch[2];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int mm = m0 + min((tid >> 4) + 16 * q, mrows - 1);
-    const int row = a.perm ? a.perm[o0 + mm] : o0 + mm;
-    xr[q] = a.X + (int64_t)row * K;
+  for (int i = 0; i < 8; ++i) {
+    const int R = 32 * wave + 4 * i + (lane >> 4);
+    wch[i] = 8 * ((lane & 15) ^ (R & 15));
+    wsrc[i] = a.W + ((int64_t)e * a.N + min(nw0 + R, a.N - 1)) * K;
   }
-  auto xload = [&](int ch, u32x4_t *v) {
-    const int k = min(ch * 128 + 8 * (tid & 15), K - 8);
-    const bool real = ch < nch;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = *(const u32x4_t *)(real ? xr[q] + k : a.X);
-  };
-  auto xstore = [&](int ch, const u32x4_t *v) {
+  for (int i = 0; i < 2; ++i) {
+    const int R = 8 * wave + 4 * i + (lane >> 4);
+    xch[i] = 8 * ((lane & 15) ^ (R & 15));
+    const int mm = m0 + min(R, mrows - 1);
+    const int row = a.perm ? a.perm[o0 + mm] : o0 + mm;
+    xsrc[i] = a.X + (int64_t)row * K;
+  }
+  const uint32_t lbase = lds_addr(smem);
+  auto issue = [&](int ch) {
+    const uint32_t sb = lbase + (uint32_t)((ch & 1) * XSTAGE);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) *(u32x4_t *)(xs[ch & 1] + xslot((tid >> 4) + 16 * q, tid & 15)) = v[q];
-  };
-  // w[2j + s]: k step j, row half s
-  auto wload = [&](int ch, u32x4_t *w) {
-    const bool real = ch < nch;
+    for (int i = 0; i < 8; ++i)
+      dma16(wsrc[i] + min(ch * 128 + wch[i], K - 8), sb + (uint32_t)((32 * wave + 4 * i) * 256));
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-        w[2 * j + s] = *(const u32x4_t *)(real ? wp[s] + min(ch * 128 + 32 * j, K - 32) : a.W);
+    for (int i = 0; i < 2; ++i)
+      dma16(xsrc[i] + min(ch * 128 + xch[i], K - 8), sb + (uint32_t)(XW + (8 * wave + 4 * i) * 256));
   };
 
-  f32x4_t acc[2][4] = {};
-  auto compute = [&](int ch, const u32x4_t *w) {
-    if (ch >= nch) return;
+  f32x4_t acc[2][2] = {};
+  issue(0);
+  for (int ch = 0; ch < nch; ++ch) {
+    if (ch + 1 < nch) {
+      issue(ch + 1);
+      dma_wait<10>();
+    } else {
+      dma_wait<0>();
+    }
+    __syncthreads();
+    const uint8_t *Ws = smem + (ch & 1) * XSTAGE, *Xs = Ws + XW;
     const int nj = min(4, (K - ch * 128) >> 5);
-    const uint8_t *xb = xs[ch & 1];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (j < nj) {
+        const int q = 4 * j + g;
+        u32x4_t av[2];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+        for (int s = 0; s < 2; ++s) av[s] = *(const u32x4_t *)(Ws + xswz(32 * wave + 16 * s + r16, q));
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
           if (b < nbop) {
-            const u32x4_t bv = *(const u32x4_t *)(xb + xslot(16 * b + r16, 4 * j + g));
-            acc[0][b] = mfma_16x16x32(w[2 * j], bv, acc[0][b]);
-            acc[1][b] = mfma_16x16x32(w[2 * j + 1], bv, acc[1][b]);
+            const u32x4_t bv = *(const u32x4_t *)(Xs + xswz(16 * b + r16, q));
+            acc[0][b] = mfma_16x16x32(av[0], bv, acc[0][b]);
+            acc[1][b] = mfma_16x16x32(av[1], bv, acc[1][b]);
           }
         }
       }
     }
-  };
-
-  // Chunk ch is computed from weight registers W[ch & 1] and LDS buffer ch & 1; step ch
-  // first loads chunk ch + 1 (activations before weights, so waiting for the activations
-  // leaves the weight loads in flight), then computes chunk ch, then stores the
-  // activations of chunk ch + 1 into the other LDS buffer.
-  u32x4_t W[2][8], X[4];
-  xload(0, X);
-  wload(0, W[0]);
-  xstore(0, X);
-  __syncthreads();
-  for (int ch = 0; ch < nch; ch += 2) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      xload(ch + u + 1, X);
-      __builtin_amdgcn_sched_barrier(0);             // keep the issue order: activations first
-      wload(ch + u + 1, W[u ^ 1]);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(ch + u, W[u]);
-      xstore(ch + u + 1, X);
-      __syncthreads();
-    }
+    __syncthreads();                                 // stage ch & 1 is refilled next round
   }
   if (n0 >= a.N) return;                             // wave past the output width
 
   // lane l, register i of acc[s][b]: D[n0 + 16s + 4g + i][m0 + 16b + r16]
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
+  for (int b = 0; b < 2; ++b) {
     const int mc = 16 * b + r16;
     if (b >= nbop || mc >= mrows) continue;
     u16 *yp = a.Y + (int64_t)(o0 + m0 + mc) * a.ldY + n0 + 4 * g;
@@ -294,8 +284,15 @@ hipError_t dg_launch_moe_group(const int *sel, int C, int K, int E, int *off, in
 
 hipError_t dg_launch_moe_expert(const MoeGemmArgs &a, hipStream_t st) {
   if (a.N < 32 || a.N % 32 || a.K < 32 || a.K % 32 || a.max_tiles < 1) return hipErrorInvalidValue;
+  static bool attr = false;
+  if (!attr) {
+    const hipError_t e = hipFuncSetAttribute((const void *)moe_expert_kernel,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, XSMEM);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
   const int NB = (a.N + 127) / 128;
-  hipLaunchKernelGGL(moe_expert_kernel, dim3(a.max_tiles * NB), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(moe_expert_kernel, dim3(a.max_tiles * NB), dim3(256), XSMEM, st, a);
   return hipGetLastError();
 }
 

@@ -26,6 +26,9 @@ CASES = {
     # few experts: groups of ~150 rows span three 64-row tiles; d and Fe leave k tails
     # past the last 128-deep chunk and output widths with idle waves
     "skewed": dict(C=300, d=160, E=4, K=2, Fe=96, Fs=64),
+    "one_token": dict(C=1, d=64, E=8, K=2, Fe=32, Fs=32),
+    "all_experts": dict(C=20, d=64, E=4, K=4, Fe=32, Fs=32),
+    "max_tokens": dict(C=1024, d=64, E=32, K=8, Fe=32, Fs=32),     # C * K = 8192, the limit
 }
 
 
