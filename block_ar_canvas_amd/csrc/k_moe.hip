@@ -136,10 +136,11 @@ DG_DEV f32x4_t mfma_16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
 // activations once per workgroup): a stage holds a 128-deep chunk of the 128 weight rows
 // (32 KiB) and of the 32 activation rows (8 KiB), 256 bytes per row with its 16-byte
 // chunks XOR-swizzled by the row's low 4 bits. Two stages: the next chunk's copies are in
-// flight while the MFMAs read the current one. Every wave issues exactly 10 copies per
-// stage (8 of weight rows, 2 of activation rows; rows past the group repeat its last row,
-// k past K repeats the last 16 bytes), so one s_waitcnt vmcnt(10) waits for the current
-// stage. 80 KiB of LDS per workgroup: two workgroups per CU.
+// flight while the MFMAs read the current one. Every wave issues the same copies every
+// stage (8 of weight rows, and the 0-2 of activation rows that reach into the tile; rows
+// past the group repeat its last row, k past K repeats the last 16 bytes), so one
+// s_waitcnt vmcnt(8 + those) waits for the current stage. 80 KiB of LDS per workgroup:
+// two workgroups per CU.
 constexpr int XW = 128 * 256, XX = MOE_TM * 256, XSTAGE = XW + XX, XSMEM = 2 * XSTAGE;
 
 DG_DEV int xswz(int row, int q) { return row * 256 + ((q ^ (row & 15)) << 4); }
@@ -176,6 +177,10 @@ __global__ __launch_bounds__(256) void moe_expert_kernel(MoeGemmArgs a) {
     const int row = a.perm ? a.perm[o0 + mm] : o0 + mm;
     xsrc[i] = a.X + (int64_t)row * K;
   }
+  // activation copies of this wave: rows [8w + 4i, +4) are copied only when the first of
+  // them is in the tile (wave-uniform); rows past the tile are never stored, so what LDS
+  // holds there does not matter
+  const int nx = __builtin_amdgcn_readfirstlane(min(2, max(0, (mrows - 8 * wave + 3) >> 2)));
   const uint32_t lbase = lds_addr(smem);
   auto issue = [&](int ch) {
     const uint32_t sb = lbase + (uint32_t)((ch & 1) * XSTAGE);
@@ -184,18 +189,26 @@ __global__ __launch_bounds__(256) void moe_expert_kernel(MoeGemmArgs a) {
       dma16(wsrc[i] + min(ch * 128 + wch[i], K - 8), sb + (uint32_t)((32 * wave + 4 * i) * 256));
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      dma16(xsrc[i] + min(ch * 128 + xch[i], K - 8), sb + (uint32_t)(XW + (8 * wave + 4 * i) * 256));
+      if (i < nx) dma16(xsrc[i] + min(ch * 128 + xch[i], K - 8), sb + (uint32_t)(XW + (8 * wave + 4 * i) * 256));
+  };
+  // this wave's copies per stage: 8 weight copies plus its activation copies in flight
+  auto wait_current = [&](bool more) {
+    if (!more) {
+      dma_wait<0>();
+    } else if (nx == 2) {
+      dma_wait<10>();
+    } else if (nx == 1) {
+      dma_wait<9>();
+    } else {
+      dma_wait<8>();
+    }
   };
 
   f32x4_t acc[2][2] = {};
   issue(0);
   for (int ch = 0; ch < nch; ++ch) {
-    if (ch + 1 < nch) {
-      issue(ch + 1);
-      dma_wait<10>();
-    } else {
-      dma_wait<0>();
-    }
+    if (ch + 1 < nch) issue(ch + 1);
+    wait_current(ch + 1 < nch);
     __syncthreads();
     const uint8_t *Ws = smem + (ch & 1) * XSTAGE, *Xs = Ws + XW;
     const int nj = min(4, (K - ch * 128) >> 5);
