@@ -330,8 +330,11 @@ dg_status dg_moe_ffn(dg_ctx ctx, const dg_moe_dims *m, int32_t C, const dg_bf16 
   gr.seg[0] = GemmSeg{Wr, m->E, nullptr, m->E, 0, 1, INT_MAX, C, 0};
   gr.out32 = logits;
   gr.ld32 = m->E;
+  const int rsplit = dg_moe_router_splits(m->d);
+  gr.ksplit = rsplit;
+  gr.split_stride = (int64_t)C * m->E;
   e = dg_launch_gemm(gr, ctx->stream);
-  if (e == hipSuccess) e = dg_launch_moe_route(logits, C, m->E, m->K, sel, gate, ctx->stream);
+  if (e == hipSuccess) e = dg_launch_moe_route(logits, rsplit, C, m->E, m->K, sel, gate, ctx->stream);
   if (e == hipSuccess) e = dg_launch_moe_group(sel, C, m->K, m->E, off, perm, pos, n_active, tiles, ctx->stream);
   if (e != hipSuccess) return hip_fail(ctx, e, "dg_moe_ffn(route)");
 

@@ -228,12 +228,16 @@ struct GemmArgs {
   // fp32 output (segment 0 only): out32[m * ld32 + n] = D[m][n] instead of bf16 stores
   float *out32;
   int ld32;
+  // fp32 output only: K split into ksplit equal parts (each a multiple of 32); part s of
+  // the sum goes to out32 + s * split_stride, and the consumer adds the parts in order.
+  int ksplit;
+  int64_t split_stride;
 };
 hipError_t dg_launch_gemm(const GemmArgs &a, hipStream_t st);
 
 // Canvas MoE FFN workspace (256-byte aligned regions).
 struct DgMoeWs {
-  size_t logits;   // router logits fp32 [C][E]
+  size_t logits;   // router logit parts fp32 [splits][C][E]
   size_t sel;      // selected experts int32 [C][K] (rank order)
   size_t gate;     // gates fp32 [C][K]
   size_t off;      // group offsets int32 [E + 1]
@@ -254,6 +258,13 @@ static inline int dg_moe_max_tiles(int C, int E, int K) {
   const int ck = C * K;
   return (E < ck ? E : ck) + ck / MOE_TM;
 }
+// Router logits are computed in this many k parts (more workgroups on a short GEMM):
+// halve the depth while it stays a multiple of 32 and at least 256, up to 8 parts.
+static inline int dg_moe_router_splits(int d) {
+  int s = 1;
+  while (s < 8 && d % (2 * s * 32) == 0 && d / (2 * s) >= 256) s *= 2;
+  return s;
+}
 static inline DgMoeWs dg_moe_ws_layout(int C, int d, int E, int K, int Fe, int Fs) {
   DgMoeWs w;
   size_t off = 0;
@@ -263,7 +274,7 @@ static inline DgMoeWs dg_moe_ws_layout(int C, int d, int E, int K, int Fe, int F
     return at;
   };
   const size_t CK = (size_t)C * K;
-  w.logits = take((size_t)C * E * 4);
+  w.logits = take((size_t)dg_moe_router_splits(d) * C * E * 4);
   w.sel = take(CK * 4);
   w.gate = take(CK * 4);
   w.off = take((size_t)(E + 1) * 4);
@@ -277,7 +288,7 @@ static inline DgMoeWs dg_moe_ws_layout(int C, int d, int E, int K, int Fe, int F
   w.total = off;
   return w;
 }
-hipError_t dg_launch_moe_route(const float *logits, int C, int E, int K, int *sel, float *gate,
+hipError_t dg_launch_moe_route(const float *logits, int splits, int C, int E, int K, int *sel, float *gate,
                                hipStream_t st);
 hipError_t dg_launch_moe_group(const int *sel, int C, int K, int E, int *off, int *perm, int *pos,
                                int *nact, int *tiles, hipStream_t st);

@@ -59,8 +59,11 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
   const int h = lane >> 5, l32 = lane & 31;
 
   // Tile of this workgroup; consecutive m tiles of one n tile share an XCD.
-  const int total = gridDim.x;
-  int idx = blockIdx.x;
+  // With a k split (fp32 output only) the grid holds ksplit copies of the tile grid.
+  const int S = (a.out32 && a.ksplit > 1) ? a.ksplit : 1;
+  const int total = gridDim.x / S;
+  const int ks = blockIdx.x / total;
+  int idx = blockIdx.x % total;
   if ((total & 7) == 0 && ((total >> 3) % MB) == 0) idx = (idx & 7) * (total >> 3) + (idx >> 3);
   const int mb = idx % MB, nbg = idx / MB;
   int si = 0;
@@ -68,7 +71,8 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
     if (nbg >= a.seg[s].nblk0) si = s;
   const GemmSeg &sg = a.seg[si];
   const int nb0 = (nbg - sg.nblk0) * BN, m0 = mb * BM;
-  const int K = a.K;
+  const int K = a.K / S;                             // depth of this part
+  const int kbase = ks * K;
   const int nst = (K + BK - 1) / BK;
 
   // Copy assignment: wave w fills rows [8w, 8w + 8) of both tiles, 4 rows (1 KiB) per
@@ -80,7 +84,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
     const int R = 8 * wave + 4 * j + (lane >> 4);
     lchunk[j] = (lane & 15) ^ (R & 15);
     const int n = min(nb0 + R, sg.N - 1);
-    wrow[j] = sg.W + (int64_t)n * K;
+    wrow[j] = sg.W + (int64_t)n * a.K + kbase;
     const int m = min(m0 + R, a.M - 1);
     if (GATHER) {
       int tok = a.tokens[m];
@@ -88,9 +92,9 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
         set_status(a.status, DGS_RANGE);
         tok = 0;
       }
-      xrow[j] = a.E + (int64_t)tok * K;
+      xrow[j] = a.E + (int64_t)tok * a.K + kbase;
     } else {
-      xrow[j] = a.A + (int64_t)m * K;
+      xrow[j] = a.A + (int64_t)m * a.K + kbase;
     }
   }
   const uint32_t lbase = lds_addr(smem);
@@ -150,7 +154,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         const int n = nb0 + (q & 1) * 32 + acc_row(rb + r, h);
-        if (n < sg.N) a.out32[(int64_t)m * a.ld32 + n] = v[r];
+        if (n < sg.N) a.out32[ks * a.split_stride + (int64_t)m * a.ld32 + n] = v[r];
       }
     }
     return;
@@ -255,7 +259,9 @@ hipError_t dg_launch_gemm(const GemmArgs &a0, hipStream_t st) {
     a.store_mode[s] = store_mode(a.seg[s]);
   }
   const int MB = (mmax + BM - 1) / BM;
-  const dim3 grid(nblk * MB);
+  const int S = (a.out32 && a.ksplit > 1) ? a.ksplit : 1;
+  if (S > 1 && a.K % (32 * S) != 0) return hipErrorInvalidValue;
+  const dim3 grid(nblk * MB * S);
   if (a.A)
     hipLaunchKernelGGL(gemm_kernel<false>, grid, dim3(512), SMEM, st, a, MB);
   else

@@ -8,7 +8,7 @@
 // experts and combine.
 //
 // moe_route_kernel: one workgroup per token; each thread holds one expert's logit (float32,
-//   from the router GEMM) and counts the experts that beat it (larger logit, or equal
+//   the router GEMM's k parts added in order) and counts the experts that beat it (larger logit, or equal
 //   with a lower id); rank < K selects it. Gates: softmax over the K selected logits.
 // moe_group_kernel: one workgroup; per expert, the number of tokens routed to it, the
 //   exclusive offsets, the token list in token order (from per-expert token bitmasks:
@@ -27,14 +27,21 @@
 
 namespace {
 
-__global__ __launch_bounds__(256) void moe_route_kernel(const float *logits, int E, int K, int *sel,
-                                                        float *gate) {
+__global__ __launch_bounds__(256) void moe_route_kernel(const float *logits, int splits, int64_t pstride,
+                                                        int E, int K, int *sel, float *gate) {
   __shared__ float lv[256];
   __shared__ float sv[32];
   const int t = blockIdx.x, tid = threadIdx.x;
   float v = -INFINITY;
   if (tid < E) {
-    v = logits[(int64_t)t * E + tid];
+    // up to 8 parts, loaded together (a clamped index keeps every load valid), added in order
+    float p[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) p[s] = logits[min(s, splits - 1) * pstride + (int64_t)t * E + tid];
+    v = p[0];
+#pragma unroll
+    for (int s = 1; s < 8; ++s)
+      if (s < splits) v += p[s];
     if (!(v == v)) v = -INFINITY;                    // a NaN logit ranks last
   }
   lv[tid] = v;
@@ -68,15 +75,20 @@ __global__ __launch_bounds__(256) void moe_group_kernel(const int *sel, int C, i
   extern __shared__ uint32_t mask[];                 // [E][W], W = C / 32 rounded up
   __shared__ int loff[257];
   const int tid = threadIdx.x, n = C * K, W = (C + 31) / 32;
+  // this thread's selections (n <= 8192: at most 32), loaded once and kept in registers
+  int es[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) es[j] = sel[min(tid + 256 * j, n - 1)];
   for (int i = tid; i < E * W; i += 256) mask[i] = 0u;
   __syncthreads();
-  for (int i = tid; i < n; i += 256) {
-    const int t = i / K, e = sel[i];
-    atomicOr(&mask[e * W + (t >> 5)], 1u << (t & 31));
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const int i = tid + 256 * j;
+    if (i < n) atomicOr(&mask[es[j] * W + ((i / K) >> 5)], 1u << ((i / K) & 31));
   }
   __syncthreads();
   // per expert: rows, 32-row tiles and a non-empty flag, packed as 14 + 9 + 9 bits (the
-  // totals stay below 8192 rows, 384 tiles and 256 experts); one inclusive scan
+  // totals stay at most 8192 rows, 504 tiles and 256 experts); one inclusive scan
   // (Hillis-Steele over the 256 threads) gives every offset at once
   __shared__ uint32_t scan[256];
   uint32_t v = 0;
@@ -106,8 +118,11 @@ __global__ __launch_bounds__(256) void moe_group_kernel(const int *sel, int C, i
     if (nact) nact[0] = (int)(incl >> 23);
   }
   __syncthreads();
-  for (int i = tid; i < n; i += 256) {
-    const int t = i / K, e = sel[i];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const int i = tid + 256 * j;
+    if (i >= n) break;
+    const int t = i / K, e = es[j];
     const uint32_t *m = mask + e * W;
     int p = loff[e];
     for (int w = 0; w < (t >> 5); ++w) p += __popc(m[w]);
@@ -282,9 +297,10 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const u16 *Yg, const u
 
 }  // namespace
 
-hipError_t dg_launch_moe_route(const float *logits, int C, int E, int K, int *sel, float *gate,
+hipError_t dg_launch_moe_route(const float *logits, int splits, int C, int E, int K, int *sel, float *gate,
                                hipStream_t st) {
-  hipLaunchKernelGGL(moe_route_kernel, dim3(C), dim3(256), 0, st, logits, E, K, sel, gate);
+  hipLaunchKernelGGL(moe_route_kernel, dim3(C), dim3(256), 0, st, logits, splits, (int64_t)C * E, E, K, sel,
+                     gate);
   return hipGetLastError();
 }
 
