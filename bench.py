@@ -422,17 +422,18 @@ def variant_canvas(ctx, cfg, Wd, Hd, rule="entropy", draw="argmax"):
 
 def moe_ffn(ctx, cfg, reps):
     """The canvas MoE FFN on one canvas at the workload's width: 128 experts, 8 routed per
-    token plus a shared expert, expert width 512, shared width 1024 (stand-in sizes;
-    random routing, so about every expert is used, where the pages report about 84 on
-    real text). Reports the call time and the weight bytes it streams (router, the
-    experts used, the shared expert) as achieved GB/s."""
+    token plus a shared expert, expert width 512, shared width 1024 (stand-in sizes). The
+    canvas rows share part of their direction, so the random router sends the canvas to
+    about 84 distinct experts, as the pages report for real text. Reports the call time
+    and the weight bytes it streams (router, the experts used, the shared expert) as
+    achieved GB/s."""
     import torch
 
     import block_ar_canvas_amd as dg
     import dg_inputs as di
     C, d, E, K, Fe, Fs = cfg.C, cfg.d, 128, 8, 512, 1024
     dev = torch.device("cuda:0")
-    inp = di.moe_inputs(C, d, E, K, Fe, Fs, seed=61)
+    inp = di.moe_inputs(C, d, E, K, Fe, Fs, seed=61, share=di.MOE_CANVAS_SHARE)
     dv = {k: _bf(v, dev) for k, v in inp.items()}
     del inp
     md = dg.MoeDims(d, E, K, Fe, Fs)
@@ -453,7 +454,8 @@ def moe_ffn(ctx, cfg, reps):
     ms = e0.elapsed_time(e1) / n
     na = int(nact.item())
     wbytes = 2 * (E * d + na * 2 * Fe * d + 2 * Fs * d)
-    return {"workload": f"canvas MoE FFN: C={C} d={d} experts={E} top-{K} Fe={Fe} shared Fs={Fs}",
+    return {"workload": f"canvas MoE FFN: C={C} d={d} experts={E} top-{K} Fe={Fe} shared Fs={Fs}, "
+                        f"canvas rows sharing {di.MOE_CANVAS_SHARE:.2f} of their variance",
             "ms_per_call": round(ms, 4), "experts_used": na,
             "weight_bytes": wbytes, "achieved_GBs": round(wbytes / (ms * 1e-3) / 1e9, 1),
             "hbm_frac": round(wbytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4)}

@@ -39,6 +39,7 @@ TAG_E, TAG_WQ, TAG_WK, TAG_WV, TAG_WO, TAG_W1, TAG_W2 = 1, 2, 3, 4, 5, 6, 7
 TAG_KP, TAG_VP = 8, 9
 TAG_TARGET, TAG_NOISE = 10, 11
 TAG_MOE_X, TAG_MOE_WR, TAG_MOE_W1, TAG_MOE_W2, TAG_MOE_W1S, TAG_MOE_W2S = 12, 13, 14, 15, 16, 17
+TAG_MOE_XG = 18
 
 # Large tensors are drawn in independent row blocks of this many elements so that
 # generation can be chunked; the block index is part of the stream key.
@@ -162,12 +163,26 @@ def prefix_kv(cfg: Config, Pcap: int | None = None, request: int = 0):
     return K, V
 
 
-def moe_inputs(C: int, d: int, E: int, K: int, Fe: int, Fs: int, seed: int) -> dict:
-    """Canvas MoE FFN stand-in weights and activations (bf16 bits): X ~ N(0, 1) rows, every
-    weight N(0, 1/fan_in). Layouts: Wr [E, d], W1 [E, Fe, d], W2 [E, d, Fe], W1s [Fs, d],
+# Share of a canvas row's variance that its canvas has in common: with the random router
+# below, a 256-token canvas of such rows routes to about 84 distinct experts of 128 at
+# top-8, the count the DiffusionGemma Technical Report page gives ("Prerequisites").
+MOE_CANVAS_SHARE = 0.56
+
+
+def moe_inputs(C: int, d: int, E: int, K: int, Fe: int, Fs: int, seed: int, share: float = 0.0) -> dict:
+    """Canvas MoE FFN stand-in weights and activations (bf16 bits): every weight
+    N(0, 1/fan_in); X rows N(0, 1) per element, x_t = sqrt(share) g + sqrt(1 - share) e_t
+    with one direction g per canvas (share = 0: independent rows, which route to nearly
+    every expert). Layouts: Wr [E, d], W1 [E, Fe, d], W2 [E, d, Fe], W1s [Fs, d],
     W2s [d, Fs]. K (experts per token) is not used for drawing."""
+    if share > 0.0:
+        g = np.random.default_rng([seed, TAG_MOE_XG]).standard_normal(d).astype(np.float32)
+        e = np.random.default_rng([seed, TAG_MOE_X]).standard_normal((C, d)).astype(np.float32)
+        X = f32_to_bf16_bits(np.float32(np.sqrt(share)) * g[None, :] + np.float32(np.sqrt(1.0 - share)) * e)
+    else:
+        X = gaussian_bf16(seed, TAG_MOE_X, (C, d), 1.0)
     return {
-        "X": gaussian_bf16(seed, TAG_MOE_X, (C, d), 1.0),
+        "X": X,
         "Wr": gaussian_bf16(seed, TAG_MOE_WR, (E, d), d ** -0.5),
         "W1": gaussian_bf16(seed, TAG_MOE_W1, (E, Fe, d), d ** -0.5),
         "W2": gaussian_bf16(seed, TAG_MOE_W2, (E, d, Fe), Fe ** -0.5),

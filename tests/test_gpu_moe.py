@@ -27,6 +27,8 @@ CASES = {
     # past the last 128-deep chunk and output widths with idle waves
     "skewed": dict(C=300, d=160, E=4, K=2, Fe=96, Fs=64),
     "one_token": dict(C=1, d=64, E=8, K=2, Fe=32, Fs=32),
+    # canvas rows sharing a direction (the bench's routing structure: about 84 experts)
+    "canvas_shared": dict(C=256, d=2048, E=128, K=8, Fe=512, Fs=1024, share=0.56),
     "all_experts": dict(C=20, d=64, E=4, K=4, Fe=32, Fs=32),
     "max_tokens": dict(C=1024, d=64, E=32, K=8, Fe=32, Fs=32),     # C * K = 8192, the limit
 }
@@ -35,7 +37,7 @@ CASES = {
 @pytest.mark.parametrize("name", list(CASES))
 def test_moe_ffn(dg_ctx, name):
     c = CASES[name]
-    inp = di.moe_inputs(c["C"], c["d"], c["E"], c["K"], c["Fe"], c["Fs"], seed=51)
+    inp = di.moe_inputs(c["C"], c["d"], c["E"], c["K"], c["Fe"], c["Fs"], seed=51, share=c.get("share", 0.0))
     md = dg.MoeDims(c["d"], c["E"], c["K"], c["Fe"], c["Fs"])
     ws = torch.empty(dg.moe_workspace_bytes(md, c["C"]), dtype=torch.uint8, device=DEV)
     Y = torch.empty(c["C"], c["d"], dtype=torch.bfloat16, device=DEV)

@@ -100,3 +100,18 @@ def test_gate_weighting_matters():
     ys = O.from_bf16(O.to_bf16(O.from_bf16(O.to_bf16(O.gelu_erf(x @ O.from_bf16(W1s).T))) @ O.from_bf16(W2s).T))
     assert np.any(O.to_bf16(acc + ys) != Y)
     assert not np.allclose(gates, 1.0 / 3)
+
+
+def test_canvas_share_gives_the_pages_expert_count():
+    # the MoE workload's input recipe: canvas rows sharing part of their direction route a
+    # 256-token canvas to about 84 of 128 experts at top-8 (DiffusionGemma Technical Report
+    # page, "Prerequisites"); independent rows reach nearly all of them
+    import dg_inputs as di
+    for seed in (51, 61):
+        inp = di.moe_inputs(256, 2048, 128, 8, 32, 32, seed=seed, share=di.MOE_CANVAS_SHARE)
+        sel, _, _ = O.moe_route(inp["X"], inp["Wr"], 8)
+        assert 72 <= len(np.unique(sel)) <= 96
+        x = O.from_bf16(inp["X"])
+        assert abs(x.std() - 1.0) < 0.05                 # rows stay N(0, 1) per element
+    inp = di.moe_inputs(256, 2048, 128, 8, 32, 32, seed=51)
+    assert len(np.unique(O.moe_route(inp["X"], inp["Wr"], 8)[0])) >= 120
