@@ -128,3 +128,64 @@ def test_commit_at_end_of_chain(dg_ctx):
         bound = np.abs(r) * 2.0 ** -7 + 2.0 ** -16 * np.max(np.abs(r))
         worst = np.unravel_index(np.argmax(err - bound), err.shape)
         assert np.all(err <= bound), (int(np.sum(err > bound)), worst, g[worst], r[worst])
+
+
+def test_prefill_commit_at_end_of_chain(dg_ctx):
+    # the chain8_prefill configuration: the last canvas's block re-encoded causally over a
+    # 34560-token cache with rotary positions (base 10000), filling the cache to Pcap
+    cfg, W, Wd = full("chain8")
+    Pcap = cfg.Pcap
+    P = cfg.P0 + (cfg.n_canvas - 1) * cfg.C
+    Kp, Vp = di.prefix_kv(cfg, Pcap)
+    rng = np.random.default_rng(cfg.seed + 500)
+    Kp[:, cfg.P0:P] = di.f32_to_bf16_bits(rng.standard_normal((cfg.Hkv, P - cfg.P0, cfg.hd)).astype(np.float32))
+    Vp[:, cfg.P0:P] = di.f32_to_bf16_bits(rng.standard_normal((cfg.Hkv, P - cfg.P0, cfg.hd)).astype(np.float32))
+    tok = rng.integers(0, cfg.V, cfg.C).astype(np.int32)
+    Kd, Vtd = upload_cache(Kp, Vp, Pcap)
+    ws = ws_for(cfg, Pcap)
+    A = torch.empty(cfg.C, cfg.d, dtype=torch.bfloat16, device=DEV)
+    dg_ctx.set_rope(10000.0)
+    try:
+        P_new = dg_ctx.prefill_block(cfg, i32_dev(tok), Wd["E"], Wd["Wq"], Wd["Wk"], Wd["Wv"], Wd["Wo"],
+                                     Kd, Vtd, P, ws, A)
+        dg_ctx.sync()
+    finally:
+        dg_ctx.set_rope(0.0)
+    assert P_new == P + cfg.C == Pcap
+    Kg, Vg = cache_logical(Kd, Vtd)
+    K_r, V_r = Kp.copy(), Vp.copy()
+    A_r, P_r = O.prefill_block(tok, W["E"], W["Wq"], W["Wk"], W["Wv"], W["Wo"], K_r, V_r, P,
+                               cfg.Hq, cfg.Hkv, cfg.hd, 10000.0)
+    assert P_r == Pcap
+    np.testing.assert_array_equal(Kg[:, :P], Kp[:, :P])
+    np.testing.assert_array_equal(Vg[:, :P], Vp[:, :P])
+    assert maxrel(O.from_bf16(Kg[:, P:]), O.from_bf16(K_r[:, P:])) <= 2e-2
+    assert maxrel(O.from_bf16(Vg[:, P:]), O.from_bf16(V_r[:, P:])) <= 2e-2
+    Ag = O.from_bf16(bits_np(A))
+    assert np.all(np.isfinite(Ag))
+    assert maxrel(Ag[ROWS], O.from_bf16(A_r)[ROWS]) <= 2e-2
+
+
+def test_batched_sampler_head_full_vocab(dg_ctx):
+    # the B = 2 batched line's launch configuration: both canvases' 512 columns in one
+    # dg_logits_entropy / dg_selfcond pass over the 262144-token vocabulary
+    cfg, W, Wd = full("gemma_head")
+    B, k = 2, 40
+    dims = dg.Dims(cfg.V, cfg.d, B * cfg.C, cfg.Hq, cfg.Hkv, cfg.hd, cfg.F)
+    ws = torch.empty(dg.workspace_bytes(dims, cfg.Pcap), dtype=torch.uint8, device=DEV)
+    H = np.concatenate([di.hidden(cfg, W["E"], b, k) for b in range(B)], axis=0)
+    tau = O.temperature(k, cfg.N)
+    ent = torch.empty(B * cfg.C, dtype=torch.float32, device=DEV)
+    am = torch.empty(B * cfg.C, dtype=torch.int32, device=DEV)
+    dg_ctx.logits_entropy(dims, bf16_dev(H), Wd["E"], tau, ws, ent, am)
+    z = torch.empty(B * cfg.C, cfg.d, dtype=torch.bfloat16, device=DEV)
+    dg_ctx.selfcond(dims, ws, Wd["E"], Wd["W1"], Wd["W2"], z)
+    dg_ctx.sync()
+    e, a = ent.cpu().numpy(), am.cpu().numpy()
+    assert np.all(np.isfinite(e)) and e.min() >= 0.0 and e.max() <= math.log(cfg.V) + 1e-3
+    rows = [0, 131, 255, 256, 400, 511]                 # both canvases, both column blocks
+    ent_r, am_r, p_r, u_r = O.logits_entropy(H, W["E"], tau, rows=rows)
+    assert np.max(np.abs(e[rows] - ent_r)) <= 1e-3
+    assert argmax_mismatch_unexcused(a[rows], am_r, u_r) == 0
+    z_r, _ = O.selfcond(p_r, W["E"], W["W1"], W["W2"])
+    assert maxrel(O.from_bf16(bits_np(z)[rows]), O.from_bf16(z_r)) <= 2e-2
