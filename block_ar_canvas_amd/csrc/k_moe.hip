@@ -132,10 +132,6 @@ __global__ __launch_bounds__(256) void moe_group_kernel(const int *sel, int C, i
   }
 }
 
-// LDS slot of the 16-byte chunk q (of 16) of activation row m: XOR swizzle so that the
-// 32 rows read by one MFMA operand load fall in distinct banks.
-DG_DEV int xslot(int m, int q) { return m * 256 + ((q ^ (m & 15)) << 4); }
-
 DG_DEV f32x4_t mfma_16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
@@ -158,6 +154,8 @@ DG_DEV f32x4_t mfma_16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
 // two workgroups per CU.
 constexpr int XW = 128 * 256, XX = MOE_TM * 256, XSTAGE = XW + XX, XSMEM = 2 * XSTAGE;
 
+// LDS byte offset of 16-byte chunk q (of 16) of a 256-byte row: XOR-swizzled by the row's
+// low 4 bits, so the 16 rows one operand read touches fall in distinct bank groups.
 DG_DEV int xswz(int row, int q) { return row * 256 + ((q ^ (row & 15)) << 4); }
 
 __global__ __launch_bounds__(256) void moe_expert_kernel(MoeGemmArgs a) {
