@@ -514,7 +514,21 @@ def chain(ctx, commit="projection", rope_base=0.0):
             loop.commit(x0)
         e1.record(stream)
         e1.synchronize()
-        out["prefill_ms_per_call"] = round(e0.elapsed_time(e1) / 10, 4)
+        ms = e0.elapsed_time(e1) / 10
+        out["prefill_ms_per_call"] = round(ms, 4)
+        # algorithmic work of one prefill call: the cache rows it reads, its weights, the
+        # gathered embedding rows and its outputs; causal attention over P_end + i + 1 keys
+        # for block row i, plus the QKV and Wo products
+        qkv = (cc.Hq + 2 * cc.Hkv) * cc.hd
+        pbytes = (2 * cc.Hkv * P_end * cc.hd * 2 + (qkv * cc.d + cc.d * cc.Hq * cc.hd) * 2
+                  + cc.C * cc.d * 2 + 2 * cc.Hkv * cc.C * cc.hd * 2 + cc.C * cc.d * 2)
+        pflops = (4.0 * cc.Hq * cc.hd * (cc.C * P_end + cc.C * (cc.C + 1) / 2)
+                  + 2.0 * cc.C * cc.d * qkv + 2.0 * cc.C * cc.Hq * cc.hd * cc.d)
+        out["prefill_keys"] = P_end + cc.C
+        out["prefill_GBs"] = round(pbytes / (ms * 1e-3) / 1e9, 1)
+        out["prefill_hbm_frac"] = round(pbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        out["prefill_tflops"] = round(pflops / (ms * 1e-3) / 1e12, 1)
+        out["prefill_mfma_frac"] = round(pflops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
         out["prefill_prefix_tokens"] = P_end
     ctx.set_rope(0.0)
     return out
