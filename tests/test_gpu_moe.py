@@ -28,6 +28,9 @@ CASES = {
     "skewed": dict(C=300, d=160, E=4, K=2, Fe=96, Fs=64),
     "one_token": dict(C=1, d=64, E=8, K=2, Fe=32, Fs=32),
     "single_expert": dict(C=37, d=64, E=1, K=1, Fe=32, Fs=32),      # one group of every row
+    # router logits in 2 and 4 k parts (d 512 and 1024; d 2048 above takes 8)
+    "router_parts2": dict(C=48, d=512, E=8, K=2, Fe=32, Fs=64),
+    "router_parts4": dict(C=64, d=1024, E=16, K=2, Fe=64, Fs=32),
     # canvas rows sharing a direction (the bench's routing structure: about 84 experts)
     "canvas_shared": dict(C=256, d=2048, E=128, K=8, Fe=512, Fs=1024, share=0.56),
     "all_experts": dict(C=20, d=64, E=4, K=4, Fe=32, Fs=32),
