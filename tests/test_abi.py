@@ -1,7 +1,7 @@
 """The C-ABI library loads and exports every declared symbol (no GPU needed).
 
-Only host-pure entry points are called here (dg_temperature, dg_workspace_bytes);
-nothing launches a kernel.
+Only host-pure entry points are called here (dg_temperature, dg_reveal_count,
+dg_workspace_bytes, dg_moe_workspace_bytes); nothing launches a kernel.
 """
 import ctypes
 import os
@@ -80,6 +80,25 @@ def test_workspace_bytes(lib):
     assert dg.workspace_bytes(big, 262400) >= dg.workspace_bytes(big, 8448)
     with pytest.raises(dg.DGError):
         dg.workspace_bytes(big.with_(hd=48), 1024)
+
+
+def test_moe_workspace_bytes(lib):
+    import block_ar_canvas_amd as dg
+
+    md = dg.MoeDims(2048, 128, 8, 512, 1024)
+    n = dg.moe_workspace_bytes(md, 256)
+    # at least: fp32 router logits, the grouped hidden rows and expert outputs (bf16)
+    assert n >= 256 * 128 * 4 + 256 * 8 * (512 + 2048) * 2
+    assert dg.moe_workspace_bytes(md, 512) > n
+    assert dg.moe_workspace_bytes(md, 1024) > 0           # C * K = 8192, the limit
+    for bad, C in ((dg.MoeDims(64, 16, 20, 32, 64), 8),   # K > E
+                   (dg.MoeDims(64, 16, 4, 40, 64), 8),    # Fe not a multiple of 32
+                   (dg.MoeDims(64, 300, 4, 32, 64), 8),   # E > 256
+                   (dg.MoeDims(64, 16, 33, 32, 64), 8),   # K > 32
+                   (dg.MoeDims(2048, 128, 8, 512, 1024), 1025),   # C > 1024
+                   (dg.MoeDims(64, 64, 16, 32, 64), 600)):        # C * K > 8192
+        with pytest.raises(dg.DGError):
+            dg.moe_workspace_bytes(bad, C)
 
 
 def test_binding_rejects_host_tensors(lib):
