@@ -10,6 +10,10 @@
  *   dg_selfcond        self-conditioning z = FFW(p0 . E)
  *   dg_stop_test       adaptive stop (mean entropy and stable argmax) / step cap
  * and, once per canvas, dg_commit_kv appends the finalized block to the KV cache.
+ * Beyond that step: dg_prefill_block (the causal re-encode commit) with dg_set_rope,
+ * dg_confidence / dg_topk_accept / dg_reveal_count (confidence-ranked acceptance),
+ * dg_sample (sampled tokens), dg_moe_ffn (the canvas mixture-of-experts FFN), and the
+ * measured ceilings dg_peak_stream_read / dg_peak_mfma_bf16.
  * The method is the DiffusionGemma inference loop as summarized by the
  * "DiffusionGemma Technical Report" page (paper.rainbus.top/paper/2608.00146),
  * section "Method steps" (1)-(5), with the sampler hyper-parameters of its
@@ -25,7 +29,9 @@
  *    Rows / columns [0, P) hold the prefix; [P, Pcap) is free capacity.
  *  - Calls validate their arguments on the host, enqueue work on the context's HIP
  *    stream and return without waiting. No call allocates or frees device memory;
- *    scratch space comes from the caller's workspace (dg_workspace_bytes).
+ *    scratch space comes from the caller's workspace (dg_workspace_bytes,
+ *    dg_moe_workspace_bytes). The context itself holds a status word, made by
+ *    dg_create, and the second stream and events that the first dg_moe_ffn call makes.
  *  - On a non-OK return nothing was enqueued; dg_last_error() describes the problem.
  *  - Conditions only the device can see (a token id outside [0, V), non-finite
  *    logits) set a sticky status word in the context, reported by dg_sync().
