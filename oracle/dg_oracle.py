@@ -49,10 +49,9 @@ Readings taken where the pages leave a step open (each restated where it is used
     previous step; otherwise the step cap N - 1 commits anyway;
   * commit: the finalized block is x^0 = argmax at the stopping step; its K/V rows are
     E[x^0] Wk^T and E[x^0] Wv^T (stand-in for the causal re-encode), appended at [P, P+C).
-  * sampled tokens (an alternative to x^0 = argmax): x~ ~ p^0 drawn in two stages, a
-    256-id vocabulary chunk by inverse CDF over chunk masses with one Philox uniform,
-    then Gumbel-max inside the chunk with Philox-driven Gumbel noise; accepted positions
-    and the commit take x~, the stop test still compares argmaxes;
+  * sampled tokens (an alternative to x^0 = argmax): x~ ~ p^0 drawn by inverse CDF over
+    the whole vocabulary with one Philox uniform per position; accepted positions and
+    the commit take x~, the stop test still compares argmaxes;
   * the commit as a causal re-encode (an alternative to the projection stand-in): one
     attention layer over the prefix and the block's earlier tokens, with rotary positions
     when a base is given, appends the block's rotated K and its V;
@@ -273,20 +272,17 @@ def confidence(H_bits, E_bits, tau, rows=None):
 
 
 def reveal_schedule(C: int, N: int):
-    """Number of positions revealed after each step of the [HUB] decoder.
+    """Number of positions revealed after each step of confidence decoding.
 
-    The page's simplified decoder starts with C masked positions and at step s reveals
-    ceil(unresolved / remaining) of them, remaining = N - s, with the same C positions
-    never revealed twice. Counted here by running that bookkeeping: a list of the
-    cumulative revealed counts after steps 0 .. N-1 (the last one is C).
+    [HUB] step 4: each step reveals ceil(unresolved / remaining steps) positions, so the
+    count after step t is n_t = n_{t-1} + ceil((C - n_{t-1}) / (N - t)) with n_{-1} = 0.
+    Returns [n_0, ..., n_{N-1}]; n_{N-1} = C.
     """
-    unresolved = C
     out = []
-    for s in range(N):
-        remaining = N - s
-        reveal = min(-(-unresolved // remaining), unresolved)
-        unresolved -= reveal
-        out.append(C - unresolved)
+    n = 0
+    for t in range(N):
+        n += -(-(C - n) // (N - t))
+        out.append(n)
     return out
 
 
@@ -337,8 +333,7 @@ def philox4x64_10(counter, key):
 
 
 STREAM_RENOISE, STREAM_INIT = 0, 1
-STREAM_CHUNK, STREAM_GUMBEL = 2, 3
-SAMPLE_CHUNK = 256          # vocabulary ids per chunk of the two-stage draw
+STREAM_SAMPLE = 2           # the uniform of a sampled token
 
 
 def uniform_token(seed, canvas, step, stream, pos, V) -> int:
@@ -376,61 +371,47 @@ def renoise(argmax, accept, seed, canvas_base, step, V):
 
 
 # ------------------------------------------------------------------ sampled tokens
-def gumbel_noise(seed, canvas, step, pos, v) -> float:
-    """G_v = -ln(-ln U), U = (h + 1/2) / 2^32, h the 32-bit half v mod 2 (0 = low) of word
-    (v mod 8) / 2 of Philox4x64-10 with counter (pos, step, 3, v / 8), key (seed, canvas)."""
-    w = philox4x64_10((pos, step, STREAM_GUMBEL, v // 8), (seed, canvas))[(v % 8) // 2]
-    h = (w >> 32) if (v % 2) else (w & 0xFFFFFFFF)
-    return -math.log(-math.log((h + 0.5) / 4294967296.0))
+def sample_uniform(seed, canvas, step, pos) -> float:
+    """The uniform of a sampled token: u = (word 0 >> 11) / 2^53 in [0, 1), from
+    Philox4x64-10 with key (seed, canvas) and counter (pos, step, 2, 0)."""
+    w = philox4x64_10((pos, step, STREAM_SAMPLE, 0), (seed, canvas))[0]
+    return (w >> 11) * 2.0 ** -53
 
 
 def sample_tokens(p, seed, canvas_base, step, B=1, with_margins=False, positions=None):
     """Sampled tokens x~ ~ p^0, the sampled-token alternative to x^0 = argmax.
 
-    [HUB] step 4 notes that real samplers draw with temperature and Gumbel noise instead
-    of always taking the most likely token. The draw (an exact sample from p):
-      1. split the vocabulary into chunks of 256 consecutive ids and pick the first chunk
-         whose running probability mass exceeds u1 = (Philox word 0 of counter
-         (pos, step, 2, 0) >> 11) / 2^53 (inverse CDF over the chunk masses);
-      2. inside the chunk take argmax_v ln p_v + G_v (Gumbel-max, ties to the lower id).
+    [HUB] step 4 notes that real samplers draw from the tempered distribution instead of
+    always taking the most likely token. The draw is the textbook inverse CDF over the
+    whole vocabulary in id order: with one uniform u per position (sample_uniform), the
+    token is the first id v whose cumulative probability sum_{v' <= v} p_v' exceeds
+    u times the total.
     p float64 [B * Cs, V] (rows = canvas b position i at b * Cs + i); canvas id =
     canvas_base + b. Returns int32 tokens; with_margins also returns, per row, the
-    distance of u1 to the nearest chunk boundary of the cumulative mass and the gap
-    between the best and second-best Gumbel score inside the chosen chunk. ``positions``
-    (B = 1 only) gives the canvas position of each row when p holds a subset of rows.
+    distance (in probability) from u times the total to the nearest cumulative boundary,
+    i.e. how far the draw is from picking a neighbouring id. ``positions`` (B = 1 only)
+    gives the canvas position of each row when p holds a subset of rows.
     """
     p = np.asarray(p, dtype=np.float64)
     rows, V = p.shape
     Cs = rows // B
-    nch = -(-V // SAMPLE_CHUNK)
     out = np.zeros(rows, dtype=np.int32)
-    m_chunk = np.zeros(rows)
-    m_gap = np.zeros(rows)
+    margin = np.zeros(rows)
     for r in range(rows):
         b, i = divmod(r, Cs)
         if positions is not None:
             b, i = 0, int(positions[r])
-        canvas = canvas_base + b
-        w = philox4x64_10((i, step, STREAM_CHUNK, 0), (seed, canvas))[0]
-        u1 = (w >> 11) * 2.0 ** -53
-        masses = np.array([p[r, t * SAMPLE_CHUNK:(t + 1) * SAMPLE_CHUNK].sum() for t in range(nch)])
-        cum = np.cumsum(masses)
-        t = int(np.searchsorted(cum, u1 * cum[-1], side="right"))
-        t = min(t, nch - 1)
-        lo = cum[t - 1] if t > 0 else 0.0
-        m_chunk[r] = min(abs(u1 * cum[-1] - lo), abs(cum[t] - u1 * cum[-1])) / cum[-1]
-        ids = range(t * SAMPLE_CHUNK, min(V, (t + 1) * SAMPLE_CHUNK))
-        scores = []
-        for v in ids:
-            pv = p[r, v]
-            scores.append(-math.inf if pv <= 0.0 else math.log(pv) + gumbel_noise(seed, canvas, step, i, v))
-        sc = np.array(scores)
-        j = int(np.argmax(sc))                     # first maximum = lower id
-        out[r] = t * SAMPLE_CHUNK + j
-        srt = np.sort(sc)
-        m_gap[r] = srt[-1] - srt[-2] if len(srt) > 1 else math.inf
+        u = sample_uniform(seed, canvas_base + b, step, i)
+        cum = np.cumsum(p[r])
+        target = u * cum[-1]
+        v = int(np.searchsorted(cum, target, side="right"))
+        if v >= V:                                  # u * total rounded onto the total
+            v = int(np.nonzero(p[r] > 0)[0][-1])
+        out[r] = v
+        lo = cum[v - 1] if v > 0 else 0.0
+        margin[r] = min(target - lo, cum[v] - target)
     if with_margins:
-        return out, m_chunk, m_gap
+        return out, margin
     return out
 
 
@@ -560,18 +541,17 @@ def prefill_block(tokens, E_bits, Wq, Wk, Wv, Wo, Kp, Vp, P, Hq, Hkv, hd, rope_b
 def moe_route(X_bits, Wr, K):
     """Router of the canvas MoE FFN ([MOE]): logits r = X Wr^T; each token takes the K
     experts with the largest logits (ties to the lower expert id) and gates them with a
-    softmax over those K logits. The selection is decided on the logits rounded to float32
-    (the device's precision for this discrete decision); gates in float64.
-    Returns (experts int32 [C, K] in rank order, gates float64 [C, K], logits float32 [C, E])."""
+    softmax over those K logits. Selection and gates are taken on the float64 logits.
+    Returns (experts int32 [C, K] in rank order, gates float64 [C, K], logits float64 [C, E])."""
     X = from_bf16(X_bits)
-    r = (X @ from_bf16(Wr).T).astype(np.float32)
+    r = X @ from_bf16(Wr).T
     C, E = r.shape
     sel = np.zeros((C, K), dtype=np.int32)
     gates = np.zeros((C, K))
     for t in range(C):
         order = sorted(range(E), key=lambda e: (-float(r[t, e]), e))[:K]
         sel[t] = order
-        v = r[t, order].astype(np.float64)
+        v = r[t, order]
         w = np.exp(v - v.max())
         gates[t] = w / w.sum()
     return sel, gates, r
@@ -632,8 +612,8 @@ def run_canvas(W, Kp, Vp, P, hidden_of_step, *, V, C, Hq, Hkv, hd, N, seed, canv
         ent, am, p, _ = logits_entropy(hidden_of_step(k), W["E"], tau)
         x0 = am
         if draw == "sample":
-            x0, m_chunk, m_gap = sample_tokens(p, seed, canvas, k, with_margins=True)
-            rec.update(sampled=x0, sample_margin_chunk=m_chunk, sample_margin_gap=m_gap)
+            x0, margin = sample_tokens(p, seed, canvas, k, with_margins=True)
+            rec.update(sampled=x0, sample_margin=margin)
         if rule == "confidence":
             conf = p.max(axis=1).astype(np.float32)
             acc, nacc = topk_accept(conf[None], schedule[k])

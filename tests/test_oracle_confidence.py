@@ -3,7 +3,8 @@
 The rule (openai-hub page "从零拆开DiffusionGemma", step 4, confidence decoding; "Text
 diffusion models" survey, section 5): a position's confidence is its largest tempered
 probability, and each step keeps the most confident positions, as many as the page's
-simplified decoder has revealed by then (ceil(unresolved / remaining steps) per step).
+simplified decoder has revealed by then (ceil(unresolved / remaining steps) per step),
+pinned by the closed form that rule reduces to.
 """
 import math
 
@@ -55,34 +56,36 @@ def test_confidence_one_hot_limit_and_scipy():
 
 
 # ------------------------------------------------------------------ reveal schedule
-def page_decoder_reveals(C, N, rng):
-    """Runs the page's decoder bookkeeping literally: a canvas of masked flags, random
-    confidences each step, reveal count ceil(unresolved / remaining), top-k among the
-    still-masked positions. Returns the number of revealed positions after each step."""
-    masked = np.ones(C, dtype=bool)
-    out = []
-    for step in range(N):
-        conf = rng.random(C)
-        conf[~masked] = -1.0
-        remaining = N - step
-        unresolved = int(masked.sum())
-        k = min(math.ceil(unresolved / remaining), unresolved)
-        if k:
-            chosen = np.argsort(-conf, kind="stable")[:k]
-            assert masked[chosen].all()
-            masked[chosen] = False
-        out.append(C - int(masked.sum()))
-    return out
+# The rule as the page states it: each step reveals ceil(unresolved / remaining steps),
+# i.e. n_t = n_{t-1} + ceil((C - n_{t-1}) / (N - t)) with n_{-1} = 0. Writing C = qN + r
+# (0 <= r < N): while t < r the unresolved count is (N - t) q + (r - t) with
+# 0 < r - t < N - t, so the step reveals q + 1; from t = r on it is (N - t) q, so the step
+# reveals q. Hence the closed form n_t = (t + 1) q + min(t + 1, r).
+def closed_form(C, N):
+    q, r = divmod(C, N)
+    return [(t + 1) * q + min(t + 1, r) for t in range(N)]
 
 
-@pytest.mark.parametrize("C,N", [(256, 48), (16, 8), (100, 7), (5, 9), (1, 1), (1000, 48)])
-def test_reveal_schedule_is_the_page_decoder(C, N):
-    rng = np.random.default_rng(C * 131 + N)
+def test_reveal_schedule_hand_worked():
+    # C = 5 over N = 9: one position per step until all five are out, then none
+    assert O.reveal_schedule(5, 9) == [1, 2, 3, 4, 5, 5, 5, 5, 5]
+    # C = 256 over N = 48: 256 = 5 * 48 + 16, six per step for 16 steps, then five
+    sched = O.reveal_schedule(256, 48)
+    assert sched[:4] == [6, 12, 18, 24]
+    assert sched[15:18] == [96, 101, 106]
+    assert sched[-2:] == [251, 256]
+    assert [b - a for a, b in zip([0] + sched, sched)] == [6] * 16 + [5] * 32
+    # C = 1 over N = 1 and C = 0
+    assert O.reveal_schedule(1, 1) == [1]
+    assert O.reveal_schedule(0, 4) == [0, 0, 0, 0]
+
+
+@pytest.mark.parametrize("C,N", [(256, 48), (16, 8), (100, 7), (5, 9), (1, 1), (1000, 48), (47, 48), (49, 48)])
+def test_reveal_schedule_closed_form(C, N):
     sched = O.reveal_schedule(C, N)
-    assert sched == page_decoder_reveals(C, N, rng)
+    assert sched == closed_form(C, N)
     assert sched[-1] == C
     assert all(a <= b for a, b in zip(sched, sched[1:]))
-    assert sched[0] == math.ceil(C / N) if C else sched[0] == 0
 
 
 def test_reveal_schedule_linear_when_divisible():
