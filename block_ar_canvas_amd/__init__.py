@@ -193,6 +193,14 @@ class Context:
     def stream(self):
         return self._stream
 
+    def torch_stream(self):
+        """The context's stream as a torch stream object, for torch work (fills, copies)
+        that must stay ordered with the library's calls."""
+        s = self._stream
+        if isinstance(s, torch.cuda.Stream):
+            return s
+        return torch.cuda.ExternalStream(self._raw_stream(s) or 0, device=torch.device("cuda", self.device))
+
     def sync(self):
         self._check(self._lib.dg_sync(self._h))
 

@@ -29,17 +29,18 @@
 // entropy rule: distinct 64-bit keys (score order, position), rank = keys below one's
 // own, accepted iff rank < k.
 //
-// Sampled tokens (same openai-hub step: real samplers draw with temperature and Gumbel
-// noise instead of taking the argmax): x~ ~ p0 in two stages that together are an exact
-// draw from p0. (1) Pick the 256-id vocabulary chunk t (a logits tile) with probability
-// proportional to its mass M_t = Z_t 2^(rho_t - R), from the tile statistics (float32
-// sums, prefix in float64), by inverse CDF: the first t whose running mass exceeds u1
-// times the total, u1 = (word 0 of counter (position, step, 2, 0)) / 2^64 on 53 bits.
-// (2) Inside the chunk, Gumbel-max over ln p~_v + G_v, G_v = -ln(-ln U_v), U_v = (h +
-// 1/2) / 2^32 with h the 32-bit half v mod 2 of word (v mod 8) / 2 of counter
-// (position, step, 3, v / 8); p~ is the stored bf16 2^(x - rho_t), whose common scale in
-// the chunk does not move the argmax.
+// Sampled tokens (same openai-hub step: real samplers draw from the tempered
+// distribution instead of taking the argmax): x~ ~ p0 by inverse CDF over the whole
+// vocabulary in id order, with one uniform u = (word 0 of counter (position, step, 2, 0)
+// >> 11) / 2^53 per position: the token is the first id whose cumulative probability
+// exceeds u times the total. Here in two levels that reach the same id: (1) the logits
+// tile t (256 ids) holding the crossing, from the running sum of the tile masses
+// M_t = Z_t 2^(rho_t - R) (float32 tile sums, prefix in float64); (2) inside the tile,
+// the first id whose running sum of the stored bf16 p~_v = 2^(x_v - rho_t) exceeds the
+// rest of the target, rescaled to the tile's units by the exact power 2^(R - rho_t).
 #include <float.h>
+
+#include <climits>
 
 #include "dg_common.h"
 
@@ -168,9 +169,10 @@ __global__ __launch_bounds__(256) void renoise_kernel(int B, int C, int V, const
 
 // One workgroup per canvas column (canvas b = column / Cs, position = column % Cs).
 __global__ __launch_bounds__(256) void sample_kernel(SampleArgs a) {
-  __shared__ double sbest[4];
-  __shared__ int sidx[4];
+  __shared__ double swave[4];
+  __shared__ double sbefore;
   __shared__ int st_star;
+  __shared__ int sfirst[4], slast[4];
   const int c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = c / a.Cs, pos = c % a.Cs;
   const uint64_t key1 = (uint64_t)(a.canvas_base + (uint32_t)b);
@@ -183,7 +185,7 @@ __global__ __launch_bounds__(256) void sample_kernel(SampleArgs a) {
   const float *tr = a.trho + (int64_t)c * a.T;
   auto mass = [&](int t) { return (double)tz[t] * ldexp(1.0, (int)(tr[t] - R)); };
 
-  // (1) the chunk: thread tid owns tiles [t0, t1); masses summed in tile order
+  // (1) the tile: thread tid owns tiles [t0, t1); masses summed in tile order
   const int per = (a.T + 255) / 256;
   const int t0 = min(tid * per, a.T), t1 = min(t0 + per, a.T);
   double loc = 0.0;
@@ -198,62 +200,72 @@ __global__ __launch_bounds__(256) void sample_kernel(SampleArgs a) {
   }
   double ex = __shfl_up(incl, 1);
   if (lane == 0) ex = 0.0;
-  if (lane == 63) sbest[wave] = incl;
+  if (lane == 63) swave[wave] = incl;
   if (tid == 0) st_star = -1;
   __syncthreads();
   double woff = 0.0;
-  for (int i = 0; i < wave; ++i) woff += sbest[i];
-  const double total = ((sbest[0] + sbest[1]) + sbest[2]) + sbest[3];
+  for (int i = 0; i < wave; ++i) woff += swave[i];
+  const double total = ((swave[0] + swave[1]) + swave[2]) + swave[3];
   uint64_t w[4] = {(uint64_t)pos, (uint64_t)a.step, 2ull, 0ull};
   philox4x64_10(w, a.seed, key1);
-  const double u1 = (double)(w[0] >> 11) * 0x1.0p-53;
-  const double target = u1 * total;
+  const double u = (double)(w[0] >> 11) * 0x1.0p-53;
+  const double target = u * total;
   const double excl = woff + ex;
   if (t0 < t1 && excl <= target && excl + loc > target) {
     double run = excl;
     int t = t0;
     for (; t < t1 - 1; ++t) {
-      run += mass(t);
-      if (run > target) break;
+      const double next = run + mass(t);
+      if (next > target) break;
+      run = next;
     }
     st_star = t;                                     // exactly one thread crosses
+    sbefore = run;                                   // mass of the tiles before t
   }
   __syncthreads();
   int ts = st_star;
-  if (ts < 0) {                                      // rounding left target >= total:
-    ts = a.T - 1;                                    // the last tile with mass
+  const bool past_end = ts < 0;                      // rounding left target >= total:
+  if (past_end) {                                    // the last id with mass
+    ts = a.T - 1;
     while (ts > 0 && !(mass(ts) > 0.0)) --ts;
   }
+  // the rest of the target in the tile's own units (p~ sums to about Z_t there)
+  const double rest = past_end ? INFINITY : (target - sbefore) * ldexp(1.0, (int)(R - tr[ts]));
 
-  // (2) Gumbel-max over the chunk's ids
+  // (2) inverse CDF inside the tile: inclusive running sum of p~ over the tile's ids
   const int v = ts * 256 + tid;
-  double score = -INFINITY;
+  double pv = 0.0;
   if (v < a.V) {
     const int64_t off = (((int64_t)(c >> 5) * a.VS + (v >> 4)) * 64 + ((v & 15) >> 3) * 32 + (c & 31)) * 8 + (v & 7);
-    const float pv = __uint_as_float((uint32_t)a.ptilde[off] << 16);
-    if (pv > 0.f) {
-      uint64_t g[4] = {(uint64_t)pos, (uint64_t)a.step, 3ull, (uint64_t)(v >> 3)};
-      philox4x64_10(g, a.seed, key1);
-      const uint64_t word = g[(v & 7) >> 1];
-      const uint32_t h = (v & 1) ? (uint32_t)(word >> 32) : (uint32_t)word;
-      const double U = ((double)h + 0.5) * 0x1.0p-32;
-      score = log((double)pv) - log(-log(U));
-    }
+    pv = (double)__uint_as_float((uint32_t)a.ptilde[off] << 16);
   }
-  int bi = v;
+  double cum = pv;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const double s2 = __shfl_xor(score, o);
-    const int i2 = __shfl_xor(bi, o);
-    if (s2 > score || (s2 == score && i2 < bi)) { score = s2; bi = i2; }
+  for (int o = 1; o < 64; o <<= 1) {
+    const double y = __shfl_up(cum, o);
+    if (lane >= o) cum += y;
   }
+  __syncthreads();                                   // swave reuse
+  if (lane == 63) swave[wave] = cum;
   __syncthreads();
-  if (lane == 0) { sbest[wave] = score; sidx[wave] = bi; }
+  for (int i = 0; i < wave; ++i) cum += swave[i];
+  // the first id whose running sum exceeds the rest (it has p~ > 0); if rounding left
+  // none, the last id with p~ > 0
+  const uint64_t over = __ballot(cum > rest);
+  const uint64_t pos_mask = __ballot(pv > 0.0);
+  if (lane == 0) {
+    sfirst[wave] = over ? wave * 64 + __builtin_ctzll(over) : INT_MAX;
+    slast[wave] = pos_mask ? wave * 64 + 63 - __builtin_clzll(pos_mask) : -1;
+  }
   __syncthreads();
   if (tid == 0) {
-    for (int i = 1; i < 4; ++i)
-      if (sbest[i] > score || (sbest[i] == score && sidx[i] < bi)) { score = sbest[i]; bi = sidx[i]; }
-    a.tokens[c] = bi;
+    int first = INT_MAX, last = -1;
+    for (int i = 0; i < 4; ++i) {
+      first = min(first, sfirst[i]);
+      last = max(last, slast[i]);
+    }
+    const int j = first != INT_MAX ? first : (last >= 0 ? last : 0);
+    a.tokens[c] = ts * 256 + j;
   }
 }
 

@@ -90,11 +90,11 @@ class CanvasLoop:
         ev = self.logits_events
         if ev is not None:
             e0 = torch.cuda.Event(enable_timing=True)
-            e0.record(self.ctx._stream)
+            e0.record(self.ctx.torch_stream())
         self.ctx.logits_entropy(dm, H, W["E"], tau, self.ws, self.entropy, am)
         if ev is not None:
             e1 = torch.cuda.Event(enable_timing=True)
-            e1.record(self.ctx._stream)
+            e1.record(self.ctx.torch_stream())
             ev.append((e0, e1))
         x0 = am
         if self.draw == "sample":
@@ -149,7 +149,8 @@ class CanvasLoop:
         uses step k's own argmax buffer, which step k + 1 does not write).
         """
         self.init_canvas(canvas)
-        self.z.zero_()
+        with torch.cuda.stream(self.ctx.torch_stream()):
+            self.z.zero_()
         k = 0
         self.step(0, hidden(0))
         if on_step is not None:
@@ -230,7 +231,8 @@ class BatchLoop:
         """Uniform random canvases (init stream) for canvas ids batch*B .. batch*B+B-1, z = 0."""
         self.batch = batch
         self.ctx.renoise(self.dims.V, None, None, self.seed, batch * self.B, 0, self.tokens)
-        self.z.zero_()
+        with torch.cuda.stream(self.ctx.torch_stream()):
+            self.z.zero_()
         self._slot = {}
 
     def step(self, k: int, H):
@@ -246,12 +248,12 @@ class BatchLoop:
         ev = self.logits_events
         if ev is not None:
             e0 = torch.cuda.Event(enable_timing=True)
-            e0.record(self.ctx._stream)
+            e0.record(self.ctx.torch_stream())
         self.ctx.logits_entropy(self.dims_all, H, W["E"], tau, self.ws, self.entropy.view(-1),
                                 am.view(-1))
         if ev is not None:
             e1 = torch.cuda.Event(enable_timing=True)
-            e1.record(self.ctx._stream)
+            e1.record(self.ctx.torch_stream())
             ev.append((e0, e1))
         x0 = am
         if self.draw == "sample":
@@ -306,7 +308,10 @@ class BatchLoop:
             flags = self.wait_flags(k)
             for i in range(B):
                 if x0[i] is None and flags[i] != STOP_GO:
-                    x0[i] = (self.sampled if self.draw == "sample" else self.argmax)[k & 1][i].clone()
+                    # the copy is ordered on the context's stream before step k + 2, the
+                    # next writer of this buffer
+                    with torch.cuda.stream(self.ctx.torch_stream()):
+                        x0[i] = (self.sampled if self.draw == "sample" else self.argmax)[k & 1][i].clone()
                     steps[i] = k + 1
             if all(x is not None for x in x0):
                 break

@@ -159,18 +159,18 @@ dg_status dg_topk_accept(dg_ctx ctx, int32_t B, int32_t C, const float *score, i
                          uint8_t *accept, int32_t *n_accept);
 
 /* Sampled tokens x~ ~ p0, the sampled-token alternative to x0 = argmax (openai-hub page
- * "从零拆开DiffusionGemma", step 4: real samplers draw with temperature and Gumbel noise
+ * "从零拆开DiffusionGemma", step 4: real samplers draw from the tempered distribution
  * rather than always taking the most likely token). ws must hold the p0 of the
  * immediately preceding dg_logits_entropy with these dims (DG_ERR_STATE otherwise).
- * The draw, exact in distribution, for column c = b * Cs + i (canvas canvas_base + b,
- * position i, Cs = C / B), with Philox4x64-10 under key (seed, canvas_base + b):
- *  1. chunk t (vocabulary ids [256 t, 256 t + 256)) = the first chunk whose running
- *     probability mass exceeds u1, u1 = (word 0 of counter (i, step, 2, 0) >> 11) / 2^53;
- *  2. token = argmax over the chunk's ids v of ln p0[c][v] + G_v (ties: lower id),
- *     G_v = -ln(-ln((h + 1/2) / 2^32)), h = the 32-bit half (v mod 2; 0 = low) of word
- *     (v mod 8) / 2 of counter (i, step, 3, v / 8).
- * On the device, masses come from the float32 tile sums and step 2 uses the stored bf16
- * probabilities. tokens [C] int32 output (0 for a column with non-finite logits).
+ * The draw is the inverse CDF over the whole vocabulary in id order: for column
+ * c = b * Cs + i (canvas canvas_base + b, position i, Cs = C / B), with
+ * u = (word 0 of Philox4x64-10 under key (seed, canvas_base + b) and counter
+ * (i, step, 2, 0)) >> 11, divided by 2^53, the token is the first id v whose cumulative
+ * probability sum_{v' <= v} p0[c][v'] exceeds u times the total. On the device the
+ * cumulative comes from the float32 per-tile sums and, inside the tile that holds the
+ * crossing, from the stored bf16 probabilities, so a draw within about 2^-9 of that
+ * tile's mass of a boundary may take the neighbouring id.
+ * tokens [C] int32 output (0 for a column with non-finite logits).
  * DG_ERR_SHAPE unless B >= 1 divides C. */
 dg_status dg_sample(dg_ctx ctx, const dg_dims *dims, const void *ws, int32_t B, uint64_t seed,
                     uint32_t canvas_base, uint32_t step, int32_t *tokens);

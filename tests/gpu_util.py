@@ -55,6 +55,33 @@ def maxrel(got, ref) -> float:
     return float(np.max(np.abs(got - ref)) / (den if den > 0 else 1.0))
 
 
+def maxrel_rows(got, ref) -> float:
+    """The largest per-row relative error: max over rows of max|got_row - ref_row| /
+    max|ref_row| (the last axis is the row). A row whose reference is all zeros is
+    measured in absolute terms. Never below maxrel of the whole tensor: the row holding
+    the largest difference has a reference maximum no larger than the tensor's."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    got = got.reshape(-1, got.shape[-1])
+    ref = ref.reshape(-1, ref.shape[-1])
+    den = np.max(np.abs(ref), axis=1)
+    den = np.where(den > 0, den, 1.0)
+    return float(np.max(np.max(np.abs(got - ref), axis=1) / den))
+
+
+def sample_excused(p_row, ref_token: int, margin: float) -> bool:
+    """Whether a sampled token that differs from the oracle's draw is excused: the
+    oracle's u times the total lies within the device's rounding of a cumulative
+    boundary. The device sums float32 tile masses (relative error far below 2e-5) and,
+    inside the 256-id tile of the crossing, the bf16-stored probabilities (each within
+    2^-9 relative), so a boundary may move by up to 2^-9 of that tile's mass; the band is
+    twice that, taken over the tiles of the token and of the id before it."""
+    p_row = np.asarray(p_row, np.float64)
+    t = {ref_token // 256, max(ref_token - 1, 0) // 256}
+    mass = max(float(p_row[256 * j:256 * j + 256].sum()) for j in t)
+    return margin <= 2.0 ** -8 * mass + 2e-5 * float(p_row.sum())
+
+
 def near_tie(u_row: np.ndarray) -> bool:
     """Top-2 gap of the oracle's tempered logits within 1e-3 max(1, |u_top|)."""
     top2 = np.partition(u_row, -2)[-2:]

@@ -5,7 +5,7 @@ Canvas tokens must agree at >= 99.9% of positions over all steps; a mismatch is
 excused only where the two sides' acceptance differs at a position whose oracle entropy
 lies within 1e-4 of the cutoff (the entropy of the last accepted or first rejected
 position), or where the argmax differs at a near-tie of the oracle's logits. Entropies
-stay within 1e-3 nats, A and z within 2e-2 max relative error at every step, and the
+stay within 1e-3 nats, A and z within 2e-2 max relative error per row at every step, and the
 stop flags are identical. Under the confidence rule the accepted counts are equal and
 the cutoff excuse is a confidence within 2e-5 (relative) of the cutoff confidence.
 """
@@ -16,7 +16,7 @@ import dg_inputs as di
 import oracle as O
 from block_ar_canvas_amd import Context
 from block_ar_canvas_amd.loop import CanvasLoop
-from gpu_util import bf16_dev, bits_np, cache_logical, maxrel, near_tie, upload_cache, upload_weights
+from gpu_util import bf16_dev, bits_np, cache_logical, maxrel, maxrel_rows, near_tie, sample_excused, upload_cache, upload_weights
 
 pytestmark = pytest.mark.gpu
 
@@ -73,15 +73,26 @@ def run_both(dg_ctx, cfg, n_canvas=1, rule="entropy", draw="argmax", commit="pro
                         "flag": lp.wait_flag(k)})
 
         loop.run_canvas(c, lambda k: Hd[k], on_step=on_step)
+        P_prev = P_o
         P_o, recs = O.run_canvas(W, Kp, Vp, P_o, lambda k: Hs[k], V=cfg.V, C=cfg.C, Hq=cfg.Hq,
                                  Hkv=cfg.Hkv, hd=cfg.hd, N=cfg.N, seed=cfg.seed, canvas=c,
                                  rule=rule, draw=draw, commit=commit, rope_base=rope_base)
         assert [r["flag"] for r in rec] == [r["flag"] for r in recs]
-        for g, r in zip(rec, recs):
+        for j, (g, r) in enumerate(zip(rec, recs)):
             assert np.max(np.abs(g["entropy"] - r["entropy"])) <= 1e-3
-            assert maxrel(O.from_bf16(g["A"]), O.from_bf16(r["A"])) <= 2e-2
-            assert maxrel(O.from_bf16(g["z"]), O.from_bf16(r["z"])) <= 2e-2
-            _, _, _, u = O.logits_entropy(Hs[r["k"]], W["E"], r["tau"])
+            # A of step k is computed on that step's input canvas; where an excused token
+            # mismatch earlier in the loop left the device's canvas different from the
+            # oracle's, A is compared with the oracle's attention on the device's own input
+            # (A feeds nothing downstream in this loop, so nothing else is affected)
+            A_ref = r["A"]
+            if j > 0 and not np.array_equal(rec[j - 1]["tokens"], r["tokens_in"]):
+                A_ref, _ = O.canvas_attn(rec[j - 1]["tokens"], rec[j - 1]["z"], W["E"], W["Wq"],
+                                         W["Wk"], W["Wv"], W["Wo"], Kp, Vp, P_prev, cfg.Hq, cfg.Hkv,
+                                         cfg.hd, rope_base=rope_base)
+                stats["attn_on_device_input"] = stats.get("attn_on_device_input", 0) + 1
+            assert maxrel_rows(O.from_bf16(g["A"]), O.from_bf16(A_ref)) <= 2e-2
+            assert maxrel_rows(O.from_bf16(g["z"]), O.from_bf16(r["z"])) <= 2e-2
+            _, _, p_k, u = O.logits_entropy(Hs[r["k"]], W["E"], r["tau"])
             if rule == "confidence":
                 # the accepted count is the schedule's on both sides (no NaN here)
                 assert int(g["accept"].sum()) == int(r["accept"].sum())
@@ -99,9 +110,9 @@ def run_both(dg_ctx, cfg, n_canvas=1, rule="entropy", draw="argmax", commit="pro
                     near_cut = g["accept"][i] != r["accept"][i] and any(
                         abs(float(r["entropy"][i]) - x) <= 1e-4 for x in cut)
                 tie = g["argmax"][i] != r["argmax"][i] and near_tie(u[i])
-                if draw == "sample":       # accepted tokens are draws: the draw's own margins
-                    tie = g["sampled"][i] != r["sampled"][i] and (
-                        r["sample_margin_chunk"][i] <= 1e-5 or r["sample_margin_gap"][i] <= 2e-2)
+                if draw == "sample":       # accepted tokens are draws: the draw's own margin
+                    tie = g["sampled"][i] != r["sampled"][i] and sample_excused(
+                        p_k[i], int(r["sampled"][i]), float(r["sample_margin"][i]))
                 if not (near_cut or tie):
                     stats["unexcused"] += 1
             if draw == "sample":
