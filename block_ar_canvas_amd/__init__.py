@@ -14,11 +14,12 @@ import os
 import torch
 
 __all__ = ["DGError", "Dims", "MoeDims", "Context", "moe_workspace_bytes", "workspace_bytes", "temperature", "reveal_count", "lib_path",
-           "STOP_GO", "STOP_STOP", "STOP_CAP", "PEAK_STREAM_BLOCKS", "PEAK_MFMA_BLOCKS"]
+           "STOP_GO", "STOP_STOP", "STOP_CAP", "PEAK_STREAM_BLOCKS", "PEAK_MFMA_BLOCKS", "STATIC_SCRATCH_BYTES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 STOP_GO, STOP_STOP, STOP_CAP = 0, 1, 2
 PEAK_STREAM_BLOCKS, PEAK_MFMA_BLOCKS = 2048, 1024     # DG_PEAK_STREAM_BLOCKS, DG_PEAK_MFMA_BLOCKS
+STATIC_SCRATCH_BYTES = 48 << 20                         # DG_STATIC_SCRATCH_BYTES
 
 _STATUS = {0: "DG_OK", 1: "DG_ERR_NULL", 2: "DG_ERR_SHAPE", 3: "DG_ERR_ALIGN", 4: "DG_ERR_RANGE",
            5: "DG_ERR_CAPACITY", 6: "DG_ERR_STATE", 7: "DG_ERR_NONFINITE", 8: "DG_ERR_HIP",
@@ -75,6 +76,7 @@ def _load():
         "dg_workspace_bytes": (ctypes.c_size_t, [D, i64]),
         "dg_temperature": (f32, [i32, i32, f32, f32]),
         "dg_canvas_attn": (i32, [_P, D, _P, _P, _P, _P, _P, _P, _P, _P, _P, i64, i64, _P, _P]),
+        "dg_canvas_attn_static": (i32, [_P, D, _P, _P, _P, _P, _P, _P, _P, _P, _P, i64, i64, _P]),
         "dg_logits_entropy": (i32, [_P, D, _P, _P, f32, _P, _P, _P]),
         "dg_entropy_accept": (i32, [_P, i32, i32, _P, f32, _P, _P]),
         "dg_confidence": (i32, [_P, D, _P, _P]),
@@ -216,6 +218,16 @@ class Context:
             _ptr(E, _BF16, "E"), _ptr(Wq, _BF16, "Wq"), _ptr(Wk, _BF16, "Wk"), _ptr(Wv, _BF16, "Wv"),
             _ptr(Wo, _BF16, "Wo"), _ptr(Kp, _BF16, "Kp", True), _ptr(Vt, _BF16, "Vt", True),
             int(P), int(Pcap), _ptr(ws, _U8, "ws"), _ptr(A, _BF16, "A")))
+
+    def canvas_attn_static(self, dims, tokens, z, E, Wq, Wk, Wv, Wo, Kp, Vt, P, A):
+        """dg_canvas_attn on the library's static per-device scratch (no workspace)."""
+        d = Dims.of(dims)
+        Pcap = Kp.shape[1] if Kp is not None else 0
+        self._check(self._lib.dg_canvas_attn_static(
+            self._h, ctypes.byref(d), _ptr(tokens, _I32, "tokens"), _ptr(z, _BF16, "z", True),
+            _ptr(E, _BF16, "E"), _ptr(Wq, _BF16, "Wq"), _ptr(Wk, _BF16, "Wk"), _ptr(Wv, _BF16, "Wv"),
+            _ptr(Wo, _BF16, "Wo"), _ptr(Kp, _BF16, "Kp", True), _ptr(Vt, _BF16, "Vt", True),
+            int(P), int(Pcap), _ptr(A, _BF16, "A")))
 
     def logits_entropy(self, dims, H, E, tau, ws, entropy, argmax):
         d = Dims.of(dims)

@@ -10,10 +10,17 @@
 #include <string.h>
 
 #include <climits>
+#include <mutex>
 #include <new>
 
 #include "../../include/dg.h"
 #include "dg_common.h"
+
+// Scratch of dg_canvas_attn_static: one copy per device, alive until the process ends.
+// In host code `scratch` only names the symbol; its device address comes from
+// hipGetSymbolAddress, looked up once per device by scratch_setup() and used everywhere
+// the host hands this memory to a kernel.
+static __device__ __align__(256) uint8_t scratch[DG_STATIC_SCRATCH_BYTES];
 
 struct dg_ctx_s {
   int device = 0;
@@ -30,6 +37,9 @@ struct dg_ctx_s {
   // first call: the shared expert runs beside the routed experts.
   hipStream_t side = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  // Device address of this device's static scratch (NULL if the lookup failed).
+  void *scratch = nullptr;
+  hipError_t scratch_err = hipSuccess;
 };
 
 namespace {
@@ -88,6 +98,129 @@ T *ws_at(void *ws, size_t off) {
   return (T *)((char *)ws + off);
 }
 
+// Per-device address of the static scratch, looked up once per device (the device must
+// be current) and kept for the life of the process, like the array itself.
+constexpr int DG_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+bool g_scratch_done[DG_MAX_DEVICES];
+void *g_scratch_ptr[DG_MAX_DEVICES];
+hipError_t g_scratch_err[DG_MAX_DEVICES];
+
+hipError_t scratch_setup(int device, void **out) {
+  *out = nullptr;
+  if (device < 0 || device >= DG_MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_done[device]) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_err[device] = e;
+    g_scratch_ptr[device] = e == hipSuccess ? p : nullptr;
+    g_scratch_done[device] = true;
+  }
+  *out = g_scratch_ptr[device];
+  return g_scratch_err[device];
+}
+
+// Workspace regions canvas attention writes: the denoiser input, Q / canvas K, V, the
+// attention output before Wo and the split partials.
+struct AttnRegions {
+  int Cpad;
+  u16 *x, *q, *kc, *vct, *o;
+  float *po, *pml;
+};
+
+// Validation shared by dg_canvas_attn and dg_canvas_attn_static (fn names the caller).
+dg_status check_canvas_attn(dg_ctx ctx, const char *fn, const dg_dims *dims, const int32_t *tokens,
+                            const dg_bf16 *z, const dg_bf16 *E, const dg_bf16 *Wq, const dg_bf16 *Wk,
+                            const dg_bf16 *Wv, const dg_bf16 *Wo, const dg_bf16 *Kp, const dg_bf16 *Vt,
+                            int64_t P, int64_t Pcap, const dg_bf16 *A) {
+  dg_status st = check_dims(ctx, dims, fn);
+  if (st) return st;
+  if ((st = check_cache(ctx, P, Pcap, fn))) return st;
+  // the attention copies address one head's cache array with 32-bit byte offsets
+  if ((int64_t)dims->Hkv * dims->hd * Pcap * 2 > (int64_t)UINT32_MAX)
+    return fail(ctx, DG_ERR_SHAPE, "%s: Hkv*hd*Pcap*2 = %lld bytes exceeds 4 GiB", fn,
+                (long long)dims->Hkv * dims->hd * Pcap * 2);
+  const struct {
+    const void *p;
+    const char *name;
+  } req[] = {{tokens, "tokens"}, {E, "E"}, {Wq, "Wq"}, {Wk, "Wk"}, {Wv, "Wv"}, {Wo, "Wo"}, {A, "A"},
+             {P > 0 ? Kp : (const void *)A, "Kp"}, {P > 0 ? Vt : (const void *)A, "Vt"}};
+  for (const auto &r : req) {
+    if (!r.p) return fail(ctx, DG_ERR_NULL, "%s: %s is NULL", fn, r.name);
+    if (!aligned16(r.p)) return fail(ctx, DG_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, r.name);
+  }
+  if (z && !aligned16(z)) return fail(ctx, DG_ERR_ALIGN, "%s: z is not 16-byte aligned", fn);
+  return DG_OK;
+}
+
+// Enqueues canvas attention (gather, QKV, rotary positions, split attention and merge,
+// Wo) over the given workspace regions. Arguments already validated.
+dg_status enqueue_canvas_attn(dg_ctx ctx, const char *fn, const dg_dims &m, const int32_t *tokens,
+                              const dg_bf16 *z, const dg_bf16 *E, const dg_bf16 *Wq, const dg_bf16 *Wk,
+                              const dg_bf16 *Wv, const dg_bf16 *Wo, const dg_bf16 *Kp,
+                              const dg_bf16 *Vt, int64_t P, int64_t Pcap, const AttnRegions &r,
+                              dg_bf16 *A) {
+  const int qd = m.Hq * m.hd, kd = m.Hkv * m.hd;
+
+  // Q, K, V of the denoiser input X = bf16(E[tokens] + z).
+  GemmArgs g{};
+  g.M = m.C;
+  g.K = m.d;
+  g.V = m.V;
+  g.status = ctx->d_status;
+  if (z) {
+    hipError_t e = dg_launch_xgather(tokens, E, z, m.V, m.C, m.d, r.x, ctx->d_status, ctx->stream);
+    if (e != hipSuccess) return hip_fail(ctx, e, fn);
+    g.A = r.x;
+  } else {
+    g.tokens = tokens;
+    g.E = E;
+  }
+  g.nseg = 3;
+  g.seg[0] = GemmSeg{Wq, qd, r.q, qd, 0, 1, INT_MAX, m.C, 0};
+  g.seg[1] = GemmSeg{Wk, kd, r.kc, kd, 0, 1, INT_MAX, r.Cpad, 0};
+  g.seg[2] = GemmSeg{Wv, kd, r.vct, 1, 0, r.Cpad, INT_MAX, r.Cpad, 0};
+  hipError_t e = dg_launch_gemm(g, ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, fn);
+  if (ctx->rope_base > 0.0) {                        // canvas token i sits at position P + i
+    e = dg_launch_rope(r.q, m.C, m.Hq, m.hd, qd, P, ctx->rope_base, ctx->stream);
+    if (e == hipSuccess) e = dg_launch_rope(r.kc, m.C, m.Hkv, m.hd, kd, P, ctx->rope_base, ctx->stream);
+    if (e != hipSuccess) return hip_fail(ctx, e, fn);
+  }
+
+  AttnArgs at{};
+  at.Q = r.q;
+  at.Kp = Kp;
+  at.Vt = Vt;
+  at.Kc = r.kc;
+  at.Vct = r.vct;
+  at.P = P;
+  at.Pcap = Pcap;
+  at.C = m.C;
+  at.Cpad = r.Cpad;
+  at.Hq = m.Hq;
+  at.Hkv = m.Hkv;
+  at.hd = m.hd;
+  at.nsplit = dg_attn_nsplit(m.Hkv, m.Hq, m.C, P);
+  at.scale_log2 = (float)(1.4426950408889634 / sqrt((double)m.hd));
+  at.po = r.po;
+  at.pml = r.pml;
+  at.O = r.o;
+  e = dg_launch_attention(at, ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, fn);
+
+  GemmArgs go{};
+  go.M = m.C;
+  go.K = qd;
+  go.A = r.o;
+  go.nseg = 1;
+  go.seg[0] = GemmSeg{Wo, m.d, A, m.d, 0, 1, INT_MAX, m.C, 0};
+  e = dg_launch_gemm(go, ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, fn);
+  return DG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -103,9 +236,13 @@ dg_status dg_create(dg_ctx *out, int device, void *hip_stream) {
   if (e == hipSuccess) e = hipMalloc((void **)&ctx->d_status, sizeof(int));
   if (e == hipSuccess) e = hipMemset(ctx->d_status, 0, sizeof(int));
   if (e != hipSuccess) {
+    if (ctx->d_status) (void)hipFree(ctx->d_status);
     delete ctx;
     return DG_ERR_HIP;
   }
+  // the device is current: its static scratch address (dg_canvas_attn_static reports a
+  // failed lookup; every other call works without it)
+  ctx->scratch_err = scratch_setup(device, &ctx->scratch);
   *out = ctx;
   return DG_OK;
 }
@@ -169,89 +306,38 @@ dg_status dg_canvas_attn(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens,
                          const dg_bf16 *Kp, const dg_bf16 *Vt, int64_t P, int64_t Pcap,
                          void *ws, dg_bf16 *A) {
   if (!ctx) return DG_ERR_NULL;
-  dg_status st = check_dims(ctx, dims, __func__);
+  dg_status st = check_canvas_attn(ctx, __func__, dims, tokens, z, E, Wq, Wk, Wv, Wo, Kp, Vt, P, Pcap, A);
   if (st) return st;
-  if ((st = check_cache(ctx, P, Pcap, __func__))) return st;
-  // the attention copies address one head's cache array with 32-bit byte offsets
-  if ((int64_t)dims->Hkv * dims->hd * Pcap * 2 > (int64_t)UINT32_MAX)
-    return fail(ctx, DG_ERR_SHAPE, "%s: Hkv*hd*Pcap*2 = %lld bytes exceeds 4 GiB", __func__,
-                (long long)dims->Hkv * dims->hd * Pcap * 2);
-  DG_REQUIRE_PTR(tokens);
-  DG_REQUIRE_PTR(E);
-  DG_REQUIRE_PTR(Wq);
-  DG_REQUIRE_PTR(Wk);
-  DG_REQUIRE_PTR(Wv);
-  DG_REQUIRE_PTR(Wo);
   DG_REQUIRE_PTR(ws);
-  DG_REQUIRE_PTR(A);
-  if (z && !aligned16(z)) return fail(ctx, DG_ERR_ALIGN, "%s: z is not 16-byte aligned", __func__);
-  if (P > 0) {
-    DG_REQUIRE_PTR(Kp);
-    DG_REQUIRE_PTR(Vt);
-  }
   const dg_dims &m = *dims;
   const DgWs w = dg_ws_layout(m.V, m.d, m.C, m.Hq, m.Hkv, m.hd, m.F, Pcap);
-  const int qd = m.Hq * m.hd, kd = m.Hkv * m.hd;
-  u16 *q = ws_at<u16>(ws, w.q), *kc = ws_at<u16>(ws, w.kc), *vct = ws_at<u16>(ws, w.vct);
-  u16 *o = ws_at<u16>(ws, w.o);
+  const AttnRegions r{w.Cpad, ws_at<u16>(ws, w.x), ws_at<u16>(ws, w.q), ws_at<u16>(ws, w.kc),
+                      ws_at<u16>(ws, w.vct), ws_at<u16>(ws, w.o), ws_at<float>(ws, w.po),
+                      ws_at<float>(ws, w.pml)};
+  return enqueue_canvas_attn(ctx, __func__, m, tokens, z, E, Wq, Wk, Wv, Wo, Kp, Vt, P, Pcap, r, A);
+}
 
-  // Q, K, V of the denoiser input X = bf16(E[tokens] + z).
-  GemmArgs g{};
-  g.M = m.C;
-  g.K = m.d;
-  g.V = m.V;
-  g.status = ctx->d_status;
-  if (z) {
-    u16 *x = ws_at<u16>(ws, w.x);
-    hipError_t e = dg_launch_xgather(tokens, E, z, m.V, m.C, m.d, x, ctx->d_status, ctx->stream);
-    if (e != hipSuccess) return hip_fail(ctx, e, "dg_canvas_attn(gather)");
-    g.A = x;
-  } else {
-    g.tokens = tokens;
-    g.E = E;
-  }
-  g.nseg = 3;
-  g.seg[0] = GemmSeg{Wq, qd, q, qd, 0, 1, INT_MAX, m.C, 0};
-  g.seg[1] = GemmSeg{Wk, kd, kc, kd, 0, 1, INT_MAX, w.Cpad, 0};
-  g.seg[2] = GemmSeg{Wv, kd, vct, 1, 0, w.Cpad, INT_MAX, w.Cpad, 0};
-  hipError_t e = dg_launch_gemm(g, ctx->stream);
-  if (e != hipSuccess) return hip_fail(ctx, e, "dg_canvas_attn(qkv)");
-  if (ctx->rope_base > 0.0) {                        // canvas token i sits at position P + i
-    e = dg_launch_rope(q, m.C, m.Hq, m.hd, qd, P, ctx->rope_base, ctx->stream);
-    if (e == hipSuccess) e = dg_launch_rope(kc, m.C, m.Hkv, m.hd, kd, P, ctx->rope_base, ctx->stream);
-    if (e != hipSuccess) return hip_fail(ctx, e, "dg_canvas_attn(rope)");
-  }
-
-  AttnArgs at{};
-  at.Q = q;
-  at.Kp = Kp;
-  at.Vt = Vt;
-  at.Kc = kc;
-  at.Vct = vct;
-  at.P = P;
-  at.Pcap = Pcap;
-  at.C = m.C;
-  at.Cpad = w.Cpad;
-  at.Hq = m.Hq;
-  at.Hkv = m.Hkv;
-  at.hd = m.hd;
-  at.nsplit = dg_attn_nsplit(m.Hkv, m.Hq, m.C, P);
-  at.scale_log2 = (float)(1.4426950408889634 / sqrt((double)m.hd));
-  at.po = ws_at<float>(ws, w.po);
-  at.pml = ws_at<float>(ws, w.pml);
-  at.O = o;
-  e = dg_launch_attention(at, ctx->stream);
-  if (e != hipSuccess) return hip_fail(ctx, e, "dg_canvas_attn(attention)");
-
-  GemmArgs go{};
-  go.M = m.C;
-  go.K = qd;
-  go.A = o;
-  go.nseg = 1;
-  go.seg[0] = GemmSeg{Wo, m.d, A, m.d, 0, 1, INT_MAX, m.C, 0};
-  e = dg_launch_gemm(go, ctx->stream);
-  if (e != hipSuccess) return hip_fail(ctx, e, "dg_canvas_attn(wo)");
-  return DG_OK;
+dg_status dg_canvas_attn_static(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens,
+                                const dg_bf16 *z, const dg_bf16 *E, const dg_bf16 *Wq,
+                                const dg_bf16 *Wk, const dg_bf16 *Wv, const dg_bf16 *Wo,
+                                const dg_bf16 *Kp, const dg_bf16 *Vt, int64_t P, int64_t Pcap,
+                                dg_bf16 *A) {
+  if (!ctx) return DG_ERR_NULL;
+  dg_status st = check_canvas_attn(ctx, __func__, dims, tokens, z, E, Wq, Wk, Wv, Wo, Kp, Vt, P, Pcap, A);
+  if (st) return st;
+  if (!ctx->scratch)
+    return fail(ctx, DG_ERR_HIP, "%s: no static scratch on device %d (%s)", __func__, ctx->device,
+                hipGetErrorString(ctx->scratch_err == hipSuccess ? hipErrorInvalidSymbol : ctx->scratch_err));
+  const dg_dims &m = *dims;
+  const DgAttnWs w = dg_attn_ws_layout(m.d, m.C, m.Hq, m.Hkv, m.hd, dg_attn_nsplit(m.Hkv, m.Hq, m.C, P));
+  if (w.total > DG_STATIC_SCRATCH_BYTES)
+    return fail(ctx, DG_ERR_CAPACITY, "%s: these dims need %zu bytes of scratch; the static scratch holds %zu",
+                __func__, w.total, (size_t)DG_STATIC_SCRATCH_BYTES);
+  void *ws = ctx->scratch;
+  const AttnRegions r{w.Cpad, ws_at<u16>(ws, w.x), ws_at<u16>(ws, w.q), ws_at<u16>(ws, w.kc),
+                      ws_at<u16>(ws, w.vct), ws_at<u16>(ws, w.o), ws_at<float>(ws, w.po),
+                      ws_at<float>(ws, w.pml)};
+  return enqueue_canvas_attn(ctx, __func__, m, tokens, z, E, Wq, Wk, Wv, Wo, Kp, Vt, P, Pcap, r, A);
 }
 
 static dg_status check_moe(dg_ctx ctx, const dg_moe_dims *m, int32_t C, const char *fn) {

@@ -203,6 +203,32 @@ static inline DgWs dg_ws_layout(int V, int d, int C, int Hq, int Hkv, int hd, in
   return w;
 }
 
+// Regions of canvas attention only (X, Q, canvas K/V, O, split partials), packed for
+// the allocation-free variant, whose scratch holds nothing else. 256-byte aligned.
+struct DgAttnWs {
+  int Cpad;
+  size_t x, q, kc, vct, o, po, pml, total;
+};
+static inline DgAttnWs dg_attn_ws_layout(int d, int C, int Hq, int Hkv, int hd, int nsplit) {
+  DgAttnWs w;
+  w.Cpad = (int)dg_round_up(C, DG_CT);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = (size_t)dg_round_up((int64_t)(off + bytes), 256);
+    return at;
+  };
+  w.x = take((size_t)w.Cpad * d * 2);
+  w.q = take((size_t)w.Cpad * Hq * hd * 2);
+  w.kc = take((size_t)w.Cpad * Hkv * hd * 2);
+  w.vct = take((size_t)w.Cpad * Hkv * hd * 2);
+  w.o = take((size_t)w.Cpad * Hq * hd * 2);
+  w.po = take((size_t)nsplit * Hq * w.Cpad * hd * 4);
+  w.pml = take((size_t)nsplit * Hq * w.Cpad * 2 * 4);
+  w.total = off;
+  return w;
+}
+
 // ------------------------------------------------------------------ launcher API
 // Host-side launchers implemented by the kernel translation units.
 struct GemmSeg {

@@ -56,7 +56,7 @@ typedef enum {
   DG_ERR_SHAPE = 2,       /* a dimension is out of the supported set                     */
   DG_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned / Pcap not a multiple of 8 */
   DG_ERR_RANGE = 4,       /* a scalar is out of range (tau <= 0, b < 0, token id, ...)   */
-  DG_ERR_CAPACITY = 5,    /* P + C > Pcap: the KV cache has no room                      */
+  DG_ERR_CAPACITY = 5,    /* P + C > Pcap (the KV cache has no room), or static scratch  */
   DG_ERR_STATE = 6,       /* dg_selfcond without a matching dg_logits_entropy            */
   DG_ERR_NONFINITE = 7,   /* device saw non-finite logits (sticky, via dg_sync)          */
   DG_ERR_HIP = 8,         /* a HIP runtime call failed                                   */
@@ -118,6 +118,25 @@ dg_status dg_canvas_attn(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens,
                          const dg_bf16 *Wk, const dg_bf16 *Wv, const dg_bf16 *Wo,
                          const dg_bf16 *Kp, const dg_bf16 *Vt, int64_t P, int64_t Pcap,
                          void *ws, dg_bf16 *A);
+
+/* dg_canvas_attn without a workspace argument and without any allocation, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation. Same arguments (minus ws), validation,
+ * kernels and results as dg_canvas_attn; its scratch (the denoiser input, Q and canvas
+ * K/V, the attention output before Wo and the split partials) lives in one
+ * DG_STATIC_SCRATCH_BYTES array per device inside the library, held until the process
+ * ends. Every call on a device shares that device's array, so calls that overlap on one
+ * device (several streams or host threads, or contexts on different streams) race and
+ * must be serialized by the caller; nothing in it needs to start zeroed.
+ * DG_ERR_CAPACITY (nothing enqueued) when the dims need more than the array holds
+ * (about 36.5 MiB at C 256, d 2048, 16 query / 8 KV heads of 128, any prefix length);
+ * DG_ERR_HIP when the array's address could not be found on this device. */
+#define DG_STATIC_SCRATCH_BYTES ((size_t)48 << 20)
+dg_status dg_canvas_attn_static(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens,
+                                const dg_bf16 *z, const dg_bf16 *E, const dg_bf16 *Wq,
+                                const dg_bf16 *Wk, const dg_bf16 *Wv, const dg_bf16 *Wo,
+                                const dg_bf16 *Kp, const dg_bf16 *Vt, int64_t P, int64_t Pcap,
+                                dg_bf16 *A);
 
 /* Sampler head (Technical Report page, "Method steps" (3)): logits H E^T, softmax at
  * temperature tau giving p0, per-position Shannon entropy in nats (clamped at 0) and
