@@ -77,7 +77,10 @@ Q_SENTINEL = 1 << 48
 
 # ------------------------------------------------------------------ bf16 storage
 def from_bf16(bits) -> np.ndarray:
-    """bf16 bit patterns -> float64 values (exact)."""
+    """bf16 bit patterns -> float64 values (exact). A float64 array is taken as values
+    already converted (callers may convert a large table such as E once)."""
+    if isinstance(bits, np.ndarray) and bits.dtype == np.float64:
+        return bits
     b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 

@@ -94,3 +94,23 @@ def argmax_mismatch_unexcused(am_gpu, am_ref, u) -> int:
         if not near_tie(u[i]):
             bad += 1
     return bad
+
+
+_workloads = {}
+
+
+def workload(name):
+    """(cfg, W bits, W with E converted to float64 for the oracle, device weights) of one
+    named full-size workload; one at a time is kept (each holds a 1 GiB vocabulary table),
+    shared by the test modules that run in a row."""
+    import dg_inputs as di
+    import oracle as O
+
+    if name not in _workloads:
+        _workloads.clear()
+        cfg = di.config(name)
+        W = di.weights(cfg)
+        W64 = dict(W)
+        W64["E"] = O.from_bf16(W["E"])
+        _workloads[name] = (cfg, W, W64, upload_weights(W))
+    return _workloads[name]
