@@ -8,10 +8,19 @@ and the next canvas's initialization fall inside the timed region too.
 
 Workload (default "gemma_head"): V=262144, d=2048, C=256, 16 query / 8 KV heads of
 128, FFW 1024, prefix 8192 tokens, N=48, synthetic seeded weights and driver hidden
-states (dg_inputs), all resident in HBM before timing starts.
+states (dg_inputs), all resident in HBM before timing starts. Every canvas attends over
+the same 8192-token prefix: after each commit the cache length is set back to it, so the
+commit's rows are rewritten by the next canvas's commit.
+
+Protocol: one whole warm-up canvas is run and discarded first (the clock ramps during
+the first tens of launches of a process), then --warmup untimed steps, then exactly
+--steps timed steps (value = steps/s). Canvas tokens/s comes from whole canvases timed
+from initialization to commit: the median of --canvases of them.
 
 Prints one JSON line: denoise steps/s (value), canvas tokens/s, the roofline of the
-dominant kernel (the sampler-head logits GEMM, timed live with HIP events) and the CPU
+dominant pair of calls (the sampler head dg_logits_entropy and self-conditioning
+dg_selfcond, which together are most of the step; both timed live with HIP events
+inside real steps), the same protocol at the tiny and small workloads, and the CPU
 oracle's rate on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -49,14 +58,22 @@ def parse():
                     help="skip the isolated attention call over a 262144-token prefix")
     ap.add_argument("--no-chain", action="store_true",
                     help="skip the 8-canvas block-AR chain with commits")
+    ap.add_argument("--no-small", action="store_true",
+                    help="skip the protocol lines of the small and tiny workloads")
+    ap.add_argument("--canvases", type=int, default=7,
+                    help="whole canvases timed for canvas tokens/s (median), after one warm-up canvas")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB device copy (for HBM counter calibration)")
     return ap.parse_args()
 
 
-def traffic_from_profiles(kernel_src: str, name: str):
-    """HBM bytes per launch from the committed counter summary, if it matches the source."""
-    path = os.path.join(ROOT, "profiles", f"{name}_traffic.txt")
+PAIR_SOURCES = ("k_logits.hip", "k_selfcond.hip", "k_gemm.hip")
+
+
+def pair_traffic_from_profiles():
+    """HBM bytes per step of the dominant pair (both calls' kernels), from the committed
+    counter summary, if it was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "sampler_pair_gemma_head_traffic.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -64,10 +81,71 @@ def traffic_from_profiles(kernel_src: str, name: str):
         parts = line.split()
         if len(parts) == 2 and not line.startswith("#"):
             vals[parts[0]] = parts[1]
-    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
-    if vals.get("source_sha256_16") != sha or "hbm_bytes_per_launch" not in vals:
+    h = hashlib.sha256()
+    for f in PAIR_SOURCES:
+        h.update(open(os.path.join(ROOT, "block_ar_canvas_amd", "csrc", f), "rb").read())
+    if vals.get("sources_sha256_16") != h.hexdigest()[:16] or "hbm_bytes_per_step" not in vals:
         return None
-    return float(vals["hbm_bytes_per_launch"])
+    return float(vals["hbm_bytes_per_step"])
+
+
+def pair_sources_sha():
+    h = hashlib.sha256()
+    for f in PAIR_SOURCES:
+        h.update(open(os.path.join(ROOT, "block_ar_canvas_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def run_protocol(loop, hidden_of, canvases: int, P0: int):
+    """One discarded warm-up canvas, then `canvases` whole canvases timed one by one from
+    initialization to commit (each over the same P0-token prefix). Returns the per-canvas
+    seconds and step counts."""
+    import torch
+
+    secs, steps = [], []
+    for c in range(canvases + 1):
+        loop.P = P0
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        n = loop.run_canvas(c, hidden_of(c))
+        torch.cuda.synchronize()
+        if c > 0:
+            secs.append(time.perf_counter() - t0)
+            steps.append(n)
+    loop.P = P0
+    return secs, steps
+
+
+def protocol_summary(secs, steps, C):
+    i = int(np.argsort(secs)[len(secs) // 2])
+    return {"canvases": len(secs), "warmup_canvases": 1,
+            "median_ms_per_canvas": round(1e3 * secs[i], 3), "steps_per_canvas": steps[i],
+            "steps_per_s": round(steps[i] / secs[i], 2),
+            "canvas_tokens_per_s": round(C / secs[i], 1),
+            "ms_per_canvas": [round(1e3 * x, 3) for x in secs]}
+
+
+def small_workload(ctx, name, canvases):
+    """The protocol at a smaller workload (tiny or small): steps/s and canvas tokens/s."""
+    import torch
+
+    import dg_inputs as di
+    from block_ar_canvas_amd.loop import CanvasLoop
+    cfg = di.config(name)
+    dev = torch.device("cuda:0")
+    W = di.weights(cfg)
+    Kp, Vp = di.prefix_kv(cfg, cfg.P0 + cfg.C)
+    Wd = {k: _bf(v, dev) for k, v in W.items()}
+    Kd = _bf(Kp, dev)
+    Vtd = _bf(np.ascontiguousarray(Vp.transpose(0, 2, 1)), dev)
+    Hd = [_bf(di.hidden_all(cfg, W["E"], c), dev) for c in range(2)]
+    loop = CanvasLoop(ctx, cfg, Wd, Kd, Vtd, cfg.P0, N=cfg.N, seed=cfg.seed)
+    secs, steps = run_protocol(loop, lambda c: (lambda k: Hd[c % 2][k]), canvases, cfg.P0)
+    ctx.sync()
+    out = protocol_summary(secs, steps, cfg.C)
+    out["workload"] = (f"{cfg.name}: V={cfg.V} d={cfg.d} C={cfg.C} Hq={cfg.Hq} Hkv={cfg.Hkv} "
+                       f"hd={cfg.hd} F={cfg.F} prefix={cfg.P0} N={cfg.N}")
+    return out
 
 
 def main():
@@ -86,9 +164,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     cfg = di.config(args.config)
-    total = args.warmup + args.steps + max(args.roofline_reps, 48)   # + the roofline pass
-    n_canvas = total // cfg.N + 2
-    Pcap = -(-(cfg.P0 + cfg.C * n_canvas) // 8) * 8
+    Pcap = -(-(cfg.P0 + cfg.C) // 8) * 8
+    n_hidden = 4                                      # driver states cycle over 4 canvases
 
     t_gen = time.time()
     W = di.weights(cfg)
@@ -101,15 +178,20 @@ def main():
     Kd = bf(Kp)
     Vtd = bf(np.ascontiguousarray(Vp.transpose(0, 2, 1)))
     del Vp
-    Hd = [bf(di.hidden_all(cfg, W["E"], c)) for c in range(n_canvas)]
+    Hd = [bf(di.hidden_all(cfg, W["E"], c)) for c in range(n_hidden)]
     torch.cuda.synchronize()
     t_gen = time.time() - t_gen
 
     ctx = dg.Context(0)
     loop = CanvasLoop(ctx, cfg, Wd, Kd, Vtd, cfg.P0, N=cfg.N, seed=cfg.seed)
 
+    # the protocol's warm-up canvas, discarded
+    loop.run_canvas(0, lambda k: Hd[0][k])
+    loop.P = cfg.P0
+    torch.cuda.synchronize()
+
     # Drive the block-AR loop step by step so that exactly `steps` steps are timed.
-    state = {"canvas": -1, "k": 0, "done": True, "commits": 0}
+    state = {"canvas": 0, "k": 0, "done": True, "commits": 0}
 
     def one_step():
         s = state
@@ -118,16 +200,15 @@ def main():
             s["k"] = 0
             s["done"] = False
             loop.init_canvas(s["canvas"])
-            loop.z.zero_()
-            loop.step(0, Hd[s["canvas"]][0])
-            s["pending"] = 0
+            loop.step(0, Hd[s["canvas"] % n_hidden][0])
             return
         k = s["k"]
         if k + 1 < cfg.N:
-            loop.step(k + 1, Hd[s["canvas"]][k + 1])
+            loop.step(k + 1, Hd[s["canvas"] % n_hidden][k + 1])
         flag = loop.wait_flag(k)
         if flag != dg.STOP_GO:
             loop.commit(loop.argmax[k & 1])
+            loop.P = cfg.P0                            # every canvas over the same prefix
             s["commits"] += 1
             s["done"] = True
             return
@@ -138,10 +219,8 @@ def main():
     def run(n):
         steps = 0
         while steps < n:
-            before = (state["canvas"], state["k"], state["done"])
             one_step()
-            after = (state["canvas"], state["k"], state["done"])
-            if not after[2]:
+            if not state["done"]:
                 steps += 1
         return steps
 
@@ -157,37 +236,34 @@ def main():
     steps_per_s = args.steps / sec
     ctx.sync()
 
-    # Roofline of the dominant kernel: the sampler-head logits GEMM (dg_logits_entropy),
-    # timed live with HIP events on the library's stream around each of its launches
-    # inside real denoise steps (the same loop, continued for max(reps, 48) steps after
-    # the timed region, so the event packets do not touch the headline step time).
-    loop.logits_events = []
+    # Roofline of the dominant pair: the sampler head (dg_logits_entropy: logits tile
+    # kernel and row finalize) and self-conditioning (dg_selfcond: p0 E split kernel,
+    # reduce, the two FFW GEMMs), timed live with HIP events on the library's stream
+    # around each call inside real denoise steps (the same loop, continued for
+    # max(reps, 48) steps after the timed region, so the event packets do not touch the
+    # headline step time).
+    loop.logits_events, loop.selfcond_events = [], []
     run(max(args.roofline_reps, 48))
     torch.cuda.synchronize()
-    evs, loop.logits_events = loop.logits_events, None
-    logits_ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
-    roofline_launches = len(evs)
-    H = Hd[0][cfg.N - 1]
-    ent = torch.empty(cfg.C, dtype=torch.float32, device=dev)
-    am = torch.empty(cfg.C, dtype=torch.int32, device=dev)
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    alg_bytes = cfg.V * cfg.d * 2 + cfg.C * cfg.d * 2 + cfg.C * 8
-    alg_flops = 2.0 * cfg.C * cfg.V * cfg.d
-    achieved = alg_bytes / (logits_ms * 1e-3) / 1e9
-    src = os.path.join(ROOT, "block_ar_canvas_amd", "csrc", "k_logits.hip")
-    traffic = traffic_from_profiles(src, "logits_tile_kernel_gemma_head")
+    evl, loop.logits_events = loop.logits_events, None
+    evs, loop.selfcond_events = loop.selfcond_events, None
+    logits_ms = sum(a.elapsed_time(b) for a, b in evl) / len(evl)
+    selfcond_ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    pair_ms = logits_ms + selfcond_ms
+    # algorithmic bytes: E read by each call, H, the FFW weights and the outputs
+    # (entropy, argmax, z); the bf16 probabilities passed between the calls are a design
+    # choice and are not counted
+    e_bytes = cfg.V * cfg.d * 2
+    ffw_bytes = 2 * cfg.F * cfg.d * 2
+    alg_bytes = 2 * e_bytes + cfg.C * cfg.d * 2 + ffw_bytes + cfg.C * 8 + cfg.C * cfg.d * 2
+    alg_flops = 2 * (2.0 * cfg.C * cfg.V * cfg.d) + 2 * (2.0 * cfg.C * cfg.d * cfg.F)
+    achieved = alg_bytes / (pair_ms * 1e-3) / 1e9
+    traffic = pair_traffic_from_profiles()
 
-    # Self-conditioning product, timed the same way (reported beside the roofline).
-    ctx.logits_entropy(cfg, H, Wd["E"], 0.4, loop.ws, ent, am)
-    z = torch.empty(cfg.C, cfg.d, dtype=torch.bfloat16, device=dev)
-    e0.record(stream)
-    for _ in range(args.roofline_reps):
-        ctx.selfcond(cfg, loop.ws, Wd["E"], Wd["W1"], Wd["W2"], z)
-    e1.record(stream)
-    e1.synchronize()
-    selfcond_ms = e0.elapsed_time(e1) / args.roofline_reps
+    # the protocol: whole canvases, init to commit
+    secs, csteps = run_protocol(loop, lambda c: (lambda k: Hd[c % n_hidden][k]), args.canvases, cfg.P0)
     ctx.sync()
+    proto = protocol_summary(secs, csteps, cfg.C)
 
     if args.calibrate_copy:
         src_t = torch.empty(1 << 29, dtype=torch.int16, device=dev)
@@ -202,6 +278,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_canvases": 1,
         "ms_per_step": round(1e3 * sec / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -212,16 +289,22 @@ def main():
                                f"hd={cfg.hd} F={cfg.F} prefix={cfg.P0} N={cfg.N}",
                    "canvas": cfg.C, "vocab": cfg.V, "prefix_tokens": cfg.P0, "max_steps": cfg.N,
                    "parallelism": "single-gpu"},
-        "canvas_tokens_per_s": round(commits * cfg.C / sec, 1),
+        "canvas_tokens_per_s": proto["canvas_tokens_per_s"],
+        "canvas_protocol": proto,
         "canvas_tokens_per_s_at_12_steps": round(steps_per_s * cfg.C / 12, 1),
         "commits_timed": commits,
-        "roofline": {"kernel": "logits_tile_kernel+row_finalize (dg_logits_entropy)",
+        "roofline": {"kernel": "dg_logits_entropy + dg_selfcond (logits_tile_kernel, row_finalize_kernel, "
+                               "selfcond_split_kernel, selfcond_reduce_kernel, 2 FFW gemm_kernel)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
-                     "ms_per_launch": round(logits_ms, 4), "launches_timed": roofline_launches,
-                     "mfma_frac": round(alg_flops / (logits_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
-        "selfcond_ms_per_call": round(selfcond_ms, 4),
+                     "traffic": traffic, "alg_bytes_per_step": alg_bytes,
+                     "alg_flop_per_step": alg_flops,
+                     "ms_per_step": round(pair_ms, 4), "launches_timed": len(evl),
+                     "logits_ms_per_call": round(logits_ms, 4),
+                     "selfcond_ms_per_call": round(selfcond_ms, 4),
+                     "mfma_frac": round(alg_flops / (pair_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                     "logits_mfma_frac": round(2.0 * cfg.C * cfg.V * cfg.d / (logits_ms * 1e-3) / 1e12
+                                               / BF16_PEAK_TFLOPS, 4)},
         "input_gen_s": round(t_gen, 1),
     }
 
@@ -233,6 +316,9 @@ def main():
         result["confidence_rule"] = variant_canvas(ctx, cfg, Wd, Hd, rule="confidence")
         result["sampled_tokens"] = variant_canvas(ctx, cfg, Wd, Hd, draw="sample")
     del Hd
+    if not args.no_small:
+        result["small"] = small_workload(ctx, "small", args.canvases)
+        result["tiny"] = small_workload(ctx, "tiny", args.canvases)
     if not args.no_chain:
         result["chain8"] = chain(ctx)
         result["chain8_prefill"] = chain(ctx, commit="prefill", rope_base=10000.0)
@@ -534,29 +620,44 @@ def chain(ctx, commit="projection", rope_base=0.0):
     return out
 
 
-def cpu_baseline(cfg, W, Kp, n_steps):
-    """The CPU oracle, as it stands, on a bounded sample: n full steps of the same canvas."""
+def cpu_info():
+    """CPU model, BLAS library and its thread count on this host."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas, threads = "unknown", os.cpu_count() or 1
+    try:
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            blas = f"{info[0].get('internal_api')} {info[0].get('version')} ({info[0].get('threading_layer')})"
+            threads = max(i.get("num_threads", 1) for i in info)
+    except Exception:
+        pass
+    return model, blas, int(threads), len(os.sched_getaffinity(0))
+
+
+def oracle_steps(cfg, W, Kp, Vp, k0, n_steps):
+    """n full oracle denoise steps of one canvas from step k0 (attention, sampler head,
+    acceptance, renoise, self-conditioning, stop test). Returns seconds."""
     import oracle as O
     import dg_inputs as di
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max(i.get("num_threads", 1) for i in threadpool_info()) or 1
-    except Exception:
-        cores = os.cpu_count() or 1
-    Kp_o = Kp[:, :cfg.P0 + cfg.C].copy()
-    _, Vp_o = di.prefix_kv(cfg, cfg.P0 + cfg.C)
     tgt = di.targets(cfg, 0)
     tok = np.random.default_rng(0).integers(0, cfg.V, cfg.C).astype(np.int32)
     z = np.zeros((cfg.C, cfg.d), np.uint16)
-    k0 = cfg.N // 2
     H = [di.hidden(cfg, W["E"], 0, k0 + i, tgt) for i in range(n_steps)]
     prev = None
     t0 = time.perf_counter()
     for i in range(n_steps):
         k = k0 + i
         tau = O.temperature(k, cfg.N)
-        O.canvas_attn(tok, z, W["E"], W["Wq"], W["Wk"], W["Wv"], W["Wo"], Kp_o, Vp_o, cfg.P0,
+        O.canvas_attn(tok, z, W["E"], W["Wq"], W["Wk"], W["Wv"], W["Wo"], Kp, Vp, cfg.P0,
                       cfg.Hq, cfg.Hkv, cfg.hd)
         ent, am, p, _ = O.logits_entropy(H[i], W["E"], tau)
         acc, _ = O.entropy_accept(ent[None], 0.1)
@@ -564,11 +665,40 @@ def cpu_baseline(cfg, W, Kp, n_steps):
         z, _ = O.selfcond(p, W["E"], W["W1"], W["W2"])
         O.stop_test(ent, am, prev, 0.005, k, cfg.N)
         prev = am
-    sec = time.perf_counter() - t0
-    return {"value": round(n_steps / sec, 5), "unit": "steps/s", "cores": int(cores),
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(cfg, W, Kp, n_steps):
+    """The CPU oracle, as it stands, on bounded samples: n full steps of the workload's
+    canvas with every BLAS thread, and two steps of the small workload with every thread
+    and one step with one thread."""
+    import dg_inputs as di
+
+    model, blas, threads, affinity = cpu_info()
+    Kp_o = Kp[:, :cfg.P0 + cfg.C].copy()
+    _, Vp_o = di.prefix_kv(cfg, cfg.P0 + cfg.C)
+    sec = oracle_steps(cfg, W, Kp_o, Vp_o, cfg.N // 2, n_steps)
+    del Kp_o, Vp_o
+    sm = di.config("small")
+    Ws = di.weights(sm)
+    Ks, Vs = di.prefix_kv(sm, sm.P0 + sm.C)
+    oracle_steps(sm, Ws, Ks, Vs, sm.N // 2, 1)                  # first-touch warm-up
+    sec_small = oracle_steps(sm, Ws, Ks, Vs, sm.N // 2, 2) / 2
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            sec_small_1 = oracle_steps(sm, Ws, Ks, Vs, sm.N // 2, 1)
+    except Exception:
+        sec_small_1 = None
+    return {"value": round(n_steps / sec, 5), "unit": "steps/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{n_steps} full denoise step(s) of {cfg.name} (k={k0}..), numpy float64, "
-                      f"{sec:.1f} s"}
+            "sample": f"{n_steps} full denoise step(s) of {cfg.name} (k={cfg.N // 2}..), numpy float64, "
+                      f"{sec:.1f} s",
+            "cpu_model": model, "blas": blas, "blas_threads": threads, "affinity_cpus": affinity,
+            "small_s_per_step": round(sec_small, 4),
+            "small_s_per_step_1_thread": None if sec_small_1 is None else round(sec_small_1, 4),
+            "small_sample": "small workload (V 32768, d 1024, prefix 2048): 2 steps with every "
+                            "BLAS thread, 1 step with one thread"}
 
 
 if __name__ == "__main__":

@@ -70,9 +70,10 @@ class CanvasLoop:
         self.flags = [torch.full((1,), -1, dtype=torch.int32, pin_memory=True) for _ in range(4)]
         self._seq = 0
         self._slot = {}
-        # When a list, every step appends a (start, end) pair of timing events recorded
-        # on the context's stream around its dg_logits_entropy call.
+        # When lists, every step appends a (start, end) pair of timing events recorded
+        # on the context's stream around its dg_logits_entropy / dg_selfcond call.
         self.logits_events = None
+        self.selfcond_events = None
 
     def init_canvas(self, canvas: int):
         """Uniform random canvas (init stream) and z = 0."""
@@ -106,7 +107,15 @@ class CanvasLoop:
         else:
             self.ctx.entropy_accept(self.entropy, self.b, self.accept, self.n_accept)
         self.ctx.renoise(dm.V, x0, self.accept, self.seed, self.canvas, k, self.tokens)
+        sev = self.selfcond_events
+        if sev is not None:
+            s0 = torch.cuda.Event(enable_timing=True)
+            s0.record(self.ctx.torch_stream())
         self.ctx.selfcond(dm, self.ws, W["E"], W["W1"], W["W2"], self.z)
+        if sev is not None:
+            s1 = torch.cuda.Event(enable_timing=True)
+            s1.record(self.ctx.torch_stream())
+            sev.append((s0, s1))
         slot = self._seq % len(self.flags)
         self._seq += 1
         self._slot[k] = slot
