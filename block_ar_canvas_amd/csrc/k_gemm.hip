@@ -210,12 +210,14 @@ __global__ __launch_bounds__(256) void xgather_kernel(const int *tokens, const u
                                                       const u16 *z, int V, int K, u16 *X,
                                                       int *status) {
   const int m = blockIdx.x;
-  const int tok = tokens[m];
-  const bool ok = tok >= 0 && tok < V;
-  if (!ok && threadIdx.x == 0) set_status(status, DGS_RANGE);
+  int tok = tokens[m];
+  if (tok < 0 || tok >= V) {                         // read as id 0, like the gather GEMM
+    if (threadIdx.x == 0) set_status(status, DGS_RANGE);
+    tok = 0;
+  }
   for (int k = threadIdx.x * 8; k < K; k += 256 * 8) {
     const uint4 zz = *(const uint4 *)(z + (int64_t)m * K + k);
-    const uint4 ee = ok ? *(const uint4 *)(E + (int64_t)tok * K + k) : make_uint4(0, 0, 0, 0);
+    const uint4 ee = *(const uint4 *)(E + (int64_t)tok * K + k);
     const uint32_t *e = (const uint32_t *)&ee, *zw = (const uint32_t *)&zz;
     uint32_t o[4];
 #pragma unroll

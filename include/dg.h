@@ -109,7 +109,7 @@ float dg_temperature(int32_t k, int32_t N, float tau0, float tau1);
  *   Q  = bf16(X Wq^T), Kc = bf16(X Wk^T), Vc = bf16(X Wv^T)
  *   O_h = softmax(Q_h [Kp_g ; Kc_g]^T / sqrt(hd)) [Vp_g ; Vc_g],  g = floor(h*Hkv/Hq)
  *   A  = bf16(O Wo^T)                           [C, d]
- * tokens [C] int32 (ids outside [0, V) set DG_ERR_RANGE on the device and read as 0);
+ * tokens [C] int32 (an id outside [0, V) sets DG_ERR_RANGE on the device and is read as id 0);
  * z [C, d] or NULL; E [V, d]; Wq [Hq*hd, d]; Wk, Wv [Hkv*hd, d]; Wo [d, Hq*hd];
  * Kp, Vt: the KV cache (layout above) holding P tokens (0 <= P <= Pcap, Pcap % 8 == 0);
  * the cache is only read. ws: workspace; A [C, d] output. */
@@ -143,8 +143,8 @@ dg_status dg_canvas_attn_static(dg_ctx ctx, const dg_dims *dims, const int32_t *
  * argmax (ties to the lowest id). H [C, d]; E [V, d]; tau > 0. Writes entropy [C]
  * float32 and argmax [C] int32, and leaves p0 (as bf16 per-tile scaled probabilities
  * plus fp32 tile statistics) in ws for dg_selfcond; the C x V probabilities are never
- * materialized in fp32. Non-finite logits give a NaN entropy for that position and
- * set DG_ERR_NONFINITE. */
+ * materialized in fp32. Non-finite logits give a NaN entropy and argmax 0 for that
+ * position and set DG_ERR_NONFINITE. */
 dg_status dg_logits_entropy(dg_ctx ctx, const dg_dims *dims, const dg_bf16 *H,
                             const dg_bf16 *E, float tau, void *ws, float *entropy,
                             int32_t *argmax);
@@ -216,8 +216,9 @@ dg_status dg_renoise(dg_ctx ctx, int32_t B, int32_t C, int32_t V, const int32_t 
 /* Self-conditioning (Technical Report page, "Method steps" (3): z = FFW(p0 E); Google
  * page, "Self-conditioning"): s = p0 E with p0 from the immediately preceding
  * dg_logits_entropy on the same workspace and dims, then z = bf16(GELU_erf(s W1^T) W2^T).
- * E [V, d]; W1 [F, d]; W2 [d, F]; z [C, d] output. DG_ERR_STATE if ws does not hold
- * the p0 of a matching dg_logits_entropy. */
+ * E [V, d]; W1 [F, d]; W2 [d, F]; z [C, d] output. A position whose logits were not
+ * finite contributes s = 0, so its z row is 0. DG_ERR_STATE if ws does not hold the p0
+ * of a matching dg_logits_entropy. */
 dg_status dg_selfcond(dg_ctx ctx, const dg_dims *dims, void *ws, const dg_bf16 *E,
                       const dg_bf16 *W1, const dg_bf16 *W2, dg_bf16 *z);
 
@@ -282,6 +283,7 @@ dg_status dg_moe_ffn(dg_ctx ctx, const dg_moe_dims *m, int32_t C, const dg_bf16 
  * positions [P, P + C) of every KV head: K = bf16(E[tokens] Wk^T), V = bf16(E[tokens]
  * Wv^T) (a stand-in for the causal re-encode of the block). Rows [0, P) are not touched.
  * tokens [C] int32 (x0 = argmax); Kp, Vt in/out; *P_out (host) = P + C.
+ * An id outside [0, V) sets DG_ERR_RANGE on the device and is read as id 0.
  * DG_ERR_CAPACITY (nothing written) when P + C > Pcap. */
 dg_status dg_commit_kv(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens,
                        const dg_bf16 *E, const dg_bf16 *Wk, const dg_bf16 *Wv,
