@@ -60,6 +60,8 @@ def parse():
                     help="skip the 8-canvas block-AR chain with commits")
     ap.add_argument("--no-small", action="store_true",
                     help="skip the protocol lines of the small and tiny workloads")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the eager-vs-graph lines of fixed-step canvases")
     ap.add_argument("--canvases", type=int, default=7,
                     help="whole canvases timed for canvas tokens/s (median), after one warm-up canvas")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -125,6 +127,51 @@ def protocol_summary(secs, steps, C):
             "ms_per_canvas": [round(1e3 * x, 3) for x in secs]}
 
 
+def graph_canvas_rate(ctx, loop, hidden, reps):
+    """Whole canvases enqueued with no host wait (init, every step, commit; no adaptive
+    stop), first eagerly and then captured once in a HIP graph and replayed: steps/s of
+    each. Against the protocol's canvases (which poll the stop flag between steps) this
+    separates what the host's launches cost from what the kernels cost."""
+    import torch
+
+    P0 = loop.P
+    old = ctx.stream
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    ctx.set_stream(s)
+    try:
+        with torch.cuda.stream(s):
+            loop.enqueue_canvas_fixed(1, hidden)            # warm-up
+            loop.P = P0
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(s):
+            for _ in range(reps):
+                loop.enqueue_canvas_fixed(1, hidden)
+                loop.P = P0
+        torch.cuda.synchronize()
+        eager = time.perf_counter() - t0
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            loop.enqueue_canvas_fixed(1, hidden)
+        loop.P = P0
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph = time.perf_counter() - t0
+        del g
+    finally:
+        torch.cuda.synchronize()
+        ctx.set_stream(old)
+    n = reps * loop.N
+    return {"canvases": reps, "eager_fixed_steps_per_s": round(n / eager, 2),
+            "graph_steps_per_s": round(n / graph, 2),
+            "graph_canvas_tokens_per_s": round(reps * loop.dims.C / graph, 1)}
+
+
 def small_workload(ctx, name, canvases):
     """The protocol at a smaller workload (tiny or small): steps/s and canvas tokens/s."""
     import torch
@@ -143,6 +190,7 @@ def small_workload(ctx, name, canvases):
     secs, steps = run_protocol(loop, lambda c: (lambda k: Hd[c % 2][k]), canvases, cfg.P0)
     ctx.sync()
     out = protocol_summary(secs, steps, cfg.C)
+    out["fixed_step_canvases"] = graph_canvas_rate(ctx, loop, lambda k: Hd[0][k], 100 if cfg.V < 4096 else 20)
     out["workload"] = (f"{cfg.name}: V={cfg.V} d={cfg.d} C={cfg.C} Hq={cfg.Hq} Hkv={cfg.Hkv} "
                        f"hd={cfg.hd} F={cfg.F} prefix={cfg.P0} N={cfg.N}")
     return out
@@ -264,6 +312,8 @@ def main():
     secs, csteps = run_protocol(loop, lambda c: (lambda k: Hd[c % n_hidden][k]), args.canvases, cfg.P0)
     ctx.sync()
     proto = protocol_summary(secs, csteps, cfg.C)
+    if not args.no_graph:
+        proto["fixed_step_canvases"] = graph_canvas_rate(ctx, loop, lambda k: Hd[0][k], 5)
 
     if args.calibrate_copy:
         src_t = torch.empty(1 << 29, dtype=torch.int16, device=dev)

@@ -175,6 +175,17 @@ class CanvasLoop:
         self.commit(self.final_tokens(k))
         return k + 1
 
+    def enqueue_canvas_fixed(self, canvas: int, hidden):
+        """Enqueues a whole canvas without any host wait: init, all N steps, and the commit
+        of the last step's block. There is no adaptive stop (the host reads no flag; the
+        stop kernels still write theirs), so the sequence is fixed and can be captured in
+        a HIP graph and replayed. hidden(k) -> H_k device tensor, read at enqueue time.
+        Returns the commit's new cache length."""
+        self.init_canvas(canvas)
+        for k in range(self.N):
+            self.step(k, hidden(k))
+        return self.commit(self.final_tokens(self.N - 1))
+
     def final_tokens(self, k: int):
         """The block step k commits: its argmax, or its sampled tokens under draw="sample"."""
         return (self.sampled if self.draw == "sample" else self.argmax)[k & 1]
