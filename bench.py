@@ -60,6 +60,8 @@ def parse():
                     help="skip the 8-canvas block-AR chain with commits")
     ap.add_argument("--no-small", action="store_true",
                     help="skip the protocol lines of the small and tiny workloads")
+    ap.add_argument("--no-cache-probe", action="store_true",
+                    help="skip the sampler head over a cache-resident slice of E")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the eager-vs-graph lines of fixed-step canvases")
     ap.add_argument("--canvases", type=int, default=7,
@@ -358,6 +360,11 @@ def main():
         "input_gen_s": round(t_gen, 1),
     }
 
+    if not args.no_cache_probe and cfg.V >= 65536:
+        cr = cache_resident_logits(ctx, cfg, Wd, args.roofline_reps)
+        # the in-step call: 1024 tiles over 256 CUs, four tiles per CU
+        cr["in_step_us_per_tile_per_cu"] = round(1e3 * logits_ms / (cfg.V / 256 / 256), 2)
+        result["cache_resident_logits"] = cr
     if not args.no_long_prefix:
         result["long_prefix_attention"] = long_prefix_attention(ctx, cfg, Wd, Hd[0], args.roofline_reps)
     del Kd, Vtd, loop
@@ -437,6 +444,39 @@ def measured_peaks(ctx):
 def _bf(a, dev):
     import torch
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def cache_resident_logits(ctx, cfg, Wd, reps):
+    """dg_logits_entropy over the first 32768 rows of E (128 MiB, held by the 256 MB
+    memory-side cache across back-to-back calls) for one 256-column canvas: 128 vocabulary
+    tiles, each the same work as one tile of the full-vocabulary call (1024 tiles, four
+    rounds of 256). If the full call were waiting on HBM, a tile would take longer there
+    than here; the per-tile times are reported side by side with the in-step call."""
+    import torch
+
+    import block_ar_canvas_amd as dg
+    dev = torch.device("cuda:0")
+    Vs = 32768
+    dims = dg.Dims(Vs, cfg.d, cfg.C, cfg.Hq, cfg.Hkv, cfg.hd, cfg.F)
+    E = Wd["E"][:Vs]
+    H = torch.randn(cfg.C, cfg.d, device=dev).to(torch.bfloat16)
+    ws = torch.empty(dg.workspace_bytes(dims, 0), dtype=torch.uint8, device=dev)
+    ent = torch.empty(cfg.C, dtype=torch.float32, device=dev)
+    am = torch.empty(cfg.C, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(10):
+        ctx.logits_entropy(dims, H, E, 0.4, ws, ent, am)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = max(reps, 20)
+    e0.record(stream)
+    for _ in range(n):
+        ctx.logits_entropy(dims, H, E, 0.4, ws, ent, am)
+    e1.record(stream)
+    e1.synchronize()
+    ctx.sync()
+    ms = e0.elapsed_time(e1) / n
+    return {"vocab_rows": Vs, "e_bytes": Vs * cfg.d * 2, "tiles": Vs // 256, "ms_per_call": round(ms, 4),
+            "us_per_tile_per_cu": round(1e3 * ms, 2)}
 
 
 def long_prefix_attention(ctx, cfg, Wd, H, reps):
