@@ -281,7 +281,11 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(AttnArgs a, int nq,
       mt = pair_max(mt) * a.scale_log2;     // the scale is positive: max commutes with it
       if (__builtin_amdgcn_ballot_w64(mt > mref + RESCALE_LOG2)) {
         const float mnew = fmaxf(mref, mt);
-        const float alpha = exp2_fast(mref - mnew);
+        // The ballot is per wave, and under the causal mask a wave can mix lanes that see
+        // keys with lanes that have seen none yet (a split starting inside the canvas, a
+        // wave straddling two heads): those keep m_ref = -inf and O = 0, and must not take
+        // exp2(-inf - -inf) = NaN.
+        const float alpha = mnew == -INFINITY ? 1.f : exp2_fast(mref - mnew);
         lsum *= alpha;
 #pragma unroll
         for (int et = 0; et < F::ET; ++et) O[et] *= alpha;
