@@ -129,3 +129,13 @@ def test_edge_commit_kv(dg_ctx, name):
     np.testing.assert_array_equal(Vtg[:, :, P2:], V0[:, :, P2:])
     assert maxrel(O.from_bf16(Kg[:, P0:P2]), O.from_bf16(Ko[:, P0:P2])) <= 2e-2
     assert maxrel(O.from_bf16(Vtg[:, :, P0:P2].transpose(0, 2, 1)), O.from_bf16(Vo[:, P0:P2])) <= 2e-2
+
+
+@pytest.mark.parametrize("name", list(EDGES))
+def test_edge_loop_parity(dg_ctx, name):
+    """Two whole canvases (all steps, commits between them) against the oracle's loop.
+    With one canvas position, or three vocabulary ids, a fraction-of-positions cap on
+    excused mismatches means nothing, so every mismatch must be excused (cutoff or tie)."""
+    from test_gpu_loop import run_both
+    s = run_both(dg_ctx, EDGES[name], n_canvas=2)
+    assert s["unexcused"] == 0, s
