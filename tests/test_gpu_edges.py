@@ -139,3 +139,32 @@ def test_edge_loop_parity(dg_ctx, name):
     from test_gpu_loop import run_both
     s = run_both(dg_ctx, EDGES[name], n_canvas=2)
     assert s["unexcused"] == 0, s
+
+
+@pytest.mark.parametrize("name", list(EDGES))
+def test_edge_sample_tokens_and_confidence(dg_ctx, name):
+    """dg_sample (inverse-CDF draw over the whole vocabulary) and dg_confidence at the edge
+    shapes; a drawn token may differ only where the oracle's target lies within the
+    device's rounding of a cumulative boundary."""
+    from gpu_util import sample_excused
+    cfg, W, Kp, Vp, Pcap, Wd = setup(name)
+    ws = ws_for(cfg, Pcap)
+    tgt = di.targets(cfg, 0)
+    for k in (0, cfg.N - 1):
+        H = di.hidden(cfg, W["E"], 0, k, tgt)
+        tau = O.temperature(k, cfg.N)
+        ent = torch.empty(cfg.C, dtype=torch.float32, device=DEV)
+        am = torch.empty(cfg.C, dtype=torch.int32, device=DEV)
+        dg_ctx.logits_entropy(cfg, bf16_dev(H), Wd["E"], tau, ws, ent, am)
+        tok = torch.full((cfg.C,), -1, dtype=torch.int32, device=DEV)
+        dg_ctx.sample(cfg, ws, 1, 4321 + k, 3, k, tok)
+        conf = torch.empty(cfg.C, dtype=torch.float32, device=DEV)
+        dg_ctx.confidence(cfg, ws, conf)
+        dg_ctx.sync()
+        _, _, p_r, _ = O.logits_entropy(H, W["E"], tau)
+        np.testing.assert_allclose(conf.cpu().numpy(), p_r.max(axis=1), rtol=2e-5, atol=0)
+        ref, margin = O.sample_tokens(p_r, 4321 + k, 3, k, B=1, with_margins=True)
+        g = tok.cpu().numpy()
+        assert np.all((g >= 0) & (g < cfg.V))
+        for i in np.nonzero(g != ref)[0]:
+            assert sample_excused(p_r[i], int(ref[i]), float(margin[i])), (k, i, g[i], ref[i])
