@@ -10,14 +10,17 @@
 //
 // With M this small every workgroup streams a long K range for a small output tile, so
 // the kernel is bound by how fast operand bytes reach the CUs, not by the MFMAs:
-//   * Workgroup tile 64 n x 64 m, K in stages of 128 (256-byte row pieces), fed by
-//     direct global -> LDS copies (global_load_lds_dwordx4) into an NS-stage ring with
-//     one barrier per stage; 256-byte LDS rows are XOR-swizzled by (row & 15) so the
-//     fragment reads are conflict-free on 64 banks.
-//   * 8 waves; wave w computes the whole 64 x 64 tile (four independent 32 x 32
-//     accumulators) for k16-step w of every stage, so each wave issues four
-//     independent MFMAs per stage instead of a dependent chain. The eight partial
-//     tiles are summed through LDS in a fixed wave order (deterministic).
+//   * Workgroup tile TN n x TM m (64 x 64, 32 x 64 or 32 x 32, chosen per launch so
+//     that the operand bytes each CU streams are fewest while the grid fills the
+//     chip), K in stages of 128 (256-byte row pieces), fed by direct global -> LDS
+//     copies (global_load_lds_dwordx4) into an NS-stage ring with one barrier per
+//     stage; 256-byte LDS rows are XOR-swizzled by (row & 15) so the fragment reads
+//     are conflict-free on 64 banks.
+//   * 8 waves; wave w computes the whole tile (up to four independent 32 x 32
+//     accumulators) for k16-step w of every stage, so a wave's MFMAs per stage do not
+//     form a dependent chain. The eight partial tiles are summed through LDS in a fixed
+//     wave order (deterministic), so every output element takes the same additions in
+//     the same order whatever the tile shape: results do not depend on the shape.
 //   * The epilogue (GELU, bf16 rounding) writes the tile to LDS and stores it with
 //     16-byte stores along whichever output direction is contiguous.
 //   * Workgroups that share a weight tile (same n tile, other m tiles) are placed on
@@ -29,30 +32,46 @@
 
 namespace {
 
-constexpr int BN = 64, BM = 64, BK = 128, NW = 8, NS = 4;
+constexpr int BK = 128, NW = 8;
 constexpr int RB = BK * 2;                  // bytes of one row piece per stage
-constexpr int TILE = 64 * RB;               // bytes of one operand tile per stage
-constexpr int STAGE = 2 * TILE;
-constexpr int RED = NW * 4 * 16 * 64 * 4;   // fp32 partial tiles of all waves
-constexpr int SMEM = NS * STAGE > RED ? NS * STAGE : RED;
-constexpr int OPITCH = BN + 8;              // bf16 output tile pitch (elements)
 
 DG_DEV int swz(int row, int chunk) { return row * RB + ((chunk ^ (row & 15)) << 4); }
 
-// s_waitcnt for "at most 4*rem of this wave's copies still in flight".
+// Shape of a launch: TN weight rows (n) x TM activation rows (m) per workgroup, each a
+// multiple of 32, and NS ring stages.
+template <int TN, int TM, int NS>
+struct Tile {
+  static constexpr int QN = TN / 32, QM = TM / 32, NQ = QN * QM;   // 32 x 32 MFMA tiles
+  static constexpr int WT = TN * RB;                // weight bytes of one stage
+  static constexpr int STAGE = WT + TM * RB;
+  static constexpr int CPW = QN + QM;               // copies per wave and stage (4 rows each)
+  static constexpr int RED = NW * NQ * 16 * 64 * 4; // fp32 partial tiles of all waves
+  static constexpr int SMEM = NS * STAGE > RED ? NS * STAGE : RED;
+  static constexpr int OPITCH = TN + 8;             // bf16 output tile pitch (elements)
+  static constexpr int RPW = NQ * 2;                // summed accumulator registers per wave
+};
+
+// s_waitcnt for "at most CPW*rem of this wave's copies still in flight" (rem <= 6).
+template <int CPW>
 DG_DEV void wait_stages(int rem) {
   switch (rem) {
     case 0: dma_wait<0>(); break;
-    case 1: dma_wait<4>(); break;
-    default: dma_wait<8>(); break;
+    case 1: dma_wait<CPW>(); break;
+    case 2: dma_wait<2 * CPW>(); break;
+    case 3: dma_wait<3 * CPW>(); break;
+    case 4: dma_wait<4 * CPW>(); break;
+    case 5: dma_wait<5 * CPW>(); break;
+    default: dma_wait<6 * CPW>(); break;
   }
 }
 
 // Output store modes of a segment (chosen on the host).
 enum { ST_SCALAR = 0, ST_NVEC = 1, ST_MVEC = 2 };
 
-template <bool GATHER>
+template <int TN, int TM, int NS, bool GATHER>
 __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
+  using T = Tile<TN, TM, NS>;
+  static_assert(TN % 32 == 0 && TM % 32 == 0 && TN <= 64 && TM <= 64 && NS >= 2 && NS <= 8, "shape");
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -70,21 +89,27 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
   for (int s = 1; s < a.nseg; ++s)
     if (nbg >= a.seg[s].nblk0) si = s;
   const GemmSeg &sg = a.seg[si];
-  const int nb0 = (nbg - sg.nblk0) * BN, m0 = mb * BM;
+  const int nb0 = (nbg - sg.nblk0) * TN, m0 = mb * TM;
   const int K = a.K / S;                             // depth of this part
   const int kbase = ks * K;
   const int nst = (K + BK - 1) / BK;
 
-  // Copy assignment: wave w fills rows [8w, 8w + 8) of both tiles, 4 rows (1 KiB) per
-  // instruction; lane l covers row 8w + 4j + l/16, physical 16-byte chunk l % 16.
-  const u16 *wrow[2], *xrow[2];
-  int lchunk[2];
+  // Copy assignment: wave w fills rows [w*TN/8, +TN/8) of the weight tile and
+  // [w*TM/8, +TM/8) of the activation tile, 4 rows (1 KiB) per instruction; lane l
+  // covers row base + l/16, physical 16-byte chunk l % 16.
+  const u16 *wrow[T::QN], *xrow[T::QM];
+  int wchunk[T::QN], xchunk[T::QM];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int R = 8 * wave + 4 * j + (lane >> 4);
-    lchunk[j] = (lane & 15) ^ (R & 15);
+  for (int j = 0; j < T::QN; ++j) {
+    const int R = (TN / 8) * wave + 4 * j + (lane >> 4);
+    wchunk[j] = (lane & 15) ^ (R & 15);
     const int n = min(nb0 + R, sg.N - 1);
     wrow[j] = sg.W + (int64_t)n * a.K + kbase;
+  }
+#pragma unroll
+  for (int j = 0; j < T::QM; ++j) {
+    const int R = (TM / 8) * wave + 4 * j + (lane >> 4);
+    xchunk[j] = (lane & 15) ^ (R & 15);
     const int m = min(m0 + R, a.M - 1);
     if (GATHER) {
       int tok = a.tokens[m];
@@ -100,106 +125,116 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
   const uint32_t lbase = lds_addr(smem);
   auto issue = [&](int i) {
     const int k0 = i * BK;
-    const uint32_t wb = lbase + (uint32_t)((i % NS) * STAGE);
+    const uint32_t wb = lbase + (uint32_t)((i % NS) * T::STAGE);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int k = min(k0 + 8 * lchunk[j], K - 8);   // chunks past K: any valid data
-      const uint32_t off = (uint32_t)((8 * wave + 4 * j) * RB);
-      dma16(wrow[j] + k, wb + off);
-      dma16(xrow[j] + k, wb + TILE + off);
+    for (int j = 0; j < T::QN; ++j) {
+      const int k = min(k0 + 8 * wchunk[j], K - 8);   // chunks past K: any valid data
+      dma16(wrow[j] + k, wb + (uint32_t)(((TN / 8) * wave + 4 * j) * RB));
+    }
+#pragma unroll
+    for (int j = 0; j < T::QM; ++j) {
+      const int k = min(k0 + 8 * xchunk[j], K - 8);
+      dma16(xrow[j] + k, wb + (uint32_t)(T::WT + ((TM / 8) * wave + 4 * j) * RB));
     }
   };
 
-  f32x16_t acc[4] = {};
+  // Wave w computes the whole tile for k16-step w of every stage; tile q = i + QN*j
+  // covers n [32i, +32) x m [32j, +32).
+  f32x16_t acc[T::NQ] = {};
   for (int i = 0; i < NS - 1 && i < nst; ++i) issue(i);
   for (int i = 0; i < nst; ++i) {
-    wait_stages(min(nst - 1 - i, NS - 2));
+    wait_stages<T::CPW>(min(nst - 1 - i, NS - 2));
     __syncthreads();
     if (i + NS - 1 < nst) issue(i + NS - 1);
     if (i * BK + 16 * wave < K) {
-      const uint8_t *Ws = smem + (i % NS) * STAGE, *Xs = Ws + TILE;
+      const uint8_t *Ws = smem + (i % NS) * T::STAGE, *Xs = Ws + T::WT;
       const int c = 2 * wave + h;
-      const u32x4_t a0 = *(const u32x4_t *)(Ws + swz(l32, c));
-      const u32x4_t a1 = *(const u32x4_t *)(Ws + swz(32 + l32, c));
-      const u32x4_t b0 = *(const u32x4_t *)(Xs + swz(l32, c));
-      const u32x4_t b1 = *(const u32x4_t *)(Xs + swz(32 + l32, c));
-      acc[0] = mfma_32x32x16(a0, b0, acc[0]);
-      acc[1] = mfma_32x32x16(a1, b0, acc[1]);
-      acc[2] = mfma_32x32x16(a0, b1, acc[2]);
-      acc[3] = mfma_32x32x16(a1, b1, acc[3]);
+      u32x4_t af[T::QN], bf[T::QM];
+#pragma unroll
+      for (int j = 0; j < T::QN; ++j) af[j] = *(const u32x4_t *)(Ws + swz(32 * j + l32, c));
+#pragma unroll
+      for (int j = 0; j < T::QM; ++j) bf[j] = *(const u32x4_t *)(Xs + swz(32 * j + l32, c));
+#pragma unroll
+      for (int jm = 0; jm < T::QM; ++jm)
+#pragma unroll
+        for (int jn = 0; jn < T::QN; ++jn)
+          acc[jn + T::QN * jm] = mfma_32x32x16(af[jn], bf[jm], acc[jn + T::QN * jm]);
     }
   }
 
-  // Sum of the eight waves' tiles. Tile q covers n [32(q&1), +32) x m [32(q>>1), +32).
+  // Sum of the eight waves' tiles in a fixed wave order; wave w then owns registers
+  // [w*RPW, +RPW) of the tile sequence (tile q = index / 16, register = index % 16).
   __syncthreads();
   float *red = (float *)smem;
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
+  for (int q = 0; q < T::NQ; ++q)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) red[((wave * 4 + q) * 16 + r) * 64 + lane] = acc[q][r];
+    for (int r = 0; r < 16; ++r) red[((wave * T::NQ + q) * 16 + r) * 64 + lane] = acc[q][r];
   __syncthreads();
-  const int q = wave >> 1, rb = 8 * (wave & 1);
-  float v[8];
+  const int q = (wave * T::RPW) >> 4, rb = (wave * T::RPW) & 15;
+  const int qn = q % T::QN, qm = q / T::QN;
+  float v[T::RPW];
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
+  for (int r = 0; r < T::RPW; ++r) {
     float s = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) s += red[((w * 4 + q) * 16 + rb + r) * 64 + lane];
+    for (int w = 0; w < NW; ++w) s += red[((w * T::NQ + q) * 16 + rb + r) * 64 + lane];
     if (a.gelu) s = 0.5f * s * (1.0f + erff(s * 0.70710678118654752f));
     v[r] = s;
   }
   if (a.out32) {                                     // fp32 output, row-major
-    const int m = m0 + (q >> 1) * 32 + l32;
+    const int m = m0 + qm * 32 + l32;
     if (m < sg.m_store) {
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int n = nb0 + (q & 1) * 32 + acc_row(rb + r, h);
+      for (int r = 0; r < T::RPW; ++r) {
+        const int n = nb0 + qn * 32 + acc_row(rb + r, h);
         if (n < sg.N) a.out32[ks * a.split_stride + (int64_t)m * a.ld32 + n] = v[r];
       }
     }
     return;
   }
   __syncthreads();
-  u16 *ot = (u16 *)smem;   // [64 m][OPITCH] bf16
-  const int ml = (q >> 1) * 32 + l32;
+  u16 *ot = (u16 *)smem;   // [TM m][OPITCH] bf16
+  const int ml = qm * 32 + l32;
 #pragma unroll
-  for (int r = 0; r < 8; ++r) ot[ml * OPITCH + (q & 1) * 32 + acc_row(rb + r, h)] = f32_to_bf16(v[r]);
+  for (int r = 0; r < T::RPW; ++r) ot[ml * T::OPITCH + qn * 32 + acc_row(rb + r, h)] = f32_to_bf16(v[r]);
   __syncthreads();
 
   const int mode = a.store_mode[si];
-  if (mode == ST_NVEC) {
-    const int row = tid >> 3, c8 = (tid & 7) * 8;
-    const int m = m0 + row, n = nb0 + c8;
-    if (m < sg.m_store && n < sg.N)
-      *(uint4 *)(sg.out + (int64_t)m * sg.sm + (int64_t)(n / sg.seg) * sg.sg +
-                 (int64_t)(n % sg.seg) * sg.se) = *(const uint4 *)(ot + row * OPITCH + c8);
-  } else if (mode == ST_MVEC) {
-    const int col = tid >> 3, r8 = (tid & 7) * 8;
+  if (mode == ST_MVEC) {
+    if (tid >= TN * (TM / 8)) return;
+    const int col = tid / (TM / 8), r8 = (tid % (TM / 8)) * 8;
     const int m = m0 + r8, n = nb0 + col;
     if (n < sg.N && m + 8 > sg.m_store) {
       for (int i = 0; i < 8 && m + i < sg.m_store; ++i)
         sg.out[(int64_t)(m + i) + (int64_t)(n / sg.seg) * sg.sg + (int64_t)(n % sg.seg) * sg.se] =
-            ot[(r8 + i) * OPITCH + col];
+            ot[(r8 + i) * T::OPITCH + col];
     } else if (n < sg.N) {
       uint32_t w4[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        w4[i] = (uint32_t)ot[(r8 + 2 * i) * OPITCH + col] |
-                ((uint32_t)ot[(r8 + 2 * i + 1) * OPITCH + col] << 16);
+        w4[i] = (uint32_t)ot[(r8 + 2 * i) * T::OPITCH + col] |
+                ((uint32_t)ot[(r8 + 2 * i + 1) * T::OPITCH + col] << 16);
       *(uint4 *)(sg.out + (int64_t)m + (int64_t)(n / sg.seg) * sg.sg + (int64_t)(n % sg.seg) * sg.se) =
           make_uint4(w4[0], w4[1], w4[2], w4[3]);
     }
-  } else {
-    const int row = tid >> 3, c8 = (tid & 7) * 8;
-    const int m = m0 + row;
-    if (m < sg.m_store) {
+    return;
+  }
+  if (tid >= TM * (TN / 8)) return;
+  const int row = tid / (TN / 8), c8 = (tid % (TN / 8)) * 8;
+  const int m = m0 + row;
+  if (mode == ST_NVEC) {
+    const int n = nb0 + c8;
+    if (m < sg.m_store && n < sg.N)
+      *(uint4 *)(sg.out + (int64_t)m * sg.sm + (int64_t)(n / sg.seg) * sg.sg +
+                 (int64_t)(n % sg.seg) * sg.se) = *(const uint4 *)(ot + row * T::OPITCH + c8);
+  } else if (m < sg.m_store) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int n = nb0 + c8 + i;
-        if (n < sg.N)
-          sg.out[(int64_t)m * sg.sm + (int64_t)(n / sg.seg) * sg.sg + (int64_t)(n % sg.seg) * sg.se] =
-              ot[row * OPITCH + c8 + i];
-      }
+    for (int i = 0; i < 8; ++i) {
+      const int n = nb0 + c8 + i;
+      if (n < sg.N)
+        sg.out[(int64_t)m * sg.sm + (int64_t)(n / sg.seg) * sg.sg + (int64_t)(n % sg.seg) * sg.se] =
+            ot[row * T::OPITCH + c8 + i];
     }
   }
 }
@@ -240,35 +275,82 @@ int store_mode(const GemmSeg &s) {
 
 }  // namespace
 
-hipError_t dg_launch_gemm(const GemmArgs &a0, hipStream_t st) {
+namespace {
+
+// Sets the segments' first n blocks and store modes for tile width TN and launches one
+// tile shape.
+template <int TN, int TM, int NS>
+hipError_t launch_tile(GemmArgs a, int S, hipStream_t st) {
+  constexpr int smem = Tile<TN, TM, NS>::SMEM;
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<false>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, SMEM);
+    hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<TN, TM, NS, false>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void *)gemm_kernel<true>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, SMEM);
+      e = hipFuncSetAttribute((const void *)gemm_kernel<TN, TM, NS, true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  GemmArgs a = a0;
-  int nblk = 0;
-  int mmax = a.M;
+  int nblk = 0, mmax = a.M;
   for (int s = 0; s < a.nseg; ++s) {
     a.seg[s].nblk0 = nblk;
-    nblk += (a.seg[s].N + BN - 1) / BN;
+    nblk += (a.seg[s].N + TN - 1) / TN;
     if (a.seg[s].m_store > mmax) mmax = a.seg[s].m_store;
     a.store_mode[s] = store_mode(a.seg[s]);
   }
-  const int MB = (mmax + BM - 1) / BM;
-  const int S = (a.out32 && a.ksplit > 1) ? a.ksplit : 1;
-  if (S > 1 && a.K % (32 * S) != 0) return hipErrorInvalidValue;
+  const int MB = (mmax + TM - 1) / TM;
   const dim3 grid(nblk * MB * S);
   if (a.A)
-    hipLaunchKernelGGL(gemm_kernel<false>, grid, dim3(512), SMEM, st, a, MB);
+    hipLaunchKernelGGL((gemm_kernel<TN, TM, NS, false>), grid, dim3(512), smem, st, a, MB);
   else
-    hipLaunchKernelGGL(gemm_kernel<true>, grid, dim3(512), SMEM, st, a, MB);
+    hipLaunchKernelGGL((gemm_kernel<TN, TM, NS, true>), grid, dim3(512), smem, st, a, MB);
   return hipGetLastError();
+}
+
+int device_cus() {
+  static int n = 0;
+  if (n <= 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+  }
+  return n;
+}
+
+}  // namespace
+
+// Tile shape: every workgroup streams (TN + TM) rows of K through its CU, so the shape
+// with the fewest operand bytes per CU, rounds of workgroups x (TN + TM), is taken; on
+// a tie the one with fewer workgroups (less total copying).
+hipError_t dg_launch_gemm(const GemmArgs &a, hipStream_t st) {
+  const int S = (a.out32 && a.ksplit > 1) ? a.ksplit : 1;
+  if (S > 1 && a.K % (32 * S) != 0) return hipErrorInvalidValue;
+  int mmax = a.M;
+  for (int s = 0; s < a.nseg; ++s)
+    if (a.seg[s].m_store > mmax) mmax = a.seg[s].m_store;
+  const int ncu = device_cus();
+  static const int shapes[3][2] = {{64, 64}, {32, 64}, {32, 32}};
+  int best = 0;
+  int64_t best_cost = INT64_MAX, best_wg = INT64_MAX;
+  for (int c = 0; c < 3; ++c) {
+    const int tn = shapes[c][0], tm = shapes[c][1];
+    int64_t nblk = 0;
+    for (int s = 0; s < a.nseg; ++s) nblk += (a.seg[s].N + tn - 1) / tn;
+    const int64_t wg = nblk * ((mmax + tm - 1) / tm) * S;
+    const int64_t cost = (wg + ncu - 1) / ncu * (tn + tm);
+    if (cost < best_cost || (cost == best_cost && wg < best_wg)) {
+      best = c;
+      best_cost = cost;
+      best_wg = wg;
+    }
+  }
+  switch (best) {
+    case 0: return launch_tile<64, 64, 4>(a, S, st);
+    case 1: return launch_tile<32, 64, 5>(a, S, st);
+    default: return launch_tile<32, 32, 4>(a, S, st);
+  }
 }
 
 namespace {
