@@ -31,8 +31,9 @@
 
 namespace {
 
-// Workgroup tile 256 vocabulary rows x 256 canvas columns, 8 waves (4 along the
-// vocabulary x 2 along the canvas), each wave 64 x 128 = 2 x 4 MFMA tiles (128
+// Workgroup tile 256 vocabulary rows x BCT canvas columns (BCT = 256, or 128 when the
+// vocabulary tiles alone would leave CUs idle), 8 waves (4 along the vocabulary x 2
+// along the canvas), each wave 64 x BCT/2 = 2 x BCT/64 MFMA tiles (up to 128
 // accumulators, two waves per SIMD so one wave's LDS-read latency hides behind the
 // other's MFMAs). The model width is consumed in steps of BK = 64 through LDS rings
 // filled by direct global -> LDS copies: E (streamed from HBM) has 3 stages, so two are
@@ -41,9 +42,10 @@ namespace {
 // lanes). LDS rows are 128 bytes with XOR-swizzled 16-byte chunks (see swz), so
 // fragment reads are free of bank conflicts. E rows are stored in perm_row order within
 // each 32-row tile, so fragment reads are plain row reads.
-constexpr int BV = DG_BV, BC = 256, BK = 64, NSE = 3, NSH = 2;
-constexpr int TILE = 256 * 128;                  // bytes of one 256-row x 64-k stage
-constexpr int SMEM = (NSE + NSH) * TILE;         // 160 KiB
+constexpr int BV = DG_BV, BK = 64, NSE = 3, NSH = 2;
+constexpr int TILE = 256 * 128;                  // bytes of one 256-row x 64-k E stage
+template <int BCT>
+constexpr int smem_bytes() { return NSE * TILE + NSH * BCT * 128; }   // 160 or 128 KiB
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -57,8 +59,12 @@ DG_DEV bool better(float u, int v, float best, int bi) {
 DG_DEV int swz(int R, int c) { return R * 128 + ((c ^ ((R >> 1) & 7)) << 4); }
 
 // HALF_TAIL: d is an odd multiple of 32, so the last K chunk holds 32 valid columns.
-template <bool HALF_TAIL>
+template <bool HALF_TAIL, int BCT>
 __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a) {
+  static_assert(BCT == 128 || BCT == 256, "canvas block");
+  constexpr int BC = BCT, NTW = BCT / 64;          // MFMA tiles per wave along the canvas
+  constexpr int HC = BCT / 64;                     // H copy instructions per wave and stage
+  constexpr int HT = BCT * 128;                    // bytes of one H stage
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   // epilogue scratch aliases the stage rings once the main loop is done
   float(*red_m)[BC] = (float(*)[BC])(smem);
@@ -96,23 +102,27 @@ __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a) {
   const int v0 = vt * BV;
   const int cb = cbk * BC;
 
-  // Copy duties per stage: rows [32*wave, 32*wave + 32) of E and of H, as 4 copy
-  // instructions of 8 rows each. Lane l of instruction j fills LDS row
-  // R = 32*wave + 8*j + l/8 at chunk slot l%8, i.e. logical chunk (l%8) ^ ((R>>1)&7).
-  const u16 *ge[4], *gh[4];
+  // Copy duties per stage: rows [32*wave, +32) of E and [BCT/8*wave, +BCT/8) of H, in
+  // copy instructions of 8 rows each. Lane l of instruction j fills LDS row
+  // R = base + 8*j + l/8 at chunk slot l%8, i.e. logical chunk (l%8) ^ ((R>>1)&7).
+  const u16 *ge[4], *gh[HC];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int R = 32 * wave + 8 * j + (lane >> 3);
     const int c = (lane & 7) ^ ((R >> 1) & 7);
     int er = v0 + (R & ~31) + perm_row(R & 31);
     er = er < a.V ? er : a.V - 1;                    // clamp: masked in the epilogue
+    ge[j] = a.E + (int64_t)er * a.d + c * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < HC; ++j) {
+    const int R = (BCT / 8) * wave + 8 * j + (lane >> 3);
+    const int c = (lane & 7) ^ ((R >> 1) & 7);
     int hr = cb + R;
     hr = hr < a.C ? hr : a.C - 1;                    // clamp: columns never stored
-    ge[j] = a.E + (int64_t)er * a.d + c * 8;
     gh[j] = a.H + (int64_t)hr * a.d + c * 8;
   }
   const uint32_t sbase = lds_addr(smem);
-  const uint32_t wrow = (uint32_t)(32 * wave) * 128u;
 
   // K order: workgroups start at different chunks (rotation by the tile index) so the
   // GPU's concurrent copies spread over the address space. With HALF_TAIL the partial
@@ -122,43 +132,47 @@ __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a) {
   const int KF = a.d / BK;
   const int rot = KF > 0 ? vt % KF : 0;
   auto kcol = [&](int it) { return (it < KF ? (it + rot) % KF : it) * BK; };
-  auto issue = [&](int it, const u16 *const *g, uint32_t st) {
+  // Copies of one stage: NJ instructions of 8 rows from rows `row0` of the stage.
+  auto issue = [&](int it, const u16 *const *g, int nj, int row0, uint32_t st) {
     const int k = kcol(it);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      if (j >= nj) break;
       int kk = k;
       if (HALF_TAIL && it == KI - 1) {
-        const int R = 32 * wave + 8 * j + (lane >> 3);
+        const int R = row0 + 8 * j + (lane >> 3);
         const int c = (lane & 7) ^ ((R >> 1) & 7);   // logical chunk of this copy lane
         kk = k - (c >= 4 ? 32 : 0);
       }
-      dma16(g[j] + kk, st + j * 1024);
+      dma16(g[j] + kk, st + (uint32_t)(row0 * 128 + j * 1024));
     }
   };
-  auto issue_e = [&](int it) { issue(it, ge, sbase + (uint32_t)(it % NSE) * TILE + wrow); };
-  auto issue_h = [&](int it) { issue(it, gh, sbase + (uint32_t)(NSE + it % NSH) * TILE + wrow); };
+  auto issue_e = [&](int it) { issue(it, ge, 4, 32 * wave, sbase + (uint32_t)(it % NSE) * TILE); };
+  auto issue_h = [&](int it) {
+    issue(it, gh, HC, (BCT / 8) * wave, sbase + (uint32_t)(NSE * TILE + (it % NSH) * HT));
+  };
 
-  f32x16_t acc[2][4];
+  f32x16_t acc[2][NTW];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+    for (int j = 0; j < NTW; ++j) acc[i][j] = f32x16_t{};
 
   auto compute = [&](int it, int nks) {
     const char *se = smem + (it % NSE) * TILE;
-    const char *sh = smem + (NSE + it % NSH) * TILE;
+    const char *sh = smem + NSE * TILE + (it % NSH) * HT;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       if (ks >= nks) break;
-      u32x4_t af[2], bf[4];
+      u32x4_t af[2], bf[NTW];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
         af[mt] = *(const u32x4_t *)(se + swz(wv * 64 + mt * 32 + l32, 2 * ks + hh));
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        bf[nt] = *(const u32x4_t *)(sh + swz(wc * 128 + nt * 32 + l32, 2 * ks + hh));
+      for (int nt = 0; nt < NTW; ++nt)
+        bf[nt] = *(const u32x4_t *)(sh + swz(wc * (BCT / 2) + nt * 32 + l32, 2 * ks + hh));
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
+      for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) acc[mt][nt] = mfma_32x32x16(af[mt], bf[nt], acc[mt][nt]);
     }
@@ -196,11 +210,11 @@ __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a) {
       for (int r = 0; r < 16; ++r)
         if (v0 + wv * 64 + mt * 32 + acc_row_perm(r, hh) >= a.V)
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) acc[mt][nt][r] = -INFINITY;
+          for (int nt = 0; nt < NTW; ++nt) acc[mt][nt][r] = -INFINITY;
   }
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int lc = wc * 128 + nt * 32 + l32;
+  for (int nt = 0; nt < NTW; ++nt) {
+    const int lc = wc * (BCT / 2) + nt * 32 + l32;
     float best = -INFINITY;
     int bi = 0x7FFFFFFF;
 #pragma unroll
@@ -231,8 +245,8 @@ __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a) {
   // ---------------- phase 2: exp2, Z_t, S_t (log2 units), and p~ fragments
   const int VS = a.T * (BV / 16);            // 16-row vocabulary steps in p~
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int lc = wc * 128 + nt * 32 + l32;
+  for (int nt = 0; nt < NTW; ++nt) {
+    const int lc = wc * (BCT / 2) + nt * 32 + l32;
     const float m = ceilf(fmaxf(fmaxf(red_m[0][lc], red_m[1][lc]), fmaxf(red_m[2][lc], red_m[3][lc])));
     const float nm = -m;
     float Z = 0.f, S = 0.f;
@@ -254,7 +268,7 @@ __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a) {
       red_z[wv][lc] = Z;
       red_s[wv][lc] = S;
     }
-    const int ctile = (cb + wc * 128 + nt * 32) / 32;
+    const int ctile = (cb + wc * (BCT / 2) + nt * 32) / 32;
     if (ctile * 32 < a.Cpad) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
@@ -413,23 +427,50 @@ hipError_t dg_launch_confidence(int C, const float *colP, float *conf, hipStream
   return hipGetLastError();
 }
 
-hipError_t dg_launch_logits(const LogitsArgs &a, hipStream_t st) {
+namespace {
+
+template <int BCT>
+hipError_t launch_tiles(const LogitsArgs &a, hipStream_t st) {
+  constexpr int smem = smem_bytes<BCT>();
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void *)logits_tile_kernel<false>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, SMEM);
+    hipError_t e = hipFuncSetAttribute((const void *)logits_tile_kernel<false, BCT>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void *)logits_tile_kernel<true>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, SMEM);
+      e = hipFuncSetAttribute((const void *)logits_tile_kernel<true, BCT>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  const dim3 grid(a.T * ((a.Cpad + BC - 1) / BC));
+  const dim3 grid(a.T * ((a.Cpad + BCT - 1) / BCT));
   if (a.d % BK)
-    hipLaunchKernelGGL(logits_tile_kernel<true>, grid, dim3(512), SMEM, st, a);
+    hipLaunchKernelGGL((logits_tile_kernel<true, BCT>), grid, dim3(512), smem, st, a);
   else
-    hipLaunchKernelGGL(logits_tile_kernel<false>, grid, dim3(512), SMEM, st, a);
-  hipError_t e = hipGetLastError();
+    hipLaunchKernelGGL((logits_tile_kernel<false, BCT>), grid, dim3(512), smem, st, a);
+  return hipGetLastError();
+}
+
+int device_cus() {
+  static int n = 0;
+  if (n <= 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+  }
+  return n;
+}
+
+}  // namespace
+
+// Canvas blocks of 128 columns when at most 128 columns are padded in, or when blocks of
+// 256 would give fewer workgroups than CUs (a short vocabulary): each workgroup then
+// streams its E tile and half as many H rows, the two blocks of a tile share the E rows
+// through L2, and twice as many CUs work. Otherwise blocks of 256 (more FLOP per copied
+// byte).
+hipError_t dg_launch_logits(const LogitsArgs &a, hipStream_t st) {
+  const bool narrow = a.Cpad <= 128 || (int64_t)a.T * ((a.Cpad + 255) / 256) < device_cus();
+  hipError_t e = narrow ? launch_tiles<128>(a, st) : launch_tiles<256>(a, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(row_finalize_kernel, dim3(a.C), dim3(256), 0, st, a);
   return hipGetLastError();
