@@ -33,8 +33,8 @@ struct dg_ctx_s {
   const void *p0_ws = nullptr;
   dg_dims p0_dims = {0, 0, 0, 0, 0, 0, 0};
   bool p0_valid = false;
-  // Second stream (default priority) and fork/join events of dg_moe_ffn, made on its
-  // first call: the shared expert runs beside the routed experts.
+  // Second stream (default priority) and fork/join events of dg_moe_ffn, made by
+  // dg_create: the shared expert runs beside the routed experts.
   hipStream_t side = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   // Device address of this device's static scratch (NULL if the lookup failed).
@@ -235,8 +235,13 @@ dg_status dg_create(dg_ctx *out, int device, void *hip_stream) {
   hipError_t e = hipSetDevice(device);
   if (e == hipSuccess) e = hipMalloc((void **)&ctx->d_status, sizeof(int));
   if (e == hipSuccess) e = hipMemset(ctx->d_status, 0, sizeof(int));
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&ctx->side, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->ev_fork, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->ev_join, hipEventDisableTiming);
   if (e != hipSuccess) {
     if (ctx->d_status) (void)hipFree(ctx->d_status);
+    if (ctx->side) (void)hipStreamDestroy(ctx->side);
+    if (ctx->ev_fork) (void)hipEventDestroy(ctx->ev_fork);
     delete ctx;
     return DG_ERR_HIP;
   }
@@ -378,12 +383,6 @@ dg_status dg_moe_ffn(dg_ctx ctx, const dg_moe_dims *m, int32_t C, const dg_bf16 
   u16 *ys = ws_at<u16>(ws, w.ys);
 
   hipError_t e = hipSuccess;
-  if (!ctx->side) {
-    e = hipStreamCreateWithFlags(&ctx->side, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->ev_fork, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->ev_join, hipEventDisableTiming);
-    if (e != hipSuccess) return hip_fail(ctx, e, "dg_moe_ffn(side stream)");
-  }
 
   // shared expert on the side stream: it needs only X, and overlaps the routing and the
   // routed experts; the combine waits for it

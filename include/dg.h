@@ -30,8 +30,8 @@
  *  - Calls validate their arguments on the host, enqueue work on the context's HIP
  *    stream and return without waiting. No call allocates or frees device memory;
  *    scratch space comes from the caller's workspace (dg_workspace_bytes,
- *    dg_moe_workspace_bytes). The context itself holds a status word, made by
- *    dg_create, and the second stream and events that the first dg_moe_ffn call makes.
+ *    dg_moe_workspace_bytes). The context itself holds a status word, a second
+ *    stream and two events (for dg_moe_ffn), all made by dg_create.
  *  - On a non-OK return nothing was enqueued; dg_last_error() describes the problem.
  *  - Conditions only the device can see (a token id outside [0, V), non-finite
  *    logits) set a sticky status word in the context, reported by dg_sync().
@@ -77,7 +77,8 @@ typedef struct {
 /* ---------------------------------------------------------------- context */
 /* Creates a context on HIP device `device` that enqueues on `hip_stream`
  * (a hipStream_t; NULL = the device's null stream). Allocates the context's status
- * word on the device. */
+ * word on the device and makes its second stream (default priority) and the two events
+ * dg_moe_ffn forks and joins with. */
 dg_status dg_create(dg_ctx *out, int device, void *hip_stream);
 void dg_destroy(dg_ctx ctx);
 /* Switches the stream later calls enqueue on. */
@@ -269,7 +270,7 @@ dg_status dg_prefill_block(dg_ctx ctx, const dg_dims *dims, const int32_t *token
  * output; n_active (device, optional) = the number of distinct experts used. The
  * workspace holds dg_moe_workspace_bytes(m, C) bytes. DG_ERR_SHAPE unless d, Fe, Fs are
  * positive multiples of 32, 1 <= K <= min(E, 32), E <= 256, C <= 1024 and C * K <= 8192.
- * The shared expert runs on a second stream of the context (made on the first call,
+ * The shared expert runs on a second stream of the context (made by dg_create,
  * default priority), forked from and joined back into the context's stream with events:
  * the call stays ordered on the context's stream like every other call. */
 typedef struct { int32_t d, E, K, Fe, Fs; } dg_moe_dims;
