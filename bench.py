@@ -760,8 +760,9 @@ def oracle_steps(cfg, W, Kp, Vp, k0, n_steps):
 
 def cpu_baseline(cfg, W, Kp, n_steps):
     """The CPU oracle, as it stands, on bounded samples: n full steps of the workload's
-    canvas with every BLAS thread, and two steps of the small workload with every thread
-    and one step with one thread."""
+    canvas with every BLAS thread; two steps of the small workload with every thread and
+    one step with one thread; a whole tiny-workload canvas; and canvas attention over the
+    262144-token prefix for one KV head (scaled to all heads)."""
     import dg_inputs as di
 
     model, blas, threads, affinity = cpu_info()
@@ -780,6 +781,12 @@ def cpu_baseline(cfg, W, Kp, n_steps):
             sec_small_1 = oracle_steps(sm, Ws, Ks, Vs, sm.N // 2, 1)
     except Exception:
         sec_small_1 = None
+    del Ws, Ks, Vs
+    ty = di.config("tiny")
+    Wt = di.weights(ty)
+    Kt, Vt = di.prefix_kv(ty, ty.P0 + ty.C)
+    sec_tiny = oracle_steps(ty, Wt, Kt, Vt, 0, ty.N) / ty.N
+    sec_lp_head = long_prefix_attention_oracle_head(cfg, W)
     return {"value": round(n_steps / sec, 5), "unit": "steps/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{n_steps} full denoise step(s) of {cfg.name} (k={cfg.N // 2}..), numpy float64, "
@@ -788,7 +795,32 @@ def cpu_baseline(cfg, W, Kp, n_steps):
             "small_s_per_step": round(sec_small, 4),
             "small_s_per_step_1_thread": None if sec_small_1 is None else round(sec_small_1, 4),
             "small_sample": "small workload (V 32768, d 1024, prefix 2048): 2 steps with every "
-                            "BLAS thread, 1 step with one thread"}
+                            "BLAS thread, 1 step with one thread",
+            "tiny_s_per_step": round(sec_tiny, 5),
+            "long_prefix_attention_s_per_call": round(sec_lp_head * cfg.Hkv, 2),
+            "long_prefix_attention_sample": f"canvas attention over the 262144-token prefix for one of "
+                                            f"{cfg.Hkv} KV heads (its {cfg.Hq // cfg.Hkv} query heads, "
+                                            f"{sec_lp_head:.1f} s), times {cfg.Hkv}"}
+
+
+def long_prefix_attention_oracle_head(cfg, W):
+    """Seconds the oracle takes for canvas attention over the long-prefix cache restricted
+    to KV head 0 and its query heads (the embedding gather, their Q/K/V projections,
+    attention over prefix + canvas, and their share of Wo), on the long-prefix workload's
+    keys and values for that head."""
+    import oracle as O
+    import dg_inputs as di
+
+    lp = di.config("long_prefix")
+    G, hd = cfg.Hq // cfg.Hkv, cfg.hd
+    Kp = di.gaussian_bf16(lp.seed, di.TAG_KP, (1, lp.P0, hd), 1.0)   # = KV head 0 of the cache
+    Vp = di.gaussian_bf16(lp.seed, di.TAG_VP, (1, lp.P0, hd), 1.0)
+    tok = di.targets(lp, 0)
+    Wq, Wk, Wv = W["Wq"][:G * hd], W["Wk"][:hd], W["Wv"][:hd]
+    Wo = np.ascontiguousarray(W["Wo"][:, :G * hd])
+    t0 = time.perf_counter()
+    O.canvas_attn(tok, None, W["E"], Wq, Wk, Wv, Wo, Kp, Vp, lp.P0, G, 1, hd)
+    return time.perf_counter() - t0
 
 
 if __name__ == "__main__":
