@@ -60,6 +60,15 @@ dg_status hip_fail(dg_ctx ctx, hipError_t e, const char *where) {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Null check, then the context's device is made current for what follows (the null
+// stream, launch attributes and CU counts are per device).
+#define DG_ENTER()                                                                \
+  do {                                                                            \
+    if (!ctx) return DG_ERR_NULL;                                                 \
+    const hipError_t e_dev = hipSetDevice(ctx->device);                           \
+    if (e_dev != hipSuccess) return hip_fail(ctx, e_dev, __func__);               \
+  } while (0)
+
 #define DG_REQUIRE_PTR(p)                                                         \
   do {                                                                            \
     if (!(p)) return fail(ctx, DG_ERR_NULL, "%s: %s is NULL", __func__, #p);      \
@@ -100,7 +109,6 @@ T *ws_at(void *ws, size_t off) {
 
 // Per-device address of the static scratch, looked up once per device (the device must
 // be current) and kept for the life of the process, like the array itself.
-constexpr int DG_MAX_DEVICES = 64;
 std::mutex g_scratch_mu;
 bool g_scratch_done[DG_MAX_DEVICES];
 void *g_scratch_ptr[DG_MAX_DEVICES];
@@ -277,7 +285,7 @@ dg_status dg_set_stream(dg_ctx ctx, void *hip_stream) {
 const char *dg_last_error(dg_ctx ctx) { return ctx ? ctx->err : "NULL context"; }
 
 dg_status dg_sync(dg_ctx ctx) {
-  if (!ctx) return DG_ERR_NULL;
+  DG_ENTER();
   hipError_t e = hipStreamSynchronize(ctx->stream);
   if (e != hipSuccess) return hip_fail(ctx, e, "dg_sync");
   int st = 0;
@@ -290,7 +298,7 @@ dg_status dg_sync(dg_ctx ctx) {
 }
 
 dg_status dg_clear_status(dg_ctx ctx) {
-  if (!ctx) return DG_ERR_NULL;
+  DG_ENTER();
   hipError_t e = hipMemsetAsync(ctx->d_status, 0, sizeof(int), ctx->stream);
   return e == hipSuccess ? DG_OK : hip_fail(ctx, e, "dg_clear_status");
 }
@@ -310,7 +318,7 @@ dg_status dg_canvas_attn(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens,
                          const dg_bf16 *Wk, const dg_bf16 *Wv, const dg_bf16 *Wo,
                          const dg_bf16 *Kp, const dg_bf16 *Vt, int64_t P, int64_t Pcap,
                          void *ws, dg_bf16 *A) {
-  if (!ctx) return DG_ERR_NULL;
+  DG_ENTER();
   dg_status st = check_canvas_attn(ctx, __func__, dims, tokens, z, E, Wq, Wk, Wv, Wo, Kp, Vt, P, Pcap, A);
   if (st) return st;
   DG_REQUIRE_PTR(ws);
@@ -327,7 +335,7 @@ dg_status dg_canvas_attn_static(dg_ctx ctx, const dg_dims *dims, const int32_t *
                                 const dg_bf16 *Wk, const dg_bf16 *Wv, const dg_bf16 *Wo,
                                 const dg_bf16 *Kp, const dg_bf16 *Vt, int64_t P, int64_t Pcap,
                                 dg_bf16 *A) {
-  if (!ctx) return DG_ERR_NULL;
+  DG_ENTER();
   dg_status st = check_canvas_attn(ctx, __func__, dims, tokens, z, E, Wq, Wk, Wv, Wo, Kp, Vt, P, Pcap, A);
   if (st) return st;
   if (!ctx->scratch)
@@ -364,7 +372,7 @@ size_t dg_moe_workspace_bytes(const dg_moe_dims *m, int32_t C) {
 dg_status dg_moe_ffn(dg_ctx ctx, const dg_moe_dims *m, int32_t C, const dg_bf16 *X,
                      const dg_bf16 *Wr, const dg_bf16 *W1, const dg_bf16 *W2, const dg_bf16 *W1s,
                      const dg_bf16 *W2s, void *ws, dg_bf16 *Y, int32_t *n_active) {
-  if (!ctx) return DG_ERR_NULL;
+  DG_ENTER();
   dg_status st = check_moe(ctx, m, C, __func__);
   if (st) return st;
   DG_REQUIRE_PTR(X);
@@ -448,7 +456,7 @@ dg_status dg_prefill_block(dg_ctx ctx, const dg_dims *dims, const int32_t *token
                            const dg_bf16 *E, const dg_bf16 *Wq, const dg_bf16 *Wk,
                            const dg_bf16 *Wv, const dg_bf16 *Wo, dg_bf16 *Kp, dg_bf16 *Vt,
                            int64_t P, int64_t Pcap, void *ws, dg_bf16 *A, int64_t *P_out) {
-  if (!ctx) return DG_ERR_NULL;
+  DG_ENTER();
   dg_status st = check_dims(ctx, dims, __func__);
   if (st) return st;
   if ((st = check_cache(ctx, P, Pcap, __func__))) return st;
@@ -537,7 +545,7 @@ dg_status dg_prefill_block(dg_ctx ctx, const dg_dims *dims, const int32_t *token
 dg_status dg_logits_entropy(dg_ctx ctx, const dg_dims *dims, const dg_bf16 *H,
                             const dg_bf16 *E, float tau, void *ws, float *entropy,
                             int32_t *argmax) {
-  if (!ctx) return DG_ERR_NULL;
+  DG_ENTER();
   dg_status st = check_dims(ctx, dims, __func__);
   if (st) return st;
   DG_REQUIRE_PTR(H);
@@ -580,7 +588,7 @@ dg_status dg_logits_entropy(dg_ctx ctx, const dg_dims *dims, const dg_bf16 *H,
 
 dg_status dg_entropy_accept(dg_ctx ctx, int32_t B, int32_t C, const float *entropy, float b,
                             uint8_t *accept, int32_t *n_accept) {
-  if (!ctx) return DG_ERR_NULL;
+  DG_ENTER();
   if (B < 1 || C < 1 || C > 1024) return fail(ctx, DG_ERR_SHAPE, "%s: need B >= 1, 1 <= C <= 1024", __func__);
   if (!entropy || !accept || !n_accept) return fail(ctx, DG_ERR_NULL, "%s: NULL buffer", __func__);
   if (!(b >= 0.f && b < 65536.f)) return fail(ctx, DG_ERR_RANGE, "%s: b=%g must be in [0, 65536)", __func__, b);
@@ -590,7 +598,7 @@ dg_status dg_entropy_accept(dg_ctx ctx, int32_t B, int32_t C, const float *entro
 }
 
 dg_status dg_confidence(dg_ctx ctx, const dg_dims *dims, const void *ws, float *confidence) {
-  if (!ctx) return DG_ERR_NULL;
+  DG_ENTER();
   dg_status st = check_dims(ctx, dims, __func__);
   if (st) return st;
   DG_REQUIRE_PTR(ws);
@@ -606,7 +614,7 @@ dg_status dg_confidence(dg_ctx ctx, const dg_dims *dims, const void *ws, float *
 
 dg_status dg_topk_accept(dg_ctx ctx, int32_t B, int32_t C, const float *score, int32_t k,
                          uint8_t *accept, int32_t *n_accept) {
-  if (!ctx) return DG_ERR_NULL;
+  DG_ENTER();
   if (B < 1 || C < 1 || C > 1024) return fail(ctx, DG_ERR_SHAPE, "%s: need B >= 1, 1 <= C <= 1024", __func__);
   if (!score || !accept || !n_accept) return fail(ctx, DG_ERR_NULL, "%s: NULL buffer", __func__);
   if (k < 0) return fail(ctx, DG_ERR_RANGE, "%s: k=%d must be >= 0", __func__, (int)k);
@@ -616,7 +624,7 @@ dg_status dg_topk_accept(dg_ctx ctx, int32_t B, int32_t C, const float *score, i
 
 dg_status dg_sample(dg_ctx ctx, const dg_dims *dims, const void *ws, int32_t B, uint64_t seed,
                     uint32_t canvas_base, uint32_t step, int32_t *tokens) {
-  if (!ctx) return DG_ERR_NULL;
+  DG_ENTER();
   dg_status st = check_dims(ctx, dims, __func__);
   if (st) return st;
   DG_REQUIRE_PTR(ws);
@@ -657,7 +665,7 @@ int32_t dg_reveal_count(int32_t C, int32_t N, int32_t step) {
 dg_status dg_renoise(dg_ctx ctx, int32_t B, int32_t C, int32_t V, const int32_t *argmax,
                      const uint8_t *accept, uint64_t seed, uint32_t canvas_base, uint32_t step,
                      int32_t *tokens) {
-  if (!ctx) return DG_ERR_NULL;
+  DG_ENTER();
   if (B < 1 || C < 1 || V < 1) return fail(ctx, DG_ERR_SHAPE, "%s: need B, C, V >= 1", __func__);
   if (!tokens) return fail(ctx, DG_ERR_NULL, "%s: tokens is NULL", __func__);
   if (accept && !argmax) return fail(ctx, DG_ERR_NULL, "%s: argmax is NULL", __func__);
@@ -667,7 +675,7 @@ dg_status dg_renoise(dg_ctx ctx, int32_t B, int32_t C, int32_t V, const int32_t 
 
 dg_status dg_selfcond(dg_ctx ctx, const dg_dims *dims, void *ws, const dg_bf16 *E,
                       const dg_bf16 *W1, const dg_bf16 *W2, dg_bf16 *z) {
-  if (!ctx) return DG_ERR_NULL;
+  DG_ENTER();
   dg_status st = check_dims(ctx, dims, __func__);
   if (st) return st;
   DG_REQUIRE_PTR(ws);
@@ -721,7 +729,7 @@ dg_status dg_selfcond(dg_ctx ctx, const dg_dims *dims, void *ws, const dg_bf16 *
 dg_status dg_stop_test(dg_ctx ctx, int32_t B, int32_t C, const float *entropy,
                        const int32_t *argmax, const int32_t *prev_argmax, float thr, int32_t step,
                        int32_t N, int32_t *flag) {
-  if (!ctx) return DG_ERR_NULL;
+  DG_ENTER();
   if (B < 1 || C < 1 || C > 1024) return fail(ctx, DG_ERR_SHAPE, "%s: need B >= 1, 1 <= C <= 1024", __func__);
   if (!entropy || !argmax || !flag) return fail(ctx, DG_ERR_NULL, "%s: NULL buffer", __func__);
   if (!(thr >= 0.f && thr < 65536.f)) return fail(ctx, DG_ERR_RANGE, "%s: thr=%g must be in [0, 65536)", __func__, thr);
@@ -734,7 +742,7 @@ dg_status dg_stop_test(dg_ctx ctx, int32_t B, int32_t C, const float *entropy,
 dg_status dg_commit_kv(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens, const dg_bf16 *E,
                        const dg_bf16 *Wk, const dg_bf16 *Wv, dg_bf16 *Kp, dg_bf16 *Vt, int64_t P,
                        int64_t Pcap, int64_t *P_out) {
-  if (!ctx) return DG_ERR_NULL;
+  DG_ENTER();
   dg_status st = check_dims(ctx, dims, __func__);
   if (st) return st;
   if ((st = check_cache(ctx, P, Pcap, __func__))) return st;
@@ -769,7 +777,7 @@ dg_status dg_commit_kv(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens, c
 }
 
 dg_status dg_peak_stream_read(dg_ctx ctx, const void *buf, size_t bytes, uint32_t *sink) {
-  if (!ctx) return DG_ERR_NULL;
+  DG_ENTER();
   DG_REQUIRE_PTR(buf);
   DG_REQUIRE_PTR(sink);
   if (bytes == 0 || bytes % 16 || ((uintptr_t)buf & 15))
@@ -779,7 +787,7 @@ dg_status dg_peak_stream_read(dg_ctx ctx, const void *buf, size_t bytes, uint32_
 }
 
 dg_status dg_peak_mfma_bf16(dg_ctx ctx, int32_t iters, float *sink) {
-  if (!ctx) return DG_ERR_NULL;
+  DG_ENTER();
   DG_REQUIRE_PTR(sink);
   if (iters < 1 || iters > 16384) return fail(ctx, DG_ERR_RANGE, "%s: iters=%d outside [1, 16384]", __func__, iters);
   const hipError_t e = dg_launch_mfma_peak(iters, sink, DG_PEAK_MFMA_BLOCKS, ctx->stream);

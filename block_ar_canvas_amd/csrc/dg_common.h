@@ -19,6 +19,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <initializer_list>
+
 typedef uint16_t u16;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -105,6 +108,41 @@ DG_DEV void set_status(int *status, int code) {
 
 static inline int64_t dg_round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 static inline int64_t dg_cdiv(int64_t x, int64_t m) { return (x + m - 1) / m; }
+
+// ------------------------------------------------------------------ host: per-device state
+// Launchers run with the calling context's device current (every API call that enqueues
+// work makes it current first). Launch attributes and the CU count are properties of a
+// device, so their caches are kept per device.
+#define DG_MAX_DEVICES 64
+static inline int dg_current_device() {
+  int d = 0;
+  return hipGetDevice(&d) == hipSuccess && d >= 0 && d < DG_MAX_DEVICES ? d : 0;
+}
+// Compute units of the current device (256 on an MI355X if the query fails).
+static inline int dg_device_cus() {
+  static std::atomic<int> cus[DG_MAX_DEVICES];
+  const int dev = dg_current_device();
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+// Raises the dynamic LDS limit of the given kernels to `bytes` on the current device, the
+// first time a launcher asks on that device (`done` is the launcher's own per-device flag
+// array). Setting it twice is harmless, so concurrent first calls need no lock.
+static inline hipError_t dg_smem_attr_once(std::atomic<bool> (&done)[DG_MAX_DEVICES], int bytes,
+                                           std::initializer_list<const void *> kernels) {
+  const int dev = dg_current_device();
+  if (done[dev].load(std::memory_order_acquire)) return hipSuccess;
+  for (const void *k : kernels) {
+    const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+  }
+  done[dev].store(true, std::memory_order_release);
+  return hipSuccess;
+}
 
 // ------------------------------------------------------------------ workspace layout
 // All regions are 256-byte aligned. Sizes depend on the dims and the cache capacity

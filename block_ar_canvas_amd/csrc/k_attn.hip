@@ -94,11 +94,10 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(AttnArgs a, int nq,
   const int t1 = (int)((int64_t)(split + 1) * ntiles / a.nsplit);
 
   // Padded V^T rows (head dims below one MFMA tile) are zero in every ring slot.
-  if (F::ER > HD) {
-    for (int i = tid; i < NS * (F::ER - HD) * 32; i += NW * 64) {
-      const int s = i / ((F::ER - HD) * 32), o = i % ((F::ER - HD) * 32);
-      *(uint32_t *)(smem + s * F::STAGE + F::KTILE + HD * 128 + 4 * o) = 0;
-    }
+  if constexpr (F::ER > HD) {
+    constexpr int PW = (F::ER - HD) * 32;            // 32-bit words of padding per slot
+    for (int i = tid; i < NS * PW; i += NW * 64)
+      *(uint32_t *)(smem + (i / PW) * F::STAGE + F::KTILE + HD * 128 + 4 * (i % PW)) = 0;
   }
 
   // Query rows of this wave: r = qb*256 + wave*32 + l32 -> (head, canvas position).
@@ -404,13 +403,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 
 template <int HD, bool CAUSAL>
 hipError_t launch(const AttnArgs &a, hipStream_t st) {
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void *)attn_split_kernel<HD, CAUSAL>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, Cfg<HD>::SMEM);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  static std::atomic<bool> attr[DG_MAX_DEVICES];
+  hipError_t e = dg_smem_attr_once(attr, Cfg<HD>::SMEM, {(const void *)attn_split_kernel<HD, CAUSAL>});
+  if (e != hipSuccess) return e;
   const int G = a.Hq / a.Hkv;
   const int nq = (G * a.C + QB - 1) / QB;
   const int ntc = (a.C + KT - 1) / KT;
@@ -418,7 +413,7 @@ hipError_t launch(const AttnArgs &a, hipStream_t st) {
   const int units = a.Hkv * a.nsplit;
   hipLaunchKernelGGL((attn_split_kernel<HD, CAUSAL>), dim3(units * nq), dim3(NW * 64), Cfg<HD>::SMEM,
                      st, a, nq, ntc, ntiles, units);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int RPB = 256 / (HD / 8);
   hipLaunchKernelGGL(attn_merge_kernel<HD>, dim3((a.Hq * a.C + RPB - 1) / RPB), dim3(256), 0, st, a);

@@ -282,16 +282,10 @@ namespace {
 template <int TN, int TM, int NS>
 hipError_t launch_tile(GemmArgs a, int S, hipStream_t st) {
   constexpr int smem = Tile<TN, TM, NS>::SMEM;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<TN, TM, NS, false>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void *)gemm_kernel<TN, TM, NS, true>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  static std::atomic<bool> attr[DG_MAX_DEVICES];
+  const hipError_t e = dg_smem_attr_once(attr, smem, {(const void *)gemm_kernel<TN, TM, NS, false>,
+                                                      (const void *)gemm_kernel<TN, TM, NS, true>});
+  if (e != hipSuccess) return e;
   int nblk = 0, mmax = a.M;
   for (int s = 0; s < a.nseg; ++s) {
     a.seg[s].nblk0 = nblk;
@@ -308,17 +302,6 @@ hipError_t launch_tile(GemmArgs a, int S, hipStream_t st) {
   return hipGetLastError();
 }
 
-int device_cus() {
-  static int n = 0;
-  if (n <= 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-  }
-  return n;
-}
-
 }  // namespace
 
 // Tile shape: every workgroup streams (TN + TM) rows of K through its CU, so the shape
@@ -330,7 +313,7 @@ hipError_t dg_launch_gemm(const GemmArgs &a, hipStream_t st) {
   int mmax = a.M;
   for (int s = 0; s < a.nseg; ++s)
     if (a.seg[s].m_store > mmax) mmax = a.seg[s].m_store;
-  const int ncu = device_cus();
+  const int ncu = dg_device_cus();
   static const int shapes[3][2] = {{64, 64}, {32, 64}, {32, 32}};
   int best = 0;
   int64_t best_cost = INT64_MAX, best_wg = INT64_MAX;

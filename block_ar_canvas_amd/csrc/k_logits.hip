@@ -432,33 +432,16 @@ namespace {
 template <int BCT>
 hipError_t launch_tiles(const LogitsArgs &a, hipStream_t st) {
   constexpr int smem = smem_bytes<BCT>();
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void *)logits_tile_kernel<false, BCT>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void *)logits_tile_kernel<true, BCT>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  static std::atomic<bool> attr[DG_MAX_DEVICES];
+  const hipError_t e = dg_smem_attr_once(attr, smem, {(const void *)logits_tile_kernel<false, BCT>,
+                                                      (const void *)logits_tile_kernel<true, BCT>});
+  if (e != hipSuccess) return e;
   const dim3 grid(a.T * ((a.Cpad + BCT - 1) / BCT));
   if (a.d % BK)
     hipLaunchKernelGGL((logits_tile_kernel<true, BCT>), grid, dim3(512), smem, st, a);
   else
     hipLaunchKernelGGL((logits_tile_kernel<false, BCT>), grid, dim3(512), smem, st, a);
   return hipGetLastError();
-}
-
-int device_cus() {
-  static int n = 0;
-  if (n <= 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-  }
-  return n;
 }
 
 }  // namespace
@@ -469,7 +452,7 @@ int device_cus() {
 // through L2, and twice as many CUs work. Otherwise blocks of 256 (more FLOP per copied
 // byte).
 hipError_t dg_launch_logits(const LogitsArgs &a, hipStream_t st) {
-  const bool narrow = a.Cpad <= 128 || (int64_t)a.T * ((a.Cpad + 255) / 256) < device_cus();
+  const bool narrow = a.Cpad <= 128 || (int64_t)a.T * ((a.Cpad + 255) / 256) < dg_device_cus();
   hipError_t e = narrow ? launch_tiles<128>(a, st) : launch_tiles<256>(a, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(row_finalize_kernel, dim3(a.C), dim3(256), 0, st, a);

@@ -311,13 +311,9 @@ hipError_t dg_launch_moe_group(const int *sel, int C, int K, int E, int *off, in
 
 hipError_t dg_launch_moe_expert(const MoeGemmArgs &a, hipStream_t st) {
   if (a.N < 32 || a.N % 32 || a.K < 32 || a.K % 32 || a.max_tiles < 1) return hipErrorInvalidValue;
-  static bool attr = false;
-  if (!attr) {
-    const hipError_t e = hipFuncSetAttribute((const void *)moe_expert_kernel,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, XSMEM);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  static std::atomic<bool> attr[DG_MAX_DEVICES];
+  const hipError_t e = dg_smem_attr_once(attr, XSMEM, {(const void *)moe_expert_kernel});
+  if (e != hipSuccess) return e;
   const int NB = (a.N + 127) / 128;
   hipLaunchKernelGGL(moe_expert_kernel, dim3(a.max_tiles * NB), dim3(256), XSMEM, st, a);
   return hipGetLastError();

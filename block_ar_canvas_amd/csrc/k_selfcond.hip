@@ -316,17 +316,13 @@ __global__ __launch_bounds__(256) void selfcond_reduce_kernel(SelfcondArgs a) {
 }  // namespace
 
 hipError_t dg_launch_selfcond(const SelfcondArgs &a, hipStream_t st) {
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void *)selfcond_split_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, SMEM);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  static std::atomic<bool> attr[DG_MAX_DEVICES];
+  hipError_t e = dg_smem_attr_once(attr, SMEM, {(const void *)selfcond_split_kernel});
+  if (e != hipSuccess) return e;
   const int nj = (a.d + BJ - 1) / BJ;
   hipLaunchKernelGGL(selfcond_split_kernel, dim3(nj * a.nsc * ((a.Cpad + BC - 1) / BC)), dim3(512),
                      SMEM, st, a, nj);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(selfcond_reduce_kernel, dim3((a.d + 15) / 16, (a.Cpad + 63) / 64), dim3(256), 0, st, a);
   return hipGetLastError();

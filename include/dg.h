@@ -35,7 +35,9 @@
  *  - On a non-OK return nothing was enqueued; dg_last_error() describes the problem.
  *  - Conditions only the device can see (a token id outside [0, V), non-finite
  *    logits) set a sticky status word in the context, reported by dg_sync().
- *  - A context is used by one host thread at a time. No C++ exception crosses the ABI.
+ *  - A context is used by one host thread at a time. Every call that enqueues work or
+ *    waits on the device first makes the context's device current on the calling thread.
+ *    No C++ exception crosses the ABI.
  */
 #ifndef DG_H
 #define DG_H
