@@ -34,6 +34,26 @@ def build(verbose: bool = False) -> str:
     if verbose and msg.strip():
         print(msg, file=sys.stderr)
     os.replace(tmp, out)
+    build_c_check(verbose)
+    return out
+
+
+def build_c_check(verbose: bool = False) -> str:
+    """Compile tests/c_abi_check.c, a plain-C user of libdg.so, with gcc into
+    c_abi_check next to the library (found there through its rpath)."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    out = os.path.join(HERE, "c_abi_check")
+    src = os.path.join(os.path.dirname(HERE), "tests", "c_abi_check.c")
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(os.path.dirname(HERE), "include"), "-I", os.path.join(rocm, "include"),
+           src, "-o", out + ".tmp", "-L", HERE, "-ldg", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-lm", "-Wl,-rpath,$ORIGIN", "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"gcc failed on {src} ({res.returncode}):\n{res.stdout}{res.stderr}")
+    if verbose and (res.stdout + res.stderr).strip():
+        print(res.stdout + res.stderr, file=sys.stderr)
+    os.replace(out + ".tmp", out)
     return out
 
 
