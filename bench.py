@@ -174,6 +174,33 @@ def graph_canvas_rate(ctx, loop, hidden, reps):
             "graph_canvas_tokens_per_s": round(reps * loop.dims.C / graph, 1)}
 
 
+def native_protocol(ctx, cfg, Wd, Kd, Vtd, hidden_of, canvases):
+    """The protocol with each canvas run by dg_run_canvas (the loop sequenced inside the
+    library: one host call per canvas instead of one per kernel call): one discarded
+    warm-up canvas, then `canvases` whole canvases from the same prefix, as in
+    run_protocol."""
+    import torch
+
+    import block_ar_canvas_amd as dg
+
+    dev = Kd.device
+    ws = torch.empty(dg.workspace_bytes(cfg, Kd.shape[1]), dtype=torch.uint8, device=dev)
+    lws = torch.empty(dg.loop_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+    x0 = torch.empty(cfg.C, dtype=torch.int32, device=dev)
+    secs, steps = [], []
+    for c in range(canvases + 1):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        n, _ = ctx.run_canvas(cfg, Wd, Kd, Vtd, cfg.P0, hidden_of(c), ws, lws, x0, N=cfg.N,
+                              seed=cfg.seed, canvas=c)
+        torch.cuda.synchronize()
+        if c > 0:
+            secs.append(time.perf_counter() - t0)
+            steps.append(n)
+    ctx.sync()
+    return protocol_summary(secs, steps, cfg.C)
+
+
 def small_workload(ctx, name, canvases):
     """The protocol at a smaller workload (tiny or small): steps/s and canvas tokens/s."""
     import torch
@@ -193,6 +220,7 @@ def small_workload(ctx, name, canvases):
     ctx.sync()
     out = protocol_summary(secs, steps, cfg.C)
     out["fixed_step_canvases"] = graph_canvas_rate(ctx, loop, lambda k: Hd[0][k], 100 if cfg.V < 4096 else 20)
+    out["native_loop"] = native_protocol(ctx, cfg, Wd, Kd, Vtd, lambda c: (lambda k: Hd[c % 2][k]), canvases)
     out["workload"] = (f"{cfg.name}: V={cfg.V} d={cfg.d} C={cfg.C} Hq={cfg.Hq} Hkv={cfg.Hkv} "
                        f"hd={cfg.hd} F={cfg.F} prefix={cfg.P0} N={cfg.N}")
     return out

@@ -13,7 +13,8 @@ import os
 
 import torch
 
-__all__ = ["DGError", "Dims", "MoeDims", "Context", "moe_workspace_bytes", "workspace_bytes", "temperature", "reveal_count", "lib_path",
+__all__ = ["DGError", "Dims", "MoeDims", "Context", "moe_workspace_bytes", "workspace_bytes", "loop_workspace_bytes",
+           "temperature", "reveal_count", "lib_path",
            "STOP_GO", "STOP_STOP", "STOP_CAP", "PEAK_STREAM_BLOCKS", "PEAK_MFMA_BLOCKS", "STATIC_SCRATCH_BYTES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -51,6 +52,21 @@ class Dims(ctypes.Structure):
         g = (lambda k: obj[k]) if isinstance(obj, dict) else (lambda k: getattr(obj, k))
         return cls(*(int(g(k)) for k in ("V", "d", "C", "Hq", "Hkv", "hd", "F")))
 
+
+class Weights(ctypes.Structure):
+    """dg_weights: device pointers of the step's weights."""
+    _fields_ = [(n, ctypes.c_void_p) for n in ("E", "Wq", "Wk", "Wv", "Wo", "W1", "W2")]
+
+
+class LoopParams(ctypes.Structure):
+    """dg_loop_params of dg_run_canvas."""
+    _fields_ = [("N", ctypes.c_int32), ("b", ctypes.c_float), ("thr", ctypes.c_float),
+                ("tau0", ctypes.c_float), ("tau1", ctypes.c_float), ("seed", ctypes.c_uint64),
+                ("canvas", ctypes.c_uint32)]
+
+
+# dg_hidden_fn: (user, step) -> device pointer of H_step
+HIDDEN_FN = ctypes.CFUNCTYPE(ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32)
 
 _P = ctypes.c_void_p
 _lib = None
@@ -94,6 +110,9 @@ def _load():
         "dg_commit_kv": (i32, [_P, D, _P, _P, _P, _P, _P, _P, i64, i64, ctypes.POINTER(i64)]),
         "dg_peak_stream_read": (i32, [_P, _P, ctypes.c_size_t, _P]),
         "dg_peak_mfma_bf16": (i32, [_P, i32, _P]),
+        "dg_loop_workspace_bytes": (ctypes.c_size_t, [D]),
+        "dg_run_canvas": (i32, [_P, D, ctypes.POINTER(Weights), _P, _P, i64, i64, ctypes.POINTER(LoopParams),
+                                HIDDEN_FN, _P, _P, _P, _P, ctypes.POINTER(i32), ctypes.POINTER(i64)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -108,6 +127,15 @@ def workspace_bytes(dims, Pcap: int) -> int:
     n = _load().dg_workspace_bytes(ctypes.byref(d), int(Pcap))
     if n == 0:
         raise DGError(2, "dg_workspace_bytes: unsupported dims")
+    return int(n)
+
+
+def loop_workspace_bytes(dims) -> int:
+    """Bytes of the device state dg_run_canvas keeps for one canvas."""
+    d = Dims.of(dims)
+    n = _load().dg_loop_workspace_bytes(ctypes.byref(d))
+    if n == 0:
+        raise DGError(2, "dg_loop_workspace_bytes: unsupported dims")
     return int(n)
 
 
@@ -319,3 +347,35 @@ class Context:
             _ptr(Wk, _BF16, "Wk"), _ptr(Wv, _BF16, "Wv"), _ptr(Kp, _BF16, "Kp"), _ptr(Vt, _BF16, "Vt"),
             int(P), int(Kp.shape[1]), ctypes.byref(out)))
         return int(out.value)
+
+    def run_canvas(self, dims, weights, Kp, Vt, P, hidden, ws, loop_ws, x0, *, N, seed, canvas,
+                   b=0.1, thr=0.005, tau0=0.8, tau1=0.4):
+        """dg_run_canvas: one whole canvas (init, steps until the stop test or the cap N,
+        the commit) sequenced in the library. hidden(k) -> H_k bf16 device tensor [C, d].
+        Returns (steps run, new cache length P); x0 [C] int32 receives the committed block."""
+        d = Dims.of(dims)
+        w = Weights(*(_ptr(weights[k], _BF16, k) for k in ("E", "Wq", "Wk", "Wv", "Wo", "W1", "W2")))
+        prm = LoopParams(int(N), float(b), float(thr), float(tau0), float(tau1), int(seed), int(canvas))
+        held, err = [], []
+
+        def cb(_user, k):
+            try:
+                t = hidden(int(k))
+                held.append(t)                  # alive until the kernels reading it have run
+                return _ptr(t, _BF16, "H")
+            except Exception as e:              # reported after the call; NULL ends the loop
+                err.append(e)
+                return None
+
+        fn = HIDDEN_FN(cb)
+        steps, p_out = ctypes.c_int32(0), ctypes.c_int64(0)
+        st = self._lib.dg_run_canvas(
+            self._h, ctypes.byref(d), ctypes.byref(w), _ptr(Kp, _BF16, "Kp"), _ptr(Vt, _BF16, "Vt"),
+            int(P), int(Kp.shape[1]), ctypes.byref(prm), fn, None, _ptr(ws, _U8, "ws"),
+            _ptr(loop_ws, _U8, "loop_ws"), _ptr(x0, _I32, "x0"), ctypes.byref(steps), ctypes.byref(p_out))
+        # the last steps may still run on the device: keep their inputs until the next call
+        self._held = held
+        if err:
+            raise err[0]
+        self._check(st)
+        return int(steps.value), int(p_out.value)

@@ -3,15 +3,18 @@
 // Host-side responsibilities: validate every argument before anything is enqueued,
 // carve the caller's workspace, and launch the kernels of each call in order on the
 // context's stream. No call allocates device memory (the context's 4-byte status word
-// is allocated once in dg_create) and no call waits for the device except dg_sync.
+// and its pinned stop flags are allocated once in dg_create) and no call waits for the
+// device except dg_sync and dg_run_canvas (which polls its steps' stop flags).
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
 
+#include <chrono>
 #include <climits>
 #include <mutex>
 #include <new>
+#include <thread>
 
 #include "../../include/dg.h"
 #include "dg_common.h"
@@ -37,6 +40,12 @@ struct dg_ctx_s {
   // dg_create: the shared expert runs beside the routed experts.
   hipStream_t side = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  // Stop flags of dg_run_canvas's steps, pinned host memory, four taken in enqueue order
+  // across calls: when a step is enqueued at most two older ones are pending (including
+  // the discarded step a stopped canvas leaves behind), so no slot is refilled while an
+  // older stop kernel may still write it.
+  int32_t *host_flags = nullptr;
+  unsigned flag_seq = 0;
   // Device address of this device's static scratch (NULL if the lookup failed).
   void *scratch = nullptr;
   hipError_t scratch_err = hipSuccess;
@@ -246,10 +255,12 @@ dg_status dg_create(dg_ctx *out, int device, void *hip_stream) {
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&ctx->side, hipStreamNonBlocking);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->ev_fork, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->ev_join, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipHostMalloc((void **)&ctx->host_flags, 4 * sizeof(int32_t), hipHostMallocDefault);
   if (e != hipSuccess) {
     if (ctx->d_status) (void)hipFree(ctx->d_status);
     if (ctx->side) (void)hipStreamDestroy(ctx->side);
     if (ctx->ev_fork) (void)hipEventDestroy(ctx->ev_fork);
+    if (ctx->ev_join) (void)hipEventDestroy(ctx->ev_join);
     delete ctx;
     return DG_ERR_HIP;
   }
@@ -273,6 +284,7 @@ void dg_destroy(dg_ctx ctx) {
   }
   if (ctx->ev_fork) (void)hipEventDestroy(ctx->ev_fork);
   if (ctx->ev_join) (void)hipEventDestroy(ctx->ev_join);
+  if (ctx->host_flags) (void)hipHostFree(ctx->host_flags);
   delete ctx;
 }
 
@@ -773,6 +785,144 @@ dg_status dg_commit_kv(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens, c
   hipError_t e = dg_launch_gemm(g, ctx->stream);
   if (e != hipSuccess) return hip_fail(ctx, e, "dg_commit_kv");
   *P_out = P + m.C;
+  return DG_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Device state of one canvas in dg_run_canvas's loop workspace, 256-byte aligned regions.
+struct LoopWs {
+  size_t tokens, z, A, entropy, am0, am1, accept, n_accept, total;
+};
+LoopWs loop_ws_layout(const dg_dims &m) {
+  LoopWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (size_t)dg_round_up((int64_t)bytes, 256);
+    return o;
+  };
+  const size_t C = (size_t)m.C, cd = C * (size_t)m.d;
+  w.tokens = take(4 * C);
+  w.z = take(2 * cd);
+  w.A = take(2 * cd);
+  w.entropy = take(4 * C);
+  w.am0 = take(4 * C);
+  w.am1 = take(4 * C);
+  w.accept = take(C);
+  w.n_accept = take(4);
+  w.total = off;
+  return w;
+}
+
+// Polls a pinned stop flag until the stop kernel's system-scope store lands (a value in
+// {0, 1, 2}); after 60 s a stream synchronization settles it or the step is reported lost.
+dg_status wait_flag(dg_ctx ctx, int slot, int k, int32_t *value) {
+  volatile int32_t *f = ctx->host_flags + slot;
+  const auto t0 = std::chrono::steady_clock::now();
+  for (int spins = 0; *f < 0; ++spins) {
+    if ((spins & 1023) == 1023) {
+      if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(60)) {
+        const hipError_t e = hipStreamSynchronize(ctx->stream);
+        if (e != hipSuccess) return hip_fail(ctx, e, "dg_run_canvas");
+        if (*f < 0) return fail(ctx, DG_ERR_HIP, "dg_run_canvas: the stop flag of step %d was never written", k);
+        break;
+      }
+      std::this_thread::yield();
+    }
+  }
+  *value = *f;
+  return DG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dg_loop_workspace_bytes(const dg_dims *m) {
+  if (!m || check_dims(nullptr, m, "dg_loop_workspace_bytes") != DG_OK) return 0;
+  return loop_ws_layout(*m).total;
+}
+
+dg_status dg_run_canvas(dg_ctx ctx, const dg_dims *dims, const dg_weights *w, dg_bf16 *Kp,
+                        dg_bf16 *Vt, int64_t P, int64_t Pcap, const dg_loop_params *prm,
+                        dg_hidden_fn hidden, void *user, void *ws, void *loop_ws, int32_t *x0,
+                        int32_t *steps, int64_t *P_out) {
+  DG_ENTER();
+  // Everything a later call of the loop could refuse is checked here, so a refused call
+  // enqueues nothing; only a NULL or misaligned H_k from the callback is found mid-loop.
+  dg_status st = check_dims(ctx, dims, __func__);
+  if (st) return st;
+  if ((st = check_cache(ctx, P, Pcap, __func__))) return st;
+  if (!w || !prm || !hidden || !steps || !P_out)
+    return fail(ctx, DG_ERR_NULL, "%s: weights, params, hidden, steps and P_out must not be NULL", __func__);
+  DG_REQUIRE_PTR(Kp);
+  DG_REQUIRE_PTR(Vt);
+  DG_REQUIRE_PTR(ws);
+  DG_REQUIRE_PTR(loop_ws);
+  DG_REQUIRE_PTR(x0);
+  const dg_bf16 *E = w->E, *Wq = w->Wq, *Wk = w->Wk, *Wv = w->Wv, *Wo = w->Wo, *W1 = w->W1, *W2 = w->W2;
+  DG_REQUIRE_PTR(E);
+  DG_REQUIRE_PTR(Wq);
+  DG_REQUIRE_PTR(Wk);
+  DG_REQUIRE_PTR(Wv);
+  DG_REQUIRE_PTR(Wo);
+  DG_REQUIRE_PTR(W1);
+  DG_REQUIRE_PTR(W2);
+  const dg_dims &m = *dims;
+  const int N = prm->N;
+  if (N < 1) return fail(ctx, DG_ERR_RANGE, "%s: N=%d must be >= 1", __func__, N);
+  if (!(prm->b >= 0.f && prm->b < 65536.f) || !(prm->thr >= 0.f && prm->thr < 65536.f))
+    return fail(ctx, DG_ERR_RANGE, "%s: b=%g and thr=%g must be in [0, 65536)", __func__, prm->b, prm->thr);
+  if (!(prm->tau0 > 0.f) || !(prm->tau1 > 0.f) || !isfinite(prm->tau0) || !isfinite(prm->tau1))
+    return fail(ctx, DG_ERR_RANGE, "%s: tau0=%g and tau1=%g must be finite and > 0", __func__, prm->tau0, prm->tau1);
+  if (P + m.C > Pcap)
+    return fail(ctx, DG_ERR_CAPACITY, "%s: P=%lld + C=%d exceeds Pcap=%lld", __func__, (long long)P, m.C,
+                (long long)Pcap);
+
+  const LoopWs L = loop_ws_layout(m);
+  int32_t *tok = ws_at<int32_t>(loop_ws, L.tokens);
+  dg_bf16 *z = ws_at<dg_bf16>(loop_ws, L.z), *A = ws_at<dg_bf16>(loop_ws, L.A);
+  float *ent = ws_at<float>(loop_ws, L.entropy);
+  int32_t *am[2] = {ws_at<int32_t>(loop_ws, L.am0), ws_at<int32_t>(loop_ws, L.am1)};
+  uint8_t *acc = ws_at<uint8_t>(loop_ws, L.accept);
+  int32_t *nacc = ws_at<int32_t>(loop_ws, L.n_accept);
+
+  // a uniform random canvas (stream 1 of the canvas's draws)
+  if ((st = dg_renoise(ctx, 1, m.C, m.V, nullptr, nullptr, prm->seed, prm->canvas, 0, tok))) return st;
+  int slot[2] = {0, 0};
+  auto step = [&](int k) -> dg_status {
+    const dg_bf16 *H = hidden(user, k);
+    if (!H) return fail(ctx, DG_ERR_NULL, "dg_run_canvas: hidden state of step %d is NULL", k);
+    if (!aligned16(H)) return fail(ctx, DG_ERR_ALIGN, "dg_run_canvas: hidden state of step %d is not 16-byte aligned", k);
+    int32_t *a = am[k & 1], *prev = k > 0 ? am[(k - 1) & 1] : nullptr;
+    dg_status r = dg_canvas_attn(ctx, dims, tok, k > 0 ? z : nullptr, E, Wq, Wk, Wv, Wo, Kp, Vt, P, Pcap, ws, A);
+    if (!r) r = dg_logits_entropy(ctx, dims, H, E, dg_temperature(k, N, prm->tau0, prm->tau1), ws, ent, a);
+    if (!r) r = dg_entropy_accept(ctx, 1, m.C, ent, prm->b, acc, nacc);
+    if (!r) r = dg_renoise(ctx, 1, m.C, m.V, a, acc, prm->seed, prm->canvas, (uint32_t)k, tok);
+    if (!r) r = dg_selfcond(ctx, dims, ws, E, W1, W2, z);
+    if (r) return r;
+    const int sl = (int)(ctx->flag_seq++ % 4);
+    slot[k & 1] = sl;
+    ctx->host_flags[sl] = -1;
+    return dg_stop_test(ctx, 1, m.C, ent, a, prev, prm->thr, k, N, ctx->host_flags + sl);
+  };
+
+  if ((st = step(0))) return st;
+  int k = 0;
+  for (;;) {
+    if (k + 1 < N && (st = step(k + 1))) return st;
+    int32_t flag = 0;
+    if ((st = wait_flag(ctx, slot[k & 1], k, &flag))) return st;
+    if (flag != 0) break;                            // stop (1) or the cap (2): commit step k
+    ++k;
+  }
+  if ((st = dg_commit_kv(ctx, dims, am[k & 1], E, Wk, Wv, Kp, Vt, P, Pcap, P_out))) return st;
+  const hipError_t e = hipMemcpyAsync(x0, am[k & 1], (size_t)m.C * 4, hipMemcpyDeviceToDevice, ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, __func__);
+  *steps = k + 1;
   return DG_OK;
 }
 

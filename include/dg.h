@@ -12,7 +12,8 @@
  * and, once per canvas, dg_commit_kv appends the finalized block to the KV cache.
  * Beyond that step: dg_prefill_block (the causal re-encode commit) with dg_set_rope,
  * dg_confidence / dg_topk_accept / dg_reveal_count (confidence-ranked acceptance),
- * dg_sample (sampled tokens), dg_moe_ffn (the canvas mixture-of-experts FFN), and the
+ * dg_sample (sampled tokens), dg_moe_ffn (the canvas mixture-of-experts FFN),
+ * dg_run_canvas (a whole canvas of the loop, sequenced in the library), and the
  * measured ceilings dg_peak_stream_read / dg_peak_mfma_bf16.
  * The method is the DiffusionGemma inference loop as summarized by the
  * "DiffusionGemma Technical Report" page (paper.rainbus.top/paper/2608.00146),
@@ -291,6 +292,43 @@ dg_status dg_moe_ffn(dg_ctx ctx, const dg_moe_dims *m, int32_t C, const dg_bf16 
 dg_status dg_commit_kv(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens,
                        const dg_bf16 *E, const dg_bf16 *Wk, const dg_bf16 *Wv,
                        dg_bf16 *Kp, dg_bf16 *Vt, int64_t P, int64_t Pcap, int64_t *P_out);
+
+/* ---------------------------------------------------------------- the canvas loop */
+/* One whole canvas of the block-autoregressive loop (Technical Report page, "Method
+ * steps" (2)-(5); tutorial chapter "DiffusionGemma", data-flow pseudocode), sequenced in
+ * the library: a uniform random canvas (dg_renoise with accept = NULL), then denoise
+ * steps k = 0, 1, ... of
+ *   dg_canvas_attn (z = 0 at k = 0), dg_logits_entropy on H_k at dg_temperature(k, N,
+ *   tau0, tau1), dg_entropy_accept with budget b, dg_renoise of the rejected positions,
+ *   dg_selfcond, dg_stop_test against the previous step's argmax,
+ * until the stop test fires or the cap N is reached, then dg_commit_kv of that step's
+ * argmax. Step k + 1 is enqueued before the host waits for step k's flag (pinned host
+ * memory of the context, polled: no stream synchronization between steps); when step k
+ * stops the canvas, step k + 1's results are discarded (it writes the other argmax
+ * buffer, and the commit reads step k's).
+ * hidden(user, k) is called on the host before step k is enqueued and returns the device
+ * pointer of H_k [C, d] bf16; it may enqueue work producing H_k on the context's stream.
+ * loop_ws holds dg_loop_workspace_bytes(dims) bytes (the canvas tokens, z, the attention
+ * output, entropies, both argmax buffers, acceptance). Outputs: x0 [C] device int32, the
+ * committed block; *steps (host) the steps run; *P_out (host) = P + C. Returns after the
+ * commit is enqueued (dg_sync waits for it). A flag not written within 60 s of waiting
+ * ends the call with DG_ERR_HIP after a stream synchronization. */
+typedef struct {
+  const dg_bf16 *E, *Wq, *Wk, *Wv, *Wo, *W1, *W2;
+} dg_weights;
+typedef struct {
+  int32_t N;                 /* step cap, >= 1 */
+  float b, thr;              /* acceptance budget and stop threshold (nats) */
+  float tau0, tau1;          /* temperature schedule endpoints */
+  uint64_t seed;             /* Philox key of the canvas draws */
+  uint32_t canvas;           /* canvas index (the Philox key's second word) */
+} dg_loop_params;
+typedef const dg_bf16 *(*dg_hidden_fn)(void *user, int32_t step);
+size_t dg_loop_workspace_bytes(const dg_dims *dims);
+dg_status dg_run_canvas(dg_ctx ctx, const dg_dims *dims, const dg_weights *w, dg_bf16 *Kp,
+                        dg_bf16 *Vt, int64_t P, int64_t Pcap, const dg_loop_params *prm,
+                        dg_hidden_fn hidden, void *user, void *ws, void *loop_ws, int32_t *x0,
+                        int32_t *steps, int64_t *P_out);
 
 /* Measured ceilings for the rooflines (measurement utilities, not steps of the method).
  * dg_peak_stream_read reads bytes (a positive multiple of 16) of the device buffer buf

@@ -120,3 +120,25 @@ def test_binding_flag_may_be_pinned_host_only(lib):
         dg._ptr(torch.zeros(1, dtype=torch.int32), torch.int32, "flag", pinned_ok=True)
     with pytest.raises(ValueError):
         dg._ptr(torch.zeros(4), torch.float32, "x", pinned_ok=False)
+
+
+def test_loop_workspace_bytes(lib):
+    import block_ar_canvas_amd as dg
+
+    for i in range(5):
+        cfg = di.config(i)
+        n = dg.loop_workspace_bytes(cfg)
+        # tokens, entropy, two argmax buffers (4 B each), acceptance, z and A (bf16 rows)
+        assert n >= cfg.C * (4 * 4 + 1) + 2 * 2 * cfg.C * cfg.d
+        assert n % 256 == 0
+    with pytest.raises(dg.DGError):
+        dg.loop_workspace_bytes(di.config(2).with_(hd=48))
+
+
+def test_run_canvas_refuses_a_null_context(lib):
+    # a NULL context is refused before anything touches a device
+    steps, P = ctypes.c_int32(0), ctypes.c_int64(0)
+    d = lib.dg_run_canvas.argtypes[1]._type_()
+    st = lib.dg_run_canvas(None, ctypes.byref(d), None, None, None, 0, 0, None, lib.dg_run_canvas.argtypes[8](), None,
+                           None, None, None, ctypes.byref(steps), ctypes.byref(P))
+    assert st == 1                                      # DG_ERR_NULL
