@@ -226,6 +226,15 @@ def small_workload(ctx, name, canvases):
     return out
 
 
+_T0 = time.time()
+
+
+def note(what: str):
+    """One progress line on stderr as a section of the run finishes (stdout carries only
+    the result line)."""
+    print(f"bench.py: {what} ({time.time() - _T0:.1f} s)", file=sys.stderr, flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -259,6 +268,7 @@ def main():
     Hd = [bf(di.hidden_all(cfg, W["E"], c)) for c in range(n_hidden)]
     torch.cuda.synchronize()
     t_gen = time.time() - t_gen
+    note("inputs on the device")
 
     ctx = dg.Context(0)
     loop = CanvasLoop(ctx, cfg, Wd, Kd, Vtd, cfg.P0, N=cfg.N, seed=cfg.seed)
@@ -304,6 +314,7 @@ def main():
 
     run(args.warmup)
     torch.cuda.synchronize()
+    note("warm-up canvas and steps")
     c0 = state["commits"]
     t0 = time.perf_counter()
     run(args.steps)
@@ -313,6 +324,7 @@ def main():
     sec = t1 - t0
     steps_per_s = args.steps / sec
     ctx.sync()
+    note(f"{args.steps} timed steps")
 
     # Roofline of the dominant pair: the sampler head (dg_logits_entropy: logits tile
     # kernel and row finalize) and self-conditioning (dg_selfcond: p0 E split kernel,
@@ -342,8 +354,10 @@ def main():
     secs, csteps = run_protocol(loop, lambda c: (lambda k: Hd[c % n_hidden][k]), args.canvases, cfg.P0)
     ctx.sync()
     proto = protocol_summary(secs, csteps, cfg.C)
+    note("whole-canvas protocol")
     if not args.no_graph:
         proto["fixed_step_canvases"] = graph_canvas_rate(ctx, loop, lambda k: Hd[0][k], 5)
+        note("fixed-step and graph canvases")
 
     if args.calibrate_copy:
         src_t = torch.empty(1 << 29, dtype=torch.int16, device=dev)
@@ -393,24 +407,32 @@ def main():
         # the in-step call: 1024 tiles over 256 CUs, four tiles per CU
         cr["in_step_us_per_tile_per_cu"] = round(1e3 * logits_ms / (cfg.V / 256 / 256), 2)
         result["cache_resident_logits"] = cr
+        note("cache-resident sampler head")
     if not args.no_long_prefix:
         result["long_prefix_attention"] = long_prefix_attention(ctx, cfg, Wd, Hd[0], args.roofline_reps)
+        note("long-prefix attention")
     del Kd, Vtd, loop
     if not args.no_batched:
         result["batched"] = [batched_canvases(ctx, cfg, Wd, Hd, B) for B in (2, 4)]
         result["confidence_rule"] = variant_canvas(ctx, cfg, Wd, Hd, rule="confidence")
         result["sampled_tokens"] = variant_canvas(ctx, cfg, Wd, Hd, draw="sample")
+        note("batched canvases and the acceptance variants")
     del Hd
     if not args.no_small:
         result["small"] = small_workload(ctx, "small", args.canvases)
+        note("small workload")
         result["tiny"] = small_workload(ctx, "tiny", args.canvases)
+        note("tiny workload")
     if not args.no_chain:
         result["chain8"] = chain(ctx)
         result["chain8_prefill"] = chain(ctx, commit="prefill", rope_base=10000.0)
+        note("chains of 8 canvases")
     if not args.no_moe:
         result["moe_ffn"] = moe_ffn(ctx, cfg, args.roofline_reps)
+        note("MoE FFN")
     if not args.no_peaks:
         pk = measured_peaks(ctx)
+        note("measured ceilings")
         result["measured_peaks"] = pk
         rf = result["roofline"]
         rf["frac_of_measured"] = round(rf["achieved"] / pk["hbm_read_GBs"], 4)
@@ -424,6 +446,7 @@ def main():
             mo["hbm_frac_of_measured"] = round(mo["achieved_GBs"] / pk["hbm_read_GBs"], 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, W, Kp, args.cpu_steps)
+        note("CPU oracle baseline")
     print(json.dumps(result))
 
 
