@@ -347,3 +347,29 @@ def test_determinism(dg_ctx):
         dg_ctx.sync()
         outs.append([x.cpu().numpy().tobytes() for x in (ent, am, z.view(torch.int16), A.view(torch.int16))])
     assert outs[0] == outs[1]
+
+
+@pytest.mark.parametrize("C", [256, 200])
+def test_sampler_head_does_not_depend_on_the_canvas_block_width(dg_ctx, C):
+    """At a 32768-token vocabulary one canvas runs the sampler head in 128-column blocks
+    (256-column blocks would leave CUs idle), and the same canvas stacked with a second
+    one runs it in 256-column blocks. Tile statistics are per (tile, column), so the
+    entropy, argmax and confidence of the shared columns must agree bit for bit."""
+    cfg = di.Config("blocks", V=32768, d=256, C=C, Hq=2, Hkv=1, hd=64, F=64, P0=0, N=4,
+                    alpha_max=8.0, seed=27)
+    W = di.weights(cfg)
+    Wd = upload_weights(W)
+    tgt = di.targets(cfg, 0)
+    H1 = di.hidden(cfg, W["E"], 0, 1, tgt)
+    H2 = di.hidden(cfg, W["E"], 1, 2, di.targets(cfg, 1))
+    tau = O.temperature(1, cfg.N)
+    outs = []
+    for cf, H in ((cfg, H1), (cfg.with_(C=2 * C), np.concatenate([H1, H2], axis=0))):
+        ws = torch.empty(dg.workspace_bytes(cf, 0), dtype=torch.uint8, device=DEV)
+        ent, am = run_head(dg_ctx, cf, Wd, H, tau, ws)
+        conf = torch.empty(cf.C, dtype=torch.float32, device=DEV)
+        dg_ctx.confidence(cf, ws, conf)
+        dg_ctx.sync()
+        outs.append((ent.cpu().numpy()[:C], am.cpu().numpy()[:C], conf.cpu().numpy()[:C]))
+    for a, b in zip(outs[0], outs[1]):
+        np.testing.assert_array_equal(a, b)
