@@ -17,7 +17,7 @@ import torch
 import block_ar_canvas_amd as dg
 import dg_inputs as di
 import oracle as O
-from gpu_util import (DEV, argmax_mismatch_unexcused, bf16_dev, bits_np, f32_dev, i32_dev,
+from gpu_util import (DEV, argmax_mismatch_unexcused, bf16_dev, bits_np, cache_logical, f32_dev, i32_dev,
                       maxrel, maxrel_rows, sample_excused, u8_dev, upload_cache, upload_weights)
 
 pytestmark = pytest.mark.gpu
@@ -373,3 +373,26 @@ def test_sampler_head_does_not_depend_on_the_canvas_block_width(dg_ctx, C):
         outs.append((ent.cpu().numpy()[:C], am.cpu().numpy()[:C], conf.cpu().numpy()[:C]))
     for a, b in zip(outs[0], outs[1]):
         np.testing.assert_array_equal(a, b)
+
+
+def test_gemm_results_do_not_depend_on_the_tile_shape(dg_ctx):
+    """The projection GEMM picks its tile shape from the output size: committing 256
+    tokens (1024 key and 1024 value features) runs 32 x 64 tiles, committing 512 runs
+    64 x 64. Each output element takes the same k order and the same fixed sum over the
+    workgroup's waves in both, so the first 256 rows must be bit-identical."""
+    cfg = di.Config("shapes", V=4000, d=256, C=256, Hq=16, Hkv=8, hd=128, F=64, P0=8, N=4,
+                    alpha_max=8.0, seed=28)
+    W = di.weights(cfg)
+    Wd = upload_weights(W)
+    Pcap = cfg.P0 + 512
+    Kp, Vp = di.prefix_kv(cfg, Pcap)
+    tok = np.random.default_rng(5).integers(0, cfg.V, 512).astype(np.int32)
+    rows = []
+    for C in (256, 512):
+        Kd, Vtd = upload_cache(Kp, Vp, Pcap)
+        dg_ctx.commit_kv(cfg.with_(C=C), i32_dev(tok[:C]), Wd["E"], Wd["Wk"], Wd["Wv"], Kd, Vtd, cfg.P0)
+        dg_ctx.sync()
+        Kg, Vg = cache_logical(Kd, Vtd)
+        rows.append((Kg[:, cfg.P0:cfg.P0 + 256].copy(), Vg[:, cfg.P0:cfg.P0 + 256].copy()))
+    np.testing.assert_array_equal(rows[0][0], rows[1][0])
+    np.testing.assert_array_equal(rows[0][1], rows[1][1])
