@@ -201,8 +201,8 @@ dg_status enqueue_canvas_attn(dg_ctx ctx, const char *fn, const dg_dims &m, cons
   hipError_t e = dg_launch_gemm(g, ctx->stream);
   if (e != hipSuccess) return hip_fail(ctx, e, fn);
   if (ctx->rope_base > 0.0) {                        // canvas token i sits at position P + i
-    e = dg_launch_rope(r.q, m.C, m.Hq, m.hd, qd, P, ctx->rope_base, ctx->stream);
-    if (e == hipSuccess) e = dg_launch_rope(r.kc, m.C, m.Hkv, m.hd, kd, P, ctx->rope_base, ctx->stream);
+    e = dg_launch_rope_store(r.q, r.kc, nullptr, m.C, r.Cpad, m.Hq, m.Hkv, m.hd, P, ctx->rope_base, nullptr,
+                             nullptr, 0, 0, ctx->stream);
     if (e != hipSuccess) return hip_fail(ctx, e, fn);
   }
 
@@ -509,11 +509,11 @@ dg_status dg_prefill_block(dg_ctx ctx, const dg_dims *dims, const int32_t *token
   g.seg[2] = GemmSeg{Wv, kd, vct, 1, 0, w.Cpad, INT_MAX, w.Cpad, 0};
   hipError_t e = dg_launch_gemm(g, ctx->stream);
   if (e != hipSuccess) return hip_fail(ctx, e, "dg_prefill_block(qkv)");
-  if (ctx->rope_base > 0.0) {
-    e = dg_launch_rope(q, m.C, m.Hq, m.hd, qd, P, ctx->rope_base, ctx->stream);
-    if (e == hipSuccess) e = dg_launch_rope(kc, m.C, m.Hkv, m.hd, kd, P, ctx->rope_base, ctx->stream);
-    if (e != hipSuccess) return hip_fail(ctx, e, "dg_prefill_block(rope)");
-  }
+  // Rotation of the block's queries and keys, and the block's rotated keys and its values
+  // into the cache rows [P, P + C) (the attention below reads the cache only below P).
+  e = dg_launch_rope_store(q, kc, vct, m.C, w.Cpad, m.Hq, m.Hkv, m.hd, P, ctx->rope_base, Kp, Vt, P, Pcap,
+                           ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "dg_prefill_block(rope, store)");
 
   // Causal attention: the prefix [0, P) and block keys j <= i.
   AttnArgs at{};
@@ -547,9 +547,6 @@ dg_status dg_prefill_block(dg_ctx ctx, const dg_dims *dims, const int32_t *token
   e = dg_launch_gemm(go, ctx->stream);
   if (e != hipSuccess) return hip_fail(ctx, e, "dg_prefill_block(wo)");
 
-  // The block's rotated keys and its values join the cache.
-  e = dg_launch_block_store(kc, vct, m.C, w.Cpad, m.Hkv, m.hd, Kp, Vt, P, Pcap, ctx->stream);
-  if (e != hipSuccess) return hip_fail(ctx, e, "dg_prefill_block(store)");
   *P_out = P + m.C;
   return DG_OK;
 }

@@ -394,10 +394,12 @@ struct AttnArgs {
   u16 *O;              // merged output [Cpad][Hq*hd]
 };
 hipError_t dg_launch_attention(const AttnArgs &a, hipStream_t st);
-hipError_t dg_launch_rope(u16 *x, int rows, int heads, int hd, int ld, int64_t pos0, double base,
-                          hipStream_t st);
-hipError_t dg_launch_block_store(const u16 *kc, const u16 *vct, int C, int Cpad, int Hkv, int hd,
-                                 u16 *Kp, u16 *Vt, int64_t P, int64_t Pcap, hipStream_t st);
+// Rotates the block's queries q [C][Hq*hd] and keys kc [C][Hkv*hd] to positions pos0 + r in
+// place (base > 0), and, when Kp is given, writes the keys to Kp rows [P, P + C) and the
+// values vct [Hkv*hd][Cpad] to Vt columns [P, P + C). One launch.
+hipError_t dg_launch_rope_store(u16 *q, u16 *kc, const u16 *vct, int C, int Cpad, int Hq, int Hkv, int hd,
+                                int64_t pos0, double base, u16 *Kp, u16 *Vt, int64_t P, int64_t Pcap,
+                                hipStream_t st);
 
 struct LogitsArgs {
   const u16 *H;        // [C][d]

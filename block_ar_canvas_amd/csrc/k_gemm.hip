@@ -338,64 +338,78 @@ hipError_t dg_launch_gemm(const GemmArgs &a, hipStream_t st) {
 
 namespace {
 
-// Rotary position embedding in place on bf16 rows, half-split pairing: the pair
-// (x_d, x_{d+hd/2}) of row r turns by (pos0 + r) * base^(-2d/hd). The openai-hub page
-// "从零拆开DiffusionGemma" (closing remarks of step 3) names rotary positions as part of
-// the full model. Angle, sine, cosine and rotation in float64: token positions reach 2^18
-// and more, where a float32 angle is already off by about 1e-2 rad.
-__global__ __launch_bounds__(256) void rope_kernel(u16 *x, int rows, int heads, int hd, int ld,
-                                                   int64_t pos0, double base) {
-  const int half = hd / 2;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)rows * heads * half) return;
-  const int d = (int)(i % half);
-  const int64_t rh = i / half;
-  const int h = (int)(rh % heads), r = (int)(rh / heads);
-  u16 *p = x + (int64_t)r * ld + h * hd;
-  const double ang = (double)(pos0 + r) * pow(base, -2.0 * d / hd);
-  double sn, cs;
-  sincos(ang, &sn, &cs);
-  const double x1 = __uint_as_float((uint32_t)p[d] << 16);
-  const double x2 = __uint_as_float((uint32_t)p[d + half] << 16);
-  p[d] = f32_to_bf16((float)(x1 * cs - x2 * sn));
-  p[d + half] = f32_to_bf16((float)(x1 * sn + x2 * cs));
-}
+// Rotary positions and the block's entry into the cache, in one launch. Three kinds of
+// work items, in this order over the grid:
+//   Q pairs (only when rotating): the pair (x_d, x_{d+hd/2}) of query head h of block row
+//     r turns by (pos0 + r) * base^(-2d/hd), in place (half-split pairing; the openai-hub
+//     page "从零拆开DiffusionGemma", closing remarks of step 3, names rotary positions as
+//     part of the full model);
+//   K pairs: the same turn for the block keys kc (when rotating), written back to kc for
+//     the attention call and, when storing, to the cache rows Kp[g][P + r];
+//   V elements (only when storing): vct [Hkv*hd][Cpad] to the cache columns Vt[g][e][P + r].
+// Angle, sine, cosine and rotation in float64: token positions reach 2^18 and more, where
+// a float32 angle is already off by about 1e-2 rad. The attention calls read the cache
+// only below P, so storing the block before they run changes nothing they read.
+struct RopeStoreArgs {
+  u16 *q, *kc;
+  const u16 *vct;
+  int C, Cpad, Hq, Hkv, hd;
+  int64_t pos0;
+  double base;         // 0: no rotation
+  u16 *Kp, *Vt;        // NULL: no store
+  int64_t P, Pcap;
+};
 
-// Appends a block's keys (rows of kc [Cpad][Hkv*hd]) and values (vct [Hkv*hd][Cpad]) to
-// the cache at token positions [P, P + C): Kp[g][P + r][e] and Vt[g][e][P + r].
-__global__ __launch_bounds__(256) void block_store_kernel(const u16 *kc, const u16 *vct, int C, int Cpad,
-                                                          int Hkv, int hd, u16 *Kp, u16 *Vt, int64_t P,
-                                                          int64_t Pcap) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)C * Hkv * hd) return;
-  {
-    const int e = (int)(i % hd);
-    const int64_t t = i / hd;
-    const int g = (int)(t % Hkv), r = (int)(t / Hkv);
-    Kp[((int64_t)g * Pcap + P + r) * hd + e] = kc[(int64_t)r * Hkv * hd + g * hd + e];
+__global__ __launch_bounds__(256) void rope_store_kernel(RopeStoreArgs a, int64_t nq, int64_t nk) {
+  const int half = a.hd / 2;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < nq + nk) {
+    const bool isq = i < nq;
+    if (!isq) i -= nq;
+    const int heads = isq ? a.Hq : a.Hkv, ld = heads * a.hd;
+    const int d = (int)(i % half);
+    const int64_t rh = i / half;
+    const int h = (int)(rh % heads), r = (int)(rh / heads);
+    u16 *p = (isq ? a.q : a.kc) + (int64_t)r * ld + h * a.hd;
+    u16 y1 = p[d], y2 = p[d + half];
+    if (a.base > 0.0) {
+      const double ang = (double)(a.pos0 + r) * pow(a.base, -2.0 * d / a.hd);
+      double sn, cs;
+      sincos(ang, &sn, &cs);
+      const double x1 = __uint_as_float((uint32_t)y1 << 16);
+      const double x2 = __uint_as_float((uint32_t)y2 << 16);
+      y1 = f32_to_bf16((float)(x1 * cs - x2 * sn));
+      y2 = f32_to_bf16((float)(x1 * sn + x2 * cs));
+      p[d] = y1;
+      p[d + half] = y2;
+    }
+    if (!isq && a.Kp) {
+      u16 *kr = a.Kp + ((int64_t)h * a.Pcap + a.P + r) * a.hd;
+      kr[d] = y1;
+      kr[d + half] = y2;
+    }
+    return;
   }
-  {
-    const int r = (int)(i % C);
-    const int64_t ge = i / C;                      // g * hd + e
-    Vt[ge * Pcap + P + r] = vct[ge * Cpad + r];
+  i -= nq + nk;
+  if (a.Kp && i < (int64_t)a.C * a.Hkv * a.hd) {
+    const int r = (int)(i % a.C);
+    const int64_t ge = i / a.C;                      // g * hd + e
+    a.Vt[ge * a.Pcap + a.P + r] = a.vct[ge * a.Cpad + r];
   }
 }
 
 }  // namespace
 
-hipError_t dg_launch_rope(u16 *x, int rows, int heads, int hd, int ld, int64_t pos0, double base,
-                          hipStream_t st) {
-  const int64_t n = (int64_t)rows * heads * (hd / 2);
-  hipLaunchKernelGGL(rope_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, x, rows, heads,
-                     hd, ld, pos0, base);
-  return hipGetLastError();
-}
-
-hipError_t dg_launch_block_store(const u16 *kc, const u16 *vct, int C, int Cpad, int Hkv, int hd,
-                                 u16 *Kp, u16 *Vt, int64_t P, int64_t Pcap, hipStream_t st) {
-  const int64_t n = (int64_t)C * Hkv * hd;
-  hipLaunchKernelGGL(block_store_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, kc, vct,
-                     C, Cpad, Hkv, hd, Kp, Vt, P, Pcap);
+hipError_t dg_launch_rope_store(u16 *q, u16 *kc, const u16 *vct, int C, int Cpad, int Hq, int Hkv, int hd,
+                                int64_t pos0, double base, u16 *Kp, u16 *Vt, int64_t P, int64_t Pcap,
+                                hipStream_t st) {
+  const RopeStoreArgs a{q, kc, vct, C, Cpad, Hq, Hkv, hd, pos0, base, Kp, Vt, P, Pcap};
+  const int64_t nq = base > 0.0 ? (int64_t)C * Hq * (hd / 2) : 0;
+  const int64_t nk = (base > 0.0 || Kp) ? (int64_t)C * Hkv * (hd / 2) : 0;
+  const int64_t nv = Kp ? (int64_t)C * Hkv * hd : 0;
+  const int64_t n = nq + nk + nv;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_store_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a, nq, nk);
   return hipGetLastError();
 }
 
