@@ -18,6 +18,12 @@ def pytest_collection_modifyitems(config, items):
     pass
 
 
+def pytest_runtest_logfinish(nodeid, location):
+    # Progress reaches a pipe after every test, not only at the end of each line of
+    # results (stdout is block-buffered there, and the full-size tests run for minutes).
+    sys.stdout.flush()
+
+
 @pytest.fixture(scope="session")
 def dg_ctx():
     """One libdg context on cuda:0 for the GPU tests (fails loudly without a GPU)."""
