@@ -35,10 +35,11 @@ SHAPES = {
     # the workgroup mappings that keep a tile's (a split's) canvas blocks on one XCD
     "wide": di.Config("wide", V=32768, d=256, C=300, Hq=4, Hkv=2, hd=64, F=128, P0=100, N=4,
                       alpha_max=8.0, seed=24),
-    # 256 vocabulary tiles (so 256-column canvas blocks) with a model width whose last
-    # 64-wide chunk is half full, and a ragged canvas; the shapes above with few tiles
-    # or at most 128 padded columns take 128-column blocks
-    "wide_tail": di.Config("wide_tail", V=65536, d=96, C=130, Hq=2, Hkv=1, hd=32, F=64, P0=50, N=4,
+    # 257 vocabulary tiles (so 256-column canvas blocks), the last one holding 77 ids, a
+    # tile count the self-conditioning splits do not divide (plain dispatch order), a
+    # model width whose last 64-wide chunk is half full, and a ragged canvas; the shapes
+    # above with few tiles or at most 128 padded columns take 128-column blocks
+    "wide_tail": di.Config("wide_tail", V=65613, d=96, C=130, Hq=2, Hkv=1, hd=32, F=64, P0=50, N=4,
                            alpha_max=8.0, seed=25),
 }
 
