@@ -107,6 +107,8 @@ def _load():
         "dg_renoise": (i32, [_P, i32, i32, i32, _P, _P, u64, u32, u32, _P]),
         "dg_selfcond": (i32, [_P, D, _P, _P, _P, _P, _P]),
         "dg_stop_test": (i32, [_P, i32, i32, _P, _P, _P, f32, i32, i32, _P]),
+        "dg_accept_renoise_stop": (i32, [_P, i32, i32, i32, _P, f32, _P, _P, _P, u64, u32, i32, f32, i32,
+                                         _P, _P, _P, _P]),
         "dg_commit_kv": (i32, [_P, D, _P, _P, _P, _P, _P, _P, i64, i64, ctypes.POINTER(i64)]),
         "dg_peak_stream_read": (i32, [_P, _P, ctypes.c_size_t, _P]),
         "dg_peak_mfma_bf16": (i32, [_P, i32, _P]),
@@ -303,6 +305,17 @@ class Context:
         self._check(self._lib.dg_stop_test(
             self._h, B, C, _ptr(entropy, _F32, "entropy"), _ptr(argmax, _I32, "argmax"),
             _ptr(prev_argmax, _I32, "prev_argmax", True), float(thr), int(step), int(N),
+            _ptr(flag, _I32, "flag", pinned_ok=True)))
+
+    def accept_renoise_stop(self, V, entropy, b, x0, argmax, prev_argmax, seed, canvas_base, step,
+                            thr, N, accept, n_accept, tokens, flag):
+        """entropy_accept, renoise (with accept) and stop_test in one launch, same results."""
+        B, C = (1, entropy.shape[0]) if entropy.dim() == 1 else tuple(entropy.shape)
+        self._check(self._lib.dg_accept_renoise_stop(
+            self._h, B, C, int(V), _ptr(entropy, _F32, "entropy"), float(b), _ptr(x0, _I32, "x0"),
+            _ptr(argmax, _I32, "argmax"), _ptr(prev_argmax, _I32, "prev_argmax", True), int(seed),
+            int(canvas_base), int(step), float(thr), int(N), _ptr(accept, _U8, "accept"),
+            _ptr(n_accept, _I32, "n_accept"), _ptr(tokens, _I32, "tokens"),
             _ptr(flag, _I32, "flag", pinned_ok=True)))
 
     def moe_ffn(self, md, X, Wr, W1, W2, W1s, W2s, ws, Y, n_active=None):

@@ -748,6 +748,27 @@ dg_status dg_stop_test(dg_ctx ctx, int32_t B, int32_t C, const float *entropy,
   return e == hipSuccess ? DG_OK : hip_fail(ctx, e, "dg_stop_test");
 }
 
+dg_status dg_accept_renoise_stop(dg_ctx ctx, int32_t B, int32_t C, int32_t V, const float *entropy,
+                                 float b, const int32_t *x0, const int32_t *argmax,
+                                 const int32_t *prev_argmax, uint64_t seed, uint32_t canvas_base,
+                                 int32_t step, float thr, int32_t N, uint8_t *accept,
+                                 int32_t *n_accept, int32_t *tokens, int32_t *flag) {
+  DG_ENTER();
+  if (B < 1 || C < 1 || C > 1024 || V < 1)
+    return fail(ctx, DG_ERR_SHAPE, "%s: need B, V >= 1 and 1 <= C <= 1024", __func__);
+  if (!entropy || !x0 || !argmax || !accept || !n_accept || !tokens || !flag)
+    return fail(ctx, DG_ERR_NULL, "%s: NULL buffer", __func__);
+  if (!(b >= 0.f && b < 65536.f)) return fail(ctx, DG_ERR_RANGE, "%s: b=%g must be in [0, 65536)", __func__, b);
+  if (!(thr >= 0.f && thr < 65536.f)) return fail(ctx, DG_ERR_RANGE, "%s: thr=%g must be in [0, 65536)", __func__, thr);
+  if (step < 0 || N < 1) return fail(ctx, DG_ERR_RANGE, "%s: need step >= 0, N >= 1", __func__);
+  const uint64_t budget = (uint64_t)floor((double)b * 4294967296.0);
+  const uint64_t limit = (uint64_t)floor((double)thr * (double)C * 4294967296.0);
+  hipError_t e = dg_launch_accept_renoise_stop(B, C, V, entropy, budget, x0, argmax, prev_argmax, seed,
+                                               canvas_base, step, limit, N, accept, n_accept, tokens, flag,
+                                               ctx->stream);
+  return e == hipSuccess ? DG_OK : hip_fail(ctx, e, __func__);
+}
+
 dg_status dg_commit_kv(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens, const dg_bf16 *E,
                        const dg_bf16 *Wk, const dg_bf16 *Wv, dg_bf16 *Kp, dg_bf16 *Vt, int64_t P,
                        int64_t Pcap, int64_t *P_out) {
@@ -897,14 +918,14 @@ dg_status dg_run_canvas(dg_ctx ctx, const dg_dims *dims, const dg_weights *w, dg
     int32_t *a = am[k & 1], *prev = k > 0 ? am[(k - 1) & 1] : nullptr;
     dg_status r = dg_canvas_attn(ctx, dims, tok, k > 0 ? z : nullptr, E, Wq, Wk, Wv, Wo, Kp, Vt, P, Pcap, ws, A);
     if (!r) r = dg_logits_entropy(ctx, dims, H, E, dg_temperature(k, N, prm->tau0, prm->tau1), ws, ent, a);
-    if (!r) r = dg_entropy_accept(ctx, 1, m.C, ent, prm->b, acc, nacc);
-    if (!r) r = dg_renoise(ctx, 1, m.C, m.V, a, acc, prm->seed, prm->canvas, (uint32_t)k, tok);
-    if (!r) r = dg_selfcond(ctx, dims, ws, E, W1, W2, z);
     if (r) return r;
     const int sl = (int)(ctx->flag_seq++ % 4);
     slot[k & 1] = sl;
     ctx->host_flags[sl] = -1;
-    return dg_stop_test(ctx, 1, m.C, ent, a, prev, prm->thr, k, N, ctx->host_flags + sl);
+    r = dg_accept_renoise_stop(ctx, 1, m.C, m.V, ent, prm->b, a, a, prev, prm->seed, prm->canvas, k,
+                               prm->thr, N, acc, nacc, tok, ctx->host_flags + sl);
+    if (!r) r = dg_selfcond(ctx, dims, ws, E, W1, W2, z);
+    return r;
   };
 
   if ((st = step(0))) return st;

@@ -23,6 +23,10 @@
 // mean entropy is <= the threshold and the argmax did not change since the previous
 // step; the step cap commits anyway.
 //
+// accept_renoise_stop_kernel runs acceptance, renoise and the stop test of a step in one
+// launch with the same arithmetic (shared routines), so the three results are bit for
+// bit those of the three kernels.
+//
 // Confidence-ranked acceptance (the openai-hub page "从零拆开DiffusionGemma", step 4,
 // confidence decoding; the "Text diffusion models" survey, section 5): each step keeps
 // the k positions the model is most confident about. Same rank construction as the
@@ -56,14 +60,12 @@ DG_DEV uint64_t entropy_q(float h) {
   return (uint64_t)ceil((double)h * 4294967296.0);
 }
 
-// tpp threads per canvas position (1, 2 or 4; tpp * C <= 1024) share that position's sum.
-__global__ __launch_bounds__(1024) void accept_kernel(int C, int tpp, const float *ent,
-                                                      uint64_t budget, uint8_t *acc, int *nacc) {
-  __shared__ ulonglong2 kq[1024];                    // (sort key, fixed-point entropy)
-  const int b = blockIdx.x, tid = threadIdx.x;
-  const int pos = tid / tpp, sub = tid % tpp;
-  const float *e = ent + (int64_t)b * C;
-
+// Acceptance of one canvas, workgroup-wide (one barrier inside): tpp threads per
+// position (1, 2 or 4; tpp * C <= 1024) share that position's sum. Returns whether
+// position pos is accepted (the same answer in all tpp threads); q receives the
+// position's fixed-point entropy, the sentinel for an entropy outside the domain.
+DG_DEV bool accept_rank(int C, int tpp, int pos, int sub, const float *e, uint64_t budget,
+                        ulonglong2 *kq, uint64_t &q_out) {
   uint64_t key = ~0ull, q = 0;
   if (pos < C) {
     const float h = e[pos];
@@ -90,7 +92,17 @@ __global__ __launch_bounds__(1024) void accept_kernel(int C, int tpp, const floa
   if (j < C) sum += kq[j].x <= key ? kq[j].y : 0ull;
   sum += sum2;
   for (int o = 1; o < tpp; o <<= 1) sum += __shfl_xor(sum, o);
-  const bool take = pos < C && sum <= budget;
+  q_out = q;
+  return pos < C && sum <= budget;
+}
+
+__global__ __launch_bounds__(1024) void accept_kernel(int C, int tpp, const float *ent,
+                                                      uint64_t budget, uint8_t *acc, int *nacc) {
+  __shared__ ulonglong2 kq[1024];                    // (sort key, fixed-point entropy)
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int pos = tid / tpp, sub = tid % tpp;
+  uint64_t q;
+  const bool take = accept_rank(C, tpp, pos, sub, ent + (int64_t)b * C, budget, kq, q);
   if (pos < C && sub == 0) acc[(int64_t)b * C + pos] = take ? 1 : 0;
   const int n = __syncthreads_count(take && sub == 0);
   if (tid == 0 && nacc) nacc[b] = n;
@@ -151,6 +163,14 @@ DG_DEV void philox4x64_10(uint64_t c[4], uint64_t k0, uint64_t k1) {
   }
 }
 
+// A token drawn uniformly over [0, V): floor(r V / 2^64), r = word 0 of Philox4x64-10
+// under key (seed, canvas) and counter (position, step, stream, 0).
+DG_DEV int uniform_token(int pos, uint32_t step, uint64_t stream, uint64_t seed, uint32_t canvas, int V) {
+  uint64_t c[4] = {(uint64_t)pos, (uint64_t)step, stream, 0ull};
+  philox4x64_10(c, seed, (uint64_t)canvas);
+  return (int)__umul64hi(c[0], (uint64_t)V);
+}
+
 __global__ __launch_bounds__(256) void renoise_kernel(int B, int C, int V, const int *am,
                                                       const uint8_t *acc, uint64_t seed,
                                                       uint32_t canvas_base, uint32_t step,
@@ -162,9 +182,7 @@ __global__ __launch_bounds__(256) void renoise_kernel(int B, int C, int V, const
     tok[i] = am[i];
     return;
   }
-  uint64_t c[4] = {(uint64_t)pos, (uint64_t)step, acc ? 0ull : 1ull, 0ull};
-  philox4x64_10(c, seed, (uint64_t)(canvas_base + (uint32_t)b));
-  tok[i] = (int)__umul64hi(c[0], (uint64_t)V);
+  tok[i] = uniform_token(pos, step, acc ? 0ull : 1ull, seed, canvas_base + (uint32_t)b, V);
 }
 
 // One workgroup per canvas column (canvas b = column / Cs, position = column % Cs).
@@ -269,6 +287,12 @@ __global__ __launch_bounds__(256) void sample_kernel(SampleArgs a) {
   }
 }
 
+// Stop flag: 1 = stop, else 2 at the step cap, else 0. A system-scope store: the flag
+// may live in pinned host memory that the host polls.
+DG_DEV void store_flag(int *flag, bool stop, int step, int N) {
+  __hip_atomic_store(flag, stop ? 1 : (step >= N - 1 ? 2 : 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 __global__ __launch_bounds__(256) void stop_kernel(int C, const float *ent, const int *am,
                                                    const int *prev, uint64_t limit, int step,
                                                    int N, int *flag) {
@@ -297,10 +321,62 @@ __global__ __launch_bounds__(256) void stop_kernel(int C, const float *ent, cons
   if (tid == 0) {
     const uint64_t tot = ssum[0] + ssum[1] + ssum[2] + ssum[3];
     const int all = sok[0] & sok[1] & sok[2] & sok[3];
-    const bool stop = step >= 1 && prev != nullptr && all && tot <= limit;
-    // system-scope store: flag may live in host memory that the host polls
-    __hip_atomic_store(flag + b, stop ? 1 : (step >= N - 1 ? 2 : 0), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_SYSTEM);
+    store_flag(flag + b, step >= 1 && prev != nullptr && all && tot <= limit, step, N);
+  }
+}
+
+// Acceptance, renoise and stop test of one step, one workgroup per canvas: the same
+// arithmetic as accept_kernel, renoise_kernel (stream 0) and stop_kernel run in that
+// order. Every position is handled by one thread (sub == 0), which reads only its own
+// x0, argmax and previous argmax after the acceptance's barrier.
+struct ArsArgs {
+  int C, tpp, V, step, N;
+  const float *ent;
+  const int *x0, *am, *prev;
+  uint64_t budget, limit, seed;
+  uint32_t canvas_base;
+  uint8_t *acc;
+  int *nacc, *tok, *flag;
+};
+
+__global__ __launch_bounds__(1024) void accept_renoise_stop_kernel(ArsArgs a) {
+  __shared__ ulonglong2 kq[1024];
+  __shared__ uint64_t ssum[16];
+  __shared__ int sok[16];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int pos = tid / a.tpp, sub = tid % a.tpp;
+  const int64_t o = (int64_t)b * a.C + pos;
+  uint64_t q;
+  const bool take = accept_rank(a.C, a.tpp, pos, sub, a.ent + (int64_t)b * a.C, a.budget, kq, q);
+  uint64_t s = 0;
+  int ok = 1;
+  if (pos < a.C && sub == 0) {
+    a.acc[o] = take ? 1 : 0;
+    a.tok[o] = take ? a.x0[o] : uniform_token(pos, (uint32_t)a.step, 0ull, a.seed, a.canvas_base + (uint32_t)b, a.V);
+    // stop-test terms: q is ceil(h 2^32) for an entropy in the domain (as the stop
+    // test sums it) and the sentinel for one outside it (which blocks the stop)
+    if (q == Q_SENTINEL) ok = 0;
+    else s = q;
+    if (a.prev && a.am[o] != a.prev[o]) ok = 0;
+  }
+  for (int off = 32; off > 0; off >>= 1) {           // integer sums: order-free
+    s += __shfl_xor(s, off);
+    ok &= __shfl_xor(ok, off);
+  }
+  if (lane == 0) {
+    ssum[wave] = s;
+    sok[wave] = ok;
+  }
+  const int n = __syncthreads_count(take && sub == 0);
+  if (tid == 0) {
+    uint64_t tot = 0;
+    int all = 1;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+      tot += ssum[w];
+      all &= sok[w];
+    }
+    a.nacc[b] = n;
+    store_flag(a.flag + b, a.step >= 1 && a.prev != nullptr && all && tot <= a.limit, a.step, a.N);
   }
 }
 
@@ -341,5 +417,33 @@ hipError_t dg_launch_renoise(int B, int C, int V, const int *am, const uint8_t *
 hipError_t dg_launch_stop(int B, int C, const float *ent, const int *am, const int *prev,
                           uint64_t limit, int step, int N, int *flag, hipStream_t st) {
   hipLaunchKernelGGL(stop_kernel, dim3(B), dim3(256), 0, st, C, ent, am, prev, limit, step, N, flag);
+  return hipGetLastError();
+}
+
+hipError_t dg_launch_accept_renoise_stop(int B, int C, int V, const float *ent, uint64_t budget,
+                                         const int *x0, const int *am, const int *prev, uint64_t seed,
+                                         uint32_t canvas_base, int step, uint64_t limit, int N,
+                                         uint8_t *acc, int *nacc, int *tok, int *flag, hipStream_t st) {
+  // C <= 1024 (checked by the caller); up to 4 threads per position as in acceptance
+  ArsArgs a{};
+  a.C = C;
+  a.tpp = C <= 256 ? 4 : C <= 512 ? 2 : 1;
+  a.V = V;
+  a.step = step;
+  a.N = N;
+  a.ent = ent;
+  a.x0 = x0;
+  a.am = am;
+  a.prev = prev;
+  a.budget = budget;
+  a.limit = limit;
+  a.seed = seed;
+  a.canvas_base = canvas_base;
+  a.acc = acc;
+  a.nacc = nacc;
+  a.tok = tok;
+  a.flag = flag;
+  const int n = (C * a.tpp + 63) / 64 * 64;
+  hipLaunchKernelGGL(accept_renoise_stop_kernel, dim3(B), dim3(n), 0, st, a);
   return hipGetLastError();
 }

@@ -3,7 +3,9 @@
 The loop follows the DiffusionGemma inference steps (Technical Report page, "Method
 steps" (2)-(5); tutorial chapter "DiffusionGemma", data-flow pseudocode): initialize
 a canvas with uniform tokens and z = 0, run at most N denoise steps (attention,
-sampler head, acceptance, renoise, self-conditioning, stop test), then commit the
+sampler head, acceptance, renoise, stop test, self-conditioning; the stop test reads
+only the entropies and argmaxes, so it runs before self-conditioning, and under the
+entropy rule acceptance, renoise and the stop test are one launch), then commit the
 finalized block x0 = argmax to the KV cache and start the next canvas.
 
 This module only sequences calls and owns the device buffers of one canvas; every
@@ -101,12 +103,19 @@ class CanvasLoop:
         if self.draw == "sample":
             x0 = self.sampled[k & 1]
             self.ctx.sample(dm, self.ws, 1, self.seed, self.canvas, k, x0)
+        slot = self._seq % len(self.flags)
+        self._seq += 1
+        self._slot[k] = slot
+        self.flags[slot].fill_(-1)
         if self.rule == "confidence":
             self.ctx.confidence(dm, self.ws, self.conf)
             self.ctx.topk_accept(self.conf, reveal_count(dm.C, self.N, k), self.accept, self.n_accept)
+            self.ctx.renoise(dm.V, x0, self.accept, self.seed, self.canvas, k, self.tokens)
+            self.ctx.stop_test(self.entropy, am, prev, self.thr, k, self.N, self.flags[slot])
         else:
-            self.ctx.entropy_accept(self.entropy, self.b, self.accept, self.n_accept)
-        self.ctx.renoise(dm.V, x0, self.accept, self.seed, self.canvas, k, self.tokens)
+            self.ctx.accept_renoise_stop(dm.V, self.entropy, self.b, x0, am, prev, self.seed, self.canvas,
+                                         k, self.thr, self.N, self.accept, self.n_accept, self.tokens,
+                                         self.flags[slot])
         sev = self.selfcond_events
         if sev is not None:
             s0 = torch.cuda.Event(enable_timing=True)
@@ -116,11 +125,6 @@ class CanvasLoop:
             s1 = torch.cuda.Event(enable_timing=True)
             s1.record(self.ctx.torch_stream())
             sev.append((s0, s1))
-        slot = self._seq % len(self.flags)
-        self._seq += 1
-        self._slot[k] = slot
-        self.flags[slot].fill_(-1)
-        self.ctx.stop_test(self.entropy, am, prev, self.thr, k, self.N, self.flags[slot])
         return am
 
     def wait_flag(self, k: int, timeout_s: float = 60.0) -> int:
@@ -279,18 +283,21 @@ class BatchLoop:
         if self.draw == "sample":
             x0 = self.sampled[k & 1]
             self.ctx.sample(self.dims_all, self.ws, self.B, self.seed, self.batch * self.B, k, x0.view(-1))
-        if self.rule == "confidence":
-            self.ctx.confidence(self.dims_all, self.ws, self.conf.view(-1))
-            self.ctx.topk_accept(self.conf, reveal_count(dm.C, self.N, k), self.accept, self.n_accept)
-        else:
-            self.ctx.entropy_accept(self.entropy, self.b, self.accept, self.n_accept)
-        self.ctx.renoise(dm.V, x0, self.accept, self.seed, self.batch * self.B, k, self.tokens)
-        self.ctx.selfcond(self.dims_all, self.ws, W["E"], W["W1"], W["W2"], self.z.view(-1, dm.d))
         slot = self._seq % len(self.flags)
         self._seq += 1
         self._slot[k] = slot
         self.flags[slot].fill_(-1)
-        self.ctx.stop_test(self.entropy, am, prev, self.thr, k, self.N, self.flags[slot])
+        base = self.batch * self.B
+        if self.rule == "confidence":
+            self.ctx.confidence(self.dims_all, self.ws, self.conf.view(-1))
+            self.ctx.topk_accept(self.conf, reveal_count(dm.C, self.N, k), self.accept, self.n_accept)
+            self.ctx.renoise(dm.V, x0, self.accept, self.seed, base, k, self.tokens)
+            self.ctx.stop_test(self.entropy, am, prev, self.thr, k, self.N, self.flags[slot])
+        else:
+            self.ctx.accept_renoise_stop(dm.V, self.entropy, self.b, x0, am, prev, self.seed, base, k,
+                                         self.thr, self.N, self.accept, self.n_accept, self.tokens,
+                                         self.flags[slot])
+        self.ctx.selfcond(self.dims_all, self.ws, W["E"], W["W1"], W["W2"], self.z.view(-1, dm.d))
         return am
 
     def wait_flags(self, k: int, timeout_s: float = 60.0):

@@ -10,6 +10,7 @@
  *   dg_selfcond        self-conditioning z = FFW(p0 . E)
  *   dg_stop_test       adaptive stop (mean entropy and stable argmax) / step cap
  * and, once per canvas, dg_commit_kv appends the finalized block to the KV cache.
+ * dg_accept_renoise_stop runs acceptance, renoise and the stop test in one launch.
  * Beyond that step: dg_prefill_block (the causal re-encode commit) with dg_set_rope,
  * dg_confidence / dg_topk_accept / dg_reveal_count (confidence-ranked acceptance),
  * dg_sample (sampled tokens), dg_moe_ffn (the canvas mixture-of-experts FFN),
@@ -238,6 +239,23 @@ dg_status dg_stop_test(dg_ctx ctx, int32_t B, int32_t C, const float *entropy,
                        const int32_t *argmax, const int32_t *prev_argmax, float thr,
                        int32_t step, int32_t N, int32_t *flag);
 
+/* The acceptance, renoise and stop test of one step in one launch (the same passages as
+ * the three calls): the results are those of
+ *   dg_entropy_accept(B, C, entropy, b, accept, n_accept);
+ *   dg_renoise(B, C, V, x0, accept, seed, canvas_base, step, tokens);
+ *   dg_stop_test(B, C, entropy, argmax, prev_argmax, thr, step, N, flag);
+ * in that order, bit for bit. x0 is what accepted positions keep (the argmax, or the
+ * dg_sample draws); argmax and prev_argmax are what the stop test compares (prev_argmax
+ * may be NULL). tokens must not overlap entropy, x0, argmax or prev_argmax.
+ * Shapes and errors as in the three calls: 1 <= C <= 1024, V >= 1, 0 <= b, thr < 65536,
+ * step >= 0, N >= 1. */
+dg_status dg_accept_renoise_stop(dg_ctx ctx, int32_t B, int32_t C, int32_t V,
+                                 const float *entropy, float b, const int32_t *x0,
+                                 const int32_t *argmax, const int32_t *prev_argmax,
+                                 uint64_t seed, uint32_t canvas_base, int32_t step, float thr,
+                                 int32_t N, uint8_t *accept, int32_t *n_accept,
+                                 int32_t *tokens, int32_t *flag);
+
 /* Rotary positions (openai-hub page "从零拆开DiffusionGemma", closing remarks of step 3:
  * the full model has rotary position encoding) for dg_canvas_attn and dg_prefill_block
  * of this context: base 0 (the default) turns them off; base > 0 rotates, in every head,
@@ -299,8 +317,8 @@ dg_status dg_commit_kv(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens,
  * the library: a uniform random canvas (dg_renoise with accept = NULL), then denoise
  * steps k = 0, 1, ... of
  *   dg_canvas_attn (z = 0 at k = 0), dg_logits_entropy on H_k at dg_temperature(k, N,
- *   tau0, tau1), dg_entropy_accept with budget b, dg_renoise of the rejected positions,
- *   dg_selfcond, dg_stop_test against the previous step's argmax,
+ *   tau0, tau1), dg_accept_renoise_stop (acceptance with budget b, renoise of the
+ *   rejected positions, the stop test against the previous step's argmax), dg_selfcond,
  * until the stop test fires or the cap N is reached, then dg_commit_kv of that step's
  * argmax. Step k + 1 is enqueued before the host waits for step k's flag (pinned host
  * memory of the context, polled: no stream synchronization between steps); when step k

@@ -7,6 +7,7 @@
  *   redrawn, inside [0, V);
  *   s = p0 E = 0, so z = W2 GELU(W1 0) = 0 whatever W1 and W2 hold;
  *   the stop test at step 0 with no previous argmax gives flag 0.
+ * dg_accept_renoise_stop on the same entropies must give the three calls' results.
  * Also: a NULL pointer and tau = 0 are refused with a message and nothing enqueued.
  * Built by the package's build step next to libdg.so; prints "c_abi_check: ok" and
  * exits 0 when every check holds, else prints the first failure and exits 1. */
@@ -48,8 +49,8 @@ int main(void) {
   void *ws = NULL;
   dg_bf16 *E = NULL, *H = NULL, *W1 = NULL, *W2 = NULL, *z = NULL;
   float *ent = NULL;
-  int32_t *am = NULL, *tok = NULL, *nacc = NULL, *flag = NULL;
-  uint8_t *acc = NULL;
+  int32_t *am = NULL, *tok = NULL, *nacc = NULL, *flag = NULL, *tok2 = NULL, *nacc2 = NULL, *flag2 = NULL;
+  uint8_t *acc = NULL, *acc2 = NULL;
   HIP_OK(hipMalloc(&ws, ws_bytes));
   HIP_OK(hipMalloc((void **)&E, (size_t)V * d * 2));
   HIP_OK(hipMalloc((void **)&H, (size_t)C * d * 2));
@@ -62,6 +63,10 @@ int main(void) {
   HIP_OK(hipMalloc((void **)&acc, (size_t)C));
   HIP_OK(hipMalloc((void **)&nacc, 4));
   HIP_OK(hipMalloc((void **)&flag, 4));
+  HIP_OK(hipMalloc((void **)&tok2, (size_t)C * 4));
+  HIP_OK(hipMalloc((void **)&acc2, (size_t)C));
+  HIP_OK(hipMalloc((void **)&nacc2, 4));
+  HIP_OK(hipMalloc((void **)&flag2, 4));
 
   /* E = 0; H, W1, W2 = arbitrary finite bf16 values (alternating +-0.5, +-0.25) */
   HIP_OK(hipMemset(E, 0, (size_t)V * d * 2));
@@ -83,11 +88,13 @@ int main(void) {
   DG_OK_OR_FAIL(ctx, dg_renoise(ctx, 1, C, V, am, acc, 7u, 0u, 0u, tok));
   DG_OK_OR_FAIL(ctx, dg_selfcond(ctx, &m, ws, E, W1, W2, z));
   DG_OK_OR_FAIL(ctx, dg_stop_test(ctx, 1, C, ent, am, NULL, 0.005f, 0, 48, flag));
+  DG_OK_OR_FAIL(ctx, dg_accept_renoise_stop(ctx, 1, C, V, ent, 0.1f, am, am, NULL, 7u, 0u, 0, 0.005f, 48,
+                                            acc2, nacc2, tok2, flag2));
   DG_OK_OR_FAIL(ctx, dg_sync(ctx));
 
   float h_ent[16];
-  int32_t h_am[16], h_tok[16], h_nacc, h_flag;
-  uint8_t h_acc[16];
+  int32_t h_am[16], h_tok[16], h_nacc, h_flag, h_tok2[16], h_nacc2, h_flag2;
+  uint8_t h_acc[16], h_acc2[16];
   HIP_OK(hipMemcpy(h_ent, ent, sizeof h_ent, hipMemcpyDeviceToHost));
   HIP_OK(hipMemcpy(h_am, am, sizeof h_am, hipMemcpyDeviceToHost));
   HIP_OK(hipMemcpy(h_tok, tok, sizeof h_tok, hipMemcpyDeviceToHost));
@@ -95,6 +102,13 @@ int main(void) {
   HIP_OK(hipMemcpy(&h_nacc, nacc, 4, hipMemcpyDeviceToHost));
   HIP_OK(hipMemcpy(&h_flag, flag, 4, hipMemcpyDeviceToHost));
   HIP_OK(hipMemcpy(host, z, (size_t)C * d * 2, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(h_tok2, tok2, sizeof h_tok2, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(h_acc2, acc2, sizeof h_acc2, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(&h_nacc2, nacc2, 4, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(&h_flag2, flag2, 4, hipMemcpyDeviceToHost));
+  if (memcmp(h_tok2, h_tok, sizeof h_tok) || memcmp(h_acc2, h_acc, sizeof h_acc) || h_nacc2 != h_nacc ||
+      h_flag2 != h_flag)
+    FAIL("dg_accept_renoise_stop differs from the three calls");
 
   const double lnV = log((double)V);
   for (int c = 0; c < C; ++c) {
@@ -111,6 +125,7 @@ int main(void) {
   free(host);
   hipFree(ws); hipFree(E); hipFree(H); hipFree(W1); hipFree(W2); hipFree(z);
   hipFree(ent); hipFree(am); hipFree(tok); hipFree(acc); hipFree(nacc); hipFree(flag);
+  hipFree(tok2); hipFree(acc2); hipFree(nacc2); hipFree(flag2);
   dg_destroy(ctx);
   printf("c_abi_check: ok\n");
   return 0;

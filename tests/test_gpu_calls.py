@@ -171,7 +171,7 @@ def test_canvas_attention_without_selfcond_term(dg_ctx):
     assert maxrel_rows(O.from_bf16(bits_np(A)), O.from_bf16(A_r)) <= 2e-2
 
 
-def _accept_cases():
+def _accept_cases_synthetic():
     rng = np.random.default_rng(31)
     cases = []
     for C in (1, 7, 16, 100, 256, 1000, 1024):
@@ -183,6 +183,11 @@ def _accept_cases():
                       0.05, 0.05, 0.05, 65535.0]], np.float32)
     cases.append(edge)
     cases.append(np.full((2, 3), 0.05, np.float32))
+    return cases
+
+
+def _accept_cases():
+    cases = _accept_cases_synthetic()
     # the oracle's own entropies along a small-config trajectory
     cfg, W, *_ = setup("small")
     tgt = di.targets(cfg, 0)
@@ -281,6 +286,82 @@ def test_stop_test_bit_exact(dg_ctx):
     flag = torch.empty(3, dtype=torch.int32, device=DEV)
     dg_ctx.stop_test(f32_dev(hb), i32_dev(ab), i32_dev(pb), 0.005, 2, 8, flag)
     np.testing.assert_array_equal(flag.cpu().numpy(), O.stop_test(hb, ab, pb, 0.005, 2, 8))
+
+
+def _ars_cases():
+    """(entropy [B, C], b, prev relation, step, N) for the one-launch acceptance, renoise
+    and stop test: the acceptance cases (NaN, infinities, ties, zeros, C up to 1024),
+    plus canvases whose mean entropy is under the threshold so the stop can fire."""
+    cases = []
+    for i, h in enumerate(_accept_cases_synthetic()):
+        B, C = h.shape
+        cases.append((h, (0.1, 0.0, 0.37, 65000.0)[i % 4], ("same", "one_changed", None)[i % 3],
+                      (0, 3, 47)[i % 3], 48))
+    rng = np.random.default_rng(53)
+    for B, C, step in ((1, 256, 5), (3, 100, 1), (2, 1024, 47), (4, 1, 2)):
+        h = rng.exponential(0.002, (B, C)).astype(np.float32)
+        cases.append((h, 0.1, "same", step, 48))
+        cases.append((h, 0.1, "one_changed", step, 48))
+    return cases
+
+
+@pytest.mark.parametrize("case", range(len(_ars_cases())))
+def test_accept_renoise_stop_matches_the_three_calls(dg_ctx, case):
+    """dg_accept_renoise_stop against the oracle's acceptance, renoise and stop test and
+    against the three separate calls, bit for bit (x0 differs from the argmax so the
+    kept tokens are checked to come from x0)."""
+    h, b, rel, step, N = _ars_cases()[case]
+    B, C = h.shape
+    V, thr, seed, base = 5000, 0.005, 2 ** 63 + 9 + case, 11 * case
+    rng = np.random.default_rng(100 + case)
+    am = rng.integers(0, V, (B, C)).astype(np.int32)
+    x0 = rng.integers(0, V, (B, C)).astype(np.int32)
+    prev = None
+    if rel is not None:
+        prev = am.copy()
+        if rel == "one_changed":
+            prev[-1, C // 2] = (prev[-1, C // 2] + 1) % V
+    acc_r, n_r = O.entropy_accept(h, b)
+    tok_r = O.renoise(x0, acc_r, seed, base, step, V)
+    flag_r = O.stop_test(h, am, prev, thr, step, N)
+
+    def fresh():
+        return (torch.full((B, C), 7, dtype=torch.uint8, device=DEV), torch.full((B,), -5, dtype=torch.int32, device=DEV),
+                torch.full((B, C), -1, dtype=torch.int32, device=DEV), torch.full((B,), -1, dtype=torch.int32, device=DEV))
+
+    hd, amd, x0d = f32_dev(h), i32_dev(am), i32_dev(x0)
+    prevd = None if prev is None else i32_dev(prev)
+    acc, n, tok, flag = fresh()
+    dg_ctx.accept_renoise_stop(V, hd, b, x0d, amd, prevd, seed, base, step, thr, N, acc, n, tok, flag)
+    acc2, n2, tok2, flag2 = fresh()
+    dg_ctx.entropy_accept(hd, b, acc2, n2)
+    dg_ctx.renoise(V, x0d, acc2, seed, base, step, tok2)
+    dg_ctx.stop_test(hd, amd, prevd, thr, step, N, flag2)
+    dg_ctx.sync()
+    np.testing.assert_array_equal(acc.cpu().numpy(), acc_r)
+    np.testing.assert_array_equal(n.cpu().numpy(), n_r)
+    np.testing.assert_array_equal(tok.cpu().numpy(), tok_r)
+    np.testing.assert_array_equal(flag.cpu().numpy(), flag_r)
+    for got, ref in ((acc, acc2), (n, n2), (tok, tok2), (flag, flag2)):
+        np.testing.assert_array_equal(got.cpu().numpy(), ref.cpu().numpy())
+
+
+def test_accept_renoise_stop_refusals(dg_ctx):
+    h = f32_dev(np.zeros((1, 8), np.float32))
+    a = i32_dev(np.zeros((1, 8), np.int32))
+    acc = torch.empty(1, 8, dtype=torch.uint8, device=DEV)
+    n = torch.empty(1, dtype=torch.int32, device=DEV)
+    tok = torch.full((1, 8), -1, dtype=torch.int32, device=DEV)
+    flag = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    for kw, err in (({"b": -0.5}, "DG_ERR_RANGE"), ({"thr": 70000.0}, "DG_ERR_RANGE"),
+                    ({"step": -1}, "DG_ERR_RANGE"), ({"N": 0}, "DG_ERR_RANGE"), ({"V": 0}, "DG_ERR_SHAPE")):
+        args = {"V": 10, "b": 0.1, "thr": 0.005, "step": 1, "N": 4, **kw}
+        with pytest.raises(dg.DGError) as ei:
+            dg_ctx.accept_renoise_stop(args["V"], h, args["b"], a, a, a, 1, 0, args["step"], args["thr"],
+                                       args["N"], acc, n, tok, flag)
+        assert ei.value.name == err
+    dg_ctx.sync()
+    assert int(tok.min().item()) == -1 and int(flag.item()) == -1
 
 
 def test_stop_flag_in_pinned_host_memory(dg_ctx):
