@@ -61,14 +61,14 @@ DG_DEV uint64_t entropy_q(float h) {
 }
 
 // Acceptance of one canvas, workgroup-wide (one barrier inside): tpp threads per
-// position (1, 2 or 4; tpp * C <= 1024) share that position's sum. Returns whether
-// position pos is accepted (the same answer in all tpp threads); q receives the
-// position's fixed-point entropy, the sentinel for an entropy outside the domain.
-DG_DEV bool accept_rank(int C, int tpp, int pos, int sub, const float *e, uint64_t budget,
+// position (1, 2 or 4; tpp * C <= 1024) share that position's sum; h is position pos's
+// entropy (read by the caller, unused for pos >= C). Returns whether position pos is
+// accepted (the same answer in all tpp threads); q receives the position's fixed-point
+// entropy, the sentinel for an entropy outside the domain.
+DG_DEV bool accept_rank(int C, int tpp, int pos, int sub, float h, uint64_t budget,
                         ulonglong2 *kq, uint64_t &q_out) {
   uint64_t key = ~0ull, q = 0;
   if (pos < C) {
-    const float h = e[pos];
     uint32_t bits;
     if (!(h < H_LIMIT)) bits = 0xFFFFFFFFu;
     else bits = h > 0.f ? __float_as_uint(h) : 0u;
@@ -101,8 +101,9 @@ __global__ __launch_bounds__(1024) void accept_kernel(int C, int tpp, const floa
   __shared__ ulonglong2 kq[1024];                    // (sort key, fixed-point entropy)
   const int b = blockIdx.x, tid = threadIdx.x;
   const int pos = tid / tpp, sub = tid % tpp;
+  const float h = pos < C ? ent[(int64_t)b * C + pos] : 0.f;
   uint64_t q;
-  const bool take = accept_rank(C, tpp, pos, sub, ent + (int64_t)b * C, budget, kq, q);
+  const bool take = accept_rank(C, tpp, pos, sub, h, budget, kq, q);
   if (pos < C && sub == 0) acc[(int64_t)b * C + pos] = take ? 1 : 0;
   const int n = __syncthreads_count(take && sub == 0);
   if (tid == 0 && nacc) nacc[b] = n;
@@ -328,7 +329,9 @@ __global__ __launch_bounds__(256) void stop_kernel(int C, const float *ent, cons
 // Acceptance, renoise and stop test of one step, one workgroup per canvas: the same
 // arithmetic as accept_kernel, renoise_kernel (stream 0) and stop_kernel run in that
 // order. Every position is handled by one thread (sub == 0), which reads only its own
-// x0, argmax and previous argmax after the acceptance's barrier.
+// x0, argmax and previous argmax. The draw and those reads do not depend on the
+// acceptance, so they are issued first, their latency and the draw's arithmetic
+// overlapping the read of the entropies.
 struct ArsArgs {
   int C, tpp, V, step, N;
   const float *ent;
@@ -341,23 +344,33 @@ struct ArsArgs {
 
 __global__ __launch_bounds__(1024) void accept_renoise_stop_kernel(ArsArgs a) {
   __shared__ ulonglong2 kq[1024];
+  __shared__ int sdraw[1024];
   __shared__ uint64_t ssum[16];
   __shared__ int sok[16];
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int pos = tid / a.tpp, sub = tid % a.tpp;
   const int64_t o = (int64_t)b * a.C + pos;
+  const bool own = pos < a.C && sub == 0;
+  const float h = pos < a.C ? a.ent[o] : 0.f;
+  int keep = 0, ok = 1;
+  if (own) {
+    keep = a.x0[o];
+    if (a.prev && a.am[o] != a.prev[o]) ok = 0;
+  }
+  // thread t draws for position t (whole waves busy), published through LDS; the
+  // acceptance's barrier orders it before the reads below
+  if (tid < a.C)
+    sdraw[tid] = uniform_token(tid, (uint32_t)a.step, 0ull, a.seed, a.canvas_base + (uint32_t)b, a.V);
   uint64_t q;
-  const bool take = accept_rank(a.C, a.tpp, pos, sub, a.ent + (int64_t)b * a.C, a.budget, kq, q);
+  const bool take = accept_rank(a.C, a.tpp, pos, sub, h, a.budget, kq, q);
   uint64_t s = 0;
-  int ok = 1;
-  if (pos < a.C && sub == 0) {
+  if (own) {
     a.acc[o] = take ? 1 : 0;
-    a.tok[o] = take ? a.x0[o] : uniform_token(pos, (uint32_t)a.step, 0ull, a.seed, a.canvas_base + (uint32_t)b, a.V);
+    a.tok[o] = take ? keep : sdraw[pos];
     // stop-test terms: q is ceil(h 2^32) for an entropy in the domain (as the stop
     // test sums it) and the sentinel for one outside it (which blocks the stop)
     if (q == Q_SENTINEL) ok = 0;
     else s = q;
-    if (a.prev && a.am[o] != a.prev[o]) ok = 0;
   }
   for (int off = 32; off > 0; off >>= 1) {           // integer sums: order-free
     s += __shfl_xor(s, off);
