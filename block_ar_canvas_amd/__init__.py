@@ -65,6 +65,15 @@ class LoopParams(ctypes.Structure):
                 ("canvas", ctypes.c_uint32)]
 
 
+class AcceptArgs(ctypes.Structure):
+    """dg_accept_args of dg_selfcond_accept."""
+    _fields_ = [("B", ctypes.c_int32), ("entropy", ctypes.c_void_p), ("b", ctypes.c_float),
+                ("x0", ctypes.c_void_p), ("argmax", ctypes.c_void_p), ("prev_argmax", ctypes.c_void_p),
+                ("seed", ctypes.c_uint64), ("canvas_base", ctypes.c_uint32), ("step", ctypes.c_int32),
+                ("thr", ctypes.c_float), ("N", ctypes.c_int32), ("accept", ctypes.c_void_p),
+                ("n_accept", ctypes.c_void_p), ("tokens", ctypes.c_void_p), ("flag", ctypes.c_void_p)]
+
+
 # dg_hidden_fn: (user, step) -> device pointer of H_step
 HIDDEN_FN = ctypes.CFUNCTYPE(ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32)
 
@@ -109,6 +118,7 @@ def _load():
         "dg_stop_test": (i32, [_P, i32, i32, _P, _P, _P, f32, i32, i32, _P]),
         "dg_accept_renoise_stop": (i32, [_P, i32, i32, i32, _P, f32, _P, _P, _P, u64, u32, i32, f32, i32,
                                          _P, _P, _P, _P]),
+        "dg_selfcond_accept": (i32, [_P, D, _P, _P, _P, _P, _P, ctypes.POINTER(AcceptArgs)]),
         "dg_commit_kv": (i32, [_P, D, _P, _P, _P, _P, _P, _P, i64, i64, ctypes.POINTER(i64)]),
         "dg_peak_stream_read": (i32, [_P, _P, ctypes.c_size_t, _P]),
         "dg_peak_mfma_bf16": (i32, [_P, i32, _P]),
@@ -317,6 +327,21 @@ class Context:
             int(canvas_base), int(step), float(thr), int(N), _ptr(accept, _U8, "accept"),
             _ptr(n_accept, _I32, "n_accept"), _ptr(tokens, _I32, "tokens"),
             _ptr(flag, _I32, "flag", pinned_ok=True)))
+
+    def selfcond_accept(self, dims, ws, E, W1, W2, z, entropy, b, x0, argmax, prev_argmax, seed,
+                        canvas_base, step, thr, N, accept, n_accept, tokens, flag):
+        """accept_renoise_stop then selfcond, same results; the acceptance work runs beside
+        self-conditioning's reduce. B canvases = the rows of entropy."""
+        d = Dims.of(dims)
+        B = 1 if entropy.dim() == 1 else entropy.shape[0]
+        a = AcceptArgs(int(B), _ptr(entropy, _F32, "entropy"), float(b), _ptr(x0, _I32, "x0"),
+                       _ptr(argmax, _I32, "argmax"), _ptr(prev_argmax, _I32, "prev_argmax", True), int(seed),
+                       int(canvas_base), int(step), float(thr), int(N), _ptr(accept, _U8, "accept"),
+                       _ptr(n_accept, _I32, "n_accept"), _ptr(tokens, _I32, "tokens"),
+                       _ptr(flag, _I32, "flag", pinned_ok=True))
+        self._check(self._lib.dg_selfcond_accept(
+            self._h, ctypes.byref(d), _ptr(ws, _U8, "ws"), _ptr(E, _BF16, "E"), _ptr(W1, _BF16, "W1"),
+            _ptr(W2, _BF16, "W2"), _ptr(z, _BF16, "z"), ctypes.byref(a)))
 
     def moe_ffn(self, md, X, Wr, W1, W2, W1s, W2s, ws, Y, n_active=None):
         C = X.shape[0]

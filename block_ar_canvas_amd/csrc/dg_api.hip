@@ -682,19 +682,12 @@ dg_status dg_renoise(dg_ctx ctx, int32_t B, int32_t C, int32_t V, const int32_t 
   return e == hipSuccess ? DG_OK : hip_fail(ctx, e, "dg_renoise");
 }
 
-dg_status dg_selfcond(dg_ctx ctx, const dg_dims *dims, void *ws, const dg_bf16 *E,
-                      const dg_bf16 *W1, const dg_bf16 *W2, dg_bf16 *z) {
-  DG_ENTER();
-  dg_status st = check_dims(ctx, dims, __func__);
-  if (st) return st;
-  DG_REQUIRE_PTR(ws);
-  DG_REQUIRE_PTR(E);
-  DG_REQUIRE_PTR(W1);
-  DG_REQUIRE_PTR(W2);
-  DG_REQUIRE_PTR(z);
-  const dg_dims &m = *dims;
-  if (!ctx->p0_valid || ctx->p0_ws != ws || memcmp(&ctx->p0_dims, &m, sizeof m) != 0)
-    return fail(ctx, DG_ERR_STATE, "%s: ws does not hold p0 of a dg_logits_entropy with these dims", __func__);
+namespace {
+
+// Self-conditioning after its arguments passed dg_selfcond's checks; with ars non-null the
+// reduce launch also runs acceptance, renoise and the stop test (ars->tpp * ars->C <= 256).
+dg_status selfcond_enqueue(dg_ctx ctx, const dg_dims &m, void *ws, const dg_bf16 *E, const dg_bf16 *W1,
+                           const dg_bf16 *W2, dg_bf16 *z, const ArsArgs *ars) {
   const DgWs w = dg_ws_layout(m.V, m.d, m.C, m.Hq, m.Hkv, m.hd, m.F, 0);
   SelfcondArgs a{};
   a.ptilde = ws_at<u16>(ws, w.ptilde);
@@ -711,7 +704,7 @@ dg_status dg_selfcond(dg_ctx ctx, const dg_dims *dims, void *ws, const dg_bf16 *
   a.nsc = w.nsc;
   a.ps = ws_at<float>(ws, w.ps);
   a.s = ws_at<u16>(ws, w.s);
-  hipError_t e = dg_launch_selfcond(a, ctx->stream);
+  hipError_t e = dg_launch_selfcond(a, ars, ctx->stream);
   if (e != hipSuccess) return hip_fail(ctx, e, "dg_selfcond(p0 E)");
 
   u16 *gbuf = ws_at<u16>(ws, w.g);
@@ -735,6 +728,24 @@ dg_status dg_selfcond(dg_ctx ctx, const dg_dims *dims, void *ws, const dg_bf16 *
   return DG_OK;
 }
 
+}  // namespace
+
+dg_status dg_selfcond(dg_ctx ctx, const dg_dims *dims, void *ws, const dg_bf16 *E,
+                      const dg_bf16 *W1, const dg_bf16 *W2, dg_bf16 *z) {
+  DG_ENTER();
+  dg_status st = check_dims(ctx, dims, __func__);
+  if (st) return st;
+  DG_REQUIRE_PTR(ws);
+  DG_REQUIRE_PTR(E);
+  DG_REQUIRE_PTR(W1);
+  DG_REQUIRE_PTR(W2);
+  DG_REQUIRE_PTR(z);
+  const dg_dims &m = *dims;
+  if (!ctx->p0_valid || ctx->p0_ws != ws || memcmp(&ctx->p0_dims, &m, sizeof m) != 0)
+    return fail(ctx, DG_ERR_STATE, "%s: ws does not hold p0 of a dg_logits_entropy with these dims", __func__);
+  return selfcond_enqueue(ctx, m, ws, E, W1, W2, z, nullptr);
+}
+
 dg_status dg_stop_test(dg_ctx ctx, int32_t B, int32_t C, const float *entropy,
                        const int32_t *argmax, const int32_t *prev_argmax, float thr, int32_t step,
                        int32_t N, int32_t *flag) {
@@ -748,25 +759,91 @@ dg_status dg_stop_test(dg_ctx ctx, int32_t B, int32_t C, const float *entropy,
   return e == hipSuccess ? DG_OK : hip_fail(ctx, e, "dg_stop_test");
 }
 
+namespace {
+
+// The checks of dg_accept_renoise_stop; fills r (tpp left 0) when they pass.
+dg_status check_ars(dg_ctx ctx, int32_t B, int32_t C, int32_t V, const float *entropy, float b,
+                    const int32_t *x0, const int32_t *argmax, const int32_t *prev_argmax, uint64_t seed,
+                    uint32_t canvas_base, int32_t step, float thr, int32_t N, uint8_t *accept,
+                    int32_t *n_accept, int32_t *tokens, int32_t *flag, const char *fn, ArsArgs &r) {
+  if (B < 1 || C < 1 || C > 1024 || V < 1)
+    return fail(ctx, DG_ERR_SHAPE, "%s: need B, V >= 1 and 1 <= C <= 1024", fn);
+  if (!entropy || !x0 || !argmax || !accept || !n_accept || !tokens || !flag)
+    return fail(ctx, DG_ERR_NULL, "%s: NULL buffer", fn);
+  if (!(b >= 0.f && b < 65536.f)) return fail(ctx, DG_ERR_RANGE, "%s: b=%g must be in [0, 65536)", fn, b);
+  if (!(thr >= 0.f && thr < 65536.f)) return fail(ctx, DG_ERR_RANGE, "%s: thr=%g must be in [0, 65536)", fn, thr);
+  if (step < 0 || N < 1) return fail(ctx, DG_ERR_RANGE, "%s: need step >= 0, N >= 1", fn);
+  r = ArsArgs{};
+  r.B = B;
+  r.C = C;
+  r.V = V;
+  r.step = step;
+  r.N = N;
+  r.ent = entropy;
+  r.x0 = x0;
+  r.am = argmax;
+  r.prev = prev_argmax;
+  r.budget = (uint64_t)floor((double)b * 4294967296.0);
+  r.limit = (uint64_t)floor((double)thr * (double)C * 4294967296.0);
+  r.seed = seed;
+  r.canvas_base = canvas_base;
+  r.acc = accept;
+  r.nacc = n_accept;
+  r.tok = tokens;
+  r.flag = flag;
+  return DG_OK;
+}
+
+hipError_t launch_ars(const ArsArgs &r, hipStream_t st) {
+  return dg_launch_accept_renoise_stop(r.B, r.C, r.V, r.ent, r.budget, r.x0, r.am, r.prev, r.seed, r.canvas_base,
+                                       r.step, r.limit, r.N, r.acc, r.nacc, r.tok, r.flag, st);
+}
+
+}  // namespace
+
 dg_status dg_accept_renoise_stop(dg_ctx ctx, int32_t B, int32_t C, int32_t V, const float *entropy,
                                  float b, const int32_t *x0, const int32_t *argmax,
                                  const int32_t *prev_argmax, uint64_t seed, uint32_t canvas_base,
                                  int32_t step, float thr, int32_t N, uint8_t *accept,
                                  int32_t *n_accept, int32_t *tokens, int32_t *flag) {
   DG_ENTER();
-  if (B < 1 || C < 1 || C > 1024 || V < 1)
-    return fail(ctx, DG_ERR_SHAPE, "%s: need B, V >= 1 and 1 <= C <= 1024", __func__);
-  if (!entropy || !x0 || !argmax || !accept || !n_accept || !tokens || !flag)
-    return fail(ctx, DG_ERR_NULL, "%s: NULL buffer", __func__);
-  if (!(b >= 0.f && b < 65536.f)) return fail(ctx, DG_ERR_RANGE, "%s: b=%g must be in [0, 65536)", __func__, b);
-  if (!(thr >= 0.f && thr < 65536.f)) return fail(ctx, DG_ERR_RANGE, "%s: thr=%g must be in [0, 65536)", __func__, thr);
-  if (step < 0 || N < 1) return fail(ctx, DG_ERR_RANGE, "%s: need step >= 0, N >= 1", __func__);
-  const uint64_t budget = (uint64_t)floor((double)b * 4294967296.0);
-  const uint64_t limit = (uint64_t)floor((double)thr * (double)C * 4294967296.0);
-  hipError_t e = dg_launch_accept_renoise_stop(B, C, V, entropy, budget, x0, argmax, prev_argmax, seed,
-                                               canvas_base, step, limit, N, accept, n_accept, tokens, flag,
-                                               ctx->stream);
+  ArsArgs r;
+  dg_status st = check_ars(ctx, B, C, V, entropy, b, x0, argmax, prev_argmax, seed, canvas_base, step, thr, N,
+                           accept, n_accept, tokens, flag, __func__, r);
+  if (st) return st;
+  hipError_t e = launch_ars(r, ctx->stream);
   return e == hipSuccess ? DG_OK : hip_fail(ctx, e, __func__);
+}
+
+dg_status dg_selfcond_accept(dg_ctx ctx, const dg_dims *dims, void *ws, const dg_bf16 *E,
+                             const dg_bf16 *W1, const dg_bf16 *W2, dg_bf16 *z,
+                             const dg_accept_args *acc) {
+  DG_ENTER();
+  dg_status st = check_dims(ctx, dims, __func__);
+  if (st) return st;
+  DG_REQUIRE_PTR(ws);
+  DG_REQUIRE_PTR(E);
+  DG_REQUIRE_PTR(W1);
+  DG_REQUIRE_PTR(W2);
+  DG_REQUIRE_PTR(z);
+  DG_REQUIRE_PTR(acc);
+  const dg_dims &m = *dims;
+  if (!ctx->p0_valid || ctx->p0_ws != ws || memcmp(&ctx->p0_dims, &m, sizeof m) != 0)
+    return fail(ctx, DG_ERR_STATE, "%s: ws does not hold p0 of a dg_logits_entropy with these dims", __func__);
+  if (acc->B < 1 || m.C % acc->B != 0)
+    return fail(ctx, DG_ERR_SHAPE, "%s: B=%d must divide C=%d", __func__, (int)acc->B, (int)m.C);
+  ArsArgs r;
+  if ((st = check_ars(ctx, acc->B, m.C / acc->B, m.V, acc->entropy, acc->b, acc->x0, acc->argmax,
+                      acc->prev_argmax, acc->seed, acc->canvas_base, acc->step, acc->thr, acc->N, acc->accept,
+                      acc->n_accept, acc->tokens, acc->flag, __func__, r)))
+    return st;
+  if (r.C <= 256) {                                  // one reduce workgroup (256 threads) per canvas
+    r.tpp = r.C <= 64 ? 4 : r.C <= 128 ? 2 : 1;
+    return selfcond_enqueue(ctx, m, ws, E, W1, W2, z, &r);
+  }
+  hipError_t e = launch_ars(r, ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, __func__);
+  return selfcond_enqueue(ctx, m, ws, E, W1, W2, z, nullptr);
 }
 
 dg_status dg_commit_kv(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens, const dg_bf16 *E,
@@ -922,10 +999,23 @@ dg_status dg_run_canvas(dg_ctx ctx, const dg_dims *dims, const dg_weights *w, dg
     const int sl = (int)(ctx->flag_seq++ % 4);
     slot[k & 1] = sl;
     ctx->host_flags[sl] = -1;
-    r = dg_accept_renoise_stop(ctx, 1, m.C, m.V, ent, prm->b, a, a, prev, prm->seed, prm->canvas, k,
-                               prm->thr, N, acc, nacc, tok, ctx->host_flags + sl);
-    if (!r) r = dg_selfcond(ctx, dims, ws, E, W1, W2, z);
-    return r;
+    dg_accept_args aa{};
+    aa.B = 1;
+    aa.entropy = ent;
+    aa.b = prm->b;
+    aa.x0 = a;
+    aa.argmax = a;
+    aa.prev_argmax = prev;
+    aa.seed = prm->seed;
+    aa.canvas_base = prm->canvas;
+    aa.step = k;
+    aa.thr = prm->thr;
+    aa.N = N;
+    aa.accept = acc;
+    aa.n_accept = nacc;
+    aa.tokens = tok;
+    aa.flag = ctx->host_flags + sl;
+    return dg_selfcond_accept(ctx, dims, ws, E, W1, W2, z, &aa);
   };
 
   if ((st = step(0))) return st;

@@ -420,6 +420,17 @@ struct LogitsArgs {
 };
 hipError_t dg_launch_logits(const LogitsArgs &a, hipStream_t st);
 
+// Acceptance, renoise and stop test of B canvases of C positions (see dg_sampler_dev.h).
+struct ArsArgs {
+  int B, C, tpp, V, step, N;
+  const float *ent;
+  const int *x0, *am, *prev;
+  uint64_t budget, limit, seed;
+  uint32_t canvas_base;
+  uint8_t *acc;
+  int *nacc, *tok, *flag;
+};
+
 struct SelfcondArgs {
   const u16 *ptilde;
   const float *trho;   // [Cpad][T] tile references
@@ -430,7 +441,9 @@ struct SelfcondArgs {
   float *ps;           // [nsc][d][Cpad]
   u16 *s;              // [Cpad][d]
 };
-hipError_t dg_launch_selfcond(const SelfcondArgs &a, hipStream_t st);
+// With ars non-null (ars->tpp * ars->C <= 256), acceptance, renoise and the stop test of
+// ars->B canvases run as extra workgroups of the reduce launch.
+hipError_t dg_launch_selfcond(const SelfcondArgs &a, const ArsArgs *ars, hipStream_t st);
 
 hipError_t dg_launch_accept(int B, int C, const float *ent, uint64_t budget, uint8_t *acc,
                             int *nacc, hipStream_t st);

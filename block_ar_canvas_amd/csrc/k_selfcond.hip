@@ -24,7 +24,7 @@
 // MFMA operands: A = E^T (j rows, vocabulary k) via two ds_read_b64_tr_b16 transposing
 // reads per fragment; B = p~ (canvas columns) via linear 16-byte reads. Each wave owns
 // 128 j x 64 canvas (4 x 2 MFMA tiles, 128 accumulators, two waves per SIMD).
-#include "dg_common.h"
+#include "dg_sampler_dev.h"
 
 namespace {
 
@@ -254,7 +254,17 @@ __global__ __launch_bounds__(512) void selfcond_split_kernel(SelfcondArgs a, int
 // the bf16 result is transposed through LDS and written along j. Splits are taken 32
 // at a time; a chunk's 32 partial loads are issued together, ahead of the scale
 // computation, so each chunk costs one memory round trip.
-__global__ __launch_bounds__(256) void selfcond_reduce_kernel(SelfcondArgs a) {
+//
+// With ars.B > 0 the rows of workgroups past ny run acceptance, renoise and the stop
+// test of canvas (blockIdx.y - ny) * gridDim.x + blockIdx.x instead (those with a
+// canvas index past ars.B exit at once): that work needs only the sampler head's
+// outputs, so it overlaps the reduce instead of taking a launch of its own.
+__global__ __launch_bounds__(256) void selfcond_reduce_kernel(SelfcondArgs a, ArsArgs ars, int ny) {
+  if ((int)blockIdx.y >= ny) {
+    const int cb = ((int)blockIdx.y - ny) * (int)gridDim.x + (int)blockIdx.x;
+    if (cb < ars.B) dgs::ars_canvas(ars, cb);
+    return;
+  }
   constexpr int PC = 32;                             // splits per chunk
   __shared__ float scale[64 * (PC + 1)];             // [c][split in chunk]
   __shared__ u16 out[64][24];
@@ -315,7 +325,7 @@ __global__ __launch_bounds__(256) void selfcond_reduce_kernel(SelfcondArgs a) {
 
 }  // namespace
 
-hipError_t dg_launch_selfcond(const SelfcondArgs &a, hipStream_t st) {
+hipError_t dg_launch_selfcond(const SelfcondArgs &a, const ArsArgs *ars, hipStream_t st) {
   static std::atomic<bool> attr[DG_MAX_DEVICES];
   hipError_t e = dg_smem_attr_once(attr, SMEM, {(const void *)selfcond_split_kernel});
   if (e != hipSuccess) return e;
@@ -324,6 +334,13 @@ hipError_t dg_launch_selfcond(const SelfcondArgs &a, hipStream_t st) {
                      SMEM, st, a, nj);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(selfcond_reduce_kernel, dim3((a.d + 15) / 16, (a.Cpad + 63) / 64), dim3(256), 0, st, a);
+  const int nx = (a.d + 15) / 16, ny = (a.Cpad + 63) / 64;
+  ArsArgs r{};
+  int rows = 0;
+  if (ars) {                                         // ars->tpp * ars->C <= 256 (caller)
+    r = *ars;
+    rows = (r.B + nx - 1) / nx;
+  }
+  hipLaunchKernelGGL(selfcond_reduce_kernel, dim3(nx, ny + rows), dim3(256), 0, st, a, r, ny);
   return hipGetLastError();
 }

@@ -3,10 +3,10 @@
 The loop follows the DiffusionGemma inference steps (Technical Report page, "Method
 steps" (2)-(5); tutorial chapter "DiffusionGemma", data-flow pseudocode): initialize
 a canvas with uniform tokens and z = 0, run at most N denoise steps (attention,
-sampler head, acceptance, renoise, stop test, self-conditioning; the stop test reads
-only the entropies and argmaxes, so it runs before self-conditioning, and under the
-entropy rule acceptance, renoise and the stop test are one launch), then commit the
-finalized block x0 = argmax to the KV cache and start the next canvas.
+sampler head, acceptance, renoise, stop test, self-conditioning; under the entropy rule
+acceptance, renoise and the stop test run beside self-conditioning's reduce, since they
+read only the sampler head's entropies and argmaxes), then commit the finalized block
+x0 = argmax to the KV cache and start the next canvas.
 
 This module only sequences calls and owns the device buffers of one canvas; every
 step of the arithmetic is a libdg kernel. The sampler head reads hidden states from
@@ -112,15 +112,17 @@ class CanvasLoop:
             self.ctx.topk_accept(self.conf, reveal_count(dm.C, self.N, k), self.accept, self.n_accept)
             self.ctx.renoise(dm.V, x0, self.accept, self.seed, self.canvas, k, self.tokens)
             self.ctx.stop_test(self.entropy, am, prev, self.thr, k, self.N, self.flags[slot])
-        else:
-            self.ctx.accept_renoise_stop(dm.V, self.entropy, self.b, x0, am, prev, self.seed, self.canvas,
-                                         k, self.thr, self.N, self.accept, self.n_accept, self.tokens,
-                                         self.flags[slot])
         sev = self.selfcond_events
         if sev is not None:
             s0 = torch.cuda.Event(enable_timing=True)
             s0.record(self.ctx.torch_stream())
-        self.ctx.selfcond(dm, self.ws, W["E"], W["W1"], W["W2"], self.z)
+        if self.rule == "confidence":
+            self.ctx.selfcond(dm, self.ws, W["E"], W["W1"], W["W2"], self.z)
+        else:
+            # acceptance, renoise and the stop test run beside self-conditioning's reduce
+            self.ctx.selfcond_accept(dm, self.ws, W["E"], W["W1"], W["W2"], self.z, self.entropy, self.b, x0,
+                                     am, prev, self.seed, self.canvas, k, self.thr, self.N, self.accept,
+                                     self.n_accept, self.tokens, self.flags[slot])
         if sev is not None:
             s1 = torch.cuda.Event(enable_timing=True)
             s1.record(self.ctx.torch_stream())
@@ -293,11 +295,11 @@ class BatchLoop:
             self.ctx.topk_accept(self.conf, reveal_count(dm.C, self.N, k), self.accept, self.n_accept)
             self.ctx.renoise(dm.V, x0, self.accept, self.seed, base, k, self.tokens)
             self.ctx.stop_test(self.entropy, am, prev, self.thr, k, self.N, self.flags[slot])
+            self.ctx.selfcond(self.dims_all, self.ws, W["E"], W["W1"], W["W2"], self.z.view(-1, dm.d))
         else:
-            self.ctx.accept_renoise_stop(dm.V, self.entropy, self.b, x0, am, prev, self.seed, base, k,
-                                         self.thr, self.N, self.accept, self.n_accept, self.tokens,
-                                         self.flags[slot])
-        self.ctx.selfcond(self.dims_all, self.ws, W["E"], W["W1"], W["W2"], self.z.view(-1, dm.d))
+            self.ctx.selfcond_accept(self.dims_all, self.ws, W["E"], W["W1"], W["W2"], self.z.view(-1, dm.d),
+                                     self.entropy, self.b, x0, am, prev, self.seed, base, k, self.thr, self.N,
+                                     self.accept, self.n_accept, self.tokens, self.flags[slot])
         return am
 
     def wait_flags(self, k: int, timeout_s: float = 60.0):

@@ -10,7 +10,8 @@
  *   dg_selfcond        self-conditioning z = FFW(p0 . E)
  *   dg_stop_test       adaptive stop (mean entropy and stable argmax) / step cap
  * and, once per canvas, dg_commit_kv appends the finalized block to the KV cache.
- * dg_accept_renoise_stop runs acceptance, renoise and the stop test in one launch.
+ * dg_accept_renoise_stop runs acceptance, renoise and the stop test in one launch, and
+ * dg_selfcond_accept runs them beside self-conditioning's reduce.
  * Beyond that step: dg_prefill_block (the causal re-encode commit) with dg_set_rope,
  * dg_confidence / dg_topk_accept / dg_reveal_count (confidence-ranked acceptance),
  * dg_sample (sampled tokens), dg_moe_ffn (the canvas mixture-of-experts FFN),
@@ -256,6 +257,36 @@ dg_status dg_accept_renoise_stop(dg_ctx ctx, int32_t B, int32_t C, int32_t V,
                                  int32_t N, uint8_t *accept, int32_t *n_accept,
                                  int32_t *tokens, int32_t *flag);
 
+/* dg_accept_renoise_stop and dg_selfcond of one step in one call, with the results of
+ *   dg_accept_renoise_stop(B, C / B, V, entropy, b, x0, argmax, prev_argmax, seed,
+ *                          canvas_base, step, thr, N, accept, n_accept, tokens, flag);
+ *   dg_selfcond(dims, ws, E, W1, W2, z);
+ * bit for bit (C and V from dims; the other arguments from *acc). For canvases of up to
+ * 256 positions the acceptance work runs as extra workgroups of the self-conditioning
+ * reduce launch, beside the reduce, instead of in a launch of its own; the stop flag is
+ * then written while s is reduced. Larger canvases take a launch of its own first.
+ * accept, n_accept, tokens and flag must not overlap ws or z. Errors: those of both
+ * calls, checked before anything is enqueued; DG_ERR_SHAPE unless B >= 1 divides C. */
+typedef struct {
+  int32_t B;                 /* canvases; dims->C / B positions each */
+  const float *entropy;      /* [B, C/B] */
+  float b;                   /* acceptance budget */
+  const int32_t *x0;         /* what accepted positions keep */
+  const int32_t *argmax, *prev_argmax;  /* compared by the stop test; prev may be NULL */
+  uint64_t seed;
+  uint32_t canvas_base;
+  int32_t step;
+  float thr;                 /* stop threshold */
+  int32_t N;                 /* step cap */
+  uint8_t *accept;           /* [B, C/B] output */
+  int32_t *n_accept;         /* [B] output */
+  int32_t *tokens;           /* [B, C/B] output */
+  int32_t *flag;             /* [B] output, device or pinned host memory */
+} dg_accept_args;
+dg_status dg_selfcond_accept(dg_ctx ctx, const dg_dims *dims, void *ws, const dg_bf16 *E,
+                             const dg_bf16 *W1, const dg_bf16 *W2, dg_bf16 *z,
+                             const dg_accept_args *acc);
+
 /* Rotary positions (openai-hub page "从零拆开DiffusionGemma", closing remarks of step 3:
  * the full model has rotary position encoding) for dg_canvas_attn and dg_prefill_block
  * of this context: base 0 (the default) turns them off; base > 0 rotates, in every head,
@@ -317,8 +348,8 @@ dg_status dg_commit_kv(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens,
  * the library: a uniform random canvas (dg_renoise with accept = NULL), then denoise
  * steps k = 0, 1, ... of
  *   dg_canvas_attn (z = 0 at k = 0), dg_logits_entropy on H_k at dg_temperature(k, N,
- *   tau0, tau1), dg_accept_renoise_stop (acceptance with budget b, renoise of the
- *   rejected positions, the stop test against the previous step's argmax), dg_selfcond,
+ *   tau0, tau1), dg_selfcond_accept (acceptance with budget b, renoise of the rejected
+ *   positions, the stop test against the previous step's argmax, self-conditioning),
  * until the stop test fires or the cap N is reached, then dg_commit_kv of that step's
  * argmax. Step k + 1 is enqueued before the host waits for step k's flag (pinned host
  * memory of the context, polled: no stream synchronization between steps); when step k

@@ -364,6 +364,88 @@ def test_accept_renoise_stop_refusals(dg_ctx):
     assert int(tok.min().item()) == -1 and int(flag.item()) == -1
 
 
+# (shape, canvases B): up to 256 positions per canvas the acceptance work runs beside the
+# reduce (tiny, ragged, hd64, small, wide_tail; ragged as 4 canvases of 25 and wide as 3
+# of 100); c1000 and wide (300 positions) take a launch of their own
+SELFCOND_ACCEPT = [("tiny", 1), ("ragged", 1), ("ragged", 4), ("hd64", 1), ("small", 1), ("wide_tail", 1),
+                   ("wide", 3), ("wide", 1), ("c1000", 1)]
+
+
+@pytest.mark.parametrize("name,B", SELFCOND_ACCEPT, ids=[f"{n}-B{b}" for n, b in SELFCOND_ACCEPT])
+def test_selfcond_accept_matches_the_separate_calls(dg_ctx, name, B):
+    """dg_selfcond_accept against dg_accept_renoise_stop followed by dg_selfcond on the same
+    sampler-head outputs, bit for bit: z, acceptance, tokens, counts and flags (a stop that
+    fires at the last step, where the argmax is unchanged, and one that cannot)."""
+    cfg, W, Kp, Vp, Pcap, Wd = setup(name)
+    tgt = di.targets(cfg, 0)
+    k = cfg.N - 1
+    H = bf16_dev(di.hidden(cfg, W["E"], 0, k, tgt))
+    tau = O.temperature(k, cfg.N)
+    Cs = cfg.C // B
+    rng = np.random.default_rng(7 + B)
+    x0 = i32_dev(rng.integers(0, cfg.V, (B, Cs)).astype(np.int32))
+    outs = []
+    for fused in (False, True):
+        ws = ws_for(cfg, Pcap)
+        ent = torch.empty(B, Cs, dtype=torch.float32, device=DEV)
+        am = torch.empty(B, Cs, dtype=torch.int32, device=DEV)
+        dg_ctx.logits_entropy(cfg, H, Wd["E"], tau, ws, ent.view(-1), am.view(-1))
+        z = torch.full((cfg.C, cfg.d), -1.0, dtype=torch.bfloat16, device=DEV)
+        acc = torch.full((B, Cs), 7, dtype=torch.uint8, device=DEV)
+        n = torch.full((B,), -5, dtype=torch.int32, device=DEV)
+        tok = torch.full((B, Cs), -1, dtype=torch.int32, device=DEV)
+        flag = torch.full((B,), -1, dtype=torch.int32, device=DEV)
+        # prev = argmax: the stop fires wherever the mean entropy is under the threshold
+        args = (0.1, x0, am, am.clone(), 2 ** 62 + 3, 5, k, 10.0, cfg.N, acc, n, tok, flag)
+        if fused:
+            dg_ctx.selfcond_accept(cfg, ws, Wd["E"], Wd["W1"], Wd["W2"], z, ent, *args)
+        else:
+            dg_ctx.accept_renoise_stop(cfg.V, ent, *args)
+            dg_ctx.selfcond(cfg, ws, Wd["E"], Wd["W1"], Wd["W2"], z)
+        dg_ctx.sync()
+        outs.append((bits_np(z).copy(), acc.cpu().numpy(), n.cpu().numpy(), tok.cpu().numpy(), flag.cpu().numpy()))
+        e = ent.cpu().numpy()
+    assert int((outs[1][3] < 0).sum()) == 0
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(a, b)
+    # the flags themselves against the oracle's stop test on the same entropies
+    am_np = am.cpu().numpy()
+    np.testing.assert_array_equal(outs[1][4], O.stop_test(e, am_np, am_np, 10.0, k, cfg.N))
+
+
+def test_selfcond_accept_refusals(dg_ctx):
+    cfg, W, Kp, Vp, Pcap, Wd = setup("ragged")
+    ws = ws_for(cfg, Pcap)
+    H = bf16_dev(di.hidden(cfg, W["E"], 0, 0, di.targets(cfg, 0)))
+    ent = torch.empty(cfg.C, dtype=torch.float32, device=DEV)
+    am = torch.empty(cfg.C, dtype=torch.int32, device=DEV)
+    dg_ctx.logits_entropy(cfg, H, Wd["E"], 0.8, ws, ent, am)
+    z = torch.full((cfg.C, cfg.d), 1.0, dtype=torch.bfloat16, device=DEV)
+    acc = torch.empty(cfg.C, dtype=torch.uint8, device=DEV)
+    n = torch.empty(1, dtype=torch.int32, device=DEV)
+    tok = torch.full((cfg.C,), -1, dtype=torch.int32, device=DEV)
+    flag = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    # 3 canvases do not divide C = 100
+    with pytest.raises(dg.DGError) as ei:
+        dg_ctx.selfcond_accept(cfg, ws, Wd["E"], Wd["W1"], Wd["W2"], z, ent.view(1, -1).expand(3, -1).contiguous(),
+                               0.1, am, am, None, 1, 0, 0, 0.005, 4, acc, n, tok, flag)
+    assert ei.value.name == "DG_ERR_SHAPE"
+    for kw, err in (({"b": -1.0}, "DG_ERR_RANGE"), ({"N": 0}, "DG_ERR_RANGE"), ({"step": -2}, "DG_ERR_RANGE")):
+        a = {"b": 0.1, "N": 4, "step": 0, **kw}
+        with pytest.raises(dg.DGError) as ei:
+            dg_ctx.selfcond_accept(cfg, ws, Wd["E"], Wd["W1"], Wd["W2"], z, ent, a["b"], am, am, None, 1, 0,
+                                   a["step"], 0.005, a["N"], acc, n, tok, flag)
+        assert ei.value.name == err
+    # a workspace without the sampler head's p0
+    with pytest.raises(dg.DGError) as ei:
+        dg_ctx.selfcond_accept(cfg, ws_for(cfg, Pcap), Wd["E"], Wd["W1"], Wd["W2"], z, ent, 0.1, am, am, None, 1,
+                               0, 0, 0.005, 4, acc, n, tok, flag)
+    assert ei.value.name == "DG_ERR_STATE"
+    dg_ctx.sync()
+    assert int(tok.min().item()) == -1 and int(flag.item()) == -1
+    assert bool((z == 1.0).all().item())
+
+
 def test_stop_flag_in_pinned_host_memory(dg_ctx):
     """The stop kernel's system-scope store reaches a pinned host flag without any copy:
     pre-filled with -1, the flag is polled until it changes, and it must equal both the
