@@ -254,22 +254,22 @@ __global__ __launch_bounds__(512) void selfcond_split_kernel(SelfcondArgs a, int
 // the bf16 result is transposed through LDS and written along j. Splits are taken 32
 // at a time; a chunk's 32 partial loads are issued together, ahead of the scale
 // computation, so each chunk costs one memory round trip.
-//
-// With ars.B > 0 the rows of workgroups past ny run acceptance, renoise and the stop
-// test of canvas (blockIdx.y - ny) * gridDim.x + blockIdx.x instead (those with a
-// canvas index past ars.B exit at once): that work needs only the sampler head's
-// outputs, so it overlaps the reduce instead of taking a launch of its own.
-__global__ __launch_bounds__(256) void selfcond_reduce_kernel(SelfcondArgs a, ArsArgs ars, int ny) {
-  if ((int)blockIdx.y >= ny) {
-    const int cb = ((int)blockIdx.y - ny) * (int)gridDim.x + (int)blockIdx.x;
-    if (cb < ars.B) dgs::ars_canvas(ars, cb);
+// The grid is one-dimensional: ars.B workgroups first, then nx x ny reduce workgroups
+// in row order (j fastest). The first ars.B run acceptance, renoise and the stop test of
+// canvas blockIdx.x instead: that work needs only the sampler head's outputs, so it
+// overlaps the reduce instead of taking a launch of its own, and it comes first in
+// dispatch order so that it starts at once even when the reduce fills every CU slot.
+__global__ __launch_bounds__(256) void selfcond_reduce_kernel(SelfcondArgs a, ArsArgs ars, int nx) {
+  if ((int)blockIdx.x < ars.B) {
+    dgs::ars_canvas(ars, blockIdx.x);
     return;
   }
+  const int wg = (int)blockIdx.x - ars.B, bx = wg % nx, by = wg / nx;
   constexpr int PC = 32;                             // splits per chunk
   __shared__ float scale[64 * (PC + 1)];             // [c][split in chunk]
   __shared__ u16 out[64][24];
   const int tid = threadIdx.x;
-  const int j0 = blockIdx.x * 16, c0 = blockIdx.y * 64;
+  const int j0 = bx * 16, c0 = by * 64;
   const int jj = tid >> 4, c4 = (tid & 15) * 4;
   const int j = j0 + jj;
   const bool live = j < a.d && c0 + c4 < a.Cpad;
@@ -335,12 +335,8 @@ hipError_t dg_launch_selfcond(const SelfcondArgs &a, const ArsArgs *ars, hipStre
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nx = (a.d + 15) / 16, ny = (a.Cpad + 63) / 64;
-  ArsArgs r{};
-  int rows = 0;
-  if (ars) {                                         // ars->tpp * ars->C <= 256 (caller)
-    r = *ars;
-    rows = (r.B + nx - 1) / nx;
-  }
-  hipLaunchKernelGGL(selfcond_reduce_kernel, dim3(nx, ny + rows), dim3(256), 0, st, a, r, ny);
+  ArsArgs r{};                                       // r.B = 0: no acceptance workgroups
+  if (ars) r = *ars;                                 // ars->tpp * ars->C <= 256 (caller)
+  hipLaunchKernelGGL(selfcond_reduce_kernel, dim3(r.B + nx * ny), dim3(256), 0, st, a, r, nx);
   return hipGetLastError();
 }
