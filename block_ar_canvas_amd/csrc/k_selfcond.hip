@@ -7,7 +7,8 @@
 // product as slow in plain framework code; here it is one split-K MFMA pass over E.
 //
 // selfcond_split_kernel computes s^T[j][c] = sum_v E[v][j] p~[c][v] 2^-n(t,c) for a
-// 256-wide slice of the model width j, up to 256 canvas columns c and one split S (a
+// 256-wide slice of the model width j, a block of BC = 256 (or 128) canvas columns c
+// and one split S (a
 // contiguous range of 256-row vocabulary tiles t). p~ holds bf16 2^(x - rho_t) from the
 // logits epilogue; n(t, c) = rho_S - rho_t is an integer, so the rescale to the split's
 // common reference is an exact exponent shift, applied to the bf16 fragments with packed
@@ -23,17 +24,21 @@
 //   p~ fragments, copied as the 1 KiB blocks the logits epilogue wrote.
 // MFMA operands: A = E^T (j rows, vocabulary k) via two ds_read_b64_tr_b16 transposing
 // reads per fragment; B = p~ (canvas columns) via linear 16-byte reads. Each wave owns
-// 128 j x 64 canvas (4 x 2 MFMA tiles, 128 accumulators, two waves per SIMD).
+// 128 j x BC/4 canvas (4 x BC/128 MFMA tiles, up to 128 accumulators, two waves per
+// SIMD). Every output element sums its split's vocabulary rows in stage order whatever
+// BC is, so both block widths give the same bits; 128-column blocks double the
+// workgroups where 256-column ones would leave CUs idle (a short vocabulary).
 #include "dg_sampler_dev.h"
 
 namespace {
 
-constexpr int BJ = 256, BC = 256, BKV = 32, NS = 4;
+constexpr int BJ = 256, BKV = 32, NS = 4;
 constexpr int ESTAGE = BKV * BJ * 2;           // 16 KiB
-constexpr int PSTAGE = 8 * 2 * 1024;           // 16 KiB: 8 canvas tiles x 2 k-steps
-constexpr int STAGE = ESTAGE + PSTAGE;
 constexpr int NTAB_MAX = 32 * 1024;            // LDS bytes for the split's shift table
-constexpr int SMEM = NS * STAGE + NTAB_MAX;    // 160 KiB
+// p~ stage: BC/32 canvas tiles x 2 k-steps of 1 KiB; SMEM 160 KiB (BC 256) or 128 KiB
+template <int BC> constexpr int pstage() { return BC / 32 * 2 * 1024; }
+template <int BC> constexpr int stage() { return ESTAGE + pstage<BC>(); }
+template <int BC> constexpr int smem_bytes() { return NS * stage<BC>() + NTAB_MAX; }
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef short v2i16_t __attribute__((ext_vector_type(2)));
@@ -51,9 +56,15 @@ DG_DEV uint32_t shift2(uint32_t w, v2i16_t dn) {
   return __builtin_bit_cast(uint32_t, x);
 }
 
+template <int BC>
 __global__ __launch_bounds__(512) void selfcond_split_kernel(SelfcondArgs a, int nj) {
+  static_assert(BC == 128 || BC == 256, "canvas block");
+  constexpr int STAGE = stage<BC>();
+  constexpr int CTW = BC / 128;                   // canvas tiles per wave
+  constexpr int PQ = BC / 128;                    // p~ copy instructions per wave and stage
+  constexpr int CPS = 2 + PQ;                     // copies per wave and stage
   extern __shared__ __attribute__((aligned(1024))) char smem[];
-  unsigned char *ntab = (unsigned char *)(smem + NS * STAGE);   // [tile in split][256 columns]
+  unsigned char *ntab = (unsigned char *)(smem + NS * STAGE);   // [tile in split][BC columns]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -86,10 +97,11 @@ __global__ __launch_bounds__(512) void selfcond_split_kernel(SelfcondArgs a, int
   const int vbeg = tile0 * DG_BV;
   const int NIT = (tile1 - tile0) * (DG_BV / BKV);
 
-  // Copy duties per stage (2 E and 2 p~ instructions per wave). E instruction `ins`
-  // fills stage rows 2*ins and 2*ins + 1 (32 lanes per 512-byte row segment).
+  // Copy duties per stage (2 E and PQ p~ instructions per wave). E instruction `ins`
+  // fills stage rows 2*ins and 2*ins + 1 (32 lanes per 512-byte row segment); p~
+  // instruction `pin` copies k-step pin & 1 of canvas tile pin >> 1.
   int erow[2], ecol[2];
-  const u16 *gp[2];
+  const u16 *gp[PQ];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int ins = wave * 2 + q;                   // 0..15
@@ -99,9 +111,13 @@ __global__ __launch_bounds__(512) void selfcond_split_kernel(SelfcondArgs a, int
     jc = jc < a.d ? jc : a.d - 8;                    // clamp: columns past d never stored
     erow[q] = v;
     ecol[q] = jc;
-    int ctile = ct0 + (ins >> 1);
+  }
+#pragma unroll
+  for (int q = 0; q < PQ; ++q) {
+    const int pin = wave * PQ + q;                  // 0 .. BC/16 - 1
+    int ctile = ct0 + (pin >> 1);
     ctile = ctile < nct ? ctile : nct - 1;           // clamp: columns never stored
-    gp[q] = a.ptilde + (((int64_t)ctile * VS + vbeg / 16 + (ins & 1)) * 64 + lane) * 8;
+    gp[q] = a.ptilde + (((int64_t)ctile * VS + vbeg / 16 + (pin & 1)) * 64 + lane) * 8;
   }
   const uint32_t sbase = lds_addr(smem);
   auto issue = [&](int it) {
@@ -113,15 +129,17 @@ __global__ __launch_bounds__(512) void selfcond_split_kernel(SelfcondArgs a, int
       int vr = vbeg + vo + erow[q];
       vr = vr < a.V ? vr : a.V - 1;                  // rows past V meet p~ = 0
       dma16(a.E + (int64_t)vr * a.d + ecol[q], st + ins * 1024);
-      dma16(gp[q] + (int64_t)(vo / 16) * 64 * 8, st + ESTAGE + ins * 1024);
     }
+#pragma unroll
+    for (int q = 0; q < PQ; ++q)
+      dma16(gp[q] + (int64_t)(vo / 16) * 64 * 8, st + ESTAGE + (wave * PQ + q) * 1024);
   };
 
-  f32x16_t acc[4][2];
+  f32x16_t acc[4][CTW];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+    for (int j = 0; j < CTW; ++j) acc[i][j] = f32x16_t{};
 
   // Transposing-read source addresses: lane i of 16-lane group g reads 4 consecutive
   // j of row 4r + i/4 (+ 16ks + 8h); the group returns E^T rows j = 16(g&1) + i.
@@ -132,8 +150,8 @@ __global__ __launch_bounds__(512) void selfcond_split_kernel(SelfcondArgs a, int
   // Operands of one 16-deep k-step: 4 E^T fragments, 2 raw p~ fragments and their
   // shift counts (the shift is applied just before the MFMAs).
   struct Frag {
-    u32x4_t af[4], bf[2];
-    short n[2];
+    u32x4_t af[4], bf[CTW];
+    short n[CTW];
   };
   auto load = [&](int it, int ks, Frag &f) {
     const char *se = smem + (it % NS) * STAGE;
@@ -153,21 +171,21 @@ __global__ __launch_bounds__(512) void selfcond_split_kernel(SelfcondArgs a, int
       f.af[jt] = u32x4_t{w[0], w[1], w[2], w[3]};
     }
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      f.n[ct] = (short)ntab[tl * BC + (wc * 2 + ct) * 32 + l32];
-      f.bf[ct] = *(const u32x4_t *)(sp + ((wc * 2 + ct) * 2 + ks) * 1024 + lane * 16);
+    for (int ct = 0; ct < CTW; ++ct) {
+      f.n[ct] = (short)ntab[tl * BC + (wc * CTW + ct) * 32 + l32];
+      f.bf[ct] = *(const u32x4_t *)(sp + ((wc * CTW + ct) * 2 + ks) * 1024 + lane * 16);
     }
   };
   auto mma = [&](const Frag &f) {
-    u32x4_t bf[2];
+    u32x4_t bf[CTW];
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
+    for (int ct = 0; ct < CTW; ++ct) {
       const v2i16_t dn = v2i16_t{(short)(f.n[ct] << 7), (short)(f.n[ct] << 7)};
       const u32x4_t v = f.bf[ct];
       bf[ct] = u32x4_t{shift2(v[0], dn), shift2(v[1], dn), shift2(v[2], dn), shift2(v[3], dn)};
     }
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+    for (int ct = 0; ct < CTW; ++ct)
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt) acc[jt][ct] = mfma_32x32x16(f.af[jt], bf[ct], acc[jt][ct]);
   };
@@ -185,7 +203,7 @@ __global__ __launch_bounds__(512) void selfcond_split_kernel(SelfcondArgs a, int
   // 8 columns' contiguous references), 64 columns per pass, and the lane group's
   // maximum comes from three xor shuffles.
   {
-    constexpr int TPL = NTAB_MAX / BC / 8;         // tiles per lane (ntl <= 8 * TPL)
+    constexpr int TPL = 16;                        // tiles per lane: ntl <= 128 = 8 * TPL
     const int ntl = tile1 - tile0;
     const int sub = tid & 7, cg = tid >> 3;
 #pragma unroll
@@ -220,8 +238,8 @@ __global__ __launch_bounds__(512) void selfcond_split_kernel(SelfcondArgs a, int
   Frag f0, f1;
   for (int it = 0; it < NIT; ++it) {
     const int ahead = NIT - 1 - it;                  // stages issued beyond this one
-    if (ahead >= 2) dma_wait<8>();
-    else if (ahead == 1) dma_wait<4>();
+    if (ahead >= 2) dma_wait<2 * CPS>();
+    else if (ahead == 1) dma_wait<CPS>();
     else dma_wait<0>();
     __syncthreads();
     if (it + NS - 1 < NIT) issue(it + NS - 1);
@@ -234,8 +252,8 @@ __global__ __launch_bounds__(512) void selfcond_split_kernel(SelfcondArgs a, int
   // Partial s^T for this split, stored as ps[split][j][c]: for each accumulator
   // register the 32 lanes of a half-wave write 32 consecutive columns (128 bytes).
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    const int c = cb + (wc * 2 + ct) * 32 + l32;
+  for (int ct = 0; ct < CTW; ++ct) {
+    const int c = cb + (wc * CTW + ct) * 32 + l32;
     if (c >= a.Cpad) continue;
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) {
@@ -323,16 +341,26 @@ __global__ __launch_bounds__(256) void selfcond_reduce_kernel(SelfcondArgs a, Ar
   }
 }
 
+template <int BC>
+hipError_t launch_split(const SelfcondArgs &a, int nj, hipStream_t st) {
+  constexpr int smem = smem_bytes<BC>();
+  static std::atomic<bool> attr[DG_MAX_DEVICES];
+  hipError_t e = dg_smem_attr_once(attr, smem, {(const void *)selfcond_split_kernel<BC>});
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(selfcond_split_kernel<BC>, dim3(nj * a.nsc * ((a.Cpad + BC - 1) / BC)), dim3(512), smem,
+                     st, a, nj);
+  return hipGetLastError();
+}
+
 }  // namespace
 
+// Canvas blocks of 128 columns when at most 128 columns are padded in, or when blocks
+// of 256 would give fewer workgroups than CUs (a short vocabulary); else 256 (each
+// copied E byte feeds twice the columns).
 hipError_t dg_launch_selfcond(const SelfcondArgs &a, const ArsArgs *ars, hipStream_t st) {
-  static std::atomic<bool> attr[DG_MAX_DEVICES];
-  hipError_t e = dg_smem_attr_once(attr, SMEM, {(const void *)selfcond_split_kernel});
-  if (e != hipSuccess) return e;
   const int nj = (a.d + BJ - 1) / BJ;
-  hipLaunchKernelGGL(selfcond_split_kernel, dim3(nj * a.nsc * ((a.Cpad + BC - 1) / BC)), dim3(512),
-                     SMEM, st, a, nj);
-  e = hipGetLastError();
+  const bool narrow = a.Cpad <= 128 || (int64_t)nj * a.nsc * ((a.Cpad + 255) / 256) < dg_device_cus();
+  hipError_t e = narrow ? launch_split<128>(a, nj, st) : launch_split<256>(a, nj, st);
   if (e != hipSuccess) return e;
   const int nx = (a.d + 15) / 16, ny = (a.Cpad + 63) / 64;
   ArsArgs r{};                                       // r.B = 0: no acceptance workgroups

@@ -7,7 +7,8 @@
  *   redrawn, inside [0, V);
  *   s = p0 E = 0, so z = W2 GELU(W1 0) = 0 whatever W1 and W2 hold;
  *   the stop test at step 0 with no previous argmax gives flag 0.
- * dg_accept_renoise_stop on the same entropies must give the three calls' results.
+ * dg_accept_renoise_stop on the same entropies must give the three calls' results, and
+ * dg_selfcond_accept after a second sampler head the same acceptance, tokens, flag and z.
  * Also: a NULL pointer and tau = 0 are refused with a message and nothing enqueued.
  * Built by the package's build step next to libdg.so; prints "c_abi_check: ok" and
  * exits 0 when every check holds, else prints the first failure and exits 1. */
@@ -50,7 +51,9 @@ int main(void) {
   dg_bf16 *E = NULL, *H = NULL, *W1 = NULL, *W2 = NULL, *z = NULL;
   float *ent = NULL;
   int32_t *am = NULL, *tok = NULL, *nacc = NULL, *flag = NULL, *tok2 = NULL, *nacc2 = NULL, *flag2 = NULL;
-  uint8_t *acc = NULL, *acc2 = NULL;
+  int32_t *tok3 = NULL, *nacc3 = NULL, *flag3 = NULL;
+  uint8_t *acc = NULL, *acc2 = NULL, *acc3 = NULL;
+  dg_bf16 *z3 = NULL;
   HIP_OK(hipMalloc(&ws, ws_bytes));
   HIP_OK(hipMalloc((void **)&E, (size_t)V * d * 2));
   HIP_OK(hipMalloc((void **)&H, (size_t)C * d * 2));
@@ -67,6 +70,11 @@ int main(void) {
   HIP_OK(hipMalloc((void **)&acc2, (size_t)C));
   HIP_OK(hipMalloc((void **)&nacc2, 4));
   HIP_OK(hipMalloc((void **)&flag2, 4));
+  HIP_OK(hipMalloc((void **)&tok3, (size_t)C * 4));
+  HIP_OK(hipMalloc((void **)&acc3, (size_t)C));
+  HIP_OK(hipMalloc((void **)&nacc3, 4));
+  HIP_OK(hipMalloc((void **)&flag3, 4));
+  HIP_OK(hipMalloc((void **)&z3, (size_t)C * d * 2));
 
   /* E = 0; H, W1, W2 = arbitrary finite bf16 values (alternating +-0.5, +-0.25) */
   HIP_OK(hipMemset(E, 0, (size_t)V * d * 2));
@@ -90,6 +98,26 @@ int main(void) {
   DG_OK_OR_FAIL(ctx, dg_stop_test(ctx, 1, C, ent, am, NULL, 0.005f, 0, 48, flag));
   DG_OK_OR_FAIL(ctx, dg_accept_renoise_stop(ctx, 1, C, V, ent, 0.1f, am, am, NULL, 7u, 0u, 0, 0.005f, 48,
                                             acc2, nacc2, tok2, flag2));
+  DG_OK_OR_FAIL(ctx, dg_logits_entropy(ctx, &m, H, E, 0.8f, ws, ent, am));
+  HIP_OK(hipMemset(z3, 0xFF, (size_t)C * d * 2));
+  dg_accept_args aa;
+  memset(&aa, 0, sizeof aa);
+  aa.B = 1;
+  aa.entropy = ent;
+  aa.b = 0.1f;
+  aa.x0 = am;
+  aa.argmax = am;
+  aa.prev_argmax = NULL;
+  aa.seed = 7u;
+  aa.canvas_base = 0u;
+  aa.step = 0;
+  aa.thr = 0.005f;
+  aa.N = 48;
+  aa.accept = acc3;
+  aa.n_accept = nacc3;
+  aa.tokens = tok3;
+  aa.flag = flag3;
+  DG_OK_OR_FAIL(ctx, dg_selfcond_accept(ctx, &m, ws, E, W1, W2, z3, &aa));
   DG_OK_OR_FAIL(ctx, dg_sync(ctx));
 
   float h_ent[16];
@@ -109,6 +137,21 @@ int main(void) {
   if (memcmp(h_tok2, h_tok, sizeof h_tok) || memcmp(h_acc2, h_acc, sizeof h_acc) || h_nacc2 != h_nacc ||
       h_flag2 != h_flag)
     FAIL("dg_accept_renoise_stop differs from the three calls");
+  HIP_OK(hipMemcpy(h_tok2, tok3, sizeof h_tok2, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(h_acc2, acc3, sizeof h_acc2, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(&h_nacc2, nacc3, 4, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(&h_flag2, flag3, 4, hipMemcpyDeviceToHost));
+  if (memcmp(h_tok2, h_tok, sizeof h_tok) || memcmp(h_acc2, h_acc, sizeof h_acc) || h_nacc2 != h_nacc ||
+      h_flag2 != h_flag)
+    FAIL("dg_selfcond_accept's acceptance differs from the three calls");
+  {
+    uint16_t *z3h = (uint16_t *)malloc((size_t)C * d * 2);
+    if (!z3h) FAIL("host allocation");
+    HIP_OK(hipMemcpy(z3h, z3, (size_t)C * d * 2, hipMemcpyDeviceToHost));
+    const int same = memcmp(z3h, host, (size_t)C * d * 2) == 0;
+    free(z3h);
+    if (!same) FAIL("dg_selfcond_accept's z differs from dg_selfcond's");
+  }
 
   const double lnV = log((double)V);
   for (int c = 0; c < C; ++c) {
@@ -126,6 +169,7 @@ int main(void) {
   hipFree(ws); hipFree(E); hipFree(H); hipFree(W1); hipFree(W2); hipFree(z);
   hipFree(ent); hipFree(am); hipFree(tok); hipFree(acc); hipFree(nacc); hipFree(flag);
   hipFree(tok2); hipFree(acc2); hipFree(nacc2); hipFree(flag2);
+  hipFree(tok3); hipFree(acc3); hipFree(nacc3); hipFree(flag3); hipFree(z3);
   dg_destroy(ctx);
   printf("c_abi_check: ok\n");
   return 0;

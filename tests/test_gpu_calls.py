@@ -539,6 +539,35 @@ def test_sampler_head_does_not_depend_on_the_canvas_block_width(dg_ctx, C):
         np.testing.assert_array_equal(a, b)
 
 
+def test_selfcond_does_not_depend_on_the_canvas_block_width(dg_ctx):
+    """At a 32768-token vocabulary and d = 2048, a 128-position canvas runs the
+    self-conditioning split in 128-column blocks (at most 128 columns padded in) and a
+    256-position canvas, whose first 128 positions are the same, in 256-column blocks
+    (8 model-width slices x 32 splits fill 256 CUs). The split count is 32 in both (it
+    depends on the 256-column block count, 1 in both). Every element of s sums its
+    split's vocabulary rows in the same order, and the FFW GEMMs do not depend on their
+    tile shape, so the shared rows of z must agree bit for bit."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if 8 * 32 < cus:
+        pytest.skip(f"{cus} CUs: the 256-position canvas would also take 128-column blocks")
+    cfg = di.Config("blocks_sc", V=32768, d=2048, C=128, Hq=2, Hkv=1, hd=64, F=256, P0=0, N=4,
+                    alpha_max=8.0, seed=28)
+    W = di.weights(cfg)
+    Wd = upload_weights(W)
+    H1 = di.hidden(cfg, W["E"], 0, 1, di.targets(cfg, 0))
+    H2 = di.hidden(cfg, W["E"], 1, 2, di.targets(cfg, 1))
+    tau = O.temperature(1, cfg.N)
+    outs = []
+    for cf, H in ((cfg, H1), (cfg.with_(C=256), np.concatenate([H1, H2], axis=0))):
+        ws = torch.empty(dg.workspace_bytes(cf, 0), dtype=torch.uint8, device=DEV)
+        ent, am = run_head(dg_ctx, cf, Wd, H, tau, ws)
+        z = torch.empty(cf.C, cf.d, dtype=torch.bfloat16, device=DEV)
+        dg_ctx.selfcond(cf, ws, Wd["E"], Wd["W1"], Wd["W2"], z)
+        dg_ctx.sync()
+        outs.append(bits_np(z)[:128].copy())
+    np.testing.assert_array_equal(outs[0], outs[1])
+
+
 def test_gemm_results_do_not_depend_on_the_tile_shape(dg_ctx):
     """The projection GEMM picks its tile shape from the output size: committing 256
     tokens (1024 key and 1024 value features) runs 32 x 64 tiles, committing 512 runs
