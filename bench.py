@@ -71,7 +71,9 @@ def parse():
     return ap.parse_args()
 
 
-PAIR_SOURCES = ("k_logits.hip", "k_selfcond.hip", "k_gemm.hip")
+# kernel sources of the pair, the shared header (workspace layout, split counts) and the
+# acceptance routines that run beside the self-conditioning reduce
+PAIR_SOURCES = ("k_logits.hip", "k_selfcond.hip", "k_gemm.hip", "dg_common.h", "dg_sampler_dev.h")
 
 
 def pair_traffic_from_profiles():
