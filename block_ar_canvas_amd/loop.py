@@ -62,13 +62,13 @@ class CanvasLoop:
         self.sampled = [torch.empty(C, dtype=torch.int32, device=dev) for _ in range(2)]
         self.accept = torch.empty(C, dtype=torch.uint8, device=dev)
         self.n_accept = torch.empty(1, dtype=torch.int32, device=dev)
-        # Stop flags live in pinned host memory; the stop kernel writes them with
+        # Stop flags live in pinned host memory; the stop test writes them with
         # system-scope stores, the host pre-fills -1 when it enqueues the step and polls,
         # so no copy or event sits between two steps' kernels on the stream. Steps take
         # the four buffers in enqueue order: when a step is enqueued, at most the two
         # steps before it may still be pending (the driving loop enqueues step k + 1 before
         # waiting for step k, and a canvas switch adds one speculative step), so a buffer
-        # is never refilled while an older step's stop kernel may still write it.
+        # is never refilled while an older step's stop test may still write it.
         self.flags = [torch.full((1,), -1, dtype=torch.int32, pin_memory=True) for _ in range(4)]
         self._seq = 0
         self._slot = {}
