@@ -269,9 +269,12 @@ __global__ __launch_bounds__(512) void selfcond_split_kernel(SelfcondArgs a, int
 // s[c][j] = bf16( sum over splits S, in split order, of
 //                 2^(rho_S - R_c) / Z_c * ps[S][j][c] ).
 // A workgroup owns 16 j x 64 c (one float4 of columns per thread): reads run along c,
-// the bf16 result is transposed through LDS and written along j. Splits are taken 32
-// at a time; a chunk's 32 partial loads are issued together, ahead of the scale
-// computation, so each chunk costs one memory round trip.
+// the bf16 result is transposed through LDS and written along j. Splits are taken 16
+// at a time; a chunk's 16 partial loads are issued together, ahead of the scale
+// computation, so each chunk costs one memory round trip. (32 at a time took 190 VGPRs
+// and two workgroups per CU, so at 512 workgroups an acceptance workgroup waited for a
+// slot; 16 take 104 VGPRs, four per CU, and measured slightly faster at every size.)
+// The summation order is the split order whatever the chunk size.
 // The grid is one-dimensional: ars.B workgroups first, then nx x ny reduce workgroups
 // in row order (j fastest). The first ars.B run acceptance, renoise and the stop test of
 // canvas blockIdx.x instead: that work needs only the sampler head's outputs, so it
@@ -283,7 +286,7 @@ __global__ __launch_bounds__(256) void selfcond_reduce_kernel(SelfcondArgs a, Ar
     return;
   }
   const int wg = (int)blockIdx.x - ars.B, bx = wg % nx, by = wg / nx;
-  constexpr int PC = 32;                             // splits per chunk
+  constexpr int PC = 16;                             // splits per chunk
   __shared__ float scale[64 * (PC + 1)];             // [c][split in chunk]
   __shared__ u16 out[64][24];
   const int tid = threadIdx.x;
