@@ -1,7 +1,8 @@
 """The C-ABI library loads and exports every declared symbol (no GPU needed).
 
 Only host-pure entry points are called here (dg_temperature, dg_reveal_count,
-dg_workspace_bytes, dg_moe_workspace_bytes); nothing launches a kernel.
+dg_workspace_bytes, dg_moe_workspace_bytes), and entry points with a NULL context, which
+refuse before touching a device; nothing launches a kernel.
 """
 import ctypes
 import os
@@ -142,3 +143,16 @@ def test_run_canvas_refuses_a_null_context(lib):
     st = lib.dg_run_canvas(None, ctypes.byref(d), None, None, None, 0, 0, None, lib.dg_run_canvas.argtypes[8](), None,
                            None, None, None, ctypes.byref(steps), ctypes.byref(P))
     assert st == 1                                      # DG_ERR_NULL
+
+
+def test_combined_sampler_calls_refuse_a_null_context(lib):
+    # the one-launch acceptance/renoise/stop call and the one beside self-conditioning's
+    # reduce are refused with DG_ERR_NULL before anything touches a device
+    st = lib.dg_accept_renoise_stop(None, 1, 16, 100, None, 0.1, None, None, None, 1, 0, 0, 0.005, 8,
+                                    None, None, None, None)
+    assert st == 1
+    import block_ar_canvas_amd as dg
+    d = dg.Dims(V=512, d=64, C=16, Hq=4, Hkv=2, hd=16, F=128)
+    a = dg.AcceptArgs()
+    st = lib.dg_selfcond_accept(None, ctypes.byref(d), None, None, None, None, None, ctypes.byref(a))
+    assert st == 1
