@@ -184,7 +184,7 @@ class CanvasLoop:
     def enqueue_canvas_fixed(self, canvas: int, hidden):
         """Enqueues a whole canvas without any host wait: init, all N steps, and the commit
         of the last step's block. There is no adaptive stop (the host reads no flag; the
-        stop kernels still write theirs), so the sequence is fixed and can be captured in
+        stop test still writes its flags), so the sequence is fixed and can be captured in
         a HIP graph and replayed. hidden(k) -> H_k device tensor, read at enqueue time.
         Returns the commit's new cache length."""
         self.init_canvas(canvas)
