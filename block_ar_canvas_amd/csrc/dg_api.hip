@@ -794,11 +794,6 @@ dg_status check_ars(dg_ctx ctx, int32_t B, int32_t C, int32_t V, const float *en
   return DG_OK;
 }
 
-hipError_t launch_ars(const ArsArgs &r, hipStream_t st) {
-  return dg_launch_accept_renoise_stop(r.B, r.C, r.V, r.ent, r.budget, r.x0, r.am, r.prev, r.seed, r.canvas_base,
-                                       r.step, r.limit, r.N, r.acc, r.nacc, r.tok, r.flag, st);
-}
-
 }  // namespace
 
 dg_status dg_accept_renoise_stop(dg_ctx ctx, int32_t B, int32_t C, int32_t V, const float *entropy,
@@ -811,7 +806,7 @@ dg_status dg_accept_renoise_stop(dg_ctx ctx, int32_t B, int32_t C, int32_t V, co
   dg_status st = check_ars(ctx, B, C, V, entropy, b, x0, argmax, prev_argmax, seed, canvas_base, step, thr, N,
                            accept, n_accept, tokens, flag, __func__, r);
   if (st) return st;
-  hipError_t e = launch_ars(r, ctx->stream);
+  hipError_t e = dg_launch_accept_renoise_stop(r, ctx->stream);
   return e == hipSuccess ? DG_OK : hip_fail(ctx, e, __func__);
 }
 
@@ -841,7 +836,7 @@ dg_status dg_selfcond_accept(dg_ctx ctx, const dg_dims *dims, void *ws, const dg
     r.tpp = r.C <= 64 ? 4 : r.C <= 128 ? 2 : 1;
     return selfcond_enqueue(ctx, m, ws, E, W1, W2, z, &r);
   }
-  hipError_t e = launch_ars(r, ctx->stream);
+  hipError_t e = dg_launch_accept_renoise_stop(r, ctx->stream);
   if (e != hipSuccess) return hip_fail(ctx, e, __func__);
   return selfcond_enqueue(ctx, m, ws, E, W1, W2, z, nullptr);
 }

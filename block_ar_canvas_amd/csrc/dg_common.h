@@ -465,8 +465,6 @@ hipError_t dg_launch_renoise(int B, int C, int V, const int *am, const uint8_t *
                              hipStream_t st);
 hipError_t dg_launch_stop(int B, int C, const float *ent, const int *am, const int *prev,
                           uint64_t limit, int step, int N, int *flag, hipStream_t st);
-// dg_launch_accept, dg_launch_renoise (with acc) and dg_launch_stop in one launch.
-hipError_t dg_launch_accept_renoise_stop(int B, int C, int V, const float *ent, uint64_t budget,
-                                         const int *x0, const int *am, const int *prev, uint64_t seed,
-                                         uint32_t canvas_base, int step, uint64_t limit, int N,
-                                         uint8_t *acc, int *nacc, int *tok, int *flag, hipStream_t st);
+// dg_launch_accept, dg_launch_renoise (with acc) and dg_launch_stop in one launch (r.tpp
+// is chosen here).
+hipError_t dg_launch_accept_renoise_stop(const ArsArgs &r, hipStream_t st);

@@ -24,8 +24,9 @@
 // step; the step cap commits anyway.
 //
 // accept_renoise_stop_kernel runs acceptance, renoise and the stop test of a step in one
-// launch with the same arithmetic (shared routines), so the three results are bit for
-// bit those of the three kernels.
+// launch. The routines are in dg_sampler_dev.h, shared with the three kernels here and
+// with the self-conditioning reduce, which can run them beside itself; every placement
+// gives the three kernels' results bit for bit.
 //
 // Confidence-ranked acceptance (the openai-hub page "从零拆开DiffusionGemma", step 4,
 // confidence decoding; the "Text diffusion models" survey, section 5): each step keeps
@@ -295,31 +296,11 @@ hipError_t dg_launch_stop(int B, int C, const float *ent, const int *am, const i
   return hipGetLastError();
 }
 
-hipError_t dg_launch_accept_renoise_stop(int B, int C, int V, const float *ent, uint64_t budget,
-                                         const int *x0, const int *am, const int *prev, uint64_t seed,
-                                         uint32_t canvas_base, int step, uint64_t limit, int N,
-                                         uint8_t *acc, int *nacc, int *tok, int *flag, hipStream_t st) {
+hipError_t dg_launch_accept_renoise_stop(const ArsArgs &r, hipStream_t st) {
   // C <= 1024 (checked by the caller); up to 4 threads per position as in acceptance
-  ArsArgs a{};
-  a.B = B;
-  a.C = C;
-  a.tpp = C <= 256 ? 4 : C <= 512 ? 2 : 1;
-  a.V = V;
-  a.step = step;
-  a.N = N;
-  a.ent = ent;
-  a.x0 = x0;
-  a.am = am;
-  a.prev = prev;
-  a.budget = budget;
-  a.limit = limit;
-  a.seed = seed;
-  a.canvas_base = canvas_base;
-  a.acc = acc;
-  a.nacc = nacc;
-  a.tok = tok;
-  a.flag = flag;
-  const int n = (C * a.tpp + 63) / 64 * 64;
-  hipLaunchKernelGGL(accept_renoise_stop_kernel, dim3(B), dim3(n), 0, st, a);
+  ArsArgs a = r;
+  a.tpp = a.C <= 256 ? 4 : a.C <= 512 ? 2 : 1;
+  const int n = (a.C * a.tpp + 63) / 64 * 64;
+  hipLaunchKernelGGL(accept_renoise_stop_kernel, dim3(a.B), dim3(n), 0, st, a);
   return hipGetLastError();
 }
