@@ -966,6 +966,9 @@ dg_status dg_run_canvas(dg_ctx ctx, const dg_dims *dims, const dg_weights *w, dg
   if (N < 1) return fail(ctx, DG_ERR_RANGE, "%s: N=%d must be >= 1", __func__, N);
   if (!(prm->b >= 0.f && prm->b < 65536.f) || !(prm->thr >= 0.f && prm->thr < 65536.f))
     return fail(ctx, DG_ERR_RANGE, "%s: b=%g and thr=%g must be in [0, 65536)", __func__, prm->b, prm->thr);
+  if (prm->commit != DG_COMMIT_PROJECTION && prm->commit != DG_COMMIT_PREFILL)
+    return fail(ctx, DG_ERR_RANGE, "%s: commit=%d is not DG_COMMIT_PROJECTION or DG_COMMIT_PREFILL", __func__,
+                (int)prm->commit);
   if (!(prm->tau0 > 0.f) || !(prm->tau1 > 0.f) || !isfinite(prm->tau0) || !isfinite(prm->tau1))
     return fail(ctx, DG_ERR_RANGE, "%s: tau0=%g and tau1=%g must be finite and > 0", __func__, prm->tau0, prm->tau1);
   if (P + m.C > Pcap)
@@ -1022,7 +1025,11 @@ dg_status dg_run_canvas(dg_ctx ctx, const dg_dims *dims, const dg_weights *w, dg
     if (flag != 0) break;                            // stop (1) or the cap (2): commit step k
     ++k;
   }
-  if ((st = dg_commit_kv(ctx, dims, am[k & 1], E, Wk, Wv, Kp, Vt, P, Pcap, P_out))) return st;
+  if (prm->commit == DG_COMMIT_PREFILL)
+    st = dg_prefill_block(ctx, dims, am[k & 1], E, Wq, Wk, Wv, Wo, Kp, Vt, P, Pcap, ws, A, P_out);
+  else
+    st = dg_commit_kv(ctx, dims, am[k & 1], E, Wk, Wv, Kp, Vt, P, Pcap, P_out);
+  if (st) return st;
   const hipError_t e = hipMemcpyAsync(x0, am[k & 1], (size_t)m.C * 4, hipMemcpyDeviceToDevice, ctx->stream);
   if (e != hipSuccess) return hip_fail(ctx, e, __func__);
   *steps = k + 1;

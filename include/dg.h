@@ -350,8 +350,10 @@ dg_status dg_commit_kv(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens,
  *   dg_canvas_attn (z = 0 at k = 0), dg_logits_entropy on H_k at dg_temperature(k, N,
  *   tau0, tau1), dg_selfcond_accept (acceptance with budget b, renoise of the rejected
  *   positions, the stop test against the previous step's argmax, self-conditioning),
- * until the stop test fires or the cap N is reached, then dg_commit_kv of that step's
- * argmax. Step k + 1 is enqueued before the host waits for step k's flag (pinned host
+ * until the stop test fires or the cap N is reached, then the commit of that step's
+ * argmax: dg_commit_kv (commit = DG_COMMIT_PROJECTION) or the causal re-encode
+ * dg_prefill_block (commit = DG_COMMIT_PREFILL; its attention output goes to loop_ws);
+ * both attention calls use the context's rotary setting (dg_set_rope). Step k + 1 is enqueued before the host waits for step k's flag (pinned host
  * memory of the context, polled: no stream synchronization between steps); when step k
  * stops the canvas, step k + 1's results are discarded (it writes the other argmax
  * buffer, and the commit reads step k's).
@@ -371,7 +373,9 @@ typedef struct {
   float tau0, tau1;          /* temperature schedule endpoints */
   uint64_t seed;             /* Philox key of the canvas draws */
   uint32_t canvas;           /* canvas index (the Philox key's second word) */
+  int32_t commit;            /* DG_COMMIT_PROJECTION or DG_COMMIT_PREFILL */
 } dg_loop_params;
+enum { DG_COMMIT_PROJECTION = 0, DG_COMMIT_PREFILL = 1 };
 typedef const dg_bf16 *(*dg_hidden_fn)(void *user, int32_t step);
 size_t dg_loop_workspace_bytes(const dg_dims *dims);
 dg_status dg_run_canvas(dg_ctx ctx, const dg_dims *dims, const dg_weights *w, dg_bf16 *Kp,
