@@ -62,10 +62,13 @@ class LoopParams(ctypes.Structure):
     """dg_loop_params of dg_run_canvas."""
     _fields_ = [("N", ctypes.c_int32), ("b", ctypes.c_float), ("thr", ctypes.c_float),
                 ("tau0", ctypes.c_float), ("tau1", ctypes.c_float), ("seed", ctypes.c_uint64),
-                ("canvas", ctypes.c_uint32), ("commit", ctypes.c_int32)]
+                ("canvas", ctypes.c_uint32), ("commit", ctypes.c_int32), ("rule", ctypes.c_int32),
+                ("draw", ctypes.c_int32)]
 
 
 COMMIT_PROJECTION, COMMIT_PREFILL = 0, 1          # dg_loop_params.commit
+RULE_ENTROPY, RULE_CONFIDENCE = 0, 1              # dg_loop_params.rule
+DRAW_ARGMAX, DRAW_SAMPLE = 0, 1                   # dg_loop_params.draw
 
 
 class AcceptArgs(ctypes.Structure):
@@ -390,19 +393,24 @@ class Context:
         return int(out.value)
 
     def run_canvas(self, dims, weights, Kp, Vt, P, hidden, ws, loop_ws, x0, *, N, seed, canvas,
-                   b=0.1, thr=0.005, tau0=0.8, tau1=0.4, commit="projection"):
+                   b=0.1, thr=0.005, tau0=0.8, tau1=0.4, commit="projection", rule="entropy",
+                   draw="argmax"):
         """dg_run_canvas: one whole canvas (init, steps until the stop test or the cap N,
         the commit) sequenced in the library. hidden(k) -> H_k bf16 device tensor [C, d].
         commit: "projection" (dg_commit_kv) or "prefill" (dg_prefill_block, the causal
-        re-encode; rotary positions as set by set_rope). Returns (steps run, new cache
+        re-encode; rotary positions as set by set_rope); rule: "entropy" or "confidence";
+        draw: "argmax" or "sample" (as in CanvasLoop). Returns (steps run, new cache
         length P); x0 [C] int32 receives the committed block."""
         d = Dims.of(dims)
         w = Weights(*(_ptr(weights[k], _BF16, k) for k in ("E", "Wq", "Wk", "Wv", "Wo", "W1", "W2")))
-        modes = {"projection": COMMIT_PROJECTION, "prefill": COMMIT_PREFILL}
-        if commit not in modes:
-            raise ValueError(f"commit must be one of {tuple(modes)}")
+        commits = {"projection": COMMIT_PROJECTION, "prefill": COMMIT_PREFILL}
+        rules = {"entropy": RULE_ENTROPY, "confidence": RULE_CONFIDENCE}
+        draws = {"argmax": DRAW_ARGMAX, "sample": DRAW_SAMPLE}
+        if commit not in commits or rule not in rules or draw not in draws:
+            raise ValueError(f"commit must be one of {tuple(commits)}, rule one of {tuple(rules)}, "
+                             f"draw one of {tuple(draws)}")
         prm = LoopParams(int(N), float(b), float(thr), float(tau0), float(tau1), int(seed), int(canvas),
-                         modes[commit])
+                         commits[commit], rules[rule], draws[draw])
         held, err = [], []
 
         def cb(_user, k):

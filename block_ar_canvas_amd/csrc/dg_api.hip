@@ -884,7 +884,7 @@ namespace {
 
 // Device state of one canvas in dg_run_canvas's loop workspace, 256-byte aligned regions.
 struct LoopWs {
-  size_t tokens, z, A, entropy, am0, am1, accept, n_accept, total;
+  size_t tokens, z, A, entropy, am0, am1, accept, n_accept, smp0, smp1, conf, total;
 };
 LoopWs loop_ws_layout(const dg_dims &m) {
   LoopWs w{};
@@ -903,6 +903,9 @@ LoopWs loop_ws_layout(const dg_dims &m) {
   w.am1 = take(4 * C);
   w.accept = take(C);
   w.n_accept = take(4);
+  w.smp0 = take(4 * C);                              // sampled tokens of even / odd steps
+  w.smp1 = take(4 * C);
+  w.conf = take(4 * C);                              // confidence scores (confidence rule)
   w.total = off;
   return w;
 }
@@ -966,6 +969,9 @@ dg_status dg_run_canvas(dg_ctx ctx, const dg_dims *dims, const dg_weights *w, dg
   if (N < 1) return fail(ctx, DG_ERR_RANGE, "%s: N=%d must be >= 1", __func__, N);
   if (!(prm->b >= 0.f && prm->b < 65536.f) || !(prm->thr >= 0.f && prm->thr < 65536.f))
     return fail(ctx, DG_ERR_RANGE, "%s: b=%g and thr=%g must be in [0, 65536)", __func__, prm->b, prm->thr);
+  if ((prm->rule != DG_RULE_ENTROPY && prm->rule != DG_RULE_CONFIDENCE) ||
+      (prm->draw != DG_DRAW_ARGMAX && prm->draw != DG_DRAW_SAMPLE))
+    return fail(ctx, DG_ERR_RANGE, "%s: rule=%d or draw=%d unknown", __func__, (int)prm->rule, (int)prm->draw);
   if (prm->commit != DG_COMMIT_PROJECTION && prm->commit != DG_COMMIT_PREFILL)
     return fail(ctx, DG_ERR_RANGE, "%s: commit=%d is not DG_COMMIT_PROJECTION or DG_COMMIT_PREFILL", __func__,
                 (int)prm->commit);
@@ -982,6 +988,9 @@ dg_status dg_run_canvas(dg_ctx ctx, const dg_dims *dims, const dg_weights *w, dg
   int32_t *am[2] = {ws_at<int32_t>(loop_ws, L.am0), ws_at<int32_t>(loop_ws, L.am1)};
   uint8_t *acc = ws_at<uint8_t>(loop_ws, L.accept);
   int32_t *nacc = ws_at<int32_t>(loop_ws, L.n_accept);
+  int32_t *smp[2] = {ws_at<int32_t>(loop_ws, L.smp0), ws_at<int32_t>(loop_ws, L.smp1)};
+  float *conf = ws_at<float>(loop_ws, L.conf);
+  const bool sample = prm->draw == DG_DRAW_SAMPLE;
 
   // a uniform random canvas (stream 1 of the canvas's draws)
   if ((st = dg_renoise(ctx, 1, m.C, m.V, nullptr, nullptr, prm->seed, prm->canvas, 0, tok))) return st;
@@ -993,15 +1002,28 @@ dg_status dg_run_canvas(dg_ctx ctx, const dg_dims *dims, const dg_weights *w, dg
     int32_t *a = am[k & 1], *prev = k > 0 ? am[(k - 1) & 1] : nullptr;
     dg_status r = dg_canvas_attn(ctx, dims, tok, k > 0 ? z : nullptr, E, Wq, Wk, Wv, Wo, Kp, Vt, P, Pcap, ws, A);
     if (!r) r = dg_logits_entropy(ctx, dims, H, E, dg_temperature(k, N, prm->tau0, prm->tau1), ws, ent, a);
+    int32_t *x0k = a;                                // what accepted positions keep
+    if (!r && sample) {
+      x0k = smp[k & 1];
+      r = dg_sample(ctx, dims, ws, 1, prm->seed, prm->canvas, (uint32_t)k, x0k);
+    }
     if (r) return r;
     const int sl = (int)(ctx->flag_seq++ % 4);
     slot[k & 1] = sl;
     ctx->host_flags[sl] = -1;
+    if (prm->rule == DG_RULE_CONFIDENCE) {
+      r = dg_confidence(ctx, dims, ws, conf);
+      if (!r) r = dg_topk_accept(ctx, 1, m.C, conf, dg_reveal_count(m.C, N, k), acc, nacc);
+      if (!r) r = dg_renoise(ctx, 1, m.C, m.V, x0k, acc, prm->seed, prm->canvas, (uint32_t)k, tok);
+      if (!r) r = dg_stop_test(ctx, 1, m.C, ent, a, prev, prm->thr, k, N, ctx->host_flags + sl);
+      if (!r) r = dg_selfcond(ctx, dims, ws, E, W1, W2, z);
+      return r;
+    }
     dg_accept_args aa{};
     aa.B = 1;
     aa.entropy = ent;
     aa.b = prm->b;
-    aa.x0 = a;
+    aa.x0 = x0k;
     aa.argmax = a;
     aa.prev_argmax = prev;
     aa.seed = prm->seed;
@@ -1025,12 +1047,13 @@ dg_status dg_run_canvas(dg_ctx ctx, const dg_dims *dims, const dg_weights *w, dg
     if (flag != 0) break;                            // stop (1) or the cap (2): commit step k
     ++k;
   }
+  const int32_t *fin = sample ? smp[k & 1] : am[k & 1];   // the block step k commits
   if (prm->commit == DG_COMMIT_PREFILL)
-    st = dg_prefill_block(ctx, dims, am[k & 1], E, Wq, Wk, Wv, Wo, Kp, Vt, P, Pcap, ws, A, P_out);
+    st = dg_prefill_block(ctx, dims, fin, E, Wq, Wk, Wv, Wo, Kp, Vt, P, Pcap, ws, A, P_out);
   else
-    st = dg_commit_kv(ctx, dims, am[k & 1], E, Wk, Wv, Kp, Vt, P, Pcap, P_out);
+    st = dg_commit_kv(ctx, dims, fin, E, Wk, Wv, Kp, Vt, P, Pcap, P_out);
   if (st) return st;
-  const hipError_t e = hipMemcpyAsync(x0, am[k & 1], (size_t)m.C * 4, hipMemcpyDeviceToDevice, ctx->stream);
+  const hipError_t e = hipMemcpyAsync(x0, fin, (size_t)m.C * 4, hipMemcpyDeviceToDevice, ctx->stream);
   if (e != hipSuccess) return hip_fail(ctx, e, __func__);
   *steps = k + 1;
   return DG_OK;

@@ -351,7 +351,11 @@ dg_status dg_commit_kv(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens,
  *   tau0, tau1), dg_selfcond_accept (acceptance with budget b, renoise of the rejected
  *   positions, the stop test against the previous step's argmax, self-conditioning),
  * until the stop test fires or the cap N is reached, then the commit of that step's
- * argmax: dg_commit_kv (commit = DG_COMMIT_PROJECTION) or the causal re-encode
+ * block. With rule = DG_RULE_CONFIDENCE the step runs dg_confidence, dg_topk_accept with
+ * dg_reveal_count(C, N, k), dg_renoise, dg_stop_test and dg_selfcond instead of
+ * dg_selfcond_accept; with draw = DG_DRAW_SAMPLE, dg_sample draws x~ after the sampler
+ * head, accepted positions keep x~ and the commit takes the last step's x~ instead of its
+ * argmax (the stop test compares argmaxes either way). The commit: dg_commit_kv (commit = DG_COMMIT_PROJECTION) or the causal re-encode
  * dg_prefill_block (commit = DG_COMMIT_PREFILL; its attention output goes to loop_ws);
  * both attention calls use the context's rotary setting (dg_set_rope). Step k + 1 is enqueued before the host waits for step k's flag (pinned host
  * memory of the context, polled: no stream synchronization between steps); when step k
@@ -360,7 +364,7 @@ dg_status dg_commit_kv(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens,
  * hidden(user, k) is called on the host before step k is enqueued and returns the device
  * pointer of H_k [C, d] bf16; it may enqueue work producing H_k on the context's stream.
  * loop_ws holds dg_loop_workspace_bytes(dims) bytes (the canvas tokens, z, the attention
- * output, entropies, both argmax buffers, acceptance). Outputs: x0 [C] device int32, the
+ * output, entropies, both argmax and sampled-token buffers, acceptance, confidences). Outputs: x0 [C] device int32, the
  * committed block; *steps (host) the steps run; *P_out (host) = P + C. Returns after the
  * commit is enqueued (dg_sync waits for it). A flag not written within 60 s of waiting
  * ends the call with DG_ERR_HIP after a stream synchronization. */
@@ -374,8 +378,12 @@ typedef struct {
   uint64_t seed;             /* Philox key of the canvas draws */
   uint32_t canvas;           /* canvas index (the Philox key's second word) */
   int32_t commit;            /* DG_COMMIT_PROJECTION or DG_COMMIT_PREFILL */
+  int32_t rule;              /* DG_RULE_ENTROPY or DG_RULE_CONFIDENCE */
+  int32_t draw;              /* DG_DRAW_ARGMAX or DG_DRAW_SAMPLE */
 } dg_loop_params;
 enum { DG_COMMIT_PROJECTION = 0, DG_COMMIT_PREFILL = 1 };
+enum { DG_RULE_ENTROPY = 0, DG_RULE_CONFIDENCE = 1 };
+enum { DG_DRAW_ARGMAX = 0, DG_DRAW_SAMPLE = 1 };
 typedef const dg_bf16 *(*dg_hidden_fn)(void *user, int32_t step);
 size_t dg_loop_workspace_bytes(const dg_dims *dims);
 dg_status dg_run_canvas(dg_ctx ctx, const dg_dims *dims, const dg_weights *w, dg_bf16 *Kp,
