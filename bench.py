@@ -17,11 +17,12 @@ the first tens of launches of a process), then --warmup untimed steps, then exac
 --steps timed steps (value = steps/s). Canvas tokens/s comes from whole canvases timed
 from initialization to commit: the median of --canvases of them.
 
-Prints one JSON line: denoise steps/s (value), canvas tokens/s, the roofline of the
-dominant pair of calls (the sampler head dg_logits_entropy and self-conditioning
-dg_selfcond, which together are most of the step; both timed live with HIP events
-inside real steps), the same protocol at the tiny and small workloads, and the CPU
-oracle's rate on a bounded sample of the same workload.
+Prints one JSON line: denoise steps/s (value), canvas tokens/s (also with each canvas
+run by the library's own loop, dg_run_canvas), the roofline of the dominant pair of
+calls (the sampler head dg_logits_entropy and self-conditioning dg_selfcond_accept,
+which together are most of the step; both timed live with HIP events inside real
+steps), the same protocol at the tiny and small workloads, and the CPU oracle's rate on
+a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -329,8 +330,9 @@ def main():
     note(f"{args.steps} timed steps")
 
     # Roofline of the dominant pair: the sampler head (dg_logits_entropy: logits tile
-    # kernel and row finalize) and self-conditioning (dg_selfcond: p0 E split kernel,
-    # reduce, the two FFW GEMMs), timed live with HIP events on the library's stream
+    # kernel and row finalize) and self-conditioning (dg_selfcond_accept: p0 E split
+    # kernel, reduce with the acceptance/renoise/stop workgroups beside it, the two FFW
+    # GEMMs), timed live with HIP events on the library's stream
     # around each call inside real denoise steps (the same loop, continued for
     # max(reps, 48) steps after the timed region, so the event packets do not touch the
     # headline step time).
@@ -344,7 +346,7 @@ def main():
     pair_ms = logits_ms + selfcond_ms
     # algorithmic bytes: E read by each call, H, the FFW weights and the outputs
     # (entropy, argmax, z); the bf16 probabilities passed between the calls are a design
-    # choice and are not counted
+    # choice and are not counted, nor are the acceptance's few KiB
     e_bytes = cfg.V * cfg.d * 2
     ffw_bytes = 2 * cfg.F * cfg.d * 2
     alg_bytes = 2 * e_bytes + cfg.C * cfg.d * 2 + ffw_bytes + cfg.C * 8 + cfg.C * cfg.d * 2
@@ -360,6 +362,9 @@ def main():
     if not args.no_graph:
         proto["fixed_step_canvases"] = graph_canvas_rate(ctx, loop, lambda k: Hd[0][k], 5)
         note("fixed-step and graph canvases")
+    proto["native_loop"] = native_protocol(ctx, cfg, Wd, Kd, Vtd, lambda c: (lambda k: Hd[c % n_hidden][k]),
+                                           args.canvases)
+    note("whole-canvas protocol in the library's loop")
 
     if args.calibrate_copy:
         src_t = torch.empty(1 << 29, dtype=torch.int16, device=dev)
@@ -389,8 +394,9 @@ def main():
         "canvas_protocol": proto,
         "canvas_tokens_per_s_at_12_steps": round(steps_per_s * cfg.C / 12, 1),
         "commits_timed": commits,
-        "roofline": {"kernel": "dg_logits_entropy + dg_selfcond (logits_tile_kernel, row_finalize_kernel, "
-                               "selfcond_split_kernel, selfcond_reduce_kernel, 2 FFW gemm_kernel)",
+        "roofline": {"kernel": "dg_logits_entropy + dg_selfcond_accept (logits_tile_kernel, row_finalize_kernel, "
+                               "selfcond_split_kernel, selfcond_reduce_kernel with the acceptance workgroups, "
+                               "2 FFW gemm_kernel)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "alg_bytes_per_step": alg_bytes,
