@@ -77,7 +77,8 @@ class AcceptArgs(ctypes.Structure):
                 ("x0", ctypes.c_void_p), ("argmax", ctypes.c_void_p), ("prev_argmax", ctypes.c_void_p),
                 ("seed", ctypes.c_uint64), ("canvas_base", ctypes.c_uint32), ("step", ctypes.c_int32),
                 ("thr", ctypes.c_float), ("N", ctypes.c_int32), ("accept", ctypes.c_void_p),
-                ("n_accept", ctypes.c_void_p), ("tokens", ctypes.c_void_p), ("flag", ctypes.c_void_p)]
+                ("n_accept", ctypes.c_void_p), ("tokens", ctypes.c_void_p), ("flag", ctypes.c_void_p),
+                ("x_next", ctypes.c_void_p)]
 
 
 # dg_hidden_fn: (user, step) -> device pointer of H_step
@@ -108,6 +109,7 @@ def _load():
         "dg_temperature": (f32, [i32, i32, f32, f32]),
         "dg_canvas_attn": (i32, [_P, D, _P, _P, _P, _P, _P, _P, _P, _P, _P, i64, i64, _P, _P]),
         "dg_canvas_attn_static": (i32, [_P, D, _P, _P, _P, _P, _P, _P, _P, _P, _P, i64, i64, _P]),
+        "dg_canvas_attn_x": (i32, [_P, D, _P, _P, _P, _P, _P, _P, _P, i64, i64, _P, _P]),
         "dg_logits_entropy": (i32, [_P, D, _P, _P, f32, _P, _P, _P]),
         "dg_entropy_accept": (i32, [_P, i32, i32, _P, f32, _P, _P]),
         "dg_confidence": (i32, [_P, D, _P, _P]),
@@ -256,6 +258,15 @@ class Context:
         self._check(self._lib.dg_clear_status(self._h))
 
     # ------------------------------------------------------------ the seven calls
+    def canvas_attn_x(self, dims, X, Wq, Wk, Wv, Wo, Kp, Vt, P, ws, A):
+        """canvas_attn on a pre-formed input X [C, d] bf16 (e.g. selfcond_accept's x_next)."""
+        d = Dims.of(dims)
+        Pcap = Kp.shape[1] if Kp is not None else 0
+        self._check(self._lib.dg_canvas_attn_x(
+            self._h, ctypes.byref(d), _ptr(X, _BF16, "X"), _ptr(Wq, _BF16, "Wq"), _ptr(Wk, _BF16, "Wk"),
+            _ptr(Wv, _BF16, "Wv"), _ptr(Wo, _BF16, "Wo"), _ptr(Kp, _BF16, "Kp", True),
+            _ptr(Vt, _BF16, "Vt", True), int(P), int(Pcap), _ptr(ws, _U8, "ws"), _ptr(A, _BF16, "A")))
+
     def canvas_attn(self, dims, tokens, z, E, Wq, Wk, Wv, Wo, Kp, Vt, P, ws, A):
         d = Dims.of(dims)
         Pcap = Kp.shape[1] if Kp is not None else 0
@@ -335,16 +346,17 @@ class Context:
             _ptr(flag, _I32, "flag", pinned_ok=True)))
 
     def selfcond_accept(self, dims, ws, E, W1, W2, z, entropy, b, x0, argmax, prev_argmax, seed,
-                        canvas_base, step, thr, N, accept, n_accept, tokens, flag):
+                        canvas_base, step, thr, N, accept, n_accept, tokens, flag, x_next=None):
         """accept_renoise_stop then selfcond, same results; the acceptance work runs beside
-        self-conditioning's reduce. B canvases = the rows of entropy."""
+        self-conditioning's reduce. B canvases = the rows of entropy. x_next [C, d] bf16,
+        optional: receives bf16(E[tokens] + z), the next step's canvas_attn_x input."""
         d = Dims.of(dims)
         B = 1 if entropy.dim() == 1 else entropy.shape[0]
         a = AcceptArgs(int(B), _ptr(entropy, _F32, "entropy"), float(b), _ptr(x0, _I32, "x0"),
                        _ptr(argmax, _I32, "argmax"), _ptr(prev_argmax, _I32, "prev_argmax", True), int(seed),
                        int(canvas_base), int(step), float(thr), int(N), _ptr(accept, _U8, "accept"),
                        _ptr(n_accept, _I32, "n_accept"), _ptr(tokens, _I32, "tokens"),
-                       _ptr(flag, _I32, "flag", pinned_ok=True))
+                       _ptr(flag, _I32, "flag", pinned_ok=True), _ptr(x_next, _BF16, "x_next", True))
         self._check(self._lib.dg_selfcond_accept(
             self._h, ctypes.byref(d), _ptr(ws, _U8, "ws"), _ptr(E, _BF16, "E"), _ptr(W1, _BF16, "W1"),
             _ptr(W2, _BF16, "W2"), _ptr(z, _BF16, "z"), ctypes.byref(a)))

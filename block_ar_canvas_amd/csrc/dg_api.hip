@@ -177,16 +177,18 @@ dg_status enqueue_canvas_attn(dg_ctx ctx, const char *fn, const dg_dims &m, cons
                               const dg_bf16 *z, const dg_bf16 *E, const dg_bf16 *Wq, const dg_bf16 *Wk,
                               const dg_bf16 *Wv, const dg_bf16 *Wo, const dg_bf16 *Kp,
                               const dg_bf16 *Vt, int64_t P, int64_t Pcap, const AttnRegions &r,
-                              dg_bf16 *A) {
+                              dg_bf16 *A, const dg_bf16 *X = nullptr) {
   const int qd = m.Hq * m.hd, kd = m.Hkv * m.hd;
 
-  // Q, K, V of the denoiser input X = bf16(E[tokens] + z).
+  // Q, K, V of the denoiser input X = bf16(E[tokens] + z) (or the caller's X).
   GemmArgs g{};
   g.M = m.C;
   g.K = m.d;
   g.V = m.V;
   g.status = ctx->d_status;
-  if (z) {
+  if (X) {
+    g.A = X;
+  } else if (z) {
     hipError_t e = dg_launch_xgather(tokens, E, z, m.V, m.C, m.d, r.x, ctx->d_status, ctx->stream);
     if (e != hipSuccess) return hip_fail(ctx, e, fn);
     g.A = r.x;
@@ -340,6 +342,25 @@ dg_status dg_canvas_attn(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens,
                       ws_at<u16>(ws, w.vct), ws_at<u16>(ws, w.o), ws_at<float>(ws, w.po),
                       ws_at<float>(ws, w.pml)};
   return enqueue_canvas_attn(ctx, __func__, m, tokens, z, E, Wq, Wk, Wv, Wo, Kp, Vt, P, Pcap, r, A);
+}
+
+dg_status dg_canvas_attn_x(dg_ctx ctx, const dg_dims *dims, const dg_bf16 *X, const dg_bf16 *Wq,
+                           const dg_bf16 *Wk, const dg_bf16 *Wv, const dg_bf16 *Wo, const dg_bf16 *Kp,
+                           const dg_bf16 *Vt, int64_t P, int64_t Pcap, void *ws, dg_bf16 *A) {
+  DG_ENTER();
+  if (!X) return fail(ctx, DG_ERR_NULL, "%s: X is NULL", __func__);
+  if (!aligned16(X)) return fail(ctx, DG_ERR_ALIGN, "%s: X is not 16-byte aligned", __func__);
+  // the shared checks, X standing in for the token ids and E (neither is read here)
+  dg_status st = check_canvas_attn(ctx, __func__, dims, (const int32_t *)X, nullptr, X, Wq, Wk, Wv, Wo, Kp, Vt, P,
+                                   Pcap, A);
+  if (st) return st;
+  DG_REQUIRE_PTR(ws);
+  const dg_dims &m = *dims;
+  const DgWs w = dg_ws_layout(m.V, m.d, m.C, m.Hq, m.Hkv, m.hd, m.F, Pcap);
+  const AttnRegions r{w.Cpad, ws_at<u16>(ws, w.x), ws_at<u16>(ws, w.q), ws_at<u16>(ws, w.kc),
+                      ws_at<u16>(ws, w.vct), ws_at<u16>(ws, w.o), ws_at<float>(ws, w.po),
+                      ws_at<float>(ws, w.pml)};
+  return enqueue_canvas_attn(ctx, __func__, m, nullptr, nullptr, nullptr, Wq, Wk, Wv, Wo, Kp, Vt, P, Pcap, r, A, X);
 }
 
 dg_status dg_canvas_attn_static(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens,
@@ -687,7 +708,8 @@ namespace {
 // Self-conditioning after its arguments passed dg_selfcond's checks; with ars non-null the
 // reduce launch also runs acceptance, renoise and the stop test (ars->tpp * ars->C <= 256).
 dg_status selfcond_enqueue(dg_ctx ctx, const dg_dims &m, void *ws, const dg_bf16 *E, const dg_bf16 *W1,
-                           const dg_bf16 *W2, dg_bf16 *z, const ArsArgs *ars) {
+                           const dg_bf16 *W2, dg_bf16 *z, const ArsArgs *ars, dg_bf16 *x_next = nullptr,
+                           const int32_t *x_tokens = nullptr) {
   const DgWs w = dg_ws_layout(m.V, m.d, m.C, m.Hq, m.Hkv, m.hd, m.F, 0);
   SelfcondArgs a{};
   a.ptilde = ws_at<u16>(ws, w.ptilde);
@@ -723,8 +745,20 @@ dg_status selfcond_enqueue(dg_ctx ctx, const dg_dims &m, void *ws, const dg_bf16
   g2.A = gbuf;
   g2.nseg = 1;
   g2.seg[0] = GemmSeg{W2, m.d, z, m.d, 0, 1, INT_MAX, m.C, 0};
+  g2.status = ctx->d_status;
+  const bool fused = x_next && dg_gemm_can_xsum(g2);
+  if (fused) {                                       // X = bf16(E[x] + z) in the W2 epilogue
+    g2.xsum = x_next;
+    g2.xtok = x_tokens;
+    g2.xE = E;
+    g2.xV = m.V;
+  }
   e = dg_launch_gemm(g2, ctx->stream);
   if (e != hipSuccess) return hip_fail(ctx, e, "dg_selfcond(W2)");
+  if (x_next && !fused) {
+    e = dg_launch_xgather(x_tokens, E, z, m.V, m.C, m.d, x_next, ctx->d_status, ctx->stream);
+    if (e != hipSuccess) return hip_fail(ctx, e, "dg_selfcond(next input)");
+  }
   return DG_OK;
 }
 
@@ -832,13 +866,15 @@ dg_status dg_selfcond_accept(dg_ctx ctx, const dg_dims *dims, void *ws, const dg
                       acc->prev_argmax, acc->seed, acc->canvas_base, acc->step, acc->thr, acc->N, acc->accept,
                       acc->n_accept, acc->tokens, acc->flag, __func__, r)))
     return st;
+  if (acc->x_next && !aligned16(acc->x_next))
+    return fail(ctx, DG_ERR_ALIGN, "%s: x_next is not 16-byte aligned", __func__);
   if (r.C <= 256) {                                  // one reduce workgroup (256 threads) per canvas
     r.tpp = r.C <= 64 ? 4 : r.C <= 128 ? 2 : 1;
-    return selfcond_enqueue(ctx, m, ws, E, W1, W2, z, &r);
+    return selfcond_enqueue(ctx, m, ws, E, W1, W2, z, &r, acc->x_next, acc->tokens);
   }
   hipError_t e = dg_launch_accept_renoise_stop(r, ctx->stream);
   if (e != hipSuccess) return hip_fail(ctx, e, __func__);
-  return selfcond_enqueue(ctx, m, ws, E, W1, W2, z, nullptr);
+  return selfcond_enqueue(ctx, m, ws, E, W1, W2, z, nullptr, acc->x_next, acc->tokens);
 }
 
 dg_status dg_commit_kv(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens, const dg_bf16 *E,
@@ -884,7 +920,7 @@ namespace {
 
 // Device state of one canvas in dg_run_canvas's loop workspace, 256-byte aligned regions.
 struct LoopWs {
-  size_t tokens, z, A, entropy, am0, am1, accept, n_accept, smp0, smp1, conf, total;
+  size_t tokens, z, A, entropy, am0, am1, accept, n_accept, smp0, smp1, conf, X, total;
 };
 LoopWs loop_ws_layout(const dg_dims &m) {
   LoopWs w{};
@@ -906,6 +942,7 @@ LoopWs loop_ws_layout(const dg_dims &m) {
   w.smp0 = take(4 * C);                              // sampled tokens of even / odd steps
   w.smp1 = take(4 * C);
   w.conf = take(4 * C);                              // confidence scores (confidence rule)
+  w.X = take(2 * cd);                                // the next step's attention input
   w.total = off;
   return w;
 }
@@ -990,7 +1027,9 @@ dg_status dg_run_canvas(dg_ctx ctx, const dg_dims *dims, const dg_weights *w, dg
   int32_t *nacc = ws_at<int32_t>(loop_ws, L.n_accept);
   int32_t *smp[2] = {ws_at<int32_t>(loop_ws, L.smp0), ws_at<int32_t>(loop_ws, L.smp1)};
   float *conf = ws_at<float>(loop_ws, L.conf);
+  dg_bf16 *X = ws_at<dg_bf16>(loop_ws, L.X);
   const bool sample = prm->draw == DG_DRAW_SAMPLE;
+  const bool x_ready = prm->rule == DG_RULE_ENTROPY;   // each step forms the next one's input
 
   // a uniform random canvas (stream 1 of the canvas's draws)
   if ((st = dg_renoise(ctx, 1, m.C, m.V, nullptr, nullptr, prm->seed, prm->canvas, 0, tok))) return st;
@@ -1000,7 +1039,9 @@ dg_status dg_run_canvas(dg_ctx ctx, const dg_dims *dims, const dg_weights *w, dg
     if (!H) return fail(ctx, DG_ERR_NULL, "dg_run_canvas: hidden state of step %d is NULL", k);
     if (!aligned16(H)) return fail(ctx, DG_ERR_ALIGN, "dg_run_canvas: hidden state of step %d is not 16-byte aligned", k);
     int32_t *a = am[k & 1], *prev = k > 0 ? am[(k - 1) & 1] : nullptr;
-    dg_status r = dg_canvas_attn(ctx, dims, tok, k > 0 ? z : nullptr, E, Wq, Wk, Wv, Wo, Kp, Vt, P, Pcap, ws, A);
+    dg_status r = k > 0 && x_ready
+                      ? dg_canvas_attn_x(ctx, dims, X, Wq, Wk, Wv, Wo, Kp, Vt, P, Pcap, ws, A)
+                      : dg_canvas_attn(ctx, dims, tok, k > 0 ? z : nullptr, E, Wq, Wk, Wv, Wo, Kp, Vt, P, Pcap, ws, A);
     if (!r) r = dg_logits_entropy(ctx, dims, H, E, dg_temperature(k, N, prm->tau0, prm->tau1), ws, ent, a);
     int32_t *x0k = a;                                // what accepted positions keep
     if (!r && sample) {
@@ -1035,6 +1076,7 @@ dg_status dg_run_canvas(dg_ctx ctx, const dg_dims *dims, const dg_weights *w, dg
     aa.n_accept = nacc;
     aa.tokens = tok;
     aa.flag = ctx->host_flags + sl;
+    aa.x_next = X;
     return dg_selfcond_accept(ctx, dims, ws, E, W1, W2, z, &aa);
   };
 

@@ -301,7 +301,16 @@ struct GemmArgs {
   // the sum goes to out32 + s * split_stride, and the consumer adds the parts in order.
   int ksplit;
   int64_t split_stride;
+  // bf16 output of segment 0 with 16-byte stores along n (ST_NVEC) only: also writes
+  // xsum[m * N + n] = bf16(E[xtok[m]][n] + D[m][n]), the next denoise step's input, with
+  // xE rows of N elements (an id outside [0, xV) sets the range status and reads row 0)
+  u16 *xsum;
+  const int *xtok;
+  const u16 *xE;
+  int xV;
 };
+// 1 when the launch can form xsum in its epilogue (segment 0 stored with ST_NVEC).
+int dg_gemm_can_xsum(const GemmArgs &a);
 hipError_t dg_launch_gemm(const GemmArgs &a, hipStream_t st);
 
 // Canvas MoE FFN workspace (256-byte aligned regions).

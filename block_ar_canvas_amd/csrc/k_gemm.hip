@@ -68,6 +68,16 @@ DG_DEV void wait_stages(int rem) {
 // Output store modes of a segment (chosen on the host).
 enum { ST_SCALAR = 0, ST_NVEC = 1, ST_MVEC = 2 };
 
+// Eight bf16 sums e + z, each added in float32 and rounded to bf16 (the denoiser input
+// X = bf16(E[x] + z), wherever it is formed).
+DG_DEV uint4 add_bf16x8(uint4 ee, uint4 zz) {
+  const uint32_t *e = (const uint32_t *)&ee, *zw = (const uint32_t *)&zz;
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(bf16lo(e[j]) + bf16lo(zw[j]), bf16hi(e[j]) + bf16hi(zw[j]));
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 template <int TN, int TM, int NS, bool GATHER>
 __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
   using T = Tile<TN, TM, NS>;
@@ -225,9 +235,19 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
   const int m = m0 + row;
   if (mode == ST_NVEC) {
     const int n = nb0 + c8;
-    if (m < sg.m_store && n < sg.N)
-      *(uint4 *)(sg.out + (int64_t)m * sg.sm + (int64_t)(n / sg.seg) * sg.sg +
-                 (int64_t)(n % sg.seg) * sg.se) = *(const uint4 *)(ot + row * T::OPITCH + c8);
+    if (m < sg.m_store && n < sg.N) {
+      const uint4 zz = *(const uint4 *)(ot + row * T::OPITCH + c8);
+      *(uint4 *)(sg.out + (int64_t)m * sg.sm + (int64_t)(n / sg.seg) * sg.sg + (int64_t)(n % sg.seg) * sg.se) = zz;
+      if (a.xsum && si == 0) {                       // the next step's input E[x] + this output
+        int tok = a.xtok[m];
+        if (tok < 0 || tok >= a.xV) {                // read as id 0, like the gather GEMM
+          set_status(a.status, DGS_RANGE);
+          tok = 0;
+        }
+        const uint4 ee = *(const uint4 *)(a.xE + (int64_t)tok * sg.N + n);
+        *(uint4 *)(a.xsum + (int64_t)m * sg.N + n) = add_bf16x8(ee, zz);
+      }
+    }
   } else if (m < sg.m_store) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -253,12 +273,7 @@ __global__ __launch_bounds__(256) void xgather_kernel(const int *tokens, const u
   for (int k = threadIdx.x * 8; k < K; k += 256 * 8) {
     const uint4 zz = *(const uint4 *)(z + (int64_t)m * K + k);
     const uint4 ee = *(const uint4 *)(E + (int64_t)tok * K + k);
-    const uint32_t *e = (const uint32_t *)&ee, *zw = (const uint32_t *)&zz;
-    uint32_t o[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      o[j] = pack_bf16x2(bf16lo(e[j]) + bf16lo(zw[j]), bf16hi(e[j]) + bf16hi(zw[j]));
-    *(uint4 *)(X + (int64_t)m * K + k) = make_uint4(o[0], o[1], o[2], o[3]);
+    *(uint4 *)(X + (int64_t)m * K + k) = add_bf16x8(ee, zz);
   }
 }
 
@@ -307,6 +322,11 @@ hipError_t launch_tile(GemmArgs a, int S, hipStream_t st) {
 // Tile shape: every workgroup streams (TN + TM) rows of K through its CU, so the shape
 // with the fewest operand bytes per CU, rounds of workgroups x (TN + TM), is taken; on
 // a tie the one with fewer workgroups (less total copying).
+int dg_gemm_can_xsum(const GemmArgs &a) {
+  const GemmSeg &s = a.seg[0];
+  return a.nseg >= 1 && !a.out32 && store_mode(s) == ST_NVEC && s.sm == s.N && s.seg >= (1 << 30) ? 1 : 0;
+}
+
 hipError_t dg_launch_gemm(const GemmArgs &a, hipStream_t st) {
   const int S = (a.out32 && a.ksplit > 1) ? a.ksplit : 1;
   if (S > 1 && a.K % (32 * S) != 0) return hipErrorInvalidValue;

@@ -62,6 +62,12 @@ class CanvasLoop:
         self.sampled = [torch.empty(C, dtype=torch.int32, device=dev) for _ in range(2)]
         self.accept = torch.empty(C, dtype=torch.uint8, device=dev)
         self.n_accept = torch.empty(1, dtype=torch.int32, device=dev)
+        # The next step's attention input bf16(E[tokens] + z), formed by the entropy rule's
+        # self-conditioning call; _x_for records the (canvas, step) that formed it and the
+        # torch version counters of tokens and z then, so a step uses it only if nothing
+        # has rewritten them since (a restored state, a caller's edit).
+        self.X = torch.empty(C, d, dtype=torch.bfloat16, device=dev)
+        self._x_for = None
         # Stop flags live in pinned host memory; the stop test writes them with
         # system-scope stores, the host pre-fills -1 when it enqueues the step and polls,
         # so no copy or event sits between two steps' kernels on the stream. Steps take
@@ -82,13 +88,18 @@ class CanvasLoop:
         self.ctx.renoise(self.dims.V, None, None, self.seed, canvas, 0, self.tokens)
         self.canvas = canvas
         self._slot = {}
+        self._x_for = None
 
     def step(self, k: int, H):
         """Enqueues denoise step k on hidden states H [C, d]; wait_flag(k) returns its flag."""
         W, dm = self.W, self.dims
         am, prev = self.argmax[k & 1], (self.argmax[(k - 1) & 1] if k > 0 else None)
-        self.ctx.canvas_attn(dm, self.tokens, self.z if k > 0 else None, W["E"], W["Wq"], W["Wk"],
-                             W["Wv"], W["Wo"], self.Kp, self.Vt, self.P, self.ws, self.A)
+        if k > 0 and self._x_for == (self.canvas, k - 1, self.tokens._version, self.z._version):
+            self.ctx.canvas_attn_x(dm, self.X, W["Wq"], W["Wk"], W["Wv"], W["Wo"], self.Kp, self.Vt, self.P,
+                                   self.ws, self.A)
+        else:
+            self.ctx.canvas_attn(dm, self.tokens, self.z if k > 0 else None, W["E"], W["Wq"], W["Wk"],
+                                 W["Wv"], W["Wo"], self.Kp, self.Vt, self.P, self.ws, self.A)
         tau = temperature(k, self.N, self.tau0, self.tau1)
         ev = self.logits_events
         if ev is not None:
@@ -118,11 +129,14 @@ class CanvasLoop:
             s0.record(self.ctx.torch_stream())
         if self.rule == "confidence":
             self.ctx.selfcond(dm, self.ws, W["E"], W["W1"], W["W2"], self.z)
+            self._x_for = None
         else:
-            # acceptance, renoise and the stop test run beside self-conditioning's reduce
+            # acceptance, renoise and the stop test run beside self-conditioning's reduce,
+            # and its FFW forms the next step's attention input
             self.ctx.selfcond_accept(dm, self.ws, W["E"], W["W1"], W["W2"], self.z, self.entropy, self.b, x0,
                                      am, prev, self.seed, self.canvas, k, self.thr, self.N, self.accept,
-                                     self.n_accept, self.tokens, self.flags[slot])
+                                     self.n_accept, self.tokens, self.flags[slot], x_next=self.X)
+            self._x_for = (self.canvas, k, self.tokens._version, self.z._version)
         if sev is not None:
             s1 = torch.cuda.Event(enable_timing=True)
             s1.record(self.ctx.torch_stream())
@@ -246,6 +260,8 @@ class BatchLoop:
         self.sampled = [torch.empty(B, C, dtype=torch.int32, device=dev) for _ in range(2)]
         self.accept = torch.empty(B, C, dtype=torch.uint8, device=dev)
         self.n_accept = torch.empty(B, dtype=torch.int32, device=dev)
+        self.X = torch.empty(B, C, d, dtype=torch.bfloat16, device=dev)   # as in CanvasLoop
+        self._x_for = None
         # Same protocol as CanvasLoop: pinned flags written by the stop kernel, four
         # buffers taken in enqueue order.
         self.flags = [torch.full((B,), -1, dtype=torch.int32, pin_memory=True) for _ in range(4)]
@@ -260,16 +276,22 @@ class BatchLoop:
         with torch.cuda.stream(self.ctx.torch_stream()):
             self.z.zero_()
         self._slot = {}
+        self._x_for = None
 
     def step(self, k: int, H):
         """Enqueues denoise step k of every canvas; H [B*C, d] holds the canvases' hidden
         states in canvas order."""
         W, dm = self.W, self.dims
         am, prev = self.argmax[k & 1], (self.argmax[(k - 1) & 1] if k > 0 else None)
+        use_x = k > 0 and self._x_for == (self.batch, k - 1, self.tokens._version, self.z._version)
         for i in range(self.B):
-            self.ctx.canvas_attn(dm, self.tokens[i], self.z[i] if k > 0 else None, W["E"], W["Wq"],
-                                 W["Wk"], W["Wv"], W["Wo"], self.Kp[i], self.Vt[i], self.P[i],
-                                 self.ws_attn, self.A[i])
+            if use_x:
+                self.ctx.canvas_attn_x(dm, self.X[i], W["Wq"], W["Wk"], W["Wv"], W["Wo"], self.Kp[i], self.Vt[i],
+                                       self.P[i], self.ws_attn, self.A[i])
+            else:
+                self.ctx.canvas_attn(dm, self.tokens[i], self.z[i] if k > 0 else None, W["E"], W["Wq"],
+                                     W["Wk"], W["Wv"], W["Wo"], self.Kp[i], self.Vt[i], self.P[i],
+                                     self.ws_attn, self.A[i])
         tau = temperature(k, self.N, self.tau0, self.tau1)
         ev = self.logits_events
         if ev is not None:
@@ -296,10 +318,13 @@ class BatchLoop:
             self.ctx.renoise(dm.V, x0, self.accept, self.seed, base, k, self.tokens)
             self.ctx.stop_test(self.entropy, am, prev, self.thr, k, self.N, self.flags[slot])
             self.ctx.selfcond(self.dims_all, self.ws, W["E"], W["W1"], W["W2"], self.z.view(-1, dm.d))
+            self._x_for = None
         else:
             self.ctx.selfcond_accept(self.dims_all, self.ws, W["E"], W["W1"], W["W2"], self.z.view(-1, dm.d),
                                      self.entropy, self.b, x0, am, prev, self.seed, base, k, self.thr, self.N,
-                                     self.accept, self.n_accept, self.tokens, self.flags[slot])
+                                     self.accept, self.n_accept, self.tokens, self.flags[slot],
+                                     x_next=self.X.view(-1, dm.d))
+            self._x_for = (self.batch, k, self.tokens._version, self.z._version)
         return am
 
     def wait_flags(self, k: int, timeout_s: float = 60.0):

@@ -125,6 +125,15 @@ dg_status dg_canvas_attn(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens,
                          const dg_bf16 *Kp, const dg_bf16 *Vt, int64_t P, int64_t Pcap,
                          void *ws, dg_bf16 *A);
 
+/* dg_canvas_attn on a denoiser input the caller formed: X [C, d] bf16 in place of
+ * bf16(E[tokens] + z) (for instance the x_next of the previous step's dg_selfcond_accept,
+ * which saves the gather launch). Same results as dg_canvas_attn given the tokens and z
+ * that X was formed from; same layouts, workspace and errors (X must be 16-byte aligned). */
+dg_status dg_canvas_attn_x(dg_ctx ctx, const dg_dims *dims, const dg_bf16 *X, const dg_bf16 *Wq,
+                           const dg_bf16 *Wk, const dg_bf16 *Wv, const dg_bf16 *Wo,
+                           const dg_bf16 *Kp, const dg_bf16 *Vt, int64_t P, int64_t Pcap,
+                           void *ws, dg_bf16 *A);
+
 /* dg_canvas_attn without a workspace argument and without any allocation, for callers
  * that cannot allocate device memory: code under HIP graph capture, tight serving
  * loops, harnesses that forbid allocation. Same arguments (minus ws), validation,
@@ -265,8 +274,11 @@ dg_status dg_accept_renoise_stop(dg_ctx ctx, int32_t B, int32_t C, int32_t V,
  * 256 positions the acceptance work runs as extra workgroups of the self-conditioning
  * reduce launch, beside the reduce, instead of in a launch of its own; the stop flag is
  * then written while s is reduced. Larger canvases take a launch of its own first.
- * accept, n_accept, tokens and flag must not overlap ws or z. Errors: those of both
- * calls, checked before anything is enqueued; DG_ERR_SHAPE unless B >= 1 divides C. */
+ * accept, n_accept, tokens and flag must not overlap ws or z. With x_next non-NULL it also
+ * writes x_next = bf16(E[tokens] + z) for the new tokens and z, the input the next step's
+ * dg_canvas_attn would form (bit for bit), so that step can take dg_canvas_attn_x.
+ * Errors: those of both calls, checked before anything is enqueued; DG_ERR_SHAPE unless
+ * B >= 1 divides C; DG_ERR_ALIGN for an x_next that is not 16-byte aligned. */
 typedef struct {
   int32_t B;                 /* canvases; dims->C / B positions each */
   const float *entropy;      /* [B, C/B] */
@@ -282,6 +294,8 @@ typedef struct {
   int32_t *n_accept;         /* [B] output */
   int32_t *tokens;           /* [B, C/B] output */
   int32_t *flag;             /* [B] output, device or pinned host memory */
+  dg_bf16 *x_next;           /* [C, d] output or NULL: bf16(E[tokens] + z), the next step's
+                                dg_canvas_attn_x input (formed in the FFW's epilogue) */
 } dg_accept_args;
 dg_status dg_selfcond_accept(dg_ctx ctx, const dg_dims *dims, void *ws, const dg_bf16 *E,
                              const dg_bf16 *W1, const dg_bf16 *W2, dg_bf16 *z,
@@ -364,7 +378,9 @@ dg_status dg_commit_kv(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens,
  * hidden(user, k) is called on the host before step k is enqueued and returns the device
  * pointer of H_k [C, d] bf16; it may enqueue work producing H_k on the context's stream.
  * loop_ws holds dg_loop_workspace_bytes(dims) bytes (the canvas tokens, z, the attention
- * output, entropies, both argmax and sampled-token buffers, acceptance, confidences). Outputs: x0 [C] device int32, the
+ * output, entropies, both argmax and sampled-token buffers, acceptance, confidences, and
+ * the next step's attention input, which the entropy rule's steps form for
+ * dg_canvas_attn_x). Outputs: x0 [C] device int32, the
  * committed block; *steps (host) the steps run; *P_out (host) = P + C. Returns after the
  * commit is enqueued (dg_sync waits for it). A flag not written within 60 s of waiting
  * ends the call with DG_ERR_HIP after a stream synchronization. */

@@ -413,6 +413,47 @@ def test_selfcond_accept_matches_the_separate_calls(dg_ctx, name, B):
     np.testing.assert_array_equal(outs[1][4], O.stop_test(e, am_np, am_np, 10.0, k, cfg.N))
 
 
+@pytest.mark.parametrize("name,B", [("ragged", 1), ("small", 1), ("ragged", 4), ("c1000", 1)],
+                         ids=["ragged", "small", "ragged-B4", "c1000"])
+def test_next_input_and_canvas_attn_x(dg_ctx, name, B):
+    """selfcond_accept's x_next is bf16(E[tokens] + z) of its own new tokens and z, bit for
+    bit (float32 add of the two bf16 values, rounded to nearest even, computed here on the
+    host from the device's tokens and z); canvas_attn_x on it gives canvas_attn's bytes."""
+    cfg, W, Kp, Vp, Pcap, Wd = setup(name)
+    ws = ws_for(cfg, Pcap)
+    k = 1
+    H = bf16_dev(di.hidden(cfg, W["E"], 0, k, di.targets(cfg, 0)))
+    Cs = cfg.C // B
+    ent = torch.empty(B, Cs, dtype=torch.float32, device=DEV)
+    am = torch.empty(B, Cs, dtype=torch.int32, device=DEV)
+    dg_ctx.logits_entropy(cfg, H, Wd["E"], O.temperature(k, cfg.N), ws, ent.view(-1), am.view(-1))
+    z = torch.empty(cfg.C, cfg.d, dtype=torch.bfloat16, device=DEV)
+    X = torch.full((cfg.C, cfg.d), -1.0, dtype=torch.bfloat16, device=DEV)
+    acc = torch.empty(B, Cs, dtype=torch.uint8, device=DEV)
+    n = torch.empty(B, dtype=torch.int32, device=DEV)
+    tok = torch.empty(B, Cs, dtype=torch.int32, device=DEV)
+    flag = torch.empty(B, dtype=torch.int32, device=DEV)
+    dg_ctx.selfcond_accept(cfg, ws, Wd["E"], Wd["W1"], Wd["W2"], z, ent, 0.1, am, am, None, 5, 0, k, 0.005, cfg.N,
+                           acc, n, tok, flag, x_next=X)
+    dg_ctx.sync()
+    t = tok.cpu().numpy().reshape(-1)
+    e = O.from_bf16(W["E"][t]).astype(np.float32)
+    ref = O.to_bf16(e + O.from_bf16(bits_np(z)).astype(np.float32))
+    np.testing.assert_array_equal(bits_np(X), ref)
+    # attention of one canvas on X against attention on (tokens, z)
+    Kd, Vtd = upload_cache(Kp, Vp)
+    cfg1 = cfg.with_(C=Cs)
+    ws1 = ws_for(cfg1, Pcap)
+    A1 = torch.empty(Cs, cfg.d, dtype=torch.bfloat16, device=DEV)
+    A2 = torch.empty(Cs, cfg.d, dtype=torch.bfloat16, device=DEV)
+    # the last canvas's rows, copied to 16-byte-aligned buffers
+    t1, z1, X1 = tok[B - 1].clone(), z[(B - 1) * Cs:].clone(), X[(B - 1) * Cs:].clone()
+    dg_ctx.canvas_attn(cfg1, t1, z1, Wd["E"], Wd["Wq"], Wd["Wk"], Wd["Wv"], Wd["Wo"], Kd, Vtd, cfg.P0, ws1, A1)
+    dg_ctx.canvas_attn_x(cfg1, X1, Wd["Wq"], Wd["Wk"], Wd["Wv"], Wd["Wo"], Kd, Vtd, cfg.P0, ws1, A2)
+    dg_ctx.sync()
+    np.testing.assert_array_equal(bits_np(A2), bits_np(A1))
+
+
 def test_selfcond_accept_refusals(dg_ctx):
     cfg, W, Kp, Vp, Pcap, Wd = setup("ragged")
     ws = ws_for(cfg, Pcap)
