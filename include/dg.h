@@ -11,7 +11,8 @@
  *   dg_stop_test       adaptive stop (mean entropy and stable argmax) / step cap
  * and, once per canvas, dg_commit_kv appends the finalized block to the KV cache.
  * dg_accept_renoise_stop runs acceptance, renoise and the stop test in one launch, and
- * dg_selfcond_accept runs them beside self-conditioning's reduce.
+ * dg_selfcond_accept runs them beside self-conditioning's reduce (and can form the next
+ * step's attention input, which dg_canvas_attn_x takes).
  * Beyond that step: dg_prefill_block (the causal re-encode commit) with dg_set_rope,
  * dg_confidence / dg_topk_accept / dg_reveal_count (confidence-ranked acceptance),
  * dg_sample (sampled tokens), dg_moe_ffn (the canvas mixture-of-experts FFN),
