@@ -172,6 +172,22 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
     }
   }
 
+  // The next step's input (segment 0, 16-byte stores along n): this thread's 16 bytes of
+  // E[x] are loaded now, so their latency overlaps the reduction below.
+  uint4 xe = make_uint4(0u, 0u, 0u, 0u);
+  const bool xdo = a.xsum && si == 0 && a.store_mode[0] == ST_NVEC && tid < TM * (TN / 8);
+  if (xdo) {
+    const int m = m0 + tid / (TN / 8), n = nb0 + (tid % (TN / 8)) * 8;
+    if (m < sg.m_store && n < sg.N) {
+      int tok = a.xtok[m];
+      if (tok < 0 || tok >= a.xV) {                  // read as id 0, like the gather GEMM
+        set_status(a.status, DGS_RANGE);
+        tok = 0;
+      }
+      xe = *(const uint4 *)(a.xE + (int64_t)tok * sg.N + n);
+    }
+  }
+
   // Sum of the eight waves' tiles in a fixed wave order; wave w then owns registers
   // [w*RPW, +RPW) of the tile sequence (tile q = index / 16, register = index % 16).
   __syncthreads();
@@ -238,15 +254,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(GemmArgs a, int MB) {
     if (m < sg.m_store && n < sg.N) {
       const uint4 zz = *(const uint4 *)(ot + row * T::OPITCH + c8);
       *(uint4 *)(sg.out + (int64_t)m * sg.sm + (int64_t)(n / sg.seg) * sg.sg + (int64_t)(n % sg.seg) * sg.se) = zz;
-      if (a.xsum && si == 0) {                       // the next step's input E[x] + this output
-        int tok = a.xtok[m];
-        if (tok < 0 || tok >= a.xV) {                // read as id 0, like the gather GEMM
-          set_status(a.status, DGS_RANGE);
-          tok = 0;
-        }
-        const uint4 ee = *(const uint4 *)(a.xE + (int64_t)tok * sg.N + n);
-        *(uint4 *)(a.xsum + (int64_t)m * sg.N + n) = add_bf16x8(ee, zz);
-      }
+      if (xdo) *(uint4 *)(a.xsum + (int64_t)m * sg.N + n) = add_bf16x8(xe, zz);   // E[x] + this output
     }
   } else if (m < sg.m_store) {
 #pragma unroll
