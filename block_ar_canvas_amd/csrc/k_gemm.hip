@@ -26,8 +26,10 @@
 //   * Workgroups that share a weight tile (same n tile, other m tiles) are placed on
 //     the same XCD, so each weight tile is fetched from HBM once per L2.
 // The embedding gather X = E[tokens] (rows read through per-lane addresses) is done by
-// the copies themselves; the self-conditioned input E[tokens] + z is formed once by
-// xgather_kernel (a bf16 add needs ALU work that a direct copy cannot do).
+// the copies themselves. The self-conditioned input bf16(E[tokens] + z) needs ALU work
+// that a direct copy cannot do: xgather_kernel forms it, or the FFW W2 launch does in
+// its epilogue (xsum), reading the E rows of the new tokens at the positions where it
+// stores z and adding with the gather kernel's routine, so both give the same bits.
 #include "dg_common.h"
 
 namespace {
