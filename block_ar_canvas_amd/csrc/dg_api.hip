@@ -143,7 +143,8 @@ hipError_t scratch_setup(int device, void **out) {
 struct AttnRegions {
   int Cpad;
   u16 *x, *q, *kc, *vct, *o;
-  float *po, *pml;
+  u16 *po;
+  float *pml;
 };
 
 // Validation shared by dg_canvas_attn and dg_canvas_attn_static (fn names the caller).
@@ -339,7 +340,7 @@ dg_status dg_canvas_attn(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens,
   const dg_dims &m = *dims;
   const DgWs w = dg_ws_layout(m.V, m.d, m.C, m.Hq, m.Hkv, m.hd, m.F, Pcap);
   const AttnRegions r{w.Cpad, ws_at<u16>(ws, w.x), ws_at<u16>(ws, w.q), ws_at<u16>(ws, w.kc),
-                      ws_at<u16>(ws, w.vct), ws_at<u16>(ws, w.o), ws_at<float>(ws, w.po),
+                      ws_at<u16>(ws, w.vct), ws_at<u16>(ws, w.o), ws_at<u16>(ws, w.po),
                       ws_at<float>(ws, w.pml)};
   return enqueue_canvas_attn(ctx, __func__, m, tokens, z, E, Wq, Wk, Wv, Wo, Kp, Vt, P, Pcap, r, A);
 }
@@ -358,7 +359,7 @@ dg_status dg_canvas_attn_x(dg_ctx ctx, const dg_dims *dims, const dg_bf16 *X, co
   const dg_dims &m = *dims;
   const DgWs w = dg_ws_layout(m.V, m.d, m.C, m.Hq, m.Hkv, m.hd, m.F, Pcap);
   const AttnRegions r{w.Cpad, ws_at<u16>(ws, w.x), ws_at<u16>(ws, w.q), ws_at<u16>(ws, w.kc),
-                      ws_at<u16>(ws, w.vct), ws_at<u16>(ws, w.o), ws_at<float>(ws, w.po),
+                      ws_at<u16>(ws, w.vct), ws_at<u16>(ws, w.o), ws_at<u16>(ws, w.po),
                       ws_at<float>(ws, w.pml)};
   return enqueue_canvas_attn(ctx, __func__, m, nullptr, nullptr, nullptr, Wq, Wk, Wv, Wo, Kp, Vt, P, Pcap, r, A, X);
 }
@@ -381,7 +382,7 @@ dg_status dg_canvas_attn_static(dg_ctx ctx, const dg_dims *dims, const int32_t *
                 __func__, w.total, (size_t)DG_STATIC_SCRATCH_BYTES);
   void *ws = ctx->scratch;
   const AttnRegions r{w.Cpad, ws_at<u16>(ws, w.x), ws_at<u16>(ws, w.q), ws_at<u16>(ws, w.kc),
-                      ws_at<u16>(ws, w.vct), ws_at<u16>(ws, w.o), ws_at<float>(ws, w.po),
+                      ws_at<u16>(ws, w.vct), ws_at<u16>(ws, w.o), ws_at<u16>(ws, w.po),
                       ws_at<float>(ws, w.pml)};
   return enqueue_canvas_attn(ctx, __func__, m, tokens, z, E, Wq, Wk, Wv, Wo, Kp, Vt, P, Pcap, r, A);
 }
@@ -553,7 +554,7 @@ dg_status dg_prefill_block(dg_ctx ctx, const dg_dims *dims, const int32_t *token
   at.nsplit = dg_attn_nsplit(m.Hkv, m.Hq, m.C, P);
   at.causal = 1;
   at.scale_log2 = (float)(1.4426950408889634 / sqrt((double)m.hd));
-  at.po = ws_at<float>(ws, w.po);
+  at.po = ws_at<u16>(ws, w.po);
   at.pml = ws_at<float>(ws, w.pml);
   at.O = o;
   e = dg_launch_attention(at, ctx->stream);

@@ -163,7 +163,7 @@ struct DgWs {
   size_t kc;       // canvas keys   bf16 [Cpad][Hkv*hd]
   size_t vct;      // canvas values bf16 [Hkv*hd][Cpad] (transposed)
   size_t o;        // attention output before Wo, bf16 [Cpad][Hq*hd]
-  size_t po;       // attention partial O fp32 [nsplit][Hq][Cpad][hd]
+  size_t po;       // attention partial O bf16 [nsplit][Hq][Cpad][hd]
   size_t pml;      // attention partial (max, sum) fp32 [nsplit][Hq][Cpad][2]
   size_t ps;       // self-cond partial s^T fp32 [nsc][d][Cpad]
   size_t s;        // s = p0 E rounded to bf16 [Cpad][d]
@@ -240,7 +240,7 @@ static inline DgWs dg_ws_layout(int V, int d, int C, int Hq, int Hkv, int hd, in
   w.x = take((size_t)w.Cpad * d * 2);
   // Regions sized by the cache capacity come last, so every other offset is the same
   // whatever Pcap the layout is computed for.
-  w.po = take((size_t)w.nsplit_max * Hq * w.Cpad * hd * 4);
+  w.po = take((size_t)w.nsplit_max * Hq * w.Cpad * hd * 2);
   w.pml = take((size_t)w.nsplit_max * Hq * w.Cpad * 2 * 4);
   w.total = off;
   return w;
@@ -266,7 +266,7 @@ static inline DgAttnWs dg_attn_ws_layout(int d, int C, int Hq, int Hkv, int hd, 
   w.kc = take((size_t)w.Cpad * Hkv * hd * 2);
   w.vct = take((size_t)w.Cpad * Hkv * hd * 2);
   w.o = take((size_t)w.Cpad * Hq * hd * 2);
-  w.po = take((size_t)nsplit * Hq * w.Cpad * hd * 4);
+  w.po = take((size_t)nsplit * Hq * w.Cpad * hd * 2);
   w.pml = take((size_t)nsplit * Hq * w.Cpad * 2 * 4);
   w.total = off;
   return w;
@@ -400,7 +400,7 @@ struct AttnArgs {
   int nsplit;
   int causal;          // 1: canvas-segment key j visible to query i only for j <= i
   float scale_log2;    // log2(e) / sqrt(hd)
-  float *po;           // [nsplit][Hq][Cpad][hd]
+  u16 *po;             // [nsplit][Hq][Cpad][hd] bf16, relative to the split's max
   float *pml;          // [nsplit][Hq][Cpad][2]
   u16 *O;              // merged output [Cpad][Hq*hd]
 };

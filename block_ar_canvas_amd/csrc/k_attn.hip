@@ -13,8 +13,10 @@
 // contiguous range of 64-key tiles. Eight waves of 32 query rows each, two per SIMD,
 // every wave on whole tiles with its own online softmax. K and V^T tiles stream
 // HBM -> registers -> LDS into a 4-slot ring (two tiles ahead), one barrier per tile.
-// The split's partial (O, max, sum) go to the workspace as row-major fp32
-// (coalesced), and attn_merge_kernel combines the splits in a fixed order.
+// The split's partial O goes to the workspace row-major in bf16 (coalesced 16-byte
+// stores; it is relative to the split's own max, so rounding it costs one bf16 ulp
+// before the merge, and A is bf16 anyway), its (max, sum) in fp32, and
+// attn_merge_kernel combines the splits in a fixed order.
 //
 // Orientation: S^T = K Q^T (keys are MFMA rows, loaded through perm_row so that the
 // probabilities come out as ready B fragments), O^T = V^T P^T (V is stored transposed
@@ -338,15 +340,18 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(AttnArgs a, int nq,
     a.pml[2 * row] = mref;
     a.pml[2 * row + 1] = lsum;
   }
-  constexpr int F4 = HD / 4;   // float4 per row
-  for (int f = lane; f < 32 * F4; f += 64) {
-    const int rl = f / F4, c4 = f % F4;
+  // The partial O is stored rounded to bf16 (its own reference and fp32 sum keep the
+  // scale): one 16-byte store per eight head dims.
+  constexpr int F8 = HD / 8;
+  for (int f = lane; f < 32 * F8; f += 64) {
+    const int rl = f / F8, c8 = f % F8;
     const int rq = qb * QB + wave * 32 + rl;
     if (rq >= G * a.C) continue;
     const int h = g * G + rq / a.C, c = rq % a.C;
-    const float *src = ot + rl * F::OPITCH + 4 * c4;
-    *(float4 *)(a.po + (((int64_t)split * a.Hq + h) * a.Cpad + c) * HD + 4 * c4) =
-        make_float4(src[0], src[1], src[2], src[3]);
+    const float *src = ot + rl * F::OPITCH + 8 * c8;
+    *(uint4 *)(a.po + (((int64_t)split * a.Hq + h) * a.Cpad + c) * HD + 8 * c8) =
+        uint4{pack_bf16x2(src[0], src[1]), pack_bf16x2(src[2], src[3]), pack_bf16x2(src[4], src[5]),
+              pack_bf16x2(src[6], src[7])};
   }
 }
 
@@ -373,23 +378,25 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   float L = 0.f, o[8] = {};
   for (int s0 = 0; s0 < ns; s0 += U) {
     float ms[U], ls[U];
-    float4 x0[U], x1[U];
+    uint4 x[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t pr = prow(min(s0 + u, ns - 1));
       ms[u] = a.pml[2 * pr];
       ls[u] = a.pml[2 * pr + 1];
-      const float4 *p = (const float4 *)(a.po + pr * HD + e0);
-      x0[u] = p[0];
-      x1[u] = p[1];
+      x[u] = *(const uint4 *)(a.po + pr * HD + e0);   // eight bf16
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {                  // branch-free: clamped repeats weigh 0
       const float e = exp2_fast(ms[u] - M);
       const float w = (s0 + u < ns && ms[u] != -INFINITY) ? e : 0.f;
       L += ls[u] * w;
-      o[0] += x0[u].x * w; o[1] += x0[u].y * w; o[2] += x0[u].z * w; o[3] += x0[u].w * w;
-      o[4] += x1[u].x * w; o[5] += x1[u].y * w; o[6] += x1[u].z * w; o[7] += x1[u].w * w;
+      const uint32_t wd[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        o[2 * k] += __uint_as_float(wd[k] << 16) * w;
+        o[2 * k + 1] += __uint_as_float(wd[k] & 0xffff0000u) * w;
+      }
     }
   }
   const float inv = 1.f / L;

@@ -145,7 +145,7 @@ dg_status dg_canvas_attn_x(dg_ctx ctx, const dg_dims *dims, const dg_bf16 *X, co
  * device (several streams or host threads, or contexts on different streams) race and
  * must be serialized by the caller; nothing in it needs to start zeroed.
  * DG_ERR_CAPACITY (nothing enqueued) when the dims need more than the array holds
- * (about 36.5 MiB at C 256, d 2048, 16 query / 8 KV heads of 128, any prefix length);
+ * (about 20.5 MiB at C 256, d 2048, 16 query / 8 KV heads of 128, any prefix length);
  * DG_ERR_HIP when the array's address could not be found on this device. */
 #define DG_STATIC_SCRATCH_BYTES ((size_t)48 << 20)
 dg_status dg_canvas_attn_static(dg_ctx ctx, const dg_dims *dims, const int32_t *tokens,

@@ -67,13 +67,13 @@ def test_static_scratch_without_selfcond_term_and_empty_prefix(dg_ctx):
 
 
 def test_static_scratch_rejects_dims_beyond_its_size(dg_ctx):
-    # 1024 positions over 32 query heads of 128 at d 4096: about 60 MiB of scratch;
+    # 1024 positions over 64 query heads of 128 at d 4096: about 60 MiB of scratch;
     # the call is refused on the host before anything is enqueued
-    dims = dg.Dims(512, 4096, 1024, 32, 8, 128, 64)
+    dims = dg.Dims(512, 4096, 1024, 64, 8, 128, 64)
     dev = lambda n, dt: torch.zeros(n, dtype=dt, device=DEV)
     tok = dev(1024, torch.int32)
     E = dev(512 * 4096, torch.bfloat16)
-    Wq = dev(4096 * 4096, torch.bfloat16)
+    Wq = dev(8192 * 4096, torch.bfloat16)   # [Hq*hd, d]; also passed as Wo [d, Hq*hd]
     Wkv = dev(1024 * 4096, torch.bfloat16)
     A = dev(1024 * 4096, torch.bfloat16)
     Kd = torch.zeros(8, 8, 128, dtype=torch.bfloat16, device=DEV)
